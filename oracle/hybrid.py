@@ -1,0 +1,239 @@
+"""The hybrid long-context attention, written out plainly in float64.
+
+Test infrastructure (see the package docstring): nothing in the product path
+imports this module.
+
+Sources (page titles; the pages print no formulas, so each step below states
+the plain reading taken where a page leaves it open):
+
+* group-reading wiki, "DeepSeek-V4 深度研究剖析":
+  §5.2 SWA keeps the most recent n_win = 128 uncompressed KV;
+  §5.3 CSA compresses every m = 4 tokens' KV into one entry, a lightning
+       indexer scores the compressed blocks and a per-query top-k of them
+       (512 Flash, 1024 Pro) enters the main attention;
+  §5.4 HCA compresses every m' = 128 tokens into one entry and attends to all
+       of them densely;
+  §11.4 the caches: compressed KV, compressed indexer keys, raw SWA KV and the
+       tail of a block not yet complete.
+* zjai.club episode 163 "Deep dive" §14 and the aifrontier EP95 walkthrough of
+  the sparse attention: one shared KV head (MQA); window and compressed entries
+  are concatenated and attended together.
+
+Readings taken where the pages are silent:
+* compression is a softmax-weighted pooling: entry = sum_j alpha[j, c] * x[j, c]
+  over the m tokens of a block, alpha = softmax over the slot axis of seeded
+  per-slot, per-channel logits;
+* indexer score I[t, b] = sum_h w[t, h] * ReLU(qI[t, h] . KI_c[b]) (no scale);
+* top-k per query token, shared by all heads; ties go to the lower block;
+* block b is visible to the query at t iff it is complete and starts before the
+  window: b < min(ceil(s(t)/m), floor((t+1)/m)), s(t) = max(0, t - n_win + 1);
+* the window W(t) = {s(t), ..., t} includes the query token;
+* one softmax over window + compressed entries, logits scaled by 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import numerics as nx
+
+
+# ----------------------------------------------------------------------------- visibility
+
+def window_start(t: int, n_win: int) -> int:
+    """First raw token of the SWA window of the query at position t."""
+    return max(0, t - n_win + 1)
+
+
+def n_visible(t: int, m: int, n_win: int) -> int:
+    """Number of compressed blocks visible at t: complete, and starting before
+    the window (so they cover exactly the tokens the window does not, up to the
+    m-1 tokens of the block that straddles the window's start)."""
+    s = window_start(t, n_win)
+    return min(-(-s // m), (t + 1) // m)
+
+
+# ----------------------------------------------------------------------------- compression
+
+def pooling_weights(z: np.ndarray) -> np.ndarray:
+    """alpha = softmax over slots (axis 0) of the logits z [m, D], in float64,
+    summed in slot order, rounded once to float32."""
+    z = np.asarray(z, dtype=np.float32).astype(np.float64)
+    e = np.exp(z - z.max(axis=0, keepdims=True))
+    s = e[0].copy()
+    for j in range(1, e.shape[0]):
+        s = s + e[j]
+    return (e / s).astype(np.float32)
+
+
+def compress_exact(x_bits: np.ndarray, alpha: np.ndarray, m: int) -> np.ndarray:
+    """Pooled value of every complete block: sum_j alpha[j] * x[b*m + j], float64.
+
+    x_bits: bf16 bits [T, D]; alpha: float32 [m, D].  Returns float64 [T//m, D].
+    Each product of a float32 weight and a bf16 value is exact in float64; the
+    m products are added in slot order."""
+    x = nx.bf16_value(x_bits)
+    nb = x.shape[0] // m
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64)
+    acc = np.zeros((nb, x.shape[1]), dtype=np.float64)
+    for j in range(m):
+        acc = acc + a[j][None, :] * x[j: nb * m: m]
+    return acc
+
+
+def store_bf16(c: np.ndarray) -> np.ndarray:
+    """Compressed entries as stored in a bf16 cache (bit patterns)."""
+    return nx.bf16_bits_from_f64(c)
+
+
+def store_fp8_pages(c: np.ndarray, page: int = 64):
+    """Compressed entries as stored in an fp8 cache: one float32 scale per
+    `page` consecutive entries (all channels), scale = amax / 448 rounded to
+    float32 (1 if the page is all zero), code = e4m3fn(entry / scale).
+    A final partial page takes its scale over the entries present.
+    Returns (codes uint8 [n, D], scales float32 [ceil(n/page)])."""
+    n = c.shape[0]
+    n_pages = -(-n // page)
+    codes = np.zeros(c.shape, dtype=np.uint8)
+    scales = np.zeros(n_pages, dtype=np.float32)
+    for p in range(n_pages):
+        blk = c[p * page:(p + 1) * page]
+        amax = np.abs(blk).max() if blk.size else 0.0
+        sc = np.float32(amax / nx.E4M3_MAX) if amax > 0 else np.float32(1.0)
+        scales[p] = sc
+        codes[p * page:(p + 1) * page] = nx.e4m3_encode(blk / np.float64(sc))
+    return codes, scales
+
+
+def fp8_values(codes: np.ndarray, scales: np.ndarray, page: int = 64) -> np.ndarray:
+    """float64 values of an fp8 cache: code value times its page's scale."""
+    v = nx.e4m3_decode(codes)
+    s = np.repeat(scales.astype(np.float64), page)[: codes.shape[0]]
+    return v * s[:, None]
+
+
+class Cache:
+    """One compressed cache as stored: `bits` (bf16 uint16 or fp8 uint8),
+    `scales` (fp8 only) and the float64 `values` the attention reads."""
+
+    def __init__(self, exact: np.ndarray, dtype: str = "bf16", page: int = 64):
+        self.dtype = dtype
+        if dtype == "bf16":
+            self.bits = store_bf16(exact)
+            self.scales = None
+            self.values = nx.bf16_value(self.bits)
+        elif dtype == "fp8":
+            self.bits, self.scales = store_fp8_pages(exact, page)
+            self.values = fp8_values(self.bits, self.scales, page)
+        else:
+            raise ValueError(dtype)
+
+    def __len__(self):
+        return self.values.shape[0]
+
+
+def compress(x_bits, z, m, dtype="bf16", page=64) -> Cache:
+    """Pool the complete blocks of x with weights softmax(z) and store them."""
+    return Cache(compress_exact(x_bits, pooling_weights(z), m), dtype, page)
+
+
+# ----------------------------------------------------------------------------- indexer and top-k
+
+def indexer_scores(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -> np.ndarray:
+    """I[b] = sum_h w[h] * max(0, qI[h] . KI_c[b]) for every row b of kic_values.
+    qi_bits: bf16 [H_I, d_I]; w: float32 [H_I]; kic_values: float64 [n, d_I]."""
+    qi = nx.bf16_value(qi_bits)
+    dots = kic_values @ qi.T                        # [n, H_I]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float32).astype(np.float64)
+
+
+def topk_blocks(scores: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, n) blocks with the largest score (ties: lower block first),
+    listed in ascending block order and padded with -1 to length k."""
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores))     # by score desc, then index asc
+    sel = np.sort(order[: min(k, n)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[: sel.shape[0]] = sel
+    return out
+
+
+# ----------------------------------------------------------------------------- attention
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """One softmax over all entries, per head.  q [H, d]; K, V [E, d] (float64).
+    Returns (O [H, d], lse [H]) with lse the natural log of the softmax
+    denominator of the scaled logits."""
+    logits = (q @ K.T) * scale                      # [H, E]
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    s = p.sum(axis=1, keepdims=True)
+    P = p / s
+    assert np.all(np.abs(P.sum(axis=1) - 1.0) < 1e-12), "softmax rows must sum to 1"
+    return P @ V, (mx + np.log(s))[:, 0]
+
+
+def _window_rows(t, n_win, k_bits, v_bits):
+    s = window_start(t, n_win)
+    return nx.bf16_value(k_bits[s: t + 1]), nx.bf16_value(v_bits[s: t + 1])
+
+
+def csa_query(t, q_bits, qi_bits, w, k_bits, v_bits, kc: Cache, vc: Cache, kic: Cache,
+              m, n_win, topk, scale=None):
+    """CSA + SWA for the query at position t.
+
+    k_bits/v_bits: raw bf16 tokens of the request (at least 0..t);
+    kc/vc/kic: compressed caches (at least the visible blocks).
+    Returns dict(o, lse, idx, scores) where idx are the selected blocks
+    (ascending, -1 padded) and scores the indexer scores of all visible blocks
+    (float64)."""
+    d = q_bits.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nv = n_visible(t, m, n_win)
+    sc = indexer_scores(qi_bits, w, kic.values[:nv])
+    idx = topk_blocks(sc, topk)
+    sel = idx[idx >= 0]
+    Kw, Vw = _window_rows(t, n_win, k_bits, v_bits)
+    K = np.concatenate([Kw, kc.values[sel]])
+    V = np.concatenate([Vw, vc.values[sel]])
+    o, lse = attend(nx.bf16_value(q_bits), K, V, scale)
+    return {"o": o, "lse": lse, "idx": idx, "scores": sc}
+
+
+def hca_query(t, q_bits, k_bits, v_bits, kc: Cache, vc: Cache, m, n_win, scale=None):
+    """HCA + SWA for the query at position t: window plus every visible block."""
+    d = q_bits.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nv = n_visible(t, m, n_win)
+    Kw, Vw = _window_rows(t, n_win, k_bits, v_bits)
+    K = np.concatenate([Kw, kc.values[:nv]])
+    V = np.concatenate([Vw, vc.values[:nv]])
+    o, lse = attend(nx.bf16_value(q_bits), K, V, scale)
+    return {"o": o, "lse": lse}
+
+
+# ----------------------------------------------------------------------------- layers
+
+def layer_caches(inp: dict, layer: str, m: int, dtype: str = "bf16", page: int = 64) -> dict:
+    """Compressed caches of one layer from its raw tokens (every complete block)."""
+    out = {"kc": compress(inp["k"], inp["zk"], m, dtype, page),
+           "vc": compress(inp["v"], inp["zv"], m, dtype, page)}
+    if layer == "csa":
+        out["kic"] = compress(inp["ki"], inp["zi"], m, "bf16", page)
+    return out
+
+
+def prefill_rows(inp: dict, layer: str, rows, m: int, n_win: int, topk: int = 0,
+                 caches: dict | None = None, dtype: str = "bf16"):
+    """Outputs of a prefill layer at the query positions `rows`."""
+    caches = layer_caches(inp, layer, m, dtype) if caches is None else caches
+    res = []
+    for t in rows:
+        if layer == "csa":
+            res.append(csa_query(t, inp["q"][t], inp["qi"][t], inp["w"][t], inp["k"], inp["v"],
+                                 caches["kc"], caches["vc"], caches["kic"], m, n_win, topk))
+        else:
+            res.append(hca_query(t, inp["q"][t], inp["k"], inp["v"],
+                                 caches["kc"], caches["vc"], m, n_win))
+    return res
