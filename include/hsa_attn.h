@@ -1,0 +1,236 @@
+/*
+ * hsa_attn.h -- hybrid long-context attention over one shared KV head
+ *               (sliding window + compressed sparse + heavily compressed),
+ *               hand-written HIP kernels for AMD MI355X (gfx950).
+ *
+ * The operations follow the hybrid attention described on the group-reading
+ * wiki page "DeepSeek-V4 深度研究剖析":
+ *   §5.2  SWA: the most recent n_win (= 128) raw KV tokens, attended exactly;
+ *   §5.3  CSA: every m (= 4) tokens' KV pooled into one compressed entry; a
+ *         lightning indexer scores the compressed blocks; a per-query top-k
+ *         (512 Flash, 1024 Pro) enters the main attention;
+ *   §5.4  HCA: every m' (= 128) tokens pooled into one entry, all attended;
+ *   §8    KV stored in low precision (bf16 / fp8);
+ *   §11.4 the heterogeneous caches: compressed KV, compressed indexer keys,
+ *         raw SWA KV, and the tail of a block that is not yet complete.
+ * One shared KV head (MQA): zjai.club episode 163 page, "Deep dive" §14.
+ * Window and compressed entries are concatenated and share one softmax:
+ * aifrontier "EP 95 解读 DeepSeek-V4 论文", section on the three components.
+ *
+ * Definitions used by every call (t = absolute 0-based token position):
+ *   window start      s(t)  = max(0, t - n_win + 1); the window is s(t)..t.
+ *   visible blocks    n_vis(t) = min(ceil(s(t)/m), floor((t+1)/m)):
+ *                     complete blocks that start before the window.  This
+ *                     needs m <= n_win.
+ *   compression       entry[b][c] = sum_{j<m} alpha[j][c] * x[b*m+j][c],
+ *                     alpha = softmax over slots j of per-slot, per-channel
+ *                     logits; accumulated in float64 and rounded once to the
+ *                     cache type (bf16 round-to-nearest-even, or fp8 e4m3fn
+ *                     with one fp32 scale = amax/448 per 64-entry page).
+ *   indexer score     I[t][b] = sum_h w[t][h] * max(0, qI[t][h] . KI_c[b]),
+ *                     fp32 accumulation, no scale.
+ *   top-k             the min(k, n_vis) blocks of largest score, ties to the
+ *                     lower block, listed ascending, padded with -1.
+ *   attention         O[t][h] = softmax_e(scale * Q[t][h] . K_e) applied to
+ *                     V_e over the window rows followed by the selected (CSA)
+ *                     or all visible (HCA) compressed entries: one softmax.
+ *
+ * Conventions
+ *   - Every pointer argument that names a tensor is a DEVICE pointer unless
+ *     stated otherwise; descriptor structs themselves are host memory and
+ *     are read during the call only.
+ *   - Layouts are row-major, innermost dimension last, as written.
+ *   - bf16 tensors are passed as raw 16-bit patterns; fp8 is OCP e4m3fn.
+ *   - Supported shapes: d = 128; H a multiple of 16, at most 128; indexer
+ *     H_I = 4 heads of d_I = 64; page_size = 64; 1 <= m <= n_win <= 1024.
+ *     Other shapes return HSA_ERR_UNSUPPORTED.
+ *   - Ownership: the caller owns every buffer, including the workspace.  The
+ *     library never allocates device memory and never synchronises, except in
+ *     hsa_check_device_error().
+ *   - Asynchrony: every compute call only enqueues work on `stream`.
+ *   - Validation: arguments are checked on the host before anything is
+ *     enqueued; a failed check returns a negative status, enqueues nothing,
+ *     and sets a thread-local message (hsa_last_error()).
+ *   - Device-side faults (a page id outside the pool, a position above the
+ *     declared maximum, a cache holding fewer entries than are visible, a
+ *     top-k index out of range) do not stop the call: the offending row reads
+ *     as zeros, a per-device fault word is set, and hsa_check_device_error()
+ *     reports it.
+ *   - Workspaces: size them with the matching *_workspace_bytes() call.  A
+ *     workspace needs no initialisation (every call clears the counters it
+ *     uses) and must not be shared by calls that may run concurrently.
+ *   - Calls that run concurrently on different streams must use different
+ *     workspaces and outputs.
+ */
+#ifndef HSA_ATTN_H
+#define HSA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSA_ABI_VERSION 1
+
+typedef enum {
+  HSA_OK = 0,
+  HSA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, inconsistent shapes */
+  HSA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (see shapes above) */
+  HSA_ERR_WORKSPACE = -3,     /* ws_bytes smaller than *_workspace_bytes() */
+  HSA_ERR_HIP = -4,           /* a HIP runtime call failed */
+  HSA_ERR_DEVICE_FAULT = -5   /* reported by hsa_check_device_error() */
+} hsa_status;
+
+typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1 } hsa_dtype;
+
+/* Device fault bits reported by hsa_check_device_error(). */
+#define HSA_FAULT_PAGE      1   /* page table entry outside [0, n_pages) */
+#define HSA_FAULT_POS       2   /* a query position above max_pos */
+#define HSA_FAULT_ENTRIES   4   /* n_entries[r] smaller than the visible blocks */
+#define HSA_FAULT_INDEX     8   /* a top-k index outside [0, n_vis) */
+
+/* Raw bf16 token rows of several requests.  Token p of request r lives in
+ * row (p mod capacity): pass capacity >= sequence length for plain arrays
+ * (prefill) or capacity = n_win for a ring (decode). */
+typedef struct {
+  void*   data;       /* bf16 [n_req][capacity][dim] */
+  int64_t capacity;   /* rows per request, >= 1 */
+  int32_t n_req;
+  int32_t dim;
+} hsa_tokens;
+
+/* A paged compressed cache (compressed K, compressed V, or compressed
+ * indexer keys; classical cache of §11.4).  Entry e of request r is slot
+ * (e mod page_size) of physical page page_table[r*pages_per_req + e/page_size]. */
+typedef struct {
+  void*          data;          /* [n_pages][page_size][dim], dtype elements */
+  float*         scale;         /* fp8: [n_pages] fp32 page scales; bf16: NULL */
+  const int32_t* page_table;    /* [n_req][pages_per_req] physical page ids */
+  int32_t*       n_entries;     /* [n_req] entries held per request */
+  int32_t        n_req;
+  int32_t        pages_per_req;
+  int32_t        n_pages;       /* pages in the pool */
+  int32_t        page_size;     /* must be 64 */
+  int32_t        dim;
+  int32_t        dtype;         /* hsa_dtype; indexer keys must be bf16 */
+} hsa_paged;
+
+/* The query tokens of a call.  Either a span (req == pos == NULL): n
+ * consecutive positions span_pos0 .. span_pos0+n-1 of request span_req, or a
+ * list (pos non-NULL): query i is request req[i] (request i if req is NULL)
+ * at position pos[i]. */
+typedef struct {
+  int32_t        n;
+  const int32_t* req;           /* [n] or NULL */
+  const int64_t* pos;           /* [n] or NULL */
+  int32_t        span_req;
+  int64_t        span_pos0;
+  int64_t        max_pos;       /* host-known bound: every position <= max_pos */
+} hsa_queries;
+
+/* Pooling weights: alpha[j][c] = softmax over slots j of z[j][c], computed in
+ * float64 (slot-order sum) and rounded once to fp32.  z, alpha: fp32 [m][dim].
+ * (Compression: wiki §5.3-§5.4; softmax-weighted pooling is this library's
+ * reading of "every m tokens' KV becomes one entry".) */
+hsa_status hsa_pooling_weights(const float* z, int32_t m, int32_t dim, float* alpha,
+                               hipStream_t stream);
+
+/* Compress blocks [first_block, first_block + n_blocks) into request `req` of
+ * `out`: block b pools tokens b*m .. b*m+m-1 of request `x_req` of x (which
+ * must still hold them) with alpha [m][dim] and stores entry b (bf16, or fp8
+ * + page scale).  Sets out->n_entries[req] = first_block + n_blocks.  fp8
+ * needs first_block % page_size == 0 (a page's scale is set by the call that
+ * fills it from its first entry).  (Wiki §5.3, §5.4, §8.) */
+hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, int32_t req,
+                           int64_t first_block, int64_t n_blocks, int32_t m, const float* alpha,
+                           hipStream_t stream);
+
+/* Lightning indexer + top-k for each query (wiki §5.3; §8 for the selector).
+ *   qI  bf16 [n][H_I][d_I]     w  fp32 [n][H_I]     kIc bf16 paged cache
+ *   idx int32 [n][k]  out: selected blocks ascending, -1 padded
+ *   score fp32 [n][k] or NULL: the indexer score of each idx entry (0 at pads)
+ * Scores are computed in fp32 from bf16 operands. */
+size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
+                                        int32_t k);
+hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w,
+                            int32_t H_I, int32_t d_I, const hsa_paged* kIc, int32_t m,
+                            int32_t n_win, int32_t k, int32_t* idx, float* score,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* CSA main attention (wiki §5.2 + §5.3): per query, one softmax over the
+ * window rows of win_k/win_v and the compressed entries idx[i][0..min(k,n_vis))
+ * of kc/vc.  Q bf16 [n][H][d]; O bf16 [n][H][d]; lse fp32 [n][H] (natural
+ * log of the softmax denominator of the scaled logits) or NULL. */
+size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win,
+                                    int32_t k);
+hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
+                        const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
+                        const hsa_paged* kc, const hsa_paged* vc, int32_t m,
+                        const int32_t* idx, int32_t k, float scale, void* O, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* HCA attention (wiki §5.2 + §5.4): as hsa_csa_attn with every visible
+ * compressed entry (b < n_vis(t)) instead of a selection. */
+size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win,
+                                    int32_t m);
+hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
+                        const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
+                        const hsa_paged* kc, const hsa_paged* vc, int32_t m, float scale,
+                        void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+typedef enum { HSA_LAYER_CSA = 0, HSA_LAYER_HCA = 1 } hsa_layer_kind;
+
+/* One attention layer's parameters and caches for decoding a batch of B
+ * requests (request b of the batch is request b of every cache). */
+typedef struct {
+  int32_t kind;                 /* hsa_layer_kind */
+  int32_t H, d, n_win, m, topk; /* topk: CSA only */
+  int32_t H_I, d_I;             /* CSA only */
+  float   scale;                /* logit scale, normally 1/sqrt(d) */
+  const float* alpha_k;         /* [m][d]   pooling weights (hsa_pooling_weights) */
+  const float* alpha_v;         /* [m][d] */
+  const float* alpha_i;         /* [m][d_I] CSA only */
+  hsa_tokens ring_k, ring_v;    /* raw window K/V, capacity >= n_win (state cache) */
+  hsa_tokens tail_i;            /* CSA: raw indexer keys of the open block, capacity >= m */
+  hsa_paged  kc, vc;            /* compressed K/V (classical cache) */
+  hsa_paged  kic;               /* CSA: compressed indexer keys (bf16) */
+} hsa_layer;
+
+/* One decode step of one layer for B requests (wiki §11.4 for the caches;
+ * §5.2-§5.4 for the attention).  pos[b] is the position of request b's new
+ * token (the request holds tokens 0..pos[b]-1).  The step
+ *   1. writes the new token's K/V into ring slot pos%capacity (and KI into
+ *      tail slot pos%capacity for CSA);
+ *   2. if (pos+1) % m == 0, compresses block (pos+1)/m - 1 from the ring and
+ *      tail and appends it at entry n_entries[b], which it then increments;
+ *   3. runs the indexer + top-k + CSA attention, or HCA attention, for the
+ *      new token's query.
+ * Q bf16 [B][H][d]; k_new, v_new bf16 [B][d]; qI bf16 [B][H_I][d_I]; kI_new
+ * bf16 [B][d_I]; w fp32 [B][H_I]; O bf16 [B][H][d]; lse fp32 [B][H] or NULL;
+ * idx_out int32 [B][topk] or NULL (CSA).  max_pos bounds every pos[b].
+ * The caller advances pos between steps.  Needs bf16 compressed K/V caches
+ * (an fp8 page's scale is fixed when the page is written whole; use
+ * hsa_kv_compress at page granularity for fp8).  No allocation and no host
+ * synchronisation: the call can be captured in a HIP graph. */
+size_t hsa_decode_step_workspace_bytes(const hsa_layer* L, int32_t B, int64_t max_pos);
+hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, int64_t max_pos,
+                           const void* Q, const void* k_new, const void* v_new,
+                           const void* qI, const void* kI_new, const float* w,
+                           void* O, float* lse, int32_t* idx_out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Helpers. */
+const char* hsa_status_string(hsa_status s);
+const char* hsa_last_error(void);                 /* thread-local detail of the last failure */
+hsa_status  hsa_check_device_error(hipStream_t stream, int32_t* fault_bits);
+                                                  /* synchronises `stream`, reads and clears
+                                                     the current device's fault word */
+int32_t     hsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSA_ATTN_H */

@@ -1,0 +1,361 @@
+"""ctypes binding of libhsa_attn.so: argument marshalling only.
+
+Every entry point here forwards to the C ABI declared in include/hsa_attn.h
+with the same name (minus the `hsa_` prefix).  Tensors are torch tensors on
+the current HIP device; pointers and the current stream are passed through,
+workspaces are allocated with torch (the library itself never allocates).
+No computation happens in Python: if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # load torch's HIP runtime first: the library binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
+
+BF16, FP8 = 0, 1
+LAYER_CSA, LAYER_HCA = 0, 1
+FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index"}
+
+
+class HsaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class _Tokens(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("capacity", C.c_int64), ("n_req", C.c_int32),
+                ("dim", C.c_int32)]
+
+
+class _Paged(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p), ("page_table", C.c_void_p),
+                ("n_entries", C.c_void_p), ("n_req", C.c_int32), ("pages_per_req", C.c_int32),
+                ("n_pages", C.c_int32), ("page_size", C.c_int32), ("dim", C.c_int32),
+                ("dtype", C.c_int32)]
+
+
+class _Queries(C.Structure):
+    _fields_ = [("n", C.c_int32), ("req", C.c_void_p), ("pos", C.c_void_p),
+                ("span_req", C.c_int32), ("span_pos0", C.c_int64), ("max_pos", C.c_int64)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("H", C.c_int32), ("d", C.c_int32), ("n_win", C.c_int32),
+                ("m", C.c_int32), ("topk", C.c_int32), ("H_I", C.c_int32), ("d_I", C.c_int32),
+                ("scale", C.c_float), ("alpha_k", C.c_void_p), ("alpha_v", C.c_void_p),
+                ("alpha_i", C.c_void_p), ("ring_k", _Tokens), ("ring_v", _Tokens),
+                ("tail_i", _Tokens), ("kc", _Paged), ("vc", _Paged), ("kic", _Paged)]
+
+
+_SIGS = {
+    "hsa_abi_version": (C.c_int32, []),
+    "hsa_last_error": (C.c_char_p, []),
+    "hsa_status_string": (C.c_char_p, [C.c_int]),
+    "hsa_check_device_error": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "hsa_pooling_weights": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "hsa_kv_compress": (C.c_int, [C.POINTER(_Tokens), C.c_int32, C.POINTER(_Paged), C.c_int32,
+                                  C.c_int64, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p]),
+    "hsa_indexer_topk_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
+                                                      C.c_int32]),
+    "hsa_indexer_topk": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int32,
+                                   C.c_int32, C.POINTER(_Paged), C.c_int32, C.c_int32, C.c_int32,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "hsa_csa_attn_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
+                                                  C.c_int32]),
+    "hsa_csa_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
+                               C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
+                               C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_void_p,
+                               C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
+                               C.c_size_t, C.c_void_p]),
+    "hsa_hca_attn_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
+                                                  C.c_int32]),
+    "hsa_hca_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
+                               C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
+                               C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_float,
+                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "hsa_decode_step_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), C.c_int32, C.c_int64]),
+    "hsa_decode_step": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_void_p, C.c_int64,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_size_t, C.c_void_p]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_hybrid_kv_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        L = lib()
+        raise HsaError(status, where,
+                       f"{L.hsa_status_string(status).decode()}: {L.hsa_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ----------------------------------------------------------------------------- descriptors
+
+@dataclass
+class Tokens:
+    """Raw bf16 rows [n_req, capacity, dim]; token p of request r is row p % capacity."""
+    data: torch.Tensor
+
+    def c(self) -> _Tokens:
+        n_req, cap, dim = self.data.shape
+        assert self.data.dtype == torch.bfloat16 and self.data.is_contiguous()
+        return _Tokens(self.data.data_ptr(), cap, n_req, dim)
+
+
+@dataclass
+class PagedCache:
+    """Compressed cache: pages [n_pages, 64, dim] (bf16, or uint8 fp8 codes with
+    `scale` [n_pages]), page_table [n_req, pages_per_req], n_entries [n_req]."""
+    data: torch.Tensor
+    page_table: torch.Tensor
+    n_entries: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+
+    @property
+    def dtype(self) -> int:
+        return FP8 if self.data.dtype == torch.uint8 else BF16
+
+    @staticmethod
+    def allocate(n_req: int, max_entries: int, dim: int, fp8: bool = False,
+                 page_order: Optional[torch.Tensor] = None, device="cuda") -> "PagedCache":
+        ppr = max(1, -(-max_entries // 64))
+        n_pages = n_req * ppr
+        dt = torch.uint8 if fp8 else torch.bfloat16
+        data = torch.zeros((n_pages, 64, dim), dtype=dt, device=device)
+        if page_order is None:
+            page_order = torch.arange(n_pages, dtype=torch.int32)
+        table = page_order.to(torch.int32).reshape(n_req, ppr).to(device)
+        scale = torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 else None
+        return PagedCache(data, table.contiguous(),
+                          torch.zeros(n_req, dtype=torch.int32, device=device), scale)
+
+    def c(self) -> _Paged:
+        n_pages, ps, dim = self.data.shape
+        n_req, ppr = self.page_table.shape
+        return _Paged(self.data.data_ptr(), None if self.scale is None else self.scale.data_ptr(),
+                      self.page_table.data_ptr(), self.n_entries.data_ptr(), n_req, ppr, n_pages,
+                      ps, dim, self.dtype)
+
+    def logical(self, r: int, n: Optional[int] = None) -> torch.Tensor:
+        """Entries 0..n-1 of request r in logical order (a gather, for inspection)."""
+        n = int(self.n_entries[r].item()) if n is None else n
+        pages = self.page_table[r, : -(-n // 64)].long()
+        return self.data[pages].reshape(-1, self.data.shape[-1])[:n]
+
+    def logical_scales(self, r: int, n: int) -> torch.Tensor:
+        pages = self.page_table[r, : -(-n // 64)].long()
+        return self.scale[pages]
+
+
+@dataclass
+class Queries:
+    """A span of consecutive positions of one request, or a list of (req, pos)."""
+    n: int
+    max_pos: int
+    span_req: int = 0
+    span_pos0: int = 0
+    pos: Optional[torch.Tensor] = None      # int64 [n]
+    req: Optional[torch.Tensor] = None      # int32 [n]
+
+    @staticmethod
+    def span(n: int, pos0: int = 0, req: int = 0) -> "Queries":
+        return Queries(n=n, max_pos=pos0 + n - 1, span_req=req, span_pos0=pos0)
+
+    @staticmethod
+    def list(pos: torch.Tensor, max_pos: int, req: Optional[torch.Tensor] = None) -> "Queries":
+        return Queries(n=pos.shape[0], max_pos=max_pos, pos=pos, req=req)
+
+    def c(self) -> _Queries:
+        return _Queries(self.n, None if self.req is None else self.req.data_ptr(),
+                        None if self.pos is None else self.pos.data_ptr(), self.span_req,
+                        self.span_pos0, self.max_pos)
+
+
+class Workspaces:
+    """Device workspaces, one per call site, grown on demand and reused across
+    calls (the library clears what it needs at the start of every call)."""
+
+    def __init__(self):
+        self._ws = {}
+
+    def get(self, key, nbytes: int, device) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        t = self._ws.get(key)
+        if t is None or t.numel() < nbytes or t.device != torch.device(device):
+            t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self._ws[key] = t
+        return t
+
+
+_WS = Workspaces()
+
+
+def _ws_args(ws: Optional[torch.Tensor]):
+    return (None, 0) if ws is None else (C.c_void_p(ws.data_ptr()), ws.numel())
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def abi_version() -> int:
+    return lib().hsa_abi_version()
+
+
+def check_device_error() -> int:
+    """Synchronise the current stream; raise if a kernel set a fault bit."""
+    bits = C.c_int32(0)
+    st = lib().hsa_check_device_error(_stream(), C.byref(bits))
+    if st != 0:
+        names = [v for k, v in FAULT_BITS.items() if bits.value & k]
+        _check(st, f"device fault {names}")
+    return bits.value
+
+
+def pooling_weights(z: torch.Tensor) -> torch.Tensor:
+    z = z.contiguous().float()
+    alpha = torch.empty_like(z)
+    _check(lib().hsa_pooling_weights(_ptr(z), z.shape[0], z.shape[1], _ptr(alpha), _stream()),
+           "pooling_weights")
+    return alpha
+
+
+def kv_compress(x: Tokens, out: PagedCache, req: int, first_block: int, n_blocks: int, m: int,
+                alpha: torch.Tensor, x_req: int = 0) -> None:
+    """Pool blocks [first_block, first_block + n_blocks) of request x_req of x into
+    request req of out."""
+    xt, pc = x.c(), out.c()
+    _check(lib().hsa_kv_compress(C.byref(xt), x_req, C.byref(pc), req, first_block, n_blocks, m,
+                                 _ptr(alpha), _stream()), "kv_compress")
+
+
+def indexer_topk(q: Queries, qI: torch.Tensor, w: torch.Tensor, kIc: PagedCache, m: int,
+                 n_win: int, k: int, with_score: bool = False, ws_key="indexer"):
+    qc, kc = q.c(), kIc.c()
+    idx = torch.empty((q.n, k), dtype=torch.int32, device=qI.device)
+    score = torch.empty((q.n, k), dtype=torch.float32, device=qI.device) if with_score else None
+    nb = lib().hsa_indexer_topk_workspace_bytes(C.byref(qc), m, n_win, k)
+    ws, wsb = _ws_args(_WS.get(ws_key, nb, qI.device))
+    _check(lib().hsa_indexer_topk(C.byref(qc), _ptr(qI), _ptr(w), qI.shape[-2], qI.shape[-1],
+                                  C.byref(kc), m, n_win, k, _ptr(idx), _ptr(score), ws, wsb,
+                                  _stream()), "indexer_topk")
+    return idx, score
+
+
+def csa_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: int,
+             kc: PagedCache, vc: PagedCache, m: int, idx: torch.Tensor, k: int,
+             scale: Optional[float] = None, with_lse: bool = False, ws_key="csa"):
+    H, d = Q.shape[-2], Q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    qc, wk, wv, kcc, vcc = q.c(), win_k.c(), win_v.c(), kc.c(), vc.c()
+    O = torch.empty_like(Q)
+    lse = torch.empty((q.n, H), dtype=torch.float32, device=Q.device) if with_lse else None
+    nb = lib().hsa_csa_attn_workspace_bytes(C.byref(qc), H, n_win, k)
+    ws, wsb = _ws_args(_WS.get(ws_key, nb, Q.device))
+    _check(lib().hsa_csa_attn(C.byref(qc), _ptr(Q), H, d, C.byref(wk), C.byref(wv), n_win,
+                              C.byref(kcc), C.byref(vcc), m, _ptr(idx), k, scale, _ptr(O),
+                              _ptr(lse), ws, wsb, _stream()), "csa_attn")
+    return O, lse
+
+
+def hca_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: int,
+             kc: PagedCache, vc: PagedCache, m: int, scale: Optional[float] = None,
+             with_lse: bool = False, ws_key="hca"):
+    H, d = Q.shape[-2], Q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    qc, wk, wv, kcc, vcc = q.c(), win_k.c(), win_v.c(), kc.c(), vc.c()
+    O = torch.empty_like(Q)
+    lse = torch.empty((q.n, H), dtype=torch.float32, device=Q.device) if with_lse else None
+    nb = lib().hsa_hca_attn_workspace_bytes(C.byref(qc), H, n_win, m)
+    ws, wsb = _ws_args(_WS.get(ws_key, nb, Q.device))
+    _check(lib().hsa_hca_attn(C.byref(qc), _ptr(Q), H, d, C.byref(wk), C.byref(wv), n_win,
+                              C.byref(kcc), C.byref(vcc), m, scale, _ptr(O), _ptr(lse), ws, wsb,
+                              _stream()), "hca_attn")
+    return O, lse
+
+
+@dataclass
+class Layer:
+    """One layer's decode state: pooling weights, window rings, caches."""
+    kind: int
+    H: int
+    n_win: int
+    m: int
+    alpha_k: torch.Tensor
+    alpha_v: torch.Tensor
+    ring_k: Tokens
+    ring_v: Tokens
+    kc: PagedCache
+    vc: PagedCache
+    topk: int = 0
+    alpha_i: Optional[torch.Tensor] = None
+    tail_i: Optional[Tokens] = None
+    kic: Optional[PagedCache] = None
+    d: int = 128
+    H_I: int = 4
+    d_I: int = 64
+    scale: Optional[float] = None
+
+    def c(self) -> _Layer:
+        L = _Layer()
+        L.kind, L.H, L.d, L.n_win, L.m, L.topk = self.kind, self.H, self.d, self.n_win, self.m, self.topk
+        L.H_I, L.d_I = self.H_I, self.d_I
+        L.scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+        L.alpha_k, L.alpha_v = self.alpha_k.data_ptr(), self.alpha_v.data_ptr()
+        L.alpha_i = self.alpha_i.data_ptr() if self.alpha_i is not None else None
+        L.ring_k, L.ring_v = self.ring_k.c(), self.ring_v.c()
+        L.kc, L.vc = self.kc.c(), self.vc.c()
+        if self.kind == LAYER_CSA:
+            L.tail_i, L.kic = self.tail_i.c(), self.kic.c()
+        return L
+
+
+def decode_step(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,
+                k_new: torch.Tensor, v_new: torch.Tensor, qI=None, kI_new=None, w=None,
+                with_lse: bool = False, with_idx: bool = False, O: Optional[torch.Tensor] = None,
+                ws_key="decode"):
+    B = pos.shape[0]
+    Lc = layer.c()
+    O = torch.empty_like(Q) if O is None else O
+    lse = torch.empty((B, layer.H), dtype=torch.float32, device=Q.device) if with_lse else None
+    idx = (torch.empty((B, layer.topk), dtype=torch.int32, device=Q.device)
+           if with_idx and layer.kind == LAYER_CSA else None)
+    nb = lib().hsa_decode_step_workspace_bytes(C.byref(Lc), B, max_pos)
+    ws, wsb = _ws_args(_WS.get((ws_key, layer.kind), nb, Q.device))
+    _check(lib().hsa_decode_step(C.byref(Lc), B, _ptr(pos), max_pos, _ptr(Q), _ptr(k_new),
+                                 _ptr(v_new), _ptr(qI), _ptr(kI_new), _ptr(w), _ptr(O),
+                                 _ptr(lse), _ptr(idx), ws, wsb, _stream()), "decode_step")
+    return O, lse, idx

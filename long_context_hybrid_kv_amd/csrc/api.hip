@@ -1,0 +1,341 @@
+// C ABI of libhsa_attn: argument validation, workspace sizing, dispatch to the
+// gfx950 kernels, status strings and the per-device fault word.
+#include <mutex>
+#include <string>
+
+#include "common.h"
+
+namespace hsa {
+
+// Device fault word: kernels OR HSA_FAULT_* bits into it (one copy per device).
+__device__ int g_fault_word;
+
+int* fault_word() {
+  static std::mutex mu;
+  static int* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_fault_word)) != hipSuccess) return nullptr;
+    ptrs[dev] = (int*)p;
+  }
+  return ptrs[dev];
+}
+
+static thread_local std::string g_err;
+
+static hsa_status fail(hsa_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define REQ(cond, msg) \
+  do { if (!(cond)) return fail(HSA_ERR_INVALID_ARG, msg); } while (0)
+#define SUP(cond, msg) \
+  do { if (!(cond)) return fail(HSA_ERR_UNSUPPORTED, msg); } while (0)
+
+static hsa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return HSA_OK;
+  return fail(HSA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+static int64_t nvis_host(int64_t t, int m, int n_win) {
+  int64_t s = t - n_win + 1 < 0 ? 0 : t - n_win + 1;
+  int64_t a = (s + m - 1) / m, b = (t + 1) / m;
+  return a < b ? a : b;
+}
+
+static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, bool allow_fp8) {
+  std::string n(name);
+  REQ(p, n + ": null descriptor");
+  REQ(p->data && p->page_table && p->n_entries, n + ": null data, page_table or n_entries");
+  REQ(p->n_req >= 1 && p->pages_per_req >= 1 && p->n_pages >= 1, n + ": empty cache");
+  SUP(p->page_size == kPage, n + ": page_size must be 64");
+  SUP(p->dim == dim, n + ": unsupported dim");
+  REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3, n + ": unknown dtype");
+  SUP(allow_fp8 || p->dtype == HSA_BF16, n + ": must be bf16");
+  REQ(p->dtype != HSA_FP8_E4M3 || p->scale, n + ": fp8 cache needs page scales");
+  return HSA_OK;
+}
+
+static hsa_status check_tokens(const hsa_tokens* t, const char* name, int dim, int64_t need_cap) {
+  std::string n(name);
+  REQ(t && t->data, n + ": null");
+  REQ(t->n_req >= 1 && t->capacity >= 1, n + ": empty");
+  SUP(t->dim == dim, n + ": unsupported dim");
+  REQ(t->capacity >= need_cap, n + ": capacity smaller than the rows it must hold");
+  return HSA_OK;
+}
+
+static hsa_status check_queries(const hsa_queries* q, int n_req) {
+  REQ(q, "queries: null");
+  REQ(q->n >= 1, "queries: n must be >= 1");
+  REQ(q->max_pos >= 0 && q->max_pos < (int64_t(1) << 40), "queries: bad max_pos");
+  if (!q->pos) {
+    REQ(!q->req, "queries: req given without pos");
+    REQ(q->span_req >= 0 && q->span_req < n_req, "queries: span_req out of range");
+    REQ(q->span_pos0 >= 0 && q->span_pos0 + q->n - 1 <= q->max_pos,
+        "queries: span exceeds max_pos");
+  } else {
+    REQ(q->req || q->n <= n_req, "queries: implicit request ids exceed the caches");
+  }
+  return HSA_OK;
+}
+
+static bool is_span(const hsa_queries* q) { return !q->pos; }
+
+static hsa_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return HSA_OK;
+  if (!ws || have < need)
+    return fail(HSA_ERR_WORKSPACE, "workspace: " + std::to_string(have) + " bytes given, " +
+                                       std::to_string(need) + " needed");
+  return HSA_OK;
+}
+
+static size_t csa_entries(int n_win, int k) { return (size_t)n_win + k; }
+
+static hsa_status check_attn_common(const hsa_queries* q, const void* Q, int H, int d,
+                                    const hsa_tokens* wk, const hsa_tokens* wv, int n_win,
+                                    const hsa_paged* kc, const hsa_paged* vc, int m, void* O) {
+  REQ(kc && vc, "attention: null cache");
+  hsa_status s;
+  if ((s = check_paged(kc, "kc", kD, true)) != HSA_OK) return s;
+  if ((s = check_paged(vc, "vc", kD, true)) != HSA_OK) return s;
+  if ((s = check_queries(q, kc->n_req)) != HSA_OK) return s;
+  REQ(kc->n_req == vc->n_req, "attention: kc and vc differ in n_req");
+  REQ(Q && O, "attention: null Q or O");
+  SUP(d == kD, "attention: d must be 128");
+  SUP(H >= 16 && H <= 128 && H % 16 == 0, "attention: H must be a multiple of 16 in [16, 128]");
+  REQ(n_win >= 1 && m >= 1, "attention: n_win and m must be >= 1");
+  SUP(m <= n_win, "attention: m > n_win leaves tokens uncovered");
+  int64_t need_cap = q->max_pos + 1 < n_win ? q->max_pos + 1 : n_win;
+  if ((s = check_tokens(wk, "win_k", kD, need_cap)) != HSA_OK) return s;
+  if ((s = check_tokens(wv, "win_v", kD, need_cap)) != HSA_OK) return s;
+  REQ(wk->n_req >= kc->n_req && wv->n_req >= kc->n_req, "attention: window holds fewer requests");
+  int64_t nv = nvis_host(q->max_pos, m, n_win);
+  REQ((int64_t)kc->pages_per_req * kPage >= nv && (int64_t)vc->pages_per_req * kPage >= nv,
+      "attention: page table shorter than the visible blocks");
+  return HSA_OK;
+}
+
+}  // namespace hsa
+
+using namespace hsa;
+
+extern "C" {
+
+int32_t hsa_abi_version(void) { return HSA_ABI_VERSION; }
+
+const char* hsa_last_error(void) { return g_err.c_str(); }
+
+const char* hsa_status_string(hsa_status s) {
+  switch (s) {
+    case HSA_OK: return "ok";
+    case HSA_ERR_INVALID_ARG: return "invalid argument";
+    case HSA_ERR_UNSUPPORTED: return "unsupported";
+    case HSA_ERR_WORKSPACE: return "workspace too small";
+    case HSA_ERR_HIP: return "HIP runtime error";
+    case HSA_ERR_DEVICE_FAULT: return "device fault";
+  }
+  return "unknown status";
+}
+
+hsa_status hsa_check_device_error(hipStream_t stream, int32_t* fault_bits) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "hipStreamSynchronize");
+  int* p = fault_word();
+  if (!p) return fail(HSA_ERR_HIP, "fault word unavailable");
+  int v = 0;
+  if ((e = hipMemcpy(&v, p, sizeof(int), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_status(e, "hipMemcpy");
+  if (v) {
+    int zero = 0;
+    if ((e = hipMemcpy(p, &zero, sizeof(int), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_status(e, "hipMemcpy");
+  }
+  if (fault_bits) *fault_bits = v;
+  return v ? fail(HSA_ERR_DEVICE_FAULT, "device fault bits " + std::to_string(v)) : HSA_OK;
+}
+
+hsa_status hsa_pooling_weights(const float* z, int32_t m, int32_t dim, float* alpha,
+                               hipStream_t stream) {
+  REQ(z && alpha, "pooling_weights: null pointer");
+  REQ(m >= 1 && m <= 4096 && dim >= 1 && dim <= 4096, "pooling_weights: bad m or dim");
+  return hip_status(launch_pooling_weights(z, m, dim, alpha, stream), "pooling_weights");
+}
+
+hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, int32_t req,
+                           int64_t first_block, int64_t n_blocks, int32_t m, const float* alpha,
+                           hipStream_t stream) {
+  REQ(out, "kv_compress: null output");
+  SUP(out->dim == kD || out->dim == kDI, "kv_compress: dim must be 128 or 64");
+  hsa_status s;
+  if ((s = check_paged(out, "out", out->dim, true)) != HSA_OK) return s;
+  if ((s = check_tokens(x, "x", out->dim, 1)) != HSA_OK) return s;
+  REQ(alpha, "kv_compress: null alpha");
+  REQ(m >= 1 && m <= 4096, "kv_compress: bad m");
+  REQ(x->capacity >= m, "kv_compress: x holds fewer than m rows");
+  REQ(req >= 0 && req < out->n_req, "kv_compress: req out of range");
+  REQ(x_req >= 0 && x_req < x->n_req, "kv_compress: x_req out of range");
+  REQ(first_block >= 0 && n_blocks >= 0, "kv_compress: negative range");
+  REQ(first_block + n_blocks <= (int64_t)out->pages_per_req * kPage,
+      "kv_compress: range exceeds the request's pages");
+  REQ(out->dtype != HSA_FP8_E4M3 || first_block % kPage == 0,
+      "kv_compress: fp8 ranges must start on a page boundary");
+  return hip_status(launch_compress(*x, x_req, *out, req, first_block, n_blocks, m, alpha, stream),
+                    "kv_compress");
+}
+
+size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
+                                        int32_t k) {
+  if (!q || q->n < 1 || m < 1 || n_win < 1 || k < 1 || q->max_pos < 0) return 0;
+  return indexer_ws_bytes(q->n, nvis_host(q->max_pos, m, n_win), k, is_span(q));
+}
+
+hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
+                            int32_t d_I, const hsa_paged* kIc, int32_t m, int32_t n_win,
+                            int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  hsa_status s;
+  if ((s = check_paged(kIc, "kIc", kDI, false)) != HSA_OK) return s;
+  if ((s = check_queries(q, kIc->n_req)) != HSA_OK) return s;
+  REQ(qI && w && idx, "indexer_topk: null qI, w or idx");
+  SUP(H_I == kHI && d_I == kDI, "indexer_topk: H_I must be 4 and d_I 64");
+  REQ(m >= 1 && n_win >= 1, "indexer_topk: bad m or n_win");
+  SUP(m <= n_win, "indexer_topk: m > n_win leaves tokens uncovered");
+  REQ(k >= 1 && k <= (1 << 20), "indexer_topk: k out of range");
+  int64_t nv = nvis_host(q->max_pos, m, n_win);
+  REQ((int64_t)kIc->pages_per_req * kPage >= nv, "indexer_topk: page table too short");
+  REQ(nv < (int64_t(1) << 31), "indexer_topk: too many blocks");
+  if ((s = check_ws(ws, ws_bytes, hsa_indexer_topk_workspace_bytes(q, m, n_win, k))) != HSA_OK)
+    return s;
+  return hip_status(launch_indexer(*q, qI, w, *kIc, m, n_win, k, idx, score, ws, ws_bytes, stream),
+                    "indexer_topk");
+}
+
+size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t k) {
+  if (!q || q->n < 1 || H < 16 || n_win < 1 || k < 1) return 0;
+  return attn_ws_bytes(q->n, H, (int64_t)csa_entries(n_win, k), is_span(q));
+}
+
+hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
+                        const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
+                        const hsa_paged* kc, const hsa_paged* vc, int32_t m, const int32_t* idx,
+                        int32_t k, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  hsa_status s;
+  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
+  REQ(idx, "csa_attn: null idx");
+  REQ(k >= 1 && k <= (1 << 20), "csa_attn: k out of range");
+  if ((s = check_ws(ws, ws_bytes, hsa_csa_attn_workspace_bytes(q, H, n_win, k))) != HSA_OK)
+    return s;
+  return hip_status(launch_attn(*q, Q, H, *win_k, *win_v, n_win, *kc, *vc, m, idx, k, scale, O,
+                                lse, ws, ws_bytes, stream),
+                    "csa_attn");
+}
+
+size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t m) {
+  if (!q || q->n < 1 || H < 16 || n_win < 1 || m < 1 || q->max_pos < 0) return 0;
+  return attn_ws_bytes(q->n, H, n_win + nvis_host(q->max_pos, m, n_win), is_span(q));
+}
+
+hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
+                        const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
+                        const hsa_paged* kc, const hsa_paged* vc, int32_t m, float scale, void* O,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hsa_status s;
+  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, hsa_hca_attn_workspace_bytes(q, H, n_win, m))) != HSA_OK)
+    return s;
+  return hip_status(launch_attn(*q, Q, H, *win_k, *win_v, n_win, *kc, *vc, m, nullptr, 0, scale,
+                                O, lse, ws, ws_bytes, stream),
+                    "hca_attn");
+}
+
+// decode_step workspace: [indexer][selected ids][attention], 256-byte aligned
+static size_t rnd256(size_t b) { return (b + 255) & ~size_t(255); }
+
+static void decode_parts(const hsa_layer* L, int32_t B, int64_t max_pos, size_t* p_idx,
+                         size_t* p_sel, size_t* p_attn) {
+  hsa_queries q{};
+  q.n = B;
+  q.pos = (const int64_t*)1;   // list mode for sizing only
+  q.max_pos = max_pos;
+  *p_idx = *p_sel = 0;
+  if (L->kind == HSA_LAYER_CSA) {
+    *p_idx = rnd256(hsa_indexer_topk_workspace_bytes(&q, L->m, L->n_win, L->topk));
+    *p_sel = rnd256(sizeof(int32_t) * (size_t)B * L->topk);
+    *p_attn = rnd256(hsa_csa_attn_workspace_bytes(&q, L->H, L->n_win, L->topk));
+  } else {
+    *p_attn = rnd256(hsa_hca_attn_workspace_bytes(&q, L->H, L->n_win, L->m));
+  }
+}
+
+size_t hsa_decode_step_workspace_bytes(const hsa_layer* L, int32_t B, int64_t max_pos) {
+  if (!L || B < 1 || max_pos < 0 || L->m < 1 || L->n_win < 1 || L->H < 16) return 0;
+  if (L->kind == HSA_LAYER_CSA && L->topk < 1) return 0;
+  size_t a, b, c;
+  decode_parts(L, B, max_pos, &a, &b, &c);
+  return a + b + c;
+}
+
+hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, int64_t max_pos,
+                           const void* Q, const void* k_new, const void* v_new, const void* qI,
+                           const void* kI_new, const float* w, void* O, float* lse,
+                           int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQ(L, "decode_step: null layer");
+  REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode_step: unknown layer kind");
+  REQ(B >= 1 && pos && Q && k_new && v_new && O, "decode_step: null argument or B < 1");
+  REQ(L->alpha_k && L->alpha_v, "decode_step: null pooling weights");
+  SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
+      "decode_step: appending to fp8 caches is not supported (page scales are set per page)");
+  REQ(L->kc.n_req >= B && L->vc.n_req >= B && L->ring_k.n_req >= B && L->ring_v.n_req >= B,
+      "decode_step: caches hold fewer than B requests");
+  REQ(L->n_win >= 1 && L->m >= 1 && L->m <= L->n_win, "decode_step: need 1 <= m <= n_win");
+  hsa_queries q{};
+  q.n = B;
+  q.pos = pos;
+  q.max_pos = max_pos;
+  hsa_status s;
+  if ((s = check_attn_common(&q, Q, L->H, L->d, &L->ring_k, &L->ring_v, L->n_win, &L->kc, &L->vc,
+                             L->m, O)) != HSA_OK)
+    return s;
+  REQ(L->ring_k.capacity >= L->n_win && L->ring_v.capacity >= L->n_win,
+      "decode_step: rings must hold n_win tokens");
+  int64_t pages_needed = (max_pos + 1) / L->m;
+  REQ((int64_t)L->kc.pages_per_req * kPage >= pages_needed &&
+          (int64_t)L->vc.pages_per_req * kPage >= pages_needed,
+      "decode_step: page table too short for the appended entries");
+  const bool csa = L->kind == HSA_LAYER_CSA;
+  if (csa) {
+    REQ(qI && kI_new && w && L->alpha_i, "decode_step: CSA needs qI, kI_new, w and alpha_i");
+    if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
+    if ((s = check_tokens(&L->tail_i, "tail_i", kDI, L->m)) != HSA_OK) return s;
+    REQ(L->kic.n_req >= B && L->tail_i.n_req >= B, "decode_step: kic holds fewer than B requests");
+    REQ((int64_t)L->kic.pages_per_req * kPage >= pages_needed, "decode_step: kic table too short");
+    SUP(L->H_I == kHI && L->d_I == kDI, "decode_step: H_I must be 4 and d_I 64");
+    REQ(L->topk >= 1 && L->topk <= (1 << 20), "decode_step: topk out of range");
+  }
+  size_t a_idx, a_sel, a_attn;
+  decode_parts(L, B, max_pos, &a_idx, &a_sel, &a_attn);
+  if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn)) != HSA_OK) return s;
+  char* base = (char*)ws;
+  hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream);
+  if (e != hipSuccess) return hip_status(e, "decode_step update");
+  if (csa) {
+    int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);
+    e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base, a_idx,
+                       stream);
+    if (e != hipSuccess) return hip_status(e, "decode_step indexer");
+    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
+                    L->topk, L->scale, O, lse, base + a_idx + a_sel, a_attn, stream);
+  } else {
+    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
+                    L->scale, O, lse, base, a_attn, stream);
+  }
+  return hip_status(e, "decode_step attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,393 @@
+// Gather + online-softmax attention for CSA and HCA over one shared KV head.
+//
+// Each query token attends, with one softmax, to its window rows (raw bf16
+// tokens s(t)..t) followed by compressed entries: the top-k selection (CSA)
+// or every visible block (HCA).  All query heads share the same rows (MQA), so
+// the heads form the N dimension of MFMA 16x16x32 bf16 tiles:
+//   S^T[e][h]  = K[e][:] . Q[h][:]     A = K rows from LDS, B = Q in registers (bf16)
+//   O^T[c][h] += V^T[c][e] * P^T[e][h] A = V^T from LDS,  B = P in registers (fp16)
+// With heads as columns, a lane owns one head in both products, so the
+// running max, the row sums and the rescaling of O stay in-lane (two lane
+// swaps finish each reduction), and the probabilities feed the second product
+// straight from the registers of the first: the k index of the second
+// product visits entries in the order the first product's result rows sit in
+// a lane, and V^T is read from LDS in that same order.
+//
+// Rows are gathered 64 entries at a time into LDS (K row-major, V transposed).
+// K stays bf16 (fp8 e4m3 codes widen to bf16 exactly; the page scale multiplies
+// the logits).  The second product runs in fp16: bf16 V values (and fp8 codes
+// times their page scale) become fp16 -- exact for bf16 magnitudes in
+// [2^-14, 65504] -- and the probabilities keep 10 fraction bits instead of 7,
+// which keeps the output error well inside what the bf16 output store adds.
+// Long decode rows are split over workgroups and merged through (max, sum,
+// partial O) in the workspace.
+#include "common.h"
+
+namespace hsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+  Queries Q;
+  const u16* q;
+  int H;
+  Tokens wk, wv;
+  int n_win;
+  Paged kc, vc;
+  int m;
+  const int32_t* idx;
+  int k;                 // > 0: CSA selection of width k; 0: HCA (all visible)
+  float scale_log2;      // logit scale times log2(e)
+  u16* O;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+  int n_splits, cps, n_hg, n_q;
+  int xcd;               // 1: keep consecutive queries on one XCD (prefill)
+  int* fault;
+};
+
+struct RowRef {
+  const uint8_t* p;      // row start, or null (reads as zeros)
+  int fp8;
+  float scale;
+};
+
+// Row of entry ge of the query's entry list in cache `c` (or window tokens `tk`).
+__device__ __forceinline__ RowRef locate(const AttnArgs& a, const Paged& c, const Tokens& tk,
+                                         int qi, int r, int64_t s0, int n_w, int E, int64_t nv,
+                                         int ge) {
+  RowRef rr{nullptr, 0, 0.f};
+  if (ge < n_w) {
+    rr.p = (const uint8_t*)tk.row(r, s0 + ge);
+    rr.scale = 1.f;
+  } else if (ge < E) {
+    int j = ge - n_w;
+    int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
+    if (b < 0 || b >= nv) {
+      atomicOr(a.fault, HSA_FAULT_INDEX);
+      return rr;
+    }
+    int page = c.page_of(r, b, a.fault);
+    if (page < 0) return rr;
+    rr.p = c.row(page, b);
+    rr.fp8 = c.dtype == HSA_FP8_E4M3;
+    rr.scale = rr.fp8 ? c.scale[page] : 1.f;
+  }
+  return rr;
+}
+
+// 8 consecutive elements (column group cg) of a V row, as fp16 (scale applied)
+__device__ __forceinline__ uint4 load8_v(const RowRef& rr, int cg) {
+  if (!rr.p) return make_uint4(0, 0, 0, 0);
+  float f[8];
+  if (!rr.fp8) {
+    uint4 u = *(const uint4*)(rr.p + cg * 16);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    uint2 c = *(const uint2*)(rr.p + cg * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(e4m3_to_bf16((c.x >> (8 * i)) & 0xFF) << 16) * rr.scale;
+      f[4 + i] = __uint_as_float(e4m3_to_bf16((c.y >> (8 * i)) & 0xFF) << 16) * rr.scale;
+    }
+  }
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    h[i] = (uint32_t)__builtin_bit_cast(u16, (_Float16)f[2 * i]) |
+           ((uint32_t)__builtin_bit_cast(u16, (_Float16)f[2 * i + 1]) << 16);
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+// 8 consecutive elements (column group cg) of a K row, as bf16
+__device__ __forceinline__ uint4 load8(const RowRef& rr, int cg) {
+  if (!rr.p) return make_uint4(0, 0, 0, 0);
+  if (!rr.fp8) return *(const uint4*)(rr.p + cg * 16);
+  uint2 c = *(const uint2*)(rr.p + cg * 8);
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[i] = e4m3_to_bf16((c.x >> (8 * i)) & 0xFF);
+    b[4 + i] = e4m3_to_bf16((c.y >> (8 * i)) & 0xFF);
+  }
+  return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                    b[6] | (b[7] << 16));
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  unsigned bid = blockIdx.x;
+  if (a.xcd) {
+    // blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous
+    // range of queries so window rows and compressed entries stay in its L2
+    unsigned per = gridDim.x / 8;
+    bid = (bid % 8) * per + bid / 8;
+  }
+  const int split = bid % a.n_splits;
+  const int rest = bid / a.n_splits;
+  const int hg = rest % a.n_hg;
+  const int qi = rest / a.n_hg;
+  if (qi >= a.n_q) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  int r;
+  int64_t t;
+  a.Q.get(qi, &r, &t, a.fault);
+  const int64_t s0 = window_start(t, a.n_win);
+  const int n_w = (int)(t - s0 + 1);
+  int64_t nv = n_visible(t, a.m, a.n_win);
+  {
+    int64_t ne = a.kc.n_entries[r];
+    int64_t ne2 = a.vc.n_entries[r];
+    ne = ne < ne2 ? ne : ne2;
+    if (nv > ne) {
+      if (split == 0 && hg == 0 && tid == 0) atomicOr(a.fault, HSA_FAULT_ENTRIES);
+      nv = ne < 0 ? 0 : ne;
+    }
+  }
+  const int n_c = a.k > 0 ? (int)(nv < a.k ? nv : a.k) : (int)nv;
+  const int E = n_w + n_c;
+  const int n_chunks = (E + 63) / 64;
+  const int c_lo = split * a.cps;
+  const int c_hi = c_lo + a.cps < n_chunks ? c_lo + a.cps : n_chunks;
+
+  const int head = hg * 16 * NW + wave * 16 + col;
+  bf16x8 qb[4];
+  {
+    const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)qi * a.H + head) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
+  }
+
+  __shared__ __align__(16) u16 Ks[64][136];
+  __shared__ __align__(16) u16 Vt[128][72];   // fp16 bits
+  __shared__ float ksc[64];
+
+  float m_i = -1e30f, l_i = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int e0 = c * 64;
+    // ---- stage K (row-major) and V (transposed) for entries e0 .. e0+63
+    for (int p = tid; p < 1024; p += NT) {
+      const int e = p >> 4, cg = p & 15;
+      RowRef rk = locate(a, a.kc, a.wk, qi, r, s0, n_w, E, nv, e0 + e);
+      *(uint4*)&Ks[e][cg * 8] = load8(rk, cg);
+      if (cg == 0) ksc[e] = rk.scale;
+    }
+    for (int p = tid; p < 1024; p += NT) {
+      const int e = p & 63, cg = p >> 6;
+      RowRef rv = locate(a, a.vc, a.wv, qi, r, s0, n_w, E, nv, e0 + e);
+      uint4 v = load8_v(rv, cg);
+      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Vt[cg * 8 + 2 * j][e] = (u16)(w4[j] & 0xFFFF);
+        Vt[cg * 8 + 2 * j + 1][e] = (u16)(w4[j] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads)
+    f32x4 sacc[4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      sacc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
+        sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], sacc[et], 0, 0, 0);
+      }
+    }
+    // ---- online softmax (lane = head `col`; rows 4g+i of each entry tile)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = et * 16 + 4 * g + i;
+        float v = (e0 + e < E) ? sacc[et][i] * a.scale_log2 * ksc[e] : -INFINITY;
+        sacc[et][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_i, mx);
+    const float alpha = exp2f(m_i - m_new);
+    // probabilities are rounded to fp16 once (the PV operand) and the row sum
+    // adds the rounded values, so the normalisation matches the weights used
+    float rs = 0.f;
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = (float)(_Float16)exp2f(sacc[et][i] - m_new);
+        sacc[et][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l_i = l_i * alpha + rs;
+    m_i = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+
+    // ---- O^T += V^T P^T, two k-steps of 32 entries
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (_Float16)sacc[2 * j][i];
+        pb[4 + i] = (_Float16)sacc[2 * j + 1][i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u16* vr = &Vt[16 * dt + col][0];
+        uint2 lo = *(const uint2*)(vr + 32 * j + 4 * g);
+        uint2 hi = *(const uint2*)(vr + 32 * j + 16 + 4 * g);
+        uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        f16x8 av = __builtin_bit_cast(f16x8, u);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
+  if (a.n_splits == 1) {
+    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+    u16* orow = a.O + ((int64_t)qi * a.H + head) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint32_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)(oacc[dt][i] * inv));
+      *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    }
+    if (g == 0 && a.lse) a.lse[(int64_t)qi * a.H + head] = (m_i + log2f(l_i)) * kLn2;
+  } else {
+    const int64_t slot = ((int64_t)qi * a.n_splits + split) * a.H + head;
+    float* po = a.part_o + slot * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt + 4 * g) = oacc[dt];
+    if (g == 0) {
+      a.part_ml[slot * 2 + 0] = m_i;
+      a.part_ml[slot * 2 + 1] = l_i;
+    }
+  }
+}
+
+// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+__global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
+                                                         const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml,
+                                                         u16* __restrict__ O,
+                                                         float* __restrict__ lse) {
+  const int qh = blockIdx.x;   // query * H + head
+  const int q = qh / H, h = qh % H, d = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s)
+    M = fmaxf(M, part_ml[(((int64_t)q * n_splits + s) * H + h) * 2]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const int64_t slot = ((int64_t)q * n_splits + s) * H + h;
+    const float wgt = exp2f(part_ml[slot * 2] - M);
+    L += wgt * part_ml[slot * 2 + 1];
+    acc += wgt * part_o[slot * kD + d];
+  }
+  O[(int64_t)qh * kD + d] = __builtin_bit_cast(u16, (__bf16)(L > 0.f ? acc / L : 0.f));
+  if (d == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------- host side
+
+struct AttnPlan {
+  int nw, n_hg, n_splits, cps;
+};
+
+static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span) {
+  AttnPlan p;
+  p.nw = (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
+  p.n_hg = H / (16 * p.nw);
+  const int64_t chunks = (max_entries + 63) / 64;
+  p.n_splits = 1;
+  if (!span) {
+    int64_t want = (512 + (int64_t)n_q * p.n_hg - 1) / ((int64_t)n_q * p.n_hg);
+    int64_t cap = chunks / 4 > 1 ? chunks / 4 : 1;
+    p.n_splits = (int)(want < cap ? want : cap);
+    if (p.n_splits < 1) p.n_splits = 1;
+  }
+  p.cps = (int)((chunks + p.n_splits - 1) / p.n_splits);
+  if (p.cps < 1) p.cps = 1;
+  return p;
+}
+
+size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span) {
+  AttnPlan p = plan(n_q, H, max_entries, span);
+  if (p.n_splits == 1) return 0;
+  const size_t slots = (size_t)n_q * p.n_splits * H;
+  return slots * kD * sizeof(float) + ((slots * 2 * sizeof(float) + 255) & ~size_t(255)) + 256;
+}
+
+hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
+                       const hsa_tokens& wv, int n_win, const hsa_paged& kc,
+                       const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
+                       void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  (void)ws_bytes;
+  const bool span = q.req == nullptr && q.pos == nullptr;
+  int64_t s_max = q.max_pos - n_win + 1 < 0 ? 0 : q.max_pos - n_win + 1;
+  int64_t nv_max = (s_max + m - 1) / m;
+  int64_t b2 = (q.max_pos + 1) / m;
+  nv_max = nv_max < b2 ? nv_max : b2;
+  int64_t max_entries = n_win + (k > 0 ? (nv_max < k ? nv_max : k) : nv_max);
+  AttnPlan p = plan(q.n, H, max_entries, span);
+  AttnArgs a;
+  a.Q = to_dev(q);
+  a.q = (const u16*)Q;
+  a.H = H;
+  a.wk = to_dev(wk);
+  a.wv = to_dev(wv);
+  a.n_win = n_win;
+  a.kc = to_dev(kc);
+  a.vc = to_dev(vc);
+  a.m = m;
+  a.idx = idx;
+  a.k = k;
+  a.scale_log2 = scale * kLog2e;
+  a.O = (u16*)O;
+  a.lse = lse;
+  a.part_o = (float*)ws;
+  const size_t slots = (size_t)q.n * p.n_splits * H;
+  a.part_ml = (float*)((char*)ws + ((slots * kD * sizeof(float) + 255) & ~size_t(255)));
+  a.n_splits = p.n_splits;
+  a.cps = p.cps;
+  a.n_hg = p.n_hg;
+  a.n_q = q.n;
+  a.fault = fault_word();
+  int64_t n_blocks = (int64_t)q.n * p.n_hg * p.n_splits;
+  a.xcd = span ? 1 : 0;
+  if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
+  if (p.nw == 4)
+    attn_kernel<4><<<(unsigned)n_blocks, 256, 0, s>>>(a);
+  else if (p.nw == 2)
+    attn_kernel<2><<<(unsigned)n_blocks, 128, 0, s>>>(a);
+  else
+    attn_kernel<1><<<(unsigned)n_blocks, 64, 0, s>>>(a);
+  if (p.n_splits > 1)
+    attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
+                                                            (u16*)O, lse);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

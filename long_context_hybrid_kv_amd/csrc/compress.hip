@@ -1,0 +1,187 @@
+// Block compression (CSA m = 4, HCA m = 128): softmax-weighted pooling of the m
+// tokens of each block into one cache entry, stored as bf16 or as fp8 e4m3fn with
+// one fp32 scale per 64-entry page.
+//
+// Pooling is accumulated in float64: each product of an fp32 weight and a bf16
+// token is exact there, so the entry is rounded only once, into the cache type.
+// The work is a streaming read of the tokens (HBM-bound); float64 FMA runs at
+// the same rate as fp32 on gfx950, so it costs nothing here.
+#include "common.h"
+
+namespace hsa {
+
+// alpha[j][c] = softmax_j(z[j][c]) in float64 (slot-order sum), rounded to fp32.
+__global__ void pooling_weights_kernel(const float* __restrict__ z, int m, int dim,
+                                       float* __restrict__ alpha) {
+  int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= dim) return;
+  float mx = z[c];
+  for (int j = 1; j < m; ++j) mx = fmaxf(mx, z[(int64_t)j * dim + c]);
+  double s = 0.0;
+  for (int j = 0; j < m; ++j) s += exp((double)z[(int64_t)j * dim + c] - (double)mx);
+  for (int j = 0; j < m; ++j)
+    alpha[(int64_t)j * dim + c] = (float)(exp((double)z[(int64_t)j * dim + c] - (double)mx) / s);
+}
+
+hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, hipStream_t s) {
+  pooling_weights_kernel<<<(dim + 63) / 64, 64, 0, s>>>(z, m, dim, alpha);
+  return hipGetLastError();
+}
+
+// One workgroup per cache page touched by [first, first + n).  Each thread owns
+// the (entry, channel) items idx = tid, tid + 256, ... of the page; consecutive
+// threads read consecutive channels of a token row (coalesced).
+template <bool FP8, int MAXV>
+__global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int req, int64_t first,
+                                                       int64_t n, int m,
+                                                       const float* __restrict__ alpha,
+                                                       Paged out, int* fault) {
+  const int dim = out.dim;
+  const int64_t page_e0 = ((first >> 6) + blockIdx.x) << 6;
+  const int64_t e_lo = page_e0 > first ? page_e0 : first;
+  const int64_t e_hi = (page_e0 + kPage) < (first + n) ? (page_e0 + kPage) : (first + n);
+  const int page = out.page_of(req, page_e0, fault);
+  if (blockIdx.x == 0 && threadIdx.x == 0) out.n_entries[req] = (int32_t)(first + n);
+  if (page < 0) return;
+
+  const int items = kPage * dim;
+  double vals[MAXV];
+  double amax = 0.0;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    int it = threadIdx.x + v * 256;
+    vals[v] = 0.0;
+    if (it >= items) continue;
+    int64_t e = page_e0 + it / dim;
+    int c = it % dim;
+    if (e < e_lo || e >= e_hi) continue;
+    double acc = 0.0;
+    for (int j = 0; j < m; ++j) {
+      const u16* row = x.row(x_req, e * m + j);
+      acc += (double)alpha[(int64_t)j * dim + c] * (double)bf16_to_f32(row[c]);
+    }
+    vals[v] = acc;
+    amax = fmax(amax, fabs(acc));
+  }
+  if (!FP8) {
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      int it = threadIdx.x + v * 256;
+      if (it >= items) continue;
+      int64_t e = page_e0 + it / dim;
+      if (e < e_lo || e >= e_hi) continue;
+      ((u16*)out.row(page, e))[it % dim] = f64_to_bf16(vals[v]);
+    }
+    return;
+  }
+  // fp8: page scale = amax / 448 over the entries written by this call
+  __shared__ double red[4];
+  for (int o = 32; o > 0; o >>= 1) amax = fmax(amax, __shfl_xor(amax, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+  if (threadIdx.x == 0) out.scale[page] = sc;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    int it = threadIdx.x + v * 256;
+    if (it >= items) continue;
+    int64_t e = page_e0 + it / dim;
+    if (e < e_lo || e >= e_hi) continue;
+    out.row(page, e)[it % dim] = f64_to_e4m3(vals[v] / (double)sc);
+  }
+}
+
+// ---------------------------------------------------------------- decode: cache upkeep
+
+// One workgroup per request: write the new token into the window ring (and its
+// indexer key into the open-block tail); when the token completes a block,
+// pool the block from the ring/tail and append it to the paged caches.  The
+// new token's own row is taken from the input, not re-read from the ring.
+__device__ __forceinline__ double pool_last(const Tokens& src, int r, int64_t blk, int m, int c,
+                                            const float* __restrict__ alpha, int dim, u16 newest) {
+  double acc = 0.0;
+  for (int j = 0; j < m - 1; ++j)
+    acc += (double)alpha[(int64_t)j * dim + c] * (double)bf16_to_f32(src.row(r, blk * m + j)[c]);
+  acc += (double)alpha[(int64_t)(m - 1) * dim + c] * (double)bf16_to_f32(newest);
+  return acc;
+}
+
+__global__ __launch_bounds__(128) void decode_update_kernel(
+    Tokens rk, Tokens rv, Tokens ti, const int64_t* __restrict__ pos, int64_t max_pos,
+    const u16* __restrict__ k_new, const u16* __restrict__ v_new, const u16* __restrict__ ki_new,
+    int m, int csa, const float* __restrict__ ak, const float* __restrict__ av,
+    const float* __restrict__ ai, Paged kc, Paged vc, Paged kic, int* fault) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  int64_t p = pos[b];
+  if (p < 0 || p > max_pos) {
+    if (c == 0) atomicOr(fault, HSA_FAULT_POS);
+    return;
+  }
+  const u16 kn = k_new[(int64_t)b * kD + c], vn = v_new[(int64_t)b * kD + c];
+  rk.row(b, p)[c] = kn;
+  rv.row(b, p)[c] = vn;
+  u16 in = 0;
+  if (csa && c < kDI) {
+    in = ki_new[(int64_t)b * kDI + c];
+    ti.row(b, p)[c] = in;
+  }
+  if ((p + 1) % m != 0) return;
+  const int64_t blk = (p + 1) / m - 1;
+  __shared__ int ok;
+  if (c == 0) {
+    int32_t ek = kc.n_entries[b], ev = vc.n_entries[b], ei = csa ? kic.n_entries[b] : (int32_t)blk;
+    ok = (ek == blk && ev == blk && ei == blk);
+    if (!ok) atomicOr(fault, HSA_FAULT_ENTRIES);
+  }
+  __syncthreads();
+  if (!ok) return;
+  int pk = kc.page_of(b, blk, fault), pv = vc.page_of(b, blk, fault);
+  if (pk >= 0) ((u16*)kc.row(pk, blk))[c] = f64_to_bf16(pool_last(rk, b, blk, m, c, ak, kD, kn));
+  if (pv >= 0) ((u16*)vc.row(pv, blk))[c] = f64_to_bf16(pool_last(rv, b, blk, m, c, av, kD, vn));
+  if (csa && c < kDI) {
+    int pi = kic.page_of(b, blk, fault);
+    if (pi >= 0) ((u16*)kic.row(pi, blk))[c] = f64_to_bf16(pool_last(ti, b, blk, m, c, ai, kDI, in));
+  }
+  __syncthreads();
+  if (c == 0) {
+    kc.n_entries[b] = (int32_t)(blk + 1);
+    vc.n_entries[b] = (int32_t)(blk + 1);
+    if (csa) kic.n_entries[b] = (int32_t)(blk + 1);
+  }
+}
+
+hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
+                                const void* k_new, const void* v_new, const void* kI_new,
+                                hipStream_t s) {
+  const int csa = L.kind == HSA_LAYER_CSA;
+  Tokens ti = csa ? to_dev(L.tail_i) : Tokens{nullptr, 1, kDI};
+  Paged kic = csa ? to_dev(L.kic) : Paged{};
+  decode_update_kernel<<<B, 128, 0, s>>>(to_dev(L.ring_k), to_dev(L.ring_v), ti, pos, max_pos,
+                                         (const u16*)k_new, (const u16*)v_new,
+                                         (const u16*)kI_new, L.m, csa, L.alpha_k, L.alpha_v,
+                                         L.alpha_i, to_dev(L.kc), to_dev(L.vc), kic, fault_word());
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,
+                           int64_t first, int64_t n, int m, const float* alpha, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t pages = ((first + n - 1) >> 6) - (first >> 6) + 1;
+  Paged o = to_dev(out);
+  Tokens t = to_dev(x);
+  if (out.dtype == HSA_FP8_E4M3) {
+    if (out.dim == kD)
+      compress_kernel<true, 32><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+    else
+      compress_kernel<true, 16><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+  } else {
+    if (out.dim == kD)
+      compress_kernel<false, 32><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+    else
+      compress_kernel<false, 16><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -1,0 +1,523 @@
+// Lightning indexer and per-query top-k selection (CSA).
+//
+// Score of block b for query t: I = sum_h w[t][h] * max(0, qI[t][h] . KI_c[b]),
+// h < 4, d_I = 64, fp32 accumulation of bf16 products.  The dot products run on
+// MFMA 16x16x32 bf16 tiles: the A operand holds query-heads as rows (4 query
+// tokens x 4 heads in prefill; one query's 4 heads and 12 zero rows in decode),
+// the B operand holds 16 compressed indexer keys, so each lane of the result
+// owns the 4 heads of one (query, block) pair and the head sum stays in-lane.
+// A B operand row is 16 contiguous bytes of a key, read straight from the
+// paged cache (no LDS).
+//
+// Selection is exact and has three stages over the scores (kept in the
+// workspace, fp32):
+//   1. histogram of the top 12 bits of the order-preserving score key, built
+//      in LDS per 2048-block chunk and added to a per-query histogram; the
+//      last chunk to finish (ticket counter) finds the bin that holds the k-th
+//      largest score;
+//   2. every chunk marks its blocks above that bin in a per-query bitmap and
+//      appends the blocks inside it to a candidate list; the last chunk to
+//      finish refines the candidates with 8-bit radix passes over the rest of
+//      the score key and then over the inverted block index (ties -> lower
+//      block), and emits the bitmap in ascending block order.
+// The counters and histograms at the head of the workspace are cleared by a
+// fill kernel at the start of every call (and returned to zero by the
+// workgroup that consumed them, for the next query chunk of a prefill call).
+#include "common.h"
+
+namespace hsa {
+
+constexpr int kCH = 2048;          // blocks per chunk (one workgroup)
+constexpr int kBins = 4096;        // first-level histogram (12 key bits)
+constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
+constexpr int kStateInts = 8;      // ticket1, ticket2, thr_bin, n_above, n_cand, n_vis
+
+struct IdxWs {
+  float* scores;        // [nq][R]
+  uint32_t* hist;       // [nq][kBins]
+  int32_t* state;       // [nq][kStateInts]
+  uint32_t* bitmap;     // [nq][R/32]
+  uint32_t* cand;       // [nq][R]
+  uint32_t* cand2;      // [nq][R]
+  int64_t R;
+};
+
+static IdxWs carve(void* ws, int nq, int64_t R) {
+  IdxWs w;
+  char* p = (char*)ws;
+  auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
+  w.state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
+  w.hist = (uint32_t*)take(sizeof(uint32_t) * kBins * nq);
+  w.scores = (float*)take(sizeof(float) * R * nq);
+  w.bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
+  w.cand = (uint32_t*)take(sizeof(uint32_t) * R * nq);
+  w.cand2 = (uint32_t*)take(sizeof(uint32_t) * R * nq);
+  w.R = R;
+  return w;
+}
+
+static size_t carve_bytes(int nq, int64_t R) {
+  auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
+  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(uint32_t) * kBins * nq) +
+         rnd(sizeof(float) * R * nq) + rnd(sizeof(uint32_t) * (R / 32) * nq) +
+         2 * rnd(sizeof(uint32_t) * R * nq);
+}
+
+static int64_t host_nvis(int64_t t, int m, int n_win) {
+  int64_t s = t - n_win + 1 < 0 ? 0 : t - n_win + 1;
+  int64_t a = (s + m - 1) / m, b = (t + 1) / m;
+  return a < b ? a : b;
+}
+
+size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
+  (void)k;
+  int64_t R = ((max_nvis + kCH - 1) / kCH) * kCH;
+  if (R < kCH) R = kCH;
+  int nq = span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q;
+  return carve_bytes(nq, R);
+}
+
+static size_t zeroed_bytes(int nq) {
+  auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
+  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(uint32_t) * kBins * nq);
+}
+
+// ---------------------------------------------------------------- device helpers
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// exclusive prefix sum over a 256-thread block; returns the block total in *total
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t s = sh[i];
+    if (i < wv) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
+}
+
+__device__ __forceinline__ int64_t clamp_nvis(int64_t nv, const int32_t* n_entries, int r,
+                                              int* fault, bool report) {
+  int64_t ne = n_entries[r];
+  if (nv > ne) {
+    if (report) atomicOr(fault, HSA_FAULT_ENTRIES);
+    nv = ne < 0 ? 0 : ne;
+  }
+  return nv;
+}
+
+// Add the LDS histogram to the query's histogram; the last chunk finds the
+// threshold bin (the bin holding the k-th largest key) and clears the counters.
+__device__ void finish_histogram(uint32_t* lhist, IdxWs ws, int qrow, int n_active,
+                                 int64_t nv, int k) {
+  __syncthreads();
+  uint32_t* gh = ws.hist + (int64_t)qrow * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    uint32_t c = lhist[i];
+    if (c) atomicAdd(gh + i, c);
+  }
+  __threadfence();
+  __syncthreads();
+  __shared__ int is_last;
+  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
+  if (threadIdx.x == 0) is_last = (atomicAdd(st + 0, 1) == n_active - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < kBins; i += 256) {
+    lhist[i] = ld_agent(gh + i);
+    gh[i] = 0;
+  }
+  __syncthreads();
+  if (nv <= k) {
+    if (threadIdx.x == 0) { st[2] = -1; st[3] = 0; }
+  } else {
+    // thread i sums bins [kBins-16(i+1), kBins-16i) (descending order)
+    const int hi = kBins - 1 - 16 * threadIdx.x;
+    uint32_t s = 0;
+    for (int j = 0; j < 16; ++j) s += lhist[hi - j];
+    __shared__ uint32_t sh[4];
+    uint32_t tot;
+    uint32_t pre = block_excl_scan(s, &tot, sh);
+    if (pre < (uint32_t)k && pre + s >= (uint32_t)k) {
+      uint32_t cum = pre;
+      for (int j = 0; j < 16; ++j) {
+        uint32_t c = lhist[hi - j];
+        if (cum + c >= (uint32_t)k) { st[2] = hi - j; st[3] = (int32_t)cum; break; }
+        cum += c;
+      }
+    }
+  }
+  if (threadIdx.x == 0) st[0] = 0;
+}
+
+// ---------------------------------------------------------------- decode: score scan
+
+__global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
+                                                       const float* __restrict__ w, Paged kic,
+                                                       int m, int n_win, int k, IdxWs ws,
+                                                       int* fault) {
+  const int qrow = blockIdx.y, chunk = blockIdx.x;
+  int r;
+  int64_t t;
+  Q.get(qrow, &r, &t, fault);
+  int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
+                          chunk == 0 && threadIdx.x == 0);
+  const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
+  if (chunk >= n_active) return;
+  if (chunk == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
+
+  __shared__ uint32_t lhist[kBins];
+  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  bf16x8 a0 = {}, a1 = {};
+  if (row < kHI) {
+    const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
+    a0 = qa[g];
+    a1 = qa[4 + g];
+  }
+  const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
+              w3 = w[qrow * kHI + 3];
+  float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const int64_t b_begin = (int64_t)chunk * kCH;
+  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
+  constexpr int UN = 4;
+  for (int64_t tile = b_begin + 16 * wv; tile < b_end; tile += 64 * UN) {
+    bf16x8 b0[UN], b1[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      int64_t b = tile + 64 * u + row;
+      b0[u] = bf16x8{};
+      b1[u] = bf16x8{};
+      if (b < b_end) {
+        int page = kic.page_of(r, b, fault);
+        if (page >= 0) {
+          const bf16x8* kr = (const bf16x8*)kic.row(page, b);
+          b0[u] = kr[g];
+          b1[u] = kr[4 + g];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc, 0, 0, 0);
+      int64_t b = tile + 64 * u + row;
+      if (g == 0 && b < b_end) {
+        float s = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
+                  w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+        srow[b] = s;
+        atomicAdd(&lhist[order_key(s) >> 20], 1u);
+      }
+    }
+  }
+  finish_histogram(lhist, ws, qrow, n_active, nv, k);
+}
+
+// ---------------------------------------------------------------- prefill: score GEMM
+
+// 16 consecutive query tokens per workgroup (4 A tiles of 4 queries x 4 heads),
+// blocks split over gridDim.y; every wave walks 16-block B tiles.
+__global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, int nq,
+                                                       const u16* __restrict__ qI,
+                                                       const float* __restrict__ w, Paged kic,
+                                                       int m, int n_win, IdxWs ws, int* fault) {
+  const int qt = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  const int r = Q.span_req;
+  const int64_t ne = kic.n_entries[r];
+  bf16x8 a[4][2];
+  float wq[4][4];
+  int64_t nvq[4];
+  int64_t nv_max = 0;
+#pragma unroll
+  for (int at = 0; at < 4; ++at) {
+    int ql = 16 * qt + 4 * at + (row >> 2);      // local row of the A operand's query
+    a[at][0] = bf16x8{};
+    a[at][1] = bf16x8{};
+    if (ql < nq) {
+      const bf16x8* qa =
+          (const bf16x8*)(qI + ((int64_t)(q_base + ql) * kHI + (row & 3)) * kDI);
+      a[at][0] = qa[g];
+      a[at][1] = qa[4 + g];
+    }
+    int qg = 16 * qt + 4 * at + g;               // local query of this lane's result rows
+    nvq[at] = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wq[at][i] = 0.f;
+    if (qg < nq) {
+      int64_t t = Q.span_pos0 + q_base + qg;
+      int64_t nv = n_visible(t, m, n_win);
+      nvq[at] = nv < ne ? nv : ne;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[at][i] = w[(int64_t)(q_base + qg) * kHI + i];
+    }
+  }
+  {
+    int ql = 16 * qt + 15 < nq ? 16 * qt + 15 : nq - 1;
+    int64_t nv = n_visible(Q.span_pos0 + q_base + ql, m, n_win);
+    if (nv > ne) {
+      if (threadIdx.x == 0 && blockIdx.y == 0) atomicOr(fault, HSA_FAULT_ENTRIES);
+      nv = ne;
+    }
+    nv_max = nv;
+  }
+  const int64_t n_tiles = (nv_max + 15) / 16;
+  const int64_t per = (n_tiles + gridDim.y - 1) / gridDim.y;
+  const int64_t t_lo = per * blockIdx.y;
+  const int64_t t_hi = t_lo + per < n_tiles ? t_lo + per : n_tiles;
+  for (int64_t tile = t_lo + wv; tile < t_hi; tile += 4) {
+    int64_t b = 16 * tile + row;
+    bf16x8 b0 = {}, b1 = {};
+    if (b < nv_max) {
+      int page = kic.page_of(r, b, fault);
+      if (page >= 0) {
+        const bf16x8* kr = (const bf16x8*)kic.row(page, b);
+        b0 = kr[g];
+        b1 = kr[4 + g];
+      }
+    }
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], b1, acc, 0, 0, 0);
+      if (b < nvq[at]) {
+        float s = wq[at][0] * fmaxf(acc[0], 0.f) + wq[at][1] * fmaxf(acc[1], 0.f) +
+                  wq[at][2] * fmaxf(acc[2], 0.f) + wq[at][3] * fmaxf(acc[3], 0.f);
+        ws.scores[(int64_t)(16 * qt + 4 * at + g) * ws.R + b] = s;
+      }
+    }
+  }
+}
+
+// prefill: first-level histogram over the stored scores
+__global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, const Paged kic,
+                                                       int m, int n_win, int k, IdxWs ws,
+                                                       int* fault) {
+  const int qrow = blockIdx.y, chunk = blockIdx.x;
+  const int r = Q.span_req;
+  int64_t t = Q.span_pos0 + q_base + qrow;
+  int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault, false);
+  const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
+  if (chunk >= n_active) return;
+  if (chunk == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
+  __shared__ uint32_t lhist[kBins];
+  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
+  __syncthreads();
+  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const int64_t b_begin = (int64_t)chunk * kCH;
+  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
+  for (int64_t b = b_begin + threadIdx.x; b < b_end; b += 256)
+    atomicAdd(&lhist[order_key(srow[b]) >> 20], 1u);
+  finish_histogram(lhist, ws, qrow, n_active, nv, k);
+}
+
+// ---------------------------------------------------------------- select, refine, emit
+
+__device__ __forceinline__ uint64_t cand_key(const float* srow, uint32_t b) {
+  return ((uint64_t)order_key(srow[b]) << 32) | (uint64_t)(~b);
+}
+
+__global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
+                                                         float* __restrict__ score, int out_row0) {
+  const int qrow = blockIdx.y, chunk = blockIdx.x;
+  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
+  const int64_t nv = st[5];
+  const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
+  if (chunk >= n_active) return;
+  const int thr = st[2];
+  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
+  uint32_t* cand = ws.cand + (int64_t)qrow * ws.R;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t b_begin = (int64_t)chunk * kCH;
+  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
+  for (int64_t base = b_begin; base < b_end; base += 256) {
+    int64_t b = base + threadIdx.x;
+    bool valid = b < b_end;
+    int bin = valid ? (int)(order_key(srow[b]) >> 20) : -2;
+    bool sel = valid && (thr < 0 || bin > thr);
+    bool cnd = valid && thr >= 0 && bin == thr;
+    if (cnd) cand[atomicAdd(st + 4, 1)] = (uint32_t)b;
+    uint64_t mask = __ballot(sel);
+    int64_t wb = base + 64 * wv;                     // first block of this wave's 64
+    if (lane == 0 && wb < b_end) {
+      bm[wb >> 5] = (uint32_t)mask;
+      if (wb + 32 < b_end) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  __shared__ int is_last;
+  if (threadIdx.x == 0) is_last = (atomicAdd(st + 1, 1) == n_active - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  // ---- refine the threshold bin: need = k - (count above the bin)
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t sh[4];
+  __shared__ int s_dstar;
+  __shared__ uint32_t s_above, s_next;
+  if (thr >= 0) {
+    int need = k - st[3];
+    uint32_t nc = (uint32_t)ld_agent(st + 4);
+    uint32_t* src = cand;
+    uint32_t* dst = ws.cand2 + (int64_t)qrow * ws.R;
+    int shift = 44;   // bits 63..52 of the composite key were the histogram bin
+    // at most 7 digit passes cover the remaining 52 key bits (scores, then ids);
+    // keys are unique (they contain the block id), so the candidates left after
+    // the last pass are exactly the ones still needed
+    while (need > 0) {
+      if (nc <= (uint32_t)need || shift < -4) {
+        for (uint32_t i = threadIdx.x; i < nc; i += 256) {
+          uint32_t b = ld_agent(src + i);
+          atomicOr(bm + (b >> 5), 1u << (b & 31));
+        }
+        break;
+      }
+      const uint64_t dmask = shift >= 0 ? 0xFFull : 0xFull;
+      const int sh_amt = shift >= 0 ? shift : 0;
+      h256[threadIdx.x] = 0;
+      if (threadIdx.x == 0) { s_next = 0; s_dstar = -1; }
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < nc; i += 256) {
+        uint32_t b = ld_agent(src + i);
+        atomicAdd(&h256[(cand_key(srow, b) >> sh_amt) & dmask], 1u);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t cum = 0;
+        for (int d = 255; d >= 0; --d) {
+          if (cum + h256[d] >= (uint32_t)need) { s_dstar = d; s_above = cum; break; }
+          cum += h256[d];
+        }
+      }
+      __syncthreads();
+      const int dstar = s_dstar;
+      if (dstar < 0) break;   // counts inconsistent: stop rather than loop
+      for (uint32_t i = threadIdx.x; i < nc; i += 256) {
+        uint32_t b = ld_agent(src + i);
+        int dg = (int)((cand_key(srow, b) >> sh_amt) & dmask);
+        if (dg > dstar) atomicOr(bm + (b >> 5), 1u << (b & 31));
+        else if (dg == dstar) dst[atomicAdd(&s_next, 1u)] = b;
+      }
+      __threadfence();
+      __syncthreads();
+      need -= (int)s_above;
+      nc = s_next;
+      uint32_t* tmp = src; src = dst; dst = tmp;
+      shift -= 8;
+      __syncthreads();
+    }
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- emit ascending block ids from the bitmap
+  const int64_t W = (nv + 31) / 32;
+  const int64_t wpt = (W + 255) / 256;
+  const int64_t w0 = wpt * threadIdx.x;
+  const int64_t w1 = w0 + wpt < W ? w0 + wpt : W;
+  uint32_t cnt = 0;
+  for (int64_t i = w0; i < w1; ++i) cnt += __popc(ld_agent(bm + i));
+  uint32_t total;
+  uint32_t o = block_excl_scan(cnt, &total, sh);
+  int32_t* irow = idx + (int64_t)(out_row0 + qrow) * k;
+  float* srow_out = score ? score + (int64_t)(out_row0 + qrow) * k : nullptr;
+  for (int64_t i = w0; i < w1; ++i) {
+    uint32_t word = ld_agent(bm + i);
+    while (word) {
+      int bit = __ffs(word) - 1;
+      word &= word - 1;
+      uint32_t b = (uint32_t)(i * 32 + bit);
+      if (o < (uint32_t)k) {
+        irow[o] = (int32_t)b;
+        if (srow_out) srow_out[o] = srow[b];
+      }
+      ++o;
+    }
+  }
+  for (int i = (int)total + threadIdx.x; i < k; i += 256) {
+    irow[i] = -1;
+    if (srow_out) srow_out[i] = 0.f;
+  }
+  if (threadIdx.x == 0) { st[1] = 0; st[4] = 0; }
+}
+
+// ---------------------------------------------------------------- host launcher
+
+hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
+                          const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
+                          float* score, void* wsp, size_t ws_bytes, hipStream_t s) {
+  (void)ws_bytes;
+  const bool span = q.req == nullptr && q.pos == nullptr;
+  const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
+  int64_t R = ((nv_max + kCH - 1) / kCH) * kCH;
+  if (R < kCH) R = kCH;
+  const unsigned n_chunks = (unsigned)(R / kCH);
+  Paged kc = to_dev(kic);
+  Queries Qd = to_dev(q);
+  int* fault = fault_word();
+  {
+    // counters and histograms start at zero whatever the workspace held before
+    const int nq_ws = span ? (q.n < kSpanQC ? q.n : kSpanQC) : q.n;
+    const int64_t n16 = (int64_t)(zeroed_bytes(nq_ws) / 16);
+    unsigned blocks = (unsigned)((n16 + 255) / 256);
+    fill_zero_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>((uint4*)wsp, n16);
+  }
+  if (!span) {
+    IdxWs ws = carve(wsp, q.n, R);
+    idx_scan_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(Qd, (const u16*)qI, w, kc, m, n_win, k,
+                                                        ws, fault);
+    idx_select_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(k, ws, idx, score, 0);
+    return hipGetLastError();
+  }
+  const int QC = q.n < kSpanQC ? q.n : kSpanQC;
+  IdxWs ws = carve(wsp, QC, R);
+  for (int q0 = 0; q0 < q.n; q0 += QC) {
+    const int nq = q.n - q0 < QC ? q.n - q0 : QC;
+    // chunk-local maximum of the visible blocks bounds the work of this pass
+    int64_t nv_hi = host_nvis(q.span_pos0 + q0 + nq - 1, m, n_win);
+    unsigned chunks_here = (unsigned)((nv_hi + kCH - 1) / kCH);
+    if (chunks_here < 1) chunks_here = 1;
+    int64_t tiles = (nv_hi + 15) / 16;
+    unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
+    if (bsplit < 1) bsplit = 1;
+    if (bsplit > 64) bsplit = 64;
+    idx_gemm_kernel<<<dim3((nq + 15) / 16, bsplit), 256, 0, s>>>(Qd, q0, nq, (const u16*)qI, w,
+                                                               kc, m, n_win, ws, fault);
+    idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+    idx_select_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(k, ws, idx, score, q0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hsa
