@@ -82,6 +82,9 @@ _SIGS = {
                                C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
                                C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_float,
                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "hsa_kernel_timing": (C.c_int, [C.c_int32, C.c_int32]),
+    "hsa_kernel_timing_read": (C.c_int, [C.c_int32, C.POINTER(C.c_double),
+                                         C.POINTER(C.c_int64)]),
     "hsa_decode_step_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), C.c_int32, C.c_int64]),
     "hsa_decode_step": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_void_p, C.c_int64,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -243,6 +246,20 @@ def check_device_error() -> int:
         names = [v for k, v in FAULT_BITS.items() if bits.value & k]
         _check(st, f"device fault {names}")
     return bits.value
+
+
+K_INDEXER_SCAN, K_INDEXER_GEMM, K_INDEXER_SEL, K_ATTN, K_COMPRESS = range(5)
+
+
+def kernel_timing(kernel_id: int, enable: bool) -> None:
+    _check(lib().hsa_kernel_timing(kernel_id, int(enable)), "kernel_timing")
+
+
+def kernel_timing_read(kernel_id: int):
+    """(total milliseconds, launches) of a timed kernel since the last read."""
+    ms, n = C.c_double(0), C.c_int64(0)
+    _check(lib().hsa_kernel_timing_read(kernel_id, C.byref(ms), C.byref(n)), "kernel_timing_read")
+    return ms.value, n.value
 
 
 def pooling_weights(z: torch.Tensor) -> torch.Tensor:

@@ -2,6 +2,7 @@
 // gfx950 kernels, status strings and the per-device fault word.
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "common.h"
 
@@ -22,6 +23,35 @@ int* fault_word() {
     ptrs[dev] = (int*)p;
   }
   return ptrs[dev];
+}
+
+// ---------------------------------------------------------------- kernel timing
+
+struct TimerState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  size_t used = 0;
+};
+static TimerState g_timers[HSA_K_COUNT];
+static std::mutex g_timer_mu;
+
+KernelTimer::KernelTimer(int id, hipStream_t s) : id_(id), s_(s), slot_(nullptr) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  TimerState& t = g_timers[id];
+  if (!t.on) return;
+  if (t.used == t.ev.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+    t.ev.emplace_back(a, b);
+  }
+  auto* pr = &t.ev[t.used++];
+  slot_ = pr;
+  (void)hipEventRecord(pr->first, s);
+}
+
+KernelTimer::~KernelTimer() {
+  if (slot_) (void)hipEventRecord(((std::pair<hipEvent_t, hipEvent_t>*)slot_)->second, s_);
 }
 
 static thread_local std::string g_err;
@@ -127,6 +157,33 @@ using namespace hsa;
 extern "C" {
 
 int32_t hsa_abi_version(void) { return HSA_ABI_VERSION; }
+
+hsa_status hsa_kernel_timing(int32_t kernel_id, int32_t enable) {
+  REQ(kernel_id >= 0 && kernel_id < HSA_K_COUNT, "kernel_timing: unknown kernel id");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timers[kernel_id].on = enable != 0;
+  return HSA_OK;
+}
+
+hsa_status hsa_kernel_timing_read(int32_t kernel_id, double* total_ms, int64_t* launches) {
+  REQ(kernel_id >= 0 && kernel_id < HSA_K_COUNT, "kernel_timing_read: unknown kernel id");
+  REQ(total_ms && launches, "kernel_timing_read: null output");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  TimerState& t = g_timers[kernel_id];
+  double sum = 0.0;
+  for (size_t i = 0; i < t.used; ++i) {
+    hipError_t e = hipEventSynchronize(t.ev[i].second);
+    if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, t.ev[i].first, t.ev[i].second)) != hipSuccess)
+      return hip_status(e, "hipEventElapsedTime");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)t.used;
+  t.used = 0;
+  return HSA_OK;
+}
 
 const char* hsa_last_error(void) { return g_err.c_str(); }
 

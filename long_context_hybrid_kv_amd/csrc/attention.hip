@@ -378,6 +378,7 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   int64_t n_blocks = (int64_t)q.n * p.n_hg * p.n_splits;
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
+  KernelTimer kt(HSA_K_ATTN, s);
   if (p.nw == 4)
     attn_kernel<4><<<(unsigned)n_blocks, 256, 0, s>>>(a);
   else if (p.nw == 2)

@@ -158,6 +158,15 @@ inline Queries to_dev(const hsa_queries& q) {
 
 int* fault_word();   // device pointer of the current device's fault word
 
+// Records start/stop events around a launch when timing is enabled for `id`.
+struct KernelTimer {
+  KernelTimer(int id, hipStream_t s);
+  ~KernelTimer();
+  int id_;
+  hipStream_t s_;
+  void* slot_;
+};
+
 hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, hipStream_t s);
 hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s);

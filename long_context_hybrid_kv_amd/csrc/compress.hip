@@ -170,6 +170,7 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
   int64_t pages = ((first + n - 1) >> 6) - (first >> 6) + 1;
   Paged o = to_dev(out);
   Tokens t = to_dev(x);
+  KernelTimer kt(HSA_K_COMPRESS, s);
   if (out.dtype == HSA_FP8_E4M3) {
     if (out.dim == kD)
       compress_kernel<true, 32><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
