@@ -379,12 +379,15 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   decode_parts(L, B, max_pos, &a_idx, &a_sel, &a_attn);
   if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn)) != HSA_OK) return s;
   char* base = (char*)ws;
-  hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream);
+  // the update kernel also clears the indexer's counters (one launch fewer)
+  hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new,
+                                      csa ? base : nullptr,
+                                      csa ? indexer_zero_bytes(B, false) : 0, stream);
   if (e != hipSuccess) return hip_status(e, "decode_step update");
   if (csa) {
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base, a_idx,
-                       stream);
+                       stream, /*ws_head_zeroed=*/true);
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, lse, base + a_idx + a_sel, a_attn, stream);

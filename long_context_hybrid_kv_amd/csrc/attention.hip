@@ -48,54 +48,76 @@ struct AttnArgs {
   int* fault;
 };
 
-struct RowRef {
-  const uint8_t* p;      // row start, or null (reads as zeros)
-  int fp8;
-  float scale;
-};
+constexpr int kMaxCps = 32;            // chunks of 64 entries per workgroup
+constexpr int kZeroRow = -2147483647 - 1;
 
-// Row of entry ge of the query's entry list in cache `c` (or window tokens `tk`).
-__device__ __forceinline__ RowRef locate(const AttnArgs& a, const Paged& c, const Tokens& tk,
-                                         int qi, int r, int64_t s0, int n_w, int E, int64_t nv,
-                                         int ge) {
-  RowRef rr{nullptr, 0, 0.f};
+// Row id of entry ge of a query: >= 0 is a row of the paged pool (page*64 + slot);
+// <= -2 encodes window row w as -2 - w; kZeroRow reads as zeros.
+__device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_t s0, int n_w,
+                                        int E, int64_t nv, int ge, int* rk, int* rv) {
   if (ge < n_w) {
-    rr.p = (const uint8_t*)tk.row(r, s0 + ge);
-    rr.scale = 1.f;
-  } else if (ge < E) {
-    int j = ge - n_w;
-    int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
-    if (b < 0 || b >= nv) {
-      atomicOr(a.fault, HSA_FAULT_INDEX);
-      return rr;
-    }
-    int page = c.page_of(r, b, a.fault);
-    if (page < 0) return rr;
-    rr.p = c.row(page, b);
-    rr.fp8 = c.dtype == HSA_FP8_E4M3;
-    rr.scale = rr.fp8 ? c.scale[page] : 1.f;
+    const int64_t p = s0 + ge;
+    *rk = -2 - (int)((int64_t)r * a.wk.capacity + p % a.wk.capacity);
+    *rv = -2 - (int)((int64_t)r * a.wv.capacity + p % a.wv.capacity);
+    return;
   }
-  return rr;
+  *rk = *rv = kZeroRow;
+  if (ge >= E) return;
+  const int j = ge - n_w;
+  const int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
+  if (b < 0 || b >= nv) {
+    atomicOr(a.fault, HSA_FAULT_INDEX);
+    return;
+  }
+  const int pk = a.kc.page_of(r, b, a.fault), pv = a.vc.page_of(r, b, a.fault);
+  if (pk >= 0) *rk = pk * kPage + (int)(b & 63);
+  if (pv >= 0) *rv = pv * kPage + (int)(b & 63);
 }
 
-// 8 consecutive elements (column group cg) of a V row, as fp16 (scale applied)
-__device__ __forceinline__ uint4 load8_v(const RowRef& rr, int cg) {
-  if (!rr.p) return make_uint4(0, 0, 0, 0);
+// Raw 16 bytes (bf16) or 8 bytes (fp8 codes, in .x/.y) of column group cg of a row.
+__device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, int row, int cg) {
+  if (row >= 0) {
+    if (c.dtype == HSA_FP8_E4M3) {
+      uint2 v = *(const uint2*)(c.data + (int64_t)row * c.dim + cg * 8);
+      return make_uint4(v.x, v.y, 0, 0);
+    }
+    return *(const uint4*)(c.data + ((int64_t)row * c.dim + cg * 8) * 2);
+  }
+  if (row == kZeroRow) return make_uint4(0, 0, 0, 0);
+  return *(const uint4*)((const u16*)tk.data + (int64_t)(-2 - row) * kD + cg * 8);
+}
+
+__device__ __forceinline__ float row_scale(const Paged& c, int row) {
+  return (row >= 0 && c.dtype == HSA_FP8_E4M3) ? c.scale[row >> 6] : 1.f;
+}
+
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint4 raw) {
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[i] = e4m3_to_bf16((raw.x >> (8 * i)) & 0xFF);
+    b[4 + i] = e4m3_to_bf16((raw.y >> (8 * i)) & 0xFF);
+  }
+  return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                    b[6] | (b[7] << 16));
+}
+
+// V piece -> 8 fp16 values (fp8 codes times the page scale; bf16 values exact
+// in the fp16 range)
+__device__ __forceinline__ uint4 v_piece_f16(uint4 raw, bool fp8, float scale) {
   float f[8];
-  if (!rr.fp8) {
-    uint4 u = *(const uint4*)(rr.p + cg * 16);
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if (fp8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(e4m3_to_bf16((raw.x >> (8 * i)) & 0xFF) << 16) * scale;
+      f[4 + i] = __uint_as_float(e4m3_to_bf16((raw.y >> (8 * i)) & 0xFF) << 16) * scale;
+    }
+  } else {
+    uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    uint2 c = *(const uint2*)(rr.p + cg * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = __uint_as_float(e4m3_to_bf16((c.x >> (8 * i)) & 0xFF) << 16) * rr.scale;
-      f[4 + i] = __uint_as_float(e4m3_to_bf16((c.y >> (8 * i)) & 0xFF) << 16) * rr.scale;
     }
   }
   uint32_t h[4];
@@ -106,24 +128,10 @@ __device__ __forceinline__ uint4 load8_v(const RowRef& rr, int cg) {
   return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
-// 8 consecutive elements (column group cg) of a K row, as bf16
-__device__ __forceinline__ uint4 load8(const RowRef& rr, int cg) {
-  if (!rr.p) return make_uint4(0, 0, 0, 0);
-  if (!rr.fp8) return *(const uint4*)(rr.p + cg * 16);
-  uint2 c = *(const uint2*)(rr.p + cg * 8);
-  uint32_t b[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    b[i] = e4m3_to_bf16((c.x >> (8 * i)) & 0xFF);
-    b[4 + i] = e4m3_to_bf16((c.y >> (8 * i)) & 0xFF);
-  }
-  return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                    b[6] | (b[7] << 16));
-}
-
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
+  constexpr int PPT = 1024 / NT;          // K (and V) pieces per thread per chunk
   unsigned bid = blockIdx.x;
   if (a.xcd) {
     // blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous
@@ -159,6 +167,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int c_lo = split * a.cps;
   const int c_hi = c_lo + a.cps < n_chunks ? c_lo + a.cps : n_chunks;
 
+  __shared__ __align__(16) u16 Ks[64][136];
+  __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
+  __shared__ float ksc[64];
+  __shared__ int rowk[kMaxCps * 64], rowv[kMaxCps * 64];
+
+  // ---- resolve the row ids of every entry of this split once
+  const int e_base = c_lo * 64;
+  const int n_ent = (c_hi > c_lo) ? (c_hi - c_lo) * 64 : 0;
+  for (int j = tid; j < n_ent; j += NT) resolve(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+
   const int head = hg * 16 * NW + wave * 16 + col;
   bf16x8 qb[4];
   {
@@ -166,37 +184,55 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
   }
+  const bool kfp8 = a.kc.dtype == HSA_FP8_E4M3, vfp8 = a.vc.dtype == HSA_FP8_E4M3;
+  __syncthreads();
 
-  __shared__ __align__(16) u16 Ks[64][136];
-  __shared__ __align__(16) u16 Vt[128][72];   // fp16 bits
-  __shared__ float ksc[64];
+  // ---- register double buffer of one chunk's rows
+  uint4 kraw[PPT], vraw[PPT];
+  int krow[PPT], vrow[PPT];
+  float kscl[PPT], vscl[PPT];
+  auto issue = [&](int c) {
+    const int lo = (c - c_lo) * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      const int ek = p >> 4, cgk = p & 15;
+      krow[i] = rowk[lo + ek];
+      kraw[i] = load_piece(a.kc, a.wk, krow[i], cgk);
+      kscl[i] = row_scale(a.kc, krow[i]);
+      const int ev = p & 63, cgv = p >> 6;
+      vrow[i] = rowv[lo + ev];
+      vraw[i] = load_piece(a.vc, a.wv, vrow[i], cgv);
+      vscl[i] = row_scale(a.vc, vrow[i]);
+    }
+  };
 
   float m_i = -1e30f, l_i = 0.f;
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (c_lo < c_hi) issue(c_lo);
   for (int c = c_lo; c < c_hi; ++c) {
     const int e0 = c * 64;
-    // ---- stage K (row-major) and V (transposed) for entries e0 .. e0+63
-    for (int p = tid; p < 1024; p += NT) {
-      const int e = p >> 4, cg = p & 15;
-      RowRef rk = locate(a, a.kc, a.wk, qi, r, s0, n_w, E, nv, e0 + e);
-      *(uint4*)&Ks[e][cg * 8] = load8(rk, cg);
-      if (cg == 0) ksc[e] = rk.scale;
-    }
-    for (int p = tid; p < 1024; p += NT) {
-      const int e = p & 63, cg = p >> 6;
-      RowRef rv = locate(a, a.vc, a.wv, qi, r, s0, n_w, E, nv, e0 + e);
-      uint4 v = load8_v(rv, cg);
+    // ---- stage K (row-major bf16) and V (transposed fp16) for entries e0 .. e0+63
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      const int ek = p >> 4, cgk = p & 15;
+      *(uint4*)&Ks[ek][cgk * 8] = (kfp8 && krow[i] >= 0) ? fp8x8_to_bf16(kraw[i]) : kraw[i];
+      if (cgk == 0) ksc[ek] = kscl[i];
+      const int ev = p & 63, cgv = p >> 6;
+      uint4 v = v_piece_f16(vraw[i], vfp8 && vrow[i] >= 0, vscl[i]);
       uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        Vt[cg * 8 + 2 * j][e] = (u16)(w4[j] & 0xFFFF);
-        Vt[cg * 8 + 2 * j + 1][e] = (u16)(w4[j] >> 16);
+        Vt[cgv * 8 + 2 * j][ev] = (u16)(w4[j] & 0xFFFF);
+        Vt[cgv * 8 + 2 * j + 1][ev] = (u16)(w4[j] >> 16);
       }
     }
     __syncthreads();
+    if (c + 1 < c_hi) issue(c + 1);   // next chunk's rows load while this one computes
 
     // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads)
     f32x4 sacc[4];
@@ -320,16 +356,19 @@ static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span) {
   AttnPlan p;
   p.nw = (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
   p.n_hg = H / (16 * p.nw);
-  const int64_t chunks = (max_entries + 63) / 64;
-  p.n_splits = 1;
+  const int64_t chunks = (max_entries + 63) / 64 > 0 ? (max_entries + 63) / 64 : 1;
+  // at most kMaxCps chunks per workgroup; decode spreads short rows over
+  // enough workgroups to fill the chip (about 4 chunks each, at least 1)
+  int64_t n = (chunks + kMaxCps - 1) / kMaxCps;
   if (!span) {
-    int64_t want = (512 + (int64_t)n_q * p.n_hg - 1) / ((int64_t)n_q * p.n_hg);
-    int64_t cap = chunks / 4 > 1 ? chunks / 4 : 1;
-    p.n_splits = (int)(want < cap ? want : cap);
-    if (p.n_splits < 1) p.n_splits = 1;
+    int64_t by4 = (chunks + 3) / 4;
+    if (by4 > n) n = by4;
+    const int64_t wgs = (int64_t)n_q * p.n_hg;
+    if (n * wgs < 256) n = (256 + wgs - 1) / wgs;
+    if (n > chunks) n = chunks;
   }
-  p.cps = (int)((chunks + p.n_splits - 1) / p.n_splits);
-  if (p.cps < 1) p.cps = 1;
+  p.cps = (int)((chunks + n - 1) / n);
+  p.n_splits = (int)((chunks + p.cps - 1) / p.cps);
   return p;
 }
 

@@ -172,9 +172,11 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s);
 
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span);
+size_t indexer_zero_bytes(int n_q, bool span);   // head of the workspace cleared per call
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
-                          float* score, void* ws, size_t ws_bytes, hipStream_t s);
+                          float* score, void* ws, size_t ws_bytes, hipStream_t s,
+                          bool ws_head_zeroed = false);
 
 size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span);
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
@@ -184,6 +186,6 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                hipStream_t s);
+                                void* zero_ptr, size_t zero_bytes, hipStream_t s);
 
 }  // namespace hsa

@@ -111,8 +111,15 @@ __global__ __launch_bounds__(128) void decode_update_kernel(
     Tokens rk, Tokens rv, Tokens ti, const int64_t* __restrict__ pos, int64_t max_pos,
     const u16* __restrict__ k_new, const u16* __restrict__ v_new, const u16* __restrict__ ki_new,
     int m, int csa, const float* __restrict__ ak, const float* __restrict__ av,
-    const float* __restrict__ ai, Paged kc, Paged vc, Paged kic, int* fault) {
+    const float* __restrict__ ai, Paged kc, Paged vc, Paged kic, uint4* zero_ptr,
+    int64_t zero_n16, int* fault) {
   const int b = blockIdx.x, c = threadIdx.x;
+  // clear this workgroup's share of the indexer counters used later in the step
+  if (zero_ptr) {
+    const int64_t per = (zero_n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = per * b, hi = lo + per < zero_n16 ? lo + per : zero_n16;
+    for (int64_t i = lo + c; i < hi; i += 128) zero_ptr[i] = make_uint4(0, 0, 0, 0);
+  }
   int64_t p = pos[b];
   if (p < 0 || p > max_pos) {
     if (c == 0) atomicOr(fault, HSA_FAULT_POS);
@@ -153,14 +160,15 @@ __global__ __launch_bounds__(128) void decode_update_kernel(
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                hipStream_t s) {
+                                void* zero_ptr, size_t zero_bytes, hipStream_t s) {
   const int csa = L.kind == HSA_LAYER_CSA;
   Tokens ti = csa ? to_dev(L.tail_i) : Tokens{nullptr, 1, kDI};
   Paged kic = csa ? to_dev(L.kic) : Paged{};
   decode_update_kernel<<<B, 128, 0, s>>>(to_dev(L.ring_k), to_dev(L.ring_v), ti, pos, max_pos,
                                          (const u16*)k_new, (const u16*)v_new,
                                          (const u16*)kI_new, L.m, csa, L.alpha_k, L.alpha_v,
-                                         L.alpha_i, to_dev(L.kc), to_dev(L.vc), kic, fault_word());
+                                         L.alpha_i, to_dev(L.kc), to_dev(L.vc), kic,
+                                         (uint4*)zero_ptr, (int64_t)(zero_bytes / 16), fault_word());
   return hipGetLastError();
 }
 

@@ -9,25 +9,26 @@
 // A B operand row is 16 contiguous bytes of a key, read straight from the
 // paged cache (no LDS).
 //
-// Selection is exact and has three stages over the scores (kept in the
-// workspace, fp32):
-//   1. histogram of the top 12 bits of the order-preserving score key, built
-//      in LDS per 2048-block chunk and added to a per-query histogram; the
-//      last chunk to finish (ticket counter) finds the bin that holds the k-th
-//      largest score;
-//   2. every chunk marks its blocks above that bin in a per-query bitmap and
-//      appends the blocks inside it to a candidate list; the last chunk to
-//      finish refines the candidates with 8-bit radix passes over the rest of
-//      the score key and then over the inverted block index (ties -> lower
-//      block), and emits the bitmap in ascending block order.
-// The counters and histograms at the head of the workspace are cleared by a
-// fill kernel at the start of every call (and returned to zero by the
-// workgroup that consumed them, for the next query chunk of a prefill call).
+// Selection is exact and takes three kernels, with no synchronisation between
+// workgroups inside a kernel (on this multi-XCD chip a device-scope fence per
+// workgroup costs more than the whole score stream):
+//   scan     fp32 scores into the workspace, and a histogram of the top 12 bits
+//            of the order-preserving score key (LDS per chunk, then added to a
+//            per-query histogram);
+//   select   every chunk finds, from the histogram, the bin holding the k-th
+//            largest score, marks its blocks above that bin in a per-query
+//            bitmap and appends the blocks inside it to a candidate list;
+//   finalize one workgroup per query refines the candidates with 8-bit radix
+//            passes over the rest of the score key and then over the inverted
+//            block index (ties -> lower block), and emits the bitmap in
+//            ascending block order.
+// The counters and histograms at the head of the workspace are cleared before
+// every call (and by finalize, for the next query chunk of a prefill call).
 #include "common.h"
 
 namespace hsa {
 
-constexpr int kCH = 2048;          // blocks per chunk (one workgroup)
+constexpr int kCH = 512;           // blocks per chunk (one workgroup)
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
 constexpr int kStateInts = 8;      // ticket1, ticket2, thr_bin, n_above, n_cand, n_vis
@@ -129,49 +130,48 @@ __device__ __forceinline__ int64_t clamp_nvis(int64_t nv, const int32_t* n_entri
   return nv;
 }
 
-// Add the LDS histogram to the query's histogram; the last chunk finds the
-// threshold bin (the bin holding the k-th largest key) and clears the counters.
-__device__ void finish_histogram(uint32_t* lhist, IdxWs ws, int qrow, int n_active,
-                                 int64_t nv, int k) {
+// Add a chunk's LDS histogram to the query's histogram (no fence: the select
+// kernel reads it after the kernel boundary).
+__device__ __forceinline__ void flush_histogram(const uint32_t* lhist, IdxWs ws, int qrow) {
   __syncthreads();
   uint32_t* gh = ws.hist + (int64_t)qrow * kBins;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     uint32_t c = lhist[i];
     if (c) atomicAdd(gh + i, c);
   }
-  __threadfence();
-  __syncthreads();
-  __shared__ int is_last;
-  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
-  if (threadIdx.x == 0) is_last = (atomicAdd(st + 0, 1) == n_active - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < kBins; i += 256) {
-    lhist[i] = ld_agent(gh + i);
-    gh[i] = 0;
-  }
-  __syncthreads();
+}
+
+// The bin that holds the k-th largest key, and how many keys lie above it
+// (thr = -1: every visible block is selected).
+__device__ void find_threshold(const uint32_t* gh, int64_t nv, int k, uint32_t* lhist,
+                               int* thr_out, int* above_out) {
+  __shared__ int s_thr, s_above;
   if (nv <= k) {
-    if (threadIdx.x == 0) { st[2] = -1; st[3] = 0; }
+    if (threadIdx.x == 0) { s_thr = -1; s_above = 0; }
+    __syncthreads();
   } else {
+    for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = gh[i];
+    if (threadIdx.x == 0) { s_thr = kBins - 1; s_above = 0; }
+    __syncthreads();
     // thread i sums bins [kBins-16(i+1), kBins-16i) (descending order)
     const int hi = kBins - 1 - 16 * threadIdx.x;
-    uint32_t s = 0;
-    for (int j = 0; j < 16; ++j) s += lhist[hi - j];
+    uint32_t sm = 0;
+    for (int j = 0; j < 16; ++j) sm += lhist[hi - j];
     __shared__ uint32_t sh[4];
     uint32_t tot;
-    uint32_t pre = block_excl_scan(s, &tot, sh);
-    if (pre < (uint32_t)k && pre + s >= (uint32_t)k) {
+    uint32_t pre = block_excl_scan(sm, &tot, sh);
+    if (pre < (uint32_t)k && pre + sm >= (uint32_t)k) {
       uint32_t cum = pre;
       for (int j = 0; j < 16; ++j) {
         uint32_t c = lhist[hi - j];
-        if (cum + c >= (uint32_t)k) { st[2] = hi - j; st[3] = (int32_t)cum; break; }
+        if (cum + c >= (uint32_t)k) { s_thr = hi - j; s_above = (int)cum; break; }
         cum += c;
       }
     }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) st[0] = 0;
+  *thr_out = s_thr;
+  *above_out = s_above;
 }
 
 // ---------------------------------------------------------------- decode: score scan
@@ -195,6 +195,14 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  const int64_t b_begin = (int64_t)chunk * kCH;
+  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
+  // physical pages of the chunk's 8 logical pages, resolved once
+  __shared__ int pg[kCH / kPage];
+  if (threadIdx.x < kCH / kPage) {
+    int64_t e = b_begin + (int64_t)threadIdx.x * kPage;
+    pg[threadIdx.x] = e < b_end ? kic.page_of(r, e, fault) : -1;
+  }
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
@@ -204,40 +212,38 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
   float* srow = ws.scores + (int64_t)qrow * ws.R;
-  const int64_t b_begin = (int64_t)chunk * kCH;
-  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
-  constexpr int UN = 4;
-  for (int64_t tile = b_begin + 16 * wv; tile < b_end; tile += 64 * UN) {
-    bf16x8 b0[UN], b1[UN];
+  __syncthreads();
+  // each wave streams 128 consecutive blocks (8 tiles of 16): all 16 loads of a
+  // lane are issued before the first MFMA
+  constexpr int NT = kCH / 4 / 16;   // tiles per wave
+  const int64_t w0b = b_begin + (int64_t)wv * (kCH / 4);
+  bf16x8 b0[NT], b1[NT];
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      int64_t b = tile + 64 * u + row;
-      b0[u] = bf16x8{};
-      b1[u] = bf16x8{};
-      if (b < b_end) {
-        int page = kic.page_of(r, b, fault);
-        if (page >= 0) {
-          const bf16x8* kr = (const bf16x8*)kic.row(page, b);
-          b0[u] = kr[g];
-          b1[u] = kr[4 + g];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc, 0, 0, 0);
-      int64_t b = tile + 64 * u + row;
-      if (g == 0 && b < b_end) {
-        float s = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
-                  w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
-        srow[b] = s;
-        atomicAdd(&lhist[order_key(s) >> 20], 1u);
-      }
+  for (int u = 0; u < NT; ++u) {
+    const int64_t b = w0b + 16 * u + row;
+    b0[u] = bf16x8{};
+    b1[u] = bf16x8{};
+    const int page = pg[(int)((w0b - b_begin + 16 * u) >> 6)];
+    if (b < b_end && page >= 0) {
+      const bf16x8* kr = (const bf16x8*)kic.row(page, b);
+      b0[u] = __builtin_nontemporal_load(kr + g);
+      b1[u] = __builtin_nontemporal_load(kr + 4 + g);
     }
   }
-  finish_histogram(lhist, ws, qrow, n_active, nv, k);
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[u], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc, 0, 0, 0);
+    const int64_t b = w0b + 16 * u + row;
+    if (g == 0 && b < b_end) {
+      float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
+                 w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+      srow[b] = sc;
+      atomicAdd(&lhist[order_key(sc) >> 20], 1u);
+    }
+  }
+  flush_histogram(lhist, ws, qrow);
 }
 
 // ---------------------------------------------------------------- prefill: score GEMM
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
   const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
   for (int64_t b = b_begin + threadIdx.x; b < b_end; b += 256)
     atomicAdd(&lhist[order_key(srow[b]) >> 20], 1u);
-  finish_histogram(lhist, ws, qrow, n_active, nv, k);
+  flush_histogram(lhist, ws, qrow);
 }
 
 // ---------------------------------------------------------------- select, refine, emit
@@ -345,14 +351,16 @@ __device__ __forceinline__ uint64_t cand_key(const float* srow, uint32_t b) {
   return ((uint64_t)order_key(srow[b]) << 32) | (uint64_t)(~b);
 }
 
-__global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
-                                                         float* __restrict__ score, int out_row0) {
+__global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws) {
   const int qrow = blockIdx.y, chunk = blockIdx.x;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
   const int64_t nv = st[5];
   const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
   if (chunk >= n_active) return;
-  const int thr = st[2];
+  __shared__ uint32_t lhist[kBins];
+  int thr, above;
+  find_threshold(ws.hist + (int64_t)qrow * kBins, nv, k, lhist, &thr, &above);
+  if (chunk == 0 && threadIdx.x == 0) { st[2] = thr; st[3] = above; }
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
   uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
   uint32_t* cand = ws.cand + (int64_t)qrow * ws.R;
@@ -365,7 +373,15 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
     int bin = valid ? (int)(order_key(srow[b]) >> 20) : -2;
     bool sel = valid && (thr < 0 || bin > thr);
     bool cnd = valid && thr >= 0 && bin == thr;
-    if (cnd) cand[atomicAdd(st + 4, 1)] = (uint32_t)b;
+    // one counter update per wave for the candidates it found
+    const uint64_t cmask = __ballot(cnd);
+    if (cmask) {
+      const int leader = __ffsll((unsigned long long)cmask) - 1;
+      uint32_t cbase = 0;
+      if (lane == leader) cbase = atomicAdd((uint32_t*)(st + 4), (uint32_t)__popcll(cmask));
+      cbase = __shfl(cbase, leader);
+      if (cnd) cand[cbase + __popcll(cmask & ((1ull << lane) - 1))] = (uint32_t)b;
+    }
     uint64_t mask = __ballot(sel);
     int64_t wb = base + 64 * wv;                     // first block of this wave's 64
     if (lane == 0 && wb < b_end) {
@@ -373,23 +389,26 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
       if (wb + 32 < b_end) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
     }
   }
-  __threadfence();
-  __syncthreads();
-  __shared__ int is_last;
-  if (threadIdx.x == 0) is_last = (atomicAdd(st + 1, 1) == n_active - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
 
-  // ---- refine the threshold bin: need = k - (count above the bin)
+// One workgroup per query: refine the threshold bin, emit ascending block ids,
+// then clear the query's counters and histogram.
+__global__ __launch_bounds__(256) void idx_finalize_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
+                                                           float* __restrict__ score, int out_row0) {
+  const int qrow = blockIdx.x;
+  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
+  const int64_t nv = st[5];
+  const int thr = st[2];
+  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
   __shared__ uint32_t h256[256];
   __shared__ uint32_t sh[4];
   __shared__ int s_dstar;
   __shared__ uint32_t s_above, s_next;
   if (thr >= 0) {
     int need = k - st[3];
-    uint32_t nc = (uint32_t)ld_agent(st + 4);
-    uint32_t* src = cand;
+    uint32_t nc = (uint32_t)st[4];
+    uint32_t* src = ws.cand + (int64_t)qrow * ws.R;
     uint32_t* dst = ws.cand2 + (int64_t)qrow * ws.R;
     int shift = 44;   // bits 63..52 of the composite key were the histogram bin
     // at most 7 digit passes cover the remaining 52 key bits (scores, then ids);
@@ -398,7 +417,7 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
     while (need > 0) {
       if (nc <= (uint32_t)need || shift < -4) {
         for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-          uint32_t b = ld_agent(src + i);
+          uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
           atomicOr(bm + (b >> 5), 1u << (b & 31));
         }
         break;
@@ -409,7 +428,7 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
       if (threadIdx.x == 0) { s_next = 0; s_dstar = -1; }
       __syncthreads();
       for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-        uint32_t b = ld_agent(src + i);
+        uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
         atomicAdd(&h256[(cand_key(srow, b) >> sh_amt) & dmask], 1u);
       }
       __syncthreads();
@@ -424,12 +443,11 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
       const int dstar = s_dstar;
       if (dstar < 0) break;   // counts inconsistent: stop rather than loop
       for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-        uint32_t b = ld_agent(src + i);
+        uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
         int dg = (int)((cand_key(srow, b) >> sh_amt) & dmask);
         if (dg > dstar) atomicOr(bm + (b >> 5), 1u << (b & 31));
         else if (dg == dstar) dst[atomicAdd(&s_next, 1u)] = b;
       }
-      __threadfence();
       __syncthreads();
       need -= (int)s_above;
       nc = s_next;
@@ -438,10 +456,10 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
       __syncthreads();
     }
   }
-  __threadfence();
   __syncthreads();
 
-  // ---- emit ascending block ids from the bitmap
+  // ---- emit ascending block ids from the bitmap (atomics above went to L2;
+  //      the block-wide barrier orders them before these loads)
   const int64_t W = (nv + 31) / 32;
   const int64_t wpt = (W + 255) / 256;
   const int64_t w0 = wpt * threadIdx.x;
@@ -469,14 +487,22 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws, int32_
     irow[i] = -1;
     if (srow_out) srow_out[i] = 0.f;
   }
-  if (threadIdx.x == 0) { st[1] = 0; st[4] = 0; }
+  // clear this query's counters and histogram for the next pass
+  uint32_t* gh = ws.hist + (int64_t)qrow * kBins;
+  for (int i = threadIdx.x; i < kBins; i += 256) gh[i] = 0;
+  if (threadIdx.x < kStateInts) st[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------- host launcher
 
+size_t indexer_zero_bytes(int n_q, bool span) {
+  return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q);
+}
+
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
-                          float* score, void* wsp, size_t ws_bytes, hipStream_t s) {
+                          float* score, void* wsp, size_t ws_bytes, hipStream_t s,
+                          bool ws_head_zeroed) {
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
@@ -486,7 +512,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
-  {
+  if (!ws_head_zeroed) {
     // counters and histograms start at zero whatever the workspace held before
     const int nq_ws = span ? (q.n < kSpanQC ? q.n : kSpanQC) : q.n;
     const int64_t n16 = (int64_t)(zeroed_bytes(nq_ws) / 16);
@@ -501,7 +527,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                                                           ws, fault);
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    idx_select_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(k, ws, idx, score, 0);
+    idx_select_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(k, ws);
+    idx_finalize_kernel<<<q.n, 256, 0, s>>>(k, ws, idx, score, 0);
     return hipGetLastError();
   }
   const int QC = q.n < kSpanQC ? q.n : kSpanQC;
@@ -523,7 +550,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
-    idx_select_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(k, ws, idx, score, q0);
+    idx_select_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(k, ws);
+    idx_finalize_kernel<<<nq, 256, 0, s>>>(k, ws, idx, score, q0);
   }
   return hipGetLastError();
 }
