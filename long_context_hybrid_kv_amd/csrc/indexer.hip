@@ -28,8 +28,11 @@
 
 namespace hsa {
 
-constexpr int kCH = 512;           // blocks per chunk (one workgroup)
+constexpr int kCH = 512;           // blocks per scan workgroup
+constexpr int kSelCH = 2048;       // blocks per select workgroup (multiple of kCH)
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
+constexpr int kCoarse = 256;       // groups of 16 bins walked by the threshold search
+constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the workspace)
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
 constexpr int kStateInts = 8;      // ticket1, ticket2, thr_bin, n_above, n_cand, n_vis
 
@@ -38,8 +41,8 @@ struct IdxWs {
   uint32_t* hist;       // [nq][kBins]
   int32_t* state;       // [nq][kStateInts]
   uint32_t* bitmap;     // [nq][R/32]
-  uint32_t* cand;       // [nq][R]
-  uint32_t* cand2;      // [nq][R]
+  uint64_t* cand;       // [nq][R]  (score key << 32 | ~block)
+  uint64_t* cand2;      // [nq][R]
   int64_t R;
 };
 
@@ -51,8 +54,8 @@ static IdxWs carve(void* ws, int nq, int64_t R) {
   w.hist = (uint32_t*)take(sizeof(uint32_t) * kBins * nq);
   w.scores = (float*)take(sizeof(float) * R * nq);
   w.bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
-  w.cand = (uint32_t*)take(sizeof(uint32_t) * R * nq);
-  w.cand2 = (uint32_t*)take(sizeof(uint32_t) * R * nq);
+  w.cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
+  w.cand2 = (uint64_t*)take(sizeof(uint64_t) * R * nq);
   w.R = R;
   return w;
 }
@@ -60,8 +63,8 @@ static IdxWs carve(void* ws, int nq, int64_t R) {
 static size_t carve_bytes(int nq, int64_t R) {
   auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
   return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(uint32_t) * kBins * nq) +
-         rnd(sizeof(float) * R * nq) + rnd(sizeof(uint32_t) * (R / 32) * nq) +
-         2 * rnd(sizeof(uint32_t) * R * nq);
+         rnd(sizeof(float) * R * nq) +
+         rnd(sizeof(uint32_t) * (R / 32) * nq) + 2 * rnd(sizeof(uint64_t) * R * nq);
 }
 
 static int64_t host_nvis(int64_t t, int m, int n_win) {
@@ -72,8 +75,8 @@ static int64_t host_nvis(int64_t t, int m, int n_win) {
 
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
   (void)k;
-  int64_t R = ((max_nvis + kCH - 1) / kCH) * kCH;
-  if (R < kCH) R = kCH;
+  int64_t R = ((max_nvis + kSelCH - 1) / kSelCH) * kSelCH;
+  if (R < kSelCH) R = kSelCH;
   int nq = span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q;
   return carve_bytes(nq, R);
 }
@@ -94,6 +97,12 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// candidate keys rewritten by this workgroup between passes: device-coherent
+// loads (LDS or L2), never a stale vector-L1 line
+__device__ __forceinline__ uint64_t ld_cand(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -142,34 +151,38 @@ __device__ __forceinline__ void flush_histogram(const uint32_t* lhist, IdxWs ws,
 }
 
 // The bin that holds the k-th largest key, and how many keys lie above it
-// (thr = -1: every visible block is selected).
-__device__ void find_threshold(const uint32_t* gh, int64_t nv, int k, uint32_t* lhist,
-                               int* thr_out, int* above_out) {
-  __shared__ int s_thr, s_above;
-  if (nv <= k) {
-    if (threadIdx.x == 0) { s_thr = -1; s_above = 0; }
-    __syncthreads();
-  } else {
-    for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = gh[i];
-    if (threadIdx.x == 0) { s_thr = kBins - 1; s_above = 0; }
-    __syncthreads();
-    // thread i sums bins [kBins-16(i+1), kBins-16i) (descending order)
-    const int hi = kBins - 1 - 16 * threadIdx.x;
+// (thr = -1: every visible block is selected).  The 4096 counts are loaded
+// with all loads in flight, summed into 256 groups of 16, and the crossing is
+// found by a block scan over the groups and a short walk inside one group.
+__device__ void find_threshold(const uint32_t* gh, int64_t nv, int k, int* thr_out,
+                               int* above_out) {
+  __shared__ int s_thr, s_above, s_cb;
+  __shared__ uint32_t s_pre;
+  __shared__ uint32_t sh[4];
+  __shared__ uint32_t grp[kCoarse][17];
+  if (threadIdx.x == 0) { s_thr = -1; s_above = 0; s_cb = -1; }
+  if (nv > k) {
+    // thread i owns group 255 - i: bins 16*(255-i) .. +15 (descending order)
+    const int gi = kCoarse - 1 - threadIdx.x;
+    const uint4* gp = (const uint4*)(gh + gi * 16);
+    const uint4 a = gp[0], b = gp[1], c = gp[2], d = gp[3];
+    const uint32_t v[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w,
+                            c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
     uint32_t sm = 0;
-    for (int j = 0; j < 16; ++j) sm += lhist[hi - j];
-    __shared__ uint32_t sh[4];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) { sm += v[j]; grp[threadIdx.x][j] = v[j]; }
     uint32_t tot;
-    uint32_t pre = block_excl_scan(sm, &tot, sh);
+    const uint32_t pre = block_excl_scan(sm, &tot, sh);
     if (pre < (uint32_t)k && pre + sm >= (uint32_t)k) {
       uint32_t cum = pre;
-      for (int j = 0; j < 16; ++j) {
-        uint32_t c = lhist[hi - j];
-        if (cum + c >= (uint32_t)k) { s_thr = hi - j; s_above = (int)cum; break; }
-        cum += c;
+      for (int j = 15; j >= 0; --j) {
+        const uint32_t f = grp[threadIdx.x][j];
+        if (cum + f >= (uint32_t)k) { s_thr = gi * 16 + j; s_above = (int)cum; break; }
+        cum += f;
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
   *thr_out = s_thr;
   *above_out = s_above;
 }
@@ -340,39 +353,53 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
   const int64_t b_begin = (int64_t)chunk * kCH;
   const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
-  for (int64_t b = b_begin + threadIdx.x; b < b_end; b += 256)
-    atomicAdd(&lhist[order_key(srow[b]) >> 20], 1u);
+  constexpr int kPer = kCH / 256;
+  float sc[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t b = b_begin + 256 * u + threadIdx.x;
+    sc[u] = b < b_end ? srow[b] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (b_begin + 256 * u + threadIdx.x < b_end) atomicAdd(&lhist[order_key(sc[u]) >> 20], 1u);
   flush_histogram(lhist, ws, qrow);
 }
 
 // ---------------------------------------------------------------- select, refine, emit
 
-__device__ __forceinline__ uint64_t cand_key(const float* srow, uint32_t b) {
-  return ((uint64_t)order_key(srow[b]) << 32) | (uint64_t)(~b);
-}
 
 __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws) {
   const int qrow = blockIdx.y, chunk = blockIdx.x;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
   const int64_t nv = st[5];
-  const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
+  const int n_active = nv > 0 ? (int)((nv + kSelCH - 1) / kSelCH) : 1;
   if (chunk >= n_active) return;
-  __shared__ uint32_t lhist[kBins];
   int thr, above;
-  find_threshold(ws.hist + (int64_t)qrow * kBins, nv, k, lhist, &thr, &above);
+  find_threshold(ws.hist + (int64_t)qrow * kBins, nv, k, &thr, &above);
   if (chunk == 0 && threadIdx.x == 0) { st[2] = thr; st[3] = above; }
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
   uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
-  uint32_t* cand = ws.cand + (int64_t)qrow * ws.R;
+  uint64_t* cand = ws.cand + (int64_t)qrow * ws.R;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t b_begin = (int64_t)chunk * kCH;
-  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
-  for (int64_t base = b_begin; base < b_end; base += 256) {
-    int64_t b = base + threadIdx.x;
-    bool valid = b < b_end;
-    int bin = valid ? (int)(order_key(srow[b]) >> 20) : -2;
-    bool sel = valid && (thr < 0 || bin > thr);
-    bool cnd = valid && thr >= 0 && bin == thr;
+  const int64_t b_begin = (int64_t)chunk * kSelCH;
+  const int64_t b_end = nv < b_begin + kSelCH ? nv : b_begin + kSelCH;
+  constexpr int kPer = kSelCH / 256;
+  float sc[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t b = b_begin + 256 * u + threadIdx.x;
+    sc[u] = b < b_end ? srow[b] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t base = b_begin + 256 * u;
+    const int64_t b = base + threadIdx.x;
+    const bool valid = b < b_end;
+    const uint32_t key = valid ? order_key(sc[u]) : 0u;
+    const int bin = valid ? (int)(key >> 20) : -2;
+    const bool sel = valid && (thr < 0 || bin > thr);
+    const bool cnd = valid && thr >= 0 && bin == thr;
     // one counter update per wave for the candidates it found
     const uint64_t cmask = __ballot(cnd);
     if (cmask) {
@@ -380,10 +407,12 @@ __global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws) {
       uint32_t cbase = 0;
       if (lane == leader) cbase = atomicAdd((uint32_t*)(st + 4), (uint32_t)__popcll(cmask));
       cbase = __shfl(cbase, leader);
-      if (cnd) cand[cbase + __popcll(cmask & ((1ull << lane) - 1))] = (uint32_t)b;
+      if (cnd)
+        cand[cbase + __popcll(cmask & ((1ull << lane) - 1))] =
+            ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b);
     }
-    uint64_t mask = __ballot(sel);
-    int64_t wb = base + 64 * wv;                     // first block of this wave's 64
+    const uint64_t mask = __ballot(sel);
+    const int64_t wb = base + 64 * wv;                 // first block of this wave's 64
     if (lane == 0 && wb < b_end) {
       bm[wb >> 5] = (uint32_t)mask;
       if (wb + 32 < b_end) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
@@ -405,11 +434,19 @@ __global__ __launch_bounds__(256) void idx_finalize_kernel(int k, IdxWs ws, int3
   __shared__ uint32_t sh[4];
   __shared__ int s_dstar;
   __shared__ uint32_t s_above, s_next;
+  __shared__ uint64_t lk_a[kCandLds], lk_b[kCandLds];
   if (thr >= 0) {
     int need = k - st[3];
     uint32_t nc = (uint32_t)st[4];
-    uint32_t* src = ws.cand + (int64_t)qrow * ws.R;
-    uint32_t* dst = ws.cand2 + (int64_t)qrow * ws.R;
+    uint64_t* gsrc = ws.cand + (int64_t)qrow * ws.R;
+    uint64_t* src = gsrc;
+    uint64_t* dst = ws.cand2 + (int64_t)qrow * ws.R;
+    if (nc <= (uint32_t)kCandLds) {          // usual case: refine in LDS
+      for (uint32_t i = threadIdx.x; i < nc; i += 256) lk_a[i] = gsrc[i];
+      src = lk_a;
+      dst = lk_b;
+      __syncthreads();
+    }
     int shift = 44;   // bits 63..52 of the composite key were the histogram bin
     // at most 7 digit passes cover the remaining 52 key bits (scores, then ids);
     // keys are unique (they contain the block id), so the candidates left after
@@ -417,7 +454,7 @@ __global__ __launch_bounds__(256) void idx_finalize_kernel(int k, IdxWs ws, int3
     while (need > 0) {
       if (nc <= (uint32_t)need || shift < -4) {
         for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-          uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
+          const uint32_t b = ~(uint32_t)ld_cand(src + i);
           atomicOr(bm + (b >> 5), 1u << (b & 31));
         }
         break;
@@ -427,60 +464,85 @@ __global__ __launch_bounds__(256) void idx_finalize_kernel(int k, IdxWs ws, int3
       h256[threadIdx.x] = 0;
       if (threadIdx.x == 0) { s_next = 0; s_dstar = -1; }
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-        uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
-        atomicAdd(&h256[(cand_key(srow, b) >> sh_amt) & dmask], 1u);
-      }
+      for (uint32_t i = threadIdx.x; i < nc; i += 256)
+        atomicAdd(&h256[(ld_cand(src + i) >> sh_amt) & dmask], 1u);
       __syncthreads();
-      if (threadIdx.x == 0) {
-        uint32_t cum = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + h256[d] >= (uint32_t)need) { s_dstar = d; s_above = cum; break; }
-          cum += h256[d];
+      {
+        // thread i owns digit 255 - i: the crossing digit by one block scan
+        const uint32_t c = h256[255 - threadIdx.x];
+        uint32_t tot;
+        const uint32_t pre = block_excl_scan(c, &tot, sh);
+        if (pre < (uint32_t)need && pre + c >= (uint32_t)need) {
+          s_dstar = 255 - threadIdx.x;
+          s_above = pre;
         }
       }
       __syncthreads();
       const int dstar = s_dstar;
       if (dstar < 0) break;   // counts inconsistent: stop rather than loop
       for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-        uint32_t b = ld_agent(src + i);   // written earlier by this workgroup: bypass L1
-        int dg = (int)((cand_key(srow, b) >> sh_amt) & dmask);
-        if (dg > dstar) atomicOr(bm + (b >> 5), 1u << (b & 31));
-        else if (dg == dstar) dst[atomicAdd(&s_next, 1u)] = b;
+        const uint64_t key = ld_cand(src + i);
+        const int dg = (int)((key >> sh_amt) & dmask);
+        if (dg > dstar) {
+          const uint32_t b = ~(uint32_t)key;
+          atomicOr(bm + (b >> 5), 1u << (b & 31));
+        } else if (dg == dstar) {
+          dst[atomicAdd(&s_next, 1u)] = key;
+        }
       }
+      __threadfence_block();
       __syncthreads();
       need -= (int)s_above;
       nc = s_next;
-      uint32_t* tmp = src; src = dst; dst = tmp;
+      uint64_t* tmp = src; src = dst; dst = tmp;
       shift -= 8;
       __syncthreads();
     }
   }
   __syncthreads();
 
-  // ---- emit ascending block ids from the bitmap (atomics above went to L2;
-  //      the block-wide barrier orders them before these loads)
+  // ---- emit ascending block ids from the bitmap.  The refine atomics are
+  //      complete at L2 after the barrier and this workgroup has not read the
+  //      bitmap before, so plain loads see them.
+  constexpr int kWpt = 32;                        // bitmap words held per thread and round
   const int64_t W = (nv + 31) / 32;
   const int64_t wpt = (W + 255) / 256;
   const int64_t w0 = wpt * threadIdx.x;
-  const int64_t w1 = w0 + wpt < W ? w0 + wpt : W;
+  uint32_t words[kWpt];
   uint32_t cnt = 0;
-  for (int64_t i = w0; i < w1; ++i) cnt += __popc(ld_agent(bm + i));
+  for (int64_t rb = 0; rb < wpt; rb += kWpt) {
+#pragma unroll
+    for (int i = 0; i < kWpt; ++i) {
+      const int64_t wi = w0 + rb + i;
+      words[i] = (rb + i < wpt && wi < W) ? bm[wi] : 0u;
+      cnt += __popc(words[i]);
+    }
+  }
   uint32_t total;
   uint32_t o = block_excl_scan(cnt, &total, sh);
   int32_t* irow = idx + (int64_t)(out_row0 + qrow) * k;
   float* srow_out = score ? score + (int64_t)(out_row0 + qrow) * k : nullptr;
-  for (int64_t i = w0; i < w1; ++i) {
-    uint32_t word = ld_agent(bm + i);
-    while (word) {
-      int bit = __ffs(word) - 1;
-      word &= word - 1;
-      uint32_t b = (uint32_t)(i * 32 + bit);
-      if (o < (uint32_t)k) {
-        irow[o] = (int32_t)b;
-        if (srow_out) srow_out[o] = srow[b];
+  for (int64_t rb = 0; rb < wpt; rb += kWpt) {
+    if (wpt > kWpt) {                             // long rows: load the round again
+#pragma unroll
+      for (int i = 0; i < kWpt; ++i) {
+        const int64_t wi = w0 + rb + i;
+        words[i] = (rb + i < wpt && wi < W) ? bm[wi] : 0u;
       }
-      ++o;
+    }
+#pragma unroll
+    for (int i = 0; i < kWpt; ++i) {
+      uint32_t word = words[i];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        const uint32_t b = (uint32_t)((w0 + rb + i) * 32 + bit);
+        if (o < (uint32_t)k) {
+          irow[o] = (int32_t)b;
+          if (srow_out) srow_out[o] = srow[b];
+        }
+        ++o;
+      }
     }
   }
   for (int i = (int)total + threadIdx.x; i < k; i += 256) {
@@ -506,9 +568,10 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
-  int64_t R = ((nv_max + kCH - 1) / kCH) * kCH;
-  if (R < kCH) R = kCH;
+  int64_t R = ((nv_max + kSelCH - 1) / kSelCH) * kSelCH;
+  if (R < kSelCH) R = kSelCH;
   const unsigned n_chunks = (unsigned)(R / kCH);
+  const unsigned n_sel = (unsigned)(R / kSelCH);
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
@@ -527,7 +590,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                                                           ws, fault);
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    idx_select_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(k, ws);
+    idx_select_kernel<<<dim3(n_sel, q.n), 256, 0, s>>>(k, ws);
     idx_finalize_kernel<<<q.n, 256, 0, s>>>(k, ws, idx, score, 0);
     return hipGetLastError();
   }
@@ -539,6 +602,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     int64_t nv_hi = host_nvis(q.span_pos0 + q0 + nq - 1, m, n_win);
     unsigned chunks_here = (unsigned)((nv_hi + kCH - 1) / kCH);
     if (chunks_here < 1) chunks_here = 1;
+    unsigned sel_here = (unsigned)((nv_hi + kSelCH - 1) / kSelCH);
+    if (sel_here < 1) sel_here = 1;
     int64_t tiles = (nv_hi + 15) / 16;
     unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
     if (bsplit < 1) bsplit = 1;
@@ -550,7 +615,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
-    idx_select_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(k, ws);
+    idx_select_kernel<<<dim3(sel_here, nq), 256, 0, s>>>(k, ws);
     idx_finalize_kernel<<<nq, 256, 0, s>>>(k, ws, idx, score, q0);
   }
   return hipGetLastError();
