@@ -84,7 +84,7 @@ typedef enum {
   HSA_ERR_DEVICE_FAULT = -5   /* reported by hsa_check_device_error() */
 } hsa_status;
 
-typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1 } hsa_dtype;
+typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2 } hsa_dtype;
 
 /* Device fault bits reported by hsa_check_device_error(). */
 #define HSA_FAULT_PAGE      1   /* page table entry outside [0, n_pages) */
@@ -162,15 +162,16 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
 
 /* CSA main attention (wiki §5.2 + §5.3): per query, one softmax over the
  * window rows of win_k/win_v and the compressed entries idx[i][0..min(k,n_vis))
- * of kc/vc.  Q bf16 [n][H][d]; O bf16 [n][H][d]; lse fp32 [n][H] (natural
- * log of the softmax denominator of the scaled logits) or NULL. */
+ * of kc/vc.  Q bf16 [n][H][d]; O [n][H][d] of o_dtype (HSA_BF16, or HSA_FP32 to
+ * keep the fp32 accumulation); lse fp32 [n][H] (natural log of the softmax
+ * denominator of the scaled logits) or NULL. */
 size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win,
                                     int32_t k);
 hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
                         const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
                         const hsa_paged* kc, const hsa_paged* vc, int32_t m,
-                        const int32_t* idx, int32_t k, float scale, void* O, float* lse,
-                        void* ws, size_t ws_bytes, hipStream_t stream);
+                        const int32_t* idx, int32_t k, float scale, void* O, int32_t o_dtype,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* HCA attention (wiki §5.2 + §5.4): as hsa_csa_attn with every visible
  * compressed entry (b < n_vis(t)) instead of a selection. */
@@ -179,7 +180,8 @@ size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_w
 hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
                         const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
                         const hsa_paged* kc, const hsa_paged* vc, int32_t m, float scale,
-                        void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                        void* O, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 typedef enum { HSA_LAYER_CSA = 0, HSA_LAYER_HCA = 1 } hsa_layer_kind;
 
@@ -190,6 +192,7 @@ typedef struct {
   int32_t H, d, n_win, m, topk; /* topk: CSA only */
   int32_t H_I, d_I;             /* CSA only */
   float   scale;                /* logit scale, normally 1/sqrt(d) */
+  int32_t o_dtype;              /* output: HSA_BF16 or HSA_FP32 */
   const float* alpha_k;         /* [m][d]   pooling weights (hsa_pooling_weights) */
   const float* alpha_v;         /* [m][d] */
   const float* alpha_i;         /* [m][d_I] CSA only */
@@ -209,7 +212,7 @@ typedef struct {
  *   3. runs the indexer + top-k + CSA attention, or HCA attention, for the
  *      new token's query.
  * Q bf16 [B][H][d]; k_new, v_new bf16 [B][d]; qI bf16 [B][H_I][d_I]; kI_new
- * bf16 [B][d_I]; w fp32 [B][H_I]; O bf16 [B][H][d]; lse fp32 [B][H] or NULL;
+ * bf16 [B][d_I]; w fp32 [B][H_I]; O [B][H][d] of L->o_dtype; lse fp32 [B][H] or NULL;
  * idx_out int32 [B][topk] or NULL (CSA).  max_pos bounds every pos[b].
  * The caller advances pos between steps.  Needs bf16 compressed K/V caches
  * (an fp8 page's scale is fixed when the page is written whole; use

@@ -20,7 +20,7 @@ import torch  # load torch's HIP runtime first: the library binds to the same on
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 
-BF16, FP8 = 0, 1
+BF16, FP8, FP32 = 0, 1, 2
 LAYER_CSA, LAYER_HCA = 0, 1
 FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index"}
 
@@ -51,7 +51,7 @@ class _Queries(C.Structure):
 class _Layer(C.Structure):
     _fields_ = [("kind", C.c_int32), ("H", C.c_int32), ("d", C.c_int32), ("n_win", C.c_int32),
                 ("m", C.c_int32), ("topk", C.c_int32), ("H_I", C.c_int32), ("d_I", C.c_int32),
-                ("scale", C.c_float), ("alpha_k", C.c_void_p), ("alpha_v", C.c_void_p),
+                ("scale", C.c_float), ("o_dtype", C.c_int32), ("alpha_k", C.c_void_p), ("alpha_v", C.c_void_p),
                 ("alpha_i", C.c_void_p), ("ring_k", _Tokens), ("ring_v", _Tokens),
                 ("tail_i", _Tokens), ("kc", _Paged), ("vc", _Paged), ("kic", _Paged)]
 
@@ -74,14 +74,15 @@ _SIGS = {
     "hsa_csa_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
                                C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
                                C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_void_p,
-                               C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
-                               C.c_size_t, C.c_void_p]),
+                               C.c_int32, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
+                               C.c_void_p, C.c_size_t, C.c_void_p]),
     "hsa_hca_attn_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
                                                   C.c_int32]),
     "hsa_hca_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
                                C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
                                C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_float,
-                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+                               C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
+                               C.c_void_p]),
     "hsa_kernel_timing": (C.c_int, [C.c_int32, C.c_int32]),
     "hsa_kernel_timing_read": (C.c_int, [C.c_int32, C.POINTER(C.c_double),
                                          C.POINTER(C.c_int64)]),
@@ -294,33 +295,34 @@ def indexer_topk(q: Queries, qI: torch.Tensor, w: torch.Tensor, kIc: PagedCache,
 
 def csa_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: int,
              kc: PagedCache, vc: PagedCache, m: int, idx: torch.Tensor, k: int,
-             scale: Optional[float] = None, with_lse: bool = False, ws_key="csa"):
+             scale: Optional[float] = None, with_lse: bool = False, out_fp32: bool = False,
+             ws_key="csa"):
     H, d = Q.shape[-2], Q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     qc, wk, wv, kcc, vcc = q.c(), win_k.c(), win_v.c(), kc.c(), vc.c()
-    O = torch.empty_like(Q)
+    O = torch.empty(Q.shape, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=Q.device)
     lse = torch.empty((q.n, H), dtype=torch.float32, device=Q.device) if with_lse else None
     nb = lib().hsa_csa_attn_workspace_bytes(C.byref(qc), H, n_win, k)
     ws, wsb = _ws_args(_WS.get(ws_key, nb, Q.device))
     _check(lib().hsa_csa_attn(C.byref(qc), _ptr(Q), H, d, C.byref(wk), C.byref(wv), n_win,
                               C.byref(kcc), C.byref(vcc), m, _ptr(idx), k, scale, _ptr(O),
-                              _ptr(lse), ws, wsb, _stream()), "csa_attn")
+                              FP32 if out_fp32 else BF16, _ptr(lse), ws, wsb, _stream()), "csa_attn")
     return O, lse
 
 
 def hca_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: int,
              kc: PagedCache, vc: PagedCache, m: int, scale: Optional[float] = None,
-             with_lse: bool = False, ws_key="hca"):
+             with_lse: bool = False, out_fp32: bool = False, ws_key="hca"):
     H, d = Q.shape[-2], Q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     qc, wk, wv, kcc, vcc = q.c(), win_k.c(), win_v.c(), kc.c(), vc.c()
-    O = torch.empty_like(Q)
+    O = torch.empty(Q.shape, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=Q.device)
     lse = torch.empty((q.n, H), dtype=torch.float32, device=Q.device) if with_lse else None
     nb = lib().hsa_hca_attn_workspace_bytes(C.byref(qc), H, n_win, m)
     ws, wsb = _ws_args(_WS.get(ws_key, nb, Q.device))
     _check(lib().hsa_hca_attn(C.byref(qc), _ptr(Q), H, d, C.byref(wk), C.byref(wv), n_win,
-                              C.byref(kcc), C.byref(vcc), m, scale, _ptr(O), _ptr(lse), ws, wsb,
-                              _stream()), "hca_attn")
+                              C.byref(kcc), C.byref(vcc), m, scale, _ptr(O),
+                              FP32 if out_fp32 else BF16, _ptr(lse), ws, wsb, _stream()), "hca_attn")
     return O, lse
 
 
@@ -345,12 +347,14 @@ class Layer:
     H_I: int = 4
     d_I: int = 64
     scale: Optional[float] = None
+    out_fp32: bool = False
 
     def c(self) -> _Layer:
         L = _Layer()
         L.kind, L.H, L.d, L.n_win, L.m, L.topk = self.kind, self.H, self.d, self.n_win, self.m, self.topk
         L.H_I, L.d_I = self.H_I, self.d_I
         L.scale = 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+        L.o_dtype = FP32 if self.out_fp32 else BF16
         L.alpha_k, L.alpha_v = self.alpha_k.data_ptr(), self.alpha_v.data_ptr()
         L.alpha_i = self.alpha_i.data_ptr() if self.alpha_i is not None else None
         L.ring_k, L.ring_v = self.ring_k.c(), self.ring_v.c()
@@ -366,7 +370,9 @@ def decode_step(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,
                 ws_key="decode"):
     B = pos.shape[0]
     Lc = layer.c()
-    O = torch.empty_like(Q) if O is None else O
+    if O is None:
+        O = torch.empty(Q.shape, dtype=torch.float32 if layer.out_fp32 else torch.bfloat16,
+                        device=Q.device)
     lse = torch.empty((B, layer.H), dtype=torch.float32, device=Q.device) if with_lse else None
     idx = (torch.empty((B, layer.topk), dtype=torch.int32, device=Q.device)
            if with_idx and layer.kind == LAYER_CSA else None)

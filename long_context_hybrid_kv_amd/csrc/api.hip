@@ -280,16 +280,17 @@ size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_w
 hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
                         const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
                         const hsa_paged* kc, const hsa_paged* vc, int32_t m, const int32_t* idx,
-                        int32_t k, float scale, void* O, float* lse, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        int32_t k, float scale, void* O, int32_t o_dtype, float* lse, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   hsa_status s;
+  REQ(o_dtype == HSA_BF16 || o_dtype == HSA_FP32, "csa_attn: o_dtype must be bf16 or fp32");
   if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
   REQ(idx, "csa_attn: null idx");
   REQ(k >= 1 && k <= (1 << 20), "csa_attn: k out of range");
   if ((s = check_ws(ws, ws_bytes, hsa_csa_attn_workspace_bytes(q, H, n_win, k))) != HSA_OK)
     return s;
   return hip_status(launch_attn(*q, Q, H, *win_k, *win_v, n_win, *kc, *vc, m, idx, k, scale, O,
-                                lse, ws, ws_bytes, stream),
+                                o_dtype, lse, ws, ws_bytes, stream),
                     "csa_attn");
 }
 
@@ -301,13 +302,15 @@ size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_w
 hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
                         const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
                         const hsa_paged* kc, const hsa_paged* vc, int32_t m, float scale, void* O,
-                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        int32_t o_dtype, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   hsa_status s;
+  REQ(o_dtype == HSA_BF16 || o_dtype == HSA_FP32, "hca_attn: o_dtype must be bf16 or fp32");
   if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
   if ((s = check_ws(ws, ws_bytes, hsa_hca_attn_workspace_bytes(q, H, n_win, m))) != HSA_OK)
     return s;
   return hip_status(launch_attn(*q, Q, H, *win_k, *win_v, n_win, *kc, *vc, m, nullptr, 0, scale,
-                                O, lse, ws, ws_bytes, stream),
+                                O, o_dtype, lse, ws, ws_bytes, stream),
                     "hca_attn");
 }
 
@@ -346,6 +349,7 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode_step: unknown layer kind");
   REQ(B >= 1 && pos && Q && k_new && v_new && O, "decode_step: null argument or B < 1");
   REQ(L->alpha_k && L->alpha_v, "decode_step: null pooling weights");
+  REQ(L->o_dtype == HSA_BF16 || L->o_dtype == HSA_FP32, "decode_step: o_dtype must be bf16 or fp32");
   SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
       "decode_step: appending to fp8 caches is not supported (page scales are set per page)");
   REQ(L->kc.n_req >= B && L->vc.n_req >= B && L->ring_k.n_req >= B && L->ring_v.n_req >= B,
@@ -390,10 +394,10 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
                        stream, /*ws_head_zeroed=*/true);
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
-                    L->topk, L->scale, O, lse, base + a_idx + a_sel, a_attn, stream);
+                    L->topk, L->scale, O, L->o_dtype, lse, base + a_idx + a_sel, a_attn, stream);
   } else {
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
-                    L->scale, O, lse, base, a_attn, stream);
+                    L->scale, O, L->o_dtype, lse, base, a_attn, stream);
   }
   return hip_status(e, "decode_step attention");
 }

@@ -39,7 +39,8 @@ struct AttnArgs {
   const int32_t* idx;
   int k;                 // > 0: CSA selection of width k; 0: HCA (all visible)
   float scale_log2;      // logit scale times log2(e)
-  u16* O;
+  void* O;
+  int o_f32;             // 1: fp32 output, 0: bf16
   float* lse;
   float* part_o;
   float* part_ml;
@@ -303,13 +304,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
   if (a.n_splits == 1) {
     const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
-    u16* orow = a.O + ((int64_t)qi * a.H + head) * kD;
+    const int64_t o0 = ((int64_t)qi * a.H + head) * kD;
+    if (a.o_f32) {
+      float* orow = (float*)a.O + o0;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      uint32_t b[4];
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt + 4 * g) = oacc[dt] * inv;
+    } else {
+      u16* orow = (u16*)a.O + o0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)(oacc[dt][i] * inv));
-      *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      for (int dt = 0; dt < 8; ++dt) {
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)(oacc[dt][i] * inv));
+        *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
     }
     if (g == 0 && a.lse) a.lse[(int64_t)qi * a.H + head] = (m_i + log2f(l_i)) * kLn2;
   } else {
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
-                                                         u16* __restrict__ O,
+                                                         void* __restrict__ O, int o_f32,
                                                          float* __restrict__ lse) {
   const int qh = blockIdx.x;   // query * H + head
   const int q = qh / H, h = qh % H, d = threadIdx.x;
@@ -342,7 +350,11 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
     L += wgt * part_ml[slot * 2 + 1];
     acc += wgt * part_o[slot * kD + d];
   }
-  O[(int64_t)qh * kD + d] = __builtin_bit_cast(u16, (__bf16)(L > 0.f ? acc / L : 0.f));
+  const float o = L > 0.f ? acc / L : 0.f;
+  if (o_f32)
+    ((float*)O)[(int64_t)qh * kD + d] = o;
+  else
+    ((u16*)O)[(int64_t)qh * kD + d] = __builtin_bit_cast(u16, (__bf16)o);
   if (d == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
 }
 
@@ -382,7 +394,8 @@ size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span) {
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
                        const hsa_tokens& wv, int n_win, const hsa_paged& kc,
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
-                       void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+                       void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   int64_t s_max = q.max_pos - n_win + 1 < 0 ? 0 : q.max_pos - n_win + 1;
@@ -404,7 +417,8 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.idx = idx;
   a.k = k;
   a.scale_log2 = scale * kLog2e;
-  a.O = (u16*)O;
+  a.O = O;
+  a.o_f32 = o_dtype == HSA_FP32;
   a.lse = lse;
   a.part_o = (float*)ws;
   const size_t slots = (size_t)q.n * p.n_splits * H;
@@ -426,7 +440,7 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
     attn_kernel<1><<<(unsigned)n_blocks, 64, 0, s>>>(a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
-                                                            (u16*)O, lse);
+                                                            O, a.o_f32, lse);
   return hipGetLastError();
 }
 

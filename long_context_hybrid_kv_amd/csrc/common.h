@@ -182,7 +182,8 @@ size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span);
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
                        const hsa_tokens& wv, int n_win, const hsa_paged& kc,
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
-                       void* O, float* lse, void* ws, size_t ws_bytes, hipStream_t s);
+                       void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t s);
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,

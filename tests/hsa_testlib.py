@@ -4,8 +4,9 @@ run the library, and compare with the oracle by the parity rules:
 * compressed entries (bf16 bits, fp8 codes and page scales): bit-exact;
 * top-k sets: equal, except at blocks whose oracle score lies within 1e-4
   (relative) of the k-th largest oracle score;
-* attention outputs: max abs error <= 1e-2 (bf16 in, fp32 accumulation);
-  lse within 1e-3.
+* attention outputs: max abs error <= 1e-2 (bf16 in, fp32 accumulation),
+  checked on fp32 outputs; a bf16 output must be the round-to-nearest-even
+  of the fp32 one; lse within 1e-3.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ import numpy as np
 import torch
 
 from long_context_hybrid_kv_amd import _lib as L
+from synth import gen
 
 OUT_TOL = 1e-2
 LSE_TOL = 1e-3
@@ -95,3 +97,87 @@ def check_out(gpu: torch.Tensor, ref: np.ndarray, where="", tol=OUT_TOL):
 
 def scale_of(d=128):
     return 1.0 / math.sqrt(d)
+
+
+# ----------------------------------------------------------------------------- decode state
+
+def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True):
+    """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
+    and the per-request token/query streams for `steps` decode steps."""
+    B = len(Ls)
+    m = w.m(layer)
+    n_win = w.n_win
+    reqs = [gen.decode_request(w, layer, r, L=int(Ls[r]), extra_tokens=steps, n_queries=steps)
+            for r in range(B)]
+    z = gen.pool_logits(w, layer)
+    max_entries = int(max(Ls)) // m + steps // m + 2
+    ppr = -(-max_entries // 64)
+    perm = (torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None)
+    def cache(dim, f8):
+        return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm)
+    st = {"reqs": reqs, "z": z, "m": m}
+    st["alpha_k"] = L.pooling_weights(torch.from_numpy(z["zk"]).cuda())
+    st["alpha_v"] = L.pooling_weights(torch.from_numpy(z["zv"]).cuda())
+    st["kc"], st["vc"] = cache(128, fp8), cache(128, fp8)
+    ring_k = torch.zeros((B, n_win, 128), dtype=torch.bfloat16, device="cuda")
+    ring_v = torch.zeros_like(ring_k)
+    if layer == "csa":
+        st["alpha_i"] = L.pooling_weights(torch.from_numpy(z["zi"]).cuda())
+        st["kic"] = cache(64, False)
+        tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda")
+    for r, d in enumerate(reqs):
+        Lr = int(Ls[r])
+        nb = Lr // m
+        for name, x, a in [("kc", "k", "alpha_k"), ("vc", "v", "alpha_v")] + \
+                ([("kic", "ki", "alpha_i")] if layer == "csa" else []):
+            if nb > 0:
+                L.kv_compress(tokens(d[x][:Lr]), st[name], r, 0, nb, m, st[a])
+        lo = max(0, Lr - n_win)
+        slots = torch.arange(lo, Lr) % n_win
+        ring_k[r, slots] = dev_bf16(d["k"][lo:Lr])
+        ring_v[r, slots] = dev_bf16(d["v"][lo:Lr])
+        if layer == "csa":
+            t0 = nb * m
+            tail[r, torch.arange(t0, Lr) % m] = dev_bf16(d["ki"][t0:Lr])
+    st["ring_k"], st["ring_v"] = L.Tokens(ring_k), L.Tokens(ring_v)
+    if layer == "csa":
+        st["tail_i"] = L.Tokens(tail)
+    return st
+
+
+def run_ops(w, layer, st, Ls, s=0):
+    """One decode query per request through the separate ops (window already
+    holds the new token)."""
+    B = len(Ls)
+    pos = torch.tensor([int(x) + s for x in Ls], dtype=torch.int64, device="cuda")
+    for r, d in enumerate(st["reqs"]):
+        p = int(Ls[r]) + s
+        st["ring_k"].data[r, p % w.n_win] = dev_bf16(d["k"][p])
+        st["ring_v"].data[r, p % w.n_win] = dev_bf16(d["v"][p])
+    q = L.Queries.list(pos, int(pos.max().item()))
+    Q = dev_bf16(np.stack([d["q"][s] for d in st["reqs"]]))
+    out = {}
+    if layer == "csa":
+        qi = dev_bf16(np.stack([d["qi"][s] for d in st["reqs"]]))
+        wt = torch.from_numpy(np.stack([d["w"][s] for d in st["reqs"]])).cuda()
+        idx, score = L.indexer_topk(q, qi, wt, st["kic"], w.m_csa, w.n_win, w.k_csa, with_score=True)
+        O, lse = L.csa_attn(q, Q, st["ring_k"], st["ring_v"], w.n_win, st["kc"], st["vc"], w.m_csa,
+                            idx, w.k_csa, with_lse=True, out_fp32=True)
+        out["idx"] = idx.cpu().numpy()
+    else:
+        O, lse = L.hca_attn(q, Q, st["ring_k"], st["ring_v"], w.n_win, st["kc"], st["vc"], w.m_hca,
+                            with_lse=True, out_fp32=True)
+    L.check_device_error()
+    out["O"], out["lse"] = to_f64(O), lse.cpu().numpy()
+    return out
+
+
+def layer_of(w, layer, st):
+    kw = dict(kind=L.LAYER_CSA if layer == "csa" else L.LAYER_HCA, H=w.H, n_win=w.n_win,
+              m=w.m(layer), alpha_k=st["alpha_k"], alpha_v=st["alpha_v"], ring_k=st["ring_k"],
+              ring_v=st["ring_v"], kc=st["kc"], vc=st["vc"], out_fp32=True)
+    if layer == "csa":
+        kw.update(topk=w.k_csa, alpha_i=st["alpha_i"], tail_i=st["tail_i"], kic=st["kic"])
+    return L.Layer(**kw)
+
+

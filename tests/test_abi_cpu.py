@@ -68,15 +68,17 @@ def test_validation_rejects_before_any_launch():
     q0 = L._Queries(0, None, None, 0, 0, 0)
     assert lib.hsa_indexer_topk(C.byref(q0), f, f, 4, 64, C.byref(ki), 4, 128, 16, f, None, f, 1 << 30, None) == -1
     # attention: H not a multiple of 16, d != 128, window capacity too small
-    assert lib.hsa_hca_attn(C.byref(q), f, 24, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, None, f, 1 << 30, None) == -2
-    assert lib.hsa_hca_attn(C.byref(q), f, 16, 64, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, None, f, 1 << 30, None) == -2
+    assert lib.hsa_hca_attn(C.byref(q), f, 24, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -2
+    assert lib.hsa_hca_attn(C.byref(q), f, 16, 64, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -2
     small = _tokens(cap=2)
-    assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(small), C.byref(small), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, None, f, 1 << 30, None) == -1
+    assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(small), C.byref(small), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -1
     # span beyond max_pos
     qb = L._Queries(4, None, None, 0, 10, 3)
-    assert lib.hsa_hca_attn(C.byref(qb), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, None, f, 1 << 30, None) == -1
+    assert lib.hsa_hca_attn(C.byref(qb), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -1
+    # unknown output dtype
+    assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 1, None, f, 1 << 30, None) == -1
     # CSA without idx
-    assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, None, f, 1 << 30, None) == -1
+    assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, 0, None, f, 1 << 30, None) == -1
 
 
 def test_decode_step_rejects_fp8_append_and_bad_layers():

@@ -57,7 +57,7 @@ def test_compress_fp8_bitexact():
     L.check_device_error()
 
 
-def _run_prefill_csa(w, inp, rows=None, page_order=None):
+def _run_prefill_csa(w, inp, rows=None, page_order=None, out_fp32=True):
     m, n_win, k, T_ = w.m_csa, w.n_win, w.k_csa, inp["k"].shape[0]
     gc = T.compress_layer(inp, "csa", m, page_order=page_order)
     q = L.Queries.span(T_)
@@ -66,7 +66,8 @@ def _run_prefill_csa(w, inp, rows=None, page_order=None):
     idx, score = L.indexer_topk(q, qi, wt, gc["kic"], m, n_win, k, with_score=True)
     Q = T.dev_bf16(inp["q"])
     tk, tv = T.tokens(inp["k"]), T.tokens(inp["v"])
-    O, lse = L.csa_attn(q, Q, tk, tv, n_win, gc["kc"], gc["vc"], m, idx, k, with_lse=True)
+    O, lse = L.csa_attn(q, Q, tk, tv, n_win, gc["kc"], gc["vc"], m, idx, k, with_lse=True,
+                        out_fp32=out_fp32)
     L.check_device_error()
     return idx.cpu().numpy(), score.cpu().numpy(), O, lse.cpu().numpy()
 
@@ -110,7 +111,7 @@ def test_prefill_4k_hca_all_rows():
     gc = T.compress_layer(inp, "hca", m)
     q = L.Queries.span(4096)
     O, lse = L.hca_attn(q, T.dev_bf16(inp["q"]), T.tokens(inp["k"]), T.tokens(inp["v"]), n_win,
-                        gc["kc"], gc["vc"], m, with_lse=True)
+                        gc["kc"], gc["vc"], m, with_lse=True, out_fp32=True)
     L.check_device_error()
     oc = _oracle_caches(inp, "hca", m)
     Ob, lse = T.to_f64(O), lse.cpu().numpy()
@@ -134,7 +135,8 @@ def test_prefill_ragged_shapes(H, n_win, k, T_):
     m = min(w.m_hca, n_win)
     gc = T.compress_layer(inp, "hca", m)
     O, lse = L.hca_attn(L.Queries.span(T_), T.dev_bf16(inp["q"]), T.tokens(inp["k"]),
-                        T.tokens(inp["v"]), n_win, gc["kc"], gc["vc"], m, with_lse=True)
+                        T.tokens(inp["v"]), n_win, gc["kc"], gc["vc"], m, with_lse=True,
+                        out_fp32=True)
     L.check_device_error()
     oc = _oracle_caches(inp, "hca", m)
     Ob = T.to_f64(O)
@@ -150,7 +152,7 @@ def test_m1_full_window_is_dense_causal():
     inp = gen.prefill_layer(w, "hca")
     gc = T.compress_layer(inp, "hca", 1)
     O, _ = L.hca_attn(L.Queries.span(700), T.dev_bf16(inp["q"]), T.tokens(inp["k"]),
-                      T.tokens(inp["v"]), 1024, gc["kc"], gc["vc"], 1)
+                      T.tokens(inp["v"]), 1024, gc["kc"], gc["vc"], 1, out_fp32=True)
     q = torch.from_numpy(nx.bf16_value(inp["q"])).float().permute(1, 0, 2)
     kk = torch.from_numpy(nx.bf16_value(inp["k"])).float()[None].expand(16, -1, -1)
     vv = torch.from_numpy(nx.bf16_value(inp["v"])).float()[None].expand(16, -1, -1)
@@ -164,7 +166,7 @@ def test_unit_values_and_head_permutation():
     one = dict(inp)
     one["v"] = gen.bf16_bits(np.ones((1500, 128), np.float32))
     one["zv"] = inp["zv"]
-    idx, _, O, _ = _run_prefill_csa(w, one)
+    idx, _, O, _ = _run_prefill_csa(w, one, out_fp32=False)
     assert np.max(np.abs(T.to_f64(O) - 1.0)) < 1e-6
     perm = np.random.default_rng(0).permutation(16)
     pinp = dict(inp)
@@ -172,3 +174,25 @@ def test_unit_values_and_head_permutation():
     _, _, O1, _ = _run_prefill_csa(w, inp)
     _, _, O2, _ = _run_prefill_csa(w, pinp)
     assert torch.equal(O1[:, perm], O2)
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    """The bf16 output store is exactly the round-to-nearest-even of the fp32
+    output (same accumulation), for CSA prefill, HCA prefill and decode splits."""
+    w = configs.shrink(configs.PREFILL_4K, T=2000, k_csa=32)
+    inp = gen.prefill_layer(w, "csa")
+    _, _, O32, l32 = _run_prefill_csa(w, inp, out_fp32=True)
+    _, _, O16, l16 = _run_prefill_csa(w, inp, out_fp32=False)
+    assert torch.equal(O32.to(torch.bfloat16), O16)
+    assert np.array_equal(l32, l16)
+    wd = configs.shrink(configs.PRO_DECODE_1M, H=128)
+    Ls = [3000, 70000]
+    st = T.build_state(wd, "hca", Ls, fp8=True)
+    pos = torch.tensor(Ls, dtype=torch.int64, device="cuda")
+    q = L.Queries.list(pos, max(Ls))
+    Q = T.dev_bf16(np.stack([d["q"][0] for d in st["reqs"]]))
+    a, _ = L.hca_attn(q, Q, st["ring_k"], st["ring_v"], wd.n_win, st["kc"], st["vc"], wd.m_hca,
+                      out_fp32=True)
+    b, _ = L.hca_attn(q, Q, st["ring_k"], st["ring_v"], wd.n_win, st["kc"], st["vc"], wd.m_hca)
+    L.check_device_error()
+    assert torch.equal(a.to(torch.bfloat16), b)
