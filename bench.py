@@ -249,11 +249,7 @@ def cpu_baseline_csa_decode(w, budget_s):
     same requests; caches are precomputed outside the timed region."""
     from oracle import hybrid as orc
     from synth import gen
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores = _cores()
     sample = []
     for r in range(2):
         d = gen.decode_request(w, "csa", r)
@@ -276,50 +272,160 @@ def cpu_baseline_csa_decode(w, budget_s):
                       f"attention over {w.n_win + w.k_csa} entries, float64), {dt:.1f}s"}
 
 
+class RawCall:
+    """A library call with pre-marshalled arguments; the stream is the caller's
+    current stream at call time (so the call can be captured in a graph)."""
+
+    def __init__(self, T, fn, args, name):
+        self.T, self.fn, self.args, self.name = T, fn, args, name
+
+    def __call__(self):
+        import torch
+        st = self.fn(*self.args, C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            self.T._check(st, self.name)
+
+
+class StepGroup:
+    def __init__(self, calls):
+        self.calls = calls
+
+    def __call__(self):
+        for c in self.calls:
+            c()
+
+
+def pro_decode_calls(T, w, lay_c, st_c, lay_h, st_h, L, keep):
+    """indexer_topk + csa_attn (CSA layer) and hca_attn (HCA layer) for one cache copy."""
+    import torch
+    B = w.B
+    p = lambda t: None if t is None else C.c_void_p(t.data_ptr())
+    q = T.Queries.list(st_c["pos"], L)
+    qc = q.c()
+    kic, kc, vc = lay_c.kic.c(), lay_c.kc.c(), lay_c.vc.c()
+    wk, wv = lay_c.ring_k.c(), lay_c.ring_v.c()
+    kch, vch = lay_h.kc.c(), lay_h.vc.c()
+    wkh, wvh = lay_h.ring_k.c(), lay_h.ring_v.c()
+    lib = T.lib()
+    idx = torch.empty((B, w.k_csa), dtype=torch.int32, device="cuda")
+    O_c = torch.empty_like(st_c["Q"])
+    O_h = torch.empty_like(st_h["Q"])
+    ws_i = torch.empty(max(1, lib.hsa_indexer_topk_workspace_bytes(C.byref(qc), w.m_csa, w.n_win, w.k_csa)),
+                       dtype=torch.uint8, device="cuda")
+    ws_c = torch.empty(max(1, lib.hsa_csa_attn_workspace_bytes(C.byref(qc), w.H, w.n_win, w.k_csa)),
+                       dtype=torch.uint8, device="cuda")
+    ws_h = torch.empty(max(1, lib.hsa_hca_attn_workspace_bytes(C.byref(qc), w.H, w.n_win, w.m_hca)),
+                       dtype=torch.uint8, device="cuda")
+    keep.extend([qc, kic, kc, vc, wk, wv, kch, vch, wkh, wvh, idx, O_c, O_h, ws_i, ws_c, ws_h, q])
+    scale = 1.0 / math.sqrt(128)
+    ci = RawCall(T, lib.hsa_indexer_topk,
+                 (C.byref(qc), p(st_c["qI"]), p(st_c["w"]), 4, 64, C.byref(kic), w.m_csa, w.n_win,
+                  w.k_csa, p(idx), None, p(ws_i), ws_i.numel()), "indexer_topk")
+    ca = RawCall(T, lib.hsa_csa_attn,
+                 (C.byref(qc), p(st_c["Q"]), w.H, 128, C.byref(wk), C.byref(wv), w.n_win, C.byref(kc),
+                  C.byref(vc), w.m_csa, p(idx), w.k_csa, C.c_float(scale), p(O_c), T.BF16, None,
+                  p(ws_c), ws_c.numel()), "csa_attn")
+    ha = RawCall(T, lib.hsa_hca_attn,
+                 (C.byref(qc), p(st_h["Q"]), w.H, 128, C.byref(wkh), C.byref(wvh), w.n_win,
+                  C.byref(kch), C.byref(vch), w.m_hca, C.c_float(scale), p(O_h), T.BF16, None,
+                  p(ws_h), ws_h.numel()), "hca_attn")
+    return StepGroup([ci, ca, ha])
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def cpu_baseline_pro_decode(w, budget_s):
+    """The oracle's step (indexer, top-k, CSA attention, HCA attention) for one
+    request at 1M context; caches (fp8) are precomputed outside the timing."""
+    from oracle import hybrid as orc
+    from synth import gen
+    L = w.L
+    dc = gen.decode_request(w, "csa", 0)
+    dh = gen.decode_request(w, "hca", 0)
+    zc, zh = gen.pool_logits(w, "csa"), gen.pool_logits(w, "hca")
+    cc = dict(kc=orc.compress(dc["k"][:L], zc["zk"], w.m_csa, "fp8"),
+              vc=orc.compress(dc["v"][:L], zc["zv"], w.m_csa, "fp8"),
+              kic=orc.compress(dc["ki"][:L], zc["zi"], w.m_csa))
+    ch = dict(kc=orc.compress(dh["k"][:L], zh["zk"], w.m_hca, "fp8"),
+              vc=orc.compress(dh["v"][:L], zh["zv"], w.m_hca, "fp8"))
+    done, t0 = 0, time.time()
+    while time.time() - t0 < budget_s or done == 0:
+        orc.csa_query(L, dc["q"][0], dc["qi"][0], dc["w"][0], dc["k"], dc["v"], cc["kc"], cc["vc"],
+                      cc["kic"], w.m_csa, w.n_win, w.k_csa)
+        orc.hca_query(L, dh["q"][0], dh["k"], dh["v"], ch["kc"], ch["vc"], w.m_hca, w.n_win)
+        done += 1
+    dt = time.time() - t0
+    return {"value": done / dt, "unit": "tok/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{done} decode steps (CSA top-{w.k_csa} over "
+                      f"{orc.n_visible(L, w.m_csa, w.n_win)} blocks + HCA over "
+                      f"{orc.n_visible(L, w.m_hca, w.n_win)} entries) of one request at context {L}, "
+                      f"float64, {dt:.1f}s"}
+
+
+def cpu_baseline_prefill(w, budget_s):
+    """The oracle's CSA and HCA outputs for sampled query rows of the 128K
+    prefill (every 997th row from the end), scaled to Ktok/s of a layer pair."""
+    from oracle import hybrid as orc
+    from synth import gen
+    T = 16384 + 1
+    inc = gen.prefill_layer(w, "csa", T=T)
+    inh = gen.prefill_layer(w, "hca", T=T)
+    cc, ch = orc.layer_caches(inc, "csa", w.m_csa), orc.layer_caches(inh, "hca", w.m_hca)
+    rows = list(range(T - 1, 0, -997))
+    done, t0 = 0, time.time()
+    while (time.time() - t0 < budget_s and done < len(rows)) or done == 0:
+        t = rows[done % len(rows)]
+        orc.prefill_rows(inc, "csa", [t], w.m_csa, w.n_win, topk=w.k_csa, caches=cc)
+        orc.prefill_rows(inh, "hca", [t], w.m_hca, w.n_win, caches=ch)
+        done += 1
+    dt = time.time() - t0
+    return {"value": done / dt / 1e3, "unit": "Ktok/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{done} query rows (CSA + HCA) at positions up to {T - 1} of the planted "
+                      f"prefill (a row's cost grows with its position; the full 128K layer has "
+                      f"rows up to 131071, so this overstates the oracle's rate), float64, {dt:.1f}s"}
+
+
 def bench_pro_decode(args, w):
-    """1M-token Pro decode: CSA (fp8 K/V, top-1024) + HCA (fp8), B = 4.  The
-    step runs the three ops (no block completes at t = 2^20)."""
+    """1M-token Pro decode: CSA (fp8 K/V, top-1024) + HCA (fp8), batch 4.  A step
+    is the indexer + top-k + CSA attention and the HCA attention (no block
+    completes at t = 2^20, so there is no cache upkeep to do)."""
     import torch
     from long_context_hybrid_kv_amd import _lib as T
     from synth import gen
     L = w.L
-    lays = {}
-    for layer in ("csa", "hca"):
-        lays[layer] = build_decode_state(w, layer, L, T, gen, args.copies, fp8=True)
+    lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True)
+            for layer in ("csa", "hca")}
     log(f"[bench] {w.name}: state built")
-    B = w.B
-    q = T.Queries.list(lays["csa"][1]["pos"], L)
-    outs = []
-
-    def one(i):
-        lc, sc = lays["csa"][0][i % args.copies], lays["csa"][1]
-        lh, sh = lays["hca"][0][i % args.copies], lays["hca"][1]
-        idx, _ = T.indexer_topk(q, sc["qI"], sc["w"], lc.kic, w.m_csa, w.n_win, w.k_csa)
-        T.csa_attn(q, sc["Q"], lc.ring_k, lc.ring_v, w.n_win, lc.kc, lc.vc, w.m_csa, idx, w.k_csa)
-        T.hca_attn(q, sh["Q"], lh.ring_k, lh.ring_v, w.n_win, lh.kc, lh.vc, w.m_hca)
-
-    for i in range(args.warmup):
-        one(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = args.steps
-    e0.record()
-    for i in range(n):
-        one(i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    scan_ms, _ = kernel_avg_ms(T, T.K_INDEXER_SCAN, one, 16)
+    keep = []
+    steps = [pro_decode_calls(T, w, lays["csa"][0][i], lays["csa"][1], lays["hca"][0][i],
+                              lays["hca"][1], L, keep) for i in range(args.copies)]
+    ms, n = time_graph(steps, args.steps, args.warmup)
+    scan_ms, cnt = kernel_avg_ms(T, T.K_INDEXER_SCAN, lambda i: steps[i % len(steps)](), 16)
     nv = (L - w.n_win + 1 + w.m_csa - 1) // w.m_csa
     nvh = (L - w.n_win + 1 + w.m_hca - 1) // w.m_hca
+    B = w.B
     scan_bytes = B * nv * 128
     step_bytes = B * (nv * 128 + w.k_csa * 256 + nvh * 256 + 2 * w.n_win * 512 + 4 * w.H * 256)
-    return {"value": B / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms,
+    gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
+    src = source_hash("indexer.hip", "common.h")
+    return {"value": B / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": n,
             "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "scan_hbm_frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "scan_avg_ms": round(scan_ms, 5), "timing": "eager (python launches)",
-            "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H,
-                       "topk": w.k_csa, "kv_dtype": "fp8_e4m3+page_scale"}}
+            "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H, "kv_heads": 1,
+                       "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
+                       "layers": "csa+hca", "kv_dtype": "fp8_e4m3+page_scale",
+                       "cache_copies": args.copies},
+            "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": committed_traffic("idx_scan_kernel", w.name, src),
+                         "algorithmic_bytes_per_launch": scan_bytes,
+                         "avg_launch_ms": round(scan_ms, 5), "launches_timed": cnt}}
 
 
 def bench_prefill(args, w):
@@ -374,6 +480,8 @@ def bench_prefill(args, w):
 
     n = max(2, min(5, args.steps // 10))
     ms_csa, ms_hca = timed(csa, n), timed(hca, n)
+    att_csa_ms, _ = kernel_avg_ms(T, T.K_ATTN, lambda i: csa(), 2)
+    att_hca_ms, _ = kernel_avg_ms(T, T.K_ATTN, lambda i: hca(), 2)
     # algorithmic MFMA work (flops): attention 4*H*d per (query, entry); indexer 2*4*64 per pair
     nv = lambda t, m: min(-(-max(0, t - w.n_win + 1) // m), (t + 1) // m)
     t = np.arange(Tn)
@@ -385,12 +493,23 @@ def bench_prefill(args, w):
     fl_idx = float(np.sum(nv_c)) * 2 * 4 * 64
     fl_hca = float(np.sum(nw + nv_h)) * 4 * w.H * 128
     tot = ms_csa + ms_hca
-    return {"value": Tn / (tot * 1e-3) / 1e3, "unit": "Ktok/s", "ms_per_layer_pair": tot,
+    # dominant kernel: the attention launch with the larger share of the pair
+    if att_hca_ms >= att_csa_ms:
+        kname, kms, kfl = "attn_kernel (HCA)", att_hca_ms, fl_hca
+    else:
+        kname, kms, kfl = "attn_kernel (CSA)", att_csa_ms, fl_csa_att
+    tf = kfl / (kms * 1e-3) / 1e12
+    return {"value": Tn / (tot * 1e-3) / 1e3, "unit": "Ktok/s", "ms_per_step": tot, "steps": 2 * n,
             "ms_csa_layer": ms_csa, "ms_hca_layer": ms_hca,
-            "mfma_frac": round((fl_csa_att + fl_idx + fl_hca) / (tot * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "ms_attn_csa": att_csa_ms, "ms_attn_hca": att_hca_ms,
+            "pair_mfma_frac": round((fl_csa_att + fl_idx + fl_hca) / (tot * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "algorithmic_tflop": round((fl_csa_att + fl_idx + fl_hca) / 1e12, 3),
-            "config": {"workload": w.name, "T": Tn, "heads": w.H, "topk": w.k_csa,
-                       "layers": "csa+hca", "planted": True}}
+            "config": {"workload": w.name, "T": Tn, "heads": w.H, "kv_heads": 1, "d": 128,
+                       "topk": w.k_csa, "window": w.n_win, "layers": "csa+hca", "planted": True},
+            "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": kfl, "avg_launch_ms": round(kms, 4)}}
 
 
 def main():
@@ -399,7 +518,9 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--copies", type=int, default=COPIES)
-    ap.add_argument("--extra", action="store_true", help="also the 1M Pro decode and 128K prefill")
+    ap.add_argument("--workload", default="csa_decode_128k",
+                    choices=["csa_decode_128k", "pro_decode_1m", "hybrid_prefill_128k"])
+    ap.add_argument("--extra", action="store_true", help="also the other two workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -420,28 +541,35 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes": 1 << 30}))
         return
     from synth import configs
-    w = configs.CSA_DECODE_128K
-    res, layers, step = bench_csa_decode(args, w)
+    runners = {"csa_decode_128k": (lambda a, w: bench_csa_decode(a, w)[0], configs.CSA_DECODE_128K,
+                                   cpu_baseline_csa_decode),
+               "pro_decode_1m": (bench_pro_decode, configs.PRO_DECODE_1M, cpu_baseline_pro_decode),
+               "hybrid_prefill_128k": (bench_prefill, configs.HYBRID_PREFILL_128K,
+                                       cpu_baseline_prefill)}
+    fn, w, cpu_fn = runners[args.workload]
+    res = fn(args, w)
+    torch.cuda.empty_cache()
     line = {"metric": METRIC, "value": round(res["value"], 1), "unit": res["unit"], "n_gpus": 1,
             "steps": res["steps"], "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) tokens; caches compressed on the GPU)",
-            "config": res["config"], "roofline": res["roofline"],
-            "step_hbm_frac": res["step_hbm_frac"]}
-    del layers, step
-    torch.cuda.empty_cache()
+            "config": res["config"], "roofline": res["roofline"]}
+    for key in ("step_hbm_frac", "pair_mfma_frac", "ms_csa_layer", "ms_hca_layer"):
+        if key in res:
+            line[key] = res[key]
     if args.extra:
         extra = {}
-        for fn, wl in ((bench_pro_decode, configs.PRO_DECODE_1M),
-                       (bench_prefill, configs.HYBRID_PREFILL_128K)):
+        for name, (efn, ew, _) in runners.items():
+            if name == args.workload:
+                continue
             try:
-                extra[wl.name] = fn(args, wl)
+                extra[name] = efn(args, ew)
             except Exception as e:   # report, keep the main line
-                extra[wl.name] = {"error": repr(e)[:300]}
+                extra[name] = {"error": repr(e)[:300]}
             torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_csa_decode(w, args.cpu_budget)
+        line["cpu_baseline"] = cpu_fn(w, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

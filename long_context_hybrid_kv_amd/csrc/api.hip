@@ -87,6 +87,7 @@ static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, boo
   REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3, n + ": unknown dtype");
   SUP(allow_fp8 || p->dtype == HSA_BF16, n + ": must be bf16");
   REQ(p->dtype != HSA_FP8_E4M3 || p->scale, n + ": fp8 cache needs page scales");
+  SUP(p->n_pages < (1 << 25), n + ": pool rows must be addressable by a 32-bit row id");
   return HSA_OK;
 }
 
@@ -96,6 +97,7 @@ static hsa_status check_tokens(const hsa_tokens* t, const char* name, int dim, i
   REQ(t->n_req >= 1 && t->capacity >= 1, n + ": empty");
   SUP(t->dim == dim, n + ": unsupported dim");
   REQ(t->capacity >= need_cap, n + ": capacity smaller than the rows it must hold");
+  SUP(t->capacity * t->n_req < (int64_t(1) << 31) - 2, n + ": rows must be addressable by a 32-bit row id");
   return HSA_OK;
 }
 
@@ -128,13 +130,16 @@ static size_t csa_entries(int n_win, int k) { return (size_t)n_win + k; }
 
 static hsa_status check_attn_common(const hsa_queries* q, const void* Q, int H, int d,
                                     const hsa_tokens* wk, const hsa_tokens* wv, int n_win,
-                                    const hsa_paged* kc, const hsa_paged* vc, int m, void* O) {
+                                    const hsa_paged* kc, const hsa_paged* vc, int m, float scale,
+                                    void* O) {
   REQ(kc && vc, "attention: null cache");
+  REQ(scale > 0.f && scale < INFINITY, "attention: scale must be positive and finite");
   hsa_status s;
   if ((s = check_paged(kc, "kc", kD, true)) != HSA_OK) return s;
   if ((s = check_paged(vc, "vc", kD, true)) != HSA_OK) return s;
   if ((s = check_queries(q, kc->n_req)) != HSA_OK) return s;
   REQ(kc->n_req == vc->n_req, "attention: kc and vc differ in n_req");
+  SUP(kc->dtype == vc->dtype, "attention: kc and vc must have the same dtype");
   REQ(Q && O, "attention: null Q or O");
   SUP(d == kD, "attention: d must be 128");
   SUP(H >= 16 && H <= 128 && H % 16 == 0, "attention: H must be a multiple of 16 in [16, 128]");
@@ -284,7 +289,8 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                         size_t ws_bytes, hipStream_t stream) {
   hsa_status s;
   REQ(o_dtype == HSA_BF16 || o_dtype == HSA_FP32, "csa_attn: o_dtype must be bf16 or fp32");
-  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
+  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, scale, O)) != HSA_OK)
+    return s;
   REQ(idx, "csa_attn: null idx");
   REQ(k >= 1 && k <= (1 << 20), "csa_attn: k out of range");
   if ((s = check_ws(ws, ws_bytes, hsa_csa_attn_workspace_bytes(q, H, n_win, k))) != HSA_OK)
@@ -306,7 +312,8 @@ hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                         hipStream_t stream) {
   hsa_status s;
   REQ(o_dtype == HSA_BF16 || o_dtype == HSA_FP32, "hca_attn: o_dtype must be bf16 or fp32");
-  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, O)) != HSA_OK) return s;
+  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, scale, O)) != HSA_OK)
+    return s;
   if ((s = check_ws(ws, ws_bytes, hsa_hca_attn_workspace_bytes(q, H, n_win, m))) != HSA_OK)
     return s;
   return hip_status(launch_attn(*q, Q, H, *win_k, *win_v, n_win, *kc, *vc, m, nullptr, 0, scale,
@@ -361,7 +368,7 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   q.max_pos = max_pos;
   hsa_status s;
   if ((s = check_attn_common(&q, Q, L->H, L->d, &L->ring_k, &L->ring_v, L->n_win, &L->kc, &L->vc,
-                             L->m, O)) != HSA_OK)
+                             L->m, L->scale, O)) != HSA_OK)
     return s;
   REQ(L->ring_k.capacity >= L->n_win && L->ring_v.capacity >= L->n_win,
       "decode_step: rings must hold n_win tokens");
@@ -386,7 +393,10 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   // the update kernel also clears the indexer's counters (one launch fewer)
   hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new,
                                       csa ? base : nullptr,
-                                      csa ? indexer_zero_bytes(B, false) : 0, stream);
+                                      csa ? indexer_zero_bytes(B, nvis_host(max_pos, L->m, L->n_win),
+                                                               false)
+                                          : 0,
+                                      stream);
   if (e != hipSuccess) return hip_status(e, "decode_step update");
   if (csa) {
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);

@@ -50,10 +50,10 @@ struct AttnArgs {
 };
 
 constexpr int kMaxCps = 32;            // chunks of 64 entries per workgroup
-constexpr int kZeroRow = -2147483647 - 1;
+constexpr int kZeroRow = -1;          // reads as zeros (neither a pool nor a window row)
 
 // Row id of entry ge of a query: >= 0 is a row of the paged pool (page*64 + slot);
-// <= -2 encodes window row w as -2 - w; kZeroRow reads as zeros.
+// <= -2 encodes window row w as -2 - w; kZeroRow (-1) reads as zeros.
 __device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_t s0, int n_w,
                                         int E, int64_t nv, int ge, int* rk, int* rv) {
   if (ge < n_w) {
@@ -75,61 +75,91 @@ __device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_
   if (pv >= 0) *rv = pv * kPage + (int)(b & 63);
 }
 
-// Raw 16 bytes (bf16) or 8 bytes (fp8 codes, in .x/.y) of column group cg of a row.
+// Raw 16 bytes (bf16) or 8 bytes (fp8 codes, in .x/.y) of column group cg of a
+// row.  Branch-free: both the window row and the pool row are loaded from
+// always-valid addresses (row 0 stands in for the one not used) and the right
+// one is selected afterwards, so the loads of a chunk stay in flight together
+// instead of waiting at divergent branch joins.
+template <bool F8>
 __device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, int row, int cg) {
-  if (row >= 0) {
-    if (c.dtype == HSA_FP8_E4M3) {
-      uint2 v = *(const uint2*)(c.data + (int64_t)row * c.dim + cg * 8);
-      return make_uint4(v.x, v.y, 0, 0);
-    }
-    return *(const uint4*)(c.data + ((int64_t)row * c.dim + cg * 8) * 2);
+  const bool pool = row >= 0, win = row <= -2;
+  const int64_t pr = pool ? row : 0;
+  const int64_t wr = win ? (int64_t)(-2 - row) : 0;
+  const uint4 wv = *(const uint4*)((const u16*)tk.data + wr * kD + cg * 8);
+  uint4 pv;
+  if (F8) {
+    const uint2 v = *(const uint2*)(c.data + pr * kD + cg * 8);
+    pv = make_uint4(v.x, v.y, 0, 0);
+  } else {
+    pv = *(const uint4*)(c.data + (pr * kD + cg * 8) * 2);
   }
-  if (row == kZeroRow) return make_uint4(0, 0, 0, 0);
-  return *(const uint4*)((const u16*)tk.data + (int64_t)(-2 - row) * kD + cg * 8);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  return pool ? pv : (win ? wv : z);
 }
 
+template <bool F8>
 __device__ __forceinline__ float row_scale(const Paged& c, int row) {
-  return (row >= 0 && c.dtype == HSA_FP8_E4M3) ? c.scale[row >> 6] : 1.f;
+  if (!F8) return 1.f;
+  const float sc = c.scale[(row >= 0 ? row : 0) >> 6];
+  return row >= 0 ? sc : 1.f;
 }
 
-__device__ __forceinline__ uint4 fp8x8_to_bf16(uint4 raw) {
-  uint32_t b[8];
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __fp16 f16x2v __attribute__((ext_vector_type(2)));
+
+// 8 e4m3fn codes (two 32-bit words) -> 8 floats, by the hardware converter
+// (exact: every e4m3 value is an fp32 value).
+__device__ __forceinline__ void fp8x8_to_f32(uint32_t lo, uint32_t hi, float f[8]) {
+  f32x2v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  f32x2v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  f32x2v c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  f32x2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+
+// two floats -> packed fp16, round to nearest even (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x, y}), h2));
+}
+
+// K piece -> 8 bf16 (fp8 codes widen exactly: keep the upper half of the float)
+__device__ __forceinline__ uint4 k_piece_bf16(uint4 raw, bool fp8) {
+  if (!fp8) return raw;
+  float f[8];
+  fp8x8_to_f32(raw.x, raw.y, f);
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    b[i] = e4m3_to_bf16((raw.x >> (8 * i)) & 0xFF);
-    b[4 + i] = e4m3_to_bf16((raw.y >> (8 * i)) & 0xFF);
-  }
-  return make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                    b[6] | (b[7] << 16));
+  for (int i = 0; i < 4; ++i)
+    w[i] = (__float_as_uint(f[2 * i]) >> 16) | (__float_as_uint(f[2 * i + 1]) & 0xFFFF0000u);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// V piece -> 8 fp16 values (fp8 codes times the page scale; bf16 values exact
-// in the fp16 range)
+// V piece -> 8 fp16 values (fp8 codes times the page scale, rounded once to
+// nearest; bf16 values are exact in the fp16 range)
 __device__ __forceinline__ uint4 v_piece_f16(uint4 raw, bool fp8, float scale) {
   float f[8];
   if (fp8) {
+    fp8x8_to_f32(raw.x, raw.y, f);
+    uint32_t h[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = __uint_as_float(e4m3_to_bf16((raw.x >> (8 * i)) & 0xFF) << 16) * scale;
-      f[4 + i] = __uint_as_float(e4m3_to_bf16((raw.y >> (8 * i)) & 0xFF) << 16) * scale;
-    }
-  } else {
-    uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
+    for (int i = 0; i < 4; ++i)
+      h[i] = (uint32_t)__builtin_bit_cast(u16, (_Float16)(f[2 * i] * scale)) |
+             ((uint32_t)__builtin_bit_cast(u16, (_Float16)(f[2 * i + 1] * scale)) << 16);
+    return make_uint4(h[0], h[1], h[2], h[3]);
   }
-  uint32_t h[4];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    h[i] = (uint32_t)__builtin_bit_cast(u16, (_Float16)f[2 * i]) |
-           ((uint32_t)__builtin_bit_cast(u16, (_Float16)f[2 * i + 1]) << 16);
-  return make_uint4(h[0], h[1], h[2], h[3]);
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return make_uint4(pack_f16(f[0], f[1]), pack_f16(f[2], f[3]), pack_f16(f[4], f[5]),
+                    pack_f16(f[6], f[7]));
 }
 
-template <int NW>
+template <int NW, bool F8>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PPT = 1024 / NT;          // K (and V) pieces per thread per chunk
@@ -185,13 +215,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
   }
-  const bool kfp8 = a.kc.dtype == HSA_FP8_E4M3, vfp8 = a.vc.dtype == HSA_FP8_E4M3;
   __syncthreads();
 
-  // ---- register double buffer of one chunk's rows
+  // ---- register double buffer of one chunk's rows.  K pieces: p = tid + NT*i
+  // is (entry p/16, column group p%16).  V pieces: this thread's entry pair
+  // (2*(tid%32), +1) in column groups tid/32 + (NT/32)*j, so that two entries
+  // share one 32-bit word of the transposed tile.
   uint4 kraw[PPT], vraw[PPT];
   int krow[PPT], vrow[PPT];
   float kscl[PPT], vscl[PPT];
+  const int vpair = tid & 31;
   auto issue = [&](int c) {
     const int lo = (c - c_lo) * 64;
 #pragma unroll
@@ -199,19 +232,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
       krow[i] = rowk[lo + ek];
-      kraw[i] = load_piece(a.kc, a.wk, krow[i], cgk);
-      kscl[i] = row_scale(a.kc, krow[i]);
-      const int ev = p & 63, cgv = p >> 6;
+      kraw[i] = load_piece<F8>(a.kc, a.wk, krow[i], cgk);
+      kscl[i] = row_scale<F8>(a.kc, krow[i]);
+      const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
       vrow[i] = rowv[lo + ev];
-      vraw[i] = load_piece(a.vc, a.wv, vrow[i], cgv);
-      vscl[i] = row_scale(a.vc, vrow[i]);
+      vraw[i] = load_piece<F8>(a.vc, a.wv, vrow[i], cgv);
+      vscl[i] = row_scale<F8>(a.vc, vrow[i]);
     }
   };
 
-  float m_i = -1e30f, l_i = 0.f;
+  float m_i = -1e30f;
   f32x4 oacc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 osum = {0.f, 0.f, 0.f, 0.f};       // row sums of P (every row of the tile)
+  f16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
   if (c_lo < c_hi) issue(c_lo);
   for (int c = c_lo; c < c_hi; ++c) {
@@ -221,15 +258,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
-      *(uint4*)&Ks[ek][cgk * 8] = (kfp8 && krow[i] >= 0) ? fp8x8_to_bf16(kraw[i]) : kraw[i];
+      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0);
       if (cgk == 0) ksc[ek] = kscl[i];
-      const int ev = p & 63, cgv = p >> 6;
-      uint4 v = v_piece_f16(vraw[i], vfp8 && vrow[i] >= 0, vscl[i]);
-      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Vt[cgv * 8 + 2 * j][ev] = (u16)(w4[j] & 0xFFFF);
-        Vt[cgv * 8 + 2 * j + 1][ev] = (u16)(w4[j] >> 16);
+    for (int j = 0; j < PPT / 2; ++j) {
+      const int cgv = (tid >> 5) + (NT / 32) * j;
+      const uint4 v0 = v_piece_f16(vraw[2 * j], F8 && vrow[2 * j] >= 0, vscl[2 * j]);
+      const uint4 v1 = v_piece_f16(vraw[2 * j + 1], F8 && vrow[2 * j + 1] >= 0, vscl[2 * j + 1]);
+      const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+      uint32_t* vt = (uint32_t*)&Vt[cgv * 8][0] + vpair;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        vt[(2 * q2) * 36] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
+        vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
       }
     }
     __syncthreads();
@@ -246,48 +288,57 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], sacc[et], 0, 0, 0);
       }
     }
-    // ---- online softmax (lane = head `col`; rows 4g+i of each entry tile)
+    // ---- online softmax (lane = head `col`; rows 4g+i of each entry tile).
+    // log2-domain logit = acc * c, c = scale*log2(e) (times the page scale of
+    // fp8 keys).  With one positive c the running max is taken on the raw
+    // accumulators; entries past the end exist only in the last chunk.
+    const bool full = e0 + 64 <= E;
     float mx = -INFINITY;
+    if (!F8) {
 #pragma unroll
-    for (int et = 0; et < 4; ++et)
+      for (int et = 0; et < 4; ++et)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = et * 16 + 4 * g + i;
-        float v = (e0 + e < E) ? sacc[et][i] * a.scale_log2 * ksc[e] : -INFINITY;
-        sacc[et][i] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int i = 0; i < 4; ++i) {
+          if (!full && e0 + et * 16 + 4 * g + i >= E) sacc[et][i] = -INFINITY;
+          mx = fmaxf(mx, sacc[et][i]);
+        }
+      mx *= a.scale_log2;
+    } else {
+#pragma unroll
+      for (int et = 0; et < 4; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = et * 16 + 4 * g + i;
+          float v = sacc[et][i] * (a.scale_log2 * ksc[e]);
+          if (!full && e0 + e >= E) v = -INFINITY;
+          sacc[et][i] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_i, mx);
     const float alpha = exp2f(m_i - m_new);
-    // probabilities are rounded to fp16 once (the PV operand) and the row sum
-    // adds the rounded values, so the normalisation matches the weights used
-    float rs = 0.f;
-#pragma unroll
-    for (int et = 0; et < 4; ++et)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = (float)(_Float16)exp2f(sacc[et][i] - m_new);
-        sacc[et][i] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    l_i = l_i * alpha + rs;
     m_i = m_new;
+    const float cst = F8 ? 1.f : a.scale_log2;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+    osum *= alpha;
 
-    // ---- O^T += V^T P^T, two k-steps of 32 entries
+    // ---- O^T += V^T P^T, two k-steps of 32 entries.  P is rounded to fp16
+    // once; an extra tile of ones in place of V^T rows accumulates the row
+    // sums of exactly those rounded weights.
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f16x8 pb;
+      uint32_t pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (_Float16)sacc[2 * j][i];
-        pb[4 + i] = (_Float16)sacc[2 * j + 1][i];
+      for (int i = 0; i < 4; i += 2) {
+        pw[i / 2] = pack_f16(exp2f(__builtin_fmaf(sacc[2 * j][i], cst, -m_new)),
+                             exp2f(__builtin_fmaf(sacc[2 * j][i + 1], cst, -m_new)));
+        pw[2 + i / 2] = pack_f16(exp2f(__builtin_fmaf(sacc[2 * j + 1][i], cst, -m_new)),
+                                 exp2f(__builtin_fmaf(sacc[2 * j + 1][i + 1], cst, -m_new)));
       }
+      const f16x8 pb = __builtin_bit_cast(f16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const u16* vr = &Vt[16 * dt + col][0];
@@ -297,9 +348,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         f16x8 av = __builtin_bit_cast(f16x8, u);
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[dt], 0, 0, 0);
       }
+      osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, osum, 0, 0, 0);
     }
     __syncthreads();
   }
+  const float l_i = osum[0];
 
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
   if (a.n_splits == 1) {
@@ -333,6 +386,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// The (m, l) of every split are staged in LDS first; the partial rows are then
+// read with all loads of a thread in flight.
+constexpr int kMergeMaxSplits = 1024;
 __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
@@ -340,16 +396,42 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          float* __restrict__ lse) {
   const int qh = blockIdx.x;   // query * H + head
   const int q = qh / H, h = qh % H, d = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    M = fmaxf(M, part_ml[(((int64_t)q * n_splits + s) * H + h) * 2]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t slot = ((int64_t)q * n_splits + s) * H + h;
-    const float wgt = exp2f(part_ml[slot * 2] - M);
-    L += wgt * part_ml[slot * 2 + 1];
-    acc += wgt * part_o[slot * kD + d];
+  __shared__ float wgt[kMergeMaxSplits];
+  __shared__ float red[2];
+  const int ns = n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits;
+  float mloc = -INFINITY;
+  for (int s = d; s < ns; s += 128) {
+    const float mv = part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
+    wgt[s] = mv;
+    mloc = fmaxf(mloc, mv);
   }
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+  if ((d & 63) == 0) red[d >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float lloc = 0.f;
+  for (int s = d; s < ns; s += 128) {
+    const float wv = exp2f(wgt[s] - M);
+    wgt[s] = wv;
+    lloc += wv * part_ml[(((int64_t)q * n_splits + s) * H + h) * 2 + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
+  if ((d & 63) == 0) red[d >> 6] = lloc;
+  __syncthreads();
+  const float L = red[0] + red[1];
+  float acc = 0.f;
+  const float* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
+  const int64_t stride = (int64_t)H * kD;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = po[(s + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += wgt[s + j] * v[j];
+  }
+  for (; s < ns; ++s) acc += wgt[s] * po[s * stride];
   const float o = L > 0.f ? acc / L : 0.f;
   if (o_f32)
     ((float*)O)[(int64_t)qh * kD + d] = o;
@@ -378,6 +460,7 @@ static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span) {
     const int64_t wgs = (int64_t)n_q * p.n_hg;
     if (n * wgs < 256) n = (256 + wgs - 1) / wgs;
     if (n > chunks) n = chunks;
+    if (n > kMergeMaxSplits) n = kMergeMaxSplits;
   }
   p.cps = (int)((chunks + n - 1) / n);
   p.n_splits = (int)((chunks + p.cps - 1) / p.cps);
@@ -432,12 +515,17 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
   KernelTimer kt(HSA_K_ATTN, s);
-  if (p.nw == 4)
-    attn_kernel<4><<<(unsigned)n_blocks, 256, 0, s>>>(a);
-  else if (p.nw == 2)
-    attn_kernel<2><<<(unsigned)n_blocks, 128, 0, s>>>(a);
-  else
-    attn_kernel<1><<<(unsigned)n_blocks, 64, 0, s>>>(a);
+  const bool f8 = kc.dtype == HSA_FP8_E4M3;
+  if (p.nw == 4) {
+    if (f8) attn_kernel<4, true><<<(unsigned)n_blocks, 256, 0, s>>>(a);
+    else attn_kernel<4, false><<<(unsigned)n_blocks, 256, 0, s>>>(a);
+  } else if (p.nw == 2) {
+    if (f8) attn_kernel<2, true><<<(unsigned)n_blocks, 128, 0, s>>>(a);
+    else attn_kernel<2, false><<<(unsigned)n_blocks, 128, 0, s>>>(a);
+  } else {
+    if (f8) attn_kernel<1, true><<<(unsigned)n_blocks, 64, 0, s>>>(a);
+    else attn_kernel<1, false><<<(unsigned)n_blocks, 64, 0, s>>>(a);
+  }
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
                                                             O, a.o_f32, lse);

@@ -172,7 +172,7 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s);
 
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span);
-size_t indexer_zero_bytes(int n_q, bool span);   // head of the workspace cleared per call
+size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span);   // cleared per call
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,

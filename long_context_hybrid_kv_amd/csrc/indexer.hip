@@ -38,33 +38,49 @@ constexpr int kStateInts = 8;      // ticket1, ticket2, thr_bin, n_above, n_cand
 
 struct IdxWs {
   float* scores;        // [nq][R]
-  uint32_t* hist;       // [nq][kBins]
+  uint32_t* hist;       // [nq][hslots][kBins]
   int32_t* state;       // [nq][kStateInts]
   uint32_t* bitmap;     // [nq][R/32]
   uint64_t* cand;       // [nq][R]  (score key << 32 | ~block)
   uint64_t* cand2;      // [nq][R]
+  int32_t* ccount;      // [nq][R/kSelCH]  candidates per select chunk (long rows)
   int64_t R;
+  int hslots;           // histogram copies per query (one per 64 scan chunks, <= 16)
 };
+
+static int hist_slots(int64_t R) {
+  const int64_t chunks = R / kCH;
+  int64_t sl = (chunks + 63) / 64;
+  return (int)(sl < 1 ? 1 : (sl > 16 ? 16 : sl));
+}
+
+static int64_t row_cap(int64_t max_nvis) {
+  int64_t R = ((max_nvis + kSelCH - 1) / kSelCH) * kSelCH;
+  return R < kSelCH ? kSelCH : R;
+}
 
 static IdxWs carve(void* ws, int nq, int64_t R) {
   IdxWs w;
   char* p = (char*)ws;
   auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
+  w.hslots = hist_slots(R);
   w.state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
-  w.hist = (uint32_t*)take(sizeof(uint32_t) * kBins * nq);
+  w.hist = (uint32_t*)take(sizeof(uint32_t) * kBins * w.hslots * nq);
   w.scores = (float*)take(sizeof(float) * R * nq);
   w.bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
   w.cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
   w.cand2 = (uint64_t*)take(sizeof(uint64_t) * R * nq);
+  w.ccount = (int32_t*)take(sizeof(int32_t) * (R / kSelCH) * nq);
   w.R = R;
   return w;
 }
 
 static size_t carve_bytes(int nq, int64_t R) {
   auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
-  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(uint32_t) * kBins * nq) +
-         rnd(sizeof(float) * R * nq) +
-         rnd(sizeof(uint32_t) * (R / 32) * nq) + 2 * rnd(sizeof(uint64_t) * R * nq);
+  return rnd(sizeof(int32_t) * kStateInts * nq) +
+         rnd(sizeof(uint32_t) * kBins * hist_slots(R) * nq) + rnd(sizeof(float) * R * nq) +
+         rnd(sizeof(uint32_t) * (R / 32) * nq) + 2 * rnd(sizeof(uint64_t) * R * nq) +
+         rnd(sizeof(int32_t) * (R / kSelCH) * nq);
 }
 
 static int64_t host_nvis(int64_t t, int m, int n_win) {
@@ -75,15 +91,15 @@ static int64_t host_nvis(int64_t t, int m, int n_win) {
 
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
   (void)k;
-  int64_t R = ((max_nvis + kSelCH - 1) / kSelCH) * kSelCH;
-  if (R < kSelCH) R = kSelCH;
   int nq = span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q;
-  return carve_bytes(nq, R);
+  return carve_bytes(nq, row_cap(max_nvis));
 }
 
-static size_t zeroed_bytes(int nq) {
+// the state and histograms at the head of the workspace, cleared per call
+static size_t zeroed_bytes(int nq, int64_t R) {
   auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
-  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(uint32_t) * kBins * nq);
+  return rnd(sizeof(int32_t) * kStateInts * nq) +
+         rnd(sizeof(uint32_t) * kBins * hist_slots(R) * nq);
 }
 
 // ---------------------------------------------------------------- device helpers
@@ -141,9 +157,10 @@ __device__ __forceinline__ int64_t clamp_nvis(int64_t nv, const int32_t* n_entri
 
 // Add a chunk's LDS histogram to the query's histogram (no fence: the select
 // kernel reads it after the kernel boundary).
-__device__ __forceinline__ void flush_histogram(const uint32_t* lhist, IdxWs ws, int qrow) {
+__device__ __forceinline__ void flush_histogram(const uint32_t* lhist, IdxWs ws, int qrow,
+                                                int chunk) {
   __syncthreads();
-  uint32_t* gh = ws.hist + (int64_t)qrow * kBins;
+  uint32_t* gh = ws.hist + ((int64_t)qrow * ws.hslots + chunk % ws.hslots) * kBins;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     uint32_t c = lhist[i];
     if (c) atomicAdd(gh + i, c);
@@ -231,17 +248,15 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   constexpr int NT = kCH / 4 / 16;   // tiles per wave
   const int64_t w0b = b_begin + (int64_t)wv * (kCH / 4);
   bf16x8 b0[NT], b1[NT];
+  // branch-free: out-of-range tiles read row 0 of page 0 and are masked later
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int64_t b = w0b + 16 * u + row;
-    b0[u] = bf16x8{};
-    b1[u] = bf16x8{};
-    const int page = pg[(int)((w0b - b_begin + 16 * u) >> 6)];
-    if (b < b_end && page >= 0) {
-      const bf16x8* kr = (const bf16x8*)kic.row(page, b);
-      b0[u] = __builtin_nontemporal_load(kr + g);
-      b1[u] = __builtin_nontemporal_load(kr + 4 + g);
-    }
+    const int pgi = pg[(int)((w0b - b_begin + 16 * u) >> 6)];
+    const bool ok = b < b_end && pgi >= 0;
+    const bf16x8* kr = (const bf16x8*)kic.row(ok ? pgi : 0, ok ? b : 0);
+    b0[u] = __builtin_nontemporal_load(kr + g);
+    b1[u] = __builtin_nontemporal_load(kr + 4 + g);
   }
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
       atomicAdd(&lhist[order_key(sc) >> 20], 1u);
     }
   }
-  flush_histogram(lhist, ws, qrow);
+  flush_histogram(lhist, ws, qrow, chunk);
 }
 
 // ---------------------------------------------------------------- prefill: score GEMM
@@ -363,202 +378,361 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (b_begin + 256 * u + threadIdx.x < b_end) atomicAdd(&lhist[order_key(sc[u]) >> 20], 1u);
-  flush_histogram(lhist, ws, qrow);
+  flush_histogram(lhist, ws, qrow, chunk);
 }
 
 // ---------------------------------------------------------------- select, refine, emit
 
 
-__global__ __launch_bounds__(256) void idx_select_kernel(int k, IdxWs ws) {
-  const int qrow = blockIdx.y, chunk = blockIdx.x;
-  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
-  const int64_t nv = st[5];
-  const int n_active = nv > 0 ? (int)((nv + kSelCH - 1) / kSelCH) : 1;
-  if (chunk >= n_active) return;
-  int thr, above;
-  find_threshold(ws.hist + (int64_t)qrow * kBins, nv, k, &thr, &above);
-  if (chunk == 0 && threadIdx.x == 0) { st[2] = thr; st[3] = above; }
-  const float* srow = ws.scores + (int64_t)qrow * ws.R;
-  uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
-  uint64_t* cand = ws.cand + (int64_t)qrow * ws.R;
+// exclusive prefix sum over an NT-thread block (NT a multiple of 64)
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t b_begin = (int64_t)chunk * kSelCH;
-  const int64_t b_end = nv < b_begin + kSelCH ? nv : b_begin + kSelCH;
-  constexpr int kPer = kSelCH / 256;
-  float sc[kPer];
+  uint32_t x = v;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t b = b_begin + 256 * u + threadIdx.x;
-    sc[u] = b < b_end ? srow[b] : 0.f;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int64_t base = b_begin + 256 * u;
-    const int64_t b = base + threadIdx.x;
-    const bool valid = b < b_end;
-    const uint32_t key = valid ? order_key(sc[u]) : 0u;
-    const int bin = valid ? (int)(key >> 20) : -2;
-    const bool sel = valid && (thr < 0 || bin > thr);
-    const bool cnd = valid && thr >= 0 && bin == thr;
-    // one counter update per wave for the candidates it found
-    const uint64_t cmask = __ballot(cnd);
-    if (cmask) {
-      const int leader = __ffsll((unsigned long long)cmask) - 1;
-      uint32_t cbase = 0;
-      if (lane == leader) cbase = atomicAdd((uint32_t*)(st + 4), (uint32_t)__popcll(cmask));
-      cbase = __shfl(cbase, leader);
-      if (cnd)
-        cand[cbase + __popcll(cmask & ((1ull << lane) - 1))] =
-            ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b);
-    }
-    const uint64_t mask = __ballot(sel);
-    const int64_t wb = base + 64 * wv;                 // first block of this wave's 64
-    if (lane == 0 && wb < b_end) {
-      bm[wb >> 5] = (uint32_t)mask;
-      if (wb + 32 < b_end) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
-    }
+  for (int i = 0; i < NT / 64; ++i) {
+    uint32_t s = sh[i];
+    if (i < wv) off += s;
+    tot += s;
   }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
 }
 
-// One workgroup per query: refine the threshold bin, emit ascending block ids,
-// then clear the query's counters and histogram.
-__global__ __launch_bounds__(256) void idx_finalize_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
-                                                           float* __restrict__ score, int out_row0) {
-  const int qrow = blockIdx.x;
+// One workgroup per query: threshold bin from the histogram, one pass over the
+// query's scores marking blocks above it in a bitmap and collecting the blocks
+// inside it, radix refinement of those candidates (score bits, then inverted
+// block id), and emission of the bitmap in ascending block order.  Bitmap and
+// candidates live in LDS when they fit (dynamic shared memory sized by the
+// host), else in the workspace.
+// mode 0: the whole selection; mode 1: threshold only (long rows, before the
+// multi-workgroup select kernel); mode 2: refine + emit only (after it).
+template <int NT>
+__global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
+                                                      float* __restrict__ score, int out_row0,
+                                                      int cand_lds, int bm_lds_words, int mode) {
+  constexpr int BPT = kBins / NT;                // histogram bins per thread
+  extern __shared__ __align__(16) uint64_t dyn[];
+  __shared__ uint32_t sh[NT / 64];
+  __shared__ int s_thr, s_above, s_dstar;
+  __shared__ uint32_t s_ncand, s_next, s_dabove;
+  __shared__ uint32_t h256[256];
+  const int qrow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
   const int64_t nv = st[5];
-  const int thr = st[2];
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
-  uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
-  __shared__ uint32_t h256[256];
-  __shared__ uint32_t sh[4];
-  __shared__ int s_dstar;
-  __shared__ uint32_t s_above, s_next;
-  __shared__ uint64_t lk_a[kCandLds], lk_b[kCandLds];
-  if (thr >= 0) {
-    int need = k - st[3];
-    uint32_t nc = (uint32_t)st[4];
-    uint64_t* gsrc = ws.cand + (int64_t)qrow * ws.R;
-    uint64_t* src = gsrc;
-    uint64_t* dst = ws.cand2 + (int64_t)qrow * ws.R;
-    if (nc <= (uint32_t)kCandLds) {          // usual case: refine in LDS
-      for (uint32_t i = threadIdx.x; i < nc; i += 256) lk_a[i] = gsrc[i];
-      src = lk_a;
-      dst = lk_b;
-      __syncthreads();
+  uint32_t* gh = ws.hist + (int64_t)qrow * ws.hslots * kBins;
+
+  // first round of scores, loaded before the threshold search (independent of it)
+  constexpr int U = NT >= 1024 ? 32 : 16;
+  float sc0[U];
+  if (mode == 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = (int64_t)u * NT + tid;
+      sc0[u] = b < ws.R ? srow[b] : 0.f;
     }
+  }
+  if (mode == 2) {
+    if (tid == 0) { s_thr = st[2]; s_above = st[3]; s_ncand = (uint32_t)st[4]; s_dabove = st[6]; }
+    __syncthreads();
+  } else {
+  // ---- threshold bin: thread i owns bins kBins-BPT(i+1) .. kBins-BPT*i-1 (descending)
+  if (tid == 0) { s_thr = -1; s_above = 0; s_ncand = 0; }
+  {
+    uint32_t v[BPT];
+    const int lo = kBins - BPT * (tid + 1);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) v[j] = 0;
+    for (int sl = 0; sl < ws.hslots; ++sl) {
+#pragma unroll
+      for (int j = 0; j < BPT / 4; ++j) {
+        const uint4 u = ((const uint4*)(gh + sl * kBins + lo))[j];
+        v[4 * j] += u.x; v[4 * j + 1] += u.y; v[4 * j + 2] += u.z; v[4 * j + 3] += u.w;
+      }
+    }
+    uint32_t sm = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) sm += v[j];
+    uint32_t tot;
+    const uint32_t pre = block_scan_nt<NT>(sm, &tot, sh);
+    if (nv > k && pre < (uint32_t)k && pre + sm >= (uint32_t)k) {
+      uint32_t cum = pre;
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (cum < (uint32_t)k && cum + v[j] >= (uint32_t)k) {
+          s_thr = lo + j;
+          s_above = (int)cum;
+          s_dabove = v[j];            // candidates in the threshold bin
+        }
+        cum += v[j];
+      }
+    }
+    // the histogram is consumed: clear it for the next pass
+    for (int sl = 0; sl < ws.hslots; ++sl) {
+#pragma unroll
+      for (int j = 0; j < BPT / 4; ++j) ((uint4*)(gh + sl * kBins + lo))[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  if (mode == 1) {
+    if (tid == 0) { st[2] = s_thr; st[3] = s_above; st[6] = s_thr >= 0 ? (int)s_dabove : 0; }
+    return;
+  }
+  }
+  const int thr = s_thr;
+  const uint32_t n_thr_bin = thr >= 0 ? s_dabove : 0;
+  uint64_t* ca = dyn;
+  uint64_t* cb = dyn + cand_lds;
+  uint32_t* bm_l = (uint32_t*)(dyn + 2 * (int64_t)cand_lds);
+  const int64_t W = (nv + 31) / 32;
+  const bool cand_in_lds = n_thr_bin <= (uint32_t)cand_lds;
+  uint64_t* csrc = cand_in_lds ? ca : ws.cand + (int64_t)qrow * ws.R;
+  uint64_t* cdst = cand_in_lds ? cb : ws.cand2 + (int64_t)qrow * ws.R;
+  if (mode == 2) {
+    // candidates sit in per-chunk regions of cand (chunk c at c*kSelCH, ccount[c]
+    // of them): compact them into LDS, or into cand2 when they do not fit
+    const int n_ch = (int)(ws.R / kSelCH);
+    const int32_t* cc = ws.ccount + (int64_t)qrow * n_ch;
+    const uint64_t* g = ws.cand + (int64_t)qrow * ws.R;
+    uint64_t* dstc = cand_in_lds ? ca : ws.cand2 + (int64_t)qrow * ws.R;
+    uint32_t run = 0;
+    for (int c0 = 0; c0 < n_ch; c0 += NT) {
+      const int c = c0 + tid;
+      const uint32_t cnt = c < n_ch ? (uint32_t)cc[c] : 0u;
+      uint32_t tot;
+      const uint32_t off = block_scan_nt<NT>(cnt, &tot, sh) + run;
+      for (uint32_t i = 0; i < cnt; ++i) dstc[off + i] = g[(int64_t)c * kSelCH + i];
+      run += tot;
+    }
+    if (tid == 0) s_ncand = run;
+    __threadfence_block();
+    __syncthreads();
+    csrc = dstc;
+    cdst = cand_in_lds ? cb : ws.cand + (int64_t)qrow * ws.R;
+  }
+  uint32_t* bm = (mode == 0 && W <= bm_lds_words) ? bm_l
+                                                   : ws.bitmap + (int64_t)qrow * (ws.R / 32);
+
+  // ---- one pass over the scores: bitmap of blocks above the bin, candidates in it
+  for (int64_t base = 0; mode == 0 && base < nv; base += (int64_t)NT * U) {
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = base + (int64_t)u * NT + tid;
+      sc[u] = base == 0 ? sc0[u] : (b < nv ? srow[b] : 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b0 = base + (int64_t)u * NT;
+      if (b0 >= nv) break;
+      const int64_t b = b0 + tid;
+      const bool valid = b < nv;
+      const uint32_t key = order_key(sc[u]);
+      const int bin = (int)(key >> 20);
+      const bool sel = valid && (thr < 0 || bin > thr);
+      const bool cnd = valid && thr >= 0 && bin == thr;
+      const uint64_t cmask = __ballot(cnd);
+      if (cmask) {
+        const int leader = __ffsll((unsigned long long)cmask) - 1;
+        uint32_t cbase = 0;
+        if (lane == leader) cbase = atomicAdd(&s_ncand, (uint32_t)__popcll(cmask));
+        cbase = __shfl(cbase, leader);
+        if (cnd) csrc[cbase + __popcll(cmask & ((1ull << lane) - 1))] =
+                     ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b);
+      }
+      const uint64_t mask = __ballot(sel);
+      const int64_t wb = b0 + 64 * wv;
+      if (lane == 0 && wb < nv) {
+        bm[wb >> 5] = (uint32_t)mask;
+        if (wb + 32 < nv) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
+      }
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // ---- refine the threshold bin: need = k - (count above the bin)
+  if (thr >= 0) {
+    int need = k - s_above;
+    uint32_t nc = s_ncand;
     int shift = 44;   // bits 63..52 of the composite key were the histogram bin
     // at most 7 digit passes cover the remaining 52 key bits (scores, then ids);
     // keys are unique (they contain the block id), so the candidates left after
     // the last pass are exactly the ones still needed
     while (need > 0) {
       if (nc <= (uint32_t)need || shift < -4) {
-        for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-          const uint32_t b = ~(uint32_t)ld_cand(src + i);
+        for (uint32_t i = tid; i < nc; i += NT) {
+          const uint32_t b = ~(uint32_t)ld_cand(csrc + i);
           atomicOr(bm + (b >> 5), 1u << (b & 31));
         }
         break;
       }
       const uint64_t dmask = shift >= 0 ? 0xFFull : 0xFull;
       const int sh_amt = shift >= 0 ? shift : 0;
-      h256[threadIdx.x] = 0;
-      if (threadIdx.x == 0) { s_next = 0; s_dstar = -1; }
+      if (tid < 256) h256[tid] = 0;
+      if (tid == 0) { s_next = 0; s_dstar = -1; }
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < nc; i += 256)
-        atomicAdd(&h256[(ld_cand(src + i) >> sh_amt) & dmask], 1u);
+      for (uint32_t i = tid; i < nc; i += NT)
+        atomicAdd(&h256[(ld_cand(csrc + i) >> sh_amt) & dmask], 1u);
       __syncthreads();
       {
-        // thread i owns digit 255 - i: the crossing digit by one block scan
-        const uint32_t c = h256[255 - threadIdx.x];
+        // digit crossing by a block scan (threads >= 256 carry zeros)
+        const uint32_t c = tid < 256 ? h256[255 - tid] : 0u;
         uint32_t tot;
-        const uint32_t pre = block_excl_scan(c, &tot, sh);
-        if (pre < (uint32_t)need && pre + c >= (uint32_t)need) {
-          s_dstar = 255 - threadIdx.x;
-          s_above = pre;
+        const uint32_t pre = block_scan_nt<NT>(c, &tot, sh);
+        if (tid < 256 && pre < (uint32_t)need && pre + c >= (uint32_t)need) {
+          s_dstar = 255 - tid;
+          s_dabove = pre;
         }
       }
       __syncthreads();
       const int dstar = s_dstar;
       if (dstar < 0) break;   // counts inconsistent: stop rather than loop
-      for (uint32_t i = threadIdx.x; i < nc; i += 256) {
-        const uint64_t key = ld_cand(src + i);
+      for (uint32_t i = tid; i < nc; i += NT) {
+        const uint64_t key = ld_cand(csrc + i);
         const int dg = (int)((key >> sh_amt) & dmask);
         if (dg > dstar) {
           const uint32_t b = ~(uint32_t)key;
           atomicOr(bm + (b >> 5), 1u << (b & 31));
         } else if (dg == dstar) {
-          dst[atomicAdd(&s_next, 1u)] = key;
+          cdst[atomicAdd(&s_next, 1u)] = key;
         }
       }
       __threadfence_block();
       __syncthreads();
-      need -= (int)s_above;
+      need -= (int)s_dabove;
       nc = s_next;
-      uint64_t* tmp = src; src = dst; dst = tmp;
+      uint64_t* tmp = csrc; csrc = cdst; cdst = tmp;
       shift -= 8;
       __syncthreads();
     }
   }
+  __threadfence_block();
   __syncthreads();
 
-  // ---- emit ascending block ids from the bitmap.  The refine atomics are
-  //      complete at L2 after the barrier and this workgroup has not read the
-  //      bitmap before, so plain loads see them.
-  constexpr int kWpt = 32;                        // bitmap words held per thread and round
-  const int64_t W = (nv + 31) / 32;
-  const int64_t wpt = (W + 255) / 256;
-  const int64_t w0 = wpt * threadIdx.x;
-  uint32_t words[kWpt];
+  // ---- emit ascending block ids
+  const int64_t wpt = (W + NT - 1) / NT;
+  const int64_t w0 = wpt * tid;
   uint32_t cnt = 0;
-  for (int64_t rb = 0; rb < wpt; rb += kWpt) {
-#pragma unroll
-    for (int i = 0; i < kWpt; ++i) {
-      const int64_t wi = w0 + rb + i;
-      words[i] = (rb + i < wpt && wi < W) ? bm[wi] : 0u;
-      cnt += __popc(words[i]);
-    }
+  for (int64_t i = 0; i < wpt; ++i) {
+    const int64_t wi = w0 + i;
+    if (wi < W) cnt += __popc(ld_agent(bm + wi));
   }
   uint32_t total;
-  uint32_t o = block_excl_scan(cnt, &total, sh);
+  uint32_t o = block_scan_nt<NT>(cnt, &total, sh);
   int32_t* irow = idx + (int64_t)(out_row0 + qrow) * k;
   float* srow_out = score ? score + (int64_t)(out_row0 + qrow) * k : nullptr;
-  for (int64_t rb = 0; rb < wpt; rb += kWpt) {
-    if (wpt > kWpt) {                             // long rows: load the round again
-#pragma unroll
-      for (int i = 0; i < kWpt; ++i) {
-        const int64_t wi = w0 + rb + i;
-        words[i] = (rb + i < wpt && wi < W) ? bm[wi] : 0u;
+  for (int64_t i = 0; i < wpt; ++i) {
+    const int64_t wi = w0 + i;
+    if (wi >= W) break;
+    uint32_t word = ld_agent(bm + wi);
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      word &= word - 1;
+      const uint32_t b = (uint32_t)(wi * 32 + bit);
+      if (o < (uint32_t)k) {
+        irow[o] = (int32_t)b;
+        if (srow_out) srow_out[o] = srow[b];
       }
-    }
-#pragma unroll
-    for (int i = 0; i < kWpt; ++i) {
-      uint32_t word = words[i];
-      while (word) {
-        const int bit = __ffs(word) - 1;
-        word &= word - 1;
-        const uint32_t b = (uint32_t)((w0 + rb + i) * 32 + bit);
-        if (o < (uint32_t)k) {
-          irow[o] = (int32_t)b;
-          if (srow_out) srow_out[o] = srow[b];
-        }
-        ++o;
-      }
+      ++o;
     }
   }
-  for (int i = (int)total + threadIdx.x; i < k; i += 256) {
+  for (int i = (int)total + tid; i < k; i += NT) {
     irow[i] = -1;
     if (srow_out) srow_out[i] = 0.f;
   }
-  // clear this query's counters and histogram for the next pass
-  uint32_t* gh = ws.hist + (int64_t)qrow * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256) gh[i] = 0;
-  if (threadIdx.x < kStateInts) st[threadIdx.x] = 0;
+  if (tid < kStateInts) st[tid] = 0;
+}
+
+// Long rows: mark the blocks of one 2048-block chunk above the threshold bin
+// (found by idx_topk_kernel mode 1) and append the ones inside it.
+__global__ __launch_bounds__(256) void idx_select_kernel(IdxWs ws) {
+  const int qrow = blockIdx.y, chunk = blockIdx.x;
+  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
+  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const int64_t b_begin = (int64_t)chunk * kSelCH;
+  constexpr int kPer = kSelCH / 256;
+  float sc[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) sc[u] = srow[b_begin + 256 * u + threadIdx.x];   // within R
+  const int64_t nv = st[5];
+  const int thr = st[2];
+  uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
+  uint64_t* cand = ws.cand + (int64_t)qrow * ws.R + b_begin;   // this chunk's region
+  __shared__ uint32_t s_cnt;
+  if (threadIdx.x == 0) s_cnt = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t b_end = nv < b_begin + kSelCH ? nv : b_begin + kSelCH;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t base = b_begin + 256 * u;
+    const int64_t b = base + threadIdx.x;
+    const bool valid = b < b_end;
+    const uint32_t key = order_key(sc[u]);
+    const int bin = (int)(key >> 20);
+    const bool sel = valid && (thr < 0 || bin > thr);
+    const bool cnd = valid && thr >= 0 && bin == thr;
+    const uint64_t cmask = __ballot(cnd);
+    if (cmask) {
+      const int leader = __ffsll((unsigned long long)cmask) - 1;
+      uint32_t cbase = 0;
+      if (lane == leader) cbase = atomicAdd(&s_cnt, (uint32_t)__popcll(cmask));
+      cbase = __shfl(cbase, leader);
+      if (cnd)
+        cand[cbase + __popcll(cmask & ((1ull << lane) - 1))] =
+            ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)b);
+    }
+    const uint64_t mask = __ballot(sel);
+    const int64_t wb = base + 64 * wv;
+    if (lane == 0 && wb < b_end) {
+      bm[wb >> 5] = (uint32_t)mask;
+      if (wb + 32 < b_end) bm[(wb >> 5) + 1] = (uint32_t)(mask >> 32);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) ws.ccount[(int64_t)qrow * (ws.R / kSelCH) + chunk] = (int32_t)s_cnt;
 }
 
 // ---------------------------------------------------------------- host launcher
 
-size_t indexer_zero_bytes(int n_q, bool span) {
-  return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q);
+size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span) {
+  return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q, row_cap(max_nvis));
+}
+
+constexpr int64_t kFusedMaxBlocks = 65536;   // longer rows: threshold / select / refine
+
+// Top-k selection from the scores and histogram in the workspace.  Rows up to
+// kFusedMaxBlocks: one workgroup per query does everything (bitmap and
+// candidates in LDS).  Longer rows: the threshold per query, a multi-workgroup
+// pass that marks the bitmap, then one workgroup per query refines and emits.
+static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
+                        int out_row0, hipStream_t s) {
+  const int64_t W = ws.R / 32;
+  const int cand = nt == 1024 ? 2048 : 1024;
+  if (ws.R <= kFusedMaxBlocks) {
+    const int bm_words = (int)W;
+    const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
+    if (nt == 1024)
+      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+    else
+      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+    return;
+  }
+  idx_topk_kernel<256><<<nq, 256, 0, s>>>(k, ws, idx, score, out_row0, 0, 0, 1);
+  idx_select_kernel<<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
+  const size_t lds = (size_t)2 * cand * sizeof(uint64_t);
+  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
@@ -568,17 +742,15 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
-  int64_t R = ((nv_max + kSelCH - 1) / kSelCH) * kSelCH;
-  if (R < kSelCH) R = kSelCH;
+  const int64_t R = row_cap(nv_max);
   const unsigned n_chunks = (unsigned)(R / kCH);
-  const unsigned n_sel = (unsigned)(R / kSelCH);
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
   if (!ws_head_zeroed) {
     // counters and histograms start at zero whatever the workspace held before
     const int nq_ws = span ? (q.n < kSpanQC ? q.n : kSpanQC) : q.n;
-    const int64_t n16 = (int64_t)(zeroed_bytes(nq_ws) / 16);
+    const int64_t n16 = (int64_t)(zeroed_bytes(nq_ws, R) / 16);
     unsigned blocks = (unsigned)((n16 + 255) / 256);
     fill_zero_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>((uint4*)wsp, n16);
   }
@@ -590,8 +762,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                                                           ws, fault);
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    idx_select_kernel<<<dim3(n_sel, q.n), 256, 0, s>>>(k, ws);
-    idx_finalize_kernel<<<q.n, 256, 0, s>>>(k, ws, idx, score, 0);
+    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
   }
   const int QC = q.n < kSpanQC ? q.n : kSpanQC;
@@ -602,8 +773,6 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     int64_t nv_hi = host_nvis(q.span_pos0 + q0 + nq - 1, m, n_win);
     unsigned chunks_here = (unsigned)((nv_hi + kCH - 1) / kCH);
     if (chunks_here < 1) chunks_here = 1;
-    unsigned sel_here = (unsigned)((nv_hi + kSelCH - 1) / kSelCH);
-    if (sel_here < 1) sel_here = 1;
     int64_t tiles = (nv_hi + 15) / 16;
     unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
     if (bsplit < 1) bsplit = 1;
@@ -615,8 +784,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     }
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
-    idx_select_kernel<<<dim3(sel_here, nq), 256, 0, s>>>(k, ws);
-    idx_finalize_kernel<<<nq, 256, 0, s>>>(k, ws, idx, score, q0);
+    launch_topk(256, nq, k, ws, idx, score, q0, s);
   }
   return hipGetLastError();
 }

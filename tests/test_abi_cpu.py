@@ -77,6 +77,10 @@ def test_validation_rejects_before_any_launch():
     assert lib.hsa_hca_attn(C.byref(qb), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -1
     # unknown output dtype
     assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 1, None, f, 1 << 30, None) == -1
+    # non-positive or non-finite logit scale
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, bad, f, 0, None, f, 1 << 30, None) == -1
+    assert b"scale" in lib.hsa_last_error()
     # CSA without idx
     assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, 0, None, f, 1 << 30, None) == -1
 
