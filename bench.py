@@ -208,6 +208,51 @@ def committed_traffic(kernel, workload, src_hash):
     return t.get("bytes_per_launch")
 
 
+def _pmc_per_dispatch(path, counter, kernel_regex):
+    """Mean value of one rocprofv3 counter per dispatch of the kernels whose
+    name matches kernel_regex (a --pmc run written with --output-format csv)."""
+    import csv
+    import re
+    rx = re.compile(kernel_regex)
+    per = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter or not rx.search(row.get("Kernel_Name", "")):
+                continue
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {kernel_regex!r}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(args):
+    """HBM-side bytes per launch of a kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for an elementwise copy of a known 1 GiB
+    (bench.py --calibrate-copy).  Writes profiles/traffic_<kernel>_<workload>.json;
+    the benchmark reports it while the kernel's source is unchanged."""
+    kernel, workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.traffic_summary
+    fk, nf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    wk, nw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    cf, _ = _pmc_per_dispatch(cfetch_csv, "FETCH_SIZE", "elementwise")
+    cw, _ = _pmc_per_dispatch(cwrite_csv, "WRITE_SIZE", "elementwise")
+    kib = float(1 << 20)   # the copy reads and writes 1 GiB
+    f_scale, w_scale = kib / cf, kib / cw
+    out = {"kernel": kernel, "workload": workload,
+           "source_hash": source_hash("indexer.hip", "common.h") if kernel.startswith("idx_")
+           else source_hash("attention.hip", "common.h"),
+           "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+           "dispatches": [nf, nw],
+           "copy_calibration": {"fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                                "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024))}
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 # ----------------------------------------------------------------------------- workloads
 
 def bench_csa_decode(args, w):
@@ -525,7 +570,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=6,
+                    metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                             "COPY_WRITE_CSV"),
+                    help="(no GPU) turn rocprofv3 --pmc counter files into HBM bytes per launch")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a "
                                    "design note only", "n_gpus": args.gpus}))
@@ -533,10 +585,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes": 1 << 30}))
         return

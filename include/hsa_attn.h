@@ -226,14 +226,17 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Optional kernel timing (tracing).  While enabled for a kernel, every launch
- * of it is bracketed by HIP events recorded on its stream; read returns the
+ * of it is timed with a pair of HIP events on its stream; read returns the
  * summed elapsed milliseconds and the number of launches since the previous
- * read (synchronising on the recorded events).  For eager execution only: do
- * not enable it while capturing a graph. */
-#define HSA_K_INDEXER_SCAN  0   /* decode: score scan + first histogram */
-#define HSA_K_INDEXER_GEMM  1   /* prefill: MFMA score GEMM */
-#define HSA_K_INDEXER_SEL   2   /* histogram / select / refine / emit */
-#define HSA_K_ATTN          3   /* gather + online-softmax attention */
+ * read (synchronising on the events).  Single kernels (SCAN, GEMM, ATTN) hand
+ * the pair to their own dispatch (hipExtLaunchKernelGGL), so the time is the
+ * kernel's execution alone; SEL and COMPRESS bracket their launch sequence
+ * with recorded events.  For eager execution only: do not enable it while
+ * capturing a graph. */
+#define HSA_K_INDEXER_SCAN  0   /* decode: score scan + first histogram (one kernel) */
+#define HSA_K_INDEXER_GEMM  1   /* prefill: MFMA score GEMM (one kernel per query chunk) */
+#define HSA_K_INDEXER_SEL   2   /* histogram / select / refine / emit (several kernels) */
+#define HSA_K_ATTN          3   /* gather + online-softmax attention (one kernel; no merge) */
 #define HSA_K_COMPRESS      4   /* block pooling */
 #define HSA_K_COUNT         5
 hsa_status hsa_kernel_timing(int32_t kernel_id, int32_t enable);

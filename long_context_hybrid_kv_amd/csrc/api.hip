@@ -35,7 +35,8 @@ struct TimerState {
 static TimerState g_timers[HSA_K_COUNT];
 static std::mutex g_timer_mu;
 
-KernelTimer::KernelTimer(int id, hipStream_t s) : id_(id), s_(s), slot_(nullptr) {
+KernelTimer::KernelTimer(int id, hipStream_t s, bool ext)
+    : id_(id), s_(s), slot_(nullptr), ext_(ext) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   TimerState& t = g_timers[id];
   if (!t.on) return;
@@ -47,11 +48,19 @@ KernelTimer::KernelTimer(int id, hipStream_t s) : id_(id), s_(s), slot_(nullptr)
   }
   auto* pr = &t.ev[t.used++];
   slot_ = pr;
-  (void)hipEventRecord(pr->first, s);
+  if (!ext_) (void)hipEventRecord(pr->first, s);
 }
 
 KernelTimer::~KernelTimer() {
-  if (slot_) (void)hipEventRecord(((std::pair<hipEvent_t, hipEvent_t>*)slot_)->second, s_);
+  if (slot_ && !ext_) (void)hipEventRecord(((std::pair<hipEvent_t, hipEvent_t>*)slot_)->second, s_);
+}
+
+hipEvent_t KernelTimer::start() const {
+  return ((std::pair<hipEvent_t, hipEvent_t>*)slot_)->first;
+}
+
+hipEvent_t KernelTimer::stop() const {
+  return ((std::pair<hipEvent_t, hipEvent_t>*)slot_)->second;
 }
 
 static thread_local std::string g_err;

@@ -514,18 +514,17 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   int64_t n_blocks = (int64_t)q.n * p.n_hg * p.n_splits;
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
-  KernelTimer kt(HSA_K_ATTN, s);
   const bool f8 = kc.dtype == HSA_FP8_E4M3;
-  if (p.nw == 4) {
-    if (f8) attn_kernel<4, true><<<(unsigned)n_blocks, 256, 0, s>>>(a);
-    else attn_kernel<4, false><<<(unsigned)n_blocks, 256, 0, s>>>(a);
-  } else if (p.nw == 2) {
-    if (f8) attn_kernel<2, true><<<(unsigned)n_blocks, 128, 0, s>>>(a);
-    else attn_kernel<2, false><<<(unsigned)n_blocks, 128, 0, s>>>(a);
-  } else {
-    if (f8) attn_kernel<1, true><<<(unsigned)n_blocks, 64, 0, s>>>(a);
-    else attn_kernel<1, false><<<(unsigned)n_blocks, 64, 0, s>>>(a);
-  }
+  const dim3 grid((unsigned)n_blocks);
+  if (p.nw == 4)
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256), 0,
+                 s, a);
+  else if (p.nw == 2)
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true> : attn_kernel<2, false>, grid, dim3(128), 0,
+                 s, a);
+  else
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true> : attn_kernel<1, false>, grid, dim3(64), 0,
+                 s, a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
                                                             O, a.o_f32, lse);

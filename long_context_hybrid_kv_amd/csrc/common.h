@@ -1,6 +1,7 @@
 // Internal helpers shared by the gfx950 kernels of libhsa_attn.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "hsa_attn.h"
@@ -159,13 +160,31 @@ inline Queries to_dev(const hsa_queries& q) {
 int* fault_word();   // device pointer of the current device's fault word
 
 // Records start/stop events around a launch when timing is enabled for `id`.
+// With ext = true no events are recorded by the timer itself: the single
+// kernel is launched by timed_launch with the pair handed to the dispatch,
+// so the events carry that kernel's own start and end times.
 struct KernelTimer {
-  KernelTimer(int id, hipStream_t s);
+  KernelTimer(int id, hipStream_t s, bool ext = false);
   ~KernelTimer();
+  hipEvent_t start() const;
+  hipEvent_t stop() const;
   int id_;
   hipStream_t s_;
   void* slot_;
+  bool ext_;
 };
+
+// Launch one kernel; when timing is on for `id`, its dispatch timestamps go
+// into the timer's event pair.
+template <typename... KA, typename... A>
+inline void timed_launch(int id, void (*kernel)(KA...), dim3 grid, dim3 block, unsigned lds,
+                         hipStream_t s, A... args) {
+  KernelTimer kt(id, s, true);
+  if (kt.slot_)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, kt.start(), kt.stop(), 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, hipStream_t s);
 hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,

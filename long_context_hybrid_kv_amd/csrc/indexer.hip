@@ -756,11 +756,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   }
   if (!span) {
     IdxWs ws = carve(wsp, q.n, R);
-    {
-      KernelTimer kt(HSA_K_INDEXER_SCAN, s);
-      idx_scan_kernel<<<dim3(n_chunks, q.n), 256, 0, s>>>(Qd, (const u16*)qI, w, kc, m, n_win, k,
-                                                          ws, fault);
-    }
+    timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel, dim3(n_chunks, q.n), dim3(256), 0, s, Qd,
+                 (const u16*)qI, w, kc, m, n_win, k, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     launch_topk(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
@@ -777,11 +774,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
     if (bsplit < 1) bsplit = 1;
     if (bsplit > 64) bsplit = 64;
-    {
-      KernelTimer kt(HSA_K_INDEXER_GEMM, s);
-      idx_gemm_kernel<<<dim3((nq + 15) / 16, bsplit), 256, 0, s>>>(Qd, q0, nq, (const u16*)qI, w,
-                                                                 kc, m, n_win, ws, fault);
-    }
+    timed_launch(HSA_K_INDEXER_GEMM, idx_gemm_kernel, dim3((nq + 15) / 16, bsplit), dim3(256), 0,
+                 s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
     launch_topk(256, nq, k, ws, idx, score, q0, s);
