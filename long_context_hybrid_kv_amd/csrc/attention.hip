@@ -21,6 +21,8 @@
 // which keeps the output error well inside what the bf16 output store adds.
 // Long decode rows are split over workgroups and merged through (max, sum,
 // partial O) in the workspace.
+#include <type_traits>
+
 #include "common.h"
 
 namespace hsa {
@@ -75,11 +77,41 @@ __device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_
   if (pv >= 0) *rv = pv * kPage + (int)(b & 63);
 }
 
+// 256 bytes of zeros: the row read for entries past the end of a query's list
+__device__ __align__(16) uint4 g_zero_row[16];
+
+// bf16 caches: the address of entry ge's K and V rows (window row, pool row, or
+// the zero row), so that a chunk's gathers are one load per 16-byte piece.
+__device__ __forceinline__ void resolve_ptr(const AttnArgs& a, int qi, int r, int64_t s0, int n_w,
+                                            int E, int64_t nv, int ge, const uint8_t** pk,
+                                            const uint8_t** pv) {
+  const uint8_t* zero = (const uint8_t*)g_zero_row;
+  if (ge < n_w) {
+    const int64_t p = s0 + ge;
+    *pk = a.wk.data + ((int64_t)r * a.wk.capacity + p % a.wk.capacity) * (kD * 2);
+    *pv = a.wv.data + ((int64_t)r * a.wv.capacity + p % a.wv.capacity) * (kD * 2);
+    return;
+  }
+  *pk = *pv = zero;
+  if (ge >= E) return;
+  const int j = ge - n_w;
+  const int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
+  if (b < 0 || b >= nv) {
+    atomicOr(a.fault, HSA_FAULT_INDEX);
+    return;
+  }
+  const int pgk = a.kc.page_of(r, b, a.fault), pgv = a.vc.page_of(r, b, a.fault);
+  if (pgk >= 0) *pk = a.kc.data + ((int64_t)pgk * kPage + (b & 63)) * (kD * 2);
+  if (pgv >= 0) *pv = a.vc.data + ((int64_t)pgv * kPage + (b & 63)) * (kD * 2);
+}
+
 // Raw 16 bytes (bf16) or 8 bytes (fp8 codes, in .x/.y) of column group cg of a
 // row.  Branch-free: both the window row and the pool row are loaded from
 // always-valid addresses (row 0 stands in for the one not used) and the right
 // one is selected afterwards, so the loads of a chunk stay in flight together
-// instead of waiting at divergent branch joins.
+// instead of waiting at divergent branch joins (measured: a variant that
+// issues one load on chunks that lie wholly in the window or the pool, behind
+// a chunk-uniform branch, is 10-30% slower).
 template <bool F8>
 __device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, int row, int cg) {
   const bool pool = row >= 0, win = row <= -2;
@@ -116,6 +148,19 @@ __device__ __forceinline__ void fp8x8_to_f32(uint32_t lo, uint32_t hi, float f[8
   f32x2v d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
   f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
 }
+
+// 16 bytes from a global-memory address held as an integer (a global, not a
+// flat, load: flat loads also count against the LDS wait counter, which would
+// make every LDS wait in the chunk loop wait for the next chunk's gathers too)
+__device__ __forceinline__ uint4 gload16(uintptr_t addr) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 2^x with the hardware instruction alone (results below 2^-126 flush to zero,
+// far below what the fp16 probabilities can hold)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // two floats -> packed fp16, round to nearest even (one v_cvt_pk_f16_f32)
 __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
@@ -193,7 +238,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
   const int n_c = a.k > 0 ? (int)(nv < a.k ? nv : a.k) : (int)nv;
-  const int E = n_w + n_c;
+  // E is the same in every lane; saying so keeps the chunk loop's conditions
+  // (last-chunk masking, loop bounds) scalar branches instead of selects
+  const int E = __builtin_amdgcn_readfirstlane(n_w + n_c);
   const int n_chunks = (E + 63) / 64;
   const int c_lo = split * a.cps;
   const int c_hi = c_lo + a.cps < n_chunks ? c_lo + a.cps : n_chunks;
@@ -201,12 +248,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __shared__ __align__(16) u16 Ks[64][136];
   __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
   __shared__ float ksc[64];
-  __shared__ int rowk[kMaxCps * 64], rowv[kMaxCps * 64];
+  // fp8: 32-bit row ids (pool rows hold fp8 codes, window rows bf16);
+  // bf16: row addresses
+  typedef typename std::conditional<F8, int, const uint8_t*>::type RowT;
+  __shared__ RowT rowk[kMaxCps * 64], rowv[kMaxCps * 64];
 
-  // ---- resolve the row ids of every entry of this split once
+  // ---- resolve the rows of every entry of this split once
   const int e_base = c_lo * 64;
   const int n_ent = (c_hi > c_lo) ? (c_hi - c_lo) * 64 : 0;
-  for (int j = tid; j < n_ent; j += NT) resolve(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+  for (int j = tid; j < n_ent; j += NT) {
+    if constexpr (F8)
+      resolve(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+    else
+      resolve_ptr(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+  }
 
   const int head = hg * 16 * NW + wave * 16 + col;
   bf16x8 qb[4];
@@ -231,13 +286,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
-      krow[i] = rowk[lo + ek];
-      kraw[i] = load_piece<F8>(a.kc, a.wk, krow[i], cgk);
-      kscl[i] = row_scale<F8>(a.kc, krow[i]);
       const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
-      vrow[i] = rowv[lo + ev];
-      vraw[i] = load_piece<F8>(a.vc, a.wv, vrow[i], cgv);
-      vscl[i] = row_scale<F8>(a.vc, vrow[i]);
+      if constexpr (F8) {
+        krow[i] = rowk[lo + ek];
+        kraw[i] = load_piece<F8>(a.kc, a.wk, krow[i], cgk);
+        kscl[i] = row_scale<F8>(a.kc, krow[i]);
+        vrow[i] = rowv[lo + ev];
+        vraw[i] = load_piece<F8>(a.vc, a.wv, vrow[i], cgv);
+        vscl[i] = row_scale<F8>(a.vc, vrow[i]);
+      } else {
+        krow[i] = vrow[i] = 0;
+        kscl[i] = vscl[i] = 1.f;
+        kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
+        vraw[i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
+      }
     }
   };
 
@@ -292,38 +354,38 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     // log2-domain logit = acc * c, c = scale*log2(e) (times the page scale of
     // fp8 keys).  With one positive c the running max is taken on the raw
     // accumulators; entries past the end exist only in the last chunk.
-    const bool full = e0 + 64 <= E;
-    float mx = -INFINITY;
-    if (!F8) {
+    if (F8) {
 #pragma unroll
       for (int et = 0; et < 4; ++et)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!full && e0 + et * 16 + 4 * g + i >= E) sacc[et][i] = -INFINITY;
-          mx = fmaxf(mx, sacc[et][i]);
-        }
-      mx *= a.scale_log2;
-    } else {
-#pragma unroll
-      for (int et = 0; et < 4; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = et * 16 + 4 * g + i;
-          float v = sacc[et][i] * (a.scale_log2 * ksc[e]);
-          if (!full && e0 + e >= E) v = -INFINITY;
-          sacc[et][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) sacc[et][i] *= a.scale_log2 * ksc[et * 16 + 4 * g + i];
     }
+    if (__builtin_expect(e0 + 64 > E, 0)) {   // the last chunk only (E is uniform)
+#pragma unroll
+      for (int et = 0; et < 4; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e0 + et * 16 + 4 * g + i >= E) sacc[et][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[et][i]);
+    if (!F8) mx *= a.scale_log2;
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_i, mx);
-    const float alpha = exp2f(m_i - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
     m_i = m_new;
     const float cst = F8 ? 1.f : a.scale_log2;
+    // the running max rarely grows once a row is under way: skip the rescale
+    // when no lane of the wave needs it (alpha is exactly 1 then)
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
-    osum *= alpha;
+      for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+      osum *= alpha;
+    }
 
     // ---- O^T += V^T P^T, two k-steps of 32 entries.  P is rounded to fp16
     // once; an extra tile of ones in place of V^T rows accumulates the row
@@ -333,10 +395,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       uint32_t pw[4];
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        pw[i / 2] = pack_f16(exp2f(__builtin_fmaf(sacc[2 * j][i], cst, -m_new)),
-                             exp2f(__builtin_fmaf(sacc[2 * j][i + 1], cst, -m_new)));
-        pw[2 + i / 2] = pack_f16(exp2f(__builtin_fmaf(sacc[2 * j + 1][i], cst, -m_new)),
-                                 exp2f(__builtin_fmaf(sacc[2 * j + 1][i + 1], cst, -m_new)));
+        pw[i / 2] = pack_f16(ex2(__builtin_fmaf(sacc[2 * j][i], cst, -m_new)),
+                             ex2(__builtin_fmaf(sacc[2 * j][i + 1], cst, -m_new)));
+        pw[2 + i / 2] = pack_f16(ex2(__builtin_fmaf(sacc[2 * j + 1][i], cst, -m_new)),
+                                 ex2(__builtin_fmaf(sacc[2 * j + 1][i + 1], cst, -m_new)));
       }
       const f16x8 pb = __builtin_bit_cast(f16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll

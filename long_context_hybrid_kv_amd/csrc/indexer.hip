@@ -211,27 +211,49 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
                                                        int m, int n_win, int k, IdxWs ws,
                                                        int* fault) {
   const int qrow = blockIdx.y, chunk = blockIdx.x;
-  int r;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  // Each wave streams 128 consecutive blocks = two whole pages.  The two page
+  // ids depend only on the request, so they are loaded alongside the query's
+  // position and entry count instead of after them: the key loads wait for one
+  // round trip, not three.
+  const int r = Q.pos ? (Q.req ? Q.req[qrow] : qrow) : Q.span_req;
+  const int64_t b_begin = (int64_t)chunk * kCH;
+  const int64_t w0b = b_begin + (int64_t)wv * (kCH / 4);
+  const int lp0 = (int)(w0b >> 6);
+  int pid[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    pid[j] = lp0 + j < kic.pages_per_req
+                 ? kic.page_table[(int64_t)r * kic.pages_per_req + lp0 + j]
+                 : -1;
+  int rq;
   int64_t t;
-  Q.get(qrow, &r, &t, fault);
-  int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
-                          chunk == 0 && threadIdx.x == 0);
+  Q.get(qrow, &rq, &t, fault);
+  const int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
+                                chunk == 0 && threadIdx.x == 0);
   const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
   if (chunk >= n_active) return;
   if (chunk == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
-
-  __shared__ uint32_t lhist[kBins];
-  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
-  const int64_t b_begin = (int64_t)chunk * kCH;
   const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
-  // physical pages of the chunk's 8 logical pages, resolved once
-  __shared__ int pg[kCH / kPage];
-  if (threadIdx.x < kCH / kPage) {
-    int64_t e = b_begin + (int64_t)threadIdx.x * kPage;
-    pg[threadIdx.x] = e < b_end ? kic.page_of(r, e, fault) : -1;
+
+  // all 16 key loads of a lane are issued before anything waits on them;
+  // branch-free: blocks out of range (or on a bad page) read row 0 of page 0
+  constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave
+  bf16x8 b0[NT], b1[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int64_t b = w0b + 16 * u + row;
+    const int pg = pid[u >> 2];
+    const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
+    const bf16x8* kr = (const bf16x8*)kic.row(ok ? pg : 0, ok ? b : 0);
+    b0[u] = __builtin_nontemporal_load(kr + g);
+    b1[u] = __builtin_nontemporal_load(kr + 4 + g);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (w0b + 64 * j < b_end && (unsigned)pid[j] >= (unsigned)kic.n_pages)
+        atomicOr(fault, HSA_FAULT_PAGE);
   }
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
@@ -241,23 +263,12 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
-  float* srow = ws.scores + (int64_t)qrow * ws.R;
+
+  // the LDS histogram is cleared while the keys are in flight
+  __shared__ uint32_t lhist[kBins];
+  __shared__ float lsc[kCH];
+  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
   __syncthreads();
-  // each wave streams 128 consecutive blocks (8 tiles of 16): all 16 loads of a
-  // lane are issued before the first MFMA
-  constexpr int NT = kCH / 4 / 16;   // tiles per wave
-  const int64_t w0b = b_begin + (int64_t)wv * (kCH / 4);
-  bf16x8 b0[NT], b1[NT];
-  // branch-free: out-of-range tiles read row 0 of page 0 and are masked later
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int64_t b = w0b + 16 * u + row;
-    const int pgi = pg[(int)((w0b - b_begin + 16 * u) >> 6)];
-    const bool ok = b < b_end && pgi >= 0;
-    const bf16x8* kr = (const bf16x8*)kic.row(ok ? pgi : 0, ok ? b : 0);
-    b0[u] = __builtin_nontemporal_load(kr + g);
-    b1[u] = __builtin_nontemporal_load(kr + 4 + g);
-  }
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -265,12 +276,17 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc, 0, 0, 0);
     const int64_t b = w0b + 16 * u + row;
     if (g == 0 && b < b_end) {
-      float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
-                 w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
-      srow[b] = sc;
+      const float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
+                       w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+      lsc[b - b_begin] = sc;
       atomicAdd(&lhist[order_key(sc) >> 20], 1u);
     }
   }
+  __syncthreads();
+  // the chunk's scores leave in one coalesced run
+  float* srow = ws.scores + (int64_t)qrow * ws.R;
+  for (int i = threadIdx.x; i < kCH; i += 256)
+    if (b_begin + i < b_end) srow[b_begin + i] = lsc[i];
   flush_histogram(lhist, ws, qrow, chunk);
 }
 
