@@ -368,33 +368,38 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
 }
 
 // prefill: first-level histogram over the stored scores
+// Prefill: histogram of the fp32 scores of one query, kHistSpan blocks per
+// workgroup (the 4096-bin LDS histogram is cleared and flushed once per
+// kHistSpan scores rather than once per scan chunk).
+constexpr int kHistSpan = 8192;
+
 __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, const Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
                                                        int* fault) {
-  const int qrow = blockIdx.y, chunk = blockIdx.x;
+  const int qrow = blockIdx.y, slice = blockIdx.x;
   const int r = Q.span_req;
   int64_t t = Q.span_pos0 + q_base + qrow;
   int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault, false);
-  const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
-  if (chunk >= n_active) return;
-  if (chunk == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
-  __shared__ uint32_t lhist[kBins];
-  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
-  __syncthreads();
+  const int64_t b_begin = (int64_t)slice * kHistSpan;
+  if (b_begin > 0 && b_begin >= nv) return;
+  if (slice == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
+  const int64_t b_end = nv < b_begin + kHistSpan ? nv : b_begin + kHistSpan;
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
-  const int64_t b_begin = (int64_t)chunk * kCH;
-  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
-  constexpr int kPer = kCH / 256;
+  constexpr int kPer = kHistSpan / 256;
+  // all loads in flight before the histogram is cleared and filled
   float sc[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int64_t b = b_begin + 256 * u + threadIdx.x;
     sc[u] = b < b_end ? srow[b] : 0.f;
   }
+  __shared__ uint32_t lhist[kBins];
+  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (b_begin + 256 * u + threadIdx.x < b_end) atomicAdd(&lhist[order_key(sc[u]) >> 20], 1u);
-  flush_histogram(lhist, ws, qrow, chunk);
+  flush_histogram(lhist, ws, qrow, slice);
 }
 
 // ---------------------------------------------------------------- select, refine, emit
@@ -784,8 +789,6 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const int nq = q.n - q0 < QC ? q.n - q0 : QC;
     // chunk-local maximum of the visible blocks bounds the work of this pass
     int64_t nv_hi = host_nvis(q.span_pos0 + q0 + nq - 1, m, n_win);
-    unsigned chunks_here = (unsigned)((nv_hi + kCH - 1) / kCH);
-    if (chunks_here < 1) chunks_here = 1;
     int64_t tiles = (nv_hi + 15) / 16;
     unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
     if (bsplit < 1) bsplit = 1;
@@ -793,7 +796,9 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     timed_launch(HSA_K_INDEXER_GEMM, idx_gemm_kernel, dim3((nq + 15) / 16, bsplit), dim3(256), 0,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    idx_hist_kernel<<<dim3(chunks_here, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+    const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
+    idx_hist_kernel<<<dim3(slices < 1 ? 1 : slices, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k,
+                                                                      ws, fault);
     launch_topk(256, nq, k, ws, idx, score, q0, s);
   }
   return hipGetLastError();
