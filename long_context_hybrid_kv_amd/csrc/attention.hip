@@ -502,6 +502,241 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
   if (d == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
 }
 
+// ---------------------------------------------------------------- prefill HCA: query pairs
+
+// Two consecutive prefill queries t0 and t1 = t0 + 1 of an HCA layer see the
+// same compressed blocks (except possibly the last: n_vis(t0) <= n_vis(t1)) and
+// windows that differ in one token at each end.  One workgroup walks the union
+// of their entries once -- window tokens s(t0)..t1, then blocks 0..n_vis(t1)-1
+// -- and every wave keeps two 16-head tiles, one per query, so each staged
+// chunk and each K / V^T operand read from LDS feeds twice the MFMA work.
+// Entries outside one query's own set are masked for that query only (in the
+// few chunks that hold such entries).  bf16 caches, 64 heads per workgroup.
+__global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
+  constexpr int NT = 256, PPT = 4;
+  unsigned bid = blockIdx.x;
+  {
+    unsigned per = gridDim.x / 8;
+    bid = (bid % 8) * per + bid / 8;
+  }
+  const int hg = bid % a.n_hg;
+  const int q0 = 2 * (int)(bid / a.n_hg);
+  if (q0 >= a.n_q) return;
+  const bool has1 = q0 + 1 < a.n_q;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  int r;
+  int64_t t0;
+  a.Q.get(q0, &r, &t0, a.fault);
+  const int64_t t1 = has1 ? t0 + 1 : t0;
+  const int64_t s0 = window_start(t0, a.n_win), s1 = window_start(t1, a.n_win);
+  const int n_wu = (int)(t1 - s0 + 1);
+  int64_t nv0 = n_visible(t0, a.m, a.n_win), nv1 = n_visible(t1, a.m, a.n_win);
+  {
+    int64_t ne = a.kc.n_entries[r];
+    const int64_t ne2 = a.vc.n_entries[r];
+    ne = ne < ne2 ? ne : ne2;
+    ne = ne < 0 ? 0 : ne;
+    if (nv1 > ne) {
+      if (hg == 0 && tid == 0) atomicOr(a.fault, HSA_FAULT_ENTRIES);
+      nv1 = ne;
+      nv0 = nv0 < ne ? nv0 : ne;
+    }
+  }
+  const int E = __builtin_amdgcn_readfirstlane(n_wu + (int)nv1);
+  const int n_chunks = (E + 63) / 64;
+  // tile 0 (t0): window entries 0..whi0, blocks < nv0; tile 1 (t1): window
+  // entries wlo1..n_wu-1, blocks < nv1
+  const int whi0 = (int)(t0 - s0), wlo1 = (int)(s1 - s0);
+  const int end0 = n_wu + (int)nv0;
+
+  __shared__ __align__(16) u16 Ks[64][136];
+  __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
+  __shared__ const uint8_t* rowk[kMaxCps * 64];
+  __shared__ const uint8_t* rowv[kMaxCps * 64];
+  {
+    const uint8_t* zero = (const uint8_t*)g_zero_row;
+    for (int j = tid; j < n_chunks * 64; j += NT) {
+      const uint8_t *pk = zero, *pv = zero;
+      if (j < n_wu) {
+        const int64_t p = s0 + j;
+        pk = a.wk.data + ((int64_t)r * a.wk.capacity + p % a.wk.capacity) * (kD * 2);
+        pv = a.wv.data + ((int64_t)r * a.wv.capacity + p % a.wv.capacity) * (kD * 2);
+      } else if (j < E) {
+        const int64_t b = j - n_wu;
+        const int pgk = a.kc.page_of(r, b, a.fault), pgv = a.vc.page_of(r, b, a.fault);
+        if (pgk >= 0) pk = a.kc.data + ((int64_t)pgk * kPage + (b & 63)) * (kD * 2);
+        if (pgv >= 0) pv = a.vc.data + ((int64_t)pgv * kPage + (b & 63)) * (kD * 2);
+      }
+      rowk[j] = pk;
+      rowv[j] = pv;
+    }
+  }
+  const int head = hg * 64 + wave * 16 + col;
+  bf16x8 qb[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qi = has1 ? q0 + j : q0;
+    const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)qi * a.H + head) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[j][ks] = qp[4 * ks + g];
+  }
+  __syncthreads();
+
+  uint4 kraw[PPT], vraw[PPT];
+  const int vpair = tid & 31;
+  auto issue = [&](int c) {
+    const int lo = c * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      const int ek = p >> 4, cgk = p & 15;
+      const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
+      kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
+      vraw[i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
+    }
+  };
+
+  float m_i[2] = {-1e30f, -1e30f};
+  f32x4 oacc[2][8], osum[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    osum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
+
+  if (n_chunks > 0) issue(0);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int e0 = c * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      *(uint4*)&Ks[p >> 4][(p & 15) * 8] = kraw[i];
+    }
+#pragma unroll
+    for (int j = 0; j < PPT / 2; ++j) {
+      const int cgv = (tid >> 5) + (NT / 32) * j;
+      const uint4 v0 = v_piece_f16(vraw[2 * j], false, 1.f);
+      const uint4 v1 = v_piece_f16(vraw[2 * j + 1], false, 1.f);
+      const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+      uint32_t* vt = (uint32_t*)&Vt[cgv * 8][0] + vpair;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        vt[(2 * q2) * 36] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
+        vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
+      }
+    }
+    __syncthreads();
+    if (c + 1 < n_chunks) issue(c + 1);
+
+    // ---- S^T = K Q^T for both queries; each K operand read once
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      sacc[0][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[1][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
+        sacc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[0][ks], sacc[0][et], 0, 0, 0);
+        sacc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[1][ks], sacc[1][et], 0, 0, 0);
+      }
+    }
+    // ---- masks, only in chunks that hold an entry outside either query's set
+    const bool clean = e0 >= wlo1 && e0 + 64 <= end0 &&
+                       (whi0 == n_wu - 1 || e0 > whi0 + 1 || e0 + 63 < whi0 + 1);
+    if (__builtin_expect(!clean, 0)) {
+#pragma unroll
+      for (int et = 0; et < 4; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = e0 + et * 16 + 4 * g + i;
+          const bool ok0 = e < n_wu ? e <= whi0 : e < end0;
+          const bool ok1 = e < n_wu ? e >= wlo1 : e < E;
+          if (!ok0) sacc[0][et][i] = -INFINITY;
+          if (!ok1) sacc[1][et][i] = -INFINITY;
+        }
+    }
+    // ---- online softmax per query tile, then O^T += V^T P^T with shared V reads
+    uint32_t pw[2][2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int et = 0; et < 4; ++et)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[j][et][i]);
+      mx *= a.scale_log2;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_i[j], mx);
+      const float alpha = ex2(m_i[j] - m_new);
+      m_i[j] = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
+        osum[j] *= alpha;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          pw[j][h][i / 2] = pack_f16(ex2(__builtin_fmaf(sacc[j][2 * h][i], a.scale_log2, -m_new)),
+                                     ex2(__builtin_fmaf(sacc[j][2 * h][i + 1], a.scale_log2, -m_new)));
+          pw[j][h][2 + i / 2] =
+              pack_f16(ex2(__builtin_fmaf(sacc[j][2 * h + 1][i], a.scale_log2, -m_new)),
+                       ex2(__builtin_fmaf(sacc[j][2 * h + 1][i + 1], a.scale_log2, -m_new)));
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f16x8 pb0 = __builtin_bit_cast(f16x8, make_uint4(pw[0][h][0], pw[0][h][1], pw[0][h][2], pw[0][h][3]));
+      const f16x8 pb1 = __builtin_bit_cast(f16x8, make_uint4(pw[1][h][0], pw[1][h][1], pw[1][h][2], pw[1][h][3]));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u16* vr = &Vt[16 * dt + col][0];
+        const uint2 lo = *(const uint2*)(vr + 32 * h + 4 * g);
+        const uint2 hi = *(const uint2*)(vr + 32 * h + 16 + 4 * g);
+        const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb0, oacc[0][dt], 0, 0, 0);
+        oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb1, oacc[1][dt], 0, 0, 0);
+      }
+      osum[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb0, osum[0], 0, 0, 0);
+      osum[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb1, osum[1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds O^T[16dt + 4g + i][head] of each query
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j == 1 && !has1) break;
+    const int qi = q0 + j;
+    const float l = osum[j][0];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t o0 = ((int64_t)qi * a.H + head) * kD;
+    if (a.o_f32) {
+      float* orow = (float*)a.O + o0;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt + 4 * g) = oacc[j][dt] * inv;
+    } else {
+      u16* orow = (u16*)a.O + o0;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)(oacc[j][dt][i] * inv));
+        *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
+    }
+    if (g == 0 && a.lse) a.lse[(int64_t)qi * a.H + head] = (m_i[j] + log2f(l)) * kLn2;
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 struct AttnPlan {
@@ -577,6 +812,17 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
   const bool f8 = kc.dtype == HSA_FP8_E4M3;
+  // prefill of an HCA layer: pairs of consecutive queries share one walk over
+  // their entries (the union of two windows needs n_win + 1 raw tokens)
+  const int64_t need_cap = q.max_pos + 1 < n_win + 1 ? q.max_pos + 1 : n_win + 1;
+  if (span && k == 0 && !f8 && H % 64 == 0 && n_win + 1 + nv_max <= kMaxCps * 64 &&
+      wk.capacity >= need_cap && wv.capacity >= need_cap) {
+    a.n_hg = H / 64;
+    a.n_splits = 1;
+    const int64_t nb = ((int64_t)(q.n + 1) / 2 * a.n_hg + 7) / 8 * 8;
+    timed_launch(HSA_K_ATTN, attn_pair_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)n_blocks);
   if (p.nw == 4)
     timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256), 0,

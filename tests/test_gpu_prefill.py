@@ -196,3 +196,28 @@ def test_bf16_output_is_rounded_fp32_output():
     b, _ = L.hca_attn(q, Q, st["ring_k"], st["ring_v"], wd.n_win, st["kc"], st["vc"], wd.m_hca)
     L.check_device_error()
     assert torch.equal(a.to(torch.bfloat16), b)
+
+
+@pytest.mark.parametrize("H,n_win,m,T_,pos0", [(64, 128, 128, 2049, 0), (128, 64, 16, 1501, 0),
+                                               (64, 128, 4, 1200, 37)])
+def test_hca_prefill_query_pairs(H, n_win, m, T_, pos0):
+    """The paired-query HCA prefill path (H a multiple of 64, bf16): odd query
+    counts (a last query without a partner), spans that start at an odd
+    position, m from 4 to 128, a window shorter than a tile, shuffled pages;
+    every row against the oracle."""
+    w = configs.shrink(configs.PREFILL_4K, H=H, n_win=n_win, T=T_, m_hca=m)
+    inp = gen.prefill_layer(w, "hca")
+    perm = torch.from_numpy(gen.page_permutation(w, "p", max(1, -(-(T_ // m) // 64))))
+    gc = T.compress_layer(inp, "hca", m, page_order=perm)
+    n = T_ - pos0
+    O, lse = L.hca_attn(L.Queries.span(n, pos0), T.dev_bf16(inp["q"][pos0:]), T.tokens(inp["k"]),
+                        T.tokens(inp["v"]), n_win, gc["kc"], gc["vc"], m, with_lse=True,
+                        out_fp32=True)
+    L.check_device_error()
+    oc = _oracle_caches(inp, "hca", m)
+    Ob, lse = T.to_f64(O), lse.cpu().numpy()
+    for i in range(n):
+        t = pos0 + i
+        r = orc.hca_query(t, inp["q"][t], inp["k"], inp["v"], oc["kc"], oc["vc"], m, n_win)
+        assert np.max(np.abs(Ob[i] - r["o"])) <= T.OUT_TOL, t
+        assert np.max(np.abs(lse[i] - r["lse"])) <= T.LSE_TOL, t
