@@ -30,6 +30,7 @@ namespace hsa {
 
 constexpr int kCH = 512;           // blocks per scan workgroup
 constexpr int kSelCH = 2048;       // blocks per select workgroup (multiple of kCH)
+constexpr int kMaxSelChunks = 1024;  // select chunks whose offsets fit in LDS
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
 constexpr int kCoarse = 256;       // groups of 16 bins walked by the threshold search
 constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the workspace)
@@ -440,7 +441,8 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, u
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, int out_row0,
-                                                      int cand_lds, int bm_lds_words, int mode) {
+                                                      int cand_lds, int bm_lds_words, int mode,
+                                                      int clear_hist) {
   constexpr int BPT = kBins / NT;                // histogram bins per thread
   extern __shared__ __align__(16) uint64_t dyn[];
   __shared__ uint32_t sh[NT / 64];
@@ -498,8 +500,9 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
         cum += v[j];
       }
     }
-    // the histogram is consumed: clear it for the next pass
-    for (int sl = 0; sl < ws.hslots; ++sl) {
+    // the histogram is consumed: clear it for the next query chunk of a
+    // prefill (a decode call clears the workspace head before its scan)
+    for (int sl = 0; clear_hist && sl < ws.hslots; ++sl) {
 #pragma unroll
       for (int j = 0; j < BPT / 4; ++j) ((uint4*)(gh + sl * kBins + lo))[j] = make_uint4(0, 0, 0, 0);
     }
@@ -526,14 +529,34 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     const int32_t* cc = ws.ccount + (int64_t)qrow * n_ch;
     const uint64_t* g = ws.cand + (int64_t)qrow * ws.R;
     uint64_t* dstc = cand_in_lds ? ca : ws.cand2 + (int64_t)qrow * ws.R;
+    // chunk offsets by a block scan, then every thread copies whole candidates:
+    // candidate i lies in the chunk c with off[c] <= i < off[c + 1]
+    __shared__ uint32_t coff[kMaxSelChunks + 1];
     uint32_t run = 0;
     for (int c0 = 0; c0 < n_ch; c0 += NT) {
       const int c = c0 + tid;
       const uint32_t cnt = c < n_ch ? (uint32_t)cc[c] : 0u;
       uint32_t tot;
       const uint32_t off = block_scan_nt<NT>(cnt, &tot, sh) + run;
-      for (uint32_t i = 0; i < cnt; ++i) dstc[off + i] = g[(int64_t)c * kSelCH + i];
+      if (n_ch <= kMaxSelChunks) {
+        if (c < n_ch) coff[c] = off;
+      } else {
+        for (uint32_t i = 0; i < cnt; ++i) dstc[off + i] = g[(int64_t)c * kSelCH + i];
+      }
       run += tot;
+      __syncthreads();   // sh is reused by the next round's scan
+    }
+    if (n_ch <= kMaxSelChunks) {
+      if (tid == 0) coff[n_ch] = run;
+      __syncthreads();
+      for (uint32_t i = tid; i < run; i += NT) {
+        int lo = 0, hi = n_ch;        // coff[lo] <= i < coff[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (coff[mid] <= i) lo = mid; else hi = mid;
+        }
+        dstc[i] = g[(int64_t)lo * kSelCH + (i - coff[lo])];
+      }
     }
     if (tid == 0) s_ncand = run;
     __threadfence_block();
@@ -641,32 +664,38 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   __threadfence_block();
   __syncthreads();
 
-  // ---- emit ascending block ids
-  const int64_t wpt = (W + NT - 1) / NT;
-  const int64_t w0 = wpt * tid;
-  uint32_t cnt = 0;
-  for (int64_t i = 0; i < wpt; ++i) {
-    const int64_t wi = w0 + i;
-    if (wi < W) cnt += __popc(ld_agent(bm + wi));
-  }
-  uint32_t total;
-  uint32_t o = block_scan_nt<NT>(cnt, &total, sh);
+  // ---- emit ascending block ids: each thread owns 8 consecutive bitmap words
+  // per round (loaded together); a block scan of their popcounts gives its
+  // output offset
   int32_t* irow = idx + (int64_t)(out_row0 + qrow) * k;
   float* srow_out = score ? score + (int64_t)(out_row0 + qrow) * k : nullptr;
-  for (int64_t i = 0; i < wpt; ++i) {
-    const int64_t wi = w0 + i;
-    if (wi >= W) break;
-    uint32_t word = ld_agent(bm + wi);
-    while (word) {
-      const int bit = __ffs(word) - 1;
-      word &= word - 1;
-      const uint32_t b = (uint32_t)(wi * 32 + bit);
-      if (o < (uint32_t)k) {
-        irow[o] = (int32_t)b;
-        if (srow_out) srow_out[o] = srow[b];
+  uint32_t total = 0;
+  for (int64_t r0 = 0; r0 < W; r0 += (int64_t)NT * 8) {
+    const int64_t w0 = r0 + (int64_t)tid * 8;
+    uint32_t wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wd[i] = w0 + i < W ? ld_agent(bm + w0 + i) : 0u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(wd[i]);
+    uint32_t tot;
+    uint32_t o = block_scan_nt<NT>(cnt, &tot, sh) + total;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t word = wd[i];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        const uint32_t b = (uint32_t)((w0 + i) * 32 + bit);
+        if (o < (uint32_t)k) {
+          irow[o] = (int32_t)b;
+          if (srow_out) srow_out[o] = srow[b];
+        }
+        ++o;
       }
-      ++o;
     }
+    total += tot;
+    __syncthreads();   // sh is reused by the next round's scan
   }
   for (int i = (int)total + tid; i < k; i += NT) {
     irow[i] = -1;
@@ -731,29 +760,32 @@ size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span) {
   return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q, row_cap(max_nvis));
 }
 
-constexpr int64_t kFusedMaxBlocks = 65536;   // longer rows: threshold / select / refine
+constexpr int64_t kFusedMaxBlocks = 16384;   // longer rows: threshold / select / refine
 
 // Top-k selection from the scores and histogram in the workspace.  Rows up to
 // kFusedMaxBlocks: one workgroup per query does everything (bitmap and
 // candidates in LDS).  Longer rows: the threshold per query, a multi-workgroup
 // pass that marks the bitmap, then one workgroup per query refines and emits.
 static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
-                        int out_row0, hipStream_t s) {
+                        int out_row0, bool clear_hist, hipStream_t s) {
   const int64_t W = ws.R / 32;
   const int cand = nt == 1024 ? 2048 : 1024;
   if (ws.R <= kFusedMaxBlocks) {
     const int bm_words = (int)W;
     const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
     if (nt == 1024)
-      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0,
+                                                   clear_hist);
     else
-      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0,
+                                                 clear_hist);
     return;
   }
-  idx_topk_kernel<256><<<nq, 256, 0, s>>>(k, ws, idx, score, out_row0, 0, 0, 1);
+  idx_topk_kernel<1024><<<nq, 1024, 0, s>>>(k, ws, idx, score, out_row0, 0, 0, 1, clear_hist);
   idx_select_kernel<<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
   const size_t lds = (size_t)2 * cand * sizeof(uint64_t);
-  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2);
+  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2,
+                                               clear_hist);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
@@ -780,7 +812,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel, dim3(n_chunks, q.n), dim3(256), 0, s, Qd,
                  (const u16*)qI, w, kc, m, n_win, k, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
+    launch_topk(1024, q.n, k, ws, idx, score, 0, false, s);
     return hipGetLastError();
   }
   const int QC = q.n < kSpanQC ? q.n : kSpanQC;
@@ -799,7 +831,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
     idx_hist_kernel<<<dim3(slices < 1 ? 1 : slices, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k,
                                                                       ws, fault);
-    launch_topk(256, nq, k, ws, idx, score, q0, s);
+    launch_topk(256, nq, k, ws, idx, score, q0, true, s);
   }
   return hipGetLastError();
 }
