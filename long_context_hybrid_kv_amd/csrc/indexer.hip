@@ -760,17 +760,21 @@ size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span) {
   return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q, row_cap(max_nvis));
 }
 
-constexpr int64_t kFusedMaxBlocks = 16384;   // longer rows: threshold / select / refine
+// rows up to these sizes take the one-workgroup-per-query path; longer rows the
+// threshold / select / refine kernels (decode: few queries, so the many-
+// workgroup classification pays off earlier)
+constexpr int64_t kFusedMaxBlocksDecode = 16384;
+constexpr int64_t kFusedMaxBlocksPrefill = 65536;
 
 // Top-k selection from the scores and histogram in the workspace.  Rows up to
-// kFusedMaxBlocks: one workgroup per query does everything (bitmap and
+// the fused-path size: one workgroup per query does everything (bitmap and
 // candidates in LDS).  Longer rows: the threshold per query, a multi-workgroup
 // pass that marks the bitmap, then one workgroup per query refines and emits.
 static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
                         int out_row0, bool clear_hist, hipStream_t s) {
   const int64_t W = ws.R / 32;
   const int cand = nt == 1024 ? 2048 : 1024;
-  if (ws.R <= kFusedMaxBlocks) {
+  if (ws.R <= (nt == 1024 ? kFusedMaxBlocksDecode : kFusedMaxBlocksPrefill)) {
     const int bm_words = (int)W;
     const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
     if (nt == 1024)
