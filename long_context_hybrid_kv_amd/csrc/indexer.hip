@@ -31,6 +31,7 @@ namespace hsa {
 constexpr int kCH = 512;           // blocks per scan workgroup
 constexpr int kSelCH = 2048;       // blocks per select workgroup (multiple of kCH)
 constexpr int kMaxSelChunks = 1024;  // select chunks whose offsets fit in LDS
+constexpr int kGemmMaxPages = 1024;  // pages of a prefill score workgroup resolved in LDS
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
 constexpr int kCoarse = 256;       // groups of 16 bins walked by the threshold search
 constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the workspace)
@@ -343,28 +344,46 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   const int64_t per = (n_tiles + gridDim.y - 1) / gridDim.y;
   const int64_t t_lo = per * blockIdx.y;
   const int64_t t_hi = t_lo + per < n_tiles ? t_lo + per : n_tiles;
-  for (int64_t tile = t_lo + wv; tile < t_hi; tile += 4) {
-    int64_t b = 16 * tile + row;
-    bf16x8 b0 = {}, b1 = {};
-    if (b < nv_max) {
-      int page = kic.page_of(r, b, fault);
-      if (page >= 0) {
-        const bf16x8* kr = (const bf16x8*)kic.row(page, b);
-        b0 = kr[g];
-        b1 = kr[4 + g];
-      }
-    }
+  // physical pages of the workgroup's tile range, resolved once
+  __shared__ int pg[kGemmMaxPages];
+  const int64_t p_lo = (16 * t_lo) >> 6;
+  const int64_t n_pg = t_hi > t_lo ? (((16 * t_hi - 1) >> 6) + 1 - p_lo) : 0;
+  const bool pg_lds = n_pg <= kGemmMaxPages;
+  if (pg_lds)
+    for (int i = threadIdx.x; i < n_pg; i += 256)
+      pg[i] = (p_lo + i) * 64 < nv_max ? kic.page_of(r, (p_lo + i) * 64, fault) : -1;
+  __syncthreads();
+  // branch-free key loads (rows past the end, or on a bad page, read row 0 of
+  // page 0 and are never stored); the next tile's keys load while this one's
+  // scores are computed
+  auto load = [&](int64_t tile, bf16x8& x0, bf16x8& x1) {
+    const int64_t b = 16 * tile + row;
+    int page = -1;
+    if (b < nv_max) page = pg_lds ? pg[(b >> 6) - p_lo] : kic.page_of(r, b, fault);
+    const bool ok = page >= 0;
+    const bf16x8* kr = (const bf16x8*)kic.row(ok ? page : 0, ok ? b : 0);
+    x0 = kr[g];
+    x1 = kr[4 + g];
+  };
+  bf16x8 c0, c1, n0 = {}, n1 = {};
+  int64_t tile = t_lo + wv;
+  if (tile < t_hi) load(tile, c0, c1);
+  for (; tile < t_hi; tile += 4) {
+    if (tile + 4 < t_hi) load(tile + 4, n0, n1);
+    const int64_t b = 16 * tile + row;
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], b0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], b1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], c0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], c1, acc, 0, 0, 0);
       if (b < nvq[at]) {
         float s = wq[at][0] * fmaxf(acc[0], 0.f) + wq[at][1] * fmaxf(acc[1], 0.f) +
                   wq[at][2] * fmaxf(acc[2], 0.f) + wq[at][3] * fmaxf(acc[3], 0.f);
         ws.scores[(int64_t)(16 * qt + 4 * at + g) * ws.R + b] = s;
       }
     }
+    c0 = n0;
+    c1 = n1;
   }
 }
 
