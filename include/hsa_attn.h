@@ -57,8 +57,9 @@
  *     as zeros, a per-device fault word is set, and hsa_check_device_error()
  *     reports it.
  *   - Workspaces: size them with the matching *_workspace_bytes() call.  A
- *     workspace needs no initialisation (every call clears the counters it
- *     uses) and must not be shared by calls that may run concurrently.
+ *     workspace needs no initialisation (every call writes whatever it later
+ *     reads: no counters carry over between calls) and must not be shared by
+ *     calls that may run concurrently.
  *   - Calls that run concurrently on different streams must use different
  *     workspaces and outputs.
  */
@@ -152,7 +153,8 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
  *   qI  bf16 [n][H_I][d_I]     w  fp32 [n][H_I]     kIc bf16 paged cache
  *   idx int32 [n][k]  out: selected blocks ascending, -1 padded
  *   score fp32 [n][k] or NULL: the indexer score of each idx entry (0 at pads)
- * Scores are computed in fp32 from bf16 operands. */
+ * Scores are computed in fp32 from bf16 operands.  Listed (decode) queries
+ * support up to 2^21 visible blocks per query (HSA_ERR_UNSUPPORTED beyond). */
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k);
 hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w,
@@ -211,6 +213,9 @@ typedef struct {
  *      tail and appends it at entry n_entries[b], which it then increments;
  *   3. runs the indexer + top-k + CSA attention, or HCA attention, for the
  *      new token's query.
+ * (Steps 1-2 of a CSA layer run in the same launch as the indexer's scan: the
+ * block completed at pos starts inside the window, so the query at pos does not
+ * see it.)
  * Q bf16 [B][H][d]; k_new, v_new bf16 [B][d]; qI bf16 [B][H_I][d_I]; kI_new
  * bf16 [B][d_I]; w fp32 [B][H_I]; O [B][H][d] of L->o_dtype; lse fp32 [B][H] or NULL;
  * idx_out int32 [B][topk] or NULL (CSA).  max_pos bounds every pos[b].

@@ -4,7 +4,7 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
+#include "update.h"
 
 namespace hsa {
 
@@ -279,7 +279,8 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
   REQ(k >= 1 && k <= (1 << 20), "indexer_topk: k out of range");
   int64_t nv = nvis_host(q->max_pos, m, n_win);
   REQ((int64_t)kIc->pages_per_req * kPage >= nv, "indexer_topk: page table too short");
-  REQ(nv < (int64_t(1) << 31), "indexer_topk: too many blocks");
+  SUP(is_span(q) || nv <= indexer_max_blocks(),
+      "indexer_topk: decode rows longer than 2^21 visible blocks are not supported");
   if ((s = check_ws(ws, ws_bytes, hsa_indexer_topk_workspace_bytes(q, m, n_win, k))) != HSA_OK)
     return s;
   return hip_status(launch_indexer(*q, qI, w, *kIc, m, n_win, k, idx, score, ws, ws_bytes, stream),
@@ -394,27 +395,27 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
     REQ((int64_t)L->kic.pages_per_req * kPage >= pages_needed, "decode_step: kic table too short");
     SUP(L->H_I == kHI && L->d_I == kDI, "decode_step: H_I must be 4 and d_I 64");
     REQ(L->topk >= 1 && L->topk <= (1 << 20), "decode_step: topk out of range");
+    SUP(nvis_host(max_pos, L->m, L->n_win) <= indexer_max_blocks(),
+        "decode_step: rows longer than 2^21 visible blocks are not supported");
   }
   size_t a_idx, a_sel, a_attn;
   decode_parts(L, B, max_pos, &a_idx, &a_sel, &a_attn);
   if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn)) != HSA_OK) return s;
   char* base = (char*)ws;
-  // the update kernel also clears the indexer's counters (one launch fewer)
-  hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new,
-                                      csa ? base : nullptr,
-                                      csa ? indexer_zero_bytes(B, nvis_host(max_pos, L->m, L->n_win),
-                                                               false)
-                                          : 0,
-                                      stream);
-  if (e != hipSuccess) return hip_status(e, "decode_step update");
+  hipError_t e;
   if (csa) {
+    // the cache upkeep runs inside the indexer's scan launch (one workgroup
+    // per request beside the scan)
+    const UpdateArgs upd = make_update_args(*L, pos, max_pos, k_new, v_new, kI_new);
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base, a_idx,
-                       stream, /*ws_head_zeroed=*/true);
+                       stream, &upd);
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_idx + a_sel, a_attn, stream);
   } else {
+    e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream);
+    if (e != hipSuccess) return hip_status(e, "decode_step update");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
                     L->scale, O, L->o_dtype, lse, base, a_attn, stream);
   }

@@ -190,12 +190,16 @@ hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, 
 hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s);
 
+struct UpdateArgs;   // update.h
+
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span);
-size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span);   // cleared per call
+int64_t indexer_max_blocks();   // longest visible-block row the decode indexer takes
+// upd: when not null, the decode cache upkeep of request i runs in the scan
+// launch (one extra workgroup per request)
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,
-                          bool ws_head_zeroed = false);
+                          const UpdateArgs* upd = nullptr);
 
 size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span);
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
@@ -204,8 +208,10 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t s);
 
+UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
+                            const void* k_new, const void* v_new, const void* kI_new);
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                void* zero_ptr, size_t zero_bytes, hipStream_t s);
+                                hipStream_t s);
 
 }  // namespace hsa

@@ -6,7 +6,7 @@
 // token is exact there, so the entry is rounded only once, into the cache type.
 // The work is a streaming read of the tokens (HBM-bound); float64 FMA runs at
 // the same rate as fp32 on gfx950, so it costs nothing here.
-#include "common.h"
+#include "update.h"
 
 namespace hsa {
 
@@ -94,81 +94,40 @@ __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int 
 
 // ---------------------------------------------------------------- decode: cache upkeep
 
-// One workgroup per request: write the new token into the window ring (and its
-// indexer key into the open-block tail); when the token completes a block,
-// pool the block from the ring/tail and append it to the paged caches.  The
-// new token's own row is taken from the input, not re-read from the ring.
-__device__ __forceinline__ double pool_last(const Tokens& src, int r, int64_t blk, int m, int c,
-                                            const float* __restrict__ alpha, int dim, u16 newest) {
-  double acc = 0.0;
-  for (int j = 0; j < m - 1; ++j)
-    acc += (double)alpha[(int64_t)j * dim + c] * (double)bf16_to_f32(src.row(r, blk * m + j)[c]);
-  acc += (double)alpha[(int64_t)(m - 1) * dim + c] * (double)bf16_to_f32(newest);
-  return acc;
+// Decode-time cache upkeep for B requests (one workgroup each); the CSA decode
+// step runs the same upkeep inside the indexer scan launch instead.
+__global__ __launch_bounds__(128) void decode_update_kernel(UpdateArgs u, int* fault) {
+  decode_update_body(u, blockIdx.x, fault);
 }
 
-__global__ __launch_bounds__(128) void decode_update_kernel(
-    Tokens rk, Tokens rv, Tokens ti, const int64_t* __restrict__ pos, int64_t max_pos,
-    const u16* __restrict__ k_new, const u16* __restrict__ v_new, const u16* __restrict__ ki_new,
-    int m, int csa, const float* __restrict__ ak, const float* __restrict__ av,
-    const float* __restrict__ ai, Paged kc, Paged vc, Paged kic, uint4* zero_ptr,
-    int64_t zero_n16, int* fault) {
-  const int b = blockIdx.x, c = threadIdx.x;
-  // clear this workgroup's share of the indexer counters used later in the step
-  if (zero_ptr) {
-    const int64_t per = (zero_n16 + gridDim.x - 1) / gridDim.x;
-    const int64_t lo = per * b, hi = lo + per < zero_n16 ? lo + per : zero_n16;
-    for (int64_t i = lo + c; i < hi; i += 128) zero_ptr[i] = make_uint4(0, 0, 0, 0);
-  }
-  int64_t p = pos[b];
-  if (p < 0 || p > max_pos) {
-    if (c == 0) atomicOr(fault, HSA_FAULT_POS);
-    return;
-  }
-  const u16 kn = k_new[(int64_t)b * kD + c], vn = v_new[(int64_t)b * kD + c];
-  rk.row(b, p)[c] = kn;
-  rv.row(b, p)[c] = vn;
-  u16 in = 0;
-  if (csa && c < kDI) {
-    in = ki_new[(int64_t)b * kDI + c];
-    ti.row(b, p)[c] = in;
-  }
-  if ((p + 1) % m != 0) return;
-  const int64_t blk = (p + 1) / m - 1;
-  __shared__ int ok;
-  if (c == 0) {
-    int32_t ek = kc.n_entries[b], ev = vc.n_entries[b], ei = csa ? kic.n_entries[b] : (int32_t)blk;
-    ok = (ek == blk && ev == blk && ei == blk);
-    if (!ok) atomicOr(fault, HSA_FAULT_ENTRIES);
-  }
-  __syncthreads();
-  if (!ok) return;
-  int pk = kc.page_of(b, blk, fault), pv = vc.page_of(b, blk, fault);
-  if (pk >= 0) ((u16*)kc.row(pk, blk))[c] = f64_to_bf16(pool_last(rk, b, blk, m, c, ak, kD, kn));
-  if (pv >= 0) ((u16*)vc.row(pv, blk))[c] = f64_to_bf16(pool_last(rv, b, blk, m, c, av, kD, vn));
-  if (csa && c < kDI) {
-    int pi = kic.page_of(b, blk, fault);
-    if (pi >= 0) ((u16*)kic.row(pi, blk))[c] = f64_to_bf16(pool_last(ti, b, blk, m, c, ai, kDI, in));
-  }
-  __syncthreads();
-  if (c == 0) {
-    kc.n_entries[b] = (int32_t)(blk + 1);
-    vc.n_entries[b] = (int32_t)(blk + 1);
-    if (csa) kic.n_entries[b] = (int32_t)(blk + 1);
-  }
+UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
+                            const void* k_new, const void* v_new, const void* kI_new) {
+  const int csa = L.kind == HSA_LAYER_CSA;
+  UpdateArgs u;
+  u.rk = to_dev(L.ring_k);
+  u.rv = to_dev(L.ring_v);
+  u.ti = csa ? to_dev(L.tail_i) : Tokens{nullptr, 1, kDI};
+  u.pos = pos;
+  u.max_pos = max_pos;
+  u.k_new = (const u16*)k_new;
+  u.v_new = (const u16*)v_new;
+  u.ki_new = (const u16*)kI_new;
+  u.m = L.m;
+  u.csa = csa;
+  u.ak = L.alpha_k;
+  u.av = L.alpha_v;
+  u.ai = L.alpha_i;
+  u.kc = to_dev(L.kc);
+  u.vc = to_dev(L.vc);
+  u.kic = csa ? to_dev(L.kic) : Paged{};
+  return u;
 }
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                void* zero_ptr, size_t zero_bytes, hipStream_t s) {
-  const int csa = L.kind == HSA_LAYER_CSA;
-  Tokens ti = csa ? to_dev(L.tail_i) : Tokens{nullptr, 1, kDI};
-  Paged kic = csa ? to_dev(L.kic) : Paged{};
-  decode_update_kernel<<<B, 128, 0, s>>>(to_dev(L.ring_k), to_dev(L.ring_v), ti, pos, max_pos,
-                                         (const u16*)k_new, (const u16*)v_new,
-                                         (const u16*)kI_new, L.m, csa, L.alpha_k, L.alpha_v,
-                                         L.alpha_i, to_dev(L.kc), to_dev(L.vc), kic,
-                                         (uint4*)zero_ptr, (int64_t)(zero_bytes / 16), fault_word());
+                                hipStream_t s) {
+  decode_update_kernel<<<B, 128, 0, s>>>(make_update_args(L, pos, max_pos, k_new, v_new, kI_new),
+                                         fault_word());
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@
 //            ascending block order.
 // The counters and histograms at the head of the workspace are cleared before
 // every call (and by finalize, for the next query chunk of a prefill call).
-#include "common.h"
+#include "update.h"
 
 namespace hsa {
 
@@ -36,38 +36,44 @@ constexpr int kBins = 4096;        // first-level histogram (12 key bits)
 constexpr int kCoarse = 256;       // groups of 16 bins walked by the threshold search
 constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the workspace)
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
-constexpr int kStateInts = 8;      // ticket1, ticket2, thr_bin, n_above, n_cand, n_vis
+constexpr int kStateInts = 8;      // -, -, thr_bin, n_above, n_cand, n_vis, n_thr_bin
+constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
+constexpr int kMaxLists = 4096;    // decode: histogram lists (scan chunks) per query
 
 struct IdxWs {
   float* scores;        // [nq][R]
-  uint32_t* hist;       // [nq][hslots][kBins]
+  uint32_t* hl;         // [nq][n_lists][list_cap] histogram lists: bin << 16 | count
+  int32_t* hl_n;        // [nq][n_lists] entries of each list
   int32_t* state;       // [nq][kStateInts]
   uint32_t* bitmap;     // [nq][R/32]
   uint64_t* cand;       // [nq][R]  (score key << 32 | ~block)
   uint64_t* cand2;      // [nq][R]
   int32_t* ccount;      // [nq][R/kSelCH]  candidates per select chunk (long rows)
   int64_t R;
-  int hslots;           // histogram copies per query (one per 64 scan chunks, <= 16)
+  int n_lists;          // one list per scan chunk (decode) or histogram slice (prefill)
+  int list_cap;         // nonzero bins a list can hold
+  int list_span;        // scores a list covers
 };
-
-static int hist_slots(int64_t R) {
-  const int64_t chunks = R / kCH;
-  int64_t sl = (chunks + 63) / 64;
-  return (int)(sl < 1 ? 1 : (sl > 16 ? 16 : sl));
-}
 
 static int64_t row_cap(int64_t max_nvis) {
   int64_t R = ((max_nvis + kSelCH - 1) / kSelCH) * kSelCH;
   return R < kSelCH ? kSelCH : R;
 }
 
-static IdxWs carve(void* ws, int nq, int64_t R) {
+static void list_shape(int64_t R, bool span, int* n_lists, int* cap, int* span_len) {
+  *span_len = span ? kHistSpan : kCH;
+  *n_lists = (int)((R + *span_len - 1) / *span_len);
+  *cap = span ? kBins : kCH;   // a list holds at most min(bins, scores) entries
+}
+
+static IdxWs carve(void* ws, int nq, int64_t R, bool span) {
   IdxWs w;
   char* p = (char*)ws;
   auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
-  w.hslots = hist_slots(R);
+  list_shape(R, span, &w.n_lists, &w.list_cap, &w.list_span);
   w.state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
-  w.hist = (uint32_t*)take(sizeof(uint32_t) * kBins * w.hslots * nq);
+  w.hl_n = (int32_t*)take(sizeof(int32_t) * w.n_lists * nq);
+  w.hl = (uint32_t*)take(sizeof(uint32_t) * w.list_cap * w.n_lists * nq);
   w.scores = (float*)take(sizeof(float) * R * nq);
   w.bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
   w.cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
@@ -77,10 +83,12 @@ static IdxWs carve(void* ws, int nq, int64_t R) {
   return w;
 }
 
-static size_t carve_bytes(int nq, int64_t R) {
+static size_t carve_bytes(int nq, int64_t R, bool span) {
   auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
-  return rnd(sizeof(int32_t) * kStateInts * nq) +
-         rnd(sizeof(uint32_t) * kBins * hist_slots(R) * nq) + rnd(sizeof(float) * R * nq) +
+  int n_lists, cap, span_len;
+  list_shape(R, span, &n_lists, &cap, &span_len);
+  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(int32_t) * n_lists * nq) +
+         rnd(sizeof(uint32_t) * cap * n_lists * nq) + rnd(sizeof(float) * R * nq) +
          rnd(sizeof(uint32_t) * (R / 32) * nq) + 2 * rnd(sizeof(uint64_t) * R * nq) +
          rnd(sizeof(int32_t) * (R / kSelCH) * nq);
 }
@@ -94,22 +102,12 @@ static int64_t host_nvis(int64_t t, int m, int n_win) {
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
   (void)k;
   int nq = span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q;
-  return carve_bytes(nq, row_cap(max_nvis));
+  return carve_bytes(nq, row_cap(max_nvis), span);
 }
 
-// the state and histograms at the head of the workspace, cleared per call
-static size_t zeroed_bytes(int nq, int64_t R) {
-  auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
-  return rnd(sizeof(int32_t) * kStateInts * nq) +
-         rnd(sizeof(uint32_t) * kBins * hist_slots(R) * nq);
-}
+int64_t indexer_max_blocks() { return (int64_t)kMaxLists * kCH; }
 
 // ---------------------------------------------------------------- device helpers
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* __restrict__ p, int64_t n16) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    p[i] = make_uint4(0, 0, 0, 0);
-}
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -157,53 +155,52 @@ __device__ __forceinline__ int64_t clamp_nvis(int64_t nv, const int32_t* n_entri
   return nv;
 }
 
-// Add a chunk's LDS histogram to the query's histogram (no fence: the select
-// kernel reads it after the kernel boundary).
-__device__ __forceinline__ void flush_histogram(const uint32_t* lhist, IdxWs ws, int qrow,
-                                                int chunk) {
-  __syncthreads();
-  uint32_t* gh = ws.hist + ((int64_t)qrow * ws.hslots + chunk % ws.hslots) * kBins;
-  for (int i = threadIdx.x; i < kBins; i += 256) {
-    uint32_t c = lhist[i];
-    if (c) atomicAdd(gh + i, c);
+// exclusive prefix sum over an NT-thread block (NT a multiple of 64)
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    uint32_t s = sh[i];
+    if (i < wv) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
 }
 
-// The bin that holds the k-th largest key, and how many keys lie above it
-// (thr = -1: every visible block is selected).  The 4096 counts are loaded
-// with all loads in flight, summed into 256 groups of 16, and the crossing is
-// found by a block scan over the groups and a short walk inside one group.
-__device__ void find_threshold(const uint32_t* gh, int64_t nv, int k, int* thr_out,
-                               int* above_out) {
-  __shared__ int s_thr, s_above, s_cb;
-  __shared__ uint32_t s_pre;
+// Write a 4096-bin LDS histogram (256 threads) as a list of its nonzero bins,
+// bin << 16 | count, into list `li` of query row `qrow`.  Lists are rewritten
+// whole by every call, so the workspace needs no clearing between calls.
+__device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const IdxWs& ws, int qrow,
+                                                int li) {
   __shared__ uint32_t sh[4];
-  __shared__ uint32_t grp[kCoarse][17];
-  if (threadIdx.x == 0) { s_thr = -1; s_above = 0; s_cb = -1; }
-  if (nv > k) {
-    // thread i owns group 255 - i: bins 16*(255-i) .. +15 (descending order)
-    const int gi = kCoarse - 1 - threadIdx.x;
-    const uint4* gp = (const uint4*)(gh + gi * 16);
-    const uint4 a = gp[0], b = gp[1], c = gp[2], d = gp[3];
-    const uint32_t v[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w,
-                            c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
-    uint32_t sm = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) { sm += v[j]; grp[threadIdx.x][j] = v[j]; }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan(sm, &tot, sh);
-    if (pre < (uint32_t)k && pre + sm >= (uint32_t)k) {
-      uint32_t cum = pre;
-      for (int j = 15; j >= 0; --j) {
-        const uint32_t f = grp[threadIdx.x][j];
-        if (cum + f >= (uint32_t)k) { s_thr = gi * 16 + j; s_above = (int)cum; break; }
-        cum += f;
-      }
-    }
-  }
   __syncthreads();
-  *thr_out = s_thr;
-  *above_out = s_above;
+  constexpr int BPT = kBins / 256;
+  uint32_t v[BPT];
+  uint32_t nz = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {   // thread t owns bins t, t + 256, ... (no bank conflicts)
+    v[j] = lhist[threadIdx.x + 256 * j];
+    nz += v[j] != 0;
+  }
+  uint32_t tot;
+  uint32_t off = block_scan_nt<256>(nz, &tot, sh);
+  uint32_t* dst = ws.hl + ((int64_t)qrow * ws.n_lists + li) * ws.list_cap;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if (v[j]) dst[off++] = ((uint32_t)(threadIdx.x + 256 * j) << 16) | v[j];
+  if (threadIdx.x == 0) ws.hl_n[(int64_t)qrow * ws.n_lists + li] = (int32_t)tot;
 }
 
 // ---------------------------------------------------------------- decode: score scan
@@ -211,8 +208,12 @@ __device__ void find_threshold(const uint32_t* gh, int64_t nv, int k, int* thr_o
 __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
-                                                       int* fault) {
+                                                       int n_chunks, UpdateArgs upd, int* fault) {
   const int qrow = blockIdx.y, chunk = blockIdx.x;
+  if (chunk >= n_chunks) {   // the extra column: cache upkeep of request qrow
+    decode_update_body(upd, qrow, fault);
+    return;
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
   // Each wave streams 128 consecutive blocks = two whole pages.  The two page
   // ids depend only on the request, so they are loaded alongside the query's
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   float* srow = ws.scores + (int64_t)qrow * ws.R;
   for (int i = threadIdx.x; i < kCH; i += 256)
     if (b_begin + i < b_end) srow[b_begin + i] = lsc[i];
-  flush_histogram(lhist, ws, qrow, chunk);
+  write_hist_list(lhist, ws, qrow, chunk);
 }
 
 // ---------------------------------------------------------------- prefill: score GEMM
@@ -389,9 +390,8 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
 
 // prefill: first-level histogram over the stored scores
 // Prefill: histogram of the fp32 scores of one query, kHistSpan blocks per
-// workgroup (the 4096-bin LDS histogram is cleared and flushed once per
-// kHistSpan scores rather than once per scan chunk).
-constexpr int kHistSpan = 8192;
+// workgroup (the 4096-bin LDS histogram is cleared and written out once per
+// kHistSpan scores).
 
 __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, const Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
@@ -419,35 +419,11 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (b_begin + 256 * u + threadIdx.x < b_end) atomicAdd(&lhist[order_key(sc[u]) >> 20], 1u);
-  flush_histogram(lhist, ws, qrow, slice);
+  write_hist_list(lhist, ws, qrow, slice);
 }
 
 // ---------------------------------------------------------------- select, refine, emit
 
-
-// exclusive prefix sum over an NT-thread block (NT a multiple of 64)
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, uint32_t* sh) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wv] = x;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    uint32_t s = sh[i];
-    if (i < wv) off += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + x - v;
-}
 
 // One workgroup per query: threshold bin from the histogram, one pass over the
 // query's scores marking blocks above it in a bitmap and collecting the blocks
@@ -460,8 +436,7 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, u
 template <int NT>
 __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, int out_row0,
-                                                      int cand_lds, int bm_lds_words, int mode,
-                                                      int clear_hist) {
+                                                      int cand_lds, int bm_lds_words, int mode) {
   constexpr int BPT = kBins / NT;                // histogram bins per thread
   extern __shared__ __align__(16) uint64_t dyn[];
   __shared__ uint32_t sh[NT / 64];
@@ -472,7 +447,6 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
   const int64_t nv = st[5];
   const float* srow = ws.scores + (int64_t)qrow * ws.R;
-  uint32_t* gh = ws.hist + (int64_t)qrow * ws.hslots * kBins;
 
   // first round of scores, loaded before the threshold search (independent of it)
   constexpr int U = NT >= 1024 ? 32 : 16;
@@ -491,17 +465,44 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   // ---- threshold bin: thread i owns bins kBins-BPT(i+1) .. kBins-BPT*i-1 (descending)
   if (tid == 0) { s_thr = -1; s_above = 0; s_ncand = 0; }
   {
+    // the query's histogram, merged in LDS from its lists (the dynamic LDS is
+    // free until candidates are collected).  Each wave takes LB lists at a
+    // time and loads their first 128 entries together, counts included, so a
+    // step costs one memory round trip; entries past a list's count are
+    // ignored.
+    uint32_t* lh = (uint32_t*)dyn;
+    for (int i = tid; i < kBins; i += NT) lh[i] = 0;
+    __syncthreads();
+    const int n_used = nv > 0 ? (int)((nv + ws.list_span - 1) / ws.list_span) : 1;
+    const int32_t* hn = ws.hl_n + (int64_t)qrow * ws.n_lists;
+    const uint32_t* hlq = ws.hl + (int64_t)qrow * ws.n_lists * ws.list_cap;
+    constexpr int NWV = NT / 64, LB = 8;
+    for (int c0 = wv * LB; c0 < n_used; c0 += NWV * LB) {
+      int cnt[LB];
+      uint32_t e0[LB], e1[LB];
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        const int c = c0 + j < n_used ? c0 + j : c0;
+        cnt[j] = c0 + j < n_used ? hn[c] : 0;
+        const uint32_t* L = hlq + (int64_t)c * ws.list_cap;   // list_cap >= 128
+        e0[j] = L[lane];
+        e1[j] = L[64 + lane];
+      }
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        if (lane < cnt[j]) atomicAdd(&lh[e0[j] >> 16], e0[j] & 0xFFFFu);
+        if (64 + lane < cnt[j]) atomicAdd(&lh[e1[j] >> 16], e1[j] & 0xFFFFu);
+        for (int i = 128 + lane; i < cnt[j]; i += 64) {   // long lists
+          const uint32_t e = hlq[(int64_t)(c0 + j) * ws.list_cap + i];
+          atomicAdd(&lh[e >> 16], e & 0xFFFFu);
+        }
+      }
+    }
+    __syncthreads();
     uint32_t v[BPT];
     const int lo = kBins - BPT * (tid + 1);
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) v[j] = 0;
-    for (int sl = 0; sl < ws.hslots; ++sl) {
-#pragma unroll
-      for (int j = 0; j < BPT / 4; ++j) {
-        const uint4 u = ((const uint4*)(gh + sl * kBins + lo))[j];
-        v[4 * j] += u.x; v[4 * j + 1] += u.y; v[4 * j + 2] += u.z; v[4 * j + 3] += u.w;
-      }
-    }
+    for (int j = 0; j < BPT; ++j) v[j] = lh[lo + j];
     uint32_t sm = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) sm += v[j];
@@ -518,12 +519,6 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
         }
         cum += v[j];
       }
-    }
-    // the histogram is consumed: clear it for the next query chunk of a
-    // prefill (a decode call clears the workspace head before its scan)
-    for (int sl = 0; clear_hist && sl < ws.hslots; ++sl) {
-#pragma unroll
-      for (int j = 0; j < BPT / 4; ++j) ((uint4*)(gh + sl * kBins + lo))[j] = make_uint4(0, 0, 0, 0);
     }
   }
   __syncthreads();
@@ -775,10 +770,6 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxWs ws) {
 
 // ---------------------------------------------------------------- host launcher
 
-size_t indexer_zero_bytes(int n_q, int64_t max_nvis, bool span) {
-  return zeroed_bytes(span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q, row_cap(max_nvis));
-}
-
 // rows up to these sizes take the one-workgroup-per-query path; longer rows the
 // threshold / select / refine kernels (decode: few queries, so the many-
 // workgroup classification pays off earlier)
@@ -790,31 +781,30 @@ constexpr int64_t kFusedMaxBlocksPrefill = 65536;
 // candidates in LDS).  Longer rows: the threshold per query, a multi-workgroup
 // pass that marks the bitmap, then one workgroup per query refines and emits.
 static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
-                        int out_row0, bool clear_hist, hipStream_t s) {
+                        int out_row0, hipStream_t s) {
   const int64_t W = ws.R / 32;
   const int cand = nt == 1024 ? 2048 : 1024;
   if (ws.R <= (nt == 1024 ? kFusedMaxBlocksDecode : kFusedMaxBlocksPrefill)) {
     const int bm_words = (int)W;
     const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
     if (nt == 1024)
-      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0,
-                                                   clear_hist);
+      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
     else
-      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0,
-                                                 clear_hist);
+      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
     return;
   }
-  idx_topk_kernel<1024><<<nq, 1024, 0, s>>>(k, ws, idx, score, out_row0, 0, 0, 1, clear_hist);
+  // the threshold pass merges the histogram lists in (dynamic) LDS
+  idx_topk_kernel<1024><<<nq, 1024, kBins * sizeof(uint32_t), s>>>(k, ws, idx, score, out_row0,
+                                                                    0, 0, 1);
   idx_select_kernel<<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
   const size_t lds = (size_t)2 * cand * sizeof(uint64_t);
-  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2,
-                                               clear_hist);
+  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* wsp, size_t ws_bytes, hipStream_t s,
-                          bool ws_head_zeroed) {
+                          const UpdateArgs* upd) {
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
@@ -823,23 +813,17 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
-  if (!ws_head_zeroed) {
-    // counters and histograms start at zero whatever the workspace held before
-    const int nq_ws = span ? (q.n < kSpanQC ? q.n : kSpanQC) : q.n;
-    const int64_t n16 = (int64_t)(zeroed_bytes(nq_ws, R) / 16);
-    unsigned blocks = (unsigned)((n16 + 255) / 256);
-    fill_zero_kernel<<<blocks < 1024 ? blocks : 1024, 256, 0, s>>>((uint4*)wsp, n16);
-  }
   if (!span) {
-    IdxWs ws = carve(wsp, q.n, R);
-    timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel, dim3(n_chunks, q.n), dim3(256), 0, s, Qd,
-                 (const u16*)qI, w, kc, m, n_win, k, ws, fault);
+    IdxWs ws = carve(wsp, q.n, R, false);
+    timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel, dim3(n_chunks + (upd ? 1 : 0), q.n),
+                 dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_chunks,
+                 upd ? *upd : UpdateArgs{}, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    launch_topk(1024, q.n, k, ws, idx, score, 0, false, s);
+    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
   }
   const int QC = q.n < kSpanQC ? q.n : kSpanQC;
-  IdxWs ws = carve(wsp, QC, R);
+  IdxWs ws = carve(wsp, QC, R, true);
   for (int q0 = 0; q0 < q.n; q0 += QC) {
     const int nq = q.n - q0 < QC ? q.n - q0 : QC;
     // chunk-local maximum of the visible blocks bounds the work of this pass
@@ -854,7 +838,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
     idx_hist_kernel<<<dim3(slices < 1 ? 1 : slices, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k,
                                                                       ws, fault);
-    launch_topk(256, nq, k, ws, idx, score, q0, true, s);
+    launch_topk(256, nq, k, ws, idx, score, q0, s);
   }
   return hipGetLastError();
 }
