@@ -28,7 +28,11 @@
 
 namespace hsa {
 
-constexpr int kCH = 512;           // blocks per scan workgroup
+constexpr int kCH = 512;           // blocks per scan chunk
+// chunks per scan workgroup (one histogram list each): long rows group 4 chunks
+// so that the threshold pass merges 4x fewer lists
+constexpr int kLongRowChunks = 256;
+static int scan_cpw(int64_t R) { return R / kCH >= kLongRowChunks ? 4 : 1; }
 constexpr int kSelCH = 2048;       // blocks per select workgroup (multiple of kCH)
 constexpr int kMaxSelChunks = 1024;  // select chunks whose offsets fit in LDS
 constexpr int kGemmMaxPages = 1024;  // pages of a prefill score workgroup resolved in LDS
@@ -38,7 +42,6 @@ constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the wo
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
 constexpr int kStateInts = 8;      // -, -, thr_bin, n_above, n_cand, n_vis, n_thr_bin
 constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
-constexpr int kMaxLists = 4096;    // decode: histogram lists (scan chunks) per query
 
 struct IdxWs {
   float* scores;        // [nq][R]
@@ -61,9 +64,9 @@ static int64_t row_cap(int64_t max_nvis) {
 }
 
 static void list_shape(int64_t R, bool span, int* n_lists, int* cap, int* span_len) {
-  *span_len = span ? kHistSpan : kCH;
+  *span_len = span ? kHistSpan : scan_cpw(R) * kCH;
   *n_lists = (int)((R + *span_len - 1) / *span_len);
-  *cap = span ? kBins : kCH;   // a list holds at most min(bins, scores) entries
+  *cap = *span_len < kBins ? *span_len : kBins;   // at most min(bins, scores) entries
 }
 
 static IdxWs carve(void* ws, int nq, int64_t R, bool span) {
@@ -105,7 +108,8 @@ size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
   return carve_bytes(nq, row_cap(max_nvis), span);
 }
 
-int64_t indexer_max_blocks() { return (int64_t)kMaxLists * kCH; }
+// decode rows up to 2^21 visible blocks (an 8M-token context at m = 4)
+int64_t indexer_max_blocks() { return int64_t(1) << 21; }
 
 // ---------------------------------------------------------------- device helpers
 
@@ -205,59 +209,68 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
 
 // ---------------------------------------------------------------- decode: score scan
 
+template <int CPW>
 __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
-                                                       int n_chunks, UpdateArgs upd, int* fault) {
-  const int qrow = blockIdx.y, chunk = blockIdx.x;
-  if (chunk >= n_chunks) {   // the extra column: cache upkeep of request qrow
+                                                       int n_groups, UpdateArgs upd, int* fault) {
+  const int qrow = blockIdx.y;
+  if ((int)blockIdx.x >= n_groups) {   // the extra column: cache upkeep of request qrow
     decode_update_body(upd, qrow, fault);
     return;
   }
+  const int c_first = blockIdx.x * CPW;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
-  // Each wave streams 128 consecutive blocks = two whole pages.  The two page
-  // ids depend only on the request, so they are loaded alongside the query's
-  // position and entry count instead of after them: the key loads wait for one
-  // round trip, not three.
+  // A workgroup scores CPW consecutive chunks of kCH blocks; in each chunk a
+  // wave streams 128 consecutive blocks = two whole pages.  The page ids depend
+  // only on the request, so they are loaded alongside the query's position and
+  // entry count instead of after them: the key loads wait for one round trip.
   const int r = Q.pos ? (Q.req ? Q.req[qrow] : qrow) : Q.span_req;
-  const int64_t b_begin = (int64_t)chunk * kCH;
-  const int64_t w0b = b_begin + (int64_t)wv * (kCH / 4);
-  const int lp0 = (int)(w0b >> 6);
-  int pid[2];
+  int pid[CPW][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    pid[j] = lp0 + j < kic.pages_per_req
-                 ? kic.page_table[(int64_t)r * kic.pages_per_req + lp0 + j]
-                 : -1;
+  for (int c = 0; c < CPW; ++c) {
+    const int lp = (int)((((int64_t)(c_first + c)) * kCH + wv * (kCH / 4)) >> 6);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pid[c][j] = lp + j < kic.pages_per_req
+                      ? kic.page_table[(int64_t)r * kic.pages_per_req + lp + j]
+                      : -1;
+  }
   int rq;
   int64_t t;
   Q.get(qrow, &rq, &t, fault);
   const int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
-                                chunk == 0 && threadIdx.x == 0);
+                                c_first == 0 && threadIdx.x == 0);
   const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
-  if (chunk >= n_active) return;
-  if (chunk == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
-  const int64_t b_end = nv < b_begin + kCH ? nv : b_begin + kCH;
+  if (c_first >= n_active) return;
+  if (c_first == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
 
-  // all 16 key loads of a lane are issued before anything waits on them;
-  // branch-free: blocks out of range (or on a bad page) read row 0 of page 0
-  constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave
-  bf16x8 b0[NT], b1[NT];
+  constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave and chunk
+  // branch-free loads: blocks out of range (or on a bad page) read row 0 of page 0
+  auto load = [&](int c, bf16x8* x0, bf16x8* x1) {
+    const int64_t cb = (int64_t)(c_first + c) * kCH;
+    const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
+    const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
 #pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int64_t b = w0b + 16 * u + row;
-    const int pg = pid[u >> 2];
-    const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
-    const bf16x8* kr = (const bf16x8*)kic.row(ok ? pg : 0, ok ? b : 0);
-    b0[u] = __builtin_nontemporal_load(kr + g);
-    b1[u] = __builtin_nontemporal_load(kr + 4 + g);
-  }
-  if (lane == 0) {
+    for (int u = 0; u < NT; ++u) {
+      const int64_t b = w0b + 16 * u + row;
+      const int pg = pid[c][u >> 2];
+      const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
+      const bf16x8* kr = (const bf16x8*)kic.row(ok ? pg : 0, ok ? b : 0);
+      x0[u] = __builtin_nontemporal_load(kr + g);
+      x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+    }
+    if (lane == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (w0b + 64 * j < b_end && (unsigned)pid[j] >= (unsigned)kic.n_pages)
-        atomicOr(fault, HSA_FAULT_PAGE);
-  }
+      for (int j = 0; j < 2; ++j)
+        if (w0b + 64 * j < b_end && (unsigned)pid[c][j] >= (unsigned)kic.n_pages)
+          atomicOr(fault, HSA_FAULT_PAGE);
+    }
+  };
+  bf16x8 xa0[NT], xa1[NT], xb0[NT], xb1[NT];
+  load(0, xa0, xa1);
+  if (CPW > 1) load(1, xb0, xb1);
+
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
@@ -266,31 +279,48 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
-
   // the LDS histogram is cleared while the keys are in flight
   __shared__ uint32_t lhist[kBins];
-  __shared__ float lsc[kCH];
+  __shared__ float lsc[CPW * kCH];
   for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
   __syncthreads();
+
+  auto score = [&](int c, const bf16x8* x0, const bf16x8* x1) {
+    const int64_t cb = (int64_t)(c_first + c) * kCH;
+    const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
+    const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
 #pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[u], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc, 0, 0, 0);
-    const int64_t b = w0b + 16 * u + row;
-    if (g == 0 && b < b_end) {
-      const float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
-                       w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
-      lsc[b - b_begin] = sc;
-      atomicAdd(&lhist[order_key(sc) >> 20], 1u);
+    for (int u = 0; u < NT; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, x0[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, x1[u], acc, 0, 0, 0);
+      const int64_t b = w0b + 16 * u + row;
+      if (g == 0 && b < b_end) {
+        const float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
+                         w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+        lsc[b - (int64_t)c_first * kCH] = sc;
+        atomicAdd(&lhist[order_key(sc) >> 20], 1u);
+      }
+    }
+  };
+  // two register buffers: the next chunk's keys load while this one is scored
+#pragma unroll
+  for (int c = 0; c < CPW; c += 2) {
+    score(c, xa0, xa1);
+    if (c + 2 < CPW) load(c + 2, xa0, xa1);
+    if (c + 1 < CPW) {
+      score(c + 1, xb0, xb1);
+      if (c + 3 < CPW) load(c + 3, xb0, xb1);
     }
   }
   __syncthreads();
-  // the chunk's scores leave in one coalesced run
+  // the scores leave in one coalesced run
   float* srow = ws.scores + (int64_t)qrow * ws.R;
-  for (int i = threadIdx.x; i < kCH; i += 256)
-    if (b_begin + i < b_end) srow[b_begin + i] = lsc[i];
-  write_hist_list(lhist, ws, qrow, chunk);
+  const int64_t s0 = (int64_t)c_first * kCH;
+  const int64_t s_end = nv < s0 + CPW * kCH ? nv : s0 + CPW * kCH;
+  for (int i = threadIdx.x; i < CPW * kCH; i += 256)
+    if (s0 + i < s_end) srow[s0 + i] = lsc[i];
+  write_hist_list(lhist, ws, qrow, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- prefill: score GEMM
@@ -815,9 +845,16 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   int* fault = fault_word();
   if (!span) {
     IdxWs ws = carve(wsp, q.n, R, false);
-    timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel, dim3(n_chunks + (upd ? 1 : 0), q.n),
-                 dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_chunks,
-                 upd ? *upd : UpdateArgs{}, fault);
+    const int cpw = scan_cpw(R);
+    const unsigned n_groups = (n_chunks + cpw - 1) / cpw;
+    const UpdateArgs ua = upd ? *upd : UpdateArgs{};
+    const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
+    if (cpw == 4)
+      timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel<4>, grid, dim3(256), 0, s, Qd,
+                   (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_groups, ua, fault);
+    else
+      timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel<1>, grid, dim3(256), 0, s, Qd,
+                   (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_groups, ua, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     launch_topk(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
