@@ -222,6 +222,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (qi >= a.n_q) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 15, g = lane >> 4;
+  // the query rows depend on nothing else: requested first
+  const int head = hg * 16 * NW + wave * 16 + col;
+  bf16x8 qb[4];
+  {
+    const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)qi * a.H + head) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
+  }
   int r;
   int64_t t;
   a.Q.get(qi, &r, &t, a.fault);
@@ -263,13 +271,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       resolve_ptr(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
   }
 
-  const int head = hg * 16 * NW + wave * 16 + col;
-  bf16x8 qb[4];
-  {
-    const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)qi * a.H + head) * kD);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
-  }
   __syncthreads();
 
   // ---- register double buffer of one chunk's rows.  K pieces: p = tid + NT*i
@@ -451,6 +452,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 // The (m, l) of every split are staged in LDS first; the partial rows are then
 // read with all loads of a thread in flight.
 constexpr int kMergeMaxSplits = 1024;
+constexpr int kMergePF = 32;          // partial outputs a merge thread requests up front
 __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
@@ -458,14 +460,22 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          float* __restrict__ lse) {
   const int qh = blockIdx.x;   // query * H + head
   const int q = qh / H, h = qh % H, d = threadIdx.x;
-  __shared__ float wgt[kMergeMaxSplits];
+  __shared__ float wgt[kMergeMaxSplits], lsm[kMergeMaxSplits];
   __shared__ float red[2];
   const int ns = n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits;
+  // the first kMergePF partial outputs, the (max, sum) pairs and the rest are
+  // all requested before anything waits on them: one memory round trip
+  const float* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
+  const int64_t stride = (int64_t)H * kD;
+  float v[kMergePF];
+#pragma unroll
+  for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : 0.f;
   float mloc = -INFINITY;
   for (int s = d; s < ns; s += 128) {
-    const float mv = part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
-    wgt[s] = mv;
-    mloc = fmaxf(mloc, mv);
+    const float2 ml = *(const float2*)&part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
+    wgt[s] = ml.x;
+    lsm[s] = ml.y;
+    mloc = fmaxf(mloc, ml.x);
   }
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
   if ((d & 63) == 0) red[d >> 6] = mloc;
@@ -476,24 +486,17 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
   for (int s = d; s < ns; s += 128) {
     const float wv = exp2f(wgt[s] - M);
     wgt[s] = wv;
-    lloc += wv * part_ml[(((int64_t)q * n_splits + s) * H + h) * 2 + 1];
+    lloc += wv * lsm[s];
   }
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
   if ((d & 63) == 0) red[d >> 6] = lloc;
   __syncthreads();
   const float L = red[0] + red[1];
   float acc = 0.f;
-  const float* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
-  const int64_t stride = (int64_t)H * kD;
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = po[(s + j) * stride];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc += wgt[s + j] * v[j];
-  }
-  for (; s < ns; ++s) acc += wgt[s] * po[s * stride];
+  for (int j = 0; j < kMergePF; ++j)
+    if (j < ns) acc += wgt[j] * v[j];
+  for (int s = kMergePF; s < ns; ++s) acc += wgt[s] * po[s * stride];
   const float o = L > 0.f ? acc / L : 0.f;
   if (o_f32)
     ((float*)O)[(int64_t)qh * kD + d] = o;
