@@ -56,8 +56,14 @@ constexpr int kZeroRow = -1;          // reads as zeros (neither a pool nor a wi
 
 // Row id of entry ge of a query: >= 0 is a row of the paged pool (page*64 + slot);
 // <= -2 encodes window row w as -2 - w; kZeroRow (-1) reads as zeros.
-__device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_t s0, int n_w,
-                                        int E, int64_t nv, int ge, int* rk, int* rv) {
+struct Prefetch;
+__device__ __forceinline__ int64_t entry_block(const AttnArgs& a, const Prefetch& pf, int qi, int j);
+__device__ __forceinline__ int entry_page(const AttnArgs& a, const Paged& c, const Prefetch& pf,
+                                          int which, int r, int64_t b);
+
+__device__ __forceinline__ void resolve(const AttnArgs& a, const Prefetch& pf, int qi, int r,
+                                        int64_t s0, int n_w, int E, int64_t nv, int ge, int* rk,
+                                        int* rv) {
   if (ge < n_w) {
     const int64_t p = s0 + ge;
     *rk = -2 - (int)((int64_t)r * a.wk.capacity + p % a.wk.capacity);
@@ -66,15 +72,48 @@ __device__ __forceinline__ void resolve(const AttnArgs& a, int qi, int r, int64_
   }
   *rk = *rv = kZeroRow;
   if (ge >= E) return;
-  const int j = ge - n_w;
-  const int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
+  const int64_t b = entry_block(a, pf, qi, ge - n_w);
   if (b < 0 || b >= nv) {
     atomicOr(a.fault, HSA_FAULT_INDEX);
     return;
   }
-  const int pk = a.kc.page_of(r, b, a.fault), pv = a.vc.page_of(r, b, a.fault);
+  const int pk = entry_page(a, a.kc, pf, 0, r, b), pv = entry_page(a, a.vc, pf, 1, r, b);
   if (pk >= 0) *rk = pk * kPage + (int)(b & 63);
   if (pv >= 0) *rv = pv * kPage + (int)(b & 63);
+}
+
+// Decode: what the rows of a split's entries depend on, loaded before the
+// query's position is known, over the span of entries the split can cover for
+// any window length 1..n_win: its top-k ids (CSA) or the page ids of its blocks
+// (HCA).  Lives in dynamic LDS.
+struct Prefetch {
+  const int* p;       // LDS, or nullptr (prefill: look up directly)
+  int lo;             // CSA: first idx position held; HCA: first page held
+  int n;              // entries held (CSA: idx positions; HCA: pages, K at p[i], V at p[64 + i])
+};
+constexpr int kPrePages = 64;   // HCA: page ids held per cache
+
+// block id of compressed entry j of query qi (CSA: its top-k id), or -1
+__device__ __forceinline__ int64_t entry_block(const AttnArgs& a, const Prefetch& pf, int qi,
+                                               int j) {
+  if (a.k <= 0) return j;
+  if (pf.p && j >= pf.lo && j < pf.lo + pf.n) return pf.p[j - pf.lo];
+  return a.idx[(int64_t)qi * a.k + j];
+}
+
+// physical page of block b of request r in cache c (which = 0: K, 1: V), or -1
+__device__ __forceinline__ int entry_page(const AttnArgs& a, const Paged& c, const Prefetch& pf,
+                                          int which, int r, int64_t b) {
+  if (pf.p && a.k <= 0) {
+    const int i = (int)(b >> 6) - pf.lo;
+    if (i >= 0 && i < pf.n) {
+      const int p = pf.p[which * kPrePages + i];
+      if ((unsigned)p < (unsigned)c.n_pages) return p;
+      atomicOr(a.fault, HSA_FAULT_PAGE);
+      return -1;
+    }
+  }
+  return c.page_of(r, b, a.fault);
 }
 
 // 256 bytes of zeros: the row read for entries past the end of a query's list
@@ -82,9 +121,9 @@ __device__ __align__(16) uint4 g_zero_row[16];
 
 // bf16 caches: the address of entry ge's K and V rows (window row, pool row, or
 // the zero row), so that a chunk's gathers are one load per 16-byte piece.
-__device__ __forceinline__ void resolve_ptr(const AttnArgs& a, int qi, int r, int64_t s0, int n_w,
-                                            int E, int64_t nv, int ge, const uint8_t** pk,
-                                            const uint8_t** pv) {
+__device__ __forceinline__ void resolve_ptr(const AttnArgs& a, const Prefetch& pf, int qi, int r,
+                                            int64_t s0, int n_w, int E, int64_t nv, int ge,
+                                            const uint8_t** pk, const uint8_t** pv) {
   const uint8_t* zero = (const uint8_t*)g_zero_row;
   if (ge < n_w) {
     const int64_t p = s0 + ge;
@@ -94,13 +133,12 @@ __device__ __forceinline__ void resolve_ptr(const AttnArgs& a, int qi, int r, in
   }
   *pk = *pv = zero;
   if (ge >= E) return;
-  const int j = ge - n_w;
-  const int64_t b = a.k > 0 ? (int64_t)a.idx[(int64_t)qi * a.k + j] : (int64_t)j;
+  const int64_t b = entry_block(a, pf, qi, ge - n_w);
   if (b < 0 || b >= nv) {
     atomicOr(a.fault, HSA_FAULT_INDEX);
     return;
   }
-  const int pgk = a.kc.page_of(r, b, a.fault), pgv = a.vc.page_of(r, b, a.fault);
+  const int pgk = entry_page(a, a.kc, pf, 0, r, b), pgv = entry_page(a, a.vc, pf, 1, r, b);
   if (pgk >= 0) *pk = a.kc.data + ((int64_t)pgk * kPage + (b & 63)) * (kD * 2);
   if (pgv >= 0) *pv = a.vc.data + ((int64_t)pgv * kPage + (b & 63)) * (kD * 2);
 }
@@ -230,16 +268,46 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = qp[4 * ks + g];
   }
-  int r;
-  int64_t t;
-  a.Q.get(qi, &r, &t, a.fault);
+  // the position, the request's entry counts and -- decode -- what the rows
+  // depend on (top-k ids, or page ids) are requested together, before any of
+  // them is used: one memory round trip instead of three
+  const bool listed = a.Q.pos != nullptr;
+  const int r = listed ? (a.Q.req ? a.Q.req[qi] : qi) : a.Q.span_req;
+  const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
+  const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
+  extern __shared__ int spre[];   // dynamic LDS: decode launches only
+  Prefetch pf{nullptr, 0, 0};
+  if (!a.xcd) {
+    const int e_nom = split * a.cps * 64, n_nom = a.cps * 64;
+    if (a.k > 0) {
+      const int lo = e_nom - a.n_win > 0 ? e_nom - a.n_win : 0;
+      const int hi = e_nom + n_nom < a.k ? e_nom + n_nom : a.k;
+      for (int i = tid; i < hi - lo; i += NT) spre[i] = a.idx[(int64_t)qi * a.k + lo + i];
+      pf = Prefetch{spre, lo, hi > lo ? hi - lo : 0};
+    } else if (!a.Q.req) {
+      const int p_lo = e_nom - a.n_win > 0 ? (e_nom - a.n_win) >> 6 : 0;
+      int n = ((e_nom + n_nom - 1) >> 6) + 1 - p_lo;
+      n = n < kPrePages ? n : kPrePages;
+      for (int i = tid; i < n; i += NT) {
+        const int lp = p_lo + i;
+        spre[i] = lp < a.kc.pages_per_req ? a.kc.page_table[(int64_t)r * a.kc.pages_per_req + lp] : -1;
+        spre[kPrePages + i] =
+            lp < a.vc.pages_per_req ? a.vc.page_table[(int64_t)r * a.vc.pages_per_req + lp] : -1;
+      }
+      pf = Prefetch{spre, p_lo, n};
+    }
+    __syncthreads();
+  }
+  int64_t t = p_raw;
+  if (listed && (t > a.Q.max_pos || t < 0)) {
+    atomicOr(a.fault, HSA_FAULT_POS);
+    t = t < 0 ? 0 : a.Q.max_pos;
+  }
   const int64_t s0 = window_start(t, a.n_win);
   const int n_w = (int)(t - s0 + 1);
   int64_t nv = n_visible(t, a.m, a.n_win);
   {
-    int64_t ne = a.kc.n_entries[r];
-    int64_t ne2 = a.vc.n_entries[r];
-    ne = ne < ne2 ? ne : ne2;
+    const int64_t ne = ne_k < ne_v ? ne_k : ne_v;
     if (nv > ne) {
       if (split == 0 && hg == 0 && tid == 0) atomicOr(a.fault, HSA_FAULT_ENTRIES);
       nv = ne < 0 ? 0 : ne;
@@ -266,9 +334,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int n_ent = (c_hi > c_lo) ? (c_hi - c_lo) * 64 : 0;
   for (int j = tid; j < n_ent; j += NT) {
     if constexpr (F8)
-      resolve(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve(a, pf, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
     else
-      resolve_ptr(a, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve_ptr(a, pf, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
   }
 
   __syncthreads();
@@ -827,15 +895,18 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
     return hipGetLastError();
   }
   const dim3 grid((unsigned)n_blocks);
+  // decode: LDS for the prefetched top-k ids (a split's entries plus one window)
+  // or page ids
+  const unsigned pre = span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int));
   if (p.nw == 4)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256), 0,
-                 s, a);
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256),
+                 pre, s, a);
   else if (p.nw == 2)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true> : attn_kernel<2, false>, grid, dim3(128), 0,
-                 s, a);
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true> : attn_kernel<2, false>, grid, dim3(128),
+                 pre, s, a);
   else
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true> : attn_kernel<1, false>, grid, dim3(64), 0,
-                 s, a);
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true> : attn_kernel<1, false>, grid, dim3(64),
+                 pre, s, a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
                                                             O, a.o_f32, lse);

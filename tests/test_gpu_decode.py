@@ -112,3 +112,56 @@ def test_decode_step_upkeep_and_outputs(layer):
             assert int(st[name].n_entries[r]) == n
             ref = orc.compress(d[x][: Ls[r] + S], st["z"][z], m)
             assert np.array_equal(T.cache_bits(st[name], r, n), ref.bits), (r, name)
+
+
+@pytest.mark.parametrize("layer", ["csa", "hca"])
+def test_listed_queries_name_their_request(layer):
+    """Queries that name their request: several queries of one request at
+    consecutive positions (as when a request verifies several new tokens at
+    once), interleaved across requests, with the full token arrays as the
+    window source.  Indexer + top-k and attention against the oracle."""
+    w = configs.shrink(configs.CSA_DECODE_128K, H=64, k_csa=64)
+    Ls = [3000, 9001]
+    S = 3
+    st = T.build_state(w, layer, Ls, steps=S)
+    m = w.m(layer)
+    reqs = st["reqs"]
+    cap = max(Ls) + S
+    full_k = np.zeros((2, cap, 128), dtype=np.uint16)
+    full_v = np.zeros_like(full_k)
+    for r, d in enumerate(reqs):
+        full_k[r, : Ls[r] + S] = d["k"]
+        full_v[r, : Ls[r] + S] = d["v"]
+    tk = L.Tokens(T.dev_bf16(full_k))
+    tv = L.Tokens(T.dev_bf16(full_v))
+    order = [(1, 0), (0, 0), (1, 1), (0, 1), (1, 2), (0, 2)]     # (request, step)
+    req = torch.tensor([r for r, _ in order], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([Ls[r] + s for r, s in order], dtype=torch.int64, device="cuda")
+    q = L.Queries.list(pos, cap - 1, req=req)
+    Q = T.dev_bf16(np.stack([reqs[r]["q"][s] for r, s in order]))
+    if layer == "csa":
+        qi = T.dev_bf16(np.stack([reqs[r]["qi"][s] for r, s in order]))
+        wt = torch.from_numpy(np.stack([reqs[r]["w"][s] for r, s in order])).cuda()
+        idx, _ = L.indexer_topk(q, qi, wt, st["kic"], m, w.n_win, w.k_csa)
+        O, lse = L.csa_attn(q, Q, tk, tv, w.n_win, st["kc"], st["vc"], m, idx, w.k_csa,
+                            with_lse=True, out_fp32=True)
+        idx = idx.cpu().numpy()
+    else:
+        O, lse = L.hca_attn(q, Q, tk, tv, w.n_win, st["kc"], st["vc"], m, with_lse=True,
+                            out_fp32=True)
+    L.check_device_error()
+    Ob, lse = T.to_f64(O), lse.cpu().numpy()
+    for i, (r, s) in enumerate(order):
+        d, t = reqs[r], Ls[r] + s
+        ref, (kc, vc) = oracle_row(w, layer, d, t, s)
+        if layer == "csa":
+            T.check_topk(idx[i], ref["scores"], w.k_csa, where=f"query {i}")
+            sel = idx[i][idx[i] >= 0]
+            if not np.array_equal(sel, ref["idx"][ref["idx"] >= 0]):
+                s0 = orc.window_start(t, w.n_win)
+                K = np.concatenate([nx.bf16_value(d["k"][s0:t + 1]), kc.values[sel]])
+                V = np.concatenate([nx.bf16_value(d["v"][s0:t + 1]), vc.values[sel]])
+                o, l = orc.attend(nx.bf16_value(d["q"][s]), K, V, T.scale_of())
+                ref = {"o": o, "lse": l}
+        assert np.max(np.abs(Ob[i] - ref["o"])) <= T.OUT_TOL, f"query {i}"
+        assert np.max(np.abs(lse[i] - ref["lse"])) <= T.LSE_TOL, f"query {i} lse"
