@@ -618,8 +618,11 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
   const int n_chunks = (E + 63) / 64;
   // tile 0 (t0): window entries 0..whi0, blocks < nv0; tile 1 (t1): window
   // entries wlo1..n_wu-1, blocks < nv1
-  const int whi0 = (int)(t0 - s0), wlo1 = (int)(s1 - s0);
-  const int end0 = n_wu + (int)nv0;
+  // uniform values, said so: the per-chunk mask test below stays a scalar branch
+  const int whi0 = __builtin_amdgcn_readfirstlane((int)(t0 - s0));
+  const int wlo1 = __builtin_amdgcn_readfirstlane((int)(s1 - s0));
+  const int end0 = __builtin_amdgcn_readfirstlane(n_wu + (int)nv0);
+  const int n_wuu = __builtin_amdgcn_readfirstlane(n_wu);
 
   __shared__ __align__(16) u16 Ks[64][136];
   __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     }
     // ---- masks, only in chunks that hold an entry outside either query's set
     const bool clean = e0 >= wlo1 && e0 + 64 <= end0 &&
-                       (whi0 == n_wu - 1 || e0 > whi0 + 1 || e0 + 63 < whi0 + 1);
+                       (whi0 == n_wuu - 1 || e0 > whi0 + 1 || e0 + 63 < whi0 + 1);
     if (__builtin_expect(!clean, 0)) {
 #pragma unroll
       for (int et = 0; et < 4; ++et)
