@@ -37,8 +37,7 @@ constexpr int kSelCH = 2048;       // blocks per select workgroup (multiple of k
 constexpr int kMaxSelChunks = 1024;  // select chunks whose offsets fit in LDS
 constexpr int kGemmMaxPages = 1024;  // pages of a prefill score workgroup resolved in LDS
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
-constexpr int kCoarse = 256;       // groups of 16 bins walked by the threshold search
-constexpr int kCandLds = 4096;     // candidates refined in LDS (more: in the workspace)
+constexpr int kBmLdsMaxWords = 16384;  // refine pass: bitmaps up to this size go to LDS
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
 constexpr int kStateInts = 8;      // -, -, thr_bin, n_above, n_cand, n_vis, n_thr_bin
 constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
@@ -488,8 +487,30 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
       sc0[u] = b < ws.R ? srow[b] : 0.f;
     }
   }
+  // mode 2: the threshold state, the first NT chunk candidate counts and the
+  // bitmap (into LDS when the host sized it in) are requested together, so
+  // the kernel waits for one round trip before the candidates
+  uint32_t cnt0 = 0;
+  uint32_t* bm_l = (uint32_t*)(dyn + 2 * (int64_t)cand_lds);
   if (mode == 2) {
-    if (tid == 0) { s_thr = st[2]; s_above = st[3]; s_ncand = (uint32_t)st[4]; s_dabove = st[6]; }
+    const int thr2 = st[2], above2 = st[3], dab2 = st[6];
+    const int n_ch = (int)(ws.R / kSelCH);
+    if (tid < n_ch) cnt0 = (uint32_t)ws.ccount[(int64_t)qrow * n_ch + tid];
+    const int W4 = bm_lds_words / 4;
+    const uint4* bsrc = (const uint4*)(ws.bitmap + (int64_t)qrow * (ws.R / 32));
+    if constexpr (NT >= 1024) {
+      constexpr int kBmPer = kBmLdsMaxWords / 4 / NT;
+      uint4 bw[kBmPer];
+#pragma unroll
+      for (int u = 0; u < kBmPer; ++u)
+        if (u * NT + tid < W4) bw[u] = bsrc[u * NT + tid];
+#pragma unroll
+      for (int u = 0; u < kBmPer; ++u)
+        if (u * NT + tid < W4) ((uint4*)bm_l)[u * NT + tid] = bw[u];
+    } else {
+      for (int i = tid; i < W4; i += NT) ((uint4*)bm_l)[i] = bsrc[i];
+    }
+    if (tid == 0) { s_thr = thr2; s_above = above2; s_dabove = dab2; }
     __syncthreads();
   } else {
   // ---- threshold bin: thread i owns bins kBins-BPT(i+1) .. kBins-BPT*i-1 (descending)
@@ -501,28 +522,37 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     // step costs one memory round trip; entries past a list's count are
     // ignored.
     uint32_t* lh = (uint32_t*)dyn;
-    for (int i = tid; i < kBins; i += NT) lh[i] = 0;
-    __syncthreads();
-    const int n_used = nv > 0 ? (int)((nv + ws.list_span - 1) / ws.list_span) : 1;
     const int32_t* hn = ws.hl_n + (int64_t)qrow * ws.n_lists;
     const uint32_t* hlq = ws.hl + (int64_t)qrow * ws.n_lists * ws.list_cap;
     constexpr int NWV = NT / 64, LB = 8;
-    for (int c0 = wv * LB; c0 < n_used; c0 += NWV * LB) {
-      int cnt[LB];
-      uint32_t e0[LB], e1[LB];
+    int cnt[LB];
+    uint32_t e0[LB], e1[LB];
+    // lists c0 .. c0 + LB - 1, clamped to the workspace's lists; the counts of
+    // lists past the row's visible blocks are dropped once its length is known
+    auto load_step = [&](int c0) {
 #pragma unroll
       for (int j = 0; j < LB; ++j) {
-        const int c = c0 + j < n_used ? c0 + j : c0;
-        cnt[j] = c0 + j < n_used ? hn[c] : 0;
+        const int c = c0 + j < ws.n_lists ? c0 + j : ws.n_lists - 1;
+        cnt[j] = hn[c];
         const uint32_t* L = hlq + (int64_t)c * ws.list_cap;   // list_cap >= 128
         e0[j] = L[lane];
         e1[j] = L[64 + lane];
       }
+    };
+    // the first step's lists are requested before the row length arrives and
+    // while the LDS histogram is cleared
+    if (wv * LB < ws.n_lists) load_step(wv * LB);
+    for (int i = tid; i < kBins; i += NT) lh[i] = 0;
+    __syncthreads();
+    const int n_used = nv > 0 ? (int)((nv + ws.list_span - 1) / ws.list_span) : 1;
+    for (int c0 = wv * LB; c0 < n_used; c0 += NWV * LB) {
+      if (c0 != wv * LB) load_step(c0);
 #pragma unroll
       for (int j = 0; j < LB; ++j) {
-        if (lane < cnt[j]) atomicAdd(&lh[e0[j] >> 16], e0[j] & 0xFFFFu);
-        if (64 + lane < cnt[j]) atomicAdd(&lh[e1[j] >> 16], e1[j] & 0xFFFFu);
-        for (int i = 128 + lane; i < cnt[j]; i += 64) {   // long lists
+        const int nj = c0 + j < n_used ? cnt[j] : 0;
+        if (lane < nj) atomicAdd(&lh[e0[j] >> 16], e0[j] & 0xFFFFu);
+        if (64 + lane < nj) atomicAdd(&lh[e1[j] >> 16], e1[j] & 0xFFFFu);
+        for (int i = 128 + lane; i < nj; i += 64) {   // long lists
           const uint32_t e = hlq[(int64_t)(c0 + j) * ws.list_cap + i];
           atomicAdd(&lh[e >> 16], e & 0xFFFFu);
         }
@@ -561,7 +591,6 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   const uint32_t n_thr_bin = thr >= 0 ? s_dabove : 0;
   uint64_t* ca = dyn;
   uint64_t* cb = dyn + cand_lds;
-  uint32_t* bm_l = (uint32_t*)(dyn + 2 * (int64_t)cand_lds);
   const int64_t W = (nv + 31) / 32;
   const bool cand_in_lds = n_thr_bin <= (uint32_t)cand_lds;
   uint64_t* csrc = cand_in_lds ? ca : ws.cand + (int64_t)qrow * ws.R;
@@ -579,7 +608,7 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     uint32_t run = 0;
     for (int c0 = 0; c0 < n_ch; c0 += NT) {
       const int c = c0 + tid;
-      const uint32_t cnt = c < n_ch ? (uint32_t)cc[c] : 0u;
+      const uint32_t cnt = c0 == 0 ? cnt0 : (c < n_ch ? (uint32_t)cc[c] : 0u);
       uint32_t tot;
       const uint32_t off = block_scan_nt<NT>(cnt, &tot, sh) + run;
       if (n_ch <= kMaxSelChunks) {
@@ -608,8 +637,8 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     csrc = dstc;
     cdst = cand_in_lds ? cb : ws.cand + (int64_t)qrow * ws.R;
   }
-  uint32_t* bm = (mode == 0 && W <= bm_lds_words) ? bm_l
-                                                   : ws.bitmap + (int64_t)qrow * (ws.R / 32);
+  const bool bm_in_lds = W <= bm_lds_words;
+  uint32_t* bm = bm_in_lds ? bm_l : ws.bitmap + (int64_t)qrow * (ws.R / 32);
 
   // ---- one pass over the scores: bitmap of blocks above the bin, candidates in it
   for (int64_t base = 0; mode == 0 && base < nv; base += (int64_t)NT * U) {
@@ -718,7 +747,8 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     const int64_t w0 = r0 + (int64_t)tid * 8;
     uint32_t wd[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wd[i] = w0 + i < W ? ld_agent(bm + w0 + i) : 0u;
+    for (int i = 0; i < 8; ++i)
+      wd[i] = w0 + i < W ? (bm_in_lds ? bm_l[w0 + i] : ld_agent(bm + w0 + i)) : 0u;
     uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) cnt += __popc(wd[i]);
@@ -827,8 +857,10 @@ static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, fl
   idx_topk_kernel<1024><<<nq, 1024, kBins * sizeof(uint32_t), s>>>(k, ws, idx, score, out_row0,
                                                                     0, 0, 1);
   idx_select_kernel<<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
-  const size_t lds = (size_t)2 * cand * sizeof(uint64_t);
-  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, 0, 2);
+  // the bitmap joins the candidates in LDS when it fits
+  const int bm_words = W <= kBmLdsMaxWords ? (int)W : 0;
+  const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
+  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
