@@ -275,7 +275,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int r = listed ? (a.Q.req ? a.Q.req[qi] : qi) : a.Q.span_req;
   const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
   const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
-  extern __shared__ int spre[];   // dynamic LDS: decode launches only
+  // dynamic LDS: the row ids of the split's entries (K, then V), then -- decode
+  // launches -- the prefetched top-k or page ids
+  // (fp8: 32-bit row ids, pool rows holding fp8 codes and window rows bf16;
+  // bf16: row addresses)
+  typedef typename std::conditional<F8, int, const uint8_t*>::type RowT;
+  extern __shared__ __align__(16) int dyn_lds[];
+  RowT* rowk = (RowT*)dyn_lds;
+  RowT* rowv = rowk + a.cps * 64;
+  int* spre = (int*)(rowv + a.cps * 64);
   Prefetch pf{nullptr, 0, 0};
   if (!a.xcd) {
     const int e_nom = split * a.cps * 64, n_nom = a.cps * 64;
@@ -324,10 +332,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __shared__ __align__(16) u16 Ks[64][136];
   __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
   __shared__ float ksc[64];
-  // fp8: 32-bit row ids (pool rows hold fp8 codes, window rows bf16);
-  // bf16: row addresses
-  typedef typename std::conditional<F8, int, const uint8_t*>::type RowT;
-  __shared__ RowT rowk[kMaxCps * 64], rowv[kMaxCps * 64];
 
   // ---- resolve the rows of every entry of this split once
   const int e_base = c_lo * 64;
@@ -626,8 +630,11 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
 
   __shared__ __align__(16) u16 Ks[64][136];
   __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
-  __shared__ const uint8_t* rowk[kMaxCps * 64];
-  __shared__ const uint8_t* rowv[kMaxCps * 64];
+  // dynamic LDS: row addresses of the union's entries (K, then V), sized by
+  // the host for the longest union
+  extern __shared__ __align__(16) int dyn_lds[];
+  const uint8_t** rowk = (const uint8_t**)dyn_lds;
+  const uint8_t** rowv = rowk + a.cps * 64;
   {
     const uint8_t* zero = (const uint8_t*)g_zero_row;
     for (int j = tid; j < n_chunks * 64; j += NT) {
@@ -893,14 +900,18 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
       wk.capacity >= need_cap && wv.capacity >= need_cap) {
     a.n_hg = H / 64;
     a.n_splits = 1;
+    a.cps = (int)((n_win + 1 + nv_max + 63) / 64);   // chunks of the longest union
     const int64_t nb = ((int64_t)(q.n + 1) / 2 * a.n_hg + 7) / 8 * 8;
-    timed_launch(HSA_K_ATTN, attn_pair_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
+    timed_launch(HSA_K_ATTN, attn_pair_kernel, dim3((unsigned)nb), dim3(256),
+                 (unsigned)(2 * a.cps * 64 * sizeof(const uint8_t*)), s, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)n_blocks);
-  // decode: LDS for the prefetched top-k ids (a split's entries plus one window)
-  // or page ids
-  const unsigned pre = span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int));
+  // dynamic LDS: the row ids of a split's entries, and -- decode -- the
+  // prefetched top-k ids (a split's entries plus one window) or page ids
+  const size_t row_bytes = f8 ? sizeof(int) : sizeof(const uint8_t*);
+  const unsigned pre = (unsigned)(2 * p.cps * 64 * row_bytes) +
+                       (span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int)));
   if (p.nw == 4)
     timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256),
                  pre, s, a);
