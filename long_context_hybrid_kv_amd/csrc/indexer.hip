@@ -324,13 +324,16 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
 
 // ---------------------------------------------------------------- prefill: score GEMM
 
-// 16 consecutive query tokens per workgroup (4 A tiles of 4 queries x 4 heads),
-// blocks split over gridDim.y; every wave walks 16-block B tiles.
+// 16 consecutive query tokens per workgroup (4 A tiles of 4 queries x 4 heads,
+// gridDim.y), blocks split over gridDim.x; every wave walks 16-block B tiles.
+// The block range is the fast grid index and the number of ranges a multiple
+// of 8: workgroups are dealt to the 8 XCDs round-robin, so each XCD's L2
+// holds the keys of one eighth of the blocks instead of all of them.
 __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, int nq,
                                                        const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, IdxWs ws, int* fault) {
-  const int qt = blockIdx.x;
+  const int qt = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
   const int r = Q.span_req;
   const int64_t ne = kic.n_entries[r];
@@ -365,14 +368,14 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     int ql = 16 * qt + 15 < nq ? 16 * qt + 15 : nq - 1;
     int64_t nv = n_visible(Q.span_pos0 + q_base + ql, m, n_win);
     if (nv > ne) {
-      if (threadIdx.x == 0 && blockIdx.y == 0) atomicOr(fault, HSA_FAULT_ENTRIES);
+      if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(fault, HSA_FAULT_ENTRIES);
       nv = ne;
     }
     nv_max = nv;
   }
   const int64_t n_tiles = (nv_max + 15) / 16;
-  const int64_t per = (n_tiles + gridDim.y - 1) / gridDim.y;
-  const int64_t t_lo = per * blockIdx.y;
+  const int64_t per = (n_tiles + gridDim.x - 1) / gridDim.x;
+  const int64_t t_lo = per * blockIdx.x;
   const int64_t t_hi = t_lo + per < n_tiles ? t_lo + per : n_tiles;
   // physical pages of the workgroup's tile range, resolved once
   __shared__ int pg[kGemmMaxPages];
@@ -898,10 +901,12 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     // chunk-local maximum of the visible blocks bounds the work of this pass
     int64_t nv_hi = host_nvis(q.span_pos0 + q0 + nq - 1, m, n_win);
     int64_t tiles = (nv_hi + 15) / 16;
-    unsigned bsplit = (unsigned)((tiles + 255) / 256);   // ~256 block tiles per workgroup
+    // ~128 block tiles per workgroup, in a multiple of 8 block ranges
+    unsigned bsplit = (unsigned)((tiles + 127) / 128);
     if (bsplit < 1) bsplit = 1;
-    if (bsplit > 64) bsplit = 64;
-    timed_launch(HSA_K_INDEXER_GEMM, idx_gemm_kernel, dim3((nq + 15) / 16, bsplit), dim3(256), 0,
+    if (bsplit > 512) bsplit = 512;
+    bsplit = (bsplit + 7) / 8 * 8;
+    timed_launch(HSA_K_INDEXER_GEMM, idx_gemm_kernel, dim3(bsplit, (nq + 15) / 16), dim3(256), 0,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
