@@ -242,7 +242,7 @@ __device__ __forceinline__ uint4 v_piece_f16(uint4 raw, bool fp8, float scale) {
                     pack_f16(f[6], f[7]));
 }
 
-template <int NW, bool F8>
+template <int NW, bool F8, bool SH>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PPT = 1024 / NT;          // K (and V) pieces per thread per chunk
@@ -329,8 +329,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int c_lo = split * a.cps;
   const int c_hi = c_lo + a.cps < n_chunks ? c_lo + a.cps : n_chunks;
 
-  __shared__ __align__(16) u16 Ks[64][136];
-  __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
+  // K tile (row-major bf16) and V^T tile (fp16 bits).  SH: one buffer for both,
+  // V^T staged once every wave has read the K tile (half the LDS, so more
+  // workgroups fit on a CU, for two more barriers per chunk)
+  constexpr int kKsH = 64 * 136, kVtH = 128 * 72;
+  __shared__ __align__(16) u16 kv_lds[SH ? (kVtH > kKsH ? kVtH : kKsH) : kKsH + kVtH];
+  u16(*Ks)[136] = (u16(*)[136])kv_lds;
+  u16(*Vt)[72] = (u16(*)[72])(kv_lds + (SH ? 0 : kKsH));
   __shared__ float ksc[64];
 
   // ---- resolve the rows of every entry of this split once
@@ -353,24 +358,35 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   int krow[PPT], vrow[PPT];
   float kscl[PPT], vscl[PPT];
   const int vpair = tid & 31;
-  auto issue = [&](int c) {
+  auto issue_k = [&](int c) {
     const int lo = (c - c_lo) * 64;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
-      const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
       if constexpr (F8) {
         krow[i] = rowk[lo + ek];
         kraw[i] = load_piece<F8>(a.kc, a.wk, krow[i], cgk);
         kscl[i] = row_scale<F8>(a.kc, krow[i]);
+      } else {
+        krow[i] = 0;
+        kscl[i] = 1.f;
+        kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
+      }
+    }
+  };
+  auto issue_v = [&](int c) {
+    const int lo = (c - c_lo) * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
+      if constexpr (F8) {
         vrow[i] = rowv[lo + ev];
         vraw[i] = load_piece<F8>(a.vc, a.wv, vrow[i], cgv);
         vscl[i] = row_scale<F8>(a.vc, vrow[i]);
       } else {
-        krow[i] = vrow[i] = 0;
-        kscl[i] = vscl[i] = 1.f;
-        kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
+        vrow[i] = 0;
+        vscl[i] = 1.f;
         vraw[i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
       }
     }
@@ -385,17 +401,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
-  if (c_lo < c_hi) issue(c_lo);
-  for (int c = c_lo; c < c_hi; ++c) {
-    const int e0 = c * 64;
-    // ---- stage K (row-major bf16) and V (transposed fp16) for entries e0 .. e0+63
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      const int ek = p >> 4, cgk = p & 15;
-      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0);
-      if (cgk == 0) ksc[ek] = kscl[i];
-    }
+  // V (transposed fp16) of the chunk in vraw -> Vt
+  auto stage_v = [&]() {
 #pragma unroll
     for (int j = 0; j < PPT / 2; ++j) {
       const int cgv = (tid >> 5) + (NT / 32) * j;
@@ -409,8 +416,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
       }
     }
+  };
+
+  if (c_lo < c_hi) {
+    issue_k(c_lo);
+    issue_v(c_lo);
+  }
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int e0 = c * 64;
+    // ---- stage K (row-major bf16), and V unless it waits for the K tile's reads
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      const int ek = p >> 4, cgk = p & 15;
+      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0);
+      if (cgk == 0) ksc[ek] = kscl[i];
+    }
+    if constexpr (!SH) stage_v();
     __syncthreads();
-    if (c + 1 < c_hi) issue(c + 1);   // next chunk's rows load while this one computes
+    // next chunk's rows load while this one computes
+    if (c + 1 < c_hi) {
+      issue_k(c + 1);
+      if constexpr (!SH) issue_v(c + 1);
+    }
 
     // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads)
     f32x4 sacc[4];
@@ -460,6 +488,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       osum *= alpha;
     }
 
+    if constexpr (SH) {
+      __syncthreads();   // every wave has read the K tile
+      stage_v();
+      __syncthreads();
+      if (c + 1 < c_hi) issue_v(c + 1);
+    }
     // ---- O^T += V^T P^T, two k-steps of 32 entries.  P is rounded to fp16
     // once; an extra tile of ones in place of V^T rows accumulates the row
     // sums of exactly those rounded weights.
@@ -628,8 +662,11 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
   const int end0 = __builtin_amdgcn_readfirstlane(n_wu + (int)nv0);
   const int n_wuu = __builtin_amdgcn_readfirstlane(n_wu);
 
-  __shared__ __align__(16) u16 Ks[64][136];
-  __shared__ __align__(16) u16 Vt[128][72];    // fp16 bits
+  // one LDS buffer for the K tile and then the V^T tile (fp16 bits), staged
+  // once every wave has read the K tile
+  __shared__ __align__(16) u16 kv_lds[128 * 72];
+  u16(*Ks)[136] = (u16(*)[136])kv_lds;
+  u16(*Vt)[72] = (u16(*)[72])kv_lds;
   // dynamic LDS: row addresses of the union's entries (K, then V), sized by
   // the host for the longest union
   extern __shared__ __align__(16) int dyn_lds[];
@@ -666,14 +703,19 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
 
   uint4 kraw[PPT], vraw[PPT];
   const int vpair = tid & 31;
-  auto issue = [&](int c) {
+  auto issue_k = [&](int c) {
     const int lo = c * 64;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
-      const int ek = p >> 4, cgk = p & 15;
+      kraw[i] = gload16((uintptr_t)rowk[lo + (p >> 4)] + (p & 15) * 16);
+    }
+  };
+  auto issue_v = [&](int c) {
+    const int lo = c * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
       const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
-      kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
       vraw[i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
     }
   };
@@ -690,14 +732,7 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
-  if (n_chunks > 0) issue(0);
-  for (int c = 0; c < n_chunks; ++c) {
-    const int e0 = c * 64;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + NT * i;
-      *(uint4*)&Ks[p >> 4][(p & 15) * 8] = kraw[i];
-    }
+  auto stage_v = [&]() {
 #pragma unroll
     for (int j = 0; j < PPT / 2; ++j) {
       const int cgv = (tid >> 5) + (NT / 32) * j;
@@ -711,8 +746,21 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
         vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
       }
     }
+  };
+
+  if (n_chunks > 0) {
+    issue_k(0);
+    issue_v(0);
+  }
+  for (int c = 0; c < n_chunks; ++c) {
+    const int e0 = c * 64;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + NT * i;
+      *(uint4*)&Ks[p >> 4][(p & 15) * 8] = kraw[i];
+    }
     __syncthreads();
-    if (c + 1 < n_chunks) issue(c + 1);
+    if (c + 1 < n_chunks) issue_k(c + 1);
 
     // ---- S^T = K Q^T for both queries; each K operand read once
     f32x4 sacc[2][4];
@@ -773,6 +821,10 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
                        ex2(__builtin_fmaf(sacc[j][2 * h + 1][i + 1], a.scale_log2, -m_new)));
         }
     }
+    __syncthreads();   // every wave has read the K tile
+    stage_v();
+    __syncthreads();
+    if (c + 1 < n_chunks) issue_v(c + 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const f16x8 pb0 = __builtin_bit_cast(f16x8, make_uint4(pw[0][h][0], pw[0][h][1], pw[0][h][2], pw[0][h][3]));
@@ -912,15 +964,19 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   const size_t row_bytes = f8 ? sizeof(int) : sizeof(const uint8_t*);
   const unsigned pre = (unsigned)(2 * p.cps * 64 * row_bytes) +
                        (span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int)));
-  if (p.nw == 4)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true> : attn_kernel<4, false>, grid, dim3(256),
-                 pre, s, a);
+  // prefill (many workgroups per CU help): one LDS buffer for the K and V^T
+  // tiles; decode (few workgroups, latency first): two
+  if (p.nw == 4 && span && !f8)
+    timed_launch(HSA_K_ATTN, attn_kernel<4, false, true>, grid, dim3(256), pre, s, a);
+  else if (p.nw == 4)
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true, false> : attn_kernel<4, false, false>, grid,
+                 dim3(256), pre, s, a);
   else if (p.nw == 2)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true> : attn_kernel<2, false>, grid, dim3(128),
-                 pre, s, a);
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true, false> : attn_kernel<2, false, false>, grid,
+                 dim3(128), pre, s, a);
   else
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true> : attn_kernel<1, false>, grid, dim3(64),
-                 pre, s, a);
+    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true, false> : attn_kernel<1, false, false>, grid,
+                 dim3(64), pre, s, a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
                                                             O, a.o_f32, lse);
