@@ -557,6 +557,28 @@ def bench_prefill(args, w):
                          "algorithmic_flops_per_launch": kfl, "avg_launch_ms": round(kms, 4)}}
 
 
+def calibrate_read(nbytes=134_217_728, reps=48):
+    """Per-launch time of a library reduction (row maxima of a [n, 4096] fp32
+    tensor) that reads nbytes once and writes almost nothing, over 8 buffers
+    so the Infinity Cache cannot hold them: the reference point for a single
+    streaming pass over as many bytes as the decode scan reads."""
+    import torch
+    bufs = [torch.randn(nbytes // 4 // 4096, 4096, device="cuda") for _ in range(8)]
+    out = torch.empty(bufs[0].shape[0], device="cuda")
+    ms = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.amax(bufs[i % 8], dim=1, out=out)
+        e1.record()
+        e1.synchronize()
+        if i >= 8:
+            ms.append(e0.elapsed_time(e1))
+    mean = sum(ms) / len(ms)
+    return {"calibration": "read", "bytes": nbytes, "mean_us": round(mean * 1e3, 2),
+            "best_us": round(min(ms) * 1e3, 2), "mean_TBps": round(nbytes / (mean * 1e-3) / 1e12, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -570,6 +592,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--calibrate-read", action="store_true",
+                    help="only time single launches of a plain 134 MB read (row maxima), "
+                         "rotating over 8 buffers: what one pass over the scan's bytes costs")
     ap.add_argument("--traffic-summary", nargs=6,
                     metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                              "COPY_WRITE_CSV"),
@@ -592,6 +617,9 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes": 1 << 30}))
+        return
+    if args.calibrate_read:
+        print(json.dumps(calibrate_read()))
         return
     from synth import configs
     runners = {"csa_decode_128k": (lambda a, w: bench_csa_decode(a, w)[0], configs.CSA_DECODE_128K,

@@ -430,7 +430,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
       *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0);
-      if (cgk == 0) ksc[ek] = kscl[i];
+      if constexpr (F8)   // page scale of each key row (bf16 rows need none)
+        if (cgk == 0) ksc[ek] = kscl[i];
     }
     if constexpr (!SH) stage_v();
     __syncthreads();
