@@ -863,7 +863,12 @@ static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, fl
   // the bitmap joins the candidates in LDS when it fits
   const int bm_words = W <= kBmLdsMaxWords ? (int)W : 0;
   const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
-  idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
+  // rows up to 64K blocks: four waves refine and emit (cheaper barriers); longer
+  // rows: sixteen (their bitmap takes 8 words per thread per round)
+  if (W <= 2048)
+    idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
+  else
+    idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
