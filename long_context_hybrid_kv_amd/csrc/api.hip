@@ -270,7 +270,7 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
                             int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
   hsa_status s;
-  if ((s = check_paged(kIc, "kIc", kDI, false)) != HSA_OK) return s;
+  if ((s = check_paged(kIc, "kIc", kDI, true)) != HSA_OK) return s;
   if ((s = check_queries(q, kIc->n_req)) != HSA_OK) return s;
   REQ(qI && w && idx, "indexer_topk: null qI, w or idx");
   SUP(H_I == kHI && d_I == kDI, "indexer_topk: H_I must be 4 and d_I 64");

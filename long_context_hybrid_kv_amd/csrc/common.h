@@ -69,6 +69,23 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
   return s | (em < 8u ? sub : nrm);
 }
 
+// 8 e4m3fn codes (two 32-bit words, code 0 in the lowest byte) -> 8 bf16
+// values, by the hardware converter: every e4m3 value is a float with at most
+// 4 significant bits, so dropping the float's low 16 bits is exact.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 c) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+  const f2 p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+  const f2 p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+  const f2 p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+  auto two = [](f2 v) {
+    return (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xFFFF0000u);
+  };
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, (u4{two(p0), two(p1), two(p2), two(p3)}));
+}
+
 // Order-preserving 32-bit key of a float (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);

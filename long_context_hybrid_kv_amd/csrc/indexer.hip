@@ -24,6 +24,8 @@
 //            ascending block order.
 // The counters and histograms at the head of the workspace are cleared before
 // every call (and by finalize, for the next query chunk of a prefill call).
+#include <type_traits>
+
 #include "update.h"
 
 namespace hsa {
@@ -208,7 +210,7 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
 
 // ---------------------------------------------------------------- decode: score scan
 
-template <int CPW>
+template <int CPW, bool F8K>
 __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
@@ -245,17 +247,26 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   if (c_first == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
 
   constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave and chunk
+  // key pieces of a lane: 8 channels each (bf16: 16 bytes; fp8 codes: 8 bytes,
+  // widened to bf16 when scored, the page scale applied to the head sum)
+  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  float ksc[CPW][2];   // fp8: scale of the wave's two pages of each chunk
   // branch-free loads: blocks out of range (or on a bad page) read row 0 of page 0
-  auto load = [&](int c, bf16x8* x0, bf16x8* x1) {
+  auto load = [&](int c, KeyT* x0, KeyT* x1) {
     const int64_t cb = (int64_t)(c_first + c) * kCH;
     const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
     const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
+    if constexpr (F8K) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ksc[c][j] = (unsigned)pid[c][j] < (unsigned)kic.n_pages ? kic.scale[pid[c][j]] : 1.f;
+    }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       const int64_t b = w0b + 16 * u + row;
       const int pg = pid[c][u >> 2];
       const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
-      const bf16x8* kr = (const bf16x8*)kic.row(ok ? pg : 0, ok ? b : 0);
+      const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
       x0[u] = __builtin_nontemporal_load(kr + g);
       x1[u] = __builtin_nontemporal_load(kr + 4 + g);
     }
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
           atomicOr(fault, HSA_FAULT_PAGE);
     }
   };
-  bf16x8 xa0[NT], xa1[NT], xb0[NT], xb1[NT];
+  KeyT xa0[NT], xa1[NT], xb0[NT], xb1[NT];
   load(0, xa0, xa1);
   if (CPW > 1) load(1, xb0, xb1);
 
@@ -284,19 +295,28 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
   __syncthreads();
 
-  auto score = [&](int c, const bf16x8* x0, const bf16x8* x1) {
+  auto score = [&](int c, const KeyT* x0, const KeyT* x1) {
     const int64_t cb = (int64_t)(c_first + c) * kCH;
     const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
     const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
+      bf16x8 k0, k1;
+      if constexpr (F8K) {
+        k0 = e4m3x8_to_bf16x8(x0[u]);
+        k1 = e4m3x8_to_bf16x8(x1[u]);
+      } else {
+        k0 = x0[u];
+        k1 = x1[u];
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, x0[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, x1[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1, acc, 0, 0, 0);
       const int64_t b = w0b + 16 * u + row;
       if (g == 0 && b < b_end) {
-        const float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
-                         w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+        float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
+                   w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
+        if constexpr (F8K) sc *= ksc[c][u >> 2];   // ReLU commutes with a scale > 0
         lsc[b - (int64_t)c_first * kCH] = sc;
         atomicAdd(&lhist[order_key(sc) >> 20], 1u);
       }
@@ -329,6 +349,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
 // The block range is the fast grid index and the number of ranges a multiple
 // of 8: workgroups are dealt to the 8 XCDs round-robin, so each XCD's L2
 // holds the keys of one eighth of the blocks instead of all of them.
+template <bool F8K>
 __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, int nq,
                                                        const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
@@ -389,34 +410,49 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   // branch-free key loads (rows past the end, or on a bad page, read row 0 of
   // page 0 and are never stored); the next tile's keys load while this one's
   // scores are computed
-  auto load = [&](int64_t tile, bf16x8& x0, bf16x8& x1) {
+  // key pieces: bf16 (16 bytes) or fp8 codes (8 bytes, widened to bf16 when
+  // scored, with the page scale applied to the head sum)
+  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  auto load = [&](int64_t tile, KeyT& x0, KeyT& x1, float& sc) {
     const int64_t b = 16 * tile + row;
     int page = -1;
     if (b < nv_max) page = pg_lds ? pg[(b >> 6) - p_lo] : kic.page_of(r, b, fault);
     const bool ok = page >= 0;
-    const bf16x8* kr = (const bf16x8*)kic.row(ok ? page : 0, ok ? b : 0);
+    const KeyT* kr = (const KeyT*)kic.row(ok ? page : 0, ok ? b : 0);
     x0 = kr[g];
     x1 = kr[4 + g];
+    if constexpr (F8K) sc = ok ? kic.scale[page] : 1.f;
   };
-  bf16x8 c0, c1, n0 = {}, n1 = {};
+  KeyT c0, c1, n0 = {}, n1 = {};
+  float cs = 1.f, ns = 1.f;
   int64_t tile = t_lo + wv;
-  if (tile < t_hi) load(tile, c0, c1);
+  if (tile < t_hi) load(tile, c0, c1, cs);
   for (; tile < t_hi; tile += 4) {
-    if (tile + 4 < t_hi) load(tile + 4, n0, n1);
+    if (tile + 4 < t_hi) load(tile + 4, n0, n1, ns);
     const int64_t b = 16 * tile + row;
+    bf16x8 k0, k1;
+    if constexpr (F8K) {
+      k0 = e4m3x8_to_bf16x8(c0);
+      k1 = e4m3x8_to_bf16x8(c1);
+    } else {
+      k0 = c0;
+      k1 = c1;
+    }
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], c0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], c1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], k0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], k1, acc, 0, 0, 0);
       if (b < nvq[at]) {
         float s = wq[at][0] * fmaxf(acc[0], 0.f) + wq[at][1] * fmaxf(acc[1], 0.f) +
                   wq[at][2] * fmaxf(acc[2], 0.f) + wq[at][3] * fmaxf(acc[3], 0.f);
+        if constexpr (F8K) s *= cs;   // ReLU commutes with a scale > 0
         ws.scores[(int64_t)(16 * qt + 4 * at + g) * ws.R + b] = s;
       }
     }
     c0 = n0;
     c1 = n1;
+    cs = ns;
   }
 }
 
@@ -889,12 +925,11 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const unsigned n_groups = (n_chunks + cpw - 1) / cpw;
     const UpdateArgs ua = upd ? *upd : UpdateArgs{};
     const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
-    if (cpw == 4)
-      timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel<4>, grid, dim3(256), 0, s, Qd,
-                   (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_groups, ua, fault);
-    else
-      timed_launch(HSA_K_INDEXER_SCAN, idx_scan_kernel<1>, grid, dim3(256), 0, s, Qd,
-                   (const u16*)qI, w, kc, m, n_win, k, ws, (int)n_groups, ua, fault);
+    const bool f8k = kic.dtype == HSA_FP8_E4M3;
+    auto scan = cpw == 4 ? (f8k ? idx_scan_kernel<4, true> : idx_scan_kernel<4, false>)
+                         : (f8k ? idx_scan_kernel<1, true> : idx_scan_kernel<1, false>);
+    timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m,
+                 n_win, k, ws, (int)n_groups, ua, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     launch_topk(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
@@ -911,7 +946,9 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     if (bsplit < 1) bsplit = 1;
     if (bsplit > 512) bsplit = 512;
     bsplit = (bsplit + 7) / 8 * 8;
-    timed_launch(HSA_K_INDEXER_GEMM, idx_gemm_kernel, dim3(bsplit, (nq + 15) / 16), dim3(256), 0,
+    timed_launch(HSA_K_INDEXER_GEMM,
+                 kic.dtype == HSA_FP8_E4M3 ? idx_gemm_kernel<true> : idx_gemm_kernel<false>,
+                 dim3(bsplit, (nq + 15) / 16), dim3(256), 0,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
