@@ -48,9 +48,11 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False):
+def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False):
     """Caches of B requests holding tokens 0..L-1, rings up to L-1, and the new
-    token's inputs (position L).  Returns (layers[copies], step inputs)."""
+    token's inputs (position L).  Returns (layers[copies], step inputs).
+    index_fp8: the indexer keys are stored fp8 (e4m3fn, one scale per page), and
+    step["kic_bf16"] holds the same keys in bf16 (for the selection recall)."""
     import torch
     B, m, n_win = w.B, w.m(layer), w.n_win
     z = gen.pool_logits(w, layer)
@@ -61,7 +63,8 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False):
     perm = torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None
     kc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
     vc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
-    kic = T.PagedCache.allocate(B, n_ent, 64, page_order=perm) if layer == "csa" else None
+    kic = T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, page_order=perm) if layer == "csa" else None
+    kic16 = T.PagedCache.allocate(B, n_ent, 64, page_order=perm) if layer == "csa" and index_fp8 else None
     ring_k = torch.zeros((B, n_win, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
     tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda") if layer == "csa" else None
@@ -77,6 +80,9 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False):
         T.kv_compress(T.Tokens(bf(d["v"][:L])[None].contiguous()), vc, r, 0, nb, m, alpha["v"])
         if layer == "csa":
             T.kv_compress(T.Tokens(bf(d["ki"][:L])[None].contiguous()), kic, r, 0, nb, m, alpha["i"])
+            if kic16 is not None:
+                T.kv_compress(T.Tokens(bf(d["ki"][:L])[None].contiguous()), kic16, r, 0, nb, m,
+                              alpha["i"])
             t0 = nb * m
             if t0 < L:
                 tail[r, torch.arange(t0, L) % m] = bf(d["ki"][t0:L])
@@ -96,6 +102,8 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False):
         step.update(qI=bf(np.stack(inp["qI"])), kI_new=bf(np.stack(inp["kI_new"])),
                     w=torch.from_numpy(np.stack(inp["w"])).cuda())
     step["pos"] = torch.full((B,), L, dtype=torch.int64, device="cuda")
+    if kic16 is not None:
+        step["kic_bf16"] = kic16
 
     def clone_cache(c):
         if c is None:
@@ -444,7 +452,9 @@ def bench_pro_decode(args, w):
     from long_context_hybrid_kv_amd import _lib as T
     from synth import gen
     L = w.L
-    lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True)
+    f8i = getattr(args, "index_fp8", False)
+    lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True,
+                                      index_fp8=f8i and layer == "csa")
             for layer in ("csa", "hca")}
     log(f"[bench] {w.name}: state built")
     keep = []
@@ -455,20 +465,35 @@ def bench_pro_decode(args, w):
     nv = (L - w.n_win + 1 + w.m_csa - 1) // w.m_csa
     nvh = (L - w.n_win + 1 + w.m_hca - 1) // w.m_hca
     B = w.B
-    scan_bytes = B * nv * 128
-    step_bytes = B * (nv * 128 + w.k_csa * 256 + nvh * 256 + 2 * w.n_win * 512 + 4 * w.H * 256)
+    # indexer key bytes per visible block: 128 (bf16), or 64 fp8 codes + the page scale
+    key_b = 64 + 4 / 64 if f8i else 128
+    scan_bytes = int(B * nv * key_b)
+    step_bytes = B * (nv * key_b + w.k_csa * 256 + nvh * 256 + 2 * w.n_win * 512 + 4 * w.H * 256)
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     src = source_hash("indexer.hip", "common.h")
+    extra = {}
+    if f8i:
+        # selection recall: how much of each query's top-k over the bf16 keys the
+        # fp8 keys select (the same tokens, compressed both ways)
+        st = lays["csa"][1]
+        q = T.Queries.list(st["pos"], L)
+        i8, _ = T.indexer_topk(q, st["qI"], st["w"], lays["csa"][0][0].kic, w.m_csa, w.n_win,
+                               w.k_csa, ws_key="recall")
+        i16, _ = T.indexer_topk(q, st["qI"], st["w"], st["kic_bf16"], w.m_csa, w.n_win,
+                                w.k_csa, ws_key="recall")
+        rec = [len(set(i8[b].tolist()) & set(i16[b].tolist())) / w.k_csa for b in range(B)]
+        extra["index_recall_vs_bf16_keys"] = round(float(np.mean(rec)), 4)
     return {"value": B / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": n,
-            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), **extra,
             "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H, "kv_heads": 1,
                        "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
+                       "indexer_keys": "fp8_e4m3+page_scale" if f8i else "bf16",
                        "layers": "csa+hca", "kv_dtype": "fp8_e4m3+page_scale",
                        "cache_copies": args.copies},
             "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": committed_traffic("idx_scan_kernel", w.name, src),
+                         "traffic": None if f8i else committed_traffic("idx_scan_kernel", w.name, src),
                          "algorithmic_bytes_per_launch": scan_bytes,
                          "avg_launch_ms": round(scan_ms, 5), "launches_timed": cnt}}
 
@@ -588,6 +613,10 @@ def main():
     ap.add_argument("--workload", default="csa_decode_128k",
                     choices=["csa_decode_128k", "pro_decode_1m", "hybrid_prefill_128k"])
     ap.add_argument("--extra", action="store_true", help="also the other two workloads")
+    ap.add_argument("--index-fp8", action="store_true",
+                    help="pro_decode_1m with fp8 indexer keys (a next row of the scope: the "
+                         "scan reads half the bytes); reports the selection recall against "
+                         "bf16 keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -603,6 +632,8 @@ def main():
     if args.traffic_summary:
         traffic_summary(args)
         return
+    if args.index_fp8 and args.workload != "pro_decode_1m":
+        ap.error("--index-fp8 applies to --workload pro_decode_1m")
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a "
                                    "design note only", "n_gpus": args.gpus}))
@@ -635,7 +666,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) tokens; caches compressed on the GPU)",
             "config": res["config"], "roofline": res["roofline"]}
-    for key in ("step_hbm_frac", "pair_mfma_frac", "ms_csa_layer", "ms_hca_layer"):
+    for key in ("step_hbm_frac", "pair_mfma_frac", "ms_csa_layer", "ms_hca_layer",
+                "index_recall_vs_bf16_keys"):
         if key in res:
             line[key] = res[key]
     if args.extra:
