@@ -150,10 +150,14 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
                            hipStream_t stream);
 
 /* Lightning indexer + top-k for each query (wiki §5.3; §8 for the selector).
- *   qI  bf16 [n][H_I][d_I]     w  fp32 [n][H_I]     kIc bf16 paged cache
+ *   qI  bf16 [n][H_I][d_I]     w  fp32 [n][H_I]
+ *   kIc paged cache of the compressed indexer keys: bf16, or fp8 e4m3fn codes
+ *       with one fp32 scale per 64-entry page (the low-precision indexer keys
+ *       of wiki §8; key value = code value * page scale)
  *   idx int32 [n][k]  out: selected blocks ascending, -1 padded
  *   score fp32 [n][k] or NULL: the indexer score of each idx entry (0 at pads)
- * Scores are computed in fp32 from bf16 operands.  Listed (decode) queries
+ * Scores are computed in fp32 from bf16 operands (fp8 codes widen to bf16
+ * exactly; the page scale multiplies the head sum).  Listed (decode) queries
  * support up to 2^21 visible blocks per query (HSA_ERR_UNSUPPORTED beyond). */
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k);
