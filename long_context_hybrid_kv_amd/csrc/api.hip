@@ -289,7 +289,8 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
 
 size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t k) {
   if (!q || q->n < 1 || H < 16 || n_win < 1 || k < 1) return 0;
-  return attn_ws_bytes(q->n, H, (int64_t)csa_entries(n_win, k), is_span(q));
+  return attn_ws_bytes(q->n, H, (int64_t)csa_entries(n_win, k), is_span(q),
+                       attn_decode_cps(k, n_win));
 }
 
 hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,
@@ -312,7 +313,8 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
 
 size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t m) {
   if (!q || q->n < 1 || H < 16 || n_win < 1 || m < 1 || q->max_pos < 0) return 0;
-  return attn_ws_bytes(q->n, H, n_win + nvis_host(q->max_pos, m, n_win), is_span(q));
+  return attn_ws_bytes(q->n, H, n_win + nvis_host(q->max_pos, m, n_win), is_span(q),
+                       attn_decode_cps(0, n_win));
 }
 
 hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,

@@ -526,19 +526,24 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
   if (a.n_splits == 1) {
-    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+    // O / l, divided exactly as the merge divides: a query whose entries fit
+    // one split gets the same bits as when its launch has more splits (the
+    // others empty) and goes through the merge
     const int64_t o0 = ((int64_t)qi * a.H + head) * kD;
+    const bool nz = l_i > 0.f;
     if (a.o_f32) {
       float* orow = (float*)a.O + o0;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(orow + 16 * dt + 4 * g) = oacc[dt] * inv;
+      for (int dt = 0; dt < 8; ++dt)
+        *(f32x4*)(orow + 16 * dt + 4 * g) = nz ? oacc[dt] / l_i : f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
       u16* orow = (u16*)a.O + o0;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         uint32_t b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)(oacc[dt][i] * inv));
+        for (int i = 0; i < 4; ++i)
+          b[i] = __builtin_bit_cast(u16, (__bf16)(nz ? oacc[dt][i] / l_i : 0.f));
         *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
     }
@@ -877,29 +882,45 @@ struct AttnPlan {
   int nw, n_hg, n_splits, cps;
 };
 
-static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span) {
+// Listed (decode) queries: a query's entries are cut into splits of a fixed
+// number of 64-entry chunks that depends only on the layer, never on the
+// batch.  A request's partial results, and so its output bit for bit, are
+// then the same alone or in any batch: splits past its own entries are empty
+// and add exact zeros in the merge, which sums splits in a fixed order.
+// CSA: a query has at most c = ceil((n_win + k) / 64) chunks; rows of up to 12
+// chunks (k = 512 with the 128-token window: 10) go in pairs, longer rows one
+// chunk per split (k = 1024: 18 splits, so that a batch of 4 still spreads
+// over the chip), and never more than 32 splits.  HCA: 4 chunks per split.
+int attn_decode_cps(int k, int n_win) {
+  if (k <= 0) return 4;
+  const int chunks = (n_win + k + 63) / 64;
+  if (chunks <= 12) return 2;
+  return (chunks + 31) / 32;
+}
+
+static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span, int decode_cps) {
   AttnPlan p;
+  (void)n_q;
   p.nw = (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
   p.n_hg = H / (16 * p.nw);
   const int64_t chunks = (max_entries + 63) / 64 > 0 ? (max_entries + 63) / 64 : 1;
-  // at most kMaxCps chunks per workgroup; decode spreads short rows over
-  // enough workgroups to fill the chip (about 4 chunks each, at least 1)
-  int64_t n = (chunks + kMaxCps - 1) / kMaxCps;
-  if (!span) {
-    int64_t by4 = (chunks + 3) / 4;
-    if (by4 > n) n = by4;
-    const int64_t wgs = (int64_t)n_q * p.n_hg;
-    if (n * wgs < 256) n = (256 + wgs - 1) / wgs;
-    if (n > chunks) n = chunks;
-    if (n > kMergeMaxSplits) n = kMergeMaxSplits;
+  if (span) {
+    // prefill: at most kMaxCps chunks per workgroup (one query's entries fit)
+    const int64_t n = (chunks + kMaxCps - 1) / kMaxCps;
+    p.cps = (int)((chunks + n - 1) / n);
+  } else {
+    p.cps = decode_cps;
+    // rows longer than the merge takes (beyond the decode limits) widen the
+    // splits and lose the batch invariance
+    if ((chunks + p.cps - 1) / p.cps > kMergeMaxSplits)
+      p.cps = (int)((chunks + kMergeMaxSplits - 1) / kMergeMaxSplits);
   }
-  p.cps = (int)((chunks + n - 1) / n);
   p.n_splits = (int)((chunks + p.cps - 1) / p.cps);
   return p;
 }
 
-size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span) {
-  AttnPlan p = plan(n_q, H, max_entries, span);
+size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span, int decode_cps) {
+  AttnPlan p = plan(n_q, H, max_entries, span, decode_cps);
   if (p.n_splits == 1) return 0;
   const size_t slots = (size_t)n_q * p.n_splits * H;
   return slots * kD * sizeof(float) + ((slots * 2 * sizeof(float) + 255) & ~size_t(255)) + 256;
@@ -917,7 +938,7 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   int64_t b2 = (q.max_pos + 1) / m;
   nv_max = nv_max < b2 ? nv_max : b2;
   int64_t max_entries = n_win + (k > 0 ? (nv_max < k ? nv_max : k) : nv_max);
-  AttnPlan p = plan(q.n, H, max_entries, span);
+  AttnPlan p = plan(q.n, H, max_entries, span, attn_decode_cps(k, n_win));
   AttnArgs a;
   a.Q = to_dev(q);
   a.q = (const u16*)Q;

@@ -218,7 +218,10 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,
                           const UpdateArgs* upd = nullptr);
 
-size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span);
+// decode: 64-entry chunks per split of a query (a layer constant, so a
+// request's result does not depend on the batch it is in)
+int attn_decode_cps(int k, int n_win);
+size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span, int decode_cps);
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
                        const hsa_tokens& wv, int n_win, const hsa_paged& kc,
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
