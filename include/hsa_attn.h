@@ -234,6 +234,30 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
                            void* O, float* lse, int32_t* idx_out,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* A draft of n_tok tokens per request for speculative decoding (the draft's
+ * queries are verified together; wiki §11.4 for the caches kept in sync).
+ * Tokens pos[b] .. pos[b]+n_tok-1 of request b are appended in order, as
+ * n_tok single-token steps would append them (rings, tail, every block they
+ * complete), then query i of request b, at position pos[b]+i, runs the
+ * indexer + top-k + CSA attention or the HCA attention and sees exactly what a
+ * single-token step at that position sees: a block completed later in the
+ * draft is not visible to it, and its window rows survive because the rings
+ * must hold n_win + n_tok - 1 tokens.  Arrays are [B][n_tok][...] versions of
+ * hsa_decode_step's (row b * n_tok + i is token / query i of request b): Q
+ * [B][n_tok][H][d]; k_new, v_new [B][n_tok][d]; qI [B][n_tok][H_I][d_I];
+ * kI_new [B][n_tok][d_I]; w [B][n_tok][H_I]; O [B][n_tok][H][d]; lse
+ * [B][n_tok][H] or NULL; idx_out [B][n_tok][topk] or NULL.  1 <= n_tok <= 256;
+ * max_pos bounds every pos[b] + n_tok - 1.  The caller advances pos by the
+ * accepted tokens (a rejected suffix must be rewound by the caller: the caches
+ * keep what the draft appended).  No allocation and no host synchronisation. */
+size_t hsa_decode_draft_workspace_bytes(const hsa_layer* L, int32_t B, int32_t n_tok,
+                                        int64_t max_pos);
+hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const int64_t* pos,
+                            int64_t max_pos, const void* Q, const void* k_new, const void* v_new,
+                            const void* qI, const void* kI_new, const float* w, void* O,
+                            float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Optional kernel timing (tracing).  While enabled for a kernel, every launch
  * of it is timed with a pair of HIP events on its stream; read returns the
  * summed elapsed milliseconds and the number of launches since the previous

@@ -91,6 +91,12 @@ _SIGS = {
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_size_t, C.c_void_p]),
+    "hsa_decode_draft_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), C.c_int32, C.c_int32,
+                                                      C.c_int64]),
+    "hsa_decode_draft": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_size_t, C.c_void_p]),
 }
 
 _lib = None
@@ -362,6 +368,26 @@ class Layer:
         if self.kind == LAYER_CSA:
             L.tail_i, L.kic = self.tail_i.c(), self.kic.c()
         return L
+
+
+def decode_draft(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,
+                 k_new: torch.Tensor, v_new: torch.Tensor, qI=None, kI_new=None, w=None,
+                 with_lse: bool = False, with_idx: bool = False, ws_key="draft"):
+    """n_tok tokens per request (arrays [B, n_tok, ...]); returns O [B, n_tok, H, d],
+    lse [B, n_tok, H] or None, idx [B, n_tok, topk] or None."""
+    B, n_tok = Q.shape[0], Q.shape[1]
+    Lc = layer.c()
+    O = torch.empty(Q.shape, dtype=torch.float32 if layer.out_fp32 else torch.bfloat16,
+                    device=Q.device)
+    lse = torch.empty((B, n_tok, layer.H), dtype=torch.float32, device=Q.device) if with_lse else None
+    idx = (torch.empty((B, n_tok, layer.topk), dtype=torch.int32, device=Q.device)
+           if with_idx and layer.kind == LAYER_CSA else None)
+    nb = lib().hsa_decode_draft_workspace_bytes(C.byref(Lc), B, n_tok, max_pos)
+    ws, wsb = _ws_args(_WS.get((ws_key, layer.kind), nb, Q.device))
+    _check(lib().hsa_decode_draft(C.byref(Lc), B, n_tok, _ptr(pos), max_pos, _ptr(Q), _ptr(k_new),
+                                  _ptr(v_new), _ptr(qI), _ptr(kI_new), _ptr(w), _ptr(O),
+                                  _ptr(lse), _ptr(idx), ws, wsb, _stream()), "decode_draft")
+    return O, lse, idx
 
 
 def decode_step(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,

@@ -360,46 +360,65 @@ size_t hsa_decode_step_workspace_bytes(const hsa_layer* L, int32_t B, int64_t ma
   return a + b + c;
 }
 
-hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, int64_t max_pos,
-                           const void* Q, const void* k_new, const void* v_new, const void* qI,
-                           const void* kI_new, const float* w, void* O, float* lse,
-                           int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  REQ(L, "decode_step: null layer");
-  REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode_step: unknown layer kind");
-  REQ(B >= 1 && pos && Q && k_new && v_new && O, "decode_step: null argument or B < 1");
-  REQ(L->alpha_k && L->alpha_v, "decode_step: null pooling weights");
-  REQ(L->o_dtype == HSA_BF16 || L->o_dtype == HSA_FP32, "decode_step: o_dtype must be bf16 or fp32");
+// Validation shared by the single-token step and the draft (n_tok tokens per
+// request; the rings must keep the first draft query's window while the
+// draft's later tokens are written).
+static hsa_status check_decode(const hsa_layer* L, int32_t B, int32_t n_tok, const int64_t* pos,
+                               int64_t max_pos, const void* Q, const void* k_new,
+                               const void* v_new, const void* qI, const void* kI_new,
+                               const float* w, void* O) {
+  REQ(L, "decode: null layer");
+  REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode: unknown layer kind");
+  REQ(B >= 1 && pos && Q && k_new && v_new && O, "decode: null argument or B < 1");
+  REQ(n_tok >= 1 && n_tok <= 256, "decode: n_tok must be in [1, 256]");
+  REQ(L->alpha_k && L->alpha_v, "decode: null pooling weights");
+  REQ(L->o_dtype == HSA_BF16 || L->o_dtype == HSA_FP32, "decode: o_dtype must be bf16 or fp32");
   SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
-      "decode_step: appending to fp8 caches is not supported (page scales are set per page)");
+      "decode: appending to fp8 caches is not supported (page scales are set per page)");
   REQ(L->kc.n_req >= B && L->vc.n_req >= B && L->ring_k.n_req >= B && L->ring_v.n_req >= B,
-      "decode_step: caches hold fewer than B requests");
-  REQ(L->n_win >= 1 && L->m >= 1 && L->m <= L->n_win, "decode_step: need 1 <= m <= n_win");
+      "decode: caches hold fewer than B requests");
+  REQ(L->n_win >= 1 && L->m >= 1 && L->m <= L->n_win, "decode: need 1 <= m <= n_win");
   hsa_queries q{};
-  q.n = B;
+  q.n = B * n_tok;
   q.pos = pos;
+  q.req = n_tok > 1 ? (const int32_t*)pos : nullptr;   // (validation only: listed per request)
   q.max_pos = max_pos;
   hsa_status s;
   if ((s = check_attn_common(&q, Q, L->H, L->d, &L->ring_k, &L->ring_v, L->n_win, &L->kc, &L->vc,
                              L->m, L->scale, O)) != HSA_OK)
     return s;
-  REQ(L->ring_k.capacity >= L->n_win && L->ring_v.capacity >= L->n_win,
-      "decode_step: rings must hold n_win tokens");
+  REQ(L->ring_k.capacity >= L->n_win + n_tok - 1 && L->ring_v.capacity >= L->n_win + n_tok - 1,
+      "decode: rings must hold n_win + n_tok - 1 tokens");
   int64_t pages_needed = (max_pos + 1) / L->m;
   REQ((int64_t)L->kc.pages_per_req * kPage >= pages_needed &&
           (int64_t)L->vc.pages_per_req * kPage >= pages_needed,
-      "decode_step: page table too short for the appended entries");
-  const bool csa = L->kind == HSA_LAYER_CSA;
-  if (csa) {
-    REQ(qI && kI_new && w && L->alpha_i, "decode_step: CSA needs qI, kI_new, w and alpha_i");
+      "decode: page table too short for the appended entries");
+  if (L->kind == HSA_LAYER_CSA) {
+    REQ(qI && kI_new && w && L->alpha_i, "decode: CSA needs qI, kI_new, w and alpha_i");
     if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
     if ((s = check_tokens(&L->tail_i, "tail_i", kDI, L->m)) != HSA_OK) return s;
-    REQ(L->kic.n_req >= B && L->tail_i.n_req >= B, "decode_step: kic holds fewer than B requests");
-    REQ((int64_t)L->kic.pages_per_req * kPage >= pages_needed, "decode_step: kic table too short");
-    SUP(L->H_I == kHI && L->d_I == kDI, "decode_step: H_I must be 4 and d_I 64");
-    REQ(L->topk >= 1 && L->topk <= (1 << 20), "decode_step: topk out of range");
+    REQ(L->kic.n_req >= B && L->tail_i.n_req >= B, "decode: kic holds fewer than B requests");
+    REQ((int64_t)L->kic.pages_per_req * kPage >= pages_needed, "decode: kic table too short");
+    SUP(L->H_I == kHI && L->d_I == kDI, "decode: H_I must be 4 and d_I 64");
+    REQ(L->topk >= 1 && L->topk <= (1 << 20), "decode: topk out of range");
     SUP(nvis_host(max_pos, L->m, L->n_win) <= indexer_max_blocks(),
-        "decode_step: rows longer than 2^21 visible blocks are not supported");
+        "decode: rows longer than 2^21 visible blocks are not supported");
   }
+  return HSA_OK;
+}
+
+hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, int64_t max_pos,
+                           const void* Q, const void* k_new, const void* v_new, const void* qI,
+                           const void* kI_new, const float* w, void* O, float* lse,
+                           int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hsa_status s;
+  if ((s = check_decode(L, B, 1, pos, max_pos, Q, k_new, v_new, qI, kI_new, w, O)) != HSA_OK)
+    return s;
+  hsa_queries q{};
+  q.n = B;
+  q.pos = pos;
+  q.max_pos = max_pos;
+  const bool csa = L->kind == HSA_LAYER_CSA;
   size_t a_idx, a_sel, a_attn;
   decode_parts(L, B, max_pos, &a_idx, &a_sel, &a_attn);
   if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn)) != HSA_OK) return s;
@@ -422,6 +441,79 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
                     L->scale, O, L->o_dtype, lse, base, a_attn, stream);
   }
   return hip_status(e, "decode_step attention");
+}
+
+// Workspace of a draft: the queries' positions and requests, then the
+// indexer's, the selection's and the attention's parts for B * n_tok queries.
+static void draft_parts(const hsa_layer* L, int32_t B, int32_t n_tok, int64_t max_pos,
+                        size_t* p_q, size_t* p_idx, size_t* p_sel, size_t* p_attn) {
+  const size_t n = (size_t)B * n_tok;
+  hsa_queries q{};
+  q.n = (int32_t)n;
+  q.pos = (const int64_t*)1;   // list mode for sizing only
+  q.req = (const int32_t*)1;
+  q.max_pos = max_pos;
+  *p_q = rnd256(sizeof(int64_t) * n) + rnd256(sizeof(int32_t) * n);
+  *p_idx = *p_sel = 0;
+  if (L->kind == HSA_LAYER_CSA) {
+    *p_idx = rnd256(hsa_indexer_topk_workspace_bytes(&q, L->m, L->n_win, L->topk));
+    *p_sel = rnd256(sizeof(int32_t) * n * L->topk);
+    *p_attn = rnd256(hsa_csa_attn_workspace_bytes(&q, L->H, L->n_win, L->topk));
+  } else {
+    *p_attn = rnd256(hsa_hca_attn_workspace_bytes(&q, L->H, L->n_win, L->m));
+  }
+}
+
+size_t hsa_decode_draft_workspace_bytes(const hsa_layer* L, int32_t B, int32_t n_tok,
+                                        int64_t max_pos) {
+  if (!L || B < 1 || n_tok < 1 || max_pos < 0 || L->m < 1 || L->n_win < 1 || L->H < 16) return 0;
+  if (L->kind == HSA_LAYER_CSA && L->topk < 1) return 0;
+  size_t a, b, c, d;
+  draft_parts(L, B, n_tok, max_pos, &a, &b, &c, &d);
+  return a + b + c + d;
+}
+
+hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const int64_t* pos,
+                            int64_t max_pos, const void* Q, const void* k_new, const void* v_new,
+                            const void* qI, const void* kI_new, const float* w, void* O,
+                            float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  hsa_status s;
+  if ((s = check_decode(L, B, n_tok, pos, max_pos, Q, k_new, v_new, qI, kI_new, w, O)) != HSA_OK)
+    return s;
+  size_t a_q, a_idx, a_sel, a_attn;
+  draft_parts(L, B, n_tok, max_pos, &a_q, &a_idx, &a_sel, &a_attn);
+  if ((s = check_ws(ws, ws_bytes, a_q + a_idx + a_sel + a_attn)) != HSA_OK) return s;
+  char* base = (char*)ws;
+  const size_t n = (size_t)B * n_tok;
+  int64_t* q_pos = (int64_t*)base;
+  int32_t* q_req = (int32_t*)(base + rnd256(sizeof(int64_t) * n));
+  // 1-2: every draft token appended in order (rings, tail, completed blocks);
+  // the queries' positions and requests land in the workspace
+  hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream, n_tok,
+                                      q_pos, q_req);
+  if (e != hipSuccess) return hip_status(e, "decode_draft update");
+  // 3: query i of request b at position pos[b] + i sees exactly what a
+  // single-token step at that position would (a block completed later in the
+  // draft is not visible to it; its window rows survive in the ring)
+  hsa_queries q{};
+  q.n = (int32_t)n;
+  q.pos = q_pos;
+  q.req = q_req;
+  q.max_pos = max_pos;
+  if (L->kind == HSA_LAYER_CSA) {
+    int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_q + a_idx);
+    e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base + a_q,
+                       a_idx, stream);
+    if (e != hipSuccess) return hip_status(e, "decode_draft indexer");
+    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
+                    L->topk, L->scale, O, L->o_dtype, lse, base + a_q + a_idx + a_sel, a_attn,
+                    stream);
+  } else {
+    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
+                    L->scale, O, L->o_dtype, lse, base + a_q, a_attn, stream);
+  }
+  return hip_status(e, "decode_draft attention");
 }
 
 }  // extern "C"

@@ -230,8 +230,12 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
 
 UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
                             const void* k_new, const void* v_new, const void* kI_new);
+// n_tok > 1: a draft of n_tok tokens per request (rows b * n_tok + i of the
+// new-token arrays), appended in order; q_pos / q_req (or null) receive the
+// request and position of each of the draft's queries
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                hipStream_t s);
+                                hipStream_t s, int n_tok = 1, int64_t* q_pos = nullptr,
+                                int32_t* q_req = nullptr);
 
 }  // namespace hsa

@@ -120,14 +120,20 @@ UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_
   u.kc = to_dev(L.kc);
   u.vc = to_dev(L.vc);
   u.kic = csa ? to_dev(L.kic) : Paged{};
+  u.n_tok = 1;
+  u.q_pos = nullptr;
+  u.q_req = nullptr;
   return u;
 }
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                hipStream_t s) {
-  decode_update_kernel<<<B, 128, 0, s>>>(make_update_args(L, pos, max_pos, k_new, v_new, kI_new),
-                                         fault_word());
+                                hipStream_t s, int n_tok, int64_t* q_pos, int32_t* q_req) {
+  UpdateArgs u = make_update_args(L, pos, max_pos, k_new, v_new, kI_new);
+  u.n_tok = n_tok;
+  u.q_pos = q_pos;
+  u.q_req = q_req;
+  decode_update_kernel<<<B, 128, 0, s>>>(u, fault_word());
   return hipGetLastError();
 }
 

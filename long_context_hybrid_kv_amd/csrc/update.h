@@ -24,6 +24,9 @@ struct UpdateArgs {
   const float* av;
   const float* ai;                   // [m][64] (CSA)
   Paged kc, vc, kic;
+  int n_tok;                         // tokens per request (a draft: n_tok > 1)
+  int64_t* q_pos;                    // [B * n_tok] positions of the draft's queries, or null
+  int32_t* q_req;                    // [B * n_tok] their requests
 };
 
 // Pool block blk of channel c from the ring/tail; the newest token's own value
@@ -37,28 +40,31 @@ __device__ __forceinline__ double pool_last(const Tokens& src, int r, int64_t bl
   return acc;
 }
 
-// Request b: write the new token's K / V (and indexer key) into the rings; when
-// it completes a block, pool the block and append it at n_entries.  Threads
-// 0..127 of the workgroup carry the channels; every thread of the workgroup
-// must call this (it synchronises the workgroup).
-__device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault) {
+// Token i of request b (position pos[b] + i): write its K / V (and indexer
+// key) into the rings; when it completes a block, pool the block and append it
+// at n_entries.  Threads 0..127 of the workgroup carry the channels (a thread
+// writes and pools its own channel, so tokens of one request are handled in
+// order without cross-thread hand-off); every thread of the workgroup must call
+// this (it synchronises the workgroup).
+__device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault) {
   const int c = threadIdx.x;
   const bool on = c < kD;
   __shared__ int ok;
-  const int64_t p = u.pos[b];
+  const int64_t p = u.pos[b] + i;
+  const int64_t row = (int64_t)b * u.n_tok + i;   // the token's row in k_new / v_new / ki_new
   if (p < 0 || p > u.max_pos) {
     if (c == 0) atomicOr(fault, HSA_FAULT_POS);
     return;
   }
   u16 kn = 0, vn = 0, in = 0;
   if (on) {
-    kn = u.k_new[(int64_t)b * kD + c];
-    vn = u.v_new[(int64_t)b * kD + c];
+    kn = u.k_new[row * kD + c];
+    vn = u.v_new[row * kD + c];
     u.rk.row(b, p)[c] = kn;
     u.rv.row(b, p)[c] = vn;
   }
   if (u.csa && c < kDI) {
-    in = u.ki_new[(int64_t)b * kDI + c];
+    in = u.ki_new[row * kDI + c];
     u.ti.row(b, p)[c] = in;
   }
   if ((p + 1) % u.m != 0) return;
@@ -89,6 +95,20 @@ __device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault
     u.vc.n_entries[b] = (int32_t)(blk + 1);
     if (u.csa) u.kic.n_entries[b] = (int32_t)(blk + 1);
   }
+}
+
+// Request b's n_tok tokens in order, and (a draft) its queries' request and
+// position for the selection and attention that follow.
+__device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault) {
+  for (int i = 0; i < u.n_tok; ++i) {
+    decode_update_token(u, b, i, fault);
+    __syncthreads();   // the next token's block check reuses the shared flag
+  }
+  if (u.q_pos)
+    for (int i = threadIdx.x; i < u.n_tok; i += blockDim.x) {
+      u.q_pos[(int64_t)b * u.n_tok + i] = u.pos[b] + i;
+      u.q_req[(int64_t)b * u.n_tok + i] = b;
+    }
 }
 
 }  // namespace hsa

@@ -101,9 +101,10 @@ def scale_of(d=128):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True):
+def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
-    and the per-request token/query streams for `steps` decode steps."""
+    and the per-request token/query streams for `steps` decode steps.  Rings
+    hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)."""
     B = len(Ls)
     m = w.m(layer)
     n_win = w.n_win
@@ -119,7 +120,8 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True):
     st["alpha_k"] = L.pooling_weights(torch.from_numpy(z["zk"]).cuda())
     st["alpha_v"] = L.pooling_weights(torch.from_numpy(z["zv"]).cuda())
     st["kc"], st["vc"] = cache(128, fp8), cache(128, fp8)
-    ring_k = torch.zeros((B, n_win, 128), dtype=torch.bfloat16, device="cuda")
+    cap = n_win if ring_cap is None else ring_cap
+    ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
     if layer == "csa":
         st["alpha_i"] = L.pooling_weights(torch.from_numpy(z["zi"]).cuda())
@@ -133,7 +135,7 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True):
             if nb > 0:
                 L.kv_compress(tokens(d[x][:Lr]), st[name], r, 0, nb, m, st[a])
         lo = max(0, Lr - n_win)
-        slots = torch.arange(lo, Lr) % n_win
+        slots = torch.arange(lo, Lr) % cap
         ring_k[r, slots] = dev_bf16(d["k"][lo:Lr])
         ring_v[r, slots] = dev_bf16(d["v"][lo:Lr])
         if layer == "csa":

@@ -103,6 +103,26 @@ def test_decode_step_rejects_fp8_append_and_bad_layers():
     assert lib.hsa_decode_step_workspace_bytes(C.byref(Lr), 0, 1000) == 0
 
 
+def test_decode_draft_validation():
+    """Drafts need 1 <= n_tok <= 256 and rings that keep the first draft
+    query's window while the later tokens are written (n_win + n_tok - 1)."""
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    Lr = L._Layer()
+    Lr.kind, Lr.H, Lr.d, Lr.n_win, Lr.m, Lr.topk, Lr.H_I, Lr.d_I = 1, 64, 128, 128, 128, 0, 4, 64
+    Lr.scale = 0.088
+    Lr.alpha_k = Lr.alpha_v = 0x1000
+    Lr.ring_k = Lr.ring_v = L._Tokens(0x1000, 128, 1, 128)     # capacity n_win only
+    Lr.kc = Lr.vc = _paged()
+    call = lambda n_tok: lib.hsa_decode_draft(C.byref(Lr), 1, n_tok, f, 1000, f, f, f, None, None,
+                                              None, f, None, None, f, 1 << 30, None)
+    assert call(0) == -1
+    assert call(257) == -1
+    assert call(4) == -1                       # ring too small for a 4-token draft
+    assert lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), 1, 0, 1000) == 0
+    assert lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), 2, 4, 1000) > 0
+
+
 def test_workspace_sizes_are_consistent():
     lib = L.lib()
     q = L._Queries(4, None, C.c_void_p(0x1000), 0, 0, 1048576)
