@@ -503,8 +503,11 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
   q.max_pos = max_pos;
   if (L->kind == HSA_LAYER_CSA) {
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_q + a_idx);
+    // draft queries of one request share the passes over its keys, up to four
+    // at a time (the largest divisor of n_tok not above 4)
+    const int group = n_tok % 4 == 0 ? 4 : n_tok % 3 == 0 ? 3 : n_tok % 2 == 0 ? 2 : 1;
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base + a_q,
-                       a_idx, stream);
+                       a_idx, stream, nullptr, group);
     if (e != hipSuccess) return hip_status(e, "decode_draft indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_q + a_idx + a_sel, a_attn,

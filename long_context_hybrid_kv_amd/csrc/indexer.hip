@@ -64,17 +64,18 @@ static int64_t row_cap(int64_t max_nvis) {
   return R < kSelCH ? kSelCH : R;
 }
 
-static void list_shape(int64_t R, bool span, int* n_lists, int* cap, int* span_len) {
-  *span_len = span ? kHistSpan : scan_cpw(R) * kCH;
+static void list_shape(int64_t R, bool span, int* n_lists, int* cap, int* span_len,
+                       bool grouped = false) {
+  *span_len = span ? kHistSpan : (grouped ? 1 : scan_cpw(R)) * kCH;
   *n_lists = (int)((R + *span_len - 1) / *span_len);
   *cap = *span_len < kBins ? *span_len : kBins;   // at most min(bins, scores) entries
 }
 
-static IdxWs carve(void* ws, int nq, int64_t R, bool span) {
+static IdxWs carve(void* ws, int nq, int64_t R, bool span, bool grouped = false) {
   IdxWs w;
   char* p = (char*)ws;
   auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
-  list_shape(R, span, &w.n_lists, &w.list_cap, &w.list_span);
+  list_shape(R, span, &w.n_lists, &w.list_cap, &w.list_span, grouped);
   w.state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
   w.hl_n = (int32_t*)take(sizeof(int32_t) * w.n_lists * nq);
   w.hl = (uint32_t*)take(sizeof(uint32_t) * w.list_cap * w.n_lists * nq);
@@ -340,6 +341,159 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   for (int i = threadIdx.x; i < CPW * kCH; i += 256)
     if (s0 + i < s_end) srow[s0 + i] = lsc[i];
   write_hist_list(lhist, ws, qrow, blockIdx.x);
+}
+
+// Write a histogram of 16-bit counts packed two bins per word (bin b in half
+// b & 1 of word b >> 1) as the list of its nonzero bins, like write_hist_list.
+__device__ __forceinline__ void write_hist_list16(const uint32_t* lh2, const IdxWs& ws, int qrow,
+                                                  int li) {
+  __shared__ uint32_t sh[4];
+  __syncthreads();
+  constexpr int BPT = kBins / 256;
+  uint32_t v[BPT];
+  uint32_t nz = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = threadIdx.x + 256 * j;
+    v[j] = (lh2[b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
+    nz += v[j] != 0;
+  }
+  uint32_t tot;
+  uint32_t off = block_scan_nt<256>(nz, &tot, sh);
+  uint32_t* dst = ws.hl + ((int64_t)qrow * ws.n_lists + li) * ws.list_cap;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if (v[j]) dst[off++] = ((uint32_t)(threadIdx.x + 256 * j) << 16) | v[j];
+  if (threadIdx.x == 0) ws.hl_n[(int64_t)qrow * ws.n_lists + li] = (int32_t)tot;
+}
+
+// ---------------------------------------------------------------- decode drafts: grouped scan
+
+// Listed queries in groups of G (2..4) consecutive queries of one request, as
+// a decode draft lays them out.  The MFMA A tile has 16 rows and one query
+// fills four (its indexer heads), so the group's queries take rows 4i..4i+3
+// and one pass over the request's keys scores all of them: lane group i
+// (lanes 16i..16i+15) receives query i's four head products of its blocks.
+// Per query, as idx_scan_kernel: the fp32 scores of its visible blocks and the
+// nonzero bins of a 4096-bin histogram as list blockIdx.x (one 512-block chunk
+// per workgroup; counts <= 512, so 16-bit bins, two per word, keep the G
+// histograms small).
+template <int G, bool F8K>
+__global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u16* __restrict__ qI,
+                                                             const float* __restrict__ w,
+                                                             Paged kic, int m, int n_win,
+                                                             IdxWs ws, int* fault) {
+  const int q0 = blockIdx.y * G;
+  const int c_first = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  const int r = Q.req ? Q.req[q0] : q0;
+  int pid[2];
+  {
+    const int lp = (int)((((int64_t)c_first) * kCH + wv * (kCH / 4)) >> 6);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pid[j] = lp + j < kic.pages_per_req ? kic.page_table[(int64_t)r * kic.pages_per_req + lp + j]
+                                          : -1;
+  }
+  int64_t nvq[G], nv_max = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    int rq;
+    int64_t t;
+    Q.get(q0 + i, &rq, &t, fault);
+    nvq[i] = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
+                        c_first == 0 && threadIdx.x == 0);
+    nv_max = nvq[i] > nv_max ? nvq[i] : nv_max;
+  }
+  const int n_active = nv_max > 0 ? (int)((nv_max + kCH - 1) / kCH) : 1;
+  if (c_first >= n_active) return;
+  if (c_first == 0)
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (threadIdx.x == i) ws.state[(int64_t)(q0 + i) * kStateInts + 5] = (int32_t)nvq[i];
+
+  constexpr int NT = kCH / 4 / 16;
+  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  const int64_t cb = (int64_t)c_first * kCH;
+  const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
+  const int64_t c_end = nv_max < cb + kCH ? nv_max : cb + kCH;
+  float ksc[2];
+  if constexpr (F8K) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      ksc[j] = (unsigned)pid[j] < (unsigned)kic.n_pages ? kic.scale[pid[j]] : 1.f;
+  }
+  KeyT x0[NT], x1[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int64_t b = w0b + 16 * u + row;
+    const int pg = pid[u >> 2];
+    const bool ok = b < c_end && (unsigned)pg < (unsigned)kic.n_pages;
+    const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
+    x0[u] = __builtin_nontemporal_load(kr + g);
+    x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (w0b + 64 * j < c_end && (unsigned)pid[j] >= (unsigned)kic.n_pages)
+        atomicOr(fault, HSA_FAULT_PAGE);
+  }
+  // A rows 4i..4i+3: query i's four heads
+  bf16x8 a0 = {}, a1 = {};
+  if ((row >> 2) < G) {
+    const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)(q0 + (row >> 2)) * kHI + (row & 3)) * kDI);
+    a0 = qa[g];
+    a1 = qa[4 + g];
+  }
+  // this lane group's query: weights and visible blocks
+  const bool gq = g < G;
+  float wg[kHI];
+#pragma unroll
+  for (int h = 0; h < kHI; ++h) wg[h] = gq ? w[(int64_t)(q0 + g) * kHI + h] : 0.f;
+  int64_t nv_g = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    if (g == i) nv_g = nvq[i];
+  const int64_t b_end_g = nv_g < cb + kCH ? nv_g : cb + kCH;
+
+  __shared__ uint32_t lh2[G][kBins / 2];
+  __shared__ float lsc[G][kCH];
+  for (int i = threadIdx.x; i < G * (kBins / 2); i += 256) (&lh2[0][0])[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    bf16x8 k0, k1;
+    if constexpr (F8K) {
+      k0 = e4m3x8_to_bf16x8(x0[u]);
+      k1 = e4m3x8_to_bf16x8(x1[u]);
+    } else {
+      k0 = x0[u];
+      k1 = x1[u];
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1, acc, 0, 0, 0);
+    const int64_t b = w0b + 16 * u + row;
+    if (gq && b < b_end_g) {
+      float sc = wg[0] * fmaxf(acc[0], 0.f) + wg[1] * fmaxf(acc[1], 0.f) +
+                 wg[2] * fmaxf(acc[2], 0.f) + wg[3] * fmaxf(acc[3], 0.f);
+      if constexpr (F8K) sc *= ksc[u >> 2];
+      lsc[g][b - cb] = sc;
+      const uint32_t bin = order_key(sc) >> 20;
+      atomicAdd(&lh2[g][bin >> 1], 1u << ((bin & 1) * 16));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float* srow = ws.scores + (int64_t)(q0 + i) * ws.R;
+    const int64_t e = nvq[i] < cb + kCH ? nvq[i] : cb + kCH;
+    for (int j = threadIdx.x; j < kCH; j += 256)
+      if (cb + j < e) srow[cb + j] = lsc[i][j];
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) write_hist_list16(&lh2[i][0], ws, q0 + i, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- prefill: score GEMM
@@ -910,7 +1064,7 @@ static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, fl
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* wsp, size_t ws_bytes, hipStream_t s,
-                          const UpdateArgs* upd) {
+                          const UpdateArgs* upd, int group) {
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
@@ -919,6 +1073,20 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
+  if (!span && group > 1 && !upd) {
+    // a draft: groups of `group` queries of one request share each key pass
+    IdxWs ws = carve(wsp, q.n, R, false, true);
+    const bool f8k = kic.dtype == HSA_FP8_E4M3;
+    const dim3 grid(n_chunks, (unsigned)(q.n / group));
+    auto scan = group == 4   ? (f8k ? idx_scan_group_kernel<4, true> : idx_scan_group_kernel<4, false>)
+                : group == 3 ? (f8k ? idx_scan_group_kernel<3, true> : idx_scan_group_kernel<3, false>)
+                             : (f8k ? idx_scan_group_kernel<2, true> : idx_scan_group_kernel<2, false>);
+    timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m,
+                 n_win, ws, fault);
+    KernelTimer kt(HSA_K_INDEXER_SEL, s);
+    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
+    return hipGetLastError();
+  }
   if (!span) {
     IdxWs ws = carve(wsp, q.n, R, false);
     const int cpw = scan_cpw(R);

@@ -18,12 +18,15 @@ from test_gpu_decode import oracle_row
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("layer,n_tok", [("csa", 6), ("hca", 5), ("csa", 1)])
+@pytest.mark.parametrize("layer,n_tok", [("csa", 6), ("csa", 4), ("hca", 5), ("csa", 1)])
 def test_draft_matches_oracle_and_caches(layer, n_tok):
+    """CSA drafts of 6 and 4 tokens score their queries in groups of 3 and 4
+    per pass over the keys; a 1-token draft takes the single-query scan."""
     w = configs.shrink(configs.RAGGED_SERVING, H=64, k_csa=64)
     # requests whose drafts complete blocks at different offsets (CSA m = 4;
-    # HCA m = 128: 126 -> block at 127; 1021 -> block at 1023)
-    Ls = [5, 126, 1000, 1021, 3000]
+    # HCA m = 128: 126 -> block at 127; 1021 -> block at 1023); 70,001 tokens:
+    # 35 scan chunks and the long-row selection (over 16,384 blocks)
+    Ls = [5, 126, 1000, 1021, 3000, 70001]
     st = T.build_state(w, layer, Ls, steps=n_tok, ring_cap=w.n_win + n_tok - 1)
     lay = T.layer_of(w, layer, st)
     reqs = st["reqs"]
