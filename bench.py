@@ -48,11 +48,14 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False):
+def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False,
+                       draft=1):
     """Caches of B requests holding tokens 0..L-1, rings up to L-1, and the new
     token's inputs (position L).  Returns (layers[copies], step inputs).
     index_fp8: the indexer keys are stored fp8 (e4m3fn, one scale per page), and
-    step["kic_bf16"] holds the same keys in bf16 (for the selection recall)."""
+    step["kic_bf16"] holds the same keys in bf16 (for the selection recall).
+    draft > 1: the step's inputs are [B][draft][...] (tokens L .. L+draft-1) and
+    the rings hold n_win + draft - 1 tokens."""
     import torch
     B, m, n_win = w.B, w.m(layer), w.n_win
     z = gen.pool_logits(w, layer)
@@ -65,7 +68,8 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
     vc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
     kic = T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, page_order=perm) if layer == "csa" else None
     kic16 = T.PagedCache.allocate(B, n_ent, 64, page_order=perm) if layer == "csa" and index_fp8 else None
-    ring_k = torch.zeros((B, n_win, 128), dtype=torch.bfloat16, device="cuda")
+    cap = n_win + draft - 1
+    ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
     tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda") if layer == "csa" else None
     inp = {"Q": [], "k_new": [], "v_new": [], "qI": [], "kI_new": [], "w": []}
@@ -74,7 +78,7 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
     for r in range(B):
-        d = gen.decode_request(w, layer, r, L=L)
+        d = gen.decode_request(w, layer, r, L=L, extra_tokens=draft, n_queries=draft)
         nb = L // m
         T.kv_compress(T.Tokens(bf(d["k"][:L])[None].contiguous()), kc, r, 0, nb, m, alpha["k"])
         T.kv_compress(T.Tokens(bf(d["v"][:L])[None].contiguous()), vc, r, 0, nb, m, alpha["v"])
@@ -86,15 +90,15 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
             t0 = nb * m
             if t0 < L:
                 tail[r, torch.arange(t0, L) % m] = bf(d["ki"][t0:L])
-            inp["qI"].append(d["qi"][0])
-            inp["kI_new"].append(d["ki"][L])
-            inp["w"].append(d["w"][0])
+            inp["qI"].append(d["qi"][0] if draft == 1 else d["qi"][:draft])
+            inp["kI_new"].append(d["ki"][L] if draft == 1 else d["ki"][L:L + draft])
+            inp["w"].append(d["w"][0] if draft == 1 else d["w"][:draft])
         lo = max(0, L - n_win)
-        ring_k[r, torch.arange(lo, L) % n_win] = bf(d["k"][lo:L])
-        ring_v[r, torch.arange(lo, L) % n_win] = bf(d["v"][lo:L])
-        inp["Q"].append(d["q"][0])
-        inp["k_new"].append(d["k"][L])
-        inp["v_new"].append(d["v"][L])
+        ring_k[r, torch.arange(lo, L) % cap] = bf(d["k"][lo:L])
+        ring_v[r, torch.arange(lo, L) % cap] = bf(d["v"][lo:L])
+        inp["Q"].append(d["q"][0] if draft == 1 else d["q"][:draft])
+        inp["k_new"].append(d["k"][L] if draft == 1 else d["k"][L:L + draft])
+        inp["v_new"].append(d["v"][L] if draft == 1 else d["v"][L:L + draft])
         torch.cuda.synchronize()
     step = {"Q": bf(np.stack(inp["Q"])), "k_new": bf(np.stack(inp["k_new"])),
             "v_new": bf(np.stack(inp["v_new"]))}
@@ -150,6 +154,24 @@ class StepCall:
         st = self.fn(*self.args, C.c_void_p(torch.cuda.current_stream().cuda_stream))
         if st != 0:
             self.T._check(st, "decode_step")
+
+
+class DraftCall(StepCall):
+    """Pre-marshalled hsa_decode_draft arguments (n_tok tokens per request)."""
+
+    def __init__(self, T, layer, step, L_max, O, n_tok):
+        import torch
+        self.T = T
+        self.lc = layer.c()
+        B = step["pos"].shape[0]
+        nb = T.lib().hsa_decode_draft_workspace_bytes(C.byref(self.lc), B, n_tok, L_max)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        p = lambda t: None if t is None else C.c_void_p(t.data_ptr())
+        self.args = (C.byref(self.lc), B, n_tok, p(step["pos"]), L_max, p(step["Q"]),
+                     p(step["k_new"]), p(step["v_new"]), p(step.get("qI")), p(step.get("kI_new")),
+                     p(step.get("w")), p(O), None, None, C.c_void_p(self.ws.data_ptr()),
+                     self.ws.numel())
+        self.fn = T.lib().hsa_decode_draft
 
 
 def time_graph(calls, steps, warmup):
@@ -268,11 +290,15 @@ def bench_csa_decode(args, w):
     from long_context_hybrid_kv_amd import _lib as T
     from synth import gen
     L = w.L
+    nd = getattr(args, "draft", 1)
     t0 = time.time()
-    layers, step = build_decode_state(w, "csa", L, T, gen, args.copies)
+    layers, step = build_decode_state(w, "csa", L, T, gen, args.copies, draft=nd)
     log(f"[bench] {w.name}: state built in {time.time() - t0:.1f}s")
     O = torch.empty_like(step["Q"])
-    calls = [StepCall(T, lay, step, L, O, f"d{i}") for i, lay in enumerate(layers)]
+    if nd > 1:
+        calls = [DraftCall(T, lay, step, L + nd - 1, O, nd) for lay in layers]
+    else:
+        calls = [StepCall(T, lay, step, L, O, f"d{i}") for i, lay in enumerate(layers)]
     ms, n = time_graph(calls, args.steps, args.warmup)
     # dominant kernel: the indexer score scan, timed eagerly
     scan_ms, cnt = kernel_avg_ms(T, T.K_INDEXER_SCAN, lambda i: calls[i % len(calls)](),
@@ -282,17 +308,18 @@ def bench_csa_decode(args, w):
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     src = source_hash("indexer.hip", "common.h")
     res = {
-        "value": w.B / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": n,
+        "value": w.B * nd / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": n,
         "config": {"workload": w.name, "batch": w.B, "context": L, "heads": w.H, "kv_heads": 1,
                    "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
-                   "kv_dtype": "bf16", "cache_copies": args.copies},
+                   "kv_dtype": "bf16", "cache_copies": args.copies,
+                   **({"draft_tokens": nd} if nd > 1 else {})},
         "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": committed_traffic("idx_scan_kernel", w.name, src),
+                     "traffic": None if nd > 1 else committed_traffic("idx_scan_kernel", w.name, src),
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "avg_launch_ms": round(scan_ms, 5), "launches_timed": cnt},
     }
-    step_bytes = w.B * (nv * 128 + w.k_csa * 512 + w.n_win * 512 + 2 * w.H * 128 * 2)
+    step_bytes = w.B * (nv * 128 + nd * (w.k_csa * 512 + w.n_win * 512 + 2 * w.H * 128 * 2))
     res["step_hbm_frac"] = round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     return res, layers, step
 
@@ -613,6 +640,10 @@ def main():
     ap.add_argument("--workload", default="csa_decode_128k",
                     choices=["csa_decode_128k", "pro_decode_1m", "hybrid_prefill_128k"])
     ap.add_argument("--extra", action="store_true", help="also the other two workloads")
+    ap.add_argument("--draft", type=int, default=1,
+                    help="csa_decode_128k: verify a draft of N tokens per request (1-3 at the "
+                         "128K position: no block completes inside it, so replays append "
+                         "nothing); tok/s counts draft tokens")
     ap.add_argument("--index-fp8", action="store_true",
                     help="pro_decode_1m with fp8 indexer keys (a next row of the scope: the "
                          "scan reads half the bytes); reports the selection recall against "
@@ -632,6 +663,8 @@ def main():
     if args.traffic_summary:
         traffic_summary(args)
         return
+    if args.draft != 1 and (args.workload != "csa_decode_128k" or not 1 <= args.draft <= 3):
+        ap.error("--draft takes 1..3 with --workload csa_decode_128k")
     if args.index_fp8 and args.workload != "pro_decode_1m":
         ap.error("--index-fp8 applies to --workload pro_decode_1m")
     if args.gpus != 1:
