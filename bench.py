@@ -270,7 +270,7 @@ def traffic_summary(args):
     kib = float(1 << 20)   # the copy reads and writes 1 GiB
     f_scale, w_scale = kib / cf, kib / cw
     out = {"kernel": kernel, "workload": workload,
-           "source_hash": source_hash("indexer.hip", "common.h") if kernel.startswith("idx_")
+           "source_hash": source_hash("indexer.hip", "common.h", "update.h") if kernel.startswith("idx_")
            else source_hash("attention.hip", "common.h"),
            "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
            "dispatches": [nf, nw],
@@ -306,7 +306,7 @@ def bench_csa_decode(args, w):
     nv = (L - w.n_win + 1 + w.m_csa - 1) // w.m_csa
     scan_bytes = w.B * nv * 128
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
-    src = source_hash("indexer.hip", "common.h")
+    src = source_hash("indexer.hip", "common.h", "update.h")
     res = {
         "value": w.B * nd / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": n,
         "config": {"workload": w.name, "batch": w.B, "context": L, "heads": w.H, "kv_heads": 1,
@@ -497,7 +497,7 @@ def bench_pro_decode(args, w):
     scan_bytes = int(B * nv * key_b)
     step_bytes = B * (nv * key_b + w.k_csa * 256 + nvh * 256 + 2 * w.n_win * 512 + 4 * w.H * 256)
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
-    src = source_hash("indexer.hip", "common.h")
+    src = source_hash("indexer.hip", "common.h", "update.h")
     extra = {}
     if f8i:
         # selection recall: how much of each query's top-k over the bf16 keys the
