@@ -592,7 +592,7 @@ def bench_prefill(args, w):
     tot = ms_csa + ms_hca
     # dominant kernel: the attention launch with the larger share of the pair
     if att_hca_ms >= att_csa_ms:
-        kname, kms, kfl = "attn_kernel (HCA)", att_hca_ms, fl_hca
+        kname, kms, kfl = "attn_pair_kernel (HCA)", att_hca_ms, fl_hca
     else:
         kname, kms, kfl = "attn_kernel (CSA)", att_csa_ms, fl_csa_att
     tf = kfl / (kms * 1e-3) / 1e12
