@@ -101,10 +101,11 @@ def scale_of(d=128):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None):
+def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
-    hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)."""
+    hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1).
+    index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page)."""
     B = len(Ls)
     m = w.m(layer)
     n_win = w.n_win
@@ -125,7 +126,7 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None):
     ring_v = torch.zeros_like(ring_k)
     if layer == "csa":
         st["alpha_i"] = L.pooling_weights(torch.from_numpy(z["zi"]).cuda())
-        st["kic"] = cache(64, False)
+        st["kic"] = cache(64, index_fp8)
         tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda")
     for r, d in enumerate(reqs):
         Lr = int(Ls[r])

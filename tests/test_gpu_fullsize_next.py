@@ -1,0 +1,110 @@
+"""GPU parity of the decode variants at the workloads' full sizes, in the launch
+configuration the benchmark times them in:
+
+* Pro decode over fp8 indexer keys: batch 4 x 1048576 tokens, 128 heads, fp8
+  caches (e4m3fn codes, one scale per 64-entry page), CSA top-1024: every
+  request, and the compressed caches bit-exact;
+* draft verification: CSA decode, batch 32 x 131072 tokens, 64 heads, top-512,
+  three draft tokens per request through hsa_decode_draft (one indexer pass
+  per request scores the three queries): every query of every request, and the
+  caches after the draft bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hybrid as orc
+from oracle import numerics as nx
+from synth import configs, gen
+
+import hsa_testlib as T
+from long_context_hybrid_kv_amd import _lib as L
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_csa(w, d, t, s, kc, vc, kic, idx, O, lse, where):
+    """The CSA query at position t (query row s of request stream d); the
+    caches hold at least its visible blocks."""
+    m = w.m_csa
+    ref = orc.csa_query(t, d["q"][s], d["qi"][s], d["w"][s], d["k"], d["v"], kc, vc, kic, m,
+                        w.n_win, w.k_csa)
+    T.check_topk(idx, ref["scores"], w.k_csa, where=where)
+    sel = idx[idx >= 0]
+    if not np.array_equal(sel, ref["idx"][ref["idx"] >= 0]):
+        # an admissible selection that differs inside the tie band: attend to it
+        s0 = orc.window_start(t, w.n_win)
+        K = np.concatenate([nx.bf16_value(d["k"][s0:t + 1]), kc.values[sel]])
+        V = np.concatenate([nx.bf16_value(d["v"][s0:t + 1]), vc.values[sel]])
+        o, l = orc.attend(nx.bf16_value(d["q"][s]), K, V, T.scale_of())
+        ref = {"o": o, "lse": l}
+    err = float(np.max(np.abs(O - ref["o"])))
+    assert err <= T.OUT_TOL, f"{where}: max abs error {err}"
+    assert np.max(np.abs(lse - ref["lse"])) <= T.LSE_TOL, f"{where}: lse"
+    return err
+
+
+def _check_cache(c, r, ref, name):
+    n = len(ref)
+    assert np.array_equal(T.cache_bits(c, r, n), ref.bits), (r, name)
+    if ref.scales is not None:
+        assert np.array_equal(c.logical_scales(r, n).cpu().numpy().view(np.uint32),
+                              ref.scales.view(np.uint32)), (r, name, "scales")
+
+
+def test_pro_decode_1m_fp8_index_full():
+    w = configs.PRO_DECODE_1M
+    Ls = [w.L] * w.B
+    st = T.build_state(w, "csa", Ls, fp8=True, shuffle=False, index_fp8=True)
+    out = T.run_ops(w, "csa", st, Ls)
+    z = gen.pool_logits(w, "csa")
+    m = w.m_csa
+    worst = 0.0
+    for r, d in enumerate(st["reqs"]):
+        kc = orc.compress(d["k"][:w.L], z["zk"], m, "fp8")
+        vc = orc.compress(d["v"][:w.L], z["zv"], m, "fp8")
+        kic = orc.compress(d["ki"][:w.L], z["zi"], m, "fp8")
+        for name, ref in (("kc", kc), ("vc", vc), ("kic", kic)):
+            _check_cache(st[name], r, ref, name)
+        worst = max(worst, _check_csa(w, d, w.L, 0, kc, vc, kic, out["idx"][r], out["O"][r],
+                                      out["lse"][r], f"req {r}"))
+    print(f"pro_decode_1m fp8 indexer keys: max abs error {worst:.3e}")
+
+
+def test_csa_decode_128k_draft3_full():
+    w = configs.CSA_DECODE_128K
+    n_tok = 3
+    Ls = [w.L] * w.B
+    st = T.build_state(w, "csa", Ls, steps=n_tok, shuffle=False, ring_cap=w.n_win + n_tok - 1)
+    lay = T.layer_of(w, "csa", st)
+    reqs = st["reqs"]
+    stack = lambda f: np.stack([np.stack([f(r, d, i) for i in range(n_tok)])
+                                for r, d in enumerate(reqs)])
+    pos = torch.tensor(Ls, dtype=torch.int64, device="cuda")
+    O, lse, idx = L.decode_draft(
+        lay, pos, max(Ls) + n_tok - 1,
+        T.dev_bf16(stack(lambda r, d, i: d["q"][i])),
+        T.dev_bf16(stack(lambda r, d, i: d["k"][Ls[r] + i])),
+        T.dev_bf16(stack(lambda r, d, i: d["v"][Ls[r] + i])),
+        qI=T.dev_bf16(stack(lambda r, d, i: d["qi"][i])),
+        kI_new=T.dev_bf16(stack(lambda r, d, i: d["ki"][Ls[r] + i])),
+        w=torch.from_numpy(stack(lambda r, d, i: d["w"][i])).cuda(),
+        with_lse=True, with_idx=True)
+    L.check_device_error()
+    Ob, lse, idx = T.to_f64(O), lse.cpu().numpy(), idx.cpu().numpy()
+    z = st["z"]
+    m = w.m_csa
+    worst = 0.0
+    for r, d in enumerate(reqs):
+        n = Ls[r] + n_tok
+        kc = orc.compress(d["k"][:n], z["zk"], m)
+        vc = orc.compress(d["v"][:n], z["zv"], m)
+        kic = orc.compress(d["ki"][:n], z["zi"], m)
+        for name, ref in (("kc", kc), ("vc", vc), ("kic", kic)):
+            assert int(st[name].n_entries[r]) == len(ref), (r, name)
+            _check_cache(st[name], r, ref, name)
+        for i in range(n_tok):
+            t = Ls[r] + i
+            worst = max(worst, _check_csa(w, d, t, i, kc, vc, kic, idx[r, i], Ob[r, i],
+                                          lse[r, i], f"req {r} t {t}"))
+    print(f"csa_decode_128k draft of {n_tok}: max abs error {worst:.3e}")
