@@ -223,6 +223,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   }
   const int c_first = blockIdx.x * CPW;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  const int r8 = lane >> 3, p8 = lane & 7;   // bf16 loads: key r8 of 8, 16-byte piece p8
   // A workgroup scores CPW consecutive chunks of kCH blocks; in each chunk a
   // wave streams 128 consecutive blocks = two whole pages.  The page ids depend
   // only on the request, so they are loaded alongside the query's position and
@@ -264,12 +265,25 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      const int64_t b = w0b + 16 * u + row;
       const int pg = pid[c][u >> 2];
-      const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
-      const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
-      x0[u] = __builtin_nontemporal_load(kr + g);
-      x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+      if constexpr (F8K) {
+        const int64_t b = w0b + 16 * u + row;
+        const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
+        const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
+        x0[u] = __builtin_nontemporal_load(kr + g);
+        x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+      } else {
+        // whole rows: each load instruction reads 8 consecutive 128-byte keys,
+        // lane (r8, p8) piece p8 of key r8 (score() moves them to the MFMA
+        // layout).  Tiles are page-aligned, so both loads stay in the page;
+        // keys past the row's end are read but never scored, and a bad page
+        // reads page 0.
+        const bool okp = (unsigned)pg < (unsigned)kic.n_pages;
+        const KeyT* kr = (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage +
+                                                   16 * (u & 3) + r8) * (kDI * 2)) + p8;
+        x0[u] = __builtin_nontemporal_load(kr);
+        x1[u] = __builtin_nontemporal_load(kr + 8 * (kDI * 2 / 16));
+      }
     }
     if (lane == 0) {
 #pragma unroll
@@ -293,6 +307,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   // the LDS histogram is cleared while the keys are in flight
   __shared__ uint32_t lhist[kBins];
   __shared__ float lsc[CPW * kCH];
+  __shared__ bf16x8 ltile[F8K ? 1 : 4][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
   for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
   __syncthreads();
 
@@ -307,8 +322,17 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
         k0 = e4m3x8_to_bf16x8(x0[u]);
         k1 = e4m3x8_to_bf16x8(x1[u]);
       } else {
-        k0 = x0[u];
-        k1 = x1[u];
+        // the wave's 16 keys through its LDS tile: piece p of key r is stored
+        // at slot p ^ (r & 7), so the row-wise writes and the MFMA-layout
+        // reads both spread over all banks.  LDS executes a wave's accesses
+        // in order; the asm statements keep the compiler from moving them
+        // past each other (lanes read what other lanes wrote).
+        asm volatile("" ::: "memory");
+        ltile[wv][r8 * 8 + (p8 ^ r8)] = x0[u];
+        ltile[wv][(8 + r8) * 8 + (p8 ^ r8)] = x1[u];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        k0 = ltile[wv][row * 8 + (g ^ (row & 7))];
+        k1 = ltile[wv][row * 8 + ((4 + g) ^ (row & 7))];
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
