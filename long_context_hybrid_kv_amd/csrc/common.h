@@ -73,6 +73,7 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // values, by the hardware converter: every e4m3 value is a float with at most
 // 4 significant bits, so dropping the float's low 16 bits is exact.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 c) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   const f2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave and chunk
   // key pieces of a lane: 8 channels each (bf16: 16 bytes; fp8 codes: 8 bytes,
   // widened to bf16 when scored, the page scale applied to the head sum)
-  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  typedef typename std::conditional<F8K, u32x4, bf16x8>::type KeyT;
   float ksc[CPW][2];   // fp8: scale of the wave's two pages of each chunk
   // branch-free loads: blocks out of range (or on a bad page) read row 0 of page 0
   auto load = [&](int c, KeyT* x0, KeyT* x1) {
@@ -266,19 +266,20 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       const int pg = pid[c][u >> 2];
+      const bool okp = (unsigned)pg < (unsigned)kic.n_pages;
       if constexpr (F8K) {
-        const int64_t b = w0b + 16 * u + row;
-        const bool ok = b < b_end && (unsigned)pg < (unsigned)kic.n_pages;
-        const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
-        x0[u] = __builtin_nontemporal_load(kr + g);
-        x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+        // 64-byte keys: one load instruction reads 16 whole keys, lane (row, g)
+        // channels 16g .. 16g+15 of key `row` (the query's channels are
+        // permuted to match).  Keys past the row's end are read but never
+        // scored; a bad page reads page 0.
+        x0[u] = __builtin_nontemporal_load(
+            (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row) * kDI) + g);
       } else {
         // whole rows: each load instruction reads 8 consecutive 128-byte keys,
         // lane (r8, p8) piece p8 of key r8 (score() moves them to the MFMA
         // layout).  Tiles are page-aligned, so both loads stay in the page;
         // keys past the row's end are read but never scored, and a bad page
         // reads page 0.
-        const bool okp = (unsigned)pg < (unsigned)kic.n_pages;
         const KeyT* kr = (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage +
                                                    16 * (u & 3) + r8) * (kDI * 2)) + p8;
         x0[u] = __builtin_nontemporal_load(kr);
@@ -296,11 +297,13 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   load(0, xa0, xa1);
   if (CPW > 1) load(1, xb0, xb1);
 
+  // query head `row` in the channel order of the keys: bf16, channels 8g..8g+7
+  // then 32+8g..; fp8, 16g..16g+7 then 16g+8..16g+15
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
-    a0 = qa[g];
-    a1 = qa[4 + g];
+    a0 = qa[F8K ? 2 * g : g];
+    a1 = qa[F8K ? 2 * g + 1 : 4 + g];
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
@@ -319,8 +322,8 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
     for (int u = 0; u < NT; ++u) {
       bf16x8 k0, k1;
       if constexpr (F8K) {
-        k0 = e4m3x8_to_bf16x8(x0[u]);
-        k1 = e4m3x8_to_bf16x8(x1[u]);
+        k0 = e4m3x8_to_bf16x8(x0[u].xy);   // channels 16g .. 16g+7
+        k1 = e4m3x8_to_bf16x8(x0[u].zw);   // channels 16g+8 .. 16g+15
       } else {
         // the wave's 16 keys through its LDS tile: piece p of key r is stored
         // at slot p ^ (r & 7), so the row-wise writes and the MFMA-layout
@@ -437,7 +440,7 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
       if (threadIdx.x == i) ws.state[(int64_t)(q0 + i) * kStateInts + 5] = (int32_t)nvq[i];
 
   constexpr int NT = kCH / 4 / 16;
-  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  typedef typename std::conditional<F8K, u32x4, bf16x8>::type KeyT;
   const int64_t cb = (int64_t)c_first * kCH;
   const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
   const int64_t c_end = nv_max < cb + kCH ? nv_max : cb + kCH;
@@ -448,14 +451,22 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
       ksc[j] = (unsigned)pid[j] < (unsigned)kic.n_pages ? kic.scale[pid[j]] : 1.f;
   }
   KeyT x0[NT], x1[NT];
+  const int r8 = lane >> 3, p8 = lane & 7;   // bf16 loads: key r8 of 8, 16-byte piece p8
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
-    const int64_t b = w0b + 16 * u + row;
     const int pg = pid[u >> 2];
-    const bool ok = b < c_end && (unsigned)pg < (unsigned)kic.n_pages;
-    const KeyT* kr = (const KeyT*)kic.row(ok ? pg : 0, ok ? b : 0);
-    x0[u] = __builtin_nontemporal_load(kr + g);
-    x1[u] = __builtin_nontemporal_load(kr + 4 + g);
+    const bool okp = (unsigned)pg < (unsigned)kic.n_pages;
+    if constexpr (F8K) {
+      // 16 whole 64-byte keys per load instruction, as in idx_scan_kernel
+      x0[u] = __builtin_nontemporal_load(
+          (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row) * kDI) + g);
+    } else {
+      // whole 128-byte keys, 8 per load instruction, as in idx_scan_kernel
+      const KeyT* kr = (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage +
+                                                 16 * (u & 3) + r8) * (kDI * 2)) + p8;
+      x0[u] = __builtin_nontemporal_load(kr);
+      x1[u] = __builtin_nontemporal_load(kr + 8 * (kDI * 2 / 16));
+    }
   }
   if (lane == 0) {
 #pragma unroll
@@ -467,8 +478,8 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
   bf16x8 a0 = {}, a1 = {};
   if ((row >> 2) < G) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)(q0 + (row >> 2)) * kHI + (row & 3)) * kDI);
-    a0 = qa[g];
-    a1 = qa[4 + g];
+    a0 = qa[F8K ? 2 * g : g];   // the keys' channel order, as in idx_scan_kernel
+    a1 = qa[F8K ? 2 * g + 1 : 4 + g];
   }
   // this lane group's query: weights and visible blocks
   const bool gq = g < G;
@@ -483,17 +494,24 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
 
   __shared__ uint32_t lh2[G][kBins / 2];
   __shared__ float lsc[G][kCH];
+  __shared__ bf16x8 ltile[F8K ? 1 : 4][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
   for (int i = threadIdx.x; i < G * (kBins / 2); i += 256) (&lh2[0][0])[i] = 0;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     bf16x8 k0, k1;
     if constexpr (F8K) {
-      k0 = e4m3x8_to_bf16x8(x0[u]);
-      k1 = e4m3x8_to_bf16x8(x1[u]);
+      k0 = e4m3x8_to_bf16x8(x0[u].xy);
+      k1 = e4m3x8_to_bf16x8(x0[u].zw);
     } else {
-      k0 = x0[u];
-      k1 = x1[u];
+      // through the wave's swizzled LDS tile into the MFMA layout, as in
+      // idx_scan_kernel
+      asm volatile("" ::: "memory");
+      ltile[wv][r8 * 8 + (p8 ^ r8)] = x0[u];
+      ltile[wv][(8 + r8) * 8 + (p8 ^ r8)] = x1[u];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      k0 = ltile[wv][row * 8 + (g ^ (row & 7))];
+      k1 = ltile[wv][row * 8 + ((4 + g) ^ (row & 7))];
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
