@@ -185,34 +185,36 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, u
   return off + x - v;
 }
 
-// Write a 4096-bin LDS histogram (256 threads) as a list of its nonzero bins,
-// bin << 16 | count, into list `li` of query row `qrow`.  Lists are rewritten
-// whole by every call, so the workspace needs no clearing between calls.
+// Write a 4096-bin LDS histogram (a workgroup of NTH threads) as a list of its
+// nonzero bins, bin << 16 | count, into list `li` of query row `qrow`.  Lists
+// are rewritten whole by every call, so the workspace needs no clearing
+// between calls.
+template <int NTH = 256>
 __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const IdxWs& ws, int qrow,
                                                 int li) {
-  __shared__ uint32_t sh[4];
+  __shared__ uint32_t sh[NTH / 64];
   __syncthreads();
-  constexpr int BPT = kBins / 256;
+  constexpr int BPT = kBins / NTH;
   uint32_t v[BPT];
   uint32_t nz = 0;
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {   // thread t owns bins t, t + 256, ... (no bank conflicts)
-    v[j] = lhist[threadIdx.x + 256 * j];
+  for (int j = 0; j < BPT; ++j) {   // thread t owns bins t, t + NTH, ... (no bank conflicts)
+    v[j] = lhist[threadIdx.x + NTH * j];
     nz += v[j] != 0;
   }
   uint32_t tot;
-  uint32_t off = block_scan_nt<256>(nz, &tot, sh);
+  uint32_t off = block_scan_nt<NTH>(nz, &tot, sh);
   uint32_t* dst = ws.hl + ((int64_t)qrow * ws.n_lists + li) * ws.list_cap;
 #pragma unroll
   for (int j = 0; j < BPT; ++j)
-    if (v[j]) dst[off++] = ((uint32_t)(threadIdx.x + 256 * j) << 16) | v[j];
+    if (v[j]) dst[off++] = ((uint32_t)(threadIdx.x + NTH * j) << 16) | v[j];
   if (threadIdx.x == 0) ws.hl_n[(int64_t)qrow * ws.n_lists + li] = (int32_t)tot;
 }
 
 // ---------------------------------------------------------------- decode: score scan
 
-template <int CPW, bool F8K>
-__global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
+template <int CPW, int NWV, bool F8K>
+__global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
                                                        int n_groups, UpdateArgs upd, int* fault) {
@@ -224,17 +226,20 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   const int c_first = blockIdx.x * CPW;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
   const int r8 = lane >> 3, p8 = lane & 7;   // bf16 loads: key r8 of 8, 16-byte piece p8
-  // A workgroup scores CPW consecutive chunks of kCH blocks; in each chunk a
-  // wave streams 128 consecutive blocks = two whole pages.  The page ids depend
-  // only on the request, so they are loaded alongside the query's position and
-  // entry count instead of after them: the key loads wait for one round trip.
+  // A workgroup of NWV waves scores CPW consecutive chunks of kCH blocks; in
+  // each chunk a wave streams BPW consecutive blocks = PPW whole pages.  The
+  // page ids depend only on the request, so they are loaded alongside the
+  // query's position and entry count instead of after them: the key loads wait
+  // for one round trip.
+  constexpr int BPW = kCH / NWV, PPW = BPW / kPage;
+  static_assert(PPW >= 1, "a wave streams whole pages");
   const int r = Q.pos ? (Q.req ? Q.req[qrow] : qrow) : Q.span_req;
-  int pid[CPW][2];
+  int pid[CPW][PPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
-    const int lp = (int)((((int64_t)(c_first + c)) * kCH + wv * (kCH / 4)) >> 6);
+    const int lp = (int)((((int64_t)(c_first + c)) * kCH + wv * BPW) >> 6);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < PPW; ++j)
       pid[c][j] = lp + j < kic.pages_per_req
                       ? kic.page_table[(int64_t)r * kic.pages_per_req + lp + j]
                       : -1;
@@ -248,19 +253,20 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   if (c_first >= n_active) return;
   if (c_first == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
 
-  constexpr int NT = kCH / 4 / 16;   // 16-block tiles per wave and chunk
-  // key pieces of a lane: 8 channels each (bf16: 16 bytes; fp8 codes: 8 bytes,
-  // widened to bf16 when scored, the page scale applied to the head sum)
+  constexpr int NT = BPW / 16;   // 16-block tiles per wave and chunk
+  // key pieces of a lane, 16 bytes each: bf16, 8 channels (two pieces per
+  // tile); fp8 codes, 16 channels (one piece per tile), widened to bf16 when
+  // scored, the page scale applied to the head sum
   typedef typename std::conditional<F8K, u32x4, bf16x8>::type KeyT;
-  float ksc[CPW][2];   // fp8: scale of the wave's two pages of each chunk
-  // branch-free loads: blocks out of range (or on a bad page) read row 0 of page 0
+  float ksc[CPW][PPW];   // fp8: scale of the wave's pages of each chunk
+  // branch-free loads (tile u lies in the wave's page u / 4)
   auto load = [&](int c, KeyT* x0, KeyT* x1) {
     const int64_t cb = (int64_t)(c_first + c) * kCH;
     const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
-    const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
+    const int64_t w0b = cb + (int64_t)wv * BPW;
     if constexpr (F8K) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < PPW; ++j)
         ksc[c][j] = (unsigned)pid[c][j] < (unsigned)kic.n_pages ? kic.scale[pid[c][j]] : 1.f;
     }
 #pragma unroll
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
     }
     if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < PPW; ++j)
         if (w0b + 64 * j < b_end && (unsigned)pid[c][j] >= (unsigned)kic.n_pages)
           atomicOr(fault, HSA_FAULT_PAGE);
     }
@@ -310,14 +316,14 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   // the LDS histogram is cleared while the keys are in flight
   __shared__ uint32_t lhist[kBins];
   __shared__ float lsc[CPW * kCH];
-  __shared__ bf16x8 ltile[F8K ? 1 : 4][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
-  for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
+  __shared__ bf16x8 ltile[F8K ? 1 : NWV][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
+  for (int i = threadIdx.x; i < kBins; i += NWV * 64) lhist[i] = 0;
   __syncthreads();
 
   auto score = [&](int c, const KeyT* x0, const KeyT* x1) {
     const int64_t cb = (int64_t)(c_first + c) * kCH;
     const int64_t b_end = nv < cb + kCH ? nv : cb + kCH;
-    const int64_t w0b = cb + (int64_t)wv * (kCH / 4);
+    const int64_t w0b = cb + (int64_t)wv * BPW;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
       bf16x8 k0, k1;
@@ -365,9 +371,9 @@ __global__ __launch_bounds__(256) void idx_scan_kernel(Queries Q, const u16* __r
   float* srow = ws.scores + (int64_t)qrow * ws.R;
   const int64_t s0 = (int64_t)c_first * kCH;
   const int64_t s_end = nv < s0 + CPW * kCH ? nv : s0 + CPW * kCH;
-  for (int i = threadIdx.x; i < CPW * kCH; i += 256)
+  for (int i = threadIdx.x; i < CPW * kCH; i += NWV * 64)
     if (s0 + i < s_end) srow[s0 + i] = lsc[i];
-  write_hist_list(lhist, ws, qrow, blockIdx.x);
+  write_hist_list<NWV * 64>(lhist, ws, qrow, blockIdx.x);
 }
 
 // Write a histogram of 16-bit counts packed two bins per word (bin b in half
@@ -1136,9 +1142,10 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const UpdateArgs ua = upd ? *upd : UpdateArgs{};
     const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
     const bool f8k = kic.dtype == HSA_FP8_E4M3;
-    auto scan = cpw == 4 ? (f8k ? idx_scan_kernel<4, true> : idx_scan_kernel<4, false>)
-                         : (f8k ? idx_scan_kernel<1, true> : idx_scan_kernel<1, false>);
-    timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m,
+    // eight waves, each streaming one page of every chunk
+    auto scan = cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true> : idx_scan_kernel<4, 8, false>)
+                         : (f8k ? idx_scan_kernel<1, 8, true> : idx_scan_kernel<1, 8, false>);
+    timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(8 * 64), 0, s, Qd, (const u16*)qI, w, kc, m,
                  n_win, k, ws, (int)n_groups, ua, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     launch_topk(1024, q.n, k, ws, idx, score, 0, s);
