@@ -148,6 +148,14 @@ def indexer_scores(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -
     return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float32).astype(np.float64)
 
 
+def indexer_scores_bf16(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -> np.ndarray:
+    """The index scores as a bf16 selector ranks them (wiki §8: the scores are
+    cast from fp32 to bf16 before the top-k): every score rounded once, after
+    the weighted head sum, to the nearest bf16 value (ties to even), as
+    float64.  The selection over them is topk_blocks (ties: lower block)."""
+    return nx.bf16_round_value(indexer_scores(qi_bits, w, kic_values))
+
+
 def topk_blocks(scores: np.ndarray, k: int) -> np.ndarray:
     """The min(k, n) blocks with the largest score (ties: lower block first),
     listed in ascending block order and padded with -1 to length k."""

@@ -197,3 +197,44 @@ def test_decode_equals_prefill_row():
     dec = orc.csa_query(L, inp["q"][L], inp["qi"][L], inp["w"][L], inp["k"][: L + 1], inp["v"][: L + 1],
                         caches["kc"], caches["vc"], caches["kic"], 4, 32, 8)
     assert np.array_equal(dec["o"], full["o"]) and np.array_equal(dec["idx"], full["idx"])
+
+
+def test_bf16_score_selection_closed_form():
+    """Scores known in closed form (one head, two channels): the bf16 selector
+    rounds after the head sum, to nearest with ties to even, and breaks equal
+    rounded scores toward the lower block."""
+    qi = np.zeros((4, 8), dtype=np.float32)
+    qi[0, :2] = 1.0                                  # head 0 = channels 0 + 1
+    w = np.array([1.0, 0.0, 0.0, 0.0], dtype=np.float32)
+    kic = np.zeros((5, 8))
+    kic[:, 0] = [1.0, 1.0, 1.0, 0.5, 1.0]
+    kic[:, 1] = [0.0, 2.0 ** -9, 2.0 ** -8 + 2.0 ** -9, 0.0, 2.0 ** -8]
+    exact = orc.indexer_scores(gen.bf16_bits(qi), w, kic)
+    assert exact.tolist() == [1.0, 1 + 2.0 ** -9, 1 + 2.0 ** -8 + 2.0 ** -9, 0.5, 1 + 2.0 ** -8]
+    s16 = orc.indexer_scores_bf16(gen.bf16_bits(qi), w, kic)
+    # the bf16 grid near 1 has spacing 2^-7: 1 + 2^-9 rounds down, 1 + 3 * 2^-9
+    # rounds up, and the midpoint 1 + 2^-8 goes to the even neighbour 1
+    assert s16.tolist() == [1.0, 1.0, 1 + 2.0 ** -7, 0.5, 1.0]
+    assert orc.topk_blocks(exact, 2).tolist() == [2, 4]
+    assert orc.topk_blocks(s16, 2).tolist() == [0, 2]          # ties at 1.0: blocks 0, 1, 4
+    assert orc.topk_blocks(s16, 3).tolist() == [0, 1, 2]
+    assert orc.topk_blocks(s16, 4).tolist() == [0, 1, 2, 4]
+
+
+def test_bf16_scores_are_rounded_bruteforce_scores():
+    r = np.random.default_rng(6)
+    qi = gen.bf16_bits(r.standard_normal((4, 8)).astype(np.float32))
+    w = (r.random(4) - 0.3).astype(np.float32)        # a negative weight too
+    kic = nx.bf16_value(gen.bf16_bits(r.standard_normal((300, 8)).astype(np.float32)))
+    got = orc.indexer_scores_bf16(qi, w, kic)
+    qv = nx.bf16_value(qi)
+    for b in range(300):
+        tot = sum(float(w[h]) * max(0.0, sum(qv[h, c] * kic[b, c] for c in range(8)))
+                  for h in range(4))
+        # a bf16 value (its bits round-trip) within half a bf16 ulp of the sum
+        assert nx.bf16_value(nx.bf16_bits_from_f64(np.array([got[b]])))[0] == got[b]
+        if tot != 0.0:
+            ulp = 2.0 ** (math.floor(math.log2(abs(tot))) - 7)
+            assert abs(got[b] - tot) <= ulp / 2 + 1e-12 * abs(tot)
+        else:
+            assert got[b] == 0.0
