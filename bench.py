@@ -554,10 +554,16 @@ def bench_prefill(args, w):
         del inp
     log(f"[bench] {w.name}: inputs built")
     q = T.Queries.span(Tn)
+    s16 = getattr(args, "index_bf16_scores", False)
+
+    def select(bf16_scores):
+        d = st["csa"]
+        return T.indexer_topk(q, d["qI"], d["w"], d["kic"], w.m_csa, w.n_win, w.k_csa,
+                              bf16_scores=bf16_scores)[0]
 
     def csa():
         d = st["csa"]
-        idx, _ = T.indexer_topk(q, d["qI"], d["w"], d["kic"], w.m_csa, w.n_win, w.k_csa)
+        idx = select(s16)
         T.csa_attn(q, d["Q"], d["k"], d["v"], w.n_win, d["kc"], d["vc"], w.m_csa, idx, w.k_csa)
 
     def hca():
@@ -596,13 +602,29 @@ def bench_prefill(args, w):
     else:
         kname, kms, kfl = "attn_kernel (CSA)", att_csa_ms, fl_csa_att
     tf = kfl / (kms * 1e-3) / 1e12
+    extra = {}
+    if s16:
+        # the selector alone with fp32 and with bf16 scores, and how many of the
+        # fp32 selection's blocks the bf16 selection keeps (rows ascending,
+        # -1 padded: padding sorts last as INT_MAX)
+        ms32, ms16 = timed(lambda: select(False), n), timed(lambda: select(True), n)
+        i32, i16 = select(False).clone(), select(True).clone()
+        big = torch.iinfo(torch.int32).max
+        i16s = torch.where(i16 < 0, torch.full_like(i16, big), i16)
+        pos = torch.searchsorted(i16s, torch.where(i32 < 0, torch.full_like(i32, big), i32))
+        hit = (i16s.gather(1, pos.clamp(max=w.k_csa - 1)) == i32) & (i32 >= 0)
+        extra = {"selector_ms_fp32_scores": round(ms32, 4), "selector_ms_bf16_scores": round(ms16, 4),
+                 "index_recall_vs_fp32_scores": round(hit.sum().item() / (i32 >= 0).sum().item(), 5)}
+        del i32, i16, i16s, pos, hit
     return {"value": Tn / (tot * 1e-3) / 1e3, "unit": "Ktok/s", "ms_per_step": tot, "steps": 2 * n,
             "ms_csa_layer": ms_csa, "ms_hca_layer": ms_hca,
             "ms_attn_csa": att_csa_ms, "ms_attn_hca": att_hca_ms,
             "pair_mfma_frac": round((fl_csa_att + fl_idx + fl_hca) / (tot * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "algorithmic_tflop": round((fl_csa_att + fl_idx + fl_hca) / 1e12, 3),
+            **extra,
             "config": {"workload": w.name, "T": Tn, "heads": w.H, "kv_heads": 1, "d": 128,
-                       "topk": w.k_csa, "window": w.n_win, "layers": "csa+hca", "planted": True},
+                       "topk": w.k_csa, "window": w.n_win, "layers": "csa+hca", "planted": True,
+                       **({"index_scores": "bf16"} if s16 else {})},
             "roofline": {"bound": "mfma", "kernel": kname, "achieved": round(tf, 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -648,6 +670,10 @@ def main():
                     help="pro_decode_1m with fp8 indexer keys (a next row of the scope: the "
                          "scan reads half the bytes); reports the selection recall against "
                          "bf16 keys")
+    ap.add_argument("--index-bf16-scores", action="store_true",
+                    help="hybrid_prefill_128k: the CSA selector ranks index scores rounded to bf16 "
+                         "(hsa_indexer_topk_bf16_scores); also times the selector alone both ways "
+                         "and reports the recall of the fp32-score selection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -667,6 +693,8 @@ def main():
         ap.error("--draft takes 1..3 with --workload csa_decode_128k")
     if args.index_fp8 and args.workload != "pro_decode_1m":
         ap.error("--index-fp8 applies to --workload pro_decode_1m")
+    if args.index_bf16_scores and args.workload != "hybrid_prefill_128k":
+        ap.error("--index-bf16-scores applies to --workload hybrid_prefill_128k")
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU sharding is a "
                                    "design note only", "n_gpus": args.gpus}))
@@ -700,7 +728,8 @@ def main():
             "data": "synthetic (seeded N(0,1) tokens; caches compressed on the GPU)",
             "config": res["config"], "roofline": res["roofline"]}
     for key in ("step_hbm_frac", "pair_mfma_frac", "ms_csa_layer", "ms_hca_layer",
-                "index_recall_vs_bf16_keys"):
+                "index_recall_vs_bf16_keys", "selector_ms_fp32_scores", "selector_ms_bf16_scores",
+                "index_recall_vs_fp32_scores"):
         if key in res:
             line[key] = res[key]
     if args.extra:

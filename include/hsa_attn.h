@@ -166,6 +166,19 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
                             int32_t n_win, int32_t k, int32_t* idx, float* score,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The same selection over index scores rounded to bf16 (wiki §8: the index
+ * scores are cast from fp32 to bf16 before the top-k selector).  Every fp32
+ * score is rounded once to the nearest bf16 (ties to even) and the top-k is
+ * taken over the rounded values, ties to the lower block; `score`, when not
+ * NULL, receives the rounded values.  Arguments, layouts, ownership,
+ * workspace (hsa_indexer_topk_workspace_bytes) and errors as
+ * hsa_indexer_topk. */
+hsa_status hsa_indexer_topk_bf16_scores(const hsa_queries* q, const void* qI, const float* w,
+                                        int32_t H_I, int32_t d_I, const hsa_paged* kIc,
+                                        int32_t m, int32_t n_win, int32_t k, int32_t* idx,
+                                        float* score, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
 /* CSA main attention (wiki §5.2 + §5.3): per query, one softmax over the
  * window rows of win_k/win_v and the compressed entries idx[i][0..min(k,n_vis))
  * of kc/vc.  Q bf16 [n][H][d]; O [n][H][d] of o_dtype (HSA_BF16, or HSA_FP32 to

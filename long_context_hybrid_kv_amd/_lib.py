@@ -69,6 +69,10 @@ _SIGS = {
     "hsa_indexer_topk": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int32,
                                    C.c_int32, C.POINTER(_Paged), C.c_int32, C.c_int32, C.c_int32,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "hsa_indexer_topk_bf16_scores": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_void_p,
+                                               C.c_int32, C.c_int32, C.POINTER(_Paged), C.c_int32,
+                                               C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                               C.c_void_p, C.c_size_t, C.c_void_p]),
     "hsa_csa_attn_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
                                                   C.c_int32]),
     "hsa_csa_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
@@ -287,15 +291,17 @@ def kv_compress(x: Tokens, out: PagedCache, req: int, first_block: int, n_blocks
 
 
 def indexer_topk(q: Queries, qI: torch.Tensor, w: torch.Tensor, kIc: PagedCache, m: int,
-                 n_win: int, k: int, with_score: bool = False, ws_key="indexer"):
+                 n_win: int, k: int, with_score: bool = False, ws_key="indexer",
+                 bf16_scores: bool = False):
+    """hsa_indexer_topk, or hsa_indexer_topk_bf16_scores (bf16_scores=True)."""
     qc, kc = q.c(), kIc.c()
     idx = torch.empty((q.n, k), dtype=torch.int32, device=qI.device)
     score = torch.empty((q.n, k), dtype=torch.float32, device=qI.device) if with_score else None
     nb = lib().hsa_indexer_topk_workspace_bytes(C.byref(qc), m, n_win, k)
     ws, wsb = _ws_args(_WS.get(ws_key, nb, qI.device))
-    _check(lib().hsa_indexer_topk(C.byref(qc), _ptr(qI), _ptr(w), qI.shape[-2], qI.shape[-1],
-                                  C.byref(kc), m, n_win, k, _ptr(idx), _ptr(score), ws, wsb,
-                                  _stream()), "indexer_topk")
+    fn = lib().hsa_indexer_topk_bf16_scores if bf16_scores else lib().hsa_indexer_topk
+    _check(fn(C.byref(qc), _ptr(qI), _ptr(w), qI.shape[-2], qI.shape[-1], C.byref(kc), m, n_win,
+              k, _ptr(idx), _ptr(score), ws, wsb, _stream()), "indexer_topk")
     return idx, score
 
 

@@ -265,10 +265,10 @@ size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t
   return indexer_ws_bytes(q->n, nvis_host(q->max_pos, m, n_win), k, is_span(q));
 }
 
-hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
-                            int32_t d_I, const hsa_paged* kIc, int32_t m, int32_t n_win,
-                            int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
+static hsa_status indexer_topk(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
+                               int32_t d_I, const hsa_paged* kIc, int32_t m, int32_t n_win,
+                               int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                               hipStream_t stream, bool s16) {
   hsa_status s;
   if ((s = check_paged(kIc, "kIc", kDI, true)) != HSA_OK) return s;
   if ((s = check_queries(q, kIc->n_req)) != HSA_OK) return s;
@@ -283,8 +283,25 @@ hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w
       "indexer_topk: decode rows longer than 2^21 visible blocks are not supported");
   if ((s = check_ws(ws, ws_bytes, hsa_indexer_topk_workspace_bytes(q, m, n_win, k))) != HSA_OK)
     return s;
-  return hip_status(launch_indexer(*q, qI, w, *kIc, m, n_win, k, idx, score, ws, ws_bytes, stream),
+  return hip_status(launch_indexer(*q, qI, w, *kIc, m, n_win, k, idx, score, ws, ws_bytes, stream,
+                                   nullptr, 1, s16),
                     "indexer_topk");
+}
+
+hsa_status hsa_indexer_topk(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
+                            int32_t d_I, const hsa_paged* kIc, int32_t m, int32_t n_win,
+                            int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return indexer_topk(q, qI, w, H_I, d_I, kIc, m, n_win, k, idx, score, ws, ws_bytes, stream,
+                      false);
+}
+
+hsa_status hsa_indexer_topk_bf16_scores(const hsa_queries* q, const void* qI, const float* w,
+                                        int32_t H_I, int32_t d_I, const hsa_paged* kIc, int32_t m,
+                                        int32_t n_win, int32_t k, int32_t* idx, float* score,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return indexer_topk(q, qI, w, H_I, d_I, kIc, m, n_win, k, idx, score, ws, ws_bytes, stream,
+                      true);
 }
 
 size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t k) {

@@ -217,9 +217,10 @@ int64_t indexer_max_blocks();   // longest visible-block row the decode indexer 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,
-                          const UpdateArgs* upd = nullptr, int group = 1);
+                          const UpdateArgs* upd = nullptr, int group = 1, bool s16 = false);
 // group (2..4, listed queries, no upd): consecutive queries g*group ..
-// g*group+group-1 belong to one request and share each pass over its keys
+// g*group+group-1 belong to one request and share each pass over its keys.
+// s16: the scores are rounded to bf16 before the selection (not with group > 1)
 
 // decode: 64-entry chunks per split of a query (a layer constant, so a
 // request's result does not depend on the batch it is in)

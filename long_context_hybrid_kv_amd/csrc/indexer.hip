@@ -128,6 +128,39 @@ __device__ __forceinline__ uint64_t ld_cand(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Index scores in the workspace: fp32, or (S16) rounded once to bf16, round
+// to nearest even, where the selection runs on bf16 scores (the wiki's bf16
+// selector).  Row q holds R scores.  Scores are rounded before they are
+// histogrammed, so every pass of the selection sees the same values.
+template <bool S16>
+__device__ __forceinline__ float score_round(float s) {
+  if constexpr (S16) return (float)(__bf16)s;
+  else return s;
+}
+template <bool S16>
+__device__ __forceinline__ void* score_row(const IdxWs& ws, int64_t q) {
+  return (char*)ws.scores + q * ws.R * (S16 ? 2 : 4);
+}
+template <bool S16>
+__device__ __forceinline__ float score_load(const void* row, int64_t i) {
+  if constexpr (S16) return __uint_as_float((uint32_t)((const u16*)row)[i] << 16);
+  else return ((const float*)row)[i];
+}
+template <bool S16>   // s: a value score_round returned
+__device__ __forceinline__ void score_store(void* row, int64_t i, float s) {
+  if constexpr (S16) ((u16*)row)[i] = (u16)(__float_as_uint(s) >> 16);
+  else ((float*)row)[i] = s;
+}
+// Score i of a row if i < lim, for a caller that ignores the value otherwise:
+// fp32 rows read 0 past lim; bf16 rows clamp the index to the row's capacity
+// R instead, so their 16-bit loads need no branch (a branch around each one
+// made the compiler wait for every load before the next).
+template <bool S16>
+__device__ __forceinline__ float score_get(const void* row, int64_t i, int64_t lim, int64_t R) {
+  if constexpr (S16) return score_load<true>(row, i < R ? i : R - 1);
+  else return i < lim ? ((const float*)row)[i] : 0.f;
+}
+
 // exclusive prefix sum over a 256-thread block; returns the block total in *total
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -159,6 +192,36 @@ __device__ __forceinline__ int64_t clamp_nvis(int64_t nv, const int32_t* n_entri
     nv = ne < 0 ? 0 : ne;
   }
   return nv;
+}
+
+// bitwise AND and OR of 64-bit values over an NT-thread block (every thread
+// gets both totals; sh64 holds 2 * NT / 64 words)
+template <int NT>
+__device__ __forceinline__ void block_and_or(uint64_t* a, uint64_t* o, uint64_t* sh64) {
+  uint32_t alo = (uint32_t)*a, ahi = (uint32_t)(*a >> 32);
+  uint32_t olo = (uint32_t)*o, ohi = (uint32_t)(*o >> 32);
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    alo &= __shfl_xor(alo, d);
+    ahi &= __shfl_xor(ahi, d);
+    olo |= __shfl_xor(olo, d);
+    ohi |= __shfl_xor(ohi, d);
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    sh64[wv] = ((uint64_t)ahi << 32) | alo;
+    sh64[NT / 64 + wv] = ((uint64_t)ohi << 32) | olo;
+  }
+  __syncthreads();
+  uint64_t x = ~0ull, y = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    x &= sh64[i];
+    y |= sh64[NT / 64 + i];
+  }
+  __syncthreads();   // sh64 is reused
+  *a = x;
+  *o = y;
 }
 
 // exclusive prefix sum over an NT-thread block (NT a multiple of 64)
@@ -213,7 +276,7 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
 
 // ---------------------------------------------------------------- decode: score scan
 
-template <int CPW, int NWV, bool F8K>
+template <int CPW, int NWV, bool F8K, bool S16>
 __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
@@ -351,6 +414,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
         float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
                    w2 * fmaxf(acc[2], 0.f) + w3 * fmaxf(acc[3], 0.f);
         if constexpr (F8K) sc *= ksc[c][u >> 2];   // ReLU commutes with a scale > 0
+        sc = score_round<S16>(sc);
         lsc[b - (int64_t)c_first * kCH] = sc;
         atomicAdd(&lhist[order_key(sc) >> 20], 1u);
       }
@@ -368,11 +432,11 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   }
   __syncthreads();
   // the scores leave in one coalesced run
-  float* srow = ws.scores + (int64_t)qrow * ws.R;
+  void* srow = score_row<S16>(ws, qrow);
   const int64_t s0 = (int64_t)c_first * kCH;
   const int64_t s_end = nv < s0 + CPW * kCH ? nv : s0 + CPW * kCH;
   for (int i = threadIdx.x; i < CPW * kCH; i += NWV * 64)
-    if (s0 + i < s_end) srow[s0 + i] = lsc[i];
+    if (s0 + i < s_end) score_store<S16>(srow, s0 + i, lsc[i]);
   write_hist_list<NWV * 64>(lhist, ws, qrow, blockIdx.x);
 }
 
@@ -551,7 +615,7 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
 // The block range is the fast grid index and the number of ranges a multiple
 // of 8: workgroups are dealt to the 8 XCDs round-robin, so each XCD's L2
 // holds the keys of one eighth of the blocks instead of all of them.
-template <bool F8K>
+template <bool F8K, bool S16>
 __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, int nq,
                                                        const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
@@ -649,7 +713,7 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
         float s = wq[at][0] * fmaxf(acc[0], 0.f) + wq[at][1] * fmaxf(acc[1], 0.f) +
                   wq[at][2] * fmaxf(acc[2], 0.f) + wq[at][3] * fmaxf(acc[3], 0.f);
         if constexpr (F8K) s *= cs;   // ReLU commutes with a scale > 0
-        ws.scores[(int64_t)(16 * qt + 4 * at + g) * ws.R + b] = s;
+        score_store<S16>(score_row<S16>(ws, 16 * qt + 4 * at + g), b, score_round<S16>(s));
       }
     }
     c0 = n0;
@@ -663,6 +727,7 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
 // workgroup (the 4096-bin LDS histogram is cleared and written out once per
 // kHistSpan scores).
 
+template <bool S16>
 __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, const Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
                                                        int* fault) {
@@ -674,14 +739,14 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
   if (b_begin > 0 && b_begin >= nv) return;
   if (slice == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
   const int64_t b_end = nv < b_begin + kHistSpan ? nv : b_begin + kHistSpan;
-  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const void* srow = score_row<S16>(ws, qrow);
   constexpr int kPer = kHistSpan / 256;
   // all loads in flight before the histogram is cleared and filled
   float sc[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int64_t b = b_begin + 256 * u + threadIdx.x;
-    sc[u] = b < b_end ? srow[b] : 0.f;
+    sc[u] = score_get<S16>(srow, b, b_end, ws.R);   // counted only below b_end
   }
   __shared__ uint32_t lhist[kBins];
   for (int i = threadIdx.x; i < kBins; i += 256) lhist[i] = 0;
@@ -703,7 +768,7 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
 // host), else in the workspace.
 // mode 0: the whole selection; mode 1: threshold only (long rows, before the
 // multi-workgroup select kernel); mode 2: refine + emit only (after it).
-template <int NT>
+template <int NT, bool S16>
 __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, int out_row0,
                                                       int cand_lds, int bm_lds_words, int mode) {
@@ -713,19 +778,26 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   __shared__ int s_thr, s_above, s_dstar;
   __shared__ uint32_t s_ncand, s_next, s_dabove;
   __shared__ uint32_t h256[256];
+  __shared__ uint64_t sh64[S16 ? 2 * (NT / 64) : 1];
   const int qrow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
   const int64_t nv = st[5];
-  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const void* srow = score_row<S16>(ws, qrow);
 
-  // first round of scores, loaded before the threshold search (independent of it)
+  // first round of scores, loaded before the threshold search (independent of
+  // it).  bf16 rows keep the raw 16 bits until the scores are classified: a
+  // conversion here would make the threshold search wait for these loads.
   constexpr int U = NT >= 1024 ? 32 : 16;
   float sc0[U];
+  uint32_t raw0[S16 ? U : 1];
   if (mode == 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t b = (int64_t)u * NT + tid;
-      sc0[u] = b < ws.R ? srow[b] : 0.f;
+      if constexpr (S16)
+        raw0[u] = ((const u16*)srow)[b < ws.R ? b : ws.R - 1];
+      else
+        sc0[u] = b < ws.R ? ((const float*)srow)[b] : 0.f;
     }
   }
   // mode 2: the threshold state, the first NT chunk candidate counts and the
@@ -887,7 +959,10 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t b = base + (int64_t)u * NT + tid;
-      sc[u] = base == 0 ? sc0[u] : (b < nv ? srow[b] : 0.f);
+      float s0;
+      if constexpr (S16) s0 = __uint_as_float(raw0[u] << 16);
+      else s0 = sc0[u];
+      sc[u] = base == 0 ? s0 : score_get<S16>(srow, b, nv, ws.R);   // classified below nv
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -926,17 +1001,36 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     int shift = 44;   // bits 63..52 of the composite key were the histogram bin
     // at most 7 digit passes cover the remaining 52 key bits (scores, then ids);
     // keys are unique (they contain the block id), so the candidates left after
-    // the last pass are exactly the ones still needed
-    while (need > 0) {
-      if (nc <= (uint32_t)need || shift < -4) {
+    // the last pass are exactly the ones still needed.  fp32 scores take the
+    // 8-bit digits in turn (they rarely tie, so one or two passes end it).
+    // bf16 scores tie often: a pass there takes the 8 bits from the highest
+    // bit in which the candidates still differ (an AND / OR reduction finds
+    // it), so no pass is spent on bits they all share; the candidates left
+    // share every bit down to that digit, so the next pass starts at least 8
+    // bits lower and 7 passes still suffice.
+    for (int pass = 0; need > 0; ++pass, shift -= 8) {
+      if (nc <= (uint32_t)need || pass >= 7) {
         for (uint32_t i = tid; i < nc; i += NT) {
           const uint32_t b = ~(uint32_t)ld_cand(csrc + i);
           atomicOr(bm + (b >> 5), 1u << (b & 31));
         }
         break;
       }
-      const uint64_t dmask = shift >= 0 ? 0xFFull : 0xFull;
-      const int sh_amt = shift >= 0 ? shift : 0;
+      uint64_t dmask = shift >= 0 ? 0xFFull : 0xFull;
+      int sh_amt = shift >= 0 ? shift : 0;
+      if constexpr (S16) {
+        uint64_t ka = ~0ull, ko = 0;
+        for (uint32_t i = tid; i < nc; i += NT) {
+          const uint64_t x = ld_cand(csrc + i);
+          ka &= x;
+          ko |= x;
+        }
+        block_and_or<NT>(&ka, &ko, sh64);
+        if (ka == ko) break;   // identical keys cannot occur: stop rather than loop
+        const int top = 63 - __clzll(ka ^ ko);
+        sh_amt = top >= 7 ? top - 7 : 0;
+        dmask = 0xFFull;
+      }
       if (tid < 256) h256[tid] = 0;
       if (tid == 0) { s_next = 0; s_dstar = -1; }
       __syncthreads();
@@ -971,7 +1065,6 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
       need -= (int)s_dabove;
       nc = s_next;
       uint64_t* tmp = csrc; csrc = cdst; cdst = tmp;
-      shift -= 8;
       __syncthreads();
     }
   }
@@ -1004,7 +1097,7 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
         const uint32_t b = (uint32_t)((w0 + i) * 32 + bit);
         if (o < (uint32_t)k) {
           irow[o] = (int32_t)b;
-          if (srow_out) srow_out[o] = srow[b];
+          if (srow_out) srow_out[o] = score_load<S16>(srow, b);
         }
         ++o;
       }
@@ -1021,15 +1114,16 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
 
 // Long rows: mark the blocks of one 2048-block chunk above the threshold bin
 // (found by idx_topk_kernel mode 1) and append the ones inside it.
+template <bool S16>
 __global__ __launch_bounds__(256) void idx_select_kernel(IdxWs ws) {
   const int qrow = blockIdx.y, chunk = blockIdx.x;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
-  const float* srow = ws.scores + (int64_t)qrow * ws.R;
+  const void* srow = score_row<S16>(ws, qrow);
   const int64_t b_begin = (int64_t)chunk * kSelCH;
   constexpr int kPer = kSelCH / 256;
   float sc[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) sc[u] = srow[b_begin + 256 * u + threadIdx.x];   // within R
+  for (int u = 0; u < kPer; ++u) sc[u] = score_load<S16>(srow, b_begin + 256 * u + threadIdx.x);   // within R
   const int64_t nv = st[5];
   const int thr = st[2];
   uint32_t* bm = ws.bitmap + (int64_t)qrow * (ws.R / 32);
@@ -1081,6 +1175,7 @@ constexpr int64_t kFusedMaxBlocksPrefill = 65536;
 // the fused-path size: one workgroup per query does everything (bitmap and
 // candidates in LDS).  Longer rows: the threshold per query, a multi-workgroup
 // pass that marks the bitmap, then one workgroup per query refines and emits.
+template <bool S16>
 static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
                         int out_row0, hipStream_t s) {
   const int64_t W = ws.R / 32;
@@ -1089,30 +1184,34 @@ static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, fl
     const int bm_words = (int)W;
     const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
     if (nt == 1024)
-      idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+      idx_topk_kernel<1024, S16><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand,
+                                                       bm_words, 0);
     else
-      idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 0);
+      idx_topk_kernel<256, S16><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand,
+                                                     bm_words, 0);
     return;
   }
   // the threshold pass merges the histogram lists in (dynamic) LDS
-  idx_topk_kernel<1024><<<nq, 1024, kBins * sizeof(uint32_t), s>>>(k, ws, idx, score, out_row0,
-                                                                    0, 0, 1);
-  idx_select_kernel<<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
+  idx_topk_kernel<1024, S16><<<nq, 1024, kBins * sizeof(uint32_t), s>>>(k, ws, idx, score,
+                                                                         out_row0, 0, 0, 1);
+  idx_select_kernel<S16><<<dim3((unsigned)(ws.R / kSelCH), nq), 256, 0, s>>>(ws);
   // the bitmap joins the candidates in LDS when it fits
   const int bm_words = W <= kBmLdsMaxWords ? (int)W : 0;
   const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
   // rows up to 64K blocks: four waves refine and emit (cheaper barriers); longer
   // rows: sixteen (their bitmap takes 8 words per thread per round)
   if (W <= 2048)
-    idx_topk_kernel<256><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
+    idx_topk_kernel<256, S16><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words,
+                                                   2);
   else
-    idx_topk_kernel<1024><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand, bm_words, 2);
+    idx_topk_kernel<1024, S16><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand,
+                                                     bm_words, 2);
 }
 
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* wsp, size_t ws_bytes, hipStream_t s,
-                          const UpdateArgs* upd, int group) {
+                          const UpdateArgs* upd, int group, bool s16) {
   (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
@@ -1121,6 +1220,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
   Paged kc = to_dev(kic);
   Queries Qd = to_dev(q);
   int* fault = fault_word();
+  if (s16 && group > 1) return hipErrorInvalidValue;   // drafts score in fp32
   if (!span && group > 1 && !upd) {
     // a draft: groups of `group` queries of one request share each key pass
     IdxWs ws = carve(wsp, q.n, R, false, true);
@@ -1132,7 +1232,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(256), 0, s, Qd, (const u16*)qI, w, kc, m,
                  n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
+    launch_topk<false>(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
   }
   if (!span) {
@@ -1143,12 +1243,21 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
     const bool f8k = kic.dtype == HSA_FP8_E4M3;
     // eight waves, each streaming one page of every chunk
-    auto scan = cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true> : idx_scan_kernel<4, 8, false>)
-                         : (f8k ? idx_scan_kernel<1, 8, true> : idx_scan_kernel<1, 8, false>);
+    auto scan = s16 ? (cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true, true>
+                                       : idx_scan_kernel<4, 8, false, true>)
+                                : (f8k ? idx_scan_kernel<1, 8, true, true>
+                                       : idx_scan_kernel<1, 8, false, true>))
+                    : (cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true, false>
+                                       : idx_scan_kernel<4, 8, false, false>)
+                                : (f8k ? idx_scan_kernel<1, 8, true, false>
+                                       : idx_scan_kernel<1, 8, false, false>));
     timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(8 * 64), 0, s, Qd, (const u16*)qI, w, kc, m,
                  n_win, k, ws, (int)n_groups, ua, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    launch_topk(1024, q.n, k, ws, idx, score, 0, s);
+    if (s16)
+      launch_topk<true>(1024, q.n, k, ws, idx, score, 0, s);
+    else
+      launch_topk<false>(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
   }
   const int QC = q.n < kSpanQC ? q.n : kSpanQC;
@@ -1163,15 +1272,21 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     if (bsplit < 1) bsplit = 1;
     if (bsplit > 512) bsplit = 512;
     bsplit = (bsplit + 7) / 8 * 8;
+    const bool f8k = kic.dtype == HSA_FP8_E4M3;
     timed_launch(HSA_K_INDEXER_GEMM,
-                 kic.dtype == HSA_FP8_E4M3 ? idx_gemm_kernel<true> : idx_gemm_kernel<false>,
+                 s16 ? (f8k ? idx_gemm_kernel<true, true> : idx_gemm_kernel<false, true>)
+                     : (f8k ? idx_gemm_kernel<true, false> : idx_gemm_kernel<false, false>),
                  dim3(bsplit, (nq + 15) / 16), dim3(256), 0,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    const unsigned slices = (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan);
-    idx_hist_kernel<<<dim3(slices < 1 ? 1 : slices, nq), 256, 0, s>>>(Qd, q0, kc, m, n_win, k,
-                                                                      ws, fault);
-    launch_topk(256, nq, k, ws, idx, score, q0, s);
+    const dim3 hgrid(nv_hi > kHistSpan ? (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan) : 1u, nq);
+    if (s16) {
+      idx_hist_kernel<true><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+      launch_topk<true>(256, nq, k, ws, idx, score, q0, s);
+    } else {
+      idx_hist_kernel<false><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+      launch_topk<false>(256, nq, k, ws, idx, score, q0, s);
+    }
   }
   return hipGetLastError();
 }

@@ -67,6 +67,12 @@ def test_validation_rejects_before_any_launch():
     # empty query set
     q0 = L._Queries(0, None, None, 0, 0, 0)
     assert lib.hsa_indexer_topk(C.byref(q0), f, f, 4, 64, C.byref(ki), 4, 128, 16, f, None, f, 1 << 30, None) == -1
+    # the bf16-score selector checks its arguments the same way
+    bs = lib.hsa_indexer_topk_bf16_scores
+    assert bs(C.byref(q), f, f, 8, 64, C.byref(ki), 4, 128, 16, f, None, f, 1 << 30, None) == -2
+    assert bs(C.byref(q), f, f, 4, 64, C.byref(ki), 4, 128, 16, f, None, f, 16, None) == -3
+    assert bs(C.byref(q0), f, f, 4, 64, C.byref(ki), 4, 128, 16, f, None, f, 1 << 30, None) == -1
+    assert bs(C.byref(q), f, f, 4, 64, C.byref(ki), 4, 128, 0, f, None, f, 1 << 30, None) == -1
     # attention: H not a multiple of 16, d != 128, window capacity too small
     assert lib.hsa_hca_attn(C.byref(q), f, 24, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -2
     assert lib.hsa_hca_attn(C.byref(q), f, 16, 64, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, 0.1, f, 0, None, f, 1 << 30, None) == -2
