@@ -113,9 +113,34 @@ def fp8_values(codes: np.ndarray, scales: np.ndarray, page: int = 64) -> np.ndar
     return v * s[:, None]
 
 
+def store_mixed_pages(c: np.ndarray, page: int = 64):
+    """Compressed K entries stored as the wiki's §8 KV entry: RoPE channels in
+    bf16, the others in fp8.  Reading (the pages give no widths): the last D/2
+    channels are the RoPE channels.  The first D/2 channels are stored as
+    store_fp8_pages stores a cache (one float32 scale per page, amax over those
+    channels only), the last D/2 as bf16.  Returns (rows uint8 [n, D/2 + D]:
+    the codes, then each bf16 channel as its two little-endian bytes; scales
+    float32 [ceil(n/page)])."""
+    n, d = c.shape
+    h = d // 2
+    codes, scales = store_fp8_pages(c[:, :h], page)
+    rope = np.ascontiguousarray(store_bf16(c[:, h:]))
+    return np.concatenate([codes, rope.view(np.uint8).reshape(n, 2 * (d - h))], axis=1), scales
+
+
+def mixed_values(rows: np.ndarray, scales: np.ndarray, page: int = 64) -> np.ndarray:
+    """float64 values of a mixed cache: code value times the page scale for the
+    first D/2 channels, the bf16 value for the RoPE channels."""
+    h = rows.shape[1] // 3
+    lo = fp8_values(rows[:, :h], scales, page)
+    hi = nx.bf16_value(np.ascontiguousarray(rows[:, h:]).view(np.uint16))
+    return np.concatenate([lo, hi], axis=1)
+
+
 class Cache:
-    """One compressed cache as stored: `bits` (bf16 uint16 or fp8 uint8),
-    `scales` (fp8 only) and the float64 `values` the attention reads."""
+    """One compressed cache as stored: `bits` (bf16 uint16, fp8 uint8, or the
+    rows of a mixed cache as uint8), `scales` (fp8 and mixed) and the float64
+    `values` the attention reads."""
 
     def __init__(self, exact: np.ndarray, dtype: str = "bf16", page: int = 64):
         self.dtype = dtype
@@ -126,6 +151,9 @@ class Cache:
         elif dtype == "fp8":
             self.bits, self.scales = store_fp8_pages(exact, page)
             self.values = fp8_values(self.bits, self.scales, page)
+        elif dtype == "mixed":
+            self.bits, self.scales = store_mixed_pages(exact, page)
+            self.values = mixed_values(self.bits, self.scales, page)
         else:
             raise ValueError(dtype)
 
@@ -224,9 +252,11 @@ def hca_query(t, q_bits, k_bits, v_bits, kc: Cache, vc: Cache, m, n_win, scale=N
 # ----------------------------------------------------------------------------- layers
 
 def layer_caches(inp: dict, layer: str, m: int, dtype: str = "bf16", page: int = 64) -> dict:
-    """Compressed caches of one layer from its raw tokens (every complete block)."""
+    """Compressed caches of one layer from its raw tokens (every complete block).
+    dtype "mixed": the K cache holds mixed entries, the V cache fp8."""
+    vdtype = "fp8" if dtype == "mixed" else dtype
     out = {"kc": compress(inp["k"], inp["zk"], m, dtype, page),
-           "vc": compress(inp["v"], inp["zv"], m, dtype, page)}
+           "vc": compress(inp["v"], inp["zv"], m, vdtype, page)}
     if layer == "csa":
         out["kic"] = compress(inp["ki"], inp["zi"], m, "bf16", page)
     return out

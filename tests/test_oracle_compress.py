@@ -115,3 +115,29 @@ def test_fp8_cache_error_bound():
     # subnormal quantum 2^-10 * scale
     err = np.abs(cache.values - c)
     assert np.all(err <= np.abs(c) * 2.0 ** -4 + sc * 2.0 ** -10 + 1e-300)
+
+
+def test_mixed_entry_format():
+    """A mixed K row (the wiki's §8 entry, RoPE channels in bf16): the first 64
+    channels as e4m3 codes with a page scale over those channels only, then the
+    64 RoPE channels as bf16, two little-endian bytes each."""
+    c = np.zeros((3, 128))
+    c[0, 0] = 448 * 2.0 ** -3        # amax of the code channels: scale 2^-3
+    c[1, 5] = -(2.0 ** -3)           # -1 in units of the scale: code 1.0111.000
+    c[2, 64] = 1.0                   # bf16 0x3F80
+    c[2, 65] = 1 + 2.0 ** -8         # a bf16 tie: to the even neighbour, 1.0
+    c[1, 127] = 1e6                  # a RoPE channel: must not set the scale
+    rows, scales = orc.store_mixed_pages(c)
+    assert rows.shape == (3, 192) and rows.dtype == np.uint8
+    assert scales.tolist() == [2.0 ** -3]
+    assert rows[0, 0] == 0x7E        # 448: 0.1111.110, the largest finite e4m3
+    assert rows[1, 5] == 0xB8
+    assert rows[2, 64:68].tolist() == [0x80, 0x3F, 0x80, 0x3F]
+    v = orc.mixed_values(rows, scales)
+    assert v[0, 0] == 56.0 and v[1, 5] == -0.125
+    assert v[2, 64] == 1.0 and v[2, 65] == 1.0
+    assert v[1, 127] == 999424.0     # 1e6 to 8 significant bits
+    assert np.count_nonzero(v) == 5
+    # the same entries in an all-fp8 cache: the RoPE channel's 1e6 sets the scale
+    _, s8 = orc.store_fp8_pages(c)
+    assert s8[0] == np.float32(1e6 / 448)
