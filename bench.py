@@ -49,13 +49,14 @@ def log(*a):
 # ----------------------------------------------------------------------------- decode state
 
 def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False,
-                       draft=1):
+                       draft=1, kmix=False):
     """Caches of B requests holding tokens 0..L-1, rings up to L-1, and the new
     token's inputs (position L).  Returns (layers[copies], step inputs).
     index_fp8: the indexer keys are stored fp8 (e4m3fn, one scale per page), and
     step["kic_bf16"] holds the same keys in bf16 (for the selection recall).
     draft > 1: the step's inputs are [B][draft][...] (tokens L .. L+draft-1) and
-    the rings hold n_win + draft - 1 tokens."""
+    the rings hold n_win + draft - 1 tokens.
+    kmix: the K caches hold mixed entries (RoPE channels bf16, the rest fp8; V fp8)."""
     import torch
     B, m, n_win = w.B, w.m(layer), w.n_win
     z = gen.pool_logits(w, layer)
@@ -64,7 +65,7 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
     n_ent = L // m + 2
     ppr = -(-n_ent // 64)
     perm = torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None
-    kc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
+    kc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm, mixed=kmix)
     vc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
     kic = T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, page_order=perm) if layer == "csa" else None
     kic16 = T.PagedCache.allocate(B, n_ent, 64, page_order=perm) if layer == "csa" and index_fp8 else None
@@ -113,7 +114,7 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
         if c is None:
             return None
         return T.PagedCache(c.data.clone(), c.page_table, c.n_entries.clone(),
-                            None if c.scale is None else c.scale.clone())
+                            None if c.scale is None else c.scale.clone(), c.mixed)
 
     layers = []
     for i in range(copies):
@@ -480,8 +481,9 @@ def bench_pro_decode(args, w):
     from synth import gen
     L = w.L
     f8i = getattr(args, "index_fp8", False)
+    kmix = getattr(args, "kv_mixed", False)
     lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True,
-                                      index_fp8=f8i and layer == "csa")
+                                      index_fp8=f8i and layer == "csa", kmix=kmix)
             for layer in ("csa", "hca")}
     log(f"[bench] {w.name}: state built")
     keep = []
@@ -495,7 +497,9 @@ def bench_pro_decode(args, w):
     # indexer key bytes per visible block: 128 (bf16), or 64 fp8 codes + the page scale
     key_b = 64 + 4 / 64 if f8i else 128
     scan_bytes = int(B * nv * key_b)
-    step_bytes = B * (nv * key_b + w.k_csa * 256 + nvh * 256 + 2 * w.n_win * 512 + 4 * w.H * 256)
+    # K + V bytes per compressed entry: fp8 128 + 128, or a mixed K row of 192
+    kv_b = 320 if kmix else 256
+    step_bytes = B * (nv * key_b + w.k_csa * kv_b + nvh * kv_b + 2 * w.n_win * 512 + 4 * w.H * 256)
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     src = source_hash("indexer.hip", "common.h", "update.h")
     extra = {}
@@ -515,7 +519,9 @@ def bench_pro_decode(args, w):
             "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H, "kv_heads": 1,
                        "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
                        "indexer_keys": "fp8_e4m3+page_scale" if f8i else "bf16",
-                       "layers": "csa+hca", "kv_dtype": "fp8_e4m3+page_scale",
+                       "layers": "csa+hca",
+                       "kv_dtype": ("k: fp8_e4m3 x64 + bf16 rope x64, v: fp8_e4m3+page_scale"
+                                    if kmix else "fp8_e4m3+page_scale"),
                        "cache_copies": args.copies},
             "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -670,6 +676,9 @@ def main():
                     help="pro_decode_1m with fp8 indexer keys (a next row of the scope: the "
                          "scan reads half the bytes); reports the selection recall against "
                          "bf16 keys")
+    ap.add_argument("--kv-mixed", action="store_true",
+                    help="pro_decode_1m: K caches hold mixed entries (the 64 RoPE channels bf16, "
+                         "the other 64 fp8 with a page scale); V stays fp8")
     ap.add_argument("--index-bf16-scores", action="store_true",
                     help="hybrid_prefill_128k: the CSA selector ranks index scores rounded to bf16 "
                          "(hsa_indexer_topk_bf16_scores); also times the selector alone both ways "
@@ -693,6 +702,8 @@ def main():
         ap.error("--draft takes 1..3 with --workload csa_decode_128k")
     if args.index_fp8 and args.workload != "pro_decode_1m":
         ap.error("--index-fp8 applies to --workload pro_decode_1m")
+    if args.kv_mixed and args.workload != "pro_decode_1m":
+        ap.error("--kv-mixed applies to --workload pro_decode_1m")
     if args.index_bf16_scores and args.workload != "hybrid_prefill_128k":
         ap.error("--index-bf16-scores applies to --workload hybrid_prefill_128k")
     if args.gpus != 1:

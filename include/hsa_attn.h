@@ -85,7 +85,12 @@ typedef enum {
   HSA_ERR_DEVICE_FAULT = -5   /* reported by hsa_check_device_error() */
 } hsa_status;
 
-typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2 } hsa_dtype;
+/* HSA_FP8_BF16_ROPE: the wiki's §8 KV entry, RoPE channels in BF16 and the
+ * others in FP8.  A row of dim channels stores channels 0 .. dim/2-1 as
+ * e4m3fn codes (dim/2 bytes, one fp32 scale per page: amax of those channels
+ * over the page / 448) followed by channels dim/2 .. dim-1, the RoPE channels,
+ * as bf16 (dim bytes): 3*dim/2 bytes per row.  Compressed K caches only. */
+typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2, HSA_FP8_BF16_ROPE = 3 } hsa_dtype;
 
 /* Device fault bits reported by hsa_check_device_error(). */
 #define HSA_FAULT_PAGE      1   /* page table entry outside [0, n_pages) */
@@ -107,8 +112,9 @@ typedef struct {
  * indexer keys; classical cache of §11.4).  Entry e of request r is slot
  * (e mod page_size) of physical page page_table[r*pages_per_req + e/page_size]. */
 typedef struct {
-  void*          data;          /* [n_pages][page_size][dim], dtype elements */
-  float*         scale;         /* fp8: [n_pages] fp32 page scales; bf16: NULL */
+  void*          data;          /* [n_pages][page_size] rows of dim dtype elements
+                                   (HSA_FP8_BF16_ROPE: rows of 3*dim/2 bytes) */
+  float*         scale;         /* fp8 codes: [n_pages] fp32 page scales; bf16: NULL */
   const int32_t* page_table;    /* [n_req][pages_per_req] physical page ids */
   int32_t*       n_entries;     /* [n_req] entries held per request */
   int32_t        n_req;
@@ -116,7 +122,8 @@ typedef struct {
   int32_t        n_pages;       /* pages in the pool */
   int32_t        page_size;     /* must be 64 */
   int32_t        dim;
-  int32_t        dtype;         /* hsa_dtype; indexer keys must be bf16 */
+  int32_t        dtype;         /* hsa_dtype: bf16 or fp8 (K, V, indexer keys);
+                                   HSA_FP8_BF16_ROPE (K, with an fp8 V cache) */
 } hsa_paged;
 
 /* The query tokens of a call.  Either a span (req == pos == NULL): n
@@ -141,9 +148,11 @@ hsa_status hsa_pooling_weights(const float* z, int32_t m, int32_t dim, float* al
 
 /* Compress blocks [first_block, first_block + n_blocks) into request `req` of
  * `out`: block b pools tokens b*m .. b*m+m-1 of request `x_req` of x (which
- * must still hold them) with alpha [m][dim] and stores entry b (bf16, or fp8
- * + page scale).  Sets out->n_entries[req] = first_block + n_blocks.  fp8
- * needs first_block % page_size == 0 (a page's scale is set by the call that
+ * must still hold them) with alpha [m][dim] and stores entry b (bf16, fp8
+ * + page scale, or HSA_FP8_BF16_ROPE: fp8 codes of the first dim/2 channels
+ * with a page scale over those channels, bf16 of the rest).  Sets
+ * out->n_entries[req] = first_block + n_blocks.  Formats with page scales
+ * need first_block % page_size == 0 (a page's scale is set by the call that
  * fills it from its first entry).  (Wiki §5.3, §5.4, §8.) */
 hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, int32_t req,
                            int64_t first_block, int64_t n_blocks, int32_t m, const float* alpha,
@@ -183,7 +192,10 @@ hsa_status hsa_indexer_topk_bf16_scores(const hsa_queries* q, const void* qI, co
  * window rows of win_k/win_v and the compressed entries idx[i][0..min(k,n_vis))
  * of kc/vc.  Q bf16 [n][H][d]; O [n][H][d] of o_dtype (HSA_BF16, or HSA_FP32 to
  * keep the fp32 accumulation); lse fp32 [n][H] (natural log of the softmax
- * denominator of the scaled logits) or NULL. */
+ * denominator of the scaled logits) or NULL.  kc and vc: both bf16, both fp8,
+ * or kc HSA_FP8_BF16_ROPE with an fp8 vc (HSA_ERR_UNSUPPORTED otherwise); a
+ * mixed K row scores as (codes . q[0:d/2]) * page scale + bf16 . q[d/2:d],
+ * both products exact in the fp32 accumulation. */
 size_t hsa_csa_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win,
                                     int32_t k);
 hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t d,

@@ -20,7 +20,7 @@ import torch  # load torch's HIP runtime first: the library binds to the same on
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 
-BF16, FP8, FP32 = 0, 1, 2
+BF16, FP8, FP32, FP8_BF16_ROPE = 0, 1, 2, 3
 LAYER_CSA, LAYER_HCA = 0, 1
 FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index"}
 
@@ -153,36 +153,51 @@ class Tokens:
 @dataclass
 class PagedCache:
     """Compressed cache: pages [n_pages, 64, dim] (bf16, or uint8 fp8 codes with
-    `scale` [n_pages]), page_table [n_req, pages_per_req], n_entries [n_req]."""
+    `scale` [n_pages]; mixed: uint8 rows of dim/2 fp8 codes then dim/2 bf16
+    RoPE channels, [n_pages, 64, 3*dim/2] bytes, with `scale`), page_table
+    [n_req, pages_per_req], n_entries [n_req]."""
     data: torch.Tensor
     page_table: torch.Tensor
     n_entries: torch.Tensor
     scale: Optional[torch.Tensor] = None
+    mixed: bool = False
 
     @property
     def dtype(self) -> int:
+        if self.mixed:
+            return FP8_BF16_ROPE
         return FP8 if self.data.dtype == torch.uint8 else BF16
+
+    @property
+    def dim(self) -> int:
+        return self.data.shape[-1] * 2 // 3 if self.mixed else self.data.shape[-1]
 
     @staticmethod
     def allocate(n_req: int, max_entries: int, dim: int, fp8: bool = False,
-                 page_order: Optional[torch.Tensor] = None, device="cuda") -> "PagedCache":
+                 page_order: Optional[torch.Tensor] = None, device="cuda",
+                 mixed: bool = False) -> "PagedCache":
+        """mixed: HSA_FP8_BF16_ROPE rows (compressed K caches)."""
         ppr = max(1, -(-max_entries // 64))
         n_pages = n_req * ppr
-        dt = torch.uint8 if fp8 else torch.bfloat16
-        data = torch.zeros((n_pages, 64, dim), dtype=dt, device=device)
+        if mixed:
+            data = torch.zeros((n_pages, 64, dim // 2 * 3), dtype=torch.uint8, device=device)
+        else:
+            dt = torch.uint8 if fp8 else torch.bfloat16
+            data = torch.zeros((n_pages, 64, dim), dtype=dt, device=device)
         if page_order is None:
             page_order = torch.arange(n_pages, dtype=torch.int32)
         table = page_order.to(torch.int32).reshape(n_req, ppr).to(device)
-        scale = torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 else None
+        scale = (torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 or mixed
+                 else None)
         return PagedCache(data, table.contiguous(),
-                          torch.zeros(n_req, dtype=torch.int32, device=device), scale)
+                          torch.zeros(n_req, dtype=torch.int32, device=device), scale, mixed)
 
     def c(self) -> _Paged:
-        n_pages, ps, dim = self.data.shape
+        n_pages, ps, _ = self.data.shape
         n_req, ppr = self.page_table.shape
         return _Paged(self.data.data_ptr(), None if self.scale is None else self.scale.data_ptr(),
                       self.page_table.data_ptr(), self.n_entries.data_ptr(), n_req, ppr, n_pages,
-                      ps, dim, self.dtype)
+                      ps, self.dim, self.dtype)
 
     def logical(self, r: int, n: Optional[int] = None) -> torch.Tensor:
         """Entries 0..n-1 of request r in logical order (a gather, for inspection)."""

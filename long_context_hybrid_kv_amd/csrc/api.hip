@@ -86,16 +86,21 @@ static int64_t nvis_host(int64_t t, int m, int n_win) {
   return a < b ? a : b;
 }
 
-static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, bool allow_fp8) {
+// allow_mixed: the cache may be HSA_FP8_BF16_ROPE (compressed K, dim 128)
+static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, bool allow_fp8,
+                              bool allow_mixed = false) {
   std::string n(name);
   REQ(p, n + ": null descriptor");
   REQ(p->data && p->page_table && p->n_entries, n + ": null data, page_table or n_entries");
   REQ(p->n_req >= 1 && p->pages_per_req >= 1 && p->n_pages >= 1, n + ": empty cache");
   SUP(p->page_size == kPage, n + ": page_size must be 64");
   SUP(p->dim == dim, n + ": unsupported dim");
-  REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3, n + ": unknown dtype");
+  REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3 || p->dtype == HSA_FP8_BF16_ROPE,
+      n + ": unknown dtype");
   SUP(allow_fp8 || p->dtype == HSA_BF16, n + ": must be bf16");
-  REQ(p->dtype != HSA_FP8_E4M3 || p->scale, n + ": fp8 cache needs page scales");
+  SUP(p->dtype != HSA_FP8_BF16_ROPE || (allow_mixed && p->dim == kD),
+      n + ": the mixed bf16-RoPE / fp8 format is for compressed K caches of dim 128");
+  REQ(p->dtype == HSA_BF16 || p->scale, n + ": fp8 cache needs page scales");
   SUP(p->n_pages < (1 << 25), n + ": pool rows must be addressable by a 32-bit row id");
   return HSA_OK;
 }
@@ -144,11 +149,12 @@ static hsa_status check_attn_common(const hsa_queries* q, const void* Q, int H, 
   REQ(kc && vc, "attention: null cache");
   REQ(scale > 0.f && scale < INFINITY, "attention: scale must be positive and finite");
   hsa_status s;
-  if ((s = check_paged(kc, "kc", kD, true)) != HSA_OK) return s;
+  if ((s = check_paged(kc, "kc", kD, true, true)) != HSA_OK) return s;
   if ((s = check_paged(vc, "vc", kD, true)) != HSA_OK) return s;
   if ((s = check_queries(q, kc->n_req)) != HSA_OK) return s;
   REQ(kc->n_req == vc->n_req, "attention: kc and vc differ in n_req");
-  SUP(kc->dtype == vc->dtype, "attention: kc and vc must have the same dtype");
+  SUP(kc->dtype == vc->dtype || (kc->dtype == HSA_FP8_BF16_ROPE && vc->dtype == HSA_FP8_E4M3),
+      "attention: kc and vc must both be bf16 or both fp8 (or a mixed kc with an fp8 vc)");
   REQ(Q && O, "attention: null Q or O");
   SUP(d == kD, "attention: d must be 128");
   SUP(H >= 16 && H <= 128 && H % 16 == 0, "attention: H must be a multiple of 16 in [16, 128]");
@@ -243,7 +249,7 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
   REQ(out, "kv_compress: null output");
   SUP(out->dim == kD || out->dim == kDI, "kv_compress: dim must be 128 or 64");
   hsa_status s;
-  if ((s = check_paged(out, "out", out->dim, true)) != HSA_OK) return s;
+  if ((s = check_paged(out, "out", out->dim, true, true)) != HSA_OK) return s;
   if ((s = check_tokens(x, "x", out->dim, 1)) != HSA_OK) return s;
   REQ(alpha, "kv_compress: null alpha");
   REQ(m >= 1 && m <= 4096, "kv_compress: bad m");
@@ -253,7 +259,7 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
   REQ(first_block >= 0 && n_blocks >= 0, "kv_compress: negative range");
   REQ(first_block + n_blocks <= (int64_t)out->pages_per_req * kPage,
       "kv_compress: range exceeds the request's pages");
-  REQ(out->dtype != HSA_FP8_E4M3 || first_block % kPage == 0,
+  REQ(out->dtype == HSA_BF16 || first_block % kPage == 0,
       "kv_compress: fp8 ranges must start on a page boundary");
   return hip_status(launch_compress(*x, x_req, *out, req, first_block, n_blocks, m, alpha, stream),
                     "kv_compress");

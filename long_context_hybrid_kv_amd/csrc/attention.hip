@@ -167,6 +167,26 @@ __device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, in
   return pool ? pv : (win ? wv : z);
 }
 
+// Column group cg of a K row of an HSA_FP8_BF16_ROPE cache (the window rows
+// are bf16): groups 0-7 are fp8 codes (8 bytes, in .x/.y), groups 8-15 the bf16
+// RoPE channels.  One 16-byte load per piece, branch-free like load_piece: a
+// code group reads the 16 bytes that hold it and its neighbour and keeps its
+// half.
+__device__ __forceinline__ uint4 load_piece_kmix(const Paged& c, const Tokens& tk, int row,
+                                                 int cg) {
+  const bool pool = row >= 0, win = row <= -2;
+  const int64_t pr = pool ? row : 0;
+  const int64_t wr = win ? (int64_t)(-2 - row) : 0;
+  const uint4 wv = *(const uint4*)((const u16*)tk.data + wr * kD + cg * 8);
+  const uint8_t* base = c.data + pr * (kD / 2 * 3);
+  const bool code = cg < 8;
+  const uint4 v = *(const uint4*)(base + (code ? (cg >> 1) * 16 : kD / 2 + (cg - 8) * 16));
+  const uint4 cv = (cg & 1) ? make_uint4(v.z, v.w, 0, 0) : make_uint4(v.x, v.y, 0, 0);
+  const uint4 pv = code ? cv : v;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  return pool ? pv : (win ? wv : z);
+}
+
 template <bool F8>
 __device__ __forceinline__ float row_scale(const Paged& c, int row) {
   if (!F8) return 1.f;
@@ -242,7 +262,8 @@ __device__ __forceinline__ uint4 v_piece_f16(uint4 raw, bool fp8, float scale) {
                     pack_f16(f[6], f[7]));
 }
 
-template <int NW, bool F8, bool SH>
+// KMIX (with F8): the K cache is HSA_FP8_BF16_ROPE, the V cache fp8
+template <int NW, bool F8, bool SH, bool KMIX>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PPT = 1024 / NT;          // K (and V) pieces per thread per chunk
@@ -366,7 +387,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int ek = p >> 4, cgk = p & 15;
       if constexpr (F8) {
         krow[i] = rowk[lo + ek];
-        kraw[i] = load_piece<F8>(a.kc, a.wk, krow[i], cgk);
+        kraw[i] = KMIX ? load_piece_kmix(a.kc, a.wk, krow[i], cgk)
+                       : load_piece<F8>(a.kc, a.wk, krow[i], cgk);
         kscl[i] = row_scale<F8>(a.kc, krow[i]);
       } else {
         krow[i] = 0;
@@ -429,7 +451,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
-      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0);
+      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0 && (!KMIX || cgk < 8));
       if constexpr (F8)   // page scale of each key row (bf16 rows need none)
         if (cgk == 0) ksc[ek] = kscl[i];
     }
@@ -441,15 +463,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       if constexpr (!SH) issue_v(c + 1);
     }
 
-    // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads)
-    f32x4 sacc[4];
+    // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads).  KMIX:
+    // the code channels (k-steps 0, 1) and the bf16 RoPE channels (2, 3)
+    // accumulate apart, as only the codes take the page scale.
+    f32x4 sacc[4], shi[KMIX ? 4 : 1];
 #pragma unroll
     for (int et = 0; et < 4; ++et) {
       sacc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KMIX) shi[et] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
-        sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], sacc[et], 0, 0, 0);
+        if (KMIX && ks >= 2)
+          shi[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], shi[et], 0, 0, 0);
+        else
+          sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], sacc[et], 0, 0, 0);
       }
     }
     // ---- online softmax (lane = head `col`; rows 4g+i of each entry tile).
@@ -460,7 +488,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int et = 0; et < 4; ++et)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[et][i] *= a.scale_log2 * ksc[et * 16 + 4 * g + i];
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (KMIX)
+            sacc[et][i] = (sacc[et][i] * ksc[et * 16 + 4 * g + i] + shi[et][i]) * a.scale_log2;
+          else
+            sacc[et][i] *= a.scale_log2 * ksc[et * 16 + 4 * g + i];
+        }
     }
     if (__builtin_expect(e0 + 64 > E, 0)) {   // the last chunk only (E is uniform)
 #pragma unroll
@@ -966,7 +999,8 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   int64_t n_blocks = (int64_t)q.n * p.n_hg * p.n_splits;
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
-  const bool f8 = kc.dtype == HSA_FP8_E4M3;
+  const bool f8 = kc.dtype != HSA_BF16;   // fp8, or a mixed K with an fp8 V
+  const bool kmix = kc.dtype == HSA_FP8_BF16_ROPE;
   // prefill of an HCA layer: pairs of consecutive queries share one walk over
   // their entries (the union of two windows needs n_win + 1 raw tokens)
   const int64_t need_cap = q.max_pos + 1 < n_win + 1 ? q.max_pos + 1 : n_win + 1;
@@ -989,16 +1023,22 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   // prefill (many workgroups per CU help): one LDS buffer for the K and V^T
   // tiles; decode (few workgroups, latency first): two
   if (p.nw == 4 && span && !f8)
-    timed_launch(HSA_K_ATTN, attn_kernel<4, false, true>, grid, dim3(256), pre, s, a);
+    timed_launch(HSA_K_ATTN, attn_kernel<4, false, true, false>, grid, dim3(256), pre, s, a);
   else if (p.nw == 4)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<4, true, false> : attn_kernel<4, false, false>, grid,
-                 dim3(256), pre, s, a);
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<4, true, false, true>
+                      : f8 ? attn_kernel<4, true, false, false> : attn_kernel<4, false, false, false>,
+                 grid, dim3(256), pre, s, a);
   else if (p.nw == 2)
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<2, true, false> : attn_kernel<2, false, false>, grid,
-                 dim3(128), pre, s, a);
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<2, true, false, true>
+                      : f8 ? attn_kernel<2, true, false, false> : attn_kernel<2, false, false, false>,
+                 grid, dim3(128), pre, s, a);
   else
-    timed_launch(HSA_K_ATTN, f8 ? attn_kernel<1, true, false> : attn_kernel<1, false, false>, grid,
-                 dim3(64), pre, s, a);
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<1, true, false, true>
+                      : f8 ? attn_kernel<1, true, false, false> : attn_kernel<1, false, false, false>,
+                 grid, dim3(64), pre, s, a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
                                                             O, a.o_f32, lse);

@@ -118,7 +118,11 @@ struct Paged {
   const int32_t* page_table;
   int32_t* n_entries;
   int32_t pages_per_req, n_pages, dim, dtype;
-  __device__ __forceinline__ int elem_bytes() const { return dtype == HSA_FP8_E4M3 ? 1 : 2; }
+  // bytes of one entry's row: dim elements, or (HSA_FP8_BF16_ROPE) dim/2 fp8
+  // codes followed by dim/2 bf16 channels
+  __device__ __forceinline__ int row_bytes() const {
+    return dtype == HSA_FP8_E4M3 ? dim : dtype == HSA_FP8_BF16_ROPE ? dim / 2 * 3 : dim * 2;
+  }
   // physical page of entry e of request r, or -1 (and a fault) if out of range
   __device__ __forceinline__ int page_of(int r, int64_t e, int* fault) const {
     int p = page_table[(int64_t)r * pages_per_req + (e >> 6)];
@@ -129,7 +133,7 @@ struct Paged {
     return p;
   }
   __device__ __forceinline__ uint8_t* row(int page, int64_t e) const {
-    return data + ((int64_t)page * kPage + (e & 63)) * dim * elem_bytes();
+    return data + ((int64_t)page * kPage + (e & 63)) * row_bytes();
   }
 };
 

@@ -31,7 +31,10 @@ hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, 
 // One workgroup per cache page touched by [first, first + n).  Each thread owns
 // the (entry, channel) items idx = tid, tid + 256, ... of the page; consecutive
 // threads read consecutive channels of a token row (coalesced).
-template <bool FP8, int MAXV>
+// FMT: HSA_BF16, HSA_FP8_E4M3 (every channel fp8, page scale over all of
+// them) or HSA_FP8_BF16_ROPE (channels below dim/2 fp8 with a page scale over
+// those channels, the RoPE channels above them bf16)
+template <int FMT, int MAXV>
 __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int req, int64_t first,
                                                        int64_t n, int m,
                                                        const float* __restrict__ alpha,
@@ -61,9 +64,9 @@ __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int 
       acc += (double)alpha[(int64_t)j * dim + c] * (double)bf16_to_f32(row[c]);
     }
     vals[v] = acc;
-    amax = fmax(amax, fabs(acc));
+    if (FMT != HSA_FP8_BF16_ROPE || c < dim / 2) amax = fmax(amax, fabs(acc));
   }
-  if (!FP8) {
+  if (FMT == HSA_BF16) {
 #pragma unroll
     for (int v = 0; v < MAXV; ++v) {
       int it = threadIdx.x + v * 256;
@@ -88,7 +91,12 @@ __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int 
     if (it >= items) continue;
     int64_t e = page_e0 + it / dim;
     if (e < e_lo || e >= e_hi) continue;
-    out.row(page, e)[it % dim] = f64_to_e4m3(vals[v] / (double)sc);
+    const int c = it % dim;
+    uint8_t* row = out.row(page, e);
+    if (FMT == HSA_FP8_BF16_ROPE && c >= dim / 2)
+      ((u16*)(row + dim / 2))[c - dim / 2] = f64_to_bf16(vals[v]);   // RoPE channel
+    else
+      row[c] = f64_to_e4m3(vals[v] / (double)sc);
   }
 }
 
@@ -144,16 +152,20 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
   Paged o = to_dev(out);
   Tokens t = to_dev(x);
   KernelTimer kt(HSA_K_COMPRESS, s);
-  if (out.dtype == HSA_FP8_E4M3) {
+  const unsigned g = (unsigned)pages;
+  int* f = fault_word();
+  if (out.dtype == HSA_FP8_BF16_ROPE) {   // K caches: dim = kD
+    compress_kernel<HSA_FP8_BF16_ROPE, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+  } else if (out.dtype == HSA_FP8_E4M3) {
     if (out.dim == kD)
-      compress_kernel<true, 32><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+      compress_kernel<HSA_FP8_E4M3, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
     else
-      compress_kernel<true, 16><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+      compress_kernel<HSA_FP8_E4M3, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   } else {
     if (out.dim == kD)
-      compress_kernel<false, 32><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+      compress_kernel<HSA_BF16, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
     else
-      compress_kernel<false, 16><<<(unsigned)pages, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, fault_word());
+      compress_kernel<HSA_BF16, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   }
   return hipGetLastError();
 }

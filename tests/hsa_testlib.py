@@ -41,19 +41,20 @@ def tokens(rows: np.ndarray, device="cuda") -> L.Tokens:
 
 
 def compress_layer(inp: dict, layer: str, m: int, fp8: bool = False, page_order=None,
-                   device="cuda"):
-    """GPU caches of one prefill layer (request 0) via hsa_kv_compress."""
+                   device="cuda", kmix: bool = False):
+    """GPU caches of one prefill layer (request 0) via hsa_kv_compress.
+    kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8."""
     T = inp["k"].shape[0]
     nb = T // m
     out = {}
-    names = [("kc", "k", "zk", fp8), ("vc", "v", "zv", fp8)]
+    names = [("kc", "k", "zk", fp8 or kmix), ("vc", "v", "zv", fp8 or kmix)]
     if layer == "csa":
         names.append(("kic", "ki", "zi", False))
     for cname, x, z, f8 in names:
         dim = inp[x].shape[1]
         alpha = L.pooling_weights(torch.from_numpy(inp[z]).to(device))
         cache = L.PagedCache.allocate(1, max(nb, 1), dim, fp8=f8, page_order=page_order,
-                                      device=device)
+                                      device=device, mixed=kmix and cname == "kc")
         L.kv_compress(tokens(inp[x], device), cache, 0, 0, nb, m, alpha)
         out[cname] = cache
         out["alpha_" + x] = alpha
@@ -61,8 +62,9 @@ def compress_layer(inp: dict, layer: str, m: int, fp8: bool = False, page_order=
 
 
 def cache_bits(cache: L.PagedCache, r: int, n: int) -> np.ndarray:
+    """Stored rows: bf16 bit patterns (uint16), or bytes (fp8 codes; mixed rows)."""
     t = cache.logical(r, n).cpu()
-    if cache.dtype == L.FP8:
+    if t.dtype == torch.uint8:
         return t.numpy()
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -101,11 +103,13 @@ def scale_of(d=128):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False):
+def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False,
+                kmix=False):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
     hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1).
-    index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page)."""
+    index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page).
+    kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8."""
     B = len(Ls)
     m = w.m(layer)
     n_win = w.n_win
@@ -115,12 +119,12 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     max_entries = int(max(Ls)) // m + steps // m + 2
     ppr = -(-max_entries // 64)
     perm = (torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None)
-    def cache(dim, f8):
-        return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm)
+    def cache(dim, f8, mixed=False):
+        return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm, mixed=mixed)
     st = {"reqs": reqs, "z": z, "m": m}
     st["alpha_k"] = L.pooling_weights(torch.from_numpy(z["zk"]).cuda())
     st["alpha_v"] = L.pooling_weights(torch.from_numpy(z["zv"]).cuda())
-    st["kc"], st["vc"] = cache(128, fp8), cache(128, fp8)
+    st["kc"], st["vc"] = cache(128, fp8 or kmix, kmix), cache(128, fp8 or kmix)
     cap = n_win if ring_cap is None else ring_cap
     ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)

@@ -35,7 +35,7 @@ def test_status_strings():
 
 
 def _paged(dim=128, dtype=0, ppr=4, fake=0x1000):
-    return L._Paged(fake, fake if dtype == 1 else None, fake, fake, 1, ppr, ppr, 64, dim, dtype)
+    return L._Paged(fake, fake if dtype in (1, 3) else None, fake, fake, 1, ppr, ppr, 64, dim, dtype)
 
 
 def _tokens(cap=4096, dim=128, fake=0x1000):
@@ -87,6 +87,16 @@ def test_validation_rejects_before_any_launch():
     for bad in (0.0, -0.1, float("inf"), float("nan")):
         assert lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 128, bad, f, 0, None, f, 1 << 30, None) == -1
     assert b"scale" in lib.hsa_last_error()
+    # the mixed bf16-RoPE / fp8 entry: K caches of dim 128 with an fp8 V cache only
+    km, k8 = _paged(dtype=L.FP8_BF16_ROPE), _paged(dtype=L.FP8)
+    hca = lambda kc, vc: lib.hsa_hca_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(kc), C.byref(vc), 128, 0.1, f, 0, None, f, 1 << 30, None)
+    assert hca(km, pc) == -2                      # with a bf16 V
+    assert hca(km, km) == -2                      # as the V cache
+    assert hca(pc, k8) == -2                      # bf16 K with fp8 V
+    assert lib.hsa_indexer_topk(C.byref(q), f, f, 4, 64, C.byref(_paged(dim=64, dtype=L.FP8_BF16_ROPE)), 4, 128, 16, f, None, f, 1 << 30, None) == -2
+    assert lib.hsa_kv_compress(C.byref(_tokens(dim=64)), 0, C.byref(_paged(dim=64, dtype=L.FP8_BF16_ROPE)), 0, 0, 1, 4, f, None) == -2
+    assert lib.hsa_kv_compress(C.byref(tk), 0, C.byref(km), 0, 3, 10, 4, f, None) == -1   # not page-aligned
+    assert lib.hsa_kv_compress(C.byref(tk), 0, C.byref(L._Paged(0x1000, None, 0x1000, 0x1000, 1, 4, 4, 64, 128, L.FP8_BF16_ROPE)), 0, 0, 1, 4, f, None) == -1   # no scales
     # CSA without idx
     assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, 0, None, f, 1 << 30, None) == -1
 

@@ -7,7 +7,9 @@ configuration the benchmark times them in:
 * draft verification: CSA decode, batch 32 x 131072 tokens, 64 heads, top-512,
   three draft tokens per request through hsa_decode_draft (one indexer pass
   per request scores the three queries): every query of every request, and the
-  caches after the draft bit-exact.
+  caches after the draft bit-exact;
+* the mixed KV entry: the 1M Pro decode with K caches holding the 64 RoPE
+  channels bf16 and the other 64 fp8, V fp8: every request, caches bit-exact.
 """
 import numpy as np
 import pytest
@@ -108,3 +110,32 @@ def test_csa_decode_128k_draft3_full():
             worst = max(worst, _check_csa(w, d, t, i, kc, vc, kic, idx[r, i], Ob[r, i],
                                           lse[r, i], f"req {r} t {t}"))
     print(f"csa_decode_128k draft of {n_tok}: max abs error {worst:.3e}")
+
+
+@pytest.mark.parametrize("layer", ["csa", "hca"])
+def test_pro_decode_1m_kv_mixed_full(layer):
+    """The 1M Pro decode with mixed K entries (the 64 RoPE channels bf16, the
+    other 64 fp8 with a page scale) and fp8 V: every request, caches bit-exact."""
+    w = configs.PRO_DECODE_1M
+    Ls = [w.L] * w.B
+    st = T.build_state(w, layer, Ls, shuffle=False, kmix=True)
+    out = T.run_ops(w, layer, st, Ls)
+    z = gen.pool_logits(w, layer)
+    m = w.m(layer)
+    worst = 0.0
+    for r, d in enumerate(st["reqs"]):
+        kc = orc.compress(d["k"][:w.L], z["zk"], m, "mixed")
+        vc = orc.compress(d["v"][:w.L], z["zv"], m, "fp8")
+        for name, ref in (("kc", kc), ("vc", vc)):
+            _check_cache(st[name], r, ref, name)
+        if layer == "csa":
+            kic = orc.compress(d["ki"][:w.L], z["zi"], m)
+            worst = max(worst, _check_csa(w, d, w.L, 0, kc, vc, kic, out["idx"][r], out["O"][r],
+                                          out["lse"][r], f"req {r}"))
+        else:
+            ref = orc.hca_query(w.L, d["q"][0], d["k"], d["v"], kc, vc, m, w.n_win)
+            err = float(np.max(np.abs(out["O"][r] - ref["o"])))
+            assert err <= T.OUT_TOL, f"req {r}: {err}"
+            assert np.max(np.abs(out["lse"][r] - ref["lse"])) <= T.LSE_TOL, f"req {r} lse"
+            worst = max(worst, err)
+    print(f"pro_decode_1m mixed K {layer}: max abs error {worst:.3e}")

@@ -57,9 +57,9 @@ def test_compress_fp8_bitexact():
     L.check_device_error()
 
 
-def _run_prefill_csa(w, inp, rows=None, page_order=None, out_fp32=True):
+def _run_prefill_csa(w, inp, rows=None, page_order=None, out_fp32=True, kmix=False):
     m, n_win, k, T_ = w.m_csa, w.n_win, w.k_csa, inp["k"].shape[0]
-    gc = T.compress_layer(inp, "csa", m, page_order=page_order)
+    gc = T.compress_layer(inp, "csa", m, page_order=page_order, kmix=kmix)
     q = L.Queries.span(T_)
     qi = T.dev_bf16(inp["qi"])
     wt = torch.from_numpy(inp["w"]).cuda()
@@ -72,9 +72,9 @@ def _run_prefill_csa(w, inp, rows=None, page_order=None, out_fp32=True):
     return idx.cpu().numpy(), score.cpu().numpy(), O, lse.cpu().numpy()
 
 
-def _check_csa_rows(w, inp, idx, score, O, lse, rows):
+def _check_csa_rows(w, inp, idx, score, O, lse, rows, dtype="bf16"):
     m, n_win, k = w.m_csa, w.n_win, w.k_csa
-    oc = _oracle_caches(inp, "csa", m)
+    oc = orc.layer_caches(inp, "csa", m, dtype)
     Ob = T.to_f64(O)
     n_diff = 0
     for t in rows:
