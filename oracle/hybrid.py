@@ -137,6 +137,35 @@ def mixed_values(rows: np.ndarray, scales: np.ndarray, page: int = 64) -> np.nda
     return np.concatenate([lo, hi], axis=1)
 
 
+def store_fp4_mx(c: np.ndarray, block: int = 32):
+    """Compressed indexer keys in fp4 (the wiki's §8 names an FP4 indexer and no
+    format).  Reading: OCP MX (Microscaling) FP4 -- e2m1 elements in blocks of
+    `block` consecutive channels of one key, each block sharing a power-of-two
+    scale 2^x stored as the e8m0 byte x + 127, with x = floor(log2(amax of the
+    block)) - 2 (2: the largest e2m1 exponent) and element = e2m1(value / 2^x),
+    clamped to +-6; a block of zeros stores x = 0.  Returns (codes uint8
+    [n, D/2], channel 2j in the low nibble of byte j; scale bytes uint8
+    [n, D/block])."""
+    n, d = c.shape
+    blk = c.reshape(n, d // block, block)
+    amax = np.abs(blk).max(axis=2)
+    _, E = np.frexp(amax)                   # amax = f * 2^E, f in [0.5, 1)
+    x = np.clip(np.where(amax > 0, E - 1 - 2, 0), -127, 127)
+    codes = nx.e2m1_encode(blk / np.ldexp(1.0, x)[:, :, None]).reshape(n, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (x + 127).astype(np.uint8)
+
+
+def fp4_values(packed: np.ndarray, scale_bytes: np.ndarray, block: int = 32) -> np.ndarray:
+    """float64 values of fp4 keys: element value times 2^(scale byte - 127)."""
+    n = packed.shape[0]
+    codes = np.empty((n, 2 * packed.shape[1]), dtype=np.uint8)
+    codes[:, 0::2] = packed & 15
+    codes[:, 1::2] = packed >> 4
+    x = scale_bytes.astype(np.int64) - 127
+    return (nx.e2m1_decode(codes).reshape(n, -1, block) * np.ldexp(1.0, x)[:, :, None]).reshape(n, -1)
+
+
 class Cache:
     """One compressed cache as stored: `bits` (bf16 uint16, fp8 uint8, or the
     rows of a mixed cache as uint8), `scales` (fp8 and mixed) and the float64
@@ -151,6 +180,9 @@ class Cache:
         elif dtype == "fp8":
             self.bits, self.scales = store_fp8_pages(exact, page)
             self.values = fp8_values(self.bits, self.scales, page)
+        elif dtype == "fp4":
+            self.bits, self.scales = store_fp4_mx(exact)
+            self.values = fp4_values(self.bits, self.scales)
         elif dtype == "mixed":
             self.bits, self.scales = store_mixed_pages(exact, page)
             self.values = mixed_values(self.bits, self.scales, page)

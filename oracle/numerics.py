@@ -13,6 +13,8 @@ formats' definitions:
   e4m3fn  1 sign, 4 exponent (bias 7), 3 fraction bits; no infinities; the
           only NaN is S.1111.111; largest finite 448; smallest normal 2^-6,
           subnormal quantum 2^-9.
+  e2m1    (OCP MX FP4) 1 sign, 2 exponent (bias 1), 1 fraction bit; no
+          infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 """
 from __future__ import annotations
 
@@ -80,3 +82,28 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
     mag = np.where(ef == 0, mf * 2.0 ** -9, (1.0 + mf / 8.0) * np.ldexp(1.0, ef - 7))
     mag = np.where((ef == 15) & (mf == 7), np.nan, mag)
     return s * mag
+
+
+E2M1_MAX = 6.0
+
+
+def e2m1_encode(x: np.ndarray) -> np.ndarray:
+    """float64 -> e2m1 codes (uint8 in 0..15): clamp to +-6, then round to
+    nearest even (quantum 0.5 below 2, 1 in [2, 4), 2 in [4, 6]).  The sign
+    bit is the sign bit of x."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x)
+    a = np.abs(np.clip(x, -E2M1_MAX, E2M1_MAX))
+    v = _round_to_quantum(a, 0, 1)                  # a representable e2m1 magnitude
+    # magnitude -> 3-bit code: 0, 0.5, 1, 1.5 -> 2v; 2, 3 -> v + 2; 4, 6 -> 4 + v / 2
+    mag = np.where(v < 2, 2 * v, np.where(v < 4, v + 2, 4 + v / 2)).astype(np.int64)
+    return (mag | (sign.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def e2m1_decode(code: np.ndarray) -> np.ndarray:
+    """e2m1 codes -> float64."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    return s * np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))

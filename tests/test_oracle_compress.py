@@ -141,3 +141,21 @@ def test_mixed_entry_format():
     # the same entries in an all-fp8 cache: the RoPE channel's 1e6 sets the scale
     _, s8 = orc.store_fp8_pages(c)
     assert s8[0] == np.float32(1e6 / 448)
+
+
+def test_fp4_mx_key_format():
+    """fp4 indexer keys (OCP MX FP4, 32-channel blocks): the block scale is
+    2^(floor(log2 amax) - 2), elements round to nearest even on the e2m1 grid
+    and clamp to 6, channel 2j sits in the low nibble of byte j."""
+    c = np.zeros((3, 64))
+    c[0, 0], c[0, 1] = 5.0, -1.25    # block amax 5: x = 0; 5 -> 4 (tie), -1.25 -> -1 (tie)
+    c[0, 32] = 7.5                   # block amax 7.5: x = 0; 7.5 clamps to 6
+    c[1, 40] = 0.3                   # amax 0.3: x = -4; 0.3 * 16 = 4.8 -> 4 -> 0.25
+    codes, sb = orc.store_fp4_mx(c)  # row 2: all zero -> x = 0 in both blocks
+    assert codes.shape == (3, 32) and sb.shape == (3, 2)
+    assert sb.tolist() == [[127, 127], [127, 123], [127, 127]]
+    assert codes[0, 0] == (0x6 | (0xA << 4))          # channel 0: +4 (0110); channel 1: -1 (1010)
+    assert codes[0, 16] == 0x7 and codes[1, 20] == 0x6 and np.count_nonzero(codes) == 3
+    v = orc.fp4_values(codes, sb)
+    assert v[0, 0] == 4.0 and v[0, 1] == -1.0 and v[0, 32] == 6.0 and v[1, 40] == 0.25
+    assert np.count_nonzero(v) == 4

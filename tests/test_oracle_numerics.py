@@ -78,3 +78,17 @@ def test_e4m3_saturates_and_ties():
     assert nx.e4m3_decode(nx.e4m3_encode(np.array([2.0 ** -10])))[0] == 0.0
     assert nx.e4m3_decode(nx.e4m3_encode(np.array([2.0 ** -10 * 1.001])))[0] == 2.0 ** -9
     assert nx.e4m3_encode(np.array([-1e-9]))[0] == 0x80
+
+
+def test_e2m1_grid_ties_and_clamp():
+    """Every e2m1 code decodes to the OCP MX FP4 grid and encodes back; the
+    midpoints between neighbours go to the even code; magnitudes clamp to 6."""
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    codes = np.arange(16, dtype=np.uint8)
+    vals = nx.e2m1_decode(codes)
+    assert vals[:8].tolist() == grid and (-vals[8:]).tolist() == grid
+    assert np.array_equal(nx.e2m1_encode(vals[1:8]), codes[1:8])
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    assert nx.e2m1_decode(nx.e2m1_encode(np.array(mids))).tolist() == [0, 1, 1, 2, 2, 4, 4]
+    assert nx.e2m1_decode(nx.e2m1_encode(np.array([7.0, -100.0, 5.99, 0.26]))).tolist() == \
+        [6, -6, 6, 0.5]
