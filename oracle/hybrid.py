@@ -163,7 +163,9 @@ def fp4_values(packed: np.ndarray, scale_bytes: np.ndarray, block: int = 32) -> 
     codes[:, 0::2] = packed & 15
     codes[:, 1::2] = packed >> 4
     x = scale_bytes.astype(np.int64) - 127
-    return (nx.e2m1_decode(codes).reshape(n, -1, block) * np.ldexp(1.0, x)[:, :, None]).reshape(n, -1)
+    d = codes.shape[1]
+    return (nx.e2m1_decode(codes).reshape(n, d // block, block) *
+            np.ldexp(1.0, x)[:, :, None]).reshape(n, d)
 
 
 class Cache:

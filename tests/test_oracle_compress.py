@@ -159,3 +159,9 @@ def test_fp4_mx_key_format():
     v = orc.fp4_values(codes, sb)
     assert v[0, 0] == 4.0 and v[0, 1] == -1.0 and v[0, 32] == 6.0 and v[1, 40] == 0.25
     assert np.count_nonzero(v) == 4
+
+
+def test_fp4_mx_empty_cache():
+    """A request with no complete block stores an empty fp4 cache."""
+    c = orc.compress(np.zeros((3, 64), dtype=np.uint16), np.zeros((4, 64), dtype=np.float32), 4, "fp4")
+    assert len(c) == 0 and c.bits.shape == (0, 32) and c.scales.shape == (0, 2)
