@@ -49,14 +49,16 @@ def log(*a):
 # ----------------------------------------------------------------------------- decode state
 
 def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False,
-                       draft=1, kmix=False):
+                       draft=1, kmix=False, index_fp4=False):
     """Caches of B requests holding tokens 0..L-1, rings up to L-1, and the new
     token's inputs (position L).  Returns (layers[copies], step inputs).
     index_fp8: the indexer keys are stored fp8 (e4m3fn, one scale per page), and
     step["kic_bf16"] holds the same keys in bf16 (for the selection recall).
     draft > 1: the step's inputs are [B][draft][...] (tokens L .. L+draft-1) and
     the rings hold n_win + draft - 1 tokens.
-    kmix: the K caches hold mixed entries (RoPE channels bf16, the rest fp8; V fp8)."""
+    kmix: the K caches hold mixed entries (RoPE channels bf16, the rest fp8; V fp8).
+    index_fp4: the indexer keys are stored fp4 (e2m1, an e8m0 scale per 32
+    channels); step["kic_bf16"] holds the same keys in bf16."""
     import torch
     B, m, n_win = w.B, w.m(layer), w.n_win
     z = gen.pool_logits(w, layer)
@@ -67,8 +69,10 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
     perm = torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None
     kc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm, mixed=kmix)
     vc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm)
-    kic = T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, page_order=perm) if layer == "csa" else None
-    kic16 = T.PagedCache.allocate(B, n_ent, 64, page_order=perm) if layer == "csa" and index_fp8 else None
+    kic = (T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, fp4=index_fp4, page_order=perm)
+           if layer == "csa" else None)
+    kic16 = (T.PagedCache.allocate(B, n_ent, 64, page_order=perm)
+             if layer == "csa" and (index_fp8 or index_fp4) else None)
     cap = n_win + draft - 1
     ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
@@ -114,7 +118,7 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
         if c is None:
             return None
         return T.PagedCache(c.data.clone(), c.page_table, c.n_entries.clone(),
-                            None if c.scale is None else c.scale.clone(), c.mixed)
+                            None if c.scale is None else c.scale.clone(), c.mixed, c.fp4)
 
     layers = []
     for i in range(copies):
@@ -482,8 +486,10 @@ def bench_pro_decode(args, w):
     L = w.L
     f8i = getattr(args, "index_fp8", False)
     kmix = getattr(args, "kv_mixed", False)
+    f4i = getattr(args, "index_fp4", False)
     lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True,
-                                      index_fp8=f8i and layer == "csa", kmix=kmix)
+                                      index_fp8=f8i and layer == "csa", kmix=kmix,
+                                      index_fp4=f4i and layer == "csa")
             for layer in ("csa", "hca")}
     log(f"[bench] {w.name}: state built")
     keep = []
@@ -494,8 +500,9 @@ def bench_pro_decode(args, w):
     nv = (L - w.n_win + 1 + w.m_csa - 1) // w.m_csa
     nvh = (L - w.n_win + 1 + w.m_hca - 1) // w.m_hca
     B = w.B
-    # indexer key bytes per visible block: 128 (bf16), or 64 fp8 codes + the page scale
-    key_b = 64 + 4 / 64 if f8i else 128
+    # indexer key bytes per visible block: 128 (bf16), 64 fp8 codes + the page
+    # scale, or 32 bytes of fp4 codes + 2 scale bytes
+    key_b = 64 + 4 / 64 if f8i else (34 if f4i else 128)
     scan_bytes = int(B * nv * key_b)
     # K + V bytes per compressed entry: fp8 128 + 128, or a mixed K row of 192
     kv_b = 320 if kmix else 256
@@ -503,9 +510,9 @@ def bench_pro_decode(args, w):
     gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     src = source_hash("indexer.hip", "common.h", "update.h")
     extra = {}
-    if f8i:
+    if f8i or f4i:
         # selection recall: how much of each query's top-k over the bf16 keys the
-        # fp8 keys select (the same tokens, compressed both ways)
+        # low-precision keys select (the same tokens, compressed both ways)
         st = lays["csa"][1]
         q = T.Queries.list(st["pos"], L)
         i8, _ = T.indexer_topk(q, st["qI"], st["w"], lays["csa"][0][0].kic, w.m_csa, w.n_win,
@@ -518,7 +525,8 @@ def bench_pro_decode(args, w):
             "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), **extra,
             "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H, "kv_heads": 1,
                        "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
-                       "indexer_keys": "fp8_e4m3+page_scale" if f8i else "bf16",
+                       "indexer_keys": ("fp8_e4m3+page_scale" if f8i else
+                                        "fp4_e2m1+e8m0_per_32" if f4i else "bf16"),
                        "layers": "csa+hca",
                        "kv_dtype": ("k: fp8_e4m3 x64 + bf16 rope x64, v: fp8_e4m3+page_scale"
                                     if kmix else "fp8_e4m3+page_scale"),
@@ -526,7 +534,8 @@ def bench_pro_decode(args, w):
             "roofline": {"bound": "hbm", "kernel": "idx_scan_kernel", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None if f8i else committed_traffic("idx_scan_kernel", w.name, src),
+                         "traffic": (None if f8i or f4i
+                                     else committed_traffic("idx_scan_kernel", w.name, src)),
                          "algorithmic_bytes_per_launch": scan_bytes,
                          "avg_launch_ms": round(scan_ms, 5), "launches_timed": cnt}}
 
@@ -676,6 +685,9 @@ def main():
                     help="pro_decode_1m with fp8 indexer keys (a next row of the scope: the "
                          "scan reads half the bytes); reports the selection recall against "
                          "bf16 keys")
+    ap.add_argument("--index-fp4", action="store_true",
+                    help="pro_decode_1m: fp4 indexer keys (e2m1, an e8m0 scale per 32 channels); "
+                         "also reports the selection recall against bf16 keys")
     ap.add_argument("--kv-mixed", action="store_true",
                     help="pro_decode_1m: K caches hold mixed entries (the 64 RoPE channels bf16, "
                          "the other 64 fp8 with a page scale); V stays fp8")
@@ -702,6 +714,8 @@ def main():
         ap.error("--draft takes 1..3 with --workload csa_decode_128k")
     if args.index_fp8 and args.workload != "pro_decode_1m":
         ap.error("--index-fp8 applies to --workload pro_decode_1m")
+    if args.index_fp4 and (args.workload != "pro_decode_1m" or args.index_fp8):
+        ap.error("--index-fp4 applies to --workload pro_decode_1m (without --index-fp8)")
     if args.kv_mixed and args.workload != "pro_decode_1m":
         ap.error("--kv-mixed applies to --workload pro_decode_1m")
     if args.index_bf16_scores and args.workload != "hybrid_prefill_128k":

@@ -90,7 +90,14 @@ typedef enum {
  * e4m3fn codes (dim/2 bytes, one fp32 scale per page: amax of those channels
  * over the page / 448) followed by channels dim/2 .. dim-1, the RoPE channels,
  * as bf16 (dim bytes): 3*dim/2 bytes per row.  Compressed K caches only. */
-typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2, HSA_FP8_BF16_ROPE = 3 } hsa_dtype;
+/* HSA_FP4_E2M1_MX: the wiki's §8 FP4 indexer, read as OCP MX FP4 -- e2m1
+ * codes (dim/2 bytes a row, channel 2j in the low nibble of byte j) in blocks
+ * of 32 channels, each block with a power-of-two scale 2^x stored as the e8m0
+ * byte x + 127, x = floor(log2(amax of the block)) - 2.  The descriptor's
+ * `scale` then points to the bytes [n_pages][page_size][dim/32].  Compressed
+ * indexer keys only. */
+typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2, HSA_FP8_BF16_ROPE = 3,
+               HSA_FP4_E2M1_MX = 4 } hsa_dtype;
 
 /* Device fault bits reported by hsa_check_device_error(). */
 #define HSA_FAULT_PAGE      1   /* page table entry outside [0, n_pages) */
@@ -114,7 +121,8 @@ typedef struct {
 typedef struct {
   void*          data;          /* [n_pages][page_size] rows of dim dtype elements
                                    (HSA_FP8_BF16_ROPE: rows of 3*dim/2 bytes) */
-  float*         scale;         /* fp8 codes: [n_pages] fp32 page scales; bf16: NULL */
+  float*         scale;         /* fp8 codes: [n_pages] fp32 page scales; bf16: NULL;
+                                   fp4: the e8m0 block-scale bytes (as above) */
   const int32_t* page_table;    /* [n_req][pages_per_req] physical page ids */
   int32_t*       n_entries;     /* [n_req] entries held per request */
   int32_t        n_req;
@@ -123,7 +131,8 @@ typedef struct {
   int32_t        page_size;     /* must be 64 */
   int32_t        dim;
   int32_t        dtype;         /* hsa_dtype: bf16 or fp8 (K, V, indexer keys);
-                                   HSA_FP8_BF16_ROPE (K, with an fp8 V cache) */
+                                   HSA_FP8_BF16_ROPE (K, with an fp8 V cache);
+                                   HSA_FP4_E2M1_MX (indexer keys) */
 } hsa_paged;
 
 /* The query tokens of a call.  Either a span (req == pos == NULL): n
@@ -160,13 +169,15 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
 
 /* Lightning indexer + top-k for each query (wiki §5.3; §8 for the selector).
  *   qI  bf16 [n][H_I][d_I]     w  fp32 [n][H_I]
- *   kIc paged cache of the compressed indexer keys: bf16, or fp8 e4m3fn codes
+ *   kIc paged cache of the compressed indexer keys: bf16, fp8 e4m3fn codes
  *       with one fp32 scale per 64-entry page (the low-precision indexer keys
- *       of wiki §8; key value = code value * page scale)
+ *       of wiki §8; key value = code value * page scale), or fp4
+ *       (HSA_FP4_E2M1_MX; key value = e2m1 value * its block's 2^x)
  *   idx int32 [n][k]  out: selected blocks ascending, -1 padded
  *   score fp32 [n][k] or NULL: the indexer score of each idx entry (0 at pads)
  * Scores are computed in fp32 from bf16 operands (fp8 codes widen to bf16
- * exactly; the page scale multiplies the head sum).  Listed (decode) queries
+ * exactly and the page scale multiplies the head sum; fp4 codes times their
+ * power-of-two block scales are bf16 values, widened exactly).  Listed (decode) queries
  * support up to 2^21 visible blocks per query (HSA_ERR_UNSUPPORTED beyond). */
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k);

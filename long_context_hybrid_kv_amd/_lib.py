@@ -20,7 +20,7 @@ import torch  # load torch's HIP runtime first: the library binds to the same on
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 
-BF16, FP8, FP32, FP8_BF16_ROPE = 0, 1, 2, 3
+BF16, FP8, FP32, FP8_BF16_ROPE, FP4 = 0, 1, 2, 3, 4
 LAYER_CSA, LAYER_HCA = 0, 1
 FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index"}
 
@@ -161,36 +161,48 @@ class PagedCache:
     n_entries: torch.Tensor
     scale: Optional[torch.Tensor] = None
     mixed: bool = False
+    fp4: bool = False
 
     @property
     def dtype(self) -> int:
         if self.mixed:
             return FP8_BF16_ROPE
+        if self.fp4:
+            return FP4
         return FP8 if self.data.dtype == torch.uint8 else BF16
 
     @property
     def dim(self) -> int:
-        return self.data.shape[-1] * 2 // 3 if self.mixed else self.data.shape[-1]
+        if self.mixed:
+            return self.data.shape[-1] * 2 // 3
+        return self.data.shape[-1] * 2 if self.fp4 else self.data.shape[-1]
 
     @staticmethod
     def allocate(n_req: int, max_entries: int, dim: int, fp8: bool = False,
                  page_order: Optional[torch.Tensor] = None, device="cuda",
-                 mixed: bool = False) -> "PagedCache":
-        """mixed: HSA_FP8_BF16_ROPE rows (compressed K caches)."""
+                 mixed: bool = False, fp4: bool = False) -> "PagedCache":
+        """mixed: HSA_FP8_BF16_ROPE rows (compressed K caches); fp4:
+        HSA_FP4_E2M1_MX rows (indexer keys) with `scale` the e8m0 block-scale
+        bytes [n_pages, 64, dim / 32]."""
         ppr = max(1, -(-max_entries // 64))
         n_pages = n_req * ppr
         if mixed:
             data = torch.zeros((n_pages, 64, dim // 2 * 3), dtype=torch.uint8, device=device)
+        elif fp4:
+            data = torch.zeros((n_pages, 64, dim // 2), dtype=torch.uint8, device=device)
         else:
             dt = torch.uint8 if fp8 else torch.bfloat16
             data = torch.zeros((n_pages, 64, dim), dtype=dt, device=device)
         if page_order is None:
             page_order = torch.arange(n_pages, dtype=torch.int32)
         table = page_order.to(torch.int32).reshape(n_req, ppr).to(device)
-        scale = (torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 or mixed
-                 else None)
+        if fp4:
+            scale = torch.full((n_pages, 64, dim // 32), 127, dtype=torch.uint8, device=device)
+        else:
+            scale = (torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 or mixed
+                     else None)
         return PagedCache(data, table.contiguous(),
-                          torch.zeros(n_req, dtype=torch.int32, device=device), scale, mixed)
+                          torch.zeros(n_req, dtype=torch.int32, device=device), scale, mixed, fp4)
 
     def c(self) -> _Paged:
         n_pages, ps, _ = self.data.shape
@@ -206,7 +218,11 @@ class PagedCache:
         return self.data[pages].reshape(-1, self.data.shape[-1])[:n]
 
     def logical_scales(self, r: int, n: int) -> torch.Tensor:
+        """Page scales of the pages holding entries 0..n-1 (fp4: the block-scale
+        bytes of entries 0..n-1, [n, dim / 32])."""
         pages = self.page_table[r, : -(-n // 64)].long()
+        if self.fp4:
+            return self.scale[pages].reshape(-1, self.scale.shape[-1])[:n]
         return self.scale[pages]
 
 

@@ -86,20 +86,24 @@ static int64_t nvis_host(int64_t t, int m, int n_win) {
   return a < b ? a : b;
 }
 
-// allow_mixed: the cache may be HSA_FP8_BF16_ROPE (compressed K, dim 128)
+// allow_mixed: the cache may be HSA_FP8_BF16_ROPE (compressed K, dim 128);
+// allow_fp4: HSA_FP4_E2M1_MX (compressed indexer keys, dim 64)
 static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, bool allow_fp8,
-                              bool allow_mixed = false) {
+                              bool allow_mixed = false, bool allow_fp4 = false) {
   std::string n(name);
   REQ(p, n + ": null descriptor");
   REQ(p->data && p->page_table && p->n_entries, n + ": null data, page_table or n_entries");
   REQ(p->n_req >= 1 && p->pages_per_req >= 1 && p->n_pages >= 1, n + ": empty cache");
   SUP(p->page_size == kPage, n + ": page_size must be 64");
   SUP(p->dim == dim, n + ": unsupported dim");
-  REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3 || p->dtype == HSA_FP8_BF16_ROPE,
+  REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3 || p->dtype == HSA_FP8_BF16_ROPE ||
+          p->dtype == HSA_FP4_E2M1_MX,
       n + ": unknown dtype");
   SUP(allow_fp8 || p->dtype == HSA_BF16, n + ": must be bf16");
   SUP(p->dtype != HSA_FP8_BF16_ROPE || (allow_mixed && p->dim == kD),
       n + ": the mixed bf16-RoPE / fp8 format is for compressed K caches of dim 128");
+  SUP(p->dtype != HSA_FP4_E2M1_MX || (allow_fp4 && p->dim == kDI),
+      n + ": fp4 is for compressed indexer keys of dim 64");
   REQ(p->dtype == HSA_BF16 || p->scale, n + ": fp8 cache needs page scales");
   SUP(p->n_pages < (1 << 25), n + ": pool rows must be addressable by a 32-bit row id");
   return HSA_OK;
@@ -249,7 +253,7 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
   REQ(out, "kv_compress: null output");
   SUP(out->dim == kD || out->dim == kDI, "kv_compress: dim must be 128 or 64");
   hsa_status s;
-  if ((s = check_paged(out, "out", out->dim, true, true)) != HSA_OK) return s;
+  if ((s = check_paged(out, "out", out->dim, true, true, true)) != HSA_OK) return s;
   if ((s = check_tokens(x, "x", out->dim, 1)) != HSA_OK) return s;
   REQ(alpha, "kv_compress: null alpha");
   REQ(m >= 1 && m <= 4096, "kv_compress: bad m");
@@ -276,7 +280,7 @@ static hsa_status indexer_topk(const hsa_queries* q, const void* qI, const float
                                int32_t k, int32_t* idx, float* score, void* ws, size_t ws_bytes,
                                hipStream_t stream, bool s16) {
   hsa_status s;
-  if ((s = check_paged(kIc, "kIc", kDI, true)) != HSA_OK) return s;
+  if ((s = check_paged(kIc, "kIc", kDI, true, false, true)) != HSA_OK) return s;
   if ((s = check_queries(q, kIc->n_req)) != HSA_OK) return s;
   REQ(qI && w && idx, "indexer_topk: null qI, w or idx");
   SUP(H_I == kHI && d_I == kDI, "indexer_topk: H_I must be 4 and d_I 64");

@@ -58,6 +58,19 @@ __device__ __forceinline__ uint8_t f64_to_e4m3(double x) {
   return (uint8_t)(sign | code);
 }
 
+// float64 -> OCP MX e2m1 code (4 bits; ties to even; saturates at +-6; the sign
+// bit follows x).  The grid's quantum is 0.5 below 2, 1 in [2, 4), 2 in [4, 6].
+__device__ __forceinline__ uint32_t f64_to_e2m1(double x) {
+  const uint32_t sign = __builtin_signbit(x) ? 8u : 0u;
+  double a = fabs(x);
+  a = a > 6.0 ? 6.0 : a;
+  const double q = a < 2.0 ? 0.5 : (a < 4.0 ? 1.0 : 2.0);
+  const double v = __builtin_rint(a / q) * q;   // representable magnitude, <= 6
+  const uint32_t mag = v < 2.0 ? (uint32_t)(2.0 * v)
+                     : v < 4.0 ? (uint32_t)(v + 2.0) : (uint32_t)(4.0 + 0.5 * v);
+  return sign | mag;
+}
+
 // e4m3fn code -> bf16 bits (exact: e4m3 values are bf16 values).  Normal
 // codes keep exponent and fraction (re-biased 7 -> 127); the eight codes with
 // a zero exponent field are subnormal multiples of 2^-9.
@@ -74,6 +87,22 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
 // 4 significant bits, so dropping the float's low 16 bits is exact.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// 8 e2m1 codes (one 32-bit word, channel 2j in the low nibble of byte j) times
+// a power-of-two scale -> bf16x8, by the hardware converter (exact: such a
+// product is a bf16 value for the scales a compressor writes).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t c, float scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+// an e8m0 scale byte (2^(byte - 127)) as a float
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 c) {
   typedef float f2 __attribute__((ext_vector_type(2)));
   const f2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
@@ -118,10 +147,14 @@ struct Paged {
   const int32_t* page_table;
   int32_t* n_entries;
   int32_t pages_per_req, n_pages, dim, dtype;
-  // bytes of one entry's row: dim elements, or (HSA_FP8_BF16_ROPE) dim/2 fp8
-  // codes followed by dim/2 bf16 channels
+  // bytes of one entry's row: dim elements, (HSA_FP8_BF16_ROPE) dim/2 fp8
+  // codes followed by dim/2 bf16 channels, or (HSA_FP4_E2M1_MX) dim/2 bytes of
+  // e2m1 nibbles
   __device__ __forceinline__ int row_bytes() const {
-    return dtype == HSA_FP8_E4M3 ? dim : dtype == HSA_FP8_BF16_ROPE ? dim / 2 * 3 : dim * 2;
+    return dtype == HSA_FP8_E4M3        ? dim
+           : dtype == HSA_FP8_BF16_ROPE ? dim / 2 * 3
+           : dtype == HSA_FP4_E2M1_MX   ? dim / 2
+                                        : dim * 2;
   }
   // physical page of entry e of request r, or -1 (and a fault) if out of range
   __device__ __forceinline__ int page_of(int r, int64_t e, int* fault) const {

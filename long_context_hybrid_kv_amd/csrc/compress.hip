@@ -32,8 +32,9 @@ hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, 
 // the (entry, channel) items idx = tid, tid + 256, ... of the page; consecutive
 // threads read consecutive channels of a token row (coalesced).
 // FMT: HSA_BF16, HSA_FP8_E4M3 (every channel fp8, page scale over all of
-// them) or HSA_FP8_BF16_ROPE (channels below dim/2 fp8 with a page scale over
-// those channels, the RoPE channels above them bf16)
+// them), HSA_FP8_BF16_ROPE (channels below dim/2 fp8 with a page scale over
+// those channels, the RoPE channels above them bf16) or HSA_FP4_E2M1_MX (dim
+// 64: e2m1 nibbles with a power-of-two scale per 32-channel block)
 template <int FMT, int MAXV>
 __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int req, int64_t first,
                                                        int64_t n, int m,
@@ -65,6 +66,31 @@ __global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int 
     }
     vals[v] = acc;
     if (FMT != HSA_FP8_BF16_ROPE || c < dim / 2) amax = fmax(amax, fabs(acc));
+  }
+  if (FMT == HSA_FP4_E2M1_MX) {
+    // dim 64: item it = entry * 64 + channel with it = tid + 256 v, so the 32
+    // channels of a block are 32 consecutive lanes of one wave (all of the same
+    // entry); the block's amax is a reduction over those lanes
+    uint8_t* sb = (uint8_t*)out.scale;
+#pragma unroll
+    for (int v = 0; v < MAXV; ++v) {
+      const int it = threadIdx.x + v * 256;
+      double a = fabs(vals[v]);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) a = fmax(a, __shfl_xor(a, o));
+      int E;
+      (void)frexp(a, &E);                       // a = f * 2^E, f in [0.5, 1)
+      int x = a > 0.0 ? E - 3 : 0;              // floor(log2 a) - 2
+      x = x < -127 ? -127 : (x > 127 ? 127 : x);
+      const uint32_t code = f64_to_e2m1(vals[v] * ldexp(1.0, -x));   // exact scaling
+      const uint32_t hi = __shfl_xor(code, 1);   // the odd channel's code
+      const int64_t e = page_e0 + it / dim;
+      const int c = it % dim;
+      if (it >= items || e < e_lo || e >= e_hi) continue;
+      if ((c & 1) == 0) out.row(page, e)[c / 2] = (uint8_t)(code | (hi << 4));
+      if ((c & 31) == 0) sb[((int64_t)page * kPage + (e & 63)) * (dim / 32) + c / 32] = (uint8_t)(x + 127);
+    }
+    return;
   }
   if (FMT == HSA_BF16) {
 #pragma unroll
@@ -154,7 +180,9 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
   KernelTimer kt(HSA_K_COMPRESS, s);
   const unsigned g = (unsigned)pages;
   int* f = fault_word();
-  if (out.dtype == HSA_FP8_BF16_ROPE) {   // K caches: dim = kD
+  if (out.dtype == HSA_FP4_E2M1_MX) {     // indexer keys: dim = kDI
+    compress_kernel<HSA_FP4_E2M1_MX, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+  } else if (out.dtype == HSA_FP8_BF16_ROPE) {   // K caches: dim = kD
     compress_kernel<HSA_FP8_BF16_ROPE, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   } else if (out.dtype == HSA_FP8_E4M3) {
     if (out.dim == kD)

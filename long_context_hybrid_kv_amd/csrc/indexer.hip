@@ -276,7 +276,8 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
 
 // ---------------------------------------------------------------- decode: score scan
 
-template <int CPW, int NWV, bool F8K, bool S16>
+// F8K: fp8 keys with a page scale; F4K: fp4 keys (MX blocks); neither: bf16
+template <int CPW, int NWV, bool F8K, bool F4K, bool S16>
 __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   // key pieces of a lane, 16 bytes each: bf16, 8 channels (two pieces per
   // tile); fp8 codes, 16 channels (one piece per tile), widened to bf16 when
   // scored, the page scale applied to the head sum
-  typedef typename std::conditional<F8K, u32x4, bf16x8>::type KeyT;
+  typedef typename std::conditional<F8K || F4K, u32x4, bf16x8>::type KeyT;
   float ksc[CPW][PPW];   // fp8: scale of the wave's pages of each chunk
   // branch-free loads (tile u lies in the wave's page u / 4)
   auto load = [&](int c, KeyT* x0, KeyT* x1) {
@@ -343,6 +344,14 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
         // scored; a bad page reads page 0.
         x0[u] = __builtin_nontemporal_load(
             (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row) * kDI) + g);
+      } else if constexpr (F4K) {
+        // 32-byte keys: one load instruction reads 16 whole keys, lane (row, g)
+        // the 16 channels 16g .. 16g+15 (all in block g / 2) and that block's
+        // scale byte (.z)
+        const int64_t er = (int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row;
+        const u32x2 cw = __builtin_nontemporal_load((const u32x2*)(kic.data + er * (kDI / 2)) + g);
+        const uint32_t sb = ((const uint8_t*)kic.scale)[er * (kDI / 32) + (g >> 1)];
+        x0[u] = u32x4{cw.x, cw.y, sb, 0u};
       } else {
         // whole rows: each load instruction reads 8 consecutive 128-byte keys,
         // lane (r8, p8) piece p8 of key r8 (score() moves them to the MFMA
@@ -367,12 +376,12 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   if (CPW > 1) load(1, xb0, xb1);
 
   // query head `row` in the channel order of the keys: bf16, channels 8g..8g+7
-  // then 32+8g..; fp8, 16g..16g+7 then 16g+8..16g+15
+  // then 32+8g..; fp8 and fp4, 16g..16g+7 then 16g+8..16g+15
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
-    a0 = qa[F8K ? 2 * g : g];
-    a1 = qa[F8K ? 2 * g + 1 : 4 + g];
+    a0 = qa[F8K || F4K ? 2 * g : g];
+    a1 = qa[F8K || F4K ? 2 * g + 1 : 4 + g];
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
@@ -393,6 +402,10 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
       if constexpr (F8K) {
         k0 = e4m3x8_to_bf16x8(x0[u].xy);   // channels 16g .. 16g+7
         k1 = e4m3x8_to_bf16x8(x0[u].zw);   // channels 16g+8 .. 16g+15
+      } else if constexpr (F4K) {
+        const float bs = e8m0_to_f32(x0[u].z);
+        k0 = e2m1x8_to_bf16x8(x0[u].x, bs);
+        k1 = e2m1x8_to_bf16x8(x0[u].y, bs);
       } else {
         // the wave's 16 keys through its LDS tile: piece p of key r is stored
         // at slot p ^ (r & 7), so the row-wise writes and the MFMA-layout
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
 // The block range is the fast grid index and the number of ranges a multiple
 // of 8: workgroups are dealt to the 8 XCDs round-robin, so each XCD's L2
 // holds the keys of one eighth of the blocks instead of all of them.
-template <bool F8K, bool S16>
+template <bool F8K, bool F4K, bool S16>
 __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, int nq,
                                                        const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
@@ -636,8 +649,8 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     if (ql < nq) {
       const bf16x8* qa =
           (const bf16x8*)(qI + ((int64_t)(q_base + ql) * kHI + (row & 3)) * kDI);
-      a[at][0] = qa[g];
-      a[at][1] = qa[4 + g];
+      a[at][0] = qa[F4K ? 2 * g : g];   // fp4 keys: channels 16g .. 16g+15 per lane
+      a[at][1] = qa[F4K ? 2 * g + 1 : 4 + g];
     }
     int qg = 16 * qt + 4 * at + g;               // local query of this lane's result rows
     nvq[at] = 0;
@@ -678,15 +691,21 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   // scores are computed
   // key pieces: bf16 (16 bytes) or fp8 codes (8 bytes, widened to bf16 when
   // scored, with the page scale applied to the head sum)
-  typedef typename std::conditional<F8K, u32x2, bf16x8>::type KeyT;
+  typedef typename std::conditional<F8K || F4K, u32x2, bf16x8>::type KeyT;
   auto load = [&](int64_t tile, KeyT& x0, KeyT& x1, float& sc) {
     const int64_t b = 16 * tile + row;
     int page = -1;
     if (b < nv_max) page = pg_lds ? pg[(b >> 6) - p_lo] : kic.page_of(r, b, fault);
     const bool ok = page >= 0;
     const KeyT* kr = (const KeyT*)kic.row(ok ? page : 0, ok ? b : 0);
-    x0 = kr[g];
-    x1 = kr[4 + g];
+    if constexpr (F4K) {
+      x0 = kr[g];   // 8 bytes: channels 16g .. 16g+15, all in block g / 2
+      const int64_t er = (int64_t)(ok ? page : 0) * kPage + (ok ? (b & 63) : 0);
+      sc = e8m0_to_f32(((const uint8_t*)kic.scale)[er * (kDI / 32) + (g >> 1)]);
+    } else {
+      x0 = kr[g];
+      x1 = kr[4 + g];
+    }
     if constexpr (F8K) sc = ok ? kic.scale[page] : 1.f;
   };
   KeyT c0, c1, n0 = {}, n1 = {};
@@ -700,6 +719,9 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     if constexpr (F8K) {
       k0 = e4m3x8_to_bf16x8(c0);
       k1 = e4m3x8_to_bf16x8(c1);
+    } else if constexpr (F4K) {
+      k0 = e2m1x8_to_bf16x8(c0.x, cs);
+      k1 = e2m1x8_to_bf16x8(c0.y, cs);
     } else {
       k0 = c0;
       k1 = c1;
@@ -1241,16 +1263,23 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const unsigned n_groups = (n_chunks + cpw - 1) / cpw;
     const UpdateArgs ua = upd ? *upd : UpdateArgs{};
     const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
-    const bool f8k = kic.dtype == HSA_FP8_E4M3;
+    const bool f8k = kic.dtype == HSA_FP8_E4M3, f4k = kic.dtype == HSA_FP4_E2M1_MX;
     // eight waves, each streaming one page of every chunk
-    auto scan = s16 ? (cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true, true>
-                                       : idx_scan_kernel<4, 8, false, true>)
-                                : (f8k ? idx_scan_kernel<1, 8, true, true>
-                                       : idx_scan_kernel<1, 8, false, true>))
-                    : (cpw == 4 ? (f8k ? idx_scan_kernel<4, 8, true, false>
-                                       : idx_scan_kernel<4, 8, false, false>)
-                                : (f8k ? idx_scan_kernel<1, 8, true, false>
-                                       : idx_scan_kernel<1, 8, false, false>));
+    auto pick = [&](auto k4_f8, auto k4_f4, auto k4_bf, auto k1_f8, auto k1_f4, auto k1_bf) {
+      return cpw == 4 ? (f8k ? k4_f8 : f4k ? k4_f4 : k4_bf) : (f8k ? k1_f8 : f4k ? k1_f4 : k1_bf);
+    };
+    auto scan = s16 ? pick(idx_scan_kernel<4, 8, true, false, true>,
+                           idx_scan_kernel<4, 8, false, true, true>,
+                           idx_scan_kernel<4, 8, false, false, true>,
+                           idx_scan_kernel<1, 8, true, false, true>,
+                           idx_scan_kernel<1, 8, false, true, true>,
+                           idx_scan_kernel<1, 8, false, false, true>)
+                    : pick(idx_scan_kernel<4, 8, true, false, false>,
+                           idx_scan_kernel<4, 8, false, true, false>,
+                           idx_scan_kernel<4, 8, false, false, false>,
+                           idx_scan_kernel<1, 8, true, false, false>,
+                           idx_scan_kernel<1, 8, false, true, false>,
+                           idx_scan_kernel<1, 8, false, false, false>);
     timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(8 * 64), 0, s, Qd, (const u16*)qI, w, kc, m,
                  n_win, k, ws, (int)n_groups, ua, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
@@ -1272,10 +1301,13 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     if (bsplit < 1) bsplit = 1;
     if (bsplit > 512) bsplit = 512;
     bsplit = (bsplit + 7) / 8 * 8;
-    const bool f8k = kic.dtype == HSA_FP8_E4M3;
+    const bool f8k = kic.dtype == HSA_FP8_E4M3, f4k = kic.dtype == HSA_FP4_E2M1_MX;
     timed_launch(HSA_K_INDEXER_GEMM,
-                 s16 ? (f8k ? idx_gemm_kernel<true, true> : idx_gemm_kernel<false, true>)
-                     : (f8k ? idx_gemm_kernel<true, false> : idx_gemm_kernel<false, false>),
+                 s16 ? (f8k   ? idx_gemm_kernel<true, false, true>
+                        : f4k ? idx_gemm_kernel<false, true, true> : idx_gemm_kernel<false, false, true>)
+                     : (f8k   ? idx_gemm_kernel<true, false, false>
+                        : f4k ? idx_gemm_kernel<false, true, false>
+                              : idx_gemm_kernel<false, false, false>),
                  dim3(bsplit, (nq + 15) / 16), dim3(256), 0,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);

@@ -35,7 +35,7 @@ def test_status_strings():
 
 
 def _paged(dim=128, dtype=0, ppr=4, fake=0x1000):
-    return L._Paged(fake, fake if dtype in (1, 3) else None, fake, fake, 1, ppr, ppr, 64, dim, dtype)
+    return L._Paged(fake, fake if dtype in (1, 3, 4) else None, fake, fake, 1, ppr, ppr, 64, dim, dtype)
 
 
 def _tokens(cap=4096, dim=128, fake=0x1000):
@@ -97,6 +97,11 @@ def test_validation_rejects_before_any_launch():
     assert lib.hsa_kv_compress(C.byref(_tokens(dim=64)), 0, C.byref(_paged(dim=64, dtype=L.FP8_BF16_ROPE)), 0, 0, 1, 4, f, None) == -2
     assert lib.hsa_kv_compress(C.byref(tk), 0, C.byref(km), 0, 3, 10, 4, f, None) == -1   # not page-aligned
     assert lib.hsa_kv_compress(C.byref(tk), 0, C.byref(L._Paged(0x1000, None, 0x1000, 0x1000, 1, 4, 4, 64, 128, L.FP8_BF16_ROPE)), 0, 0, 1, 4, f, None) == -1   # no scales
+    # fp4: compressed indexer keys of dim 64 only
+    k4 = _paged(dim=64, dtype=L.FP4)
+    assert hca(_paged(dtype=L.FP4), _paged(dtype=L.FP4)) == -2          # as K / V caches
+    assert lib.hsa_kv_compress(C.byref(tk), 0, C.byref(_paged(dtype=L.FP4)), 0, 0, 1, 4, f, None) == -2
+    assert lib.hsa_kv_compress(C.byref(_tokens(dim=64)), 0, C.byref(k4), 0, 3, 10, 4, f, None) == -1
     # CSA without idx
     assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, 0, None, f, 1 << 30, None) == -1
 
