@@ -635,6 +635,7 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
                                                        int m, int n_win, IdxWs ws, int* fault) {
   const int qt = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
+  const int r8 = lane >> 3, p8 = lane & 7;   // bf16 loads: key r8 of 8, 16-byte piece p8
   const int r = Q.span_req;
   const int64_t ne = kic.n_entries[r];
   bf16x8 a[4][2];
@@ -702,12 +703,24 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
       x0 = kr[g];   // 8 bytes: channels 16g .. 16g+15, all in block g / 2
       const int64_t er = (int64_t)(ok ? page : 0) * kPage + (ok ? (b & 63) : 0);
       sc = e8m0_to_f32(((const uint8_t*)kic.scale)[er * (kDI / 32) + (g >> 1)]);
-    } else {
+    } else if constexpr (F8K) {
       x0 = kr[g];
       x1 = kr[4 + g];
+    } else {
+      // whole 128-byte keys, 8 per load instruction (lane (r8, p8): piece p8 of
+      // keys r8 and r8 + 8 of the tile), as in the decode scan; a tile is 16
+      // keys of one page, so its first key's page serves both loads, and keys
+      // past the row's end are read but never stored
+      const int64_t bt = 16 * tile;            // < nv_max for every tile walked
+      const int pt = pg_lds ? pg[(bt >> 6) - p_lo] : kic.page_of(r, bt, fault);
+      const KeyT* kt = (const KeyT*)(kic.data + ((int64_t)(pt >= 0 ? pt : 0) * kPage +
+                                                 (bt & 63) + r8) * (kDI * 2)) + p8;
+      x0 = kt[0];
+      x1 = kt[8 * (kDI * 2 / 16)];
     }
     if constexpr (F8K) sc = ok ? kic.scale[page] : 1.f;
   };
+  __shared__ bf16x8 ltile[F8K || F4K ? 1 : 4][F8K || F4K ? 1 : 128];   // bf16: a tile per wave
   KeyT c0, c1, n0 = {}, n1 = {};
   float cs = 1.f, ns = 1.f;
   int64_t tile = t_lo + wv;
@@ -723,8 +736,13 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
       k0 = e2m1x8_to_bf16x8(c0.x, cs);
       k1 = e2m1x8_to_bf16x8(c0.y, cs);
     } else {
-      k0 = c0;
-      k1 = c1;
+      // through the wave's swizzled LDS tile into the MFMA layout (as the scan)
+      asm volatile("" ::: "memory");
+      ltile[wv][r8 * 8 + (p8 ^ r8)] = c0;
+      ltile[wv][(8 + r8) * 8 + (p8 ^ r8)] = c1;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      k0 = ltile[wv][row * 8 + (g ^ (row & 7))];
+      k1 = ltile[wv][row * 8 + ((4 + g) ^ (row & 7))];
     }
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
