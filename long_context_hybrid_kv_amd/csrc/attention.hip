@@ -352,11 +352,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   // K tile (row-major bf16) and V^T tile (fp16 bits).  SH: one buffer for both,
   // V^T staged once every wave has read the K tile (half the LDS, so more
-  // workgroups fit on a CU, for two more barriers per chunk)
-  constexpr int kKsH = 64 * 136, kVtH = 128 * 72;
+  // workgroups fit on a CU, for two more barriers per chunk).  V^T row pitch:
+  // SH (the prefill) 34 dwords, which spreads the 16 rows one P V operand
+  // read touches over distinct bank pairs (36 put rows r and r + 8 on the
+  // same banks: 4% of the prefill attention time); decode keeps 36, measured
+  // as fast or faster there
+  constexpr int kVtP = SH ? 68 : 72;
+  constexpr int kKsH = 64 * 136, kVtH = 128 * kVtP;
   __shared__ __align__(16) u16 kv_lds[SH ? (kVtH > kKsH ? kVtH : kKsH) : kKsH + kVtH];
   u16(*Ks)[136] = (u16(*)[136])kv_lds;
-  u16(*Vt)[72] = (u16(*)[72])(kv_lds + (SH ? 0 : kKsH));
+  u16(*Vt)[kVtP] = (u16(*)[kVtP])(kv_lds + (SH ? 0 : kKsH));
   __shared__ float ksc[64];
 
   // ---- resolve the rows of every entry of this split once
@@ -434,8 +439,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       uint32_t* vt = (uint32_t*)&Vt[cgv * 8][0] + vpair;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        vt[(2 * q2) * 36] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
-        vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
+        vt[(2 * q2) * (kVtP / 2)] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
+        vt[(2 * q2 + 1) * (kVtP / 2)] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
       }
     }
   };
@@ -701,11 +706,12 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
   const int end0 = __builtin_amdgcn_readfirstlane(n_wu + (int)nv0);
   const int n_wuu = __builtin_amdgcn_readfirstlane(n_wu);
 
-  // one LDS buffer for the K tile and then the V^T tile (fp16 bits), staged
-  // once every wave has read the K tile
+  // one LDS buffer for the K tile and then the V^T tile (fp16 bits, row pitch
+  // 34 dwords: the 16 rows of a P V operand read on distinct bank pairs),
+  // staged once every wave has read the K tile
   __shared__ __align__(16) u16 kv_lds[128 * 72];
   u16(*Ks)[136] = (u16(*)[136])kv_lds;
-  u16(*Vt)[72] = (u16(*)[72])kv_lds;
+  u16(*Vt)[68] = (u16(*)[68])kv_lds;
   // dynamic LDS: row addresses of the union's entries (K, then V), sized by
   // the host for the longest union
   extern __shared__ __align__(16) int dyn_lds[];
@@ -781,8 +787,8 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
       uint32_t* vt = (uint32_t*)&Vt[cgv * 8][0] + vpair;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        vt[(2 * q2) * 36] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
-        vt[(2 * q2 + 1) * 36] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
+        vt[(2 * q2) * 34] = (a0[q2] & 0xFFFFu) | (a1[q2] << 16);
+        vt[(2 * q2 + 1) * 34] = (a0[q2] >> 16) | (a1[q2] & 0xFFFF0000u);
       }
     }
   };

@@ -199,11 +199,11 @@ def test_bf16_output_is_rounded_fp32_output():
 
 
 @pytest.mark.parametrize("H,n_win,m,T_,pos0", [(64, 128, 128, 2049, 0), (128, 64, 16, 1501, 0),
-                                               (64, 128, 4, 1200, 37)])
+                                               (64, 128, 4, 1200, 37), (64, 32, 8, 1026, 0)])
 def test_hca_prefill_query_pairs(H, n_win, m, T_, pos0):
-    """The paired-query HCA prefill path (H a multiple of 64, bf16): odd query
-    counts (a last query without a partner), spans that start at an odd
-    position, m from 4 to 128, a window shorter than a tile, shuffled pages;
+    """The paired-query HCA prefill path (H a multiple of 64, bf16): odd and
+    even query counts (a last query without a partner), spans that start at an
+    odd position, m from 4 to 128, windows shorter than a tile, shuffled pages;
     every row against the oracle."""
     w = configs.shrink(configs.PREFILL_4K, H=H, n_win=n_win, T=T_, m_hca=m)
     inp = gen.prefill_layer(w, "hca")
