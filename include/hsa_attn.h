@@ -104,6 +104,10 @@ typedef enum { HSA_BF16 = 0, HSA_FP8_E4M3 = 1, HSA_FP32 = 2, HSA_FP8_BF16_ROPE =
 #define HSA_FAULT_POS       2   /* a query position above max_pos */
 #define HSA_FAULT_ENTRIES   4   /* n_entries[r] smaller than the visible blocks */
 #define HSA_FAULT_INDEX     8   /* a top-k index outside [0, n_vis) */
+#define HSA_FAULT_REQ      16   /* a listed request id outside [0, n_req) of the caches
+                                   (the query reads request 0 instead) */
+#define HSA_FAULT_RANGE    32   /* an attention output is not finite: a V value outside
+                                   fp16's range (|v| > 65504) entered the P.V product */
 
 /* Raw bf16 token rows of several requests.  Token p of request r lives in
  * row (p mod capacity): pass capacity >= sequence length for plain arrays
@@ -283,9 +287,11 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
  * [B][n_tok][H][d]; k_new, v_new [B][n_tok][d]; qI [B][n_tok][H_I][d_I];
  * kI_new [B][n_tok][d_I]; w [B][n_tok][H_I]; O [B][n_tok][H][d]; lse
  * [B][n_tok][H] or NULL; idx_out [B][n_tok][topk] or NULL.  1 <= n_tok <= 256;
- * max_pos bounds every pos[b] + n_tok - 1.  The caller advances pos by the
- * accepted tokens (a rejected suffix must be rewound by the caller: the caches
- * keep what the draft appended).  No allocation and no host synchronisation. */
+ * max_pos bounds every pos[b] + n_tok - 1.  A CSA layer's indexer tail must
+ * hold m + n_tok - 1 rows, so that hsa_decode_rewind can drop any rejected
+ * suffix.  The caller advances pos by the accepted tokens and rewinds the
+ * caches to them with hsa_decode_rewind (the draft appended every token).
+ * No allocation and no host synchronisation. */
 size_t hsa_decode_draft_workspace_bytes(const hsa_layer* L, int32_t B, int32_t n_tok,
                                         int64_t max_pos);
 hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const int64_t* pos,
@@ -293,6 +299,20 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
                             const void* qI, const void* kI_new, const float* w, void* O,
                             float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* Rewind a layer's caches after a draft whose suffix was rejected (zjai.club
+ * episode 163 page, "Deep dive" §16: the caches stay in step across prefill,
+ * decode and speculative decode).  Request b keeps tokens 0 .. keep[b]-1:
+ * n_entries[b] of the compressed K, V (and, CSA, indexer-key) caches becomes
+ * keep[b] / m, dropping every block a rejected token completed.  The rings
+ * and the indexer tail need no change: a slot is position mod capacity, so
+ * the next tokens overwrite the rejected rows before any query reads them,
+ * and the sizes hsa_decode_draft requires keep the kept rows intact.
+ * keep int64 [B] (device).  bf16 caches only.  A keep[b] < 0, or one asking
+ * for more blocks than a cache holds, leaves request b unchanged and raises
+ * HSA_FAULT_POS / HSA_FAULT_ENTRIES.  No allocation, no host synchronisation. */
+hsa_status hsa_decode_rewind(const hsa_layer* L, int32_t B, const int64_t* keep,
+                             hipStream_t stream);
 
 /* Optional kernel timing (tracing).  While enabled for a kernel, every launch
  * of it is timed with a pair of HIP events on its stream; read returns the

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
 
 BF16, FP8, FP32, FP8_BF16_ROPE, FP4 = 0, 1, 2, 3, 4
 LAYER_CSA, LAYER_HCA = 0, 1
-FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index"}
+FAULT_BITS = {1: "page", 2: "pos", 4: "entries", 8: "index", 16: "req", 32: "range"}
 
 
 class HsaError(RuntimeError):
@@ -95,6 +95,7 @@ _SIGS = {
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_size_t, C.c_void_p]),
+    "hsa_decode_rewind": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_void_p, C.c_void_p]),
     "hsa_decode_draft_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), C.c_int32, C.c_int32,
                                                       C.c_int64]),
     "hsa_decode_draft": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_int32, C.c_void_p, C.c_int64,
@@ -445,3 +446,10 @@ def decode_step(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,
                                  _ptr(v_new), _ptr(qI), _ptr(kI_new), _ptr(w), _ptr(O),
                                  _ptr(lse), _ptr(idx), ws, wsb, _stream()), "decode_step")
     return O, lse, idx
+
+
+def decode_rewind(layer: Layer, keep: torch.Tensor) -> None:
+    """hsa_decode_rewind: request b keeps tokens 0 .. keep[b]-1 (int64 [B], device)."""
+    Lc = layer.c()
+    _check(lib().hsa_decode_rewind(C.byref(Lc), keep.shape[0], _ptr(keep), _stream()),
+           "decode_rewind")

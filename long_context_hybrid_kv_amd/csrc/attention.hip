@@ -262,6 +262,19 @@ __device__ __forceinline__ uint4 v_piece_f16(uint4 raw, bool fp8, float scale) {
                     pack_f16(f[6], f[7]));
 }
 
+// Raise HSA_FAULT_RANGE when an output accumulator is not finite: V values are
+// staged in fp16 for the P V product, so a |v| above 65504 (or a non-finite
+// input) turns the affected outputs into inf / NaN; the fault word reports it.
+template <int N>
+__device__ __forceinline__ void check_finite(const f32x4 (&acc)[N], int* fault) {
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    bad |= !(__builtin_isfinite(acc[i][0]) && __builtin_isfinite(acc[i][1]) &&
+             __builtin_isfinite(acc[i][2]) && __builtin_isfinite(acc[i][3]));
+  if (bad) atomicOr(fault, HSA_FAULT_RANGE);
+}
+
 // KMIX (with F8): the K cache is HSA_FP8_BF16_ROPE, the V cache fp8
 template <int NW, bool F8, bool SH, bool KMIX>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
@@ -293,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // depend on (top-k ids, or page ids) are requested together, before any of
   // them is used: one memory round trip instead of three
   const bool listed = a.Q.pos != nullptr;
-  const int r = listed ? (a.Q.req ? a.Q.req[qi] : qi) : a.Q.span_req;
+  const int r = a.Q.req_of(qi, a.fault);
   const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
   const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
   // dynamic LDS: the row ids of the split's entries (K, then V), then -- decode
@@ -561,6 +574,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     __syncthreads();
   }
   const float l_i = osum[0];
+  check_finite(oacc, a.fault);
 
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
   if (a.n_splits == 1) {
@@ -607,7 +621,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
                                                          const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          void* __restrict__ O, int o_f32,
-                                                         float* __restrict__ lse) {
+                                                         float* __restrict__ lse, int* fault) {
   const int qh = blockIdx.x;   // query * H + head
   const int q = qh / H, h = qh % H, d = threadIdx.x;
   __shared__ float wgt[kMergeMaxSplits], lsm[kMergeMaxSplits];
@@ -648,6 +662,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
     if (j < ns) acc += wgt[j] * v[j];
   for (int s = kMergePF; s < ns; ++s) acc += wgt[s] * po[s * stride];
   const float o = L > 0.f ? acc / L : 0.f;
+  if (!__builtin_isfinite(o)) atomicOr(fault, HSA_FAULT_RANGE);
   if (o_f32)
     ((float*)O)[(int64_t)qh * kD + d] = o;
   else
@@ -890,6 +905,8 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head] of each query
+  check_finite(oacc[0], a.fault);
+  check_finite(oacc[1], a.fault);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (j == 1 && !has1) break;
@@ -970,7 +987,6 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t s) {
-  (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   int64_t s_max = q.max_pos - n_win + 1 < 0 ? 0 : q.max_pos - n_win + 1;
   int64_t nv_max = (s_max + m - 1) / m;
@@ -978,8 +994,11 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   nv_max = nv_max < b2 ? nv_max : b2;
   int64_t max_entries = n_win + (k > 0 ? (nv_max < k ? nv_max : k) : nv_max);
   AttnPlan p = plan(q.n, H, max_entries, span, attn_decode_cps(k, n_win));
+  // the partials this launch writes must fit the workspace it was given
+  if (attn_ws_bytes(q.n, H, max_entries, span, attn_decode_cps(k, n_win)) > ws_bytes)
+    return hipErrorInvalidValue;
   AttnArgs a;
-  a.Q = to_dev(q);
+  a.Q = to_dev(q, kc.n_req);
   a.q = (const u16*)Q;
   a.H = H;
   a.wk = to_dev(wk);
@@ -1047,7 +1066,7 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                  grid, dim3(64), pre, s, a);
   if (p.n_splits > 1)
     attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
-                                                            O, a.o_f32, lse);
+                                                            O, a.o_f32, lse, a.fault);
   return hipGetLastError();
 }
 

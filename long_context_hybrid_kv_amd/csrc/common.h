@@ -185,9 +185,21 @@ struct Queries {
   int32_t span_req;
   int64_t span_pos0;
   int64_t max_pos;
+  int32_t n_req;        // requests the caches hold: listed ids must lie below it
+  // request of query i; a listed id outside [0, n_req) reads request 0 and
+  // raises HSA_FAULT_REQ
+  __device__ __forceinline__ int req_of(int i, int* fault) const {
+    if (!pos) return span_req;
+    const int r = req ? req[i] : i;
+    if ((unsigned)r >= (unsigned)n_req) {
+      atomicOr(fault, HSA_FAULT_REQ);
+      return 0;
+    }
+    return r;
+  }
   __device__ __forceinline__ void get(int i, int* r, int64_t* t, int* fault) const {
+    *r = req_of(i, fault);
     if (pos) {
-      *r = req ? req[i] : i;
       int64_t p = pos[i];
       if (p > max_pos || p < 0) {
         atomicOr(fault, HSA_FAULT_POS);
@@ -195,7 +207,6 @@ struct Queries {
       }
       *t = p;
     } else {
-      *r = span_req;
       *t = span_pos0 + i;
     }
   }
@@ -206,8 +217,8 @@ inline Paged to_dev(const hsa_paged& p) {
                p.n_pages, p.dim, p.dtype};
 }
 inline Tokens to_dev(const hsa_tokens& t) { return Tokens{(uint8_t*)t.data, t.capacity, t.dim}; }
-inline Queries to_dev(const hsa_queries& q) {
-  return Queries{q.req, q.pos, q.span_req, q.span_pos0, q.max_pos};
+inline Queries to_dev(const hsa_queries& q, int n_req) {
+  return Queries{q.req, q.pos, q.span_req, q.span_pos0, q.max_pos, n_req};
 }
 
 // ---------------------------------------------------------------- host-side launchers
@@ -247,7 +258,8 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
 
 struct UpdateArgs;   // update.h
 
-size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span);
+// group > 1 (listed queries): the draft scan's workspace shape
+size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span, int group = 1);
 int64_t indexer_max_blocks();   // longest visible-block row the decode indexer takes
 // upd: when not null, the decode cache upkeep of request i runs in the scan
 // launch (one extra workgroup per request)
@@ -268,6 +280,9 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t s);
+
+// n_entries of request b := keep[b] / m in every cache of the layer
+hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, hipStream_t s);
 
 UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
                             const void* k_new, const void* v_new, const void* kI_new);

@@ -71,31 +71,32 @@ static void list_shape(int64_t R, bool span, int* n_lists, int* cap, int* span_l
   *cap = *span_len < kBins ? *span_len : kBins;   // at most min(bins, scores) entries
 }
 
-static IdxWs carve(void* ws, int nq, int64_t R, bool span, bool grouped = false) {
-  IdxWs w;
-  char* p = (char*)ws;
-  auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
-  list_shape(R, span, &w.n_lists, &w.list_cap, &w.list_span, grouped);
-  w.state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
-  w.hl_n = (int32_t*)take(sizeof(int32_t) * w.n_lists * nq);
-  w.hl = (uint32_t*)take(sizeof(uint32_t) * w.list_cap * w.n_lists * nq);
-  w.scores = (float*)take(sizeof(float) * R * nq);
-  w.bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
-  w.cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
-  w.cand2 = (uint64_t*)take(sizeof(uint64_t) * R * nq);
-  w.ccount = (int32_t*)take(sizeof(int32_t) * (R / kSelCH) * nq);
-  w.R = R;
-  return w;
+// The workspace layout, walked once for sizing (base == nullptr) and once for
+// carving, so the two can never disagree.  grouped: the draft scan's shape
+// (one histogram list per 512-block chunk at every row length).
+static size_t layout(char* base, int nq, int64_t R, bool span, bool grouped, IdxWs* w) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = base ? base + off : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return r;
+  };
+  list_shape(R, span, &w->n_lists, &w->list_cap, &w->list_span, grouped);
+  w->state = (int32_t*)take(sizeof(int32_t) * kStateInts * nq);
+  w->hl_n = (int32_t*)take(sizeof(int32_t) * w->n_lists * nq);
+  w->hl = (uint32_t*)take(sizeof(uint32_t) * w->list_cap * w->n_lists * nq);
+  w->scores = (float*)take(sizeof(float) * R * nq);
+  w->bitmap = (uint32_t*)take(sizeof(uint32_t) * (R / 32) * nq);
+  w->cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
+  w->cand2 = (uint64_t*)take(sizeof(uint64_t) * R * nq);
+  w->ccount = (int32_t*)take(sizeof(int32_t) * (R / kSelCH) * nq);
+  w->R = R;
+  return off;
 }
 
-static size_t carve_bytes(int nq, int64_t R, bool span) {
-  auto rnd = [](size_t b) { return (b + 255) & ~size_t(255); };
-  int n_lists, cap, span_len;
-  list_shape(R, span, &n_lists, &cap, &span_len);
-  return rnd(sizeof(int32_t) * kStateInts * nq) + rnd(sizeof(int32_t) * n_lists * nq) +
-         rnd(sizeof(uint32_t) * cap * n_lists * nq) + rnd(sizeof(float) * R * nq) +
-         rnd(sizeof(uint32_t) * (R / 32) * nq) + 2 * rnd(sizeof(uint64_t) * R * nq) +
-         rnd(sizeof(int32_t) * (R / kSelCH) * nq);
+static size_t carve_bytes(int nq, int64_t R, bool span, bool grouped) {
+  IdxWs w;
+  return layout(nullptr, nq, R, span, grouped, &w);
 }
 
 static int64_t host_nvis(int64_t t, int m, int n_win) {
@@ -104,10 +105,10 @@ static int64_t host_nvis(int64_t t, int m, int n_win) {
   return a < b ? a : b;
 }
 
-size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span) {
+size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span, int group) {
   (void)k;
   int nq = span ? (n_q < kSpanQC ? n_q : kSpanQC) : n_q;
-  return carve_bytes(nq, row_cap(max_nvis), span);
+  return carve_bytes(nq, row_cap(max_nvis), span, !span && group > 1);
 }
 
 // decode rows up to 2^21 visible blocks (an 8M-token context at m = 4)
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   // for one round trip.
   constexpr int BPW = kCH / NWV, PPW = BPW / kPage;
   static_assert(PPW >= 1, "a wave streams whole pages");
-  const int r = Q.pos ? (Q.req ? Q.req[qrow] : qrow) : Q.span_req;
+  const int r = Q.req_of(qrow, fault);
   int pid[CPW][PPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(256) void idx_scan_group_kernel(Queries Q, const u1
   const int q0 = blockIdx.y * G;
   const int c_first = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, row = lane & 15, g = lane >> 4;
-  const int r = Q.req ? Q.req[q0] : q0;
+  const int r = Q.req_of(q0, fault);
   int pid[2];
   {
     const int lp = (int)((((int64_t)c_first) * kCH + wv * (kCH / 4)) >> 6);
@@ -1252,18 +1253,22 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* wsp, size_t ws_bytes, hipStream_t s,
                           const UpdateArgs* upd, int group, bool s16) {
-  (void)ws_bytes;
   const bool span = q.req == nullptr && q.pos == nullptr;
   const int64_t nv_max = host_nvis(q.max_pos, m, n_win);
   const int64_t R = row_cap(nv_max);
   const unsigned n_chunks = (unsigned)(R / kCH);
   Paged kc = to_dev(kic);
-  Queries Qd = to_dev(q);
+  Queries Qd = to_dev(q, kic.n_req);
   int* fault = fault_word();
   if (s16 && group > 1) return hipErrorInvalidValue;   // drafts score in fp32
-  if (!span && group > 1 && !upd) {
+  // the layout this launch carves must fit the workspace it was given
+  IdxWs ws;
+  const int nq_ws = span ? (q.n < kSpanQC ? q.n : kSpanQC) : q.n;
+  const bool grouped = !span && group > 1 && !upd;
+  if (layout(nullptr, nq_ws, R, span, grouped, &ws) > ws_bytes) return hipErrorInvalidValue;
+  layout((char*)wsp, nq_ws, R, span, grouped, &ws);
+  if (grouped) {
     // a draft: groups of `group` queries of one request share each key pass
-    IdxWs ws = carve(wsp, q.n, R, false, true);
     const bool f8k = kic.dtype == HSA_FP8_E4M3;
     const dim3 grid(n_chunks, (unsigned)(q.n / group));
     auto scan = group == 4   ? (f8k ? idx_scan_group_kernel<4, true> : idx_scan_group_kernel<4, false>)
@@ -1276,7 +1281,6 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     return hipGetLastError();
   }
   if (!span) {
-    IdxWs ws = carve(wsp, q.n, R, false);
     const int cpw = scan_cpw(R);
     const unsigned n_groups = (n_chunks + cpw - 1) / cpw;
     const UpdateArgs ua = upd ? *upd : UpdateArgs{};
@@ -1307,8 +1311,7 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
       launch_topk<false>(1024, q.n, k, ws, idx, score, 0, s);
     return hipGetLastError();
   }
-  const int QC = q.n < kSpanQC ? q.n : kSpanQC;
-  IdxWs ws = carve(wsp, QC, R, true);
+  const int QC = nq_ws;
   for (int q0 = 0; q0 < q.n; q0 += QC) {
     const int nq = q.n - q0 < QC ? q.n - q0 : QC;
     // chunk-local maximum of the visible blocks bounds the work of this pass
