@@ -76,7 +76,8 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
     cap = n_win + draft - 1
     ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
-    tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda") if layer == "csa" else None
+    tail = (torch.zeros((B, m + draft - 1, 64), dtype=torch.bfloat16, device="cuda")
+            if layer == "csa" else None)
     inp = {"Q": [], "k_new": [], "v_new": [], "qI": [], "kI_new": [], "w": []}
 
     def bf(a):
@@ -94,7 +95,7 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
                               alpha["i"])
             t0 = nb * m
             if t0 < L:
-                tail[r, torch.arange(t0, L) % m] = bf(d["ki"][t0:L])
+                tail[r, torch.arange(t0, L) % tail.shape[1]] = bf(d["ki"][t0:L])
             inp["qI"].append(d["qi"][0] if draft == 1 else d["qi"][:draft])
             inp["kI_new"].append(d["ki"][L] if draft == 1 else d["ki"][L:L + draft])
             inp["w"].append(d["w"][0] if draft == 1 else d["w"][:draft])

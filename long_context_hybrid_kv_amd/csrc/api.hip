@@ -272,7 +272,7 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k) {
   if (!q || q->n < 1 || m < 1 || n_win < 1 || k < 1 || q->max_pos < 0) return 0;
-  return indexer_ws_bytes(q->n, nvis_host(q->max_pos, m, n_win), k, is_span(q));
+  return indexer_ws_bytes(q->n, nvis_host(q->max_pos, m, n_win), k, is_span(q), 1);
 }
 
 static hsa_status indexer_topk(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
@@ -423,7 +423,9 @@ static hsa_status check_decode(const hsa_layer* L, int32_t B, int32_t n_tok, con
   if (L->kind == HSA_LAYER_CSA) {
     REQ(qI && kI_new && w && L->alpha_i, "decode: CSA needs qI, kI_new, w and alpha_i");
     if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
-    if ((s = check_tokens(&L->tail_i, "tail_i", kDI, L->m)) != HSA_OK) return s;
+    // a draft's rejected tokens must not overwrite a kept token of the open
+    // block (hsa_decode_rewind): the tail holds m + n_tok - 1 rows
+    if ((s = check_tokens(&L->tail_i, "tail_i", kDI, L->m + n_tok - 1)) != HSA_OK) return s;
     REQ(L->kic.n_req >= B && L->tail_i.n_req >= B, "decode: kic holds fewer than B requests");
     REQ((int64_t)L->kic.pages_per_req * kPage >= pages_needed, "decode: kic table too short");
     SUP(L->H_I == kHI && L->d_I == kDI, "decode: H_I must be 4 and d_I 64");
@@ -470,8 +472,15 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   return hip_status(e, "decode_step attention");
 }
 
+// Draft queries of one request share the passes over its keys, up to four at
+// a time: the largest divisor of n_tok not above 4.
+static int draft_group(int n_tok) {
+  return n_tok % 4 == 0 ? 4 : n_tok % 3 == 0 ? 3 : n_tok % 2 == 0 ? 2 : 1;
+}
+
 // Workspace of a draft: the queries' positions and requests, then the
-// indexer's, the selection's and the attention's parts for B * n_tok queries.
+// indexer's (in the grouped scan's shape), the selection's and the
+// attention's parts for B * n_tok queries.
 static void draft_parts(const hsa_layer* L, int32_t B, int32_t n_tok, int64_t max_pos,
                         size_t* p_q, size_t* p_idx, size_t* p_sel, size_t* p_attn) {
   const size_t n = (size_t)B * n_tok;
@@ -483,7 +492,8 @@ static void draft_parts(const hsa_layer* L, int32_t B, int32_t n_tok, int64_t ma
   *p_q = rnd256(sizeof(int64_t) * n) + rnd256(sizeof(int32_t) * n);
   *p_idx = *p_sel = 0;
   if (L->kind == HSA_LAYER_CSA) {
-    *p_idx = rnd256(hsa_indexer_topk_workspace_bytes(&q, L->m, L->n_win, L->topk));
+    *p_idx = rnd256(indexer_ws_bytes((int)n, nvis_host(max_pos, L->m, L->n_win), L->topk, false,
+                                     draft_group(n_tok)));
     *p_sel = rnd256(sizeof(int32_t) * n * L->topk);
     *p_attn = rnd256(hsa_csa_attn_workspace_bytes(&q, L->H, L->n_win, L->topk));
   } else {
@@ -530,11 +540,8 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
   q.max_pos = max_pos;
   if (L->kind == HSA_LAYER_CSA) {
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_q + a_idx);
-    // draft queries of one request share the passes over its keys, up to four
-    // at a time (the largest divisor of n_tok not above 4)
-    const int group = n_tok % 4 == 0 ? 4 : n_tok % 3 == 0 ? 3 : n_tok % 2 == 0 ? 2 : 1;
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base + a_q,
-                       a_idx, stream, nullptr, group);
+                       a_idx, stream, nullptr, draft_group(n_tok));
     if (e != hipSuccess) return hip_status(e, "decode_draft indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_q + a_idx + a_sel, a_attn,
@@ -544,6 +551,25 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
                     L->scale, O, L->o_dtype, lse, base + a_q, a_attn, stream);
   }
   return hip_status(e, "decode_draft attention");
+}
+
+hsa_status hsa_decode_rewind(const hsa_layer* L, int32_t B, const int64_t* keep,
+                             hipStream_t stream) {
+  REQ(L, "decode_rewind: null layer");
+  REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode_rewind: unknown layer kind");
+  REQ(B >= 1 && keep, "decode_rewind: null keep or B < 1");
+  REQ(L->m >= 1, "decode_rewind: bad m");
+  SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
+      "decode_rewind: the caches must be bf16 (as hsa_decode_step and hsa_decode_draft append)");
+  hsa_status s;
+  if ((s = check_paged(&L->kc, "kc", kD, false)) != HSA_OK) return s;
+  if ((s = check_paged(&L->vc, "vc", kD, false)) != HSA_OK) return s;
+  REQ(L->kc.n_req >= B && L->vc.n_req >= B, "decode_rewind: caches hold fewer than B requests");
+  if (L->kind == HSA_LAYER_CSA) {
+    if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
+    REQ(L->kic.n_req >= B, "decode_rewind: kic holds fewer than B requests");
+  }
+  return hip_status(launch_decode_rewind(*L, B, keep, stream), "decode_rewind");
 }
 
 }  // extern "C"

@@ -134,6 +134,38 @@ __global__ __launch_bounds__(128) void decode_update_kernel(UpdateArgs u, int* f
   decode_update_body(u, blockIdx.x, fault);
 }
 
+// Rewind after a draft: request b keeps tokens 0 .. keep[b] - 1, so each of its
+// caches keeps the keep[b] / m blocks those tokens complete.  A request whose
+// keep lies outside [0, (n_entries + 1) * m) of any cache (more blocks than the
+// cache holds) is left as it is and raises a fault.
+__global__ void decode_rewind_kernel(const int64_t* __restrict__ keep, int B, int m, Paged kc,
+                                     Paged vc, Paged kic, int csa, int* fault) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int64_t p = keep[b];
+  if (p < 0) {
+    atomicOr(fault, HSA_FAULT_POS);
+    return;
+  }
+  const int64_t e = p / m;
+  const bool ok = e <= kc.n_entries[b] && e <= vc.n_entries[b] && (!csa || e <= kic.n_entries[b]);
+  if (!ok) {
+    atomicOr(fault, HSA_FAULT_ENTRIES);
+    return;
+  }
+  kc.n_entries[b] = (int32_t)e;
+  vc.n_entries[b] = (int32_t)e;
+  if (csa) kic.n_entries[b] = (int32_t)e;
+}
+
+hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, hipStream_t s) {
+  const int csa = L.kind == HSA_LAYER_CSA;
+  decode_rewind_kernel<<<(B + 255) / 256, 256, 0, s>>>(keep, B, L.m, to_dev(L.kc), to_dev(L.vc),
+                                                       csa ? to_dev(L.kic) : Paged{}, csa,
+                                                       fault_word());
+  return hipGetLastError();
+}
+
 UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
                             const void* k_new, const void* v_new, const void* kI_new) {
   const int csa = L.kind == HSA_LAYER_CSA;

@@ -177,3 +177,15 @@ def ragged_lengths(w: Workload) -> np.ndarray:
 def page_permutation(w: Workload, name: str, n_pages: int) -> np.ndarray:
     """A seeded shuffle of a pool of physical pages."""
     return rng(w.seed, f"pages.{name}").permutation(n_pages).astype(np.int32)
+
+
+def rejected_tokens(w: Workload, layer: str, r: int, n: int) -> dict:
+    """n draft tokens of request r that speculative decoding rejects: K, V (and
+    KI for CSA) rows from streams of their own, different from the request's
+    history at the same positions."""
+    s, d = w.seed, w.d
+    out = {"k": _normal_rows(s, f"{layer}.rej.k.{r}", n, (d,)),
+           "v": _normal_rows(s, f"{layer}.rej.v.{r}", n, (d,))}
+    if layer == "csa":
+        out["ki"] = _normal_rows(s, f"{layer}.rej.ki.{r}", n, (w.d_I,))
+    return out

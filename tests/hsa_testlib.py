@@ -104,10 +104,12 @@ def scale_of(d=128):
 # ----------------------------------------------------------------------------- decode state
 
 def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False,
-                kmix=False):
+                kmix=False, tail_cap=None):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
-    hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1).
+    hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)
+    and the indexer tail tail_cap tokens (default m; a draft of n tokens needs
+    m + n - 1).
     index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page).
     kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8."""
     B = len(Ls)
@@ -131,7 +133,8 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     if layer == "csa":
         st["alpha_i"] = L.pooling_weights(torch.from_numpy(z["zi"]).cuda())
         st["kic"] = cache(64, index_fp8)
-        tail = torch.zeros((B, m, 64), dtype=torch.bfloat16, device="cuda")
+        tcap = m if tail_cap is None else tail_cap
+        tail = torch.zeros((B, tcap, 64), dtype=torch.bfloat16, device="cuda")
     for r, d in enumerate(reqs):
         Lr = int(Ls[r])
         nb = Lr // m
@@ -145,7 +148,7 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
         ring_v[r, slots] = dev_bf16(d["v"][lo:Lr])
         if layer == "csa":
             t0 = nb * m
-            tail[r, torch.arange(t0, Lr) % m] = dev_bf16(d["ki"][t0:Lr])
+            tail[r, torch.arange(t0, Lr) % tail.shape[1]] = dev_bf16(d["ki"][t0:Lr])
     st["ring_k"], st["ring_v"] = L.Tokens(ring_k), L.Tokens(ring_v)
     if layer == "csa":
         st["tail_i"] = L.Tokens(tail)
@@ -188,3 +191,64 @@ def layer_of(w, layer, st):
     return L.Layer(**kw)
 
 
+
+
+# ----------------------------------------------------------------------------- bf16 index scores
+
+# The GPU's fp32 index score differs from the exact one by at most this many
+# fp32 unit roundoffs (2^-24) times A = sum_h w_h sum_c |qI[h][c] * KI[c]|:
+# a 64-term dot product in any summation order (63), the weight product (1),
+# the four-term head sum (3), with a margin.
+BF16_SCORE_ULPS = 80
+
+
+def score_abs_bound(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -> np.ndarray:
+    """A per block: the sum of the absolute values of the terms of its score."""
+    from oracle import numerics as nx
+    qa = np.abs(nx.bf16_value(qi_bits))                         # [H_I, d_I]
+    return (np.abs(kic_values) @ qa.T) @ np.asarray(w, dtype=np.float64)
+
+
+def check_topk_bf16(gpu_idx, gpu_score, exact, A, k, where=""):
+    """The exact rule for a selection over bf16-rounded scores.  The GPU rounds
+    its fp32 score, which lies within delta = BF16_SCORE_ULPS * 2^-24 * A of the
+    exact score, so its bf16 value lies in [bf16(exact - delta), bf16(exact +
+    delta)] -- a single value unless a rounding boundary falls inside.  The
+    selection passes iff it is exactly the top-k (ties to the lower block) for
+    some choice of values inside those brackets: every reported score lies in
+    its block's bracket, and every block left out can rank below the k-th
+    selected one (its bracket's low end is lower, or equal with a higher block
+    id).  Rows with no bracket wider than one value must equal the oracle's
+    selection exactly.  Returns whether the row equals the oracle's selection."""
+    from oracle import hybrid as orc
+    from oracle import numerics as nx
+    n = exact.shape[0]
+    n_sel = min(k, n)
+    g = gpu_idx[:n_sel]
+    assert np.all(gpu_idx[n_sel:] == -1), f"{where}: padding"
+    assert n_sel == 0 or (g.min() >= 0 and g.max() < n and np.all(np.diff(g) > 0)), \
+        f"{where}: ids not ascending and in range"
+    ref16 = nx.bf16_round_value(exact)
+    same = np.array_equal(g, orc.topk_blocks(ref16, k)[:n_sel])
+    if n_sel == 0:
+        return True
+    delta = BF16_SCORE_ULPS * 2.0 ** -24 * A
+    lo, hi = nx.bf16_round_value(exact - delta), nx.bf16_round_value(exact + delta)
+    s = gpu_score[:n_sel].astype(np.float64)
+    assert np.array_equal(nx.bf16_round_value(s), s), f"{where}: reported scores are not bf16 values"
+    bad = np.nonzero((s < lo[g]) | (s > hi[g]))[0]
+    assert bad.size == 0, f"{where}: {bad.size} reported scores outside their bracket, e.g. block {g[bad[0]]}"
+    if n_sel == n:
+        assert np.array_equal(g, np.arange(n)), f"{where}: must select all"
+        return True
+    # the k-th selected block by (score desc, id asc): the lowest score, highest id
+    t = s.min()
+    b_t = g[s == t].max()
+    out = np.ones(n, dtype=bool)
+    out[g] = False
+    u = np.nonzero(out)[0]
+    ok = (lo[u] < t) | ((lo[u] == t) & (u > b_t))
+    assert np.all(ok), f"{where}: {np.sum(~ok)} blocks left out that rank above the k-th, e.g. {u[~ok][:5]}"
+    if np.array_equal(lo, hi):
+        assert same, f"{where}: no score is near a rounding boundary, yet the selection differs"
+    return same

@@ -153,3 +153,71 @@ def test_workspace_sizes_are_consistent():
     b = lib.hsa_indexer_topk_workspace_bytes(C.byref(qs), 4, 128, 512)
     assert 0 < b < 8 << 30             # prefill is processed in query chunks
     assert lib.hsa_csa_attn_workspace_bytes(C.byref(qs), 64, 128, 512) == 0   # no split in prefill
+
+
+def _csa_layer(m=4, tail_cap=4, topk=1024, ring_cap=131):
+    Lr = L._Layer()
+    Lr.kind, Lr.H, Lr.d, Lr.n_win, Lr.m, Lr.topk, Lr.H_I, Lr.d_I = 0, 64, 128, 128, m, topk, 4, 64
+    Lr.scale = 0.088
+    Lr.alpha_k = Lr.alpha_v = Lr.alpha_i = 0x1000
+    Lr.ring_k = Lr.ring_v = L._Tokens(0x1000, ring_cap, 1, 128)
+    Lr.tail_i = L._Tokens(0x1000, tail_cap, 1, 64)
+    Lr.kc = Lr.vc = _paged(ppr=1 << 14)
+    Lr.kic = _paged(dim=64, ppr=1 << 14)
+    return Lr
+
+
+def test_decode_rewind_validation():
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    Lr = _csa_layer()
+    assert lib.hsa_decode_rewind(None, 1, f, None) == -1
+    assert lib.hsa_decode_rewind(C.byref(Lr), 0, f, None) == -1
+    assert lib.hsa_decode_rewind(C.byref(Lr), 1, None, None) == -1
+    assert lib.hsa_decode_rewind(C.byref(Lr), 2, f, None) == -1      # caches hold 1 request
+    Lr.kc = Lr.vc = _paged(dtype=L.FP8)
+    assert lib.hsa_decode_rewind(C.byref(Lr), 1, f, None) == -2
+
+
+def test_draft_needs_a_tail_for_rewinds():
+    """A CSA draft of n tokens needs an indexer tail of m + n - 1 rows: a
+    rejected token must not overwrite a kept token of the block still open."""
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    # a 16-byte workspace: a call that passes validation stops at the
+    # workspace check (-3) before anything is enqueued
+    call = lambda Lr, n_tok: lib.hsa_decode_draft(C.byref(Lr), 1, n_tok, f, 1000, f, f, f, f, f,
+                                                  f, f, None, None, f, 16, None)
+    assert call(_csa_layer(tail_cap=4), 4) == -1
+    assert b"tail_i" in lib.hsa_last_error()
+    assert call(_csa_layer(tail_cap=4 + 3), 4) == -3
+
+
+def _rnd(b):
+    return (b + 255) // 256 * 256
+
+
+def _grouped_indexer_bytes(nq, nvis):
+    """The draft scan's workspace layout: one histogram list of up to 512 bins
+    per 512-block chunk, fp32 scores, a bitmap, two candidate arrays and the
+    per-2048-block candidate counts, for nq queries over rows of R blocks."""
+    R = max(2048, -(-nvis // 2048) * 2048)
+    n_lists = R // 512
+    return (_rnd(4 * 8 * nq) + _rnd(4 * n_lists * nq) + _rnd(4 * 512 * n_lists * nq) +
+            _rnd(4 * R * nq) + _rnd(R // 8 * nq) + 2 * _rnd(8 * R * nq) + _rnd(4 * (R // 2048) * nq))
+
+
+@pytest.mark.parametrize("max_pos", [600_000, 1_048_579])
+def test_draft_workspace_covers_the_grouped_scan(max_pos):
+    """At rows of more than 131,072 blocks the single-query scan groups four
+    chunks per histogram list, the draft scan does not; a draft's workspace
+    must hold the draft scan's (larger) list layout."""
+    lib = L.lib()
+    B, n_tok, topk = 4, 4, 1024
+    Lr = _csa_layer(tail_cap=4 + n_tok - 1, topk=topk, ring_cap=128 + n_tok - 1)
+    n = B * n_tok
+    nvis = min(-(-max(0, max_pos - 127) // 4), (max_pos + 1) // 4)
+    q = L._Queries(n, C.c_void_p(0x1000), C.c_void_p(0x1000), 0, 0, max_pos)
+    attn = _rnd(lib.hsa_csa_attn_workspace_bytes(C.byref(q), 64, 128, topk))
+    need = _rnd(8 * n) + _rnd(4 * n) + _rnd(_grouped_indexer_bytes(n, nvis)) + _rnd(4 * n * topk) + attn
+    assert lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), B, n_tok, max_pos) >= need

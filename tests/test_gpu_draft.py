@@ -27,7 +27,8 @@ def test_draft_matches_oracle_and_caches(layer, n_tok):
     # HCA m = 128: 126 -> block at 127; 1021 -> block at 1023); 70,001 tokens:
     # 35 scan chunks and the long-row selection (over 16,384 blocks)
     Ls = [5, 126, 1000, 1021, 3000, 70001]
-    st = T.build_state(w, layer, Ls, steps=n_tok, ring_cap=w.n_win + n_tok - 1)
+    st = T.build_state(w, layer, Ls, steps=n_tok, ring_cap=w.n_win + n_tok - 1,
+                       tail_cap=w.m(layer) + n_tok - 1)
     lay = T.layer_of(w, layer, st)
     reqs = st["reqs"]
     B = len(Ls)

@@ -77,7 +77,8 @@ def test_csa_decode_128k_draft3_full():
     w = configs.CSA_DECODE_128K
     n_tok = 3
     Ls = [w.L] * w.B
-    st = T.build_state(w, "csa", Ls, steps=n_tok, shuffle=False, ring_cap=w.n_win + n_tok - 1)
+    st = T.build_state(w, "csa", Ls, steps=n_tok, shuffle=False, ring_cap=w.n_win + n_tok - 1,
+                       tail_cap=w.m_csa + n_tok - 1)
     lay = T.layer_of(w, "csa", st)
     reqs = st["reqs"]
     stack = lambda f: np.stack([np.stack([f(r, d, i) for i in range(n_tok)])

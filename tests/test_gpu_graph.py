@@ -80,7 +80,8 @@ def test_decode_draft_graph_replays():
     w = configs.shrink(configs.CSA_DECODE_128K, B=4)
     n_tok = 3
     Ls = [1000, 5000, 20000, 70000]        # L % 4 == 0: no block completes in L .. L+2
-    st = T.build_state(w, "csa", Ls, steps=n_tok, ring_cap=w.n_win + n_tok - 1)
+    st = T.build_state(w, "csa", Ls, steps=n_tok, ring_cap=w.n_win + n_tok - 1,
+                       tail_cap=w.m_csa + n_tok - 1)
     lay = T.layer_of(w, "csa", st)
     pos = torch.tensor(Ls, dtype=torch.int64, device="cuda")
     x = _step_inputs(st, Ls, n_tok)
