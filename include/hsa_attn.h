@@ -274,6 +274,25 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
                            void* O, float* lse, int32_t* idx_out,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as hsa_decode_step, arguments and results alike, with its workspace
+ * taken from the library's own device scratch of HSA_NOALLOC_SCRATCH_BYTES
+ * (one copy per GPU, held until the process ends) instead of a caller buffer.
+ * A step whose hsa_decode_step_workspace_bytes() exceeds it returns
+ * HSA_ERR_WORKSPACE and enqueues nothing (128 MiB covers 16 requests at 1M
+ * tokens).  The call allocates nothing and does not synchronise.  Every call
+ * on one GPU shares that GPU's scratch (the step needs it cleared of nothing:
+ * it writes whatever it later reads), so calls that may overlap on one GPU
+ * -- on different streams, or from different threads -- race; serialise them
+ * or use hsa_decode_step with workspaces of their own. */
+#define HSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+hsa_status hsa_decode_step_noalloc(const hsa_layer* L, int32_t B, const int64_t* pos,
+                                   int64_t max_pos, const void* Q, const void* k_new,
+                                   const void* v_new, const void* qI, const void* kI_new,
+                                   const float* w, void* O, float* lse, int32_t* idx_out,
+                                   hipStream_t stream);
+
 /* A draft of n_tok tokens per request for speculative decoding (the draft's
  * queries are verified together; wiki §11.4 for the caches kept in sync).
  * Tokens pos[b] .. pos[b]+n_tok-1 of request b are appended in order, as

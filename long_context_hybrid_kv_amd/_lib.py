@@ -95,6 +95,10 @@ _SIGS = {
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_size_t, C.c_void_p]),
+    "hsa_decode_step_noalloc": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_void_p, C.c_int64,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                          C.c_void_p, C.c_void_p]),
     "hsa_decode_rewind": (C.c_int, [C.POINTER(_Layer), C.c_int32, C.c_void_p, C.c_void_p]),
     "hsa_decode_draft_workspace_bytes": (C.c_size_t, [C.POINTER(_Layer), C.c_int32, C.c_int32,
                                                       C.c_int64]),
@@ -453,3 +457,17 @@ def decode_rewind(layer: Layer, keep: torch.Tensor) -> None:
     Lc = layer.c()
     _check(lib().hsa_decode_rewind(C.byref(Lc), keep.shape[0], _ptr(keep), _stream()),
            "decode_rewind")
+
+
+def decode_step_noalloc(layer: Layer, pos: torch.Tensor, max_pos: int, Q: torch.Tensor,
+                        k_new: torch.Tensor, v_new: torch.Tensor, qI=None, kI_new=None, w=None,
+                        O: torch.Tensor = None, lse: Optional[torch.Tensor] = None,
+                        idx: Optional[torch.Tensor] = None):
+    """hsa_decode_step_noalloc: the caller passes every output buffer (O
+    [B, H, d], lse [B, H] or None, idx [B, topk] or None); the library's own
+    device scratch serves as the workspace."""
+    B = pos.shape[0]
+    Lc = layer.c()
+    _check(lib().hsa_decode_step_noalloc(C.byref(Lc), B, _ptr(pos), max_pos, _ptr(Q), _ptr(k_new),
+                                         _ptr(v_new), _ptr(qI), _ptr(kI_new), _ptr(w), _ptr(O),
+                                         _ptr(lse), _ptr(idx), _stream()), "decode_step_noalloc")

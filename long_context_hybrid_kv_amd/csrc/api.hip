@@ -25,6 +25,28 @@ int* fault_word() {
   return ptrs[dev];
 }
 
+// ---------------------------------------------------------------- allocation-free decode
+
+// Workspace of hsa_decode_step_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: host code uses only the address that
+// hipGetSymbolAddress returns for the current device (scratch_ptr()).
+static __device__ __align__(256) uint8_t scratch[HSA_NOALLOC_SCRATCH_BYTES];
+
+static void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 // ---------------------------------------------------------------- kernel timing
 
 struct TimerState {
@@ -570,6 +592,24 @@ hsa_status hsa_decode_rewind(const hsa_layer* L, int32_t B, const int64_t* keep,
     REQ(L->kic.n_req >= B, "decode_rewind: kic holds fewer than B requests");
   }
   return hip_status(launch_decode_rewind(*L, B, keep, stream), "decode_rewind");
+}
+
+hsa_status hsa_decode_step_noalloc(const hsa_layer* L, int32_t B, const int64_t* pos,
+                                   int64_t max_pos, const void* Q, const void* k_new,
+                                   const void* v_new, const void* qI, const void* kI_new,
+                                   const float* w, void* O, float* lse, int32_t* idx_out,
+                                   hipStream_t stream) {
+  const size_t need = hsa_decode_step_workspace_bytes(L, B, max_pos);
+  if (need > HSA_NOALLOC_SCRATCH_BYTES)
+    return fail(HSA_ERR_WORKSPACE,
+                "decode_step_noalloc: this step needs " + std::to_string(need) +
+                    " bytes of workspace, more than the library's " +
+                    std::to_string((size_t)HSA_NOALLOC_SCRATCH_BYTES) + "-byte scratch");
+  void* ws = scratch_ptr();
+  if (!ws) return fail(HSA_ERR_HIP, "decode_step_noalloc: no scratch address on this device");
+  // the decode workspace needs no clearing: every call writes what it reads
+  return hsa_decode_step(L, B, pos, max_pos, Q, k_new, v_new, qI, kI_new, w, O, lse, idx_out, ws,
+                         HSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -221,3 +221,21 @@ def test_draft_workspace_covers_the_grouped_scan(max_pos):
     attn = _rnd(lib.hsa_csa_attn_workspace_bytes(C.byref(q), 64, 128, topk))
     need = _rnd(8 * n) + _rnd(4 * n) + _rnd(_grouped_indexer_bytes(n, nvis)) + _rnd(4 * n * topk) + attn
     assert lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), B, n_tok, max_pos) >= need
+
+
+def test_noalloc_step_refuses_steps_beyond_its_scratch():
+    """A step whose workspace exceeds the library's 128 MiB scratch returns
+    HSA_ERR_WORKSPACE before anything is enqueued."""
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    Lr = _csa_layer(topk=1024)
+    Lr.kc = Lr.vc = _paged(ppr=1 << 16)
+    Lr.kic = _paged(dim=64, ppr=1 << 16)
+    B = 1
+    Lr.kc.n_req = Lr.vc.n_req = Lr.kic.n_req = 64
+    Lr.ring_k.n_req = Lr.ring_v.n_req = Lr.tail_i.n_req = 64
+    need = lib.hsa_decode_step_workspace_bytes(C.byref(Lr), 64, 4 << 20)
+    assert need > 128 << 20
+    assert lib.hsa_decode_step_noalloc(C.byref(Lr), 64, f, 4 << 20, f, f, f, f, f, f, f, None,
+                                       None, None) == -3
+    assert b"scratch" in lib.hsa_last_error()
