@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define HSA_ABI_VERSION 1
+#define HSA_ABI_VERSION 2
 
 typedef enum {
   HSA_OK = 0,
@@ -137,7 +137,22 @@ typedef struct {
   int32_t        dtype;         /* hsa_dtype: bf16 or fp8 (K, V, indexer keys);
                                    HSA_FP8_BF16_ROPE (K, with an fp8 V cache);
                                    HSA_FP4_E2M1_MX (indexer keys) */
+  double*        stash;         /* fp8 K / V caches that decoding appends to: float64
+                                   [n_req][128][dim], the exact (pooled, unrounded)
+                                   values of each request's last 128 entries, entry e
+                                   at row e mod 128; NULL otherwise (see below) */
 } hsa_paged;
+
+/* Appending to an fp8 cache.  A page's scale is amax/448 over its entries,
+ * so it is not final until the page is full.  The stash (part of the state
+ * cache of wiki §11.4) keeps the exact values of the page still filling: every
+ * append writes its entry's row and re-encodes that page from the stash with
+ * the scale of the entries it now holds, so a page's codes and scale always
+ * equal a from-scratch compression of exactly the entries present (the rule
+ * hsa_kv_compress applies to a final partial page).  hsa_kv_compress fills
+ * the stash rows of the last page it writes when the descriptor has one; 128
+ * rows (two pages) let hsa_decode_rewind restore a kept page even after a
+ * rejected draft started the next one. */
 
 /* The query tokens of a call.  Either a span (req == pos == NULL): n
  * consecutive positions span_pos0 .. span_pos0+n-1 of request span_req, or a

@@ -40,7 +40,7 @@ class _Paged(C.Structure):
     _fields_ = [("data", C.c_void_p), ("scale", C.c_void_p), ("page_table", C.c_void_p),
                 ("n_entries", C.c_void_p), ("n_req", C.c_int32), ("pages_per_req", C.c_int32),
                 ("n_pages", C.c_int32), ("page_size", C.c_int32), ("dim", C.c_int32),
-                ("dtype", C.c_int32)]
+                ("dtype", C.c_int32), ("stash", C.c_void_p)]
 
 
 class _Queries(C.Structure):
@@ -167,6 +167,7 @@ class PagedCache:
     scale: Optional[torch.Tensor] = None
     mixed: bool = False
     fp4: bool = False
+    stash: Optional[torch.Tensor] = None    # fp8 caches appended to: float64 [n_req, 128, dim]
 
     @property
     def dtype(self) -> int:
@@ -185,10 +186,12 @@ class PagedCache:
     @staticmethod
     def allocate(n_req: int, max_entries: int, dim: int, fp8: bool = False,
                  page_order: Optional[torch.Tensor] = None, device="cuda",
-                 mixed: bool = False, fp4: bool = False) -> "PagedCache":
+                 mixed: bool = False, fp4: bool = False, stash: bool = False) -> "PagedCache":
         """mixed: HSA_FP8_BF16_ROPE rows (compressed K caches); fp4:
         HSA_FP4_E2M1_MX rows (indexer keys) with `scale` the e8m0 block-scale
-        bytes [n_pages, 64, dim / 32]."""
+        bytes [n_pages, 64, dim / 32]; stash (fp8 and mixed): the float64
+        values of each request's last 128 entries, which decoding needs to
+        append to an fp8 cache."""
         ppr = max(1, -(-max_entries // 64))
         n_pages = n_req * ppr
         if mixed:
@@ -206,15 +209,19 @@ class PagedCache:
         else:
             scale = (torch.ones(n_pages, dtype=torch.float32, device=device) if fp8 or mixed
                      else None)
+        st = (torch.zeros((n_req, 128, dim), dtype=torch.float64, device=device)
+              if stash and (fp8 or mixed) else None)
         return PagedCache(data, table.contiguous(),
-                          torch.zeros(n_req, dtype=torch.int32, device=device), scale, mixed, fp4)
+                          torch.zeros(n_req, dtype=torch.int32, device=device), scale, mixed, fp4,
+                          st)
 
     def c(self) -> _Paged:
         n_pages, ps, _ = self.data.shape
         n_req, ppr = self.page_table.shape
         return _Paged(self.data.data_ptr(), None if self.scale is None else self.scale.data_ptr(),
                       self.page_table.data_ptr(), self.n_entries.data_ptr(), n_req, ppr, n_pages,
-                      ps, self.dim, self.dtype)
+                      ps, self.dim, self.dtype,
+                      None if self.stash is None else self.stash.data_ptr())
 
     def logical(self, r: int, n: Optional[int] = None) -> torch.Tensor:
         """Entries 0..n-1 of request r in logical order (a gather, for inspection)."""

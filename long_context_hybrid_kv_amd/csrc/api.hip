@@ -382,6 +382,18 @@ hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                     "hca_attn");
 }
 
+// The compressed K / V caches a decode step, draft or rewind may append to:
+// both bf16, or fp8 (a mixed K with an fp8 V, or both fp8) with a stash each.
+static hsa_status check_append_caches(const hsa_layer* L, const std::string& who) {
+  const int kt = L->kc.dtype, vt = L->vc.dtype;
+  const bool bf = kt == HSA_BF16 && vt == HSA_BF16;
+  const bool f8 = (kt == HSA_FP8_E4M3 || kt == HSA_FP8_BF16_ROPE) && vt == HSA_FP8_E4M3;
+  SUP(bf || f8, who + ": K / V caches must be both bf16, or fp8 (K fp8 or mixed, V fp8)");
+  REQ(bf || (L->kc.stash && L->vc.stash),
+      who + ": appending to fp8 caches needs their stashes (the exact values of the open page)");
+  return HSA_OK;
+}
+
 // decode_step workspace: [indexer][selected ids][attention], 256-byte aligned
 static size_t rnd256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -422,8 +434,10 @@ static hsa_status check_decode(const hsa_layer* L, int32_t B, int32_t n_tok, con
   REQ(n_tok >= 1 && n_tok <= 256, "decode: n_tok must be in [1, 256]");
   REQ(L->alpha_k && L->alpha_v, "decode: null pooling weights");
   REQ(L->o_dtype == HSA_BF16 || L->o_dtype == HSA_FP32, "decode: o_dtype must be bf16 or fp32");
-  SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
-      "decode: appending to fp8 caches is not supported (page scales are set per page)");
+  {
+    hsa_status sa = check_append_caches(L, "decode");
+    if (sa != HSA_OK) return sa;
+  }
   REQ(L->kc.n_req >= B && L->vc.n_req >= B && L->ring_k.n_req >= B && L->ring_v.n_req >= B,
       "decode: caches hold fewer than B requests");
   REQ(L->n_win >= 1 && L->m >= 1 && L->m <= L->n_win, "decode: need 1 <= m <= n_win");
@@ -581,11 +595,10 @@ hsa_status hsa_decode_rewind(const hsa_layer* L, int32_t B, const int64_t* keep,
   REQ(L->kind == HSA_LAYER_CSA || L->kind == HSA_LAYER_HCA, "decode_rewind: unknown layer kind");
   REQ(B >= 1 && keep, "decode_rewind: null keep or B < 1");
   REQ(L->m >= 1, "decode_rewind: bad m");
-  SUP(L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16,
-      "decode_rewind: the caches must be bf16 (as hsa_decode_step and hsa_decode_draft append)");
   hsa_status s;
-  if ((s = check_paged(&L->kc, "kc", kD, false)) != HSA_OK) return s;
-  if ((s = check_paged(&L->vc, "vc", kD, false)) != HSA_OK) return s;
+  if ((s = check_paged(&L->kc, "kc", kD, true, true)) != HSA_OK) return s;
+  if ((s = check_paged(&L->vc, "vc", kD, true)) != HSA_OK) return s;
+  if ((s = check_append_caches(L, "decode_rewind")) != HSA_OK) return s;
   REQ(L->kc.n_req >= B && L->vc.n_req >= B, "decode_rewind: caches hold fewer than B requests");
   if (L->kind == HSA_LAYER_CSA) {
     if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;

@@ -141,12 +141,18 @@ __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int n_win) {
 
 // ---------------------------------------------------------------- descriptors passed by value
 
+constexpr int kStashRows = 128;   // stash rows per request (entry e at e mod 128)
+
 struct Paged {
   uint8_t* data;
   float* scale;
   const int32_t* page_table;
   int32_t* n_entries;
   int32_t pages_per_req, n_pages, dim, dtype;
+  double* stash;        // fp8 caches appended to: [n_req][kStashRows][dim] exact values, or null
+  __device__ __forceinline__ double* stash_row(int r, int64_t e) const {
+    return stash + ((int64_t)r * kStashRows + (e & (kStashRows - 1))) * dim;
+  }
   // bytes of one entry's row: dim elements, (HSA_FP8_BF16_ROPE) dim/2 fp8
   // codes followed by dim/2 bf16 channels, or (HSA_FP4_E2M1_MX) dim/2 bytes of
   // e2m1 nibbles
@@ -214,7 +220,7 @@ struct Queries {
 
 inline Paged to_dev(const hsa_paged& p) {
   return Paged{(uint8_t*)p.data, p.scale, p.page_table, p.n_entries, p.pages_per_req,
-               p.n_pages, p.dim, p.dtype};
+               p.n_pages, p.dim, p.dtype, p.stash};
 }
 inline Tokens to_dev(const hsa_tokens& t) { return Tokens{(uint8_t*)t.data, t.capacity, t.dim}; }
 inline Queries to_dev(const hsa_queries& q, int n_req) {

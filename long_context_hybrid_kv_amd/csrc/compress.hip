@@ -4,8 +4,18 @@
 //
 // Pooling is accumulated in float64: each product of an fp32 weight and a bf16
 // token is exact there, so the entry is rounded only once, into the cache type.
-// The work is a streaming read of the tokens (HBM-bound); float64 FMA runs at
-// the same rate as fp32 on gfx950, so it costs nothing here.
+// The work is a streaming read of the tokens (HBM-bound): m float64 FMAs per
+// 2-byte token value, far below gfx950's vector float64 rate (half its fp32
+// rate) at the bandwidth the reads allow.
+//
+// Layout of the work: a lane pools two adjacent channels of one entry, so a
+// wave reads one whole 256-byte token row per load instruction (dim 128; two
+// 128-byte rows, one per entry, for dim 64) and the slot loop's loads are all
+// in flight together.  Formats without a page-wide scale (bf16, fp4 with its
+// 32-channel blocks) give every entry its own wave(s) -- 1,024 waves for the
+// 128K-token HCA layer, 32,768 for the CSA layer; fp8 formats, whose page
+// scale depends on all 64 entries of a page, give each page one workgroup of
+// 16 waves (4 entries each) and reduce the page amax in LDS.
 #include "update.h"
 
 namespace hsa {
@@ -28,101 +38,135 @@ hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, 
   return hipGetLastError();
 }
 
-// One workgroup per cache page touched by [first, first + n).  Each thread owns
-// the (entry, channel) items idx = tid, tid + 256, ... of the page; consecutive
-// threads read consecutive channels of a token row (coalesced).
-// FMT: HSA_BF16, HSA_FP8_E4M3 (every channel fp8, page scale over all of
-// them), HSA_FP8_BF16_ROPE (channels below dim/2 fp8 with a page scale over
-// those channels, the RoPE channels above them bf16) or HSA_FP4_E2M1_MX (dim
-// 64: e2m1 nibbles with a power-of-two scale per 32-channel block)
-template <int FMT, int MAXV>
-__global__ __launch_bounds__(256) void compress_kernel(Tokens x, int x_req, int req, int64_t first,
-                                                       int64_t n, int m,
-                                                       const float* __restrict__ alpha,
-                                                       Paged out, int* fault) {
+// Pooled value (float64, slot order) of channels c and c + 1 of entry e: the
+// entry's m token rows are consecutive positions e*m .. e*m+m-1 of request
+// x_req (row = position mod capacity, wrapped without a division per row).
+__device__ __forceinline__ void pool2(const Tokens& x, int x_req, int64_t e, int m,
+                                      const float* __restrict__ alpha, int dim, int c,
+                                      double* s0, double* s1) {
+  const int64_t cap = x.capacity;
+  int64_t p = (e * m) % cap;
+  const uint32_t* base = (const uint32_t*)((const u16*)x.data + (int64_t)x_req * cap * dim + c);
+  const int64_t stride = dim / 2;              // 32-bit words per row
+  double a0 = 0.0, a1 = 0.0;
+#pragma unroll 16
+  for (int j = 0; j < m; ++j) {
+    const uint32_t v = __builtin_nontemporal_load(base + p * stride);
+    const float2 al = *(const float2*)(alpha + (int64_t)j * dim + c);
+    // each product is exact in float64, so contraction into an FMA changes nothing
+    a0 += (double)al.x * (double)__uint_as_float(v << 16);
+    a1 += (double)al.y * (double)__uint_as_float(v & 0xFFFF0000u);
+    p = p + 1 == cap ? 0 : p + 1;
+  }
+  *s0 = a0;
+  *s1 = a1;
+}
+
+// Entries [first, first + n) without a page-wide scale: HSA_BF16 (dim 128 or
+// 64) and HSA_FP4_E2M1_MX (dim 64, power-of-two scale per 32-channel block).
+// Lanes per entry L = dim / 2; a wave holds 64 / L entries; a 256-thread
+// workgroup 4 * 64 / L of them.
+template <int FMT>
+__global__ __launch_bounds__(256) void compress_rows_kernel(Tokens x, int x_req, int req,
+                                                            int64_t first, int64_t n, int m,
+                                                            const float* __restrict__ alpha,
+                                                            Paged out, int* fault) {
   const int dim = out.dim;
+  const int lpe = dim / 2;                     // lanes per entry
+  const int lane = threadIdx.x & 63;
+  const int per_wg = 256 / lpe;
+  const int64_t i = (int64_t)blockIdx.x * per_wg + threadIdx.x / lpe;
+  if (blockIdx.x == 0 && threadIdx.x == 0) out.n_entries[req] = (int32_t)(first + n);
+  if (i >= n) return;
+  const int64_t e = first + i;
+  const int c = 2 * (lane % lpe);
+  double v0, v1;
+  pool2(x, x_req, e, m, alpha, dim, c, &v0, &v1);
+  const int page = out.page_of(req, e, fault);
+  if (FMT == HSA_FP4_E2M1_MX) {
+    // the 32-channel block of these channels spans 16 lanes: its amax, the
+    // power-of-two scale 2^x, x = floor(log2 amax) - 2, then two e2m1 codes
+    double a = fmax(fabs(v0), fabs(v1));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) a = fmax(a, __shfl_xor(a, o));
+    int E;
+    (void)frexp(a, &E);                        // a = f * 2^E, f in [0.5, 1)
+    int xs = a > 0.0 ? E - 3 : 0;
+    xs = xs < -127 ? -127 : (xs > 127 ? 127 : xs);
+    const double inv = ldexp(1.0, -xs);        // exact scaling
+    const uint32_t code = f64_to_e2m1(v0 * inv) | (f64_to_e2m1(v1 * inv) << 4);
+    if (page < 0) return;
+    out.row(page, e)[c / 2] = (uint8_t)code;
+    if ((c & 31) == 0)
+      ((uint8_t*)out.scale)[((int64_t)page * kPage + (e & 63)) * (dim / 32) + c / 32] =
+          (uint8_t)(xs + 127);
+    return;
+  }
+  if (page < 0) return;
+  ((uint32_t*)out.row(page, e))[c / 2] = (uint32_t)f64_to_bf16(v0) | ((uint32_t)f64_to_bf16(v1) << 16);
+}
+
+// Entries of formats with a page-wide fp32 scale: HSA_FP8_E4M3 (dim 128 or 64;
+// scale over every channel) and HSA_FP8_BF16_ROPE (dim 128; scale over the
+// fp8 channels 0 .. dim/2-1, the RoPE channels stored bf16).  One 1024-thread
+// workgroup per page touched by [first, first + n) (the host requires a page
+// aligned first); each of its 16 waves pools 4 of the page's 64 entries (dim
+// 128: one entry per wave at a time; dim 64: two).  The page scale
+// = amax / 448 over the entries this call writes.
+template <int FMT>
+__global__ __launch_bounds__(1024) void compress_page_kernel(Tokens x, int x_req, int req,
+                                                             int64_t first, int64_t n, int m,
+                                                             const float* __restrict__ alpha,
+                                                             Paged out, int* fault) {
+  const int dim = out.dim;
+  const int lpe = dim / 2;
+  const int epw = 64 / lpe;                    // entries a wave pools at once
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t page_e0 = ((first >> 6) + blockIdx.x) << 6;
-  const int64_t e_lo = page_e0 > first ? page_e0 : first;
   const int64_t e_hi = (page_e0 + kPage) < (first + n) ? (page_e0 + kPage) : (first + n);
   const int page = out.page_of(req, page_e0, fault);
   if (blockIdx.x == 0 && threadIdx.x == 0) out.n_entries[req] = (int32_t)(first + n);
-  if (page < 0) return;
-
-  const int items = kPage * dim;
-  double vals[MAXV];
+  const int c = 2 * (lane % lpe);
+  constexpr int kMaxIt = 4;                    // 64 entries / 16 waves, dim 128
+  double v[kMaxIt][2];
   double amax = 0.0;
+  const int n_it = 4 / epw;
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    int it = threadIdx.x + v * 256;
-    vals[v] = 0.0;
-    if (it >= items) continue;
-    int64_t e = page_e0 + it / dim;
-    int c = it % dim;
-    if (e < e_lo || e >= e_hi) continue;
-    double acc = 0.0;
-    for (int j = 0; j < m; ++j) {
-      const u16* row = x.row(x_req, e * m + j);
-      acc += (double)alpha[(int64_t)j * dim + c] * (double)bf16_to_f32(row[c]);
-    }
-    vals[v] = acc;
-    if (FMT != HSA_FP8_BF16_ROPE || c < dim / 2) amax = fmax(amax, fabs(acc));
+  for (int it = 0; it < kMaxIt; ++it) {
+    v[it][0] = v[it][1] = 0.0;
+    if (it >= n_it) continue;
+    const int64_t e = page_e0 + (int64_t)(wv * 4 + it * epw + lane / lpe);
+    if (e >= e_hi) continue;
+    pool2(x, x_req, e, m, alpha, dim, c, &v[it][0], &v[it][1]);
+    if (FMT != HSA_FP8_BF16_ROPE || c < dim / 2) amax = fmax(amax, fmax(fabs(v[it][0]), fabs(v[it][1])));
+    // the last page written keeps its exact values for later appends
+    if (out.stash && blockIdx.x == gridDim.x - 1)
+      *(double2*)(out.stash_row(req, e) + c) = make_double2(v[it][0], v[it][1]);
   }
-  if (FMT == HSA_FP4_E2M1_MX) {
-    // dim 64: item it = entry * 64 + channel with it = tid + 256 v, so the 32
-    // channels of a block are 32 consecutive lanes of one wave (all of the same
-    // entry); the block's amax is a reduction over those lanes
-    uint8_t* sb = (uint8_t*)out.scale;
+  __shared__ double red[16];
 #pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-      const int it = threadIdx.x + v * 256;
-      double a = fabs(vals[v]);
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) a = fmax(a, __shfl_xor(a, o));
-      int E;
-      (void)frexp(a, &E);                       // a = f * 2^E, f in [0.5, 1)
-      int x = a > 0.0 ? E - 3 : 0;              // floor(log2 a) - 2
-      x = x < -127 ? -127 : (x > 127 ? 127 : x);
-      const uint32_t code = f64_to_e2m1(vals[v] * ldexp(1.0, -x));   // exact scaling
-      const uint32_t hi = __shfl_xor(code, 1);   // the odd channel's code
-      const int64_t e = page_e0 + it / dim;
-      const int c = it % dim;
-      if (it >= items || e < e_lo || e >= e_hi) continue;
-      if ((c & 1) == 0) out.row(page, e)[c / 2] = (uint8_t)(code | (hi << 4));
-      if ((c & 31) == 0) sb[((int64_t)page * kPage + (e & 63)) * (dim / 32) + c / 32] = (uint8_t)(x + 127);
-    }
-    return;
-  }
-  if (FMT == HSA_BF16) {
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-      int it = threadIdx.x + v * 256;
-      if (it >= items) continue;
-      int64_t e = page_e0 + it / dim;
-      if (e < e_lo || e >= e_hi) continue;
-      ((u16*)out.row(page, e))[it % dim] = f64_to_bf16(vals[v]);
-    }
-    return;
-  }
-  // fp8: page scale = amax / 448 over the entries written by this call
-  __shared__ double red[4];
   for (int o = 32; o > 0; o >>= 1) amax = fmax(amax, __shfl_xor(amax, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  if (lane == 0) red[wv] = amax;
   __syncthreads();
-  amax = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-  float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+  amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmax(amax, red[i]);
+  if (page < 0) return;
+  const float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
   if (threadIdx.x == 0) out.scale[page] = sc;
 #pragma unroll
-  for (int v = 0; v < MAXV; ++v) {
-    int it = threadIdx.x + v * 256;
-    if (it >= items) continue;
-    int64_t e = page_e0 + it / dim;
-    if (e < e_lo || e >= e_hi) continue;
-    const int c = it % dim;
+  for (int it = 0; it < kMaxIt; ++it) {
+    if (it >= n_it) continue;
+    const int64_t e = page_e0 + (int64_t)(wv * 4 + it * epw + lane / lpe);
+    if (e >= e_hi) continue;
     uint8_t* row = out.row(page, e);
-    if (FMT == HSA_FP8_BF16_ROPE && c >= dim / 2)
-      ((u16*)(row + dim / 2))[c - dim / 2] = f64_to_bf16(vals[v]);   // RoPE channel
-    else
-      row[c] = f64_to_e4m3(vals[v] / (double)sc);
+    if (FMT == HSA_FP8_BF16_ROPE && c >= dim / 2) {       // RoPE channels: bf16
+      ((uint32_t*)(row + dim / 2))[(c - dim / 2) / 2] =
+          (uint32_t)f64_to_bf16(v[it][0]) | ((uint32_t)f64_to_bf16(v[it][1]) << 16);
+    } else {
+      ((uint16_t*)row)[c / 2] = (uint16_t)(f64_to_e4m3(v[it][0] / (double)sc) |
+                                           ((uint32_t)f64_to_e4m3(v[it][1] / (double)sc) << 8));
+    }
   }
 }
 
@@ -137,32 +181,37 @@ __global__ __launch_bounds__(128) void decode_update_kernel(UpdateArgs u, int* f
 // Rewind after a draft: request b keeps tokens 0 .. keep[b] - 1, so each of its
 // caches keeps the keep[b] / m blocks those tokens complete.  A request whose
 // keep lies outside [0, (n_entries + 1) * m) of any cache (more blocks than the
-// cache holds) is left as it is and raises a fault.
-__global__ void decode_rewind_kernel(const int64_t* __restrict__ keep, int B, int m, Paged kc,
-                                     Paged vc, Paged kic, int csa, int* fault) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
+// cache holds) is left as it is and raises a fault.  fp8 K / V caches then
+// re-encode the page still filling from the stash, with the scale of the
+// entries they keep.  One 128-thread workgroup per request.
+__global__ __launch_bounds__(128) void decode_rewind_kernel(const int64_t* __restrict__ keep,
+                                                            int m, Paged kc, Paged vc, Paged kic,
+                                                            int csa, int* fault) {
+  const int b = blockIdx.x;
+  __shared__ double red[16];
   const int64_t p = keep[b];
-  if (p < 0) {
-    atomicOr(fault, HSA_FAULT_POS);
-    return;
-  }
-  const int64_t e = p / m;
-  const bool ok = e <= kc.n_entries[b] && e <= vc.n_entries[b] && (!csa || e <= kic.n_entries[b]);
+  const int64_t e = p < 0 ? 0 : p / m;
+  const bool ok = p >= 0 && e <= kc.n_entries[b] && e <= vc.n_entries[b] &&
+                  (!csa || e <= kic.n_entries[b]);
+  __syncthreads();   // every thread has read the counts before thread 0 rewrites them
   if (!ok) {
-    atomicOr(fault, HSA_FAULT_ENTRIES);
+    if (threadIdx.x == 0) atomicOr(fault, p < 0 ? HSA_FAULT_POS : HSA_FAULT_ENTRIES);
     return;
   }
-  kc.n_entries[b] = (int32_t)e;
-  vc.n_entries[b] = (int32_t)e;
-  if (csa) kic.n_entries[b] = (int32_t)e;
+  if (threadIdx.x == 0) {
+    kc.n_entries[b] = (int32_t)e;
+    vc.n_entries[b] = (int32_t)e;
+    if (csa) kic.n_entries[b] = (int32_t)e;
+  }
+  if (e % kPage == 0) return;   // no page is partly filled
+  if (kc.dtype != HSA_BF16) reencode_open_page(kc, b, e, false, fault, red);
+  if (vc.dtype != HSA_BF16) reencode_open_page(vc, b, e, false, fault, red);
 }
 
 hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, hipStream_t s) {
   const int csa = L.kind == HSA_LAYER_CSA;
-  decode_rewind_kernel<<<(B + 255) / 256, 256, 0, s>>>(keep, B, L.m, to_dev(L.kc), to_dev(L.vc),
-                                                       csa ? to_dev(L.kic) : Paged{}, csa,
-                                                       fault_word());
+  decode_rewind_kernel<<<B, 128, 0, s>>>(keep, L.m, to_dev(L.kc), to_dev(L.vc),
+                                         csa ? to_dev(L.kic) : Paged{}, csa, fault_word());
   return hipGetLastError();
 }
 
@@ -206,26 +255,23 @@ hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, i
 hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int64_t pages = ((first + n - 1) >> 6) - (first >> 6) + 1;
   Paged o = to_dev(out);
   Tokens t = to_dev(x);
   KernelTimer kt(HSA_K_COMPRESS, s);
-  const unsigned g = (unsigned)pages;
   int* f = fault_word();
-  if (out.dtype == HSA_FP4_E2M1_MX) {     // indexer keys: dim = kDI
-    compress_kernel<HSA_FP4_E2M1_MX, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
-  } else if (out.dtype == HSA_FP8_BF16_ROPE) {   // K caches: dim = kD
-    compress_kernel<HSA_FP8_BF16_ROPE, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
-  } else if (out.dtype == HSA_FP8_E4M3) {
-    if (out.dim == kD)
-      compress_kernel<HSA_FP8_E4M3, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+  if (out.dtype == HSA_FP8_E4M3 || out.dtype == HSA_FP8_BF16_ROPE) {
+    const unsigned g = (unsigned)(((first + n - 1) >> 6) - (first >> 6) + 1);
+    if (out.dtype == HSA_FP8_BF16_ROPE)
+      compress_page_kernel<HSA_FP8_BF16_ROPE><<<g, 1024, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
     else
-      compress_kernel<HSA_FP8_E4M3, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+      compress_page_kernel<HSA_FP8_E4M3><<<g, 1024, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   } else {
-    if (out.dim == kD)
-      compress_kernel<HSA_BF16, 32><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+    const int per_wg = 256 / (out.dim / 2);
+    const unsigned g = (unsigned)((n + per_wg - 1) / per_wg);
+    if (out.dtype == HSA_FP4_E2M1_MX)
+      compress_rows_kernel<HSA_FP4_E2M1_MX><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
     else
-      compress_kernel<HSA_BF16, 16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+      compress_rows_kernel<HSA_BF16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   }
   return hipGetLastError();
 }

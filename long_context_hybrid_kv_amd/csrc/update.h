@@ -40,6 +40,71 @@ __device__ __forceinline__ double pool_last(const Tokens& src, int r, int64_t bl
   return acc;
 }
 
+// Largest v over the workgroup (every thread calls it; red holds >= 16 doubles).
+__device__ __forceinline__ double block_max(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  __syncthreads();   // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double m = 0.0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = fmax(m, red[i]);
+  return m;
+}
+
+// Re-encode the page holding entries p0 .. ne-1 (p0 = the page's first entry,
+// ne > p0) of request b of an fp8 K / V cache from its stash: scale = amax /
+// 448 over those entries (the fp8 channels of a mixed K), codes = e4m3(value /
+// scale), the RoPE channels of a mixed K as bf16.  Thread c < kD carries
+// channel c; every thread of the workgroup calls it.  only_last: the caller
+// knows the page already holds entries p0 .. ne-2 encoded with some scale; if
+// the new scale equals it, only entry ne-1 is written.
+__device__ inline void reencode_open_page(const Paged& pc, int b, int64_t ne, bool only_last,
+                                          int* fault, double* red) {
+  const int c = threadIdx.x;
+  const bool on = c < kD;
+  const int64_t p0 = (ne - 1) & ~int64_t(kPage - 1);
+  const int pg = pc.page_of(b, p0, fault);
+  const bool scaled = on && (pc.dtype == HSA_FP8_E4M3 || c < kD / 2);
+  double amax = 0.0;
+  if (scaled)
+    for (int64_t e = p0; e < ne; ++e) amax = fmax(amax, fabs(pc.stash_row(b, e)[c]));
+  const float old = pg >= 0 ? pc.scale[pg] : 0.f;   // read before thread 0 rewrites it
+  amax = block_max(amax, red);
+  if (pg < 0) return;
+  const float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+  const int64_t e_lo = (only_last && sc == old) ? ne - 1 : p0;
+  if (on) {
+    for (int64_t e = e_lo; e < ne; ++e) {
+      const double v = pc.stash_row(b, e)[c];
+      uint8_t* row = pc.row(pg, e);
+      if (pc.dtype == HSA_FP8_BF16_ROPE && c >= kD / 2)
+        ((u16*)(row + kD / 2))[c - kD / 2] = f64_to_bf16(v);
+      else
+        row[c] = f64_to_e4m3(v / (double)sc);
+    }
+  }
+  if (c == 0) pc.scale[pg] = sc;
+}
+
+// Append entry blk (pooled value v of channel c, threads c < kD) to request b
+// of a compressed K or V cache: bf16 rounds it into its row; fp8 formats keep
+// the exact value in the stash and re-encode the open page.  Every thread of
+// the workgroup calls it.
+__device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, int* fault,
+                                 double* red) {
+  const int c = threadIdx.x;
+  if (pc.dtype == HSA_BF16) {
+    if (c < kD) {
+      const int pg = pc.page_of(b, blk, fault);
+      if (pg >= 0) ((u16*)pc.row(pg, blk))[c] = f64_to_bf16(v);
+    }
+    return;
+  }
+  if (c < kD) pc.stash_row(b, blk)[c] = v;
+  reencode_open_page(pc, b, blk + 1, (blk & (kPage - 1)) != 0, fault, red);
+}
+
 // Token i of request b (position pos[b] + i): write its K / V (and indexer
 // key) into the rings; when it completes a block, pool the block and append it
 // at n_entries.  Threads 0..127 of the workgroup carry the channels (a thread
@@ -77,12 +142,12 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
   }
   __syncthreads();
   if (!ok) return;
-  if (on) {
-    const int pk = u.kc.page_of(b, blk, fault), pv = u.vc.page_of(b, blk, fault);
-    if (pk >= 0)
-      ((u16*)u.kc.row(pk, blk))[c] = f64_to_bf16(pool_last(u.rk, b, blk, u.m, c, u.ak, kD, kn));
-    if (pv >= 0)
-      ((u16*)u.vc.row(pv, blk))[c] = f64_to_bf16(pool_last(u.rv, b, blk, u.m, c, u.av, kD, vn));
+  {
+    __shared__ double red[16];
+    const double vk = on ? pool_last(u.rk, b, blk, u.m, c, u.ak, kD, kn) : 0.0;
+    const double vv = on ? pool_last(u.rv, b, blk, u.m, c, u.av, kD, vn) : 0.0;
+    append_kv(u.kc, b, blk, vk, fault, red);
+    append_kv(u.vc, b, blk, vv, fault, red);
   }
   if (u.csa && c < kDI) {
     const int pi = u.kic.page_of(b, blk, fault);

@@ -104,12 +104,13 @@ def scale_of(d=128):
 # ----------------------------------------------------------------------------- decode state
 
 def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False,
-                kmix=False, tail_cap=None):
+                kmix=False, tail_cap=None, stash=False):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
     hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)
     and the indexer tail tail_cap tokens (default m; a draft of n tokens needs
-    m + n - 1).
+    m + n - 1).  stash: fp8 K / V caches carry the stash that appending to them
+    needs (hsa_kv_compress fills it for the last page).
     index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page).
     kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8."""
     B = len(Ls)
@@ -121,12 +122,14 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     max_entries = int(max(Ls)) // m + steps // m + 2
     ppr = -(-max_entries // 64)
     perm = (torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None)
-    def cache(dim, f8, mixed=False):
-        return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm, mixed=mixed)
+    def cache(dim, f8, mixed=False, st_=False):
+        return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm, mixed=mixed,
+                                     stash=st_)
     st = {"reqs": reqs, "z": z, "m": m}
     st["alpha_k"] = L.pooling_weights(torch.from_numpy(z["zk"]).cuda())
     st["alpha_v"] = L.pooling_weights(torch.from_numpy(z["zv"]).cuda())
-    st["kc"], st["vc"] = cache(128, fp8 or kmix, kmix), cache(128, fp8 or kmix)
+    st["kc"] = cache(128, fp8 or kmix, kmix, stash)
+    st["vc"] = cache(128, fp8 or kmix, False, stash)
     cap = n_win if ring_cap is None else ring_cap
     ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= set(L._SIGS), "binding misses a declared entry point"
-    assert lib.hsa_abi_version() == 1
+    assert lib.hsa_abi_version() == 2
 
 
 def test_status_strings():
@@ -106,7 +106,9 @@ def test_validation_rejects_before_any_launch():
     assert lib.hsa_csa_attn(C.byref(q), f, 16, 128, C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4, None, 64, 0.1, f, 0, None, f, 1 << 30, None) == -1
 
 
-def test_decode_step_rejects_fp8_append_and_bad_layers():
+def test_decode_step_fp8_append_rules_and_bad_layers():
+    """Appending to fp8 caches needs a stash per cache (the exact values of the
+    page still filling); K and V must be both bf16 or both fp8 (K may be mixed)."""
     lib = L.lib()
     f = C.c_void_p(0x1000)
     Lr = L._Layer()
@@ -114,8 +116,19 @@ def test_decode_step_rejects_fp8_append_and_bad_layers():
     Lr.scale = 0.088
     Lr.alpha_k = Lr.alpha_v = 0x1000
     Lr.ring_k = Lr.ring_v = L._Tokens(0x1000, 128, 1, 128)
-    Lr.kc = Lr.vc = _paged(dtype=1)
-    assert lib.hsa_decode_step(C.byref(Lr), 1, f, 1000, f, f, f, None, None, None, f, None, None, f, 1 << 30, None) == -2
+    # 10^6 tokens of context: 7,812 HCA entries need a split workspace, so a
+    # valid call stops at the (16-byte) workspace check before any launch
+    step = lambda ws=1 << 30: lib.hsa_decode_step(C.byref(Lr), 1, f, 10 ** 6, f, f, f, None,
+                                                   None, None, f, None, None, f, ws, None)
+    Lr.kc = Lr.vc = _paged(dtype=1, ppr=256)
+    assert step() == -1 and b"stash" in lib.hsa_last_error()
+    stashed = _paged(dtype=1, ppr=256)
+    stashed.stash = 0x1000
+    Lr.kc, Lr.vc = stashed, _paged(ppr=256)
+    assert step() == -2                       # fp8 K with a bf16 V
+    Lr.kc = Lr.vc = stashed
+    assert lib.hsa_decode_step_workspace_bytes(C.byref(Lr), 1, 10 ** 6) > 16
+    assert step(16) == -3                     # valid: stops at the workspace check
     Lr.kc = Lr.vc = _paged()
     Lr.kind = 7
     assert lib.hsa_decode_step(C.byref(Lr), 1, f, 1000, f, f, f, None, None, None, f, None, None, f, 1 << 30, None) == -1
@@ -176,7 +189,9 @@ def test_decode_rewind_validation():
     assert lib.hsa_decode_rewind(C.byref(Lr), 1, None, None) == -1
     assert lib.hsa_decode_rewind(C.byref(Lr), 2, f, None) == -1      # caches hold 1 request
     Lr.kc = Lr.vc = _paged(dtype=L.FP8)
-    assert lib.hsa_decode_rewind(C.byref(Lr), 1, f, None) == -2
+    assert lib.hsa_decode_rewind(C.byref(Lr), 1, f, None) == -1     # fp8 without stashes
+    Lr.kc = _paged()
+    assert lib.hsa_decode_rewind(C.byref(Lr), 1, f, None) == -2     # bf16 K, fp8 V
 
 
 def test_draft_needs_a_tail_for_rewinds():
