@@ -20,7 +20,10 @@
 // [2^-14, 65504] -- and the probabilities keep 10 fraction bits instead of 7,
 // which keeps the output error well inside what the bf16 output store adds.
 // Long decode rows are split over workgroups and merged through (max, sum,
-// partial O) in the workspace.
+// normalized partial O) in the workspace: a split stores o = O / sum in fp16
+// (|o| <= max |v|, which the fp16 V staging already bounds), halving the
+// partial traffic; a decode query whose entries fit one split divides exactly
+// as the merge does, so its bits do not depend on the batch around it.
 #include <type_traits>
 
 #include "common.h"
@@ -44,8 +47,8 @@ struct AttnArgs {
   void* O;
   int o_f32;             // 1: fp32 output, 0: bf16
   float* lse;
-  float* part_o;
-  float* part_ml;
+  u16* part_o;           // fp16 [n][splits][H][128]: o = O / sum of the split
+  float* part_ml;        // [n][splits][H][2]: (max, sum)
   int n_splits, cps, n_hg, n_q;
   int xcd;               // 1: keep consecutive queries on one XCD (prefill)
   int* fault;
@@ -577,34 +580,47 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   check_finite(oacc, a.fault);
 
   // ---- epilogue: lane holds O^T[16dt + 4g + i][head]
+  // the split's normalized output, rounded to fp16 (0 for an empty split)
+  const bool nz = l_i > 0.f;
+  const bool listed_q = a.Q.pos != nullptr;
   if (a.n_splits == 1) {
-    // O / l, divided exactly as the merge divides: a query whose entries fit
-    // one split gets the same bits as when its launch has more splits (the
-    // others empty) and goes through the merge
+    // decode: (l * fp16(O / l)) / l, the merge's arithmetic for a query with one
+    // non-empty split, so a query's bits do not depend on its batch; prefill
+    // (spans, never split): O / l
     const int64_t o0 = ((int64_t)qi * a.H + head) * kD;
-    const bool nz = l_i > 0.f;
+    float ov[8][4];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o = nz ? oacc[dt][i] / l_i : 0.f;
+        const float o16 = (float)(_Float16)o;
+        ov[dt][i] = !listed_q ? o : (nz ? (l_i * o16) / l_i : 0.f);
+      }
     if (a.o_f32) {
       float* orow = (float*)a.O + o0;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *(f32x4*)(orow + 16 * dt + 4 * g) = nz ? oacc[dt] / l_i : f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(orow + 16 * dt + 4 * g) = f32x4{ov[dt][0], ov[dt][1], ov[dt][2], ov[dt][3]};
     } else {
       u16* orow = (u16*)a.O + o0;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         uint32_t b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          b[i] = __builtin_bit_cast(u16, (__bf16)(nz ? oacc[dt][i] / l_i : 0.f));
+        for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(u16, (__bf16)ov[dt][i]);
         *(uint2*)(orow + 16 * dt + 4 * g) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
     }
     if (g == 0 && a.lse) a.lse[(int64_t)qi * a.H + head] = (m_i + log2f(l_i)) * kLn2;
   } else {
     const int64_t slot = ((int64_t)qi * a.n_splits + split) * a.H + head;
-    float* po = a.part_o + slot * kD;
+    u16* po = a.part_o + slot * kD;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + 16 * dt + 4 * g) = oacc[dt];
+    for (int dt = 0; dt < 8; ++dt)
+      *(uint2*)(po + 16 * dt + 4 * g) =
+          make_uint2(pack_f16(nz ? oacc[dt][0] / l_i : 0.f, nz ? oacc[dt][1] / l_i : 0.f),
+                     pack_f16(nz ? oacc[dt][2] / l_i : 0.f, nz ? oacc[dt][3] / l_i : 0.f));
     if (g == 0) {
       a.part_ml[slot * 2 + 0] = m_i;
       a.part_ml[slot * 2 + 1] = l_i;
@@ -612,13 +628,14 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// The (m, l) of every split are staged in LDS first; the partial rows are then
-// read with all loads of a thread in flight.
+// Merge split partials: O = sum_s w_s o_s / sum_s w_s, w_s = 2^(m_s - M) l_s,
+// with o_s the split's normalized fp16 output.  The (m, l) of every split are
+// staged in LDS first; the partial rows are then read with all loads of a
+// thread in flight.
 constexpr int kMergeMaxSplits = 1024;
 constexpr int kMergePF = 32;          // partial outputs a merge thread requests up front
 __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
-                                                         const float* __restrict__ part_o,
+                                                         const u16* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          void* __restrict__ O, int o_f32,
                                                          float* __restrict__ lse, int* fault) {
@@ -629,11 +646,11 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
   const int ns = n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits;
   // the first kMergePF partial outputs, the (max, sum) pairs and the rest are
   // all requested before anything waits on them: one memory round trip
-  const float* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
+  const u16* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
   const int64_t stride = (int64_t)H * kD;
-  float v[kMergePF];
+  u16 v[kMergePF];
 #pragma unroll
-  for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : 0.f;
+  for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : (u16)0;
   float mloc = -INFINITY;
   for (int s = d; s < ns; s += 128) {
     const float2 ml = *(const float2*)&part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
@@ -648,19 +665,20 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
   __syncthreads();
   float lloc = 0.f;
   for (int s = d; s < ns; s += 128) {
-    const float wv = exp2f(wgt[s] - M);
-    wgt[s] = wv;
-    lloc += wv * lsm[s];
+    const float wl = exp2f(wgt[s] - M) * lsm[s];
+    wgt[s] = wl;
+    lloc += wl;
   }
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
   if ((d & 63) == 0) red[d >> 6] = lloc;
   __syncthreads();
   const float L = red[0] + red[1];
+  auto f16v = [](u16 x) { return (float)__builtin_bit_cast(_Float16, x); };
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < kMergePF; ++j)
-    if (j < ns) acc += wgt[j] * v[j];
-  for (int s = kMergePF; s < ns; ++s) acc += wgt[s] * po[s * stride];
+    if (j < ns) acc += wgt[j] * f16v(v[j]);
+  for (int s = kMergePF; s < ns; ++s) acc += wgt[s] * f16v(po[s * stride]);
   const float o = L > 0.f ? acc / L : 0.f;
   if (!__builtin_isfinite(o)) atomicOr(fault, HSA_FAULT_RANGE);
   if (o_f32)
@@ -957,7 +975,9 @@ int attn_decode_cps(int k, int n_win) {
 static AttnPlan plan(int n_q, int H, int64_t max_entries, bool span, int decode_cps) {
   AttnPlan p;
   (void)n_q;
-  p.nw = (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
+  // decode with 128 heads: one 8-wave workgroup covers every head, so a
+  // split's rows are gathered once (two 4-wave head groups gathered them twice)
+  p.nw = (!span && H % 128 == 0) ? 8 : (H % 64 == 0) ? 4 : (H % 32 == 0) ? 2 : 1;
   p.n_hg = H / (16 * p.nw);
   const int64_t chunks = (max_entries + 63) / 64 > 0 ? (max_entries + 63) / 64 : 1;
   if (span) {
@@ -979,7 +999,8 @@ size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span, int decode_
   AttnPlan p = plan(n_q, H, max_entries, span, decode_cps);
   if (p.n_splits == 1) return 0;
   const size_t slots = (size_t)n_q * p.n_splits * H;
-  return slots * kD * sizeof(float) + ((slots * 2 * sizeof(float) + 255) & ~size_t(255)) + 256;
+  return ((slots * kD * sizeof(u16) + 255) & ~size_t(255)) +
+         ((slots * 2 * sizeof(float) + 255) & ~size_t(255)) + 256;
 }
 
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
@@ -1013,9 +1034,9 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.O = O;
   a.o_f32 = o_dtype == HSA_FP32;
   a.lse = lse;
-  a.part_o = (float*)ws;
+  a.part_o = (u16*)ws;
   const size_t slots = (size_t)q.n * p.n_splits * H;
-  a.part_ml = (float*)((char*)ws + ((slots * kD * sizeof(float) + 255) & ~size_t(255)));
+  a.part_ml = (float*)((char*)ws + ((slots * kD * sizeof(u16) + 255) & ~size_t(255)));
   a.n_splits = p.n_splits;
   a.cps = p.cps;
   a.n_hg = p.n_hg;
@@ -1049,6 +1070,11 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   // tiles; decode (few workgroups, latency first): two
   if (p.nw == 4 && span && !f8)
     timed_launch(HSA_K_ATTN, attn_kernel<4, false, true, false>, grid, dim3(256), pre, s, a);
+  else if (p.nw == 8)
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<8, true, false, true>
+                      : f8 ? attn_kernel<8, true, false, false> : attn_kernel<8, false, false, false>,
+                 grid, dim3(512), pre, s, a);
   else if (p.nw == 4)
     timed_launch(HSA_K_ATTN,
                  kmix ? attn_kernel<4, true, false, true>

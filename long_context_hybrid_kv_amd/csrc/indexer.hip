@@ -285,7 +285,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
                                                        int n_groups, UpdateArgs upd, int* fault) {
   const int qrow = blockIdx.y;
   if ((int)blockIdx.x >= n_groups) {   // the extra column: cache upkeep of request qrow
-    decode_update_body(upd, qrow, fault);
+    decode_update_body<false>(upd, qrow, fault);   // bf16 caches only (the host's rule)
     return;
   }
   const int c_first = blockIdx.x * CPW;

@@ -88,13 +88,14 @@ __device__ inline void reencode_open_page(const Paged& pc, int b, int64_t ne, bo
 }
 
 // Append entry blk (pooled value v of channel c, threads c < kD) to request b
-// of a compressed K or V cache: bf16 rounds it into its row; fp8 formats keep
-// the exact value in the stash and re-encode the open page.  Every thread of
-// the workgroup calls it.
+// of a compressed K or V cache: bf16 rounds it into its row; fp8 formats (F8
+// only) keep the exact value in the stash and re-encode the open page.  Every
+// thread of the workgroup calls it.
+template <bool F8>
 __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, int* fault,
                                  double* red) {
   const int c = threadIdx.x;
-  if (pc.dtype == HSA_BF16) {
+  if (!F8 || pc.dtype == HSA_BF16) {
     if (c < kD) {
       const int pg = pc.page_of(b, blk, fault);
       if (pg >= 0) ((u16*)pc.row(pg, blk))[c] = f64_to_bf16(v);
@@ -110,7 +111,11 @@ __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, 
 // at n_entries.  Threads 0..127 of the workgroup carry the channels (a thread
 // writes and pools its own channel, so tokens of one request are handled in
 // order without cross-thread hand-off); every thread of the workgroup must call
-// this (it synchronises the workgroup).
+// this (it synchronises the workgroup).  F8: the K / V caches may be fp8 (the
+// standalone upkeep kernel); the indexer scan launch, which carries the upkeep
+// of bf16 CSA layers, is compiled without that path (its float64 page loops
+// would raise the scan's registers).
+template <bool F8>
 __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault) {
   const int c = threadIdx.x;
   const bool on = c < kD;
@@ -146,8 +151,8 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
     __shared__ double red[16];
     const double vk = on ? pool_last(u.rk, b, blk, u.m, c, u.ak, kD, kn) : 0.0;
     const double vv = on ? pool_last(u.rv, b, blk, u.m, c, u.av, kD, vn) : 0.0;
-    append_kv(u.kc, b, blk, vk, fault, red);
-    append_kv(u.vc, b, blk, vv, fault, red);
+    append_kv<F8>(u.kc, b, blk, vk, fault, red);
+    append_kv<F8>(u.vc, b, blk, vv, fault, red);
   }
   if (u.csa && c < kDI) {
     const int pi = u.kic.page_of(b, blk, fault);
@@ -164,9 +169,10 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
 
 // Request b's n_tok tokens in order, and (a draft) its queries' request and
 // position for the selection and attention that follow.
+template <bool F8>
 __device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault) {
   for (int i = 0; i < u.n_tok; ++i) {
-    decode_update_token(u, b, i, fault);
+    decode_update_token<F8>(u, b, i, fault);
     __syncthreads();   // the next token's block check reuses the shared flag
   }
   if (u.q_pos)
