@@ -490,18 +490,14 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   char* base = (char*)ws;
   hipError_t e;
   if (csa) {
-    // bf16 caches: the cache upkeep runs inside the indexer's scan launch (one
-    // workgroup per request beside the scan); fp8 caches (page re-encoding)
-    // take the standalone upkeep kernel first
-    const bool fused = L->kc.dtype == HSA_BF16 && L->vc.dtype == HSA_BF16;
+    // the cache upkeep rides in one of the indexer's launches (which one
+    // depends on the cache formats and the row length: launch_indexer); the
+    // block completed at pos starts inside the window, so no query of this
+    // step sees it and the scan never reads what the upkeep writes
     const UpdateArgs upd = make_update_args(*L, pos, max_pos, k_new, v_new, kI_new);
-    if (!fused) {
-      e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream);
-      if (e != hipSuccess) return hip_status(e, "decode_step update");
-    }
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base, a_idx,
-                       stream, fused ? &upd : nullptr);
+                       stream, &upd);
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
     e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_idx + a_sel, a_attn, stream);

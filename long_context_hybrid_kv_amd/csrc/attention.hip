@@ -392,45 +392,54 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   __syncthreads();
 
-  // ---- register double buffer of one chunk's rows.  K pieces: p = tid + NT*i
-  // is (entry p/16, column group p%16).  V pieces: this thread's entry pair
+  // ---- register buffers of a chunk's rows.  K pieces: p = tid + NT*i is
+  // (entry p/16, column group p%16).  V pieces: this thread's entry pair
   // (2*(tid%32), +1) in column groups tid/32 + (NT/32)*j, so that two entries
-  // share one 32-bit word of the transposed tile.
-  uint4 kraw[PPT], vraw[PPT];
-  int krow[PPT], vrow[PPT];
-  float kscl[PPT], vscl[PPT];
+  // share one 32-bit word of the transposed tile.  Decode keeps DEPTH = 2
+  // chunks of gathers in flight (chunk c + 2 loads while chunk c computes);
+  // prefill (SH) one, its registers going to occupancy instead.  The buffer
+  // index is always a compile-time constant (the chunk loop is unrolled by
+  // DEPTH), so the arrays stay in registers.
+  constexpr int DEPTH = (SH || NW < 4) ? 1 : 2;
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  uint4 kraw[DEPTH][PPT], vraw[DEPTH][PPT];
+  int krow[DEPTH][PPT], vrow[DEPTH][PPT];
+  float kscl[DEPTH][PPT], vscl[DEPTH][PPT];
   const int vpair = tid & 31;
-  auto issue_k = [&](int c) {
+  auto issue_k = [&](int c, auto bi) {
+    constexpr int b = decltype(bi)::value;
     const int lo = (c - c_lo) * 64;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
       if constexpr (F8) {
-        krow[i] = rowk[lo + ek];
-        kraw[i] = KMIX ? load_piece_kmix(a.kc, a.wk, krow[i], cgk)
-                       : load_piece<F8>(a.kc, a.wk, krow[i], cgk);
-        kscl[i] = row_scale<F8>(a.kc, krow[i]);
+        krow[b][i] = rowk[lo + ek];
+        kraw[b][i] = KMIX ? load_piece_kmix(a.kc, a.wk, krow[b][i], cgk)
+                          : load_piece<F8>(a.kc, a.wk, krow[b][i], cgk);
+        kscl[b][i] = row_scale<F8>(a.kc, krow[b][i]);
       } else {
-        krow[i] = 0;
-        kscl[i] = 1.f;
-        kraw[i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
+        krow[b][i] = 0;
+        kscl[b][i] = 1.f;
+        kraw[b][i] = gload16((uintptr_t)rowk[lo + ek] + cgk * 16);
       }
     }
   };
-  auto issue_v = [&](int c) {
+  auto issue_v = [&](int c, auto bi) {
+    constexpr int b = decltype(bi)::value;
     const int lo = (c - c_lo) * 64;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
       if constexpr (F8) {
-        vrow[i] = rowv[lo + ev];
-        vraw[i] = load_piece<F8>(a.vc, a.wv, vrow[i], cgv);
-        vscl[i] = row_scale<F8>(a.vc, vrow[i]);
+        vrow[b][i] = rowv[lo + ev];
+        vraw[b][i] = load_piece<F8>(a.vc, a.wv, vrow[b][i], cgv);
+        vscl[b][i] = row_scale<F8>(a.vc, vrow[b][i]);
       } else {
-        vrow[i] = 0;
-        vscl[i] = 1.f;
-        vraw[i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
+        vrow[b][i] = 0;
+        vscl[b][i] = 1.f;
+        vraw[b][i] = gload16((uintptr_t)rowv[lo + ev] + cgv * 16);
       }
     }
   };
@@ -444,13 +453,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
-  // V (transposed fp16) of the chunk in vraw -> Vt
-  auto stage_v = [&]() {
+  // V (transposed fp16) of the chunk in buffer b -> Vt
+  auto stage_v = [&](auto bi) {
+    constexpr int b = decltype(bi)::value;
 #pragma unroll
     for (int j = 0; j < PPT / 2; ++j) {
       const int cgv = (tid >> 5) + (NT / 32) * j;
-      const uint4 v0 = v_piece_f16(vraw[2 * j], F8 && vrow[2 * j] >= 0, vscl[2 * j]);
-      const uint4 v1 = v_piece_f16(vraw[2 * j + 1], F8 && vrow[2 * j + 1] >= 0, vscl[2 * j + 1]);
+      const uint4 v0 = v_piece_f16(vraw[b][2 * j], F8 && vrow[b][2 * j] >= 0, vscl[b][2 * j]);
+      const uint4 v1 =
+          v_piece_f16(vraw[b][2 * j + 1], F8 && vrow[b][2 * j + 1] >= 0, vscl[b][2 * j + 1]);
       const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
       uint32_t* vt = (uint32_t*)&Vt[cgv * 8][0] + vpair;
 #pragma unroll
@@ -461,29 +472,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   };
 
-  if (c_lo < c_hi) {
-    issue_k(c_lo);
-    issue_v(c_lo);
-  }
-  for (int c = c_lo; c < c_hi; ++c) {
+  // one chunk from buffer b; then buffer b receives chunk c + DEPTH
+  auto body = [&](int c, auto bi) {
+    constexpr int b = decltype(bi)::value;
     const int e0 = c * 64;
     // ---- stage K (row-major bf16), and V unless it waits for the K tile's reads
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + NT * i;
       const int ek = p >> 4, cgk = p & 15;
-      *(uint4*)&Ks[ek][cgk * 8] = k_piece_bf16(kraw[i], F8 && krow[i] >= 0 && (!KMIX || cgk < 8));
+      *(uint4*)&Ks[ek][cgk * 8] =
+          k_piece_bf16(kraw[b][i], F8 && krow[b][i] >= 0 && (!KMIX || cgk < 8));
       if constexpr (F8)   // page scale of each key row (bf16 rows need none)
-        if (cgk == 0) ksc[ek] = kscl[i];
+        if (cgk == 0) ksc[ek] = kscl[b][i];
     }
-    if constexpr (!SH) stage_v();
+    if constexpr (!SH) stage_v(bi);
     __syncthreads();
-    // next chunk's rows load while this one computes
-    if (c + 1 < c_hi) {
-      issue_k(c + 1);
-      if constexpr (!SH) issue_v(c + 1);
+    // chunk c + DEPTH loads while this one computes
+    if (c + DEPTH < c_hi) {
+      issue_k(c + DEPTH, bi);
+      if constexpr (!SH) issue_v(c + DEPTH, bi);
     }
-
     // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads).  KMIX:
     // the code channels (k-steps 0, 1) and the bf16 RoPE channels (2, 3)
     // accumulate apart, as only the codes take the page scale.
@@ -545,9 +554,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
     if constexpr (SH) {
       __syncthreads();   // every wave has read the K tile
-      stage_v();
+      stage_v(bi);
       __syncthreads();
-      if (c + 1 < c_hi) issue_v(c + 1);
+      if (c + DEPTH < c_hi) issue_v(c + DEPTH, bi);
     }
     // ---- O^T += V^T P^T, two k-steps of 32 entries.  P is rounded to fp16
     // once; an extra tile of ones in place of V^T rows accumulates the row
@@ -575,6 +584,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, osum, 0, 0, 0);
     }
     __syncthreads();
+  };
+
+  if (c_lo < c_hi) {
+    issue_k(c_lo, B0{});
+    issue_v(c_lo, B0{});
+  }
+  if constexpr (DEPTH == 2) {
+    if (c_lo + 1 < c_hi) {
+      issue_k(c_lo + 1, B1{});
+      issue_v(c_lo + 1, B1{});
+    }
+    for (int c = c_lo; c < c_hi; c += 2) {
+      body(c, B0{});
+      if (c + 1 < c_hi) body(c + 1, B1{});
+    }
+  } else {
+    for (int c = c_lo; c < c_hi; ++c) body(c, B0{});
   }
   const float l_i = osum[0];
   check_finite(oacc, a.fault);
@@ -629,63 +655,71 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 }
 
 // Merge split partials: O = sum_s w_s o_s / sum_s w_s, w_s = 2^(m_s - M) l_s,
-// with o_s the split's normalized fp16 output.  The (m, l) of every split are
-// staged in LDS first; the partial rows are then read with all loads of a
-// thread in flight.
+// with o_s the split's normalized fp16 output.  One wave per (query, head):
+// lane j owns output dims 2j, 2j+1 (one 4-byte load of two fp16 values per
+// split) and split s's (m, l) sits in lane s mod 64, so every reduction stays
+// inside the wave and a split's place in it does not depend on how many
+// splits the launch has.  The first kMergePF partial rows are requested before
+// the (m, l) pairs are reduced.
 constexpr int kMergeMaxSplits = 1024;
-constexpr int kMergePF = 32;          // partial outputs a merge thread requests up front
-__global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits,
-                                                         const u16* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml,
-                                                         void* __restrict__ O, int o_f32,
-                                                         float* __restrict__ lse, int* fault) {
+constexpr int kMergePF = 32;          // partial rows a lane requests up front
+__global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
+                                                        const u16* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        void* __restrict__ O, int o_f32,
+                                                        float* __restrict__ lse, int* fault) {
   const int qh = blockIdx.x;   // query * H + head
-  const int q = qh / H, h = qh % H, d = threadIdx.x;
-  __shared__ float wgt[kMergeMaxSplits], lsm[kMergeMaxSplits];
-  __shared__ float red[2];
+  const int q = qh / H, h = qh % H, lane = threadIdx.x;
+  __shared__ float wgt[kMergeMaxSplits];
   const int ns = n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits;
-  // the first kMergePF partial outputs, the (max, sum) pairs and the rest are
-  // all requested before anything waits on them: one memory round trip
-  const u16* po = part_o + ((int64_t)q * n_splits * H + h) * kD + d;
-  const int64_t stride = (int64_t)H * kD;
-  u16 v[kMergePF];
+  const uint32_t* po = (const uint32_t*)(part_o + ((int64_t)q * n_splits * H + h) * kD) + lane;
+  const int64_t stride = (int64_t)H * kD / 2;    // 32-bit words between splits
+  uint32_t v[kMergePF];
 #pragma unroll
-  for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : (u16)0;
+  for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : 0u;
   float mloc = -INFINITY;
-  for (int s = d; s < ns; s += 128) {
+  for (int s = lane; s < ns; s += 64) {
     const float2 ml = *(const float2*)&part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
     wgt[s] = ml.x;
-    lsm[s] = ml.y;
     mloc = fmaxf(mloc, ml.x);
   }
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  if ((d & 63) == 0) red[d >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  __syncthreads();
+  const float M = mloc;
   float lloc = 0.f;
-  for (int s = d; s < ns; s += 128) {
-    const float wl = exp2f(wgt[s] - M) * lsm[s];
+  for (int s = lane; s < ns; s += 64) {
+    const float ls = part_ml[(((int64_t)q * n_splits + s) * H + h) * 2 + 1];
+    const float wl = exp2f(wgt[s] - M) * ls;
     wgt[s] = wl;
     lloc += wl;
   }
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
-  if ((d & 63) == 0) red[d >> 6] = lloc;
-  __syncthreads();
-  const float L = red[0] + red[1];
-  auto f16v = [](u16 x) { return (float)__builtin_bit_cast(_Float16, x); };
-  float acc = 0.f;
+  const float L = lloc;
+  __syncthreads();   // wgt[] written by other lanes
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int j = 0; j < kMergePF; ++j)
-    if (j < ns) acc += wgt[j] * f16v(v[j]);
-  for (int s = kMergePF; s < ns; ++s) acc += wgt[s] * f16v(po[s * stride]);
-  const float o = L > 0.f ? acc / L : 0.f;
-  if (!__builtin_isfinite(o)) atomicOr(fault, HSA_FAULT_RANGE);
+    if (j < ns) {
+      const h2 x = __builtin_bit_cast(h2, v[j]);
+      a0 += wgt[j] * (float)x.x;
+      a1 += wgt[j] * (float)x.y;
+    }
+  for (int s = kMergePF; s < ns; ++s) {
+    const h2 x = __builtin_bit_cast(h2, po[s * stride]);
+    a0 += wgt[s] * (float)x.x;
+    a1 += wgt[s] * (float)x.y;
+  }
+  const float o0 = L > 0.f ? a0 / L : 0.f, o1 = L > 0.f ? a1 / L : 0.f;
+  if (!(__builtin_isfinite(o0) && __builtin_isfinite(o1))) atomicOr(fault, HSA_FAULT_RANGE);
   if (o_f32)
-    ((float*)O)[(int64_t)qh * kD + d] = o;
+    *(float2*)((float*)O + (int64_t)qh * kD + 2 * lane) = make_float2(o0, o1);
   else
-    ((u16*)O)[(int64_t)qh * kD + d] = __builtin_bit_cast(u16, (__bf16)o);
-  if (d == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
+    ((uint32_t*)((u16*)O + (int64_t)qh * kD))[lane] =
+        (uint32_t)__builtin_bit_cast(u16, (__bf16)o0) |
+        ((uint32_t)__builtin_bit_cast(u16, (__bf16)o1) << 16);
+  if (lane == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------- prefill HCA: query pairs
@@ -1091,8 +1125,8 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                       : f8 ? attn_kernel<1, true, false, false> : attn_kernel<1, false, false, false>,
                  grid, dim3(64), pre, s, a);
   if (p.n_splits > 1)
-    attn_merge_kernel<<<(unsigned)(q.n * H), 128, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
-                                                            O, a.o_f32, lse, a.fault);
+    attn_merge_kernel<<<(unsigned)(q.n * H), 64, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
+                                                           O, a.o_f32, lse, a.fault);
   return hipGetLastError();
 }
 

@@ -268,7 +268,8 @@ struct UpdateArgs;   // update.h
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span, int group = 1);
 int64_t indexer_max_blocks();   // longest visible-block row the decode indexer takes
 // upd: when not null, the decode cache upkeep of request i runs in the scan
-// launch (one extra workgroup per request)
+// launch (bf16 caches: one extra workgroup per request), in the candidate
+// selection launch (fp8 caches, long rows) or in its own launch before the scan
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,
@@ -287,6 +288,8 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t s);
 
+// the decode upkeep kernel over prepared arguments (B requests, one token each)
+hipError_t launch_update(const UpdateArgs& u, int B, hipStream_t s);
 // n_entries of request b := keep[b] / m in every cache of the layer
 hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, hipStream_t s);
 

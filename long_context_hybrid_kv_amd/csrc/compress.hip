@@ -241,6 +241,11 @@ UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_
   return u;
 }
 
+hipError_t launch_update(const UpdateArgs& u, int B, hipStream_t s) {
+  decode_update_kernel<<<B, 128, 0, s>>>(u, fault_word());
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
                                 hipStream_t s, int n_tok, int64_t* q_pos, int32_t* q_req) {

@@ -7,23 +7,38 @@
 // the B operand holds 16 compressed indexer keys, so each lane of the result
 // owns the 4 heads of one (query, block) pair and the head sum stays in-lane.
 // A B operand row is 16 contiguous bytes of a key, read straight from the
-// paged cache (no LDS).
+// paged cache; prefill stages the A operand (queries) in LDS.
 //
-// Selection is exact and takes three kernels, with no synchronisation between
-// workgroups inside a kernel (on this multi-XCD chip a device-scope fence per
-// workgroup costs more than the whole score stream):
+// Selection is exact, with no synchronisation between workgroups inside a
+// kernel (on this multi-XCD chip a device-scope fence per workgroup costs more
+// than the whole score stream).  Every path begins with
 //   scan     fp32 scores into the workspace, and a histogram of the top 12 bits
-//            of the order-preserving score key (LDS per chunk, then added to a
-//            per-query histogram);
-//   select   every chunk finds, from the histogram, the bin holding the k-th
-//            largest score, marks its blocks above that bin in a per-query
-//            bitmap and appends the blocks inside it to a candidate list;
+//            of the order-preserving score key per chunk in LDS.
+// Decode rows of more than kFusedMaxBlocksDecode blocks then take the
+// candidate path, two kernels in all:
+//   scan     also hands over, per workgroup, the nonzero bins at or above the
+//            bin of its c-th largest score (c ~ 3k / workgroups) and the keys
+//            in them (at most kCandCap);
+//   cand     one workgroup per query merges those bin lists into the row's
+//            histogram above the cut, finds the bin holding the k-th largest
+//            score, and settles the selection from the candidate union alone:
+//            bins above it are taken whole, the threshold bin is refined with
+//            radix passes over the rest of the key (ties -> lower block).  If
+//            the union cannot prove the answer (a workgroup's cut lies at or
+//            above the threshold bin, or a list overflowed) the workgroup
+//            selects over the whole row instead.
+// Prefill, and rows too long for the bitmap in LDS, take three kernels:
+//   select   every chunk finds, from the per-query histogram, the bin holding
+//            the k-th largest score, marks its blocks above that bin in a
+//            per-query bitmap and appends the blocks inside it to a candidate
+//            list;
 //   finalize one workgroup per query refines the candidates with 8-bit radix
 //            passes over the rest of the score key and then over the inverted
 //            block index (ties -> lower block), and emits the bitmap in
 //            ascending block order.
-// The counters and histograms at the head of the workspace are cleared before
-// every call (and by finalize, for the next query chunk of a prefill call).
+// The workspace needs no clearing between calls: histogram and candidate lists
+// are rewritten whole by the kernels that produce them, and the per-query
+// counters are reset by the kernel that owns them before their first use.
 #include <type_traits>
 
 #include "update.h"
@@ -41,8 +56,21 @@ constexpr int kGemmMaxPages = 1024;  // pages of a prefill score workgroup resol
 constexpr int kBins = 4096;        // first-level histogram (12 key bits)
 constexpr int kBmLdsMaxWords = 16384;  // refine pass: bitmaps up to this size go to LDS
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
-constexpr int kStateInts = 8;      // -, -, thr_bin, n_above, n_cand, n_vis, n_thr_bin
+// per-query state: [2] threshold bin, [3] blocks above it, [5] visible blocks,
+// [6] blocks in the threshold bin; the candidate path records instead in [6]
+// which selection served the query (0 the union; 1..4 the whole row: list
+// overflow, no threshold bin, cut at or above it, union incomplete) and in [7]
+// the union size << 16 | threshold-bin size
+constexpr int kStateInts = 8;
 constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
+// decode candidate selection (long rows): each scan workgroup hands over the
+// scores in the histogram bins down to the one holding its c-th largest, at
+// most kCandCap of them; one workgroup per query selects from their union
+constexpr int kCandCap = 256;      // candidates a scan workgroup may write
+constexpr int kCandBmMaxWords = 16384;   // bitmap words of the emission in LDS
+constexpr int kTopBins = 16;       // nonzero bins >= its cut bin a scan workgroup may list
+constexpr int kThrCandMax = 4096;  // candidates of the threshold bin the selection refines in LDS
+constexpr int kUnionMax = 8192;    // candidates of a query the selection takes (8 per thread)
 
 struct IdxWs {
   float* scores;        // [nq][R]
@@ -53,6 +81,11 @@ struct IdxWs {
   uint64_t* cand;       // [nq][R]  (score key << 32 | ~block)
   uint64_t* cand2;      // [nq][R]
   int32_t* ccount;      // [nq][R/kSelCH]  candidates per select chunk (long rows)
+  uint64_t* wcand;      // decode, listed queries: [nq][n_lists][kCandCap] candidate keys
+  int32_t* wcnt;        // [nq][n_lists] candidates each scan workgroup found (> kCandCap: overflow)
+  int32_t* wbin;        // [nq][n_lists] its cut bin: every score left out lies in a lower bin (-1: none)
+  uint32_t* wtop;       // [nq][n_lists][kTopBins] its nonzero bins >= the cut bin: bin << 16 | count
+  int32_t* wntop;       // [nq][n_lists] entries of that list (> kTopBins: overflow)
   int64_t R;
   int n_lists;          // one list per scan chunk (decode) or histogram slice (prefill)
   int list_cap;         // nonzero bins a list can hold
@@ -90,6 +123,12 @@ static size_t layout(char* base, int nq, int64_t R, bool span, bool grouped, Idx
   w->cand = (uint64_t*)take(sizeof(uint64_t) * R * nq);
   w->cand2 = (uint64_t*)take(sizeof(uint64_t) * R * nq);
   w->ccount = (int32_t*)take(sizeof(int32_t) * (R / kSelCH) * nq);
+  const bool cand = !span && !grouped;
+  w->wcand = cand ? (uint64_t*)take(sizeof(uint64_t) * kCandCap * w->n_lists * nq) : nullptr;
+  w->wcnt = cand ? (int32_t*)take(sizeof(int32_t) * w->n_lists * nq) : nullptr;
+  w->wbin = cand ? (int32_t*)take(sizeof(int32_t) * w->n_lists * nq) : nullptr;
+  w->wtop = cand ? (uint32_t*)take(sizeof(uint32_t) * kTopBins * w->n_lists * nq) : nullptr;
+  w->wntop = cand ? (int32_t*)take(sizeof(int32_t) * w->n_lists * nq) : nullptr;
   w->R = R;
   return off;
 }
@@ -275,6 +314,82 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
   if (threadIdx.x == 0) ws.hl_n[(int64_t)qrow * ws.n_lists + li] = (int32_t)tot;
 }
 
+// Candidates of one scan workgroup (decode, long rows): the cut bin b_c is the
+// highest bin of the workgroup's 4096-bin histogram whose count from the top
+// reaches c_local; every score in a bin >= b_c is written as a key
+// (score key << 32 | ~block), at most kCandCap of them, and every score left
+// out lies in a bin below b_c.  wcnt records how many there were (more than
+// kCandCap: the selection falls back to the full row), wbin the cut bin (-1
+// when nothing was left out).  n_sc scores in lsc belong to blocks s0 ...
+template <int NTH>
+__device__ __forceinline__ void write_candidates(const uint32_t* lhist, const float* lsc, int n_sc,
+                                                 int64_t s0, const IdxWs& ws, int qrow, int wg,
+                                                 int c_local) {
+  __shared__ uint32_t sh[NTH / 64];
+  __shared__ int s_bc;
+  __shared__ uint32_t s_n;
+  constexpr int BPT = kBins / NTH;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lo = kBins - BPT * (tid + 1);        // thread 0 owns the highest bins
+  uint32_t v[BPT], sm = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    v[j] = lhist[lo + j];
+    sm += v[j];
+  }
+  if (tid == 0) { s_bc = 0; s_n = 0; }
+  uint32_t tot;
+  const uint32_t pre = block_scan_nt<NTH>(sm, &tot, sh);
+  if (pre < (uint32_t)c_local && pre + sm >= (uint32_t)c_local) {
+    uint32_t cum = pre;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (cum < (uint32_t)c_local && cum + v[j] >= (uint32_t)c_local) s_bc = lo + j;
+      cum += v[j];
+    }
+  }
+  __syncthreads();
+  const int bc = s_bc;                           // 0 when the workgroup holds fewer scores
+  {
+    // the nonzero bins >= bc, listed as bin << 16 | count
+    uint32_t nz = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) nz += (lo + j >= bc && v[j] != 0);
+    uint32_t ntot;
+    uint32_t o = block_scan_nt<NTH>(nz, &ntot, sh);
+    uint32_t* lst = ws.wtop + ((int64_t)qrow * ws.n_lists + wg) * kTopBins;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j)
+      if (lo + j >= bc && v[j] != 0) {
+        if (o < (uint32_t)kTopBins) lst[o] = ((uint32_t)(lo + j) << 16) | v[j];
+        ++o;
+      }
+    if (tid == 0) ws.wntop[(int64_t)qrow * ws.n_lists + wg] = (int32_t)ntot;
+  }
+  uint64_t* dst = ws.wcand + ((int64_t)qrow * ws.n_lists + wg) * kCandCap;
+  for (int base = 0; base < n_sc; base += NTH) {
+    const int i = base + tid;
+    const uint32_t key = i < n_sc ? order_key(lsc[i]) : 0u;
+    const bool c = i < n_sc && (int)(key >> 20) >= bc;
+    const uint64_t cm = __ballot(c);
+    if (cm) {
+      const int leader = __ffsll((unsigned long long)cm) - 1;
+      uint32_t cb = 0;
+      if (lane == leader) cb = atomicAdd(&s_n, (uint32_t)__popcll(cm));
+      cb = __shfl(cb, leader);
+      const uint32_t pos = cb + __popcll(cm & ((1ull << lane) - 1));
+      if (c && pos < (uint32_t)kCandCap)
+        dst[pos] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(s0 + i));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ws.wcnt[(int64_t)qrow * ws.n_lists + wg] = (int32_t)s_n;
+    // anything below the cut bin left out?  (bins below bc hold tot - s_n scores)
+    ws.wbin[(int64_t)qrow * ws.n_lists + wg] = s_n < (uint32_t)n_sc ? bc : -1;
+  }
+}
+
 // ---------------------------------------------------------------- decode: score scan
 
 // F8K: fp8 keys with a page scale; F4K: fp4 keys (MX blocks); neither: bf16
@@ -282,7 +397,8 @@ template <int CPW, int NWV, bool F8K, bool F4K, bool S16>
 __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16* __restrict__ qI,
                                                        const float* __restrict__ w, Paged kic,
                                                        int m, int n_win, int k, IdxWs ws,
-                                                       int n_groups, UpdateArgs upd, int* fault) {
+                                                       int n_groups, UpdateArgs upd, int cand_k,
+                                                       int* fault) {
   const int qrow = blockIdx.y;
   if ((int)blockIdx.x >= n_groups) {   // the extra column: cache upkeep of request qrow
     decode_update_body<false>(upd, qrow, fault);   // bf16 caches only (the host's rule)
@@ -451,7 +567,16 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   const int64_t s_end = nv < s0 + CPW * kCH ? nv : s0 + CPW * kCH;
   for (int i = threadIdx.x; i < CPW * kCH; i += NWV * 64)
     if (s0 + i < s_end) score_store<S16>(srow, s0 + i, lsc[i]);
-  write_hist_list<NWV * 64>(lhist, ws, qrow, blockIdx.x);
+  if (cand_k > 0) {
+    // candidates per workgroup: three times the query's top-k spread over its
+    // workgroups (so one workgroup rarely holds more of the top-k than it hands
+    // over), at least 16, at most half the candidate space
+    const int n_act = (n_active + CPW - 1) / CPW;
+    int c_local = (3 * cand_k + n_act - 1) / n_act;
+    c_local = c_local < 16 ? 16 : (c_local > kCandCap / 2 ? kCandCap / 2 : c_local);
+    write_candidates<NWV * 64>(lhist, lsc, (int)(s_end - s0), s0, ws, qrow, blockIdx.x, c_local);
+  } else
+    write_hist_list<NWV * 64>(lhist, ws, qrow, blockIdx.x);
 }
 
 // Write a histogram of 16-bit counts packed two bins per word (bin b in half
@@ -1204,6 +1329,255 @@ __global__ __launch_bounds__(256) void idx_select_kernel(IdxWs ws) {
   if (threadIdx.x == 0) ws.ccount[(int64_t)qrow * (ws.R / kSelCH) + chunk] = (int32_t)s_cnt;
 }
 
+// The k-th largest of n unique 64-bit keys key(i), i < n, all sharing the bits
+// above bit `bits` with `prefix`: radix digits of up to 8 bits from bit bits-1
+// down (every thread of the NT-thread workgroup calls it; h256 and sh are
+// workgroup scratch).  Stops as soon as the keys sharing the digits chosen so
+// far are exactly the ones still needed, so the returned threshold T
+// satisfies: key >= T  <=>  key is among the k largest.
+template <int NT, typename KeyFn>
+__device__ uint64_t radix_kth(int64_t n, int k, KeyFn key, int bits, uint64_t prefix,
+                              uint32_t* h256, uint32_t* sh) {
+  __shared__ int s_d;
+  __shared__ uint32_t s_above, s_cnt;
+  uint64_t mask = bits >= 64 ? 0ull : ~0ull << bits;
+  uint32_t need = (uint32_t)k;
+  for (int hi = bits; hi > 0; hi -= 8) {
+    const int wdt = hi >= 8 ? 8 : hi, shift = hi - wdt;
+    const uint64_t dm = (1ull << wdt) - 1;
+    if (threadIdx.x < 256) h256[threadIdx.x] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+      const uint64_t x = key(i);
+      if ((x & mask) == prefix) atomicAdd(&h256[(x >> shift) & dm], 1u);
+    }
+    __syncthreads();
+    {
+      const uint32_t c = threadIdx.x < 256 ? h256[255 - threadIdx.x] : 0u;
+      uint32_t tot;
+      const uint32_t pre = block_scan_nt<NT>(c, &tot, sh);
+      if (threadIdx.x < 256 && pre < need && pre + c >= need) {
+        s_d = 255 - (int)threadIdx.x;
+        s_above = pre;
+        s_cnt = c;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_d << shift;
+    mask |= dm << shift;
+    need -= s_above;
+    const uint32_t cnt = s_cnt;
+    __syncthreads();   // s_d, s_above, s_cnt are rewritten by the next digit
+    if (cnt == need) break;   // all keys with this prefix are selected
+  }
+  return prefix;
+}
+
+// Decode, long rows: the top-k of a query from the candidates its scan
+// workgroups wrote.  With T the k-th largest candidate key, the union holds the
+// row's top-k exactly when T's bin is at least every workgroup's cut bin (all
+// scores left out lie below that bin, so below T); otherwise (or when a
+// workgroup overflowed its candidate space) the k-th key is selected over the
+// whole score row.  The selected ids are marked in an LDS bitmap and emitted
+// ascending.  One workgroup per query.
+// Workgroups past the queries (blockIdx.x >= n_q) run the decode cache upkeep
+// of request blockIdx.x - n_q, fp8 caches included: the selection reads no
+// cache, and the attention that reads them is the next launch.
+template <bool S16>
+__global__ __launch_bounds__(1024) void idx_cand_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
+                                                        float* __restrict__ score, int n_q,
+                                                        UpdateArgs upd, int* fault) {
+  constexpr int NT = 1024, BPT = kBins / NT;
+  if ((int)blockIdx.x >= n_q) {
+    decode_update_body<true>(upd, blockIdx.x - n_q, fault);
+    return;
+  }
+  extern __shared__ __align__(16) uint64_t dyn[];
+  uint64_t* tc = dyn;                                     // [kThrCandMax] threshold-bin candidates
+  uint32_t* bm = (uint32_t*)(dyn + kThrCandMax);          // [R / 32]
+  __shared__ uint32_t sh[NT / 64];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_off[NT + 1];
+  __shared__ uint8_t s_ntop[NT];
+  __shared__ int s_bad, s_maxbc, s_thr;
+  __shared__ uint32_t s_above, s_ntc;
+  const int qrow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* st = ws.state + (int64_t)qrow * kStateInts;
+  const int64_t nv = st[5];
+  const void* srow = score_row<S16>(ws, qrow);
+  int32_t* irow = idx + (int64_t)qrow * k;
+  float* srow_out = score ? score + (int64_t)qrow * k : nullptr;
+  const int64_t W = (nv + 31) / 32;
+  for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) hist[tid + NT * j] = 0;
+  if (tid == 0) { s_bad = 0; s_maxbc = -1; s_thr = -1; s_above = 0; s_ntc = 0; }
+  if (nv > k) {
+    const int n_wg = (int)((nv + ws.list_span - 1) / ws.list_span);
+    const int64_t wrow = (int64_t)qrow * ws.n_lists;
+    const int cnt = tid < n_wg ? ws.wcnt[wrow + tid] : 0;
+    const int bcw = tid < n_wg ? ws.wbin[wrow + tid] : -1;
+    const int ntop = tid < n_wg ? ws.wntop[wrow + tid] : 0;
+    uint32_t tot;
+    const uint32_t off = block_scan_nt<NT>((uint32_t)(cnt < kCandCap ? cnt : kCandCap), &tot, sh);
+    if (tid < n_wg) {
+      s_off[tid] = off;
+      s_ntop[tid] = (uint8_t)(ntop < kTopBins ? ntop : kTopBins);
+    }
+    if (tid == 0) s_off[n_wg] = tot;
+    if (cnt > kCandCap || ntop > kTopBins) atomicOr(&s_bad, 1);
+    if (tot > (uint32_t)kUnionMax && tid == 0) atomicOr(&s_bad, 1);
+    if (bcw >= 0) atomicMax(&s_maxbc, bcw);
+    __syncthreads();
+    // the union's histogram from the workgroups' top-bin lists: every entry's
+    // load is issued before any is used (n_wg * kTopBins <= 16 per thread)
+    {
+      constexpr int PER = (NT * kTopBins) / NT;   // list slots per thread, n_wg <= NT
+      uint32_t e[PER];
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int slot = r * NT + tid, g = slot / kTopBins, j = slot % kTopBins;
+        e[r] = (g < n_wg && j < s_ntop[g]) ? ws.wtop[(wrow + g) * kTopBins + j] : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < PER; ++r)
+        if (e[r]) atomicAdd(&hist[e[r] >> 16], e[r] & 0xFFFFu);
+    }
+    __syncthreads();
+    // threshold bin: thread t owns bins kBins - BPT(t+1) .. kBins - BPT t - 1
+    {
+      const int lo = kBins - BPT * (tid + 1);
+      uint32_t v[BPT], sm = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        v[j] = hist[lo + j];
+        sm += v[j];
+      }
+      uint32_t ht;
+      const uint32_t pre = block_scan_nt<NT>(sm, &ht, sh);
+      if (pre < (uint32_t)k && pre + sm >= (uint32_t)k) {
+        uint32_t cum = pre;
+#pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+          if (cum < (uint32_t)k && cum + v[j] >= (uint32_t)k) { s_thr = lo + j; s_above = cum; }
+          cum += v[j];
+        }
+      }
+    }
+    __syncthreads();
+    // the union holds the row's top-k iff every score left out lies in a bin
+    // below the threshold bin
+    bool full = s_bad != 0 || s_thr < 0 || s_thr < s_maxbc;
+    if (!full) {
+      const int thr = s_thr;
+      // one pass over the candidates: above the bin -> bitmap, in it -> refine
+      // every candidate load in flight before any is used (tot <= kUnionMax)
+      constexpr int PER = kUnionMax / NT;
+      uint64_t xs[PER];
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const uint32_t i = (uint32_t)(r * NT + tid);
+        xs[r] = 0;
+        if (i < tot) {
+          int a = 0, b = n_wg;                // s_off[a] <= i < s_off[b]
+          while (b - a > 1) {
+            const int mid = (a + b) >> 1;
+            if (s_off[mid] <= i) a = mid; else b = mid;
+          }
+          xs[r] = ws.wcand[(wrow + a) * kCandCap + (i - s_off[a])];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const uint32_t i = (uint32_t)(r * NT + tid);
+        const uint64_t x = xs[r];
+        const int bin = i < tot ? (int)(x >> 52) : -1;
+        if (bin > thr) {
+          const uint32_t blk = ~(uint32_t)x;
+          atomicOr(&bm[blk >> 5], 1u << (blk & 31));
+        }
+        const bool c = bin == thr;
+        const uint64_t cm = __ballot(c);
+        if (cm) {
+          const int leader = __ffsll((unsigned long long)cm) - 1;
+          uint32_t cb = 0;
+          if (lane == leader) cb = atomicAdd(&s_ntc, (uint32_t)__popcll(cm));
+          cb = __shfl(cb, leader);
+          const uint32_t p = cb + __popcll(cm & ((1ull << lane) - 1));
+          if (c && p < (uint32_t)kThrCandMax) tc[p] = x;
+        }
+      }
+      __syncthreads();
+      const uint32_t ntc = s_ntc;
+      if (ntc > (uint32_t)kThrCandMax) {
+        full = true;                          // uniform: every thread read s_ntc
+        for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
+        __syncthreads();
+      } else {
+        const uint64_t T = radix_kth<NT>((int64_t)ntc, k - (int)s_above,
+                                         [&](int64_t i) { return tc[i]; }, 52,
+                                         (uint64_t)thr << 52, h256, sh);
+        for (uint32_t i = tid; i < ntc; i += NT)
+          if (tc[i] >= T) {
+            const uint32_t blk = ~(uint32_t)tc[i];
+            atomicOr(&bm[blk >> 5], 1u << (blk & 31));
+          }
+      }
+    }
+    if (tid == 0) {   // which path served the query, and the union / threshold-bin sizes
+      st[6] = full ? (s_bad ? 1 : (s_thr < 0 ? 2 : (s_thr < s_maxbc ? 3 : 4))) : 0;
+      st[7] = (int32_t)((tot << 16) | (s_ntc & 0xFFFF));
+    }
+    if (full) {
+      // exact selection over the whole row (rare)
+      auto fkey = [&](int64_t i) {
+        return ((uint64_t)order_key(score_load<S16>(srow, i)) << 32) | (uint64_t)(~(uint32_t)i);
+      };
+      const uint64_t T = radix_kth<NT>(nv, k, fkey, 64, 0ull, h256, sh);
+      for (int64_t i = tid; i < nv; i += NT)
+        if (fkey(i) >= T) atomicOr(&bm[i >> 5], 1u << (i & 31));
+    }
+  } else {
+    __syncthreads();
+    for (int64_t i = tid; i < nv; i += NT) atomicOr(&bm[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  // emit ascending block ids: each thread owns 8 consecutive bitmap words per round
+  uint32_t total = 0;
+  for (int64_t r0 = 0; r0 < W; r0 += (int64_t)NT * 8) {
+    const int64_t w0 = r0 + (int64_t)tid * 8;
+    uint32_t wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wd[i] = w0 + i < W ? bm[w0 + i] : 0u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(wd[i]);
+    uint32_t tot;
+    uint32_t o = block_scan_nt<NT>(cnt, &tot, sh) + total;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t word = wd[i];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        const uint32_t b = (uint32_t)((w0 + i) * 32 + bit);
+        if (o < (uint32_t)k) {
+          irow[o] = (int32_t)b;
+          if (srow_out) srow_out[o] = score_load<S16>(srow, b);
+        }
+        ++o;
+      }
+    }
+    total += tot;
+    __syncthreads();   // sh is reused by the next round's scan
+  }
+  for (int i = (int)total + tid; i < k; i += NT) {
+    irow[i] = -1;
+    if (srow_out) srow_out[i] = 0.f;
+  }
+}
+
 // ---------------------------------------------------------------- host launcher
 
 // rows up to these sizes take the one-workgroup-per-query path; longer rows the
@@ -1284,7 +1658,6 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     const int cpw = scan_cpw(R);
     const unsigned n_groups = (n_chunks + cpw - 1) / cpw;
     const UpdateArgs ua = upd ? *upd : UpdateArgs{};
-    const dim3 grid(n_groups + (upd ? 1 : 0), q.n);
     const bool f8k = kic.dtype == HSA_FP8_E4M3, f4k = kic.dtype == HSA_FP4_E2M1_MX;
     // eight waves, each streaming one page of every chunk
     auto pick = [&](auto k4_f8, auto k4_f4, auto k4_bf, auto k1_f8, auto k1_f4, auto k1_bf) {
@@ -1302,13 +1675,34 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                            idx_scan_kernel<1, 8, true, false, false>,
                            idx_scan_kernel<1, 8, false, true, false>,
                            idx_scan_kernel<1, 8, false, false, false>);
+    // long rows whose emission bitmap fits in LDS: the scan hands over
+    // candidates and one kernel selects from them (two launches instead of the
+    // threshold / select / refine chain)
+    const bool cand = R > kFusedMaxBlocksDecode && R / 32 <= kCandBmMaxWords;
+    // the decode cache upkeep: bf16 K / V caches in the scan launch; fp8 ones
+    // (page re-encoding, whose registers the scan should not carry) in the
+    // candidate selection launch, or on their own before the scan
+    const bool f8upd = upd && (upd->kc.dtype != HSA_BF16 || upd->vc.dtype != HSA_BF16);
+    if (f8upd && !cand) {
+      hipError_t e = launch_update(*upd, q.n, s);
+      if (e != hipSuccess) return e;
+    }
+    const dim3 grid(n_groups + (upd && !f8upd ? 1 : 0), q.n);
     timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(8 * 64), 0, s, Qd, (const u16*)qI, w, kc, m,
-                 n_win, k, ws, (int)n_groups, ua, fault);
+                 n_win, k, ws, (int)n_groups, ua, cand ? k : 0, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
-    if (s16)
+    if (cand) {
+      const size_t lds = (size_t)kThrCandMax * sizeof(uint64_t) + (size_t)(R / 32) * sizeof(uint32_t);
+      const unsigned g = (unsigned)q.n + (f8upd ? (unsigned)q.n : 0u);
+      if (s16)
+        idx_cand_kernel<true><<<g, 1024, lds, s>>>(k, ws, idx, score, q.n, ua, fault);
+      else
+        idx_cand_kernel<false><<<g, 1024, lds, s>>>(k, ws, idx, score, q.n, ua, fault);
+    } else if (s16) {
       launch_topk<true>(1024, q.n, k, ws, idx, score, 0, s);
-    else
+    } else {
       launch_topk<false>(1024, q.n, k, ws, idx, score, 0, s);
+    }
     return hipGetLastError();
   }
   const int QC = nq_ws;
