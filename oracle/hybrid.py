@@ -29,6 +29,10 @@ Readings taken where the pages are silent:
   window: b < min(ceil(s(t)/m), floor((t+1)/m)), s(t) = max(0, t - n_win + 1);
 * the window W(t) = {s(t), ..., t} includes the query token;
 * one softmax over window + compressed entries, logits scaled by 1/sqrt(d).
+* positional rotation (optional, rope_theta > 0): the last 64 channels of every
+  key and query head turn as adjacent pairs (rope_exact); a key is rotated at
+  its own position before it enters the window or a block, so a compressed
+  entry pools rotated keys and a query's scores depend only on offsets.
 """
 from __future__ import annotations
 
@@ -52,6 +56,65 @@ def n_visible(t: int, m: int, n_win: int) -> int:
     m-1 tokens of the block that straddles the window's start)."""
     s = window_start(t, n_win)
     return min(-(-s // m), (t + 1) // m)
+
+
+# ----------------------------------------------------------------------------- positional rotation
+
+ROPE_DIM = 64   # rotated channels: the last 64 of a key row or of a query head
+
+
+def rope_inv_freq(theta: float) -> np.ndarray:
+    """Rotation frequency of channel pair i < 32: theta^(-2i/64), held in
+    float32 (the usual inverse-frequency table), returned as float64 values.
+
+    The group-reading wiki "DeepSeek-V4 深度研究剖析" §8 keeps the KV cache's
+    RoPE channels apart from the others and names no rotation; this is the
+    rotary embedding's textbook form (RoFormer) over the last 64 channels."""
+    i = np.arange(ROPE_DIM // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * i / ROPE_DIM).astype(np.float32).astype(np.float64)
+
+
+def rope_exact(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotate the last 64 channels of every row of x (float64 values, last axis
+    the channels) in float64, without rounding to a storage format.
+
+    pos holds the position of each row (x's shape without the channel axis,
+    or anything broadcasting to it).  Pair i is channels (d-64+2i, d-63+2i);
+    at position p it turns by the angle p * f_i (f_i from rope_inv_freq):
+        x' = x cos - y sin,   y' = x sin + y cos,
+    each product rounded to float64, then the sum (no fused multiply-add).
+    The other channels are returned unchanged."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    d = x.shape[-1]
+    assert d >= ROPE_DIM and d % 2 == 0
+    r0 = d - ROPE_DIM
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(theta)
+    c, s = np.cos(ang), np.sin(ang)
+    ev = x[..., r0::2].copy()
+    od = x[..., r0 + 1::2].copy()
+    x[..., r0::2] = ev * c - od * s
+    x[..., r0 + 1::2] = ev * s + od * c
+    return x
+
+
+def rope(x_bits: np.ndarray, pos, theta: float) -> np.ndarray:
+    """bf16 rows (bit patterns) rotated at their positions: rope_exact of
+    their values, rounded once to bf16.  This is what enters the window ring
+    and the compression (a key is rotated at its own position before it is
+    cached; a compressed entry pools rotated keys) and what a query attends
+    with."""
+    return nx.bf16_bits_from_f64(rope_exact(nx.bf16_value(x_bits), pos, theta))
+
+
+def rotate_tokens(inp: dict, theta: float) -> dict:
+    """A layer's raw inputs with K and Q rotated: K row t at position t, the
+    query of position t (q[t], all heads) at t.  Other inputs unchanged."""
+    out = dict(inp)
+    T = inp["k"].shape[0]
+    out["k"] = rope(inp["k"], np.arange(T), theta)
+    nq = inp["q"].shape[0]
+    out["q"] = rope(inp["q"], np.arange(nq)[:, None], theta)
+    return out
 
 
 # ----------------------------------------------------------------------------- compression
