@@ -34,6 +34,15 @@
  *   attention         O[t][h] = softmax_e(scale * Q[t][h] . K_e) applied to
  *                     V_e over the window rows followed by the selected (CSA)
  *                     or all visible (HCA) compressed entries: one softmax.
+ *   partial RoPE      (optional; §8 keeps these channels in bf16) the last 64
+ *                     channels of a key row or query head, as pairs
+ *                     (d-64+2i, d-63+2i), i < 32, turn by the angle p * f_i at
+ *                     position p: x' = x cos - y sin, y' = x sin + y cos, with
+ *                     f_i = theta^(-2i/64) rounded to fp32; angle, cos, sin
+ *                     and the turn in float64 (no fused multiply-add), then
+ *                     one bf16 rounding.  A key is turned at its own position
+ *                     before it is cached, so a compressed entry pools turned
+ *                     keys and scores depend only on position offsets.
  *
  * Conventions
  *   - Every pointer argument that names a tensor is a DEVICE pointer unless
@@ -74,7 +83,7 @@
 extern "C" {
 #endif
 
-#define HSA_ABI_VERSION 2
+#define HSA_ABI_VERSION 3
 
 typedef enum {
   HSA_OK = 0,
@@ -244,6 +253,18 @@ hsa_status hsa_hca_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                         void* O, int32_t o_dtype, float* lse, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* Partial RoPE over rows of bf16 heads (the definition above; wiki §8 keeps
+ * the channels it turns in bf16).  x, y: bf16 [n_rows][heads][dim], dim >= 64
+ * and a multiple of 8, 16-byte aligned; y == x turns in place (only the last
+ * 64 channels of each head are written), otherwise y must not overlap x and
+ * receives the other channels unchanged.  Row i is at position pos[i] (device
+ * int64 [n_rows]) or, with pos NULL, pos0 + i.  theta > 0 and finite.
+ * Prefill turns its K token rows (heads = 1) and its queries with this call
+ * before compressing and attending; the decode calls turn their own.  A listed
+ * position below 0 leaves its row unturned and sets HSA_FAULT_POS. */
+hsa_status hsa_rope(const void* x, void* y, int64_t n_rows, int32_t heads, int32_t dim,
+                    const int64_t* pos, int64_t pos0, double theta, hipStream_t stream);
+
 typedef enum { HSA_LAYER_CSA = 0, HSA_LAYER_HCA = 1 } hsa_layer_kind;
 
 /* One attention layer's parameters and caches for decoding a batch of B
@@ -261,27 +282,33 @@ typedef struct {
   hsa_tokens tail_i;            /* CSA: raw indexer keys of the open block, capacity >= m */
   hsa_paged  kc, vc;            /* compressed K/V (classical cache) */
   hsa_paged  kic;               /* CSA: compressed indexer keys (bf16) */
+  double     rope_theta;        /* > 0: partial RoPE with this base (the ring
+                                   and the caches then hold turned keys); 0: Q
+                                   and K are used as given */
 } hsa_layer;
 
 /* One decode step of one layer for B requests (wiki §11.4 for the caches;
  * §5.2-§5.4 for the attention).  pos[b] is the position of request b's new
  * token (the request holds tokens 0..pos[b]-1).  The step
  *   1. writes the new token's K/V into ring slot pos%capacity (and KI into
- *      tail slot pos%capacity for CSA);
+ *      tail slot pos%capacity for CSA); with rope_theta > 0 the K row is
+ *      turned at pos first, and the queries are turned into the workspace;
  *   2. if (pos+1) % m == 0, compresses block (pos+1)/m - 1 from the ring and
- *      tail and appends it at entry n_entries[b], which it then increments;
+ *      tail and appends it at entry n_entries[b], which it then increments
+ *      (fp8 caches: the entry's exact value goes to the stash and the page
+ *      still filling is re-encoded with the scale of the entries it holds);
  *   3. runs the indexer + top-k + CSA attention, or HCA attention, for the
  *      new token's query.
- * (Steps 1-2 of a CSA layer run in the same launch as the indexer's scan: the
- * block completed at pos starts inside the window, so the query at pos does not
- * see it.)
+ * The block completed at pos starts inside the window, so the query at pos
+ * does not see it: steps 1-2 of a CSA layer ride in one of the indexer's
+ * launches instead of a launch of their own.
  * Q bf16 [B][H][d]; k_new, v_new bf16 [B][d]; qI bf16 [B][H_I][d_I]; kI_new
  * bf16 [B][d_I]; w fp32 [B][H_I]; O [B][H][d] of L->o_dtype; lse fp32 [B][H] or NULL;
  * idx_out int32 [B][topk] or NULL (CSA).  max_pos bounds every pos[b].
- * The caller advances pos between steps.  Needs bf16 compressed K/V caches
- * (an fp8 page's scale is fixed when the page is written whole; use
- * hsa_kv_compress at page granularity for fp8).  No allocation and no host
- * synchronisation: the call can be captured in a HIP graph. */
+ * The caller advances pos between steps.  Compressed K/V caches: bf16, or fp8
+ * (HSA_FP8_E4M3, or HSA_FP8_BF16_ROPE K) with fp8 V, both with stashes.  No
+ * allocation and no host synchronisation: the call can be captured in a HIP
+ * graph. */
 size_t hsa_decode_step_workspace_bytes(const hsa_layer* L, int32_t B, int64_t max_pos);
 hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, int64_t max_pos,
                            const void* Q, const void* k_new, const void* v_new,

@@ -53,11 +53,14 @@ class _Layer(C.Structure):
                 ("m", C.c_int32), ("topk", C.c_int32), ("H_I", C.c_int32), ("d_I", C.c_int32),
                 ("scale", C.c_float), ("o_dtype", C.c_int32), ("alpha_k", C.c_void_p), ("alpha_v", C.c_void_p),
                 ("alpha_i", C.c_void_p), ("ring_k", _Tokens), ("ring_v", _Tokens),
-                ("tail_i", _Tokens), ("kc", _Paged), ("vc", _Paged), ("kic", _Paged)]
+                ("tail_i", _Tokens), ("kc", _Paged), ("vc", _Paged), ("kic", _Paged),
+                ("rope_theta", C.c_double)]
 
 
 _SIGS = {
     "hsa_abi_version": (C.c_int32, []),
+    "hsa_rope": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+                           C.c_int64, C.c_double, C.c_void_p]),
     "hsa_last_error": (C.c_char_p, []),
     "hsa_status_string": (C.c_char_p, [C.c_int]),
     "hsa_check_device_error": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
@@ -324,6 +327,19 @@ def pooling_weights(z: torch.Tensor) -> torch.Tensor:
     return alpha
 
 
+def rope(x: torch.Tensor, theta: float, pos: Optional[torch.Tensor] = None, pos0: int = 0,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hsa_rope over bf16 rows x [n_rows, dim] or [n_rows, heads, dim]: row i at
+    position pos[i] (int64, device) or pos0 + i.  out=x turns in place; by
+    default a new tensor receives the result."""
+    x = x.contiguous()
+    heads, dim = (1, x.shape[1]) if x.dim() == 2 else (x.shape[1], x.shape[2])
+    y = torch.empty_like(x) if out is None else out
+    _check(lib().hsa_rope(_ptr(x), _ptr(y), x.shape[0], heads, dim, _ptr(pos), pos0, float(theta),
+                          _stream()), "rope")
+    return y
+
+
 def kv_compress(x: Tokens, out: PagedCache, req: int, first_block: int, n_blocks: int, m: int,
                 alpha: torch.Tensor, x_req: int = 0) -> None:
     """Pool blocks [first_block, first_block + n_blocks) of request x_req of x into
@@ -403,6 +419,7 @@ class Layer:
     d_I: int = 64
     scale: Optional[float] = None
     out_fp32: bool = False
+    rope_theta: float = 0.0           # > 0: the step turns its keys and queries (partial RoPE)
 
     def c(self) -> _Layer:
         L = _Layer()
@@ -416,6 +433,7 @@ class Layer:
         L.kc, L.vc = self.kc.c(), self.vc.c()
         if self.kind == LAYER_CSA:
             L.tail_i, L.kic = self.tail_i.c(), self.kic.c()
+        L.rope_theta = self.rope_theta
         return L
 
 

@@ -1,5 +1,6 @@
 // C ABI of libhsa_attn: argument validation, workspace sizing, dispatch to the
 // gfx950 kernels, status strings and the per-device fault word.
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -291,6 +292,23 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
                     "kv_compress");
 }
 
+hsa_status hsa_rope(const void* x, void* y, int64_t n_rows, int32_t heads, int32_t dim,
+                    const int64_t* pos, int64_t pos0, double theta, hipStream_t stream) {
+  REQ(n_rows >= 0, "rope: negative n_rows");
+  REQ(heads >= 1 && heads <= 4096, "rope: heads must be in [1, 4096]");
+  REQ(dim >= kRopeDim && dim % 8 == 0 && dim <= 4096,
+      "rope: dim must be a multiple of 8 in [64, 4096]");
+  REQ(std::isfinite(theta) && theta > 0.0, "rope: theta must be finite and > 0");
+  if (n_rows == 0) return HSA_OK;
+  REQ(x && y, "rope: null x or y");
+  REQ((((uintptr_t)x | (uintptr_t)y) & 15) == 0, "rope: x and y must be 16-byte aligned");
+  REQ(pos || (pos0 >= 0 && pos0 <= INT64_MAX - n_rows), "rope: positions out of range");
+  const uintptr_t bytes = (uintptr_t)n_rows * heads * dim * sizeof(uint16_t);
+  const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+  REQ(xa == ya || xa + bytes <= ya || ya + bytes <= xa, "rope: y overlaps x without equalling it");
+  return hip_status(launch_rope(x, y, n_rows, heads, dim, pos, pos0, theta, stream), "rope");
+}
+
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k) {
   if (!q || q->n < 1 || m < 1 || n_win < 1 || k < 1 || q->max_pos < 0) return 0;
@@ -397,6 +415,11 @@ static hsa_status check_append_caches(const hsa_layer* L, const std::string& who
 // decode_step workspace: [indexer][selected ids][attention], 256-byte aligned
 static size_t rnd256(size_t b) { return (b + 255) & ~size_t(255); }
 
+static size_t rope_q_bytes(const hsa_layer* L, size_t n_q) {
+  return L->rope_theta > 0.0 ? rnd256(sizeof(uint16_t) * n_q * L->H * kD) : 0;
+}
+
+// (with RoPE the turned queries follow the attention's part)
 static void decode_parts(const hsa_layer* L, int32_t B, int64_t max_pos, size_t* p_idx,
                          size_t* p_sel, size_t* p_attn) {
   hsa_queries q{};
@@ -418,7 +441,7 @@ size_t hsa_decode_step_workspace_bytes(const hsa_layer* L, int32_t B, int64_t ma
   if (L->kind == HSA_LAYER_CSA && L->topk < 1) return 0;
   size_t a, b, c;
   decode_parts(L, B, max_pos, &a, &b, &c);
-  return a + b + c;
+  return a + b + c + rope_q_bytes(L, (size_t)B);
 }
 
 // Validation shared by the single-token step and the draft (n_tok tokens per
@@ -434,6 +457,8 @@ static hsa_status check_decode(const hsa_layer* L, int32_t B, int32_t n_tok, con
   REQ(n_tok >= 1 && n_tok <= 256, "decode: n_tok must be in [1, 256]");
   REQ(L->alpha_k && L->alpha_v, "decode: null pooling weights");
   REQ(L->o_dtype == HSA_BF16 || L->o_dtype == HSA_FP32, "decode: o_dtype must be bf16 or fp32");
+  REQ(std::isfinite(L->rope_theta) && L->rope_theta >= 0.0,
+      "decode: rope_theta must be finite and >= 0 (0: no RoPE)");
   {
     hsa_status sa = check_append_caches(L, "decode");
     if (sa != HSA_OK) return sa;
@@ -486,25 +511,30 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
   const bool csa = L->kind == HSA_LAYER_CSA;
   size_t a_idx, a_sel, a_attn;
   decode_parts(L, B, max_pos, &a_idx, &a_sel, &a_attn);
-  if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn)) != HSA_OK) return s;
+  const size_t a_q = rope_q_bytes(L, (size_t)B);
+  if ((s = check_ws(ws, ws_bytes, a_idx + a_sel + a_attn + a_q)) != HSA_OK) return s;
   char* base = (char*)ws;
+  // RoPE: the upkeep writes the turned queries here, and the attention reads them
+  void* q_rot = a_q ? base + a_idx + a_sel + a_attn : nullptr;
+  const void* Qa = a_q ? q_rot : Q;
   hipError_t e;
   if (csa) {
     // the cache upkeep rides in one of the indexer's launches (which one
     // depends on the cache formats and the row length: launch_indexer); the
     // block completed at pos starts inside the window, so no query of this
     // step sees it and the scan never reads what the upkeep writes
-    const UpdateArgs upd = make_update_args(*L, pos, max_pos, k_new, v_new, kI_new);
+    const UpdateArgs upd = make_update_args(*L, pos, max_pos, k_new, v_new, kI_new, Q, q_rot);
     int32_t* sel = idx_out ? idx_out : (int32_t*)(base + a_idx);
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base, a_idx,
                        stream, &upd);
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
-    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
+    e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_idx + a_sel, a_attn, stream);
   } else {
-    e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream);
+    e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream, 1, nullptr,
+                             nullptr, Q, q_rot);
     if (e != hipSuccess) return hip_status(e, "decode_step update");
-    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
+    e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
                     L->scale, O, L->o_dtype, lse, base, a_attn, stream);
   }
   return hip_status(e, "decode_step attention");
@@ -545,7 +575,7 @@ size_t hsa_decode_draft_workspace_bytes(const hsa_layer* L, int32_t B, int32_t n
   if (L->kind == HSA_LAYER_CSA && L->topk < 1) return 0;
   size_t a, b, c, d;
   draft_parts(L, B, n_tok, max_pos, &a, &b, &c, &d);
-  return a + b + c + d;
+  return a + b + c + d + rope_q_bytes(L, (size_t)B * n_tok);
 }
 
 hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const int64_t* pos,
@@ -558,15 +588,19 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
     return s;
   size_t a_q, a_idx, a_sel, a_attn;
   draft_parts(L, B, n_tok, max_pos, &a_q, &a_idx, &a_sel, &a_attn);
-  if ((s = check_ws(ws, ws_bytes, a_q + a_idx + a_sel + a_attn)) != HSA_OK) return s;
-  char* base = (char*)ws;
   const size_t n = (size_t)B * n_tok;
+  const size_t a_rq = rope_q_bytes(L, n);
+  if ((s = check_ws(ws, ws_bytes, a_q + a_idx + a_sel + a_attn + a_rq)) != HSA_OK) return s;
+  char* base = (char*)ws;
   int64_t* q_pos = (int64_t*)base;
   int32_t* q_req = (int32_t*)(base + rnd256(sizeof(int64_t) * n));
+  void* q_rot = a_rq ? base + a_q + a_idx + a_sel + a_attn : nullptr;
+  const void* Qa = a_rq ? q_rot : Q;
   // 1-2: every draft token appended in order (rings, tail, completed blocks);
-  // the queries' positions and requests land in the workspace
+  // the queries' positions and requests (and, with RoPE, the turned queries)
+  // land in the workspace
   hipError_t e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream, n_tok,
-                                      q_pos, q_req);
+                                      q_pos, q_req, Q, q_rot);
   if (e != hipSuccess) return hip_status(e, "decode_draft update");
   // 3: query i of request b at position pos[b] + i sees exactly what a
   // single-token step at that position would (a block completed later in the
@@ -581,11 +615,11 @@ hsa_status hsa_decode_draft(const hsa_layer* L, int32_t B, int32_t n_tok, const 
     e = launch_indexer(q, qI, w, L->kic, L->m, L->n_win, L->topk, sel, nullptr, base + a_q,
                        a_idx, stream, nullptr, draft_group(n_tok));
     if (e != hipSuccess) return hip_status(e, "decode_draft indexer");
-    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
+    e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_q + a_idx + a_sel, a_attn,
                     stream);
   } else {
-    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
+    e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
                     L->scale, O, L->o_dtype, lse, base + a_q, a_attn, stream);
   }
   return hip_status(e, "decode_draft attention");

@@ -12,6 +12,7 @@ constexpr int kD = 128;        // head dim of Q/K/V
 constexpr int kDI = 64;        // indexer head dim
 constexpr int kHI = 4;         // indexer heads
 constexpr int kPage = 64;      // entries per cache page
+constexpr int kRopeDim = 64;   // rotated channels: the last 64 of a key row or a query head
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -31,6 +32,32 @@ __device__ __forceinline__ u16 f64_to_bf16(double x) {
   double q = ldexp(1.0, ee - 7);            // bf16 quantum in that binade
   double v = __builtin_rint(x / q) * q;     // exact scaling, one rounding
   return (u16)(__float_as_uint((float)v) >> 16);   // v is a bf16 value: exact
+}
+
+// ---------------------------------------------------------------- positional rotation
+// Partial RoPE (group-reading wiki "DeepSeek-V4 深度研究剖析" §8 keeps these
+// channels of the KV cache in bf16): the last kRopeDim channels of a key row or
+// of a query head turn as adjacent pairs (d-64+2i, d-63+2i) by the angle p * f_i
+// at position p, with f_i = theta^(-2i/64) held in fp32.  The angle, its cos and
+// sin and the turn are float64 (each product rounded, then the sum: no fused
+// multiply-add); the result is rounded once to bf16.
+struct RopeTab {
+  double f[kRopeDim / 2];   // f_i: the fp32 table's values
+};
+RopeTab make_rope_tab(double theta);   // host
+
+// Channel `odd` of a pair (x, y) turned by the angle whose cos / sin are c / s.
+__device__ __forceinline__ double rope_turn(double x, double y, double c, double s, bool odd) {
+#pragma clang fp contract(off)
+  return odd ? x * s + y * c : x * c - y * s;
+}
+
+// A bf16 pair (the even channel in the low half) turned by the angle whose
+// cos / sin are c / s.
+__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t w, double c, double s) {
+  const double x = bf16_to_f32((u16)(w & 0xFFFFu)), y = bf16_to_f32((u16)(w >> 16));
+  return (uint32_t)f64_to_bf16(rope_turn(x, y, c, s, false)) |
+         ((uint32_t)f64_to_bf16(rope_turn(x, y, c, s, true)) << 16);
 }
 
 // float64 -> OCP fp8 e4m3fn code (ties to even; saturates at +-448; the sign
@@ -262,14 +289,21 @@ hipError_t launch_pooling_weights(const float* z, int m, int dim, float* alpha, 
 hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out, int req,
                            int64_t first, int64_t n, int m, const float* alpha, hipStream_t s);
 
+// rows of `heads` bf16 heads of `dim` channels: y = x with the last 64 channels
+// of every head turned at the row's position (pos[i], or pos0 + i); y == x
+// rotates in place, otherwise the other channels are copied
+hipError_t launch_rope(const void* x, void* y, int64_t n_rows, int heads, int dim,
+                       const int64_t* pos, int64_t pos0, double theta, hipStream_t s);
+
 struct UpdateArgs;   // update.h
 
 // group > 1 (listed queries): the draft scan's workspace shape
 size_t indexer_ws_bytes(int n_q, int64_t max_nvis, int k, bool span, int group = 1);
 int64_t indexer_max_blocks();   // longest visible-block row the decode indexer takes
 // upd: when not null, the decode cache upkeep of request i runs in the scan
-// launch (bf16 caches: one extra workgroup per request), in the candidate
-// selection launch (fp8 caches, long rows) or in its own launch before the scan
+// launch (bf16 caches without RoPE: one extra workgroup per request), in the
+// candidate selection launch (fp8 caches or RoPE, long rows) or in its own
+// launch before the scan
 hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                           const hsa_paged& kic, int m, int n_win, int k, int32_t* idx,
                           float* score, void* ws, size_t ws_bytes, hipStream_t s,
@@ -293,14 +327,17 @@ hipError_t launch_update(const UpdateArgs& u, int B, hipStream_t s);
 // n_entries of request b := keep[b] / m in every cache of the layer
 hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, hipStream_t s);
 
+// Q / q_rot: with L.rope_theta > 0 the upkeep writes the queries Q turned to q_rot
 UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
-                            const void* k_new, const void* v_new, const void* kI_new);
+                            const void* k_new, const void* v_new, const void* kI_new,
+                            const void* Q = nullptr, void* q_rot = nullptr);
 // n_tok > 1: a draft of n_tok tokens per request (rows b * n_tok + i of the
 // new-token arrays), appended in order; q_pos / q_req (or null) receive the
 // request and position of each of the draft's queries
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
                                 hipStream_t s, int n_tok = 1, int64_t* q_pos = nullptr,
-                                int32_t* q_req = nullptr);
+                                int32_t* q_req = nullptr, const void* Q = nullptr,
+                                void* q_rot = nullptr);
 
 }  // namespace hsa

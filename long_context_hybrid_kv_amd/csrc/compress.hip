@@ -216,9 +216,10 @@ hipError_t launch_decode_rewind(const hsa_layer& L, int B, const int64_t* keep, 
 }
 
 UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_pos,
-                            const void* k_new, const void* v_new, const void* kI_new) {
+                            const void* k_new, const void* v_new, const void* kI_new,
+                            const void* Q, void* q_rot) {
   const int csa = L.kind == HSA_LAYER_CSA;
-  UpdateArgs u;
+  UpdateArgs u{};
   u.rk = to_dev(L.ring_k);
   u.rv = to_dev(L.ring_v);
   u.ti = csa ? to_dev(L.tail_i) : Tokens{nullptr, 1, kDI};
@@ -238,6 +239,11 @@ UpdateArgs make_update_args(const hsa_layer& L, const int64_t* pos, int64_t max_
   u.n_tok = 1;
   u.q_pos = nullptr;
   u.q_req = nullptr;
+  u.rope_on = L.rope_theta > 0.0;
+  if (u.rope_on) u.rope = make_rope_tab(L.rope_theta);
+  u.q_in = (const u16*)Q;
+  u.q_out = u.rope_on ? (u16*)q_rot : nullptr;
+  u.H = L.H;
   return u;
 }
 
@@ -248,8 +254,9 @@ hipError_t launch_update(const UpdateArgs& u, int B, hipStream_t s) {
 
 hipError_t launch_decode_update(const hsa_layer& L, int B, const int64_t* pos, int64_t max_pos,
                                 const void* k_new, const void* v_new, const void* kI_new,
-                                hipStream_t s, int n_tok, int64_t* q_pos, int32_t* q_req) {
-  UpdateArgs u = make_update_args(L, pos, max_pos, k_new, v_new, kI_new);
+                                hipStream_t s, int n_tok, int64_t* q_pos, int32_t* q_req,
+                                const void* Q, void* q_rot) {
+  UpdateArgs u = make_update_args(L, pos, max_pos, k_new, v_new, kI_new, Q, q_rot);
   u.n_tok = n_tok;
   u.q_pos = q_pos;
   u.q_req = q_req;

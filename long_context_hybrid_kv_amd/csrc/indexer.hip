@@ -401,7 +401,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
                                                        int* fault) {
   const int qrow = blockIdx.y;
   if ((int)blockIdx.x >= n_groups) {   // the extra column: cache upkeep of request qrow
-    decode_update_body<false>(upd, qrow, fault);   // bf16 caches only (the host's rule)
+    decode_update_body<false>(upd, qrow, fault);   // bf16 caches, no RoPE (the host's rule)
     return;
   }
   const int c_first = blockIdx.x * CPW;
@@ -1679,21 +1679,22 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     // candidates and one kernel selects from them (two launches instead of the
     // threshold / select / refine chain)
     const bool cand = R > kFusedMaxBlocksDecode && R / 32 <= kCandBmMaxWords;
-    // the decode cache upkeep: bf16 K / V caches in the scan launch; fp8 ones
-    // (page re-encoding, whose registers the scan should not carry) in the
-    // candidate selection launch, or on their own before the scan
-    const bool f8upd = upd && (upd->kc.dtype != HSA_BF16 || upd->vc.dtype != HSA_BF16);
-    if (f8upd && !cand) {
+    // the decode cache upkeep: plain bf16 K / V caches in the scan launch; the
+    // full upkeep (fp8 page re-encoding, RoPE: registers the scan should not
+    // carry) in the candidate selection launch, or on its own before the scan
+    const bool full_upd = upd && (upd->kc.dtype != HSA_BF16 || upd->vc.dtype != HSA_BF16 ||
+                               upd->rope_on);
+    if (full_upd && !cand) {
       hipError_t e = launch_update(*upd, q.n, s);
       if (e != hipSuccess) return e;
     }
-    const dim3 grid(n_groups + (upd && !f8upd ? 1 : 0), q.n);
+    const dim3 grid(n_groups + (upd && !full_upd ? 1 : 0), q.n);
     timed_launch(HSA_K_INDEXER_SCAN, scan, grid, dim3(8 * 64), 0, s, Qd, (const u16*)qI, w, kc, m,
                  n_win, k, ws, (int)n_groups, ua, cand ? k : 0, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     if (cand) {
       const size_t lds = (size_t)kThrCandMax * sizeof(uint64_t) + (size_t)(R / 32) * sizeof(uint32_t);
-      const unsigned g = (unsigned)q.n + (f8upd ? (unsigned)q.n : 0u);
+      const unsigned g = (unsigned)q.n + (full_upd ? (unsigned)q.n : 0u);
       if (s16)
         idx_cand_kernel<true><<<g, 1024, lds, s>>>(k, ws, idx, score, q.n, ua, fault);
       else

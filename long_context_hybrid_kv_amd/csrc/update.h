@@ -2,11 +2,12 @@
 // 深度研究剖析" §11.4: the raw window and the incomplete tail live in a state
 // cache; every m tokens the tail becomes one compressed entry).
 //
-// Shared by the standalone upkeep kernel (HCA layers) and by the indexer scan
-// kernel, which runs the upkeep of request b in one extra workgroup beside the
-// scan of request b (CSA layers): the block that completes at position t is
-// not visible to the query at t (it starts inside the window), so the scan
-// never reads what the upkeep writes in the same launch.
+// Shared by the standalone upkeep kernel (HCA layers, drafts), the indexer
+// scan kernel (plain bf16 CSA layers: one extra workgroup per request beside
+// its scan) and the candidate selection kernel (CSA layers with fp8 caches or
+// RoPE, long rows: extra workgroups beside the selection).  The block that
+// completes at position t is not visible to the query at t (it starts inside
+// the window), so nothing in the same launch reads what the upkeep writes.
 #pragma once
 #include "common.h"
 
@@ -27,6 +28,14 @@ struct UpdateArgs {
   int n_tok;                         // tokens per request (a draft: n_tok > 1)
   int64_t* q_pos;                    // [B * n_tok] positions of the draft's queries, or null
   int32_t* q_req;                    // [B * n_tok] their requests
+  // partial RoPE (rope_on; the full upkeep only): each new key is turned at
+  // its position before it enters the ring, so a block pools turned keys, and
+  // the queries q_in [B * n_tok][H][128] are written turned to q_out
+  int rope_on;
+  RopeTab rope;
+  const u16* q_in;
+  u16* q_out;
+  int H;
 };
 
 // Pool block blk of channel c from the ring/tail; the newest token's own value
@@ -111,10 +120,10 @@ __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, 
 // at n_entries.  Threads 0..127 of the workgroup carry the channels (a thread
 // writes and pools its own channel, so tokens of one request are handled in
 // order without cross-thread hand-off); every thread of the workgroup must call
-// this (it synchronises the workgroup).  F8: the K / V caches may be fp8 (the
-// standalone upkeep kernel); the indexer scan launch, which carries the upkeep
-// of bf16 CSA layers, is compiled without that path (its float64 page loops
-// would raise the scan's registers).
+// this (it synchronises the workgroup).  F8: the full upkeep -- the K / V
+// caches may be fp8, keys and queries may be turned (RoPE); the indexer scan
+// launch, which carries the upkeep of plain bf16 CSA layers, is compiled
+// without it (its float64 page loops would raise the scan's registers).
 template <bool F8>
 __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault) {
   const int c = threadIdx.x;
@@ -130,6 +139,20 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
   if (on) {
     kn = u.k_new[row * kD + c];
     vn = u.v_new[row * kD + c];
+  }
+  if constexpr (F8) {
+    if (u.rope_on) {   // uniform: every lane takes part in the exchange
+      const u16 other = (u16)__shfl_xor((int)kn, 1);
+      if (on && c >= kD - kRopeDim) {
+        const bool odd = c & 1;
+        double sn, cs;
+        sincos((double)p * u.rope.f[(c - (kD - kRopeDim)) >> 1], &sn, &cs);
+        const double x = bf16_to_f32(odd ? other : kn), y = bf16_to_f32(odd ? kn : other);
+        kn = f64_to_bf16(rope_turn(x, y, cs, sn, odd));
+      }
+    }
+  }
+  if (on) {
     u.rk.row(b, p)[c] = kn;
     u.rv.row(b, p)[c] = vn;
   }
@@ -167,6 +190,36 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
   }
 }
 
+// Request b's n_tok queries turned for the attention (F8 upkeep, rope_on):
+// the angles' cos / sin once per query in LDS, then the query's 32-bit words,
+// the RoPE pairs turned and the other channels copied.  A position outside
+// [0, max_pos] (reported by the token step) is clamped, as the attention does.
+__device__ inline void rope_queries(const UpdateArgs& u, int b) {
+  __shared__ double qcs[kRopeDim / 2][2];
+  const int words = u.H * (kD / 2);
+  for (int i = 0; i < u.n_tok; ++i) {
+    int64_t p = u.pos[b] + i;
+    p = p < 0 ? 0 : (p > u.max_pos ? u.max_pos : p);
+    __syncthreads();   // the previous query's angles are no longer read
+    if (threadIdx.x < kRopeDim / 2) {
+      double sn, cs;
+      sincos((double)p * u.rope.f[threadIdx.x], &sn, &cs);
+      qcs[threadIdx.x][0] = cs;
+      qcs[threadIdx.x][1] = sn;
+    }
+    __syncthreads();
+    const int64_t q0 = ((int64_t)b * u.n_tok + i) * u.H * kD;
+    const uint32_t* src = (const uint32_t*)(u.q_in + q0);
+    uint32_t* dst = (uint32_t*)(u.q_out + q0);
+    for (int wi = threadIdx.x; wi < words; wi += blockDim.x) {
+      const int j = wi & (kD / 2 - 1);   // word within the head
+      const int f = j - (kD - kRopeDim) / 2;
+      const uint32_t w = src[wi];
+      dst[wi] = f >= 0 ? rope_pair_bf16(w, qcs[f][0], qcs[f][1]) : w;
+    }
+  }
+}
+
 // Request b's n_tok tokens in order, and (a draft) its queries' request and
 // position for the selection and attention that follow.
 template <bool F8>
@@ -175,6 +228,8 @@ __device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault
     decode_update_token<F8>(u, b, i, fault);
     __syncthreads();   // the next token's block check reuses the shared flag
   }
+  if constexpr (F8)
+    if (u.q_out) rope_queries(u, b);
   if (u.q_pos)
     for (int i = threadIdx.x; i < u.n_tok; i += blockDim.x) {
       u.q_pos[(int64_t)b * u.n_tok + i] = u.pos[b] + i;

@@ -104,7 +104,7 @@ def scale_of(d=128):
 # ----------------------------------------------------------------------------- decode state
 
 def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False,
-                kmix=False, tail_cap=None, stash=False):
+                kmix=False, tail_cap=None, stash=False, rope=0.0):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
     hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)
@@ -112,7 +112,9 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     m + n - 1).  stash: fp8 K / V caches carry the stash that appending to them
     needs (hsa_kv_compress fills it for the last page).
     index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page).
-    kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8."""
+    kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8.
+    rope > 0: the history's keys are turned at their positions (hsa_rope)
+    before they are compressed and put in the ring, as a RoPE layer holds them."""
     B = len(Ls)
     m = w.m(layer)
     n_win = w.n_win
@@ -141,13 +143,17 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     for r, d in enumerate(reqs):
         Lr = int(Ls[r])
         nb = Lr // m
+        k_hist = dev_bf16(d["k"][:Lr])
+        if rope > 0:
+            k_hist = L.rope(k_hist, rope)
         for name, x, a in [("kc", "k", "alpha_k"), ("vc", "v", "alpha_v")] + \
                 ([("kic", "ki", "alpha_i")] if layer == "csa" else []):
             if nb > 0:
-                L.kv_compress(tokens(d[x][:Lr]), st[name], r, 0, nb, m, st[a])
+                src = L.Tokens(k_hist[None].contiguous()) if x == "k" else tokens(d[x][:Lr])
+                L.kv_compress(src, st[name], r, 0, nb, m, st[a])
         lo = max(0, Lr - n_win)
         slots = torch.arange(lo, Lr) % cap
-        ring_k[r, slots] = dev_bf16(d["k"][lo:Lr])
+        ring_k[r, slots] = k_hist[lo:Lr]
         ring_v[r, slots] = dev_bf16(d["v"][lo:Lr])
         if layer == "csa":
             t0 = nb * m
@@ -185,10 +191,10 @@ def run_ops(w, layer, st, Ls, s=0):
     return out
 
 
-def layer_of(w, layer, st):
+def layer_of(w, layer, st, rope=0.0):
     kw = dict(kind=L.LAYER_CSA if layer == "csa" else L.LAYER_HCA, H=w.H, n_win=w.n_win,
               m=w.m(layer), alpha_k=st["alpha_k"], alpha_v=st["alpha_v"], ring_k=st["ring_k"],
-              ring_v=st["ring_v"], kc=st["kc"], vc=st["vc"], out_fp32=True)
+              ring_v=st["ring_v"], kc=st["kc"], vc=st["vc"], out_fp32=True, rope_theta=rope)
     if layer == "csa":
         kw.update(topk=w.k_csa, alpha_i=st["alpha_i"], tail_i=st["tail_i"], kic=st["kic"])
     return L.Layer(**kw)

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) <= set(L._SIGS), "binding misses a declared entry point"
-    assert lib.hsa_abi_version() == 2
+    assert lib.hsa_abi_version() == 3
 
 
 def test_status_strings():
@@ -254,3 +254,44 @@ def test_noalloc_step_refuses_steps_beyond_its_scratch():
     assert lib.hsa_decode_step_noalloc(C.byref(Lr), 64, f, 4 << 20, f, f, f, f, f, f, f, None,
                                        None, None) == -3
     assert b"scratch" in lib.hsa_last_error()
+
+
+def test_rope_validation():
+    """hsa_rope: heads >= 1, dim a multiple of 8 in [64, 4096], theta > 0 and
+    finite, 16-byte aligned rows, y equal to x or apart from it, positions
+    that cannot overflow; an empty call is a no-op."""
+    lib = L.lib()
+    f, g = C.c_void_p(0x1000), C.c_void_p(0x1000 + 64 * 128 * 2)
+    r = lambda x=f, y=f, n=64, h=1, d=128, pos=None, p0=0, th=10000.0: lib.hsa_rope(
+        x, y, n, h, d, pos, p0, th, None)
+    assert r(n=0, x=None, y=None) == 0
+    assert r(x=None) == -1
+    assert r(n=-1) == -1
+    assert r(h=0) == -1
+    assert r(d=32) == -1 and r(d=100) == -1
+    assert r(th=0.0) == -1 and r(th=-1.0) == -1 and r(th=float("inf")) == -1
+    assert r(x=C.c_void_p(0x1008)) == -1                     # not 16-byte aligned
+    assert r(y=C.c_void_p(0x1000 + 128)) == -1                # overlaps x, not equal
+    assert r(p0=-1) == -1
+    assert r(p0=(1 << 63) - 10) == -1                         # pos0 + n overflows
+    assert b"rope" in lib.hsa_last_error()
+
+
+def test_decode_rope_theta_rules_and_workspace():
+    """A layer's rope_theta must be finite and >= 0; with RoPE the step's
+    workspace also holds the turned queries (B x H x 128 bf16)."""
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    Lr = _csa_layer(tail_cap=4)
+    base = lib.hsa_decode_step_workspace_bytes(C.byref(Lr), 2, 1000)
+    Lr.rope_theta = 10000.0
+    with_rope = lib.hsa_decode_step_workspace_bytes(C.byref(Lr), 2, 1000)
+    assert with_rope >= base + 2 * 64 * 128 * 2
+    d0 = lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), 2, 3, 1000)
+    Lr.rope_theta = 0.0
+    assert d0 >= lib.hsa_decode_draft_workspace_bytes(C.byref(Lr), 2, 3, 1000) + 6 * 64 * 128 * 2
+    for bad in (-1.0, float("nan"), float("inf")):
+        Lr.rope_theta = bad
+        assert lib.hsa_decode_step(C.byref(Lr), 1, f, 1000, f, f, f, f, f, f, f, None, None, f,
+                                   1 << 30, None) == -1
+        assert b"rope_theta" in lib.hsa_last_error()
