@@ -64,13 +64,19 @@ __device__ __forceinline__ int64_t entry_block(const AttnArgs& a, const Prefetch
 __device__ __forceinline__ int entry_page(const AttnArgs& a, const Paged& c, const Prefetch& pf,
                                           int which, int r, int64_t b);
 
+// Ring slot of window row ge: the window start's slot w0 (= s0 mod capacity,
+// computed once per workgroup) plus ge, wrapped once (ge < n_win <= capacity)
+__device__ __forceinline__ int64_t ring_slot(int64_t w0, int ge, int64_t cap) {
+  const int64_t sl = w0 + ge;
+  return sl >= cap ? sl - cap : sl;
+}
+
 __device__ __forceinline__ void resolve(const AttnArgs& a, const Prefetch& pf, int qi, int r,
-                                        int64_t s0, int n_w, int E, int64_t nv, int ge, int* rk,
-                                        int* rv) {
+                                        int64_t w0k, int64_t w0v, int n_w, int E, int64_t nv,
+                                        int ge, int* rk, int* rv) {
   if (ge < n_w) {
-    const int64_t p = s0 + ge;
-    *rk = -2 - (int)((int64_t)r * a.wk.capacity + p % a.wk.capacity);
-    *rv = -2 - (int)((int64_t)r * a.wv.capacity + p % a.wv.capacity);
+    *rk = -2 - (int)((int64_t)r * a.wk.capacity + ring_slot(w0k, ge, a.wk.capacity));
+    *rv = -2 - (int)((int64_t)r * a.wv.capacity + ring_slot(w0v, ge, a.wv.capacity));
     return;
   }
   *rk = *rv = kZeroRow;
@@ -125,13 +131,12 @@ __device__ __align__(16) uint4 g_zero_row[16];
 // bf16 caches: the address of entry ge's K and V rows (window row, pool row, or
 // the zero row), so that a chunk's gathers are one load per 16-byte piece.
 __device__ __forceinline__ void resolve_ptr(const AttnArgs& a, const Prefetch& pf, int qi, int r,
-                                            int64_t s0, int n_w, int E, int64_t nv, int ge,
-                                            const uint8_t** pk, const uint8_t** pv) {
+                                            int64_t w0k, int64_t w0v, int n_w, int E, int64_t nv,
+                                            int ge, const uint8_t** pk, const uint8_t** pv) {
   const uint8_t* zero = (const uint8_t*)g_zero_row;
   if (ge < n_w) {
-    const int64_t p = s0 + ge;
-    *pk = a.wk.data + ((int64_t)r * a.wk.capacity + p % a.wk.capacity) * (kD * 2);
-    *pv = a.wv.data + ((int64_t)r * a.wv.capacity + p % a.wv.capacity) * (kD * 2);
+    *pk = a.wk.data + ((int64_t)r * a.wk.capacity + ring_slot(w0k, ge, a.wk.capacity)) * (kD * 2);
+    *pv = a.wv.data + ((int64_t)r * a.wv.capacity + ring_slot(w0v, ge, a.wv.capacity)) * (kD * 2);
     return;
   }
   *pk = *pv = zero;
@@ -383,11 +388,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // ---- resolve the rows of every entry of this split once
   const int e_base = c_lo * 64;
   const int n_ent = (c_hi > c_lo) ? (c_hi - c_lo) * 64 : 0;
+  // the window start's ring slots: one division per workgroup (s0 is uniform)
+  const int64_t w0k = s0 % a.wk.capacity, w0v = s0 % a.wv.capacity;
   for (int j = tid; j < n_ent; j += NT) {
     if constexpr (F8)
-      resolve(a, pf, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
     else
-      resolve_ptr(a, pf, qi, r, s0, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve_ptr(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
   }
 
   __syncthreads();
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 // splits the launch has.  The first kMergePF partial rows are requested before
 // the (m, l) pairs are reduced.
 constexpr int kMergeMaxSplits = 1024;
-constexpr int kMergePF = 32;          // partial rows a lane requests up front
+constexpr int kMergePF = 64;          // partial rows a lane requests up front (HCA: 44 splits at 1M)
 __global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
                                                         const u16* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
@@ -786,12 +793,14 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
   const uint8_t** rowv = rowk + a.cps * 64;
   {
     const uint8_t* zero = (const uint8_t*)g_zero_row;
+    // n_wu <= n_win + 1 rows from s0: at most one wrap of a ring whose
+    // capacity the host checked (>= n_win + 1, or every position fits)
+    const int64_t w0k = s0 % a.wk.capacity, w0v = s0 % a.wv.capacity;
     for (int j = tid; j < n_chunks * 64; j += NT) {
       const uint8_t *pk = zero, *pv = zero;
       if (j < n_wu) {
-        const int64_t p = s0 + j;
-        pk = a.wk.data + ((int64_t)r * a.wk.capacity + p % a.wk.capacity) * (kD * 2);
-        pv = a.wv.data + ((int64_t)r * a.wv.capacity + p % a.wv.capacity) * (kD * 2);
+        pk = a.wk.data + ((int64_t)r * a.wk.capacity + ring_slot(w0k, j, a.wk.capacity)) * (kD * 2);
+        pv = a.wv.data + ((int64_t)r * a.wv.capacity + ring_slot(w0v, j, a.wv.capacity)) * (kD * 2);
       } else if (j < E) {
         const int64_t b = j - n_wu;
         const int pgk = a.kc.page_of(r, b, a.fault), pgv = a.vc.page_of(r, b, a.fault);
@@ -998,9 +1007,12 @@ struct AttnPlan {
 // CSA: a query has at most c = ceil((n_win + k) / 64) chunks; rows of up to 12
 // chunks (k = 512 with the 128-token window: 10) go in pairs, longer rows one
 // chunk per split (k = 1024: 18 splits, so that a batch of 4 still spreads
-// over the chip), and never more than 32 splits.  HCA: 4 chunks per split.
+// over the chip), and never more than 32 splits.  HCA: 3 chunks per split (a
+// batch of 4 at 1M tokens: 176 workgroups, one per CU with a chain of three
+// chunks; 4 chunks left 124 CUs idle behind a longer chain, and 2 chunks make
+// 260 workgroups, so that four CUs run two and set the kernel's time).
 int attn_decode_cps(int k, int n_win) {
-  if (k <= 0) return 4;
+  if (k <= 0) return 3;
   const int chunks = (n_win + k + 63) / 64;
   if (chunks <= 12) return 2;
   return (chunks + 31) / 32;

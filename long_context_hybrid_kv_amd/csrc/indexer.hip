@@ -58,9 +58,10 @@ constexpr int kBmLdsMaxWords = 16384;  // refine pass: bitmaps up to this size g
 constexpr int kSpanQC = 2048;      // prefill: queries per workspace pass
 // per-query state: [2] threshold bin, [3] blocks above it, [5] visible blocks,
 // [6] blocks in the threshold bin; the candidate path records instead in [6]
-// which selection served the query (0 the union; 1..4 the whole row: list
-// overflow, no threshold bin, cut at or above it, union incomplete) and in [7]
-// the union size << 16 | threshold-bin size
+// which selection served the query (0 the union; the whole row: 1 a list
+// overflowed, 2 no threshold bin, 3 a workgroup's cut at or above it, 4 the
+// threshold bin holds more than kThrCandMax) and in [7] the union size << 16 |
+// threshold-bin size
 constexpr int kStateInts = 8;
 constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
 // decode candidate selection (long rows): each scan workgroup hands over the
@@ -70,7 +71,7 @@ constexpr int kCandCap = 256;      // candidates a scan workgroup may write
 constexpr int kCandBmMaxWords = 16384;   // bitmap words of the emission in LDS
 constexpr int kTopBins = 16;       // nonzero bins >= its cut bin a scan workgroup may list
 constexpr int kThrCandMax = 4096;  // candidates of the threshold bin the selection refines in LDS
-constexpr int kUnionMax = 8192;    // candidates of a query the selection takes (8 per thread)
+constexpr int kCandMaxLists = 256;  // scan workgroups (lists) of a query the selection merges
 
 struct IdxWs {
   float* scores;        // [nq][R]
@@ -791,6 +792,14 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
       for (int i = 0; i < 4; ++i) wq[at][i] = w[(int64_t)(q_base + qg) * kHI + i];
     }
   }
+  // every query's visible blocks (clamped to the cache), for the selection
+  if (blockIdx.x == 0 && wv == 0 && row == 0) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      const int qg = 16 * qt + 4 * at + g;
+      if (qg < nq) ws.state[(int64_t)qg * kStateInts + 5] = (int32_t)nvq[at];
+    }
+  }
   {
     int ql = 16 * qt + 15 < nq ? 16 * qt + 15 : nq - 1;
     int64_t nv = n_visible(Q.span_pos0 + q_base + ql, m, n_win);
@@ -933,7 +942,10 @@ __global__ __launch_bounds__(256) void idx_hist_kernel(Queries Q, int q_base, co
 // candidates live in LDS when they fit (dynamic shared memory sized by the
 // host), else in the workspace.
 // mode 0: the whole selection; mode 1: threshold only (long rows, before the
-// multi-workgroup select kernel); mode 2: refine + emit only (after it).
+// multi-workgroup select kernel); mode 2: refine + emit only (after it); mode
+// 3: the whole selection with the query's histogram built from its own score
+// row instead of histogram lists (prefill: the scores are read from HBM once
+// and again from L2, and no histogram kernel runs).
 template <int NT, bool S16>
 __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
                                                       float* __restrict__ score, int out_row0,
@@ -956,7 +968,8 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   constexpr int U = NT >= 1024 ? 32 : 16;
   float sc0[U];
   uint32_t raw0[S16 ? U : 1];
-  if (mode == 0) {
+  const bool whole = mode == 0 || mode == 3;
+  if (whole) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t b = (int64_t)u * NT + tid;
@@ -1001,6 +1014,26 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
     // step costs one memory round trip; entries past a list's count are
     // ignored.
     uint32_t* lh = (uint32_t*)dyn;
+    if (mode == 3) {
+      // the row's own histogram: the first round from the scores already
+      // loaded, the rest in rounds of U loads per thread
+      for (int i = tid; i < kBins; i += NT) lh[i] = 0;
+      __syncthreads();
+      for (int64_t base = 0; base < nv; base += (int64_t)NT * U) {
+        float hv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t b = base + (int64_t)u * NT + tid;
+          float s0;
+          if constexpr (S16) s0 = __uint_as_float(raw0[u] << 16);
+          else s0 = sc0[u];
+          hv[u] = base == 0 ? s0 : score_get<S16>(srow, b, nv, ws.R);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (base + (int64_t)u * NT + tid < nv) atomicAdd(&lh[order_key(hv[u]) >> 20], 1u);
+      }
+    } else {
     const int32_t* hn = ws.hl_n + (int64_t)qrow * ws.n_lists;
     const uint32_t* hlq = ws.hl + (int64_t)qrow * ws.n_lists * ws.list_cap;
     constexpr int NWV = NT / 64, LB = 8;
@@ -1036,6 +1069,7 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
           atomicAdd(&lh[e >> 16], e & 0xFFFFu);
         }
       }
+    }
     }
     __syncthreads();
     uint32_t v[BPT];
@@ -1120,7 +1154,7 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   uint32_t* bm = bm_in_lds ? bm_l : ws.bitmap + (int64_t)qrow * (ws.R / 32);
 
   // ---- one pass over the scores: bitmap of blocks above the bin, candidates in it
-  for (int64_t base = 0; mode == 0 && base < nv; base += (int64_t)NT * U) {
+  for (int64_t base = 0; whole && base < nv; base += (int64_t)NT * U) {
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1383,11 +1417,15 @@ __device__ uint64_t radix_kth(int64_t n, int k, KeyFn key, int bits, uint64_t pr
 // Workgroups past the queries (blockIdx.x >= n_q) run the decode cache upkeep
 // of request blockIdx.x - n_q, fp8 caches included: the selection reads no
 // cache, and the attention that reads them is the next launch.
+// (one 1024-thread workgroup per CU is all it needs: four waves per SIMD, so
+// the registers of four, and no spill of the many scalar arguments to memory)
 template <bool S16>
-__global__ __launch_bounds__(1024) void idx_cand_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void idx_cand_kernel(int k, IdxWs ws, int32_t* __restrict__ idx,
                                                         float* __restrict__ score, int n_q,
                                                         UpdateArgs upd, int* fault) {
   constexpr int NT = 1024, BPT = kBins / NT;
+  constexpr int TB = kTopBins * kCandMaxLists / NT;   // top-bin slots a thread loads
+  constexpr int SPEC = 8;                              // candidates a thread loads up front
   if ((int)blockIdx.x >= n_q) {
     decode_update_body<true>(upd, blockIdx.x - n_q, fault);
     return;
@@ -1398,51 +1436,88 @@ __global__ __launch_bounds__(1024) void idx_cand_kernel(int k, IdxWs ws, int32_t
   __shared__ uint32_t sh[NT / 64];
   __shared__ uint32_t h256[256];
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t s_off[NT + 1];
-  __shared__ uint8_t s_ntop[NT];
-  __shared__ int s_bad, s_maxbc, s_thr;
-  __shared__ uint32_t s_above, s_ntc;
-  const int qrow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ int16_t s_cnt[kCandMaxLists];               // candidates of each live list
+  __shared__ uint8_t s_ntop[kCandMaxLists];              // top bins of each live list
+  __shared__ int s_bad, s_maxbc, s_thr, s_ovf;
+  __shared__ uint32_t s_above, s_ntc, s_tot;
+  const int qrow = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   int32_t* st = ws.state + (int64_t)qrow * kStateInts;
-  const int64_t nv = st[5];
   const void* srow = score_row<S16>(ws, qrow);
   int32_t* irow = idx + (int64_t)qrow * k;
   float* srow_out = score ? score + (int64_t)qrow * k : nullptr;
+  // ---- every load the selection needs is issued before any is used: the
+  // row length, each scan workgroup's count, cut bin, top-bin count and top
+  // bins, and the first cov candidates of every list (tpl threads per list,
+  // SPEC keys each; only a tie storm makes a list longer, read in a second
+  // pass).  Lists past the row's own (a shorter row in the batch) are masked
+  // once its length is known.
+  const int nl = ws.n_lists;
+  const int64_t wrow = (int64_t)qrow * nl;
+  const int64_t nv = st[5];
+  int cnt = 0, bcw = -1, ntop = 0;
+  if (tid < nl) {
+    cnt = ws.wcnt[wrow + tid];
+    bcw = ws.wbin[wrow + tid];
+    ntop = ws.wntop[wrow + tid];
+  }
+  uint32_t e[TB];
+#pragma unroll
+  for (int r = 0; r < TB; ++r) {
+    const int slot = r * NT + tid;
+    e[r] = slot / kTopBins < nl ? ws.wtop[wrow * kTopBins + slot] : 0u;
+  }
+  const int tpl = NT / nl;                                // threads per list (>= 4)
+  const int lg = tid / tpl, sub = tid - lg * tpl;
+  const int cov = tpl * SPEC < kCandCap ? tpl * SPEC : kCandCap;
+  uint64_t xs[SPEC];
+#pragma unroll
+  for (int u = 0; u < SPEC; u += 2) {
+    const int j = sub * SPEC + u;
+    const uint4 v = (lg < nl && j < cov)
+                        ? *(const uint4*)(ws.wcand + (wrow + lg) * kCandCap + j)
+                        : make_uint4(0, 0, 0, 0);
+    xs[u] = ((uint64_t)v.y << 32) | v.x;
+    xs[u + 1] = ((uint64_t)v.w << 32) | v.z;
+  }
   const int64_t W = (nv + 31) / 32;
   for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) hist[tid + NT * j] = 0;
-  if (tid == 0) { s_bad = 0; s_maxbc = -1; s_thr = -1; s_above = 0; s_ntc = 0; }
+  if (tid == 0) {
+    s_bad = 0; s_maxbc = -1; s_thr = -1; s_ovf = 0; s_above = 0; s_ntc = 0; s_tot = 0;
+  }
+  const int n_wg = (int)((nv + ws.list_span - 1) / ws.list_span);   // this row's lists
+  if (tid < nl) {
+    const bool live = tid < n_wg;
+    s_cnt[tid] = (int16_t)(live ? (cnt < kCandCap ? cnt : kCandCap) : 0);
+    s_ntop[tid] = (uint8_t)(live ? (ntop < kTopBins ? ntop : kTopBins) : 0);
+  }
+  __syncthreads();
+  uint32_t tot = 0;
   if (nv > k) {
-    const int n_wg = (int)((nv + ws.list_span - 1) / ws.list_span);
-    const int64_t wrow = (int64_t)qrow * ws.n_lists;
-    const int cnt = tid < n_wg ? ws.wcnt[wrow + tid] : 0;
-    const int bcw = tid < n_wg ? ws.wbin[wrow + tid] : -1;
-    const int ntop = tid < n_wg ? ws.wntop[wrow + tid] : 0;
-    uint32_t tot;
-    const uint32_t off = block_scan_nt<NT>((uint32_t)(cnt < kCandCap ? cnt : kCandCap), &tot, sh);
-    if (tid < n_wg) {
-      s_off[tid] = off;
-      s_ntop[tid] = (uint8_t)(ntop < kTopBins ? ntop : kTopBins);
-    }
-    if (tid == 0) s_off[n_wg] = tot;
-    if (cnt > kCandCap || ntop > kTopBins) atomicOr(&s_bad, 1);
-    if (tot > (uint32_t)kUnionMax && tid == 0) atomicOr(&s_bad, 1);
-    if (bcw >= 0) atomicMax(&s_maxbc, bcw);
-    __syncthreads();
-    // the union's histogram from the workgroups' top-bin lists: every entry's
-    // load is issued before any is used (n_wg * kTopBins <= 16 per thread)
-    {
-      constexpr int PER = (NT * kTopBins) / NT;   // list slots per thread, n_wg <= NT
-      uint32_t e[PER];
+    {   // the live lists' flags, largest cut and sum: one atomic per wave
+      const bool live = tid < nl && tid < n_wg;
+      const bool bad = live && (cnt > kCandCap || ntop > kTopBins), ovf = live && cnt > cov;
+      int mbc = live ? bcw : -1;
+      uint32_t sum = live ? (uint32_t)cnt : 0u;
 #pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int slot = r * NT + tid, g = slot / kTopBins, j = slot % kTopBins;
-        e[r] = (g < n_wg && j < s_ntop[g]) ? ws.wtop[(wrow + g) * kTopBins + j] : 0u;
+      for (int o = 32; o > 0; o >>= 1) {
+        mbc = max(mbc, __shfl_xor(mbc, o));
+        sum += __shfl_xor(sum, o);
       }
+      const uint64_t bb = __ballot(bad), bo = __ballot(ovf);
+      if (lane == 0 && tid < nl) {
+        if (bb) atomicOr(&s_bad, 1);
+        if (bo) atomicOr(&s_ovf, 1);
+        if (mbc >= 0) atomicMax(&s_maxbc, mbc);
+        atomicAdd(&s_tot, sum);
+      }
+    }
+    // the union's histogram from the workgroups' top-bin lists
 #pragma unroll
-      for (int r = 0; r < PER; ++r)
-        if (e[r]) atomicAdd(&hist[e[r] >> 16], e[r] & 0xFFFFu);
+    for (int r = 0; r < TB; ++r) {
+      const int slot = r * NT + tid, g = slot / kTopBins, j = slot % kTopBins;
+      if (g < nl && j < s_ntop[g] && e[r] != 0u) atomicAdd(&hist[e[r] >> 16], e[r] & 0xFFFFu);
     }
     __syncthreads();
     // threshold bin: thread t owns bins kBins - BPT(t+1) .. kBins - BPT t - 1
@@ -1468,31 +1543,13 @@ __global__ __launch_bounds__(1024) void idx_cand_kernel(int k, IdxWs ws, int32_t
     __syncthreads();
     // the union holds the row's top-k iff every score left out lies in a bin
     // below the threshold bin
+    tot = s_tot;
     bool full = s_bad != 0 || s_thr < 0 || s_thr < s_maxbc;
     if (!full) {
       const int thr = s_thr;
-      // one pass over the candidates: above the bin -> bitmap, in it -> refine
-      // every candidate load in flight before any is used (tot <= kUnionMax)
-      constexpr int PER = kUnionMax / NT;
-      uint64_t xs[PER];
-#pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const uint32_t i = (uint32_t)(r * NT + tid);
-        xs[r] = 0;
-        if (i < tot) {
-          int a = 0, b = n_wg;                // s_off[a] <= i < s_off[b]
-          while (b - a > 1) {
-            const int mid = (a + b) >> 1;
-            if (s_off[mid] <= i) a = mid; else b = mid;
-          }
-          xs[r] = ws.wcand[(wrow + a) * kCandCap + (i - s_off[a])];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const uint32_t i = (uint32_t)(r * NT + tid);
-        const uint64_t x = xs[r];
-        const int bin = i < tot ? (int)(x >> 52) : -1;
+      // above the bin -> bitmap; in it -> the threshold-bin candidates
+      auto classify = [&](uint64_t x, bool valid) {
+        const int bin = valid ? (int)(x >> 52) : -1;
         if (bin > thr) {
           const uint32_t blk = ~(uint32_t)x;
           atomicOr(&bm[blk >> 5], 1u << (blk & 31));
@@ -1506,6 +1563,24 @@ __global__ __launch_bounds__(1024) void idx_cand_kernel(int k, IdxWs ws, int32_t
           cb = __shfl(cb, leader);
           const uint32_t p = cb + __popcll(cm & ((1ull << lane) - 1));
           if (c && p < (uint32_t)kThrCandMax) tc[p] = x;
+        }
+      };
+      const int my_cnt = lg < nl ? s_cnt[lg] : 0;
+#pragma unroll
+      for (int u = 0; u < SPEC; ++u) {
+        const int j = sub * SPEC + u;
+        classify(xs[u], j < my_cnt && j < cov);
+      }
+      if (s_ovf) {   // uniform: some list holds more than was read up front
+        for (int base = cov; base < kCandCap; base += tpl * SPEC) {
+          uint64_t y[SPEC];
+#pragma unroll
+          for (int u = 0; u < SPEC; ++u) {
+            const int j = base + sub * SPEC + u;
+            y[u] = j < my_cnt ? ws.wcand[(wrow + lg) * kCandCap + j] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < SPEC; ++u) classify(y[u], base + sub * SPEC + u < my_cnt);
         }
       }
       __syncthreads();
@@ -1592,18 +1667,19 @@ constexpr int64_t kFusedMaxBlocksPrefill = 65536;
 // pass that marks the bitmap, then one workgroup per query refines and emits.
 template <bool S16>
 static void launch_topk(int nt, int nq, int k, const IdxWs& ws, int32_t* idx, float* score,
-                        int out_row0, hipStream_t s) {
+                        int out_row0, hipStream_t s, bool self_hist = false) {
   const int64_t W = ws.R / 32;
   const int cand = nt == 1024 ? 2048 : 1024;
   if (ws.R <= (nt == 1024 ? kFusedMaxBlocksDecode : kFusedMaxBlocksPrefill)) {
     const int bm_words = (int)W;
     const size_t lds = (size_t)2 * cand * sizeof(uint64_t) + (size_t)bm_words * sizeof(uint32_t);
+    const int mode = self_hist ? 3 : 0;
     if (nt == 1024)
       idx_topk_kernel<1024, S16><<<nq, 1024, lds, s>>>(k, ws, idx, score, out_row0, cand,
-                                                       bm_words, 0);
+                                                       bm_words, mode);
     else
       idx_topk_kernel<256, S16><<<nq, 256, lds, s>>>(k, ws, idx, score, out_row0, cand,
-                                                     bm_words, 0);
+                                                     bm_words, mode);
     return;
   }
   // the threshold pass merges the histogram lists in (dynamic) LDS
@@ -1678,7 +1754,8 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     // long rows whose emission bitmap fits in LDS: the scan hands over
     // candidates and one kernel selects from them (two launches instead of the
     // threshold / select / refine chain)
-    const bool cand = R > kFusedMaxBlocksDecode && R / 32 <= kCandBmMaxWords;
+    const bool cand = R > kFusedMaxBlocksDecode && R / 32 <= kCandBmMaxWords &&
+                      ws.n_lists <= kCandMaxLists;
     // the decode cache upkeep: plain bf16 K / V caches in the scan launch; the
     // full upkeep (fp8 page re-encoding, RoPE: registers the scan should not
     // carry) in the candidate selection launch, or on its own before the scan
@@ -1728,12 +1805,15 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
                  s, Qd, q0, nq, (const u16*)qI, w, kc, m, n_win, ws, fault);
     KernelTimer kt(HSA_K_INDEXER_SEL, s);
     const dim3 hgrid(nv_hi > kHistSpan ? (unsigned)((nv_hi + kHistSpan - 1) / kHistSpan) : 1u, nq);
+    // rows the one-kernel selection takes build their histograms themselves;
+    // longer rows merge the lists of the histogram kernel
+    const bool self_hist = R <= kFusedMaxBlocksPrefill;
     if (s16) {
-      idx_hist_kernel<true><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
-      launch_topk<true>(256, nq, k, ws, idx, score, q0, s);
+      if (!self_hist) idx_hist_kernel<true><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+      launch_topk<true>(256, nq, k, ws, idx, score, q0, s, self_hist);
     } else {
-      idx_hist_kernel<false><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
-      launch_topk<false>(256, nq, k, ws, idx, score, q0, s);
+      if (!self_hist) idx_hist_kernel<false><<<hgrid, 256, 0, s>>>(Qd, q0, kc, m, n_win, k, ws, fault);
+      launch_topk<false>(256, nq, k, ws, idx, score, q0, s, self_hist);
     }
   }
   return hipGetLastError();

@@ -124,13 +124,29 @@ __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, 
 // caches may be fp8, keys and queries may be turned (RoPE); the indexer scan
 // launch, which carries the upkeep of plain bf16 CSA layers, is compiled
 // without it (its float64 page loops would raise the scan's registers).
+// With RoPE (F8 path) the token's pair angles are computed here, once, and
+// left in rcs[i] = (cos, sin) for the query at the same position; a position
+// outside [0, max_pos] is clamped for that (the attention clamps it too).
 template <bool F8>
-__device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault) {
+__device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault,
+                                           double (*rcs)[2]) {
   const int c = threadIdx.x;
   const bool on = c < kD;
   __shared__ int ok;
   const int64_t p = u.pos[b] + i;
   const int64_t row = (int64_t)b * u.n_tok + i;   // the token's row in k_new / v_new / ki_new
+  double sn = 0.0, cs = 1.0;
+  if constexpr (F8) {
+    if (u.rope_on && on && c >= kD - kRopeDim) {
+      const int64_t pc = p < 0 ? 0 : (p > u.max_pos ? u.max_pos : p);
+      const int fi = (c - (kD - kRopeDim)) >> 1;
+      sincos((double)pc * u.rope.f[fi], &sn, &cs);
+      if (!(c & 1)) {
+        rcs[fi][0] = cs;
+        rcs[fi][1] = sn;
+      }
+    }
+  }
   if (p < 0 || p > u.max_pos) {
     if (c == 0) atomicOr(fault, HSA_FAULT_POS);
     return;
@@ -145,8 +161,6 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
       const u16 other = (u16)__shfl_xor((int)kn, 1);
       if (on && c >= kD - kRopeDim) {
         const bool odd = c & 1;
-        double sn, cs;
-        sincos((double)p * u.rope.f[(c - (kD - kRopeDim)) >> 1], &sn, &cs);
         const double x = bf16_to_f32(odd ? other : kn), y = bf16_to_f32(odd ? kn : other);
         kn = f64_to_bf16(rope_turn(x, y, cs, sn, odd));
       }
@@ -190,33 +204,18 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
   }
 }
 
-// Request b's n_tok queries turned for the attention (F8 upkeep, rope_on):
-// the angles' cos / sin once per query in LDS, then the query's 32-bit words,
-// the RoPE pairs turned and the other channels copied.  A position outside
-// [0, max_pos] (reported by the token step) is clamped, as the attention does.
-__device__ inline void rope_queries(const UpdateArgs& u, int b) {
-  __shared__ double qcs[kRopeDim / 2][2];
+// Query i of request b turned for the attention (F8 upkeep, rope_on) with the
+// pair angles rcs the token step at the same position left in LDS: the
+// query's 32-bit words, RoPE pairs turned and the other channels copied.
+__device__ inline void rope_query(const UpdateArgs& u, int b, int i, const double (*rcs)[2]) {
   const int words = u.H * (kD / 2);
-  for (int i = 0; i < u.n_tok; ++i) {
-    int64_t p = u.pos[b] + i;
-    p = p < 0 ? 0 : (p > u.max_pos ? u.max_pos : p);
-    __syncthreads();   // the previous query's angles are no longer read
-    if (threadIdx.x < kRopeDim / 2) {
-      double sn, cs;
-      sincos((double)p * u.rope.f[threadIdx.x], &sn, &cs);
-      qcs[threadIdx.x][0] = cs;
-      qcs[threadIdx.x][1] = sn;
-    }
-    __syncthreads();
-    const int64_t q0 = ((int64_t)b * u.n_tok + i) * u.H * kD;
-    const uint32_t* src = (const uint32_t*)(u.q_in + q0);
-    uint32_t* dst = (uint32_t*)(u.q_out + q0);
-    for (int wi = threadIdx.x; wi < words; wi += blockDim.x) {
-      const int j = wi & (kD / 2 - 1);   // word within the head
-      const int f = j - (kD - kRopeDim) / 2;
-      const uint32_t w = src[wi];
-      dst[wi] = f >= 0 ? rope_pair_bf16(w, qcs[f][0], qcs[f][1]) : w;
-    }
+  const int64_t q0 = ((int64_t)b * u.n_tok + i) * u.H * kD;
+  const uint32_t* src = (const uint32_t*)(u.q_in + q0);
+  uint32_t* dst = (uint32_t*)(u.q_out + q0);
+  for (int wi = threadIdx.x; wi < words; wi += blockDim.x) {
+    const int f = (wi & (kD / 2 - 1)) - (kD - kRopeDim) / 2;   // pair of the word, if RoPE
+    const uint32_t w = src[wi];
+    dst[wi] = f >= 0 ? rope_pair_bf16(w, rcs[f][0], rcs[f][1]) : w;
   }
 }
 
@@ -224,12 +223,17 @@ __device__ inline void rope_queries(const UpdateArgs& u, int b) {
 // position for the selection and attention that follow.
 template <bool F8>
 __device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault) {
+  __shared__ double rcs[kRopeDim / 2][2];   // RoPE: the current token's pair angles
   for (int i = 0; i < u.n_tok; ++i) {
-    decode_update_token<F8>(u, b, i, fault);
-    __syncthreads();   // the next token's block check reuses the shared flag
+    decode_update_token<F8>(u, b, i, fault, rcs);
+    __syncthreads();   // the next token's block check reuses the shared flag; rcs is complete
+    if constexpr (F8) {
+      if (u.q_out) {
+        rope_query(u, b, i, rcs);
+        __syncthreads();   // rcs is rewritten by the next token
+      }
+    }
   }
-  if constexpr (F8)
-    if (u.q_out) rope_queries(u, b);
   if (u.q_pos)
     for (int i = threadIdx.x; i < u.n_tok; i += blockDim.x) {
       u.q_pos[(int64_t)b * u.n_tok + i] = u.pos[b] + i;
