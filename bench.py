@@ -305,9 +305,10 @@ def committed_counter(kind, kernel, workload, key):
     return t.get(key)
 
 
-def _pmc_rows(path, counter, kernel_regex, reduce="sum"):
+def _pmc_rows(path, counter, kernel_regex, reduce="sum", grid=None):
     """Per-dispatch values of one rocprofv3 counter for the kernels whose name
-    matches kernel_regex (summed, or the maximum, over the counter's instances)."""
+    matches kernel_regex (and, if given, whose grid size is `grid` threads),
+    summed, or the maximum, over the counter's instances."""
     import csv
     import re
     rx = re.compile(kernel_regex)
@@ -316,16 +317,18 @@ def _pmc_rows(path, counter, kernel_regex, reduce="sum"):
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter or not rx.search(row.get("Kernel_Name", "")):
                 continue
+            if grid is not None and int(row.get("Grid_Size", -1)) != grid:
+                continue
             key = row.get("Dispatch_Id") or row.get("Correlation_Id")
             v = float(row["Counter_Value"])
             per[key] = max(per.get(key, 0.0), v) if reduce == "max" else per.get(key, 0.0) + v
     return per
 
 
-def _pmc_per_dispatch(path, counter, kernel_regex, reduce="sum"):
+def _pmc_per_dispatch(path, counter, kernel_regex, reduce="sum", grid=None):
     """Mean per dispatch of one rocprofv3 counter over the kernels whose name
     matches kernel_regex (a --pmc run written with --output-format csv)."""
-    per = _pmc_rows(path, counter, kernel_regex, reduce)
+    per = _pmc_rows(path, counter, kernel_regex, reduce, grid)
     if not per:
         raise SystemExit(f"{path}: no {counter} rows for kernels matching {kernel_regex!r}")
     return sum(per.values()) / len(per), len(per)
@@ -337,21 +340,22 @@ def traffic_summary(args):
     same counter reads for an elementwise copy of a known 1 GiB
     (bench.py --calibrate-copy).  Writes profiles/traffic_<kernel>_<workload>.json."""
     kernel, workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.traffic_summary
-    fk, nf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
-    wk, nw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kernel)
+    fk, nf = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE", kernel, grid=args.grid)
+    wk, nw = _pmc_per_dispatch(write_csv, "WRITE_SIZE", kernel, grid=args.grid)
     cf, _ = _pmc_per_dispatch(cfetch_csv, "FETCH_SIZE", "elementwise")
     cw, _ = _pmc_per_dispatch(cwrite_csv, "WRITE_SIZE", "elementwise")
     kib = float(1 << 20)   # the copy reads and writes 1 GiB
     f_scale, w_scale = kib / cf, kib / cw
     name = kernel.split("<")[0]
-    out = {"kernel": kernel, "workload": workload,
+    tag = name + (f"_{args.label}" if args.label else "")
+    out = {"kernel": kernel, "workload": workload, "grid_threads": args.grid,
            "source_hash": source_hash(*kernel_sources(name)),
            "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
            "dispatches": [nf, nw],
            "copy_calibration": {"fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
                                 "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
            "bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024))}
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -360,26 +364,28 @@ def traffic_summary(args):
 def mfma_summary(args):
     """MFMA utilisation of a kernel from one rocprofv3 --pmc run of
     SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
-    SQ_INSTS_VALU_MFMA_MOPS_F16 and GRBM_GUI_ACTIVE: busy = MFMA busy cycles
-    summed over the 1,024 SIMDs / (GPU active cycles x 1,024); the MOPS
-    counters count MFMA multiply-adds / 512, so x 512 x 2 is the MFMA flops the
-    kernel executed (padding and masked entries included), compared with the
-    algorithmic flops per launch given on the command line.
-    Writes profiles/mfma_<kernel>_<workload>.json."""
+    SQ_INSTS_VALU_MFMA_MOPS_F16 and GRBM_GUI_ACTIVE.  As read on this part:
+    GRBM_GUI_ACTIVE comes as one value per dispatch, the sum over the 8 XCDs
+    (value / 8 = the kernel's active cycles: ~2.1 GHz times its duration under
+    the profiler); SQ_VALU_MFMA_BUSY_CYCLES sums 16 cycles per 16x16x32 MFMA
+    over all 1,024 SIMDs, so busy = BUSY / (active x 1,024); the MOPS counters
+    count MFMA flops / 512 (x 512 reproduces the algorithmic flops of the score
+    GEMM exactly), compared with the algorithmic flops per launch given on the
+    command line.  Writes profiles/mfma_<kernel>_<workload>.json."""
     kernel, workload, csv_path, alg_flops = args.mfma_summary
     alg = float(alg_flops)
     busy, n = _pmc_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", kernel)
     bf16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel)
     f16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_F16", kernel)
-    # GRBM_GUI_ACTIVE is reported per XCD: the kernel's active cycles are the largest
-    active, _ = _pmc_per_dispatch(csv_path, "GRBM_GUI_ACTIVE", kernel, reduce="max")
+    grbm, _ = _pmc_per_dispatch(csv_path, "GRBM_GUI_ACTIVE", kernel)
+    active = grbm / 8
     simds = 256 * 4
-    executed = (bf16 + f16) * 512 * 2
+    executed = (bf16 + f16) * 512
     name = kernel.split("<")[0]
     out = {"kernel": kernel, "workload": workload,
            "source_hash": source_hash(*kernel_sources(name)), "dispatches": n,
            "mfma_busy_cycles_per_simd": round(busy / simds, 1),
-           "gpu_active_cycles": round(active, 1),
+           "active_cycles": round(active, 1),
            "mfma_busy_frac": round(busy / (active * simds), 4),
            "mfma_flops_executed": executed, "algorithmic_flops": alg,
            "executed_over_algorithmic": round(executed / alg, 3)}
@@ -1077,6 +1083,10 @@ def main():
                     metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                              "COPY_WRITE_CSV"),
                     help="(no GPU) turn rocprofv3 --pmc counter files into HBM bytes per launch")
+    ap.add_argument("--grid", type=int, default=None,
+                    help="--traffic-summary: only launches of this grid size (threads)")
+    ap.add_argument("--label", default="",
+                    help="--traffic-summary: suffix of the summary's name (e.g. csa, hca)")
     ap.add_argument("--mfma-summary", nargs=4,
                     metavar=("KERNEL", "WORKLOAD", "PMC_CSV", "ALGORITHMIC_FLOPS"),
                     help="(no GPU) turn a rocprofv3 --pmc run of the MFMA counters into MFMA "

@@ -8,14 +8,15 @@
 // 2-byte token value, far below gfx950's vector float64 rate (half its fp32
 // rate) at the bandwidth the reads allow.
 //
-// Layout of the work: a lane pools two adjacent channels of one entry, so a
-// wave reads one whole 256-byte token row per load instruction (dim 128; two
-// 128-byte rows, one per entry, for dim 64) and the slot loop's loads are all
-// in flight together.  Formats without a page-wide scale (bf16, fp4 with its
-// 32-channel blocks) give every entry its own wave(s) -- 1,024 waves for the
-// 128K-token HCA layer, 32,768 for the CSA layer; fp8 formats, whose page
-// scale depends on all 64 entries of a page, give each page one workgroup of
-// 16 waves (4 entries each) and reduce the page amax in LDS.
+// Layout of the work: a lane pools two adjacent channels, so a wave reads one
+// whole 256-byte token row per load instruction (dim 128; two 128-byte rows
+// for dim 64).  Formats without a page-wide scale (bf16, fp4 with its
+// 32-channel blocks) give each lane group a run of consecutive entries whose
+// token rows are consecutive (one HCA entry, or 16 CSA entries: 64 rows),
+// with the run's row loads in flight together and the pooling weights in LDS;
+// fp8 formats, whose page scale depends on all 64 entries of a page, give each
+// page one workgroup of 16 waves (4 entries each) and reduce the page amax in
+// LDS.
 #include "update.h"
 
 namespace hsa {
@@ -64,24 +65,18 @@ __device__ __forceinline__ void pool2(const Tokens& x, int x_req, int64_t e, int
 
 // Entries [first, first + n) without a page-wide scale: HSA_BF16 (dim 128 or
 // 64) and HSA_FP4_E2M1_MX (dim 64, power-of-two scale per 32-channel block).
-// Lanes per entry L = dim / 2; a wave holds 64 / L entries; a 256-thread
-// workgroup 4 * 64 / L of them.
+// A lane group (dim / 2 lanes, two channels per lane) pools a run of epr =
+// max(1, RR / m) consecutive entries: their m * epr token rows are consecutive
+// positions, read RR at a time with every token load of the batch in flight
+// before the slot-order accumulation uses them (bf16, RR = 64: an HCA entry in
+// two batches, sixteen CSA entries in one).  The pooling weights sit in LDS
+// when they fit (m * dim <= kAlphaLds floats), else they are read from memory.
+constexpr int kAlphaLds = 16384;
+template <int FMT> constexpr int run_rows() { return FMT == HSA_FP4_E2M1_MX ? 16 : 64; }
+
 template <int FMT>
-__global__ __launch_bounds__(256) void compress_rows_kernel(Tokens x, int x_req, int req,
-                                                            int64_t first, int64_t n, int m,
-                                                            const float* __restrict__ alpha,
-                                                            Paged out, int* fault) {
-  const int dim = out.dim;
-  const int lpe = dim / 2;                     // lanes per entry
-  const int lane = threadIdx.x & 63;
-  const int per_wg = 256 / lpe;
-  const int64_t i = (int64_t)blockIdx.x * per_wg + threadIdx.x / lpe;
-  if (blockIdx.x == 0 && threadIdx.x == 0) out.n_entries[req] = (int32_t)(first + n);
-  if (i >= n) return;
-  const int64_t e = first + i;
-  const int c = 2 * (lane % lpe);
-  double v0, v1;
-  pool2(x, x_req, e, m, alpha, dim, c, &v0, &v1);
+__device__ __forceinline__ void store_entry(const Paged& out, int req, int64_t e, int c,
+                                            double v0, double v1, int* fault) {
   const int page = out.page_of(req, e, fault);
   if (FMT == HSA_FP4_E2M1_MX) {
     // the 32-channel block of these channels spans 16 lanes: its amax, the
@@ -98,12 +93,85 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(Tokens x, int x_req,
     if (page < 0) return;
     out.row(page, e)[c / 2] = (uint8_t)code;
     if ((c & 31) == 0)
-      ((uint8_t*)out.scale)[((int64_t)page * kPage + (e & 63)) * (dim / 32) + c / 32] =
+      ((uint8_t*)out.scale)[((int64_t)page * kPage + (e & 63)) * (out.dim / 32) + c / 32] =
           (uint8_t)(xs + 127);
     return;
   }
   if (page < 0) return;
   ((uint32_t*)out.row(page, e))[c / 2] = (uint32_t)f64_to_bf16(v0) | ((uint32_t)f64_to_bf16(v1) << 16);
+}
+
+template <int FMT, bool ALDS>
+__global__ __launch_bounds__(256) void compress_rows_kernel(Tokens x, int x_req, int req,
+                                                            int64_t first, int64_t n, int m,
+                                                            const float* __restrict__ alpha,
+                                                            Paged out, int* fault) {
+  constexpr int kRunRows = run_rows<FMT>();
+  extern __shared__ float s_alpha[];
+  const int dim = out.dim;
+  const float* al = ALDS ? s_alpha : alpha;
+  const int lpe = dim / 2;                     // lanes per entry
+  const int lane = threadIdx.x & 63;
+  const int epr = m >= kRunRows ? 1 : kRunRows / m;
+  const int per_wg = 256 / lpe;                // runs per workgroup
+  const int64_t i0 = ((int64_t)blockIdx.x * per_wg + threadIdx.x / lpe) * epr;
+  if (blockIdx.x == 0 && threadIdx.x == 0) out.n_entries[req] = (int32_t)(first + n);
+  const int c = 2 * (lane % lpe);
+  const int rows = i0 < n ? (int)(n - i0 < epr ? n - i0 : epr) * m : 0;
+  const int64_t cap = x.capacity;
+  const uint32_t* base = (const uint32_t*)((const u16*)x.data + (int64_t)x_req * cap * dim + c);
+  const int64_t stride = dim / 2;              // 32-bit words per row
+  int64_t p = ((first + i0) * m) % cap;        // ring row of the run's first token
+  double a0 = 0.0, a1 = 0.0;
+  int j = 0;                                   // slot of the next row
+  int64_t e = first + i0;                      // entry of the next row
+  uint32_t v[kRunRows];
+  auto load_batch = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < kRunRows; ++u) {
+      v[u] = r0 + u < rows ? __builtin_nontemporal_load(base + p * stride) : 0u;
+      p = p + 1 == cap ? 0 : p + 1;
+    }
+  };
+  load_batch(0);   // in flight while the weights are staged
+  if constexpr (ALDS) {
+    // 16-byte pieces, sixteen per thread in flight (the host checked the
+    // weights' alignment; m * dim is a multiple of 4)
+    const int n4 = m * dim / 4;
+    const float4* a4 = (const float4*)alpha;
+    for (int i0 = 0; i0 < n4; i0 += 256 * 16) {
+      float4 t[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 256 + threadIdx.x;
+        t[u] = i < n4 ? a4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 256 + threadIdx.x;
+        if (i < n4) ((float4*)s_alpha)[i] = t[u];
+      }
+    }
+    __syncthreads();
+  }
+  for (int r0 = 0; r0 < rows; r0 += kRunRows) {
+    if (r0 > 0) load_batch(r0);
+#pragma unroll
+    for (int u = 0; u < kRunRows; ++u) {
+      if (r0 + u < rows) {
+        const float2 w = *(const float2*)(al + (int64_t)j * dim + c);
+        // each product is exact in float64, so contraction into an FMA changes nothing
+        a0 += (double)w.x * (double)__uint_as_float(v[u] << 16);
+        a1 += (double)w.y * (double)__uint_as_float(v[u] & 0xFFFF0000u);
+        if (++j == m) {
+          store_entry<FMT>(out, req, e, c, a0, a1, fault);
+          a0 = a1 = 0.0;
+          j = 0;
+          ++e;
+        }
+      }
+    }
+  }
 }
 
 // Entries of formats with a page-wide fp32 scale: HSA_FP8_E4M3 (dim 128 or 64;
@@ -278,12 +346,20 @@ hipError_t launch_compress(const hsa_tokens& x, int x_req, const hsa_paged& out,
     else
       compress_page_kernel<HSA_FP8_E4M3><<<g, 1024, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   } else {
+    const bool f4 = out.dtype == HSA_FP4_E2M1_MX;
     const int per_wg = 256 / (out.dim / 2);
-    const unsigned g = (unsigned)((n + per_wg - 1) / per_wg);
-    if (out.dtype == HSA_FP4_E2M1_MX)
-      compress_rows_kernel<HSA_FP4_E2M1_MX><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+    const int rr = f4 ? run_rows<HSA_FP4_E2M1_MX>() : run_rows<HSA_BF16>();
+    const int epr = m >= rr ? 1 : rr / m;
+    const int64_t runs = (n + epr - 1) / epr;
+    const unsigned g = (unsigned)((runs + per_wg - 1) / per_wg);
+    const bool alds = (int64_t)m * out.dim <= kAlphaLds && ((uintptr_t)alpha & 15) == 0;
+    const unsigned lds = alds ? (unsigned)(m * out.dim * sizeof(float)) : 0u;
+    if (f4)
+      (alds ? compress_rows_kernel<HSA_FP4_E2M1_MX, true> : compress_rows_kernel<HSA_FP4_E2M1_MX, false>)
+          <<<g, 256, lds, s>>>(t, x_req, req, first, n, m, alpha, o, f);
     else
-      compress_rows_kernel<HSA_BF16><<<g, 256, 0, s>>>(t, x_req, req, first, n, m, alpha, o, f);
+      (alds ? compress_rows_kernel<HSA_BF16, true> : compress_rows_kernel<HSA_BF16, false>)
+          <<<g, 256, lds, s>>>(t, x_req, req, first, n, m, alpha, o, f);
   }
   return hipGetLastError();
 }
