@@ -383,7 +383,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __shared__ __align__(16) u16 kv_lds[SH ? (kVtH > kKsH ? kVtH : kKsH) : kKsH + kVtH];
   u16(*Ks)[136] = (u16(*)[136])kv_lds;
   u16(*Vt)[kVtP] = (u16(*)[kVtP])(kv_lds + (SH ? 0 : kKsH));
-  __shared__ float ksc[64];
+  __shared__ __align__(16) float ksc[64];
 
   // ---- resolve the rows of every entry of this split once
   const int e_base = c_lo * 64;
@@ -503,33 +503,46 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     // ---- S^T = K Q^T for 64 entries x 16 heads (this wave's heads).  KMIX:
     // the code channels (k-steps 0, 1) and the bf16 RoPE channels (2, 3)
     // accumulate apart, as only the codes take the page scale.
+    // every K operand of the chunk is read from LDS before the first MFMA
+    // (one LDS round trip instead of one per operand), and the four entry
+    // tiles' accumulations interleave
     f32x4 sacc[4], shi[KMIX ? 4 : 1];
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[et][ks] = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
 #pragma unroll
     for (int et = 0; et < 4; ++et) {
       sacc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KMIX) shi[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
-        if (KMIX && ks >= 2)
-          shi[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], shi[et], 0, 0, 0);
-        else
-          sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[ks], sacc[et], 0, 0, 0);
-      }
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        if (KMIX && ks >= 2)
+          shi[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[ks], shi[et], 0, 0, 0);
+        else
+          sacc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[ks], sacc[et], 0, 0, 0);
+      }
     // ---- online softmax (lane = head `col`; rows 4g+i of each entry tile).
     // log2-domain logit = acc * c, c = scale*log2(e) (times the page scale of
     // fp8 keys).  With one positive c the running max is taken on the raw
     // accumulators; entries past the end exist only in the last chunk.
     if (F8) {
+      // the key rows' page scales, four per 16-byte read
+      f32x4 kscv[4];
+#pragma unroll
+      for (int et = 0; et < 4; ++et) kscv[et] = *(const f32x4*)&ksc[et * 16 + 4 * g];
 #pragma unroll
       for (int et = 0; et < 4; ++et)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (KMIX)
-            sacc[et][i] = (sacc[et][i] * ksc[et * 16 + 4 * g + i] + shi[et][i]) * a.scale_log2;
+            sacc[et][i] = (sacc[et][i] * kscv[et][i] + shi[et][i]) * a.scale_log2;
           else
-            sacc[et][i] *= a.scale_log2 * ksc[et * 16 + 4 * g + i];
+            sacc[et][i] *= a.scale_log2 * kscv[et][i];
         }
     }
     if (__builtin_expect(e0 + 64 > E, 0)) {   // the last chunk only (E is uniform)
@@ -579,15 +592,22 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
                                  ex2(__builtin_fmaf(sacc[2 * j + 1][i + 1], cst, -m_new)));
       }
       const f16x8 pb = __builtin_bit_cast(f16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      // the step's V^T operands, all read before the MFMAs use them
+      f16x8 vf[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const u16* vr = &Vt[16 * dt + col][0];
         uint2 lo = *(const uint2*)(vr + 32 * j + 4 * g);
         uint2 hi = *(const uint2*)(vr + 32 * j + 16 + 4 * g);
-        uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        f16x8 av = __builtin_bit_cast(f16x8, u);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[dt], 0, 0, 0);
+        vf[dt] = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pb, oacc[dt], 0, 0, 0);
+      // schedule: the step's LDS reads (8 pairs) ahead of its MFMAs, so their
+      // latencies overlap instead of one wait per operand
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // MFMA
       osum = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, osum, 0, 0, 0);
     }
     __syncthreads();
@@ -883,19 +903,27 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     __syncthreads();
     if (c + 1 < n_chunks) issue_k(c + 1);
 
-    // ---- S^T = K Q^T for both queries; each K operand read once
+    // ---- S^T = K Q^T for both queries; each K operand read once, all of
+    // them before the first MFMA (one LDS round trip), the eight
+    // accumulations interleaved
     f32x4 sacc[2][4];
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[et][ks] = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
 #pragma unroll
     for (int et = 0; et < 4; ++et) {
       sacc[0][et] = f32x4{0.f, 0.f, 0.f, 0.f};
       sacc[1][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
-        sacc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[0][ks], sacc[0][et], 0, 0, 0);
-        sacc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[1][ks], sacc[1][et], 0, 0, 0);
-      }
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        sacc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[0][ks], sacc[0][et], 0, 0, 0);
+        sacc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[1][ks], sacc[1][et], 0, 0, 0);
+      }
     // ---- masks, only in chunks that hold an entry outside either query's set
     const bool clean = e0 >= wlo1 && e0 + 64 <= end0 &&
                        (whi0 == n_wuu - 1 || e0 > whi0 + 1 || e0 + 63 < whi0 + 1);
@@ -950,15 +978,22 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     for (int h = 0; h < 2; ++h) {
       const f16x8 pb0 = __builtin_bit_cast(f16x8, make_uint4(pw[0][h][0], pw[0][h][1], pw[0][h][2], pw[0][h][3]));
       const f16x8 pb1 = __builtin_bit_cast(f16x8, make_uint4(pw[1][h][0], pw[1][h][1], pw[1][h][2], pw[1][h][3]));
+      f16x8 vf[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const u16* vr = &Vt[16 * dt + col][0];
         const uint2 lo = *(const uint2*)(vr + 32 * h + 4 * g);
         const uint2 hi = *(const uint2*)(vr + 32 * h + 16 + 4 * g);
-        const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb0, oacc[0][dt], 0, 0, 0);
-        oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb1, oacc[1][dt], 0, 0, 0);
+        vf[dt] = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pb0, oacc[0][dt], 0, 0, 0);
+        oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pb1, oacc[1][dt], 0, 0, 0);
+      }
+      // the step's LDS reads ahead of its MFMAs (their latencies overlap)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
       osum[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb0, osum[0], 0, 0, 0);
       osum[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb1, osum[1], 0, 0, 0);
     }
