@@ -490,8 +490,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int ek = p >> 4, cgk = p & 15;
       *(uint4*)&Ks[ek][cgk * 8] =
           k_piece_bf16(kraw[b][i], F8 && krow[b][i] >= 0 && (!KMIX || cgk < 8));
-      if constexpr (F8)   // page scale of each key row (bf16 rows need none)
-        if (cgk == 0) ksc[ek] = kscl[b][i];
+      // page scale of each key row (bf16 rows need none); fp8 K: times the
+      // logit scale, the product the softmax takes (the same fp32 value)
+      if constexpr (F8)
+        if (cgk == 0) ksc[ek] = KMIX ? kscl[b][i] : a.scale_log2 * kscl[b][i];
     }
     if constexpr (!SH) stage_v(bi);
     __syncthreads();
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
           if constexpr (KMIX)
             sacc[et][i] = (sacc[et][i] * kscv[et][i] + shi[et][i]) * a.scale_log2;
           else
-            sacc[et][i] *= a.scale_log2 * kscv[et][i];
+            sacc[et][i] *= kscv[et][i];
         }
     }
     if (__builtin_expect(e0 + 64 > E, 0)) {   // the last chunk only (E is uniform)
@@ -903,27 +905,19 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     __syncthreads();
     if (c + 1 < n_chunks) issue_k(c + 1);
 
-    // ---- S^T = K Q^T for both queries; each K operand read once, all of
-    // them before the first MFMA (one LDS round trip), the eight
-    // accumulations interleaved
+    // ---- S^T = K Q^T for both queries; each K operand read once
     f32x4 sacc[2][4];
-    bf16x8 kf[4][4];
-#pragma unroll
-    for (int et = 0; et < 4; ++et)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[et][ks] = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
 #pragma unroll
     for (int et = 0; et < 4; ++et) {
       sacc[0][et] = f32x4{0.f, 0.f, 0.f, 0.f};
       sacc[1][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int et = 0; et < 4; ++et) {
-        sacc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[0][ks], sacc[0][et], 0, 0, 0);
-        sacc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[et][ks], qb[1][ks], sacc[1][et], 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 av = *(const bf16x8*)&Ks[et * 16 + col][ks * 32 + 8 * g];
+        sacc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[0][ks], sacc[0][et], 0, 0, 0);
+        sacc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[1][ks], sacc[1][et], 0, 0, 0);
       }
+    }
     // ---- masks, only in chunks that hold an entry outside either query's set
     const bool clean = e0 >= wlo1 && e0 + 64 <= end0 &&
                        (whi0 == n_wuu - 1 || e0 > whi0 + 1 || e0 + 63 < whi0 + 1);
@@ -978,22 +972,15 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     for (int h = 0; h < 2; ++h) {
       const f16x8 pb0 = __builtin_bit_cast(f16x8, make_uint4(pw[0][h][0], pw[0][h][1], pw[0][h][2], pw[0][h][3]));
       const f16x8 pb1 = __builtin_bit_cast(f16x8, make_uint4(pw[1][h][0], pw[1][h][1], pw[1][h][2], pw[1][h][3]));
-      f16x8 vf[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const u16* vr = &Vt[16 * dt + col][0];
         const uint2 lo = *(const uint2*)(vr + 32 * h + 4 * g);
         const uint2 hi = *(const uint2*)(vr + 32 * h + 16 + 4 * g);
-        vf[dt] = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const f16x8 av = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb0, oacc[0][dt], 0, 0, 0);
+        oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb1, oacc[1][dt], 0, 0, 0);
       }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        oacc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pb0, oacc[0][dt], 0, 0, 0);
-        oacc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt], pb1, oacc[1][dt], 0, 0, 0);
-      }
-      // the step's LDS reads ahead of its MFMAs (their latencies overlap)
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
       osum[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb0, osum[0], 0, 0, 0);
       osum[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb1, osum[1], 0, 0, 0);
     }

@@ -1487,6 +1487,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     s_bad = 0; s_maxbc = -1; s_thr = -1; s_ovf = 0; s_above = 0; s_ntc = 0; s_tot = 0;
   }
   const int n_wg = (int)((nv + ws.list_span - 1) / ws.list_span);   // this row's lists
+  int path = 0;
   if (tid < nl) {
     const bool live = tid < n_wg;
     s_cnt[tid] = (int16_t)(live ? (cnt < kCandCap ? cnt : kCandCap) : 0);
@@ -1600,10 +1601,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
           }
       }
     }
-    if (tid == 0) {   // which path served the query, and the union / threshold-bin sizes
-      st[6] = full ? (s_bad ? 1 : (s_thr < 0 ? 2 : (s_thr < s_maxbc ? 3 : 4))) : 0;
-      st[7] = (int32_t)((tot << 16) | (s_ntc & 0xFFFF));
-    }
+    if (tid == 0)   // which path served the query (stored at the end, off the critical path)
+      path = full ? (s_bad ? 1 : (s_thr < 0 ? 2 : (s_thr < s_maxbc ? 3 : 4))) : 0;
     if (full) {
       // exact selection over the whole row (rare)
       auto fkey = [&](int64_t i) {
@@ -1650,6 +1649,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   for (int i = (int)total + tid; i < k; i += NT) {
     irow[i] = -1;
     if (srow_out) srow_out[i] = 0.f;
+  }
+  if (tid == 0) {   // the path code and the union / threshold-bin sizes (diagnostics)
+    st[6] = path;
+    st[7] = (int32_t)((tot << 16) | (s_ntc & 0xFFFF));
   }
 }
 
