@@ -301,7 +301,9 @@ typedef struct {
  *      new token's query.
  * The block completed at pos starts inside the window, so the query at pos
  * does not see it: steps 1-2 of a CSA layer ride in one of the indexer's
- * launches instead of a launch of their own.
+ * launches instead of a launch of their own, and those of an HCA layer
+ * without RoPE follow the attention, in the launch that merges its splits
+ * (the attention reads the new token's K/V from k_new / v_new).
  * Q bf16 [B][H][d]; k_new, v_new bf16 [B][d]; qI bf16 [B][H_I][d_I]; kI_new
  * bf16 [B][d_I]; w fp32 [B][H_I]; O [B][H][d] of L->o_dtype; lse fp32 [B][H] or NULL;
  * idx_out int32 [B][topk] or NULL (CSA).  max_pos bounds every pos[b].

@@ -530,12 +530,20 @@ hsa_status hsa_decode_step(const hsa_layer* L, int32_t B, const int64_t* pos, in
     if (e != hipSuccess) return hip_status(e, "decode_step indexer");
     e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, sel,
                     L->topk, L->scale, O, L->o_dtype, lse, base + a_idx + a_sel, a_attn, stream);
-  } else {
+  } else if (a_q) {
+    // RoPE: the attention needs the turned key and queries the upkeep writes
     e = launch_decode_update(*L, B, pos, max_pos, k_new, v_new, kI_new, stream, 1, nullptr,
                              nullptr, Q, q_rot);
     if (e != hipSuccess) return hip_status(e, "decode_step update");
     e = launch_attn(q, Qa, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
                     L->scale, O, L->o_dtype, lse, base, a_attn, stream);
+  } else {
+    // the block completed at pos is not visible to the query at pos, so the
+    // upkeep may follow the attention (in its merge launch): launch_attn
+    // places it
+    const UpdateArgs upd = make_update_args(*L, pos, max_pos, k_new, v_new, kI_new);
+    e = launch_attn(q, Q, L->H, L->ring_k, L->ring_v, L->n_win, L->kc, L->vc, L->m, nullptr, 0,
+                    L->scale, O, L->o_dtype, lse, base, a_attn, stream, &upd);
   }
   return hip_status(e, "decode_step attention");
 }

@@ -26,7 +26,7 @@
 // as the merge does, so its bits do not depend on the batch around it.
 #include <type_traits>
 
-#include "common.h"
+#include "update.h"
 
 namespace hsa {
 
@@ -52,6 +52,12 @@ struct AttnArgs {
   int n_splits, cps, n_hg, n_q;
   int xcd;               // 1: keep consecutive queries on one XCD (prefill)
   int* fault;
+  // decode with the cache upkeep after the attention: the query's own token
+  // (the newest window row) is read from row qi of knew / vnew instead of the
+  // ring, where it is not yet written; its F8 row id is -2 - (ring_rows + qi)
+  const u16* knew;
+  const u16* vnew;
+  int64_t ring_rows;     // n_req * capacity of the rings
 };
 
 constexpr int kMaxCps = 32;            // chunks of 64 entries per workgroup
@@ -71,10 +77,15 @@ __device__ __forceinline__ int64_t ring_slot(int64_t w0, int ge, int64_t cap) {
   return sl >= cap ? sl - cap : sl;
 }
 
+template <bool NR>
 __device__ __forceinline__ void resolve(const AttnArgs& a, const Prefetch& pf, int qi, int r,
                                         int64_t w0k, int64_t w0v, int n_w, int E, int64_t nv,
                                         int ge, int* rk, int* rv) {
   if (ge < n_w) {
+    if (NR && ge == n_w - 1) {   // the query's own token, from knew / vnew
+      *rk = *rv = -2 - (int)(a.ring_rows + qi);
+      return;
+    }
     *rk = -2 - (int)((int64_t)r * a.wk.capacity + ring_slot(w0k, ge, a.wk.capacity));
     *rv = -2 - (int)((int64_t)r * a.wv.capacity + ring_slot(w0v, ge, a.wv.capacity));
     return;
@@ -130,11 +141,17 @@ __device__ __align__(16) uint4 g_zero_row[16];
 
 // bf16 caches: the address of entry ge's K and V rows (window row, pool row, or
 // the zero row), so that a chunk's gathers are one load per 16-byte piece.
+template <bool NR>
 __device__ __forceinline__ void resolve_ptr(const AttnArgs& a, const Prefetch& pf, int qi, int r,
                                             int64_t w0k, int64_t w0v, int n_w, int E, int64_t nv,
                                             int ge, const uint8_t** pk, const uint8_t** pv) {
   const uint8_t* zero = (const uint8_t*)g_zero_row;
   if (ge < n_w) {
+    if (NR && ge == n_w - 1) {   // the query's own token, from knew / vnew
+      *pk = (const uint8_t*)(a.knew + (int64_t)qi * kD);
+      *pv = (const uint8_t*)(a.vnew + (int64_t)qi * kD);
+      return;
+    }
     *pk = a.wk.data + ((int64_t)r * a.wk.capacity + ring_slot(w0k, ge, a.wk.capacity)) * (kD * 2);
     *pv = a.wv.data + ((int64_t)r * a.wv.capacity + ring_slot(w0v, ge, a.wv.capacity)) * (kD * 2);
     return;
@@ -158,12 +175,16 @@ __device__ __forceinline__ void resolve_ptr(const AttnArgs& a, const Prefetch& p
 // instead of waiting at divergent branch joins (measured: a variant that
 // issues one load on chunks that lie wholly in the window or the pool, behind
 // a chunk-uniform branch, is 10-30% slower).
-template <bool F8>
-__device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, int row, int cg) {
+template <bool F8, bool NR>
+__device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, int row, int cg,
+                                            const u16* knew, int64_t ring_rows) {
   const bool pool = row >= 0, win = row <= -2;
   const int64_t pr = pool ? row : 0;
-  const int64_t wr = win ? (int64_t)(-2 - row) : 0;
-  const uint4 wv = *(const uint4*)((const u16*)tk.data + wr * kD + cg * 8);
+  const int64_t w = win ? (int64_t)(-2 - row) : 0;
+  const bool nw = NR && w >= ring_rows;       // the query's own token
+  const u16* wb = nw ? knew : (const u16*)tk.data;
+  const int64_t wr = nw ? w - ring_rows : w;
+  const uint4 wv = *(const uint4*)(wb + wr * kD + cg * 8);
   uint4 pv;
   if (F8) {
     const uint2 v = *(const uint2*)(c.data + pr * kD + cg * 8);
@@ -180,12 +201,16 @@ __device__ __forceinline__ uint4 load_piece(const Paged& c, const Tokens& tk, in
 // RoPE channels.  One 16-byte load per piece, branch-free like load_piece: a
 // code group reads the 16 bytes that hold it and its neighbour and keeps its
 // half.
+template <bool NR>
 __device__ __forceinline__ uint4 load_piece_kmix(const Paged& c, const Tokens& tk, int row,
-                                                 int cg) {
+                                                 int cg, const u16* knew, int64_t ring_rows) {
   const bool pool = row >= 0, win = row <= -2;
   const int64_t pr = pool ? row : 0;
-  const int64_t wr = win ? (int64_t)(-2 - row) : 0;
-  const uint4 wv = *(const uint4*)((const u16*)tk.data + wr * kD + cg * 8);
+  const int64_t w = win ? (int64_t)(-2 - row) : 0;
+  const bool nw = NR && w >= ring_rows;       // the query's own token
+  const u16* wb = nw ? knew : (const u16*)tk.data;
+  const int64_t wr = nw ? w - ring_rows : w;
+  const uint4 wv = *(const uint4*)(wb + wr * kD + cg * 8);
   const uint8_t* base = c.data + pr * (kD / 2 * 3);
   const bool code = cg < 8;
   const uint4 v = *(const uint4*)(base + (code ? (cg >> 1) * 16 : kD / 2 + (cg - 8) * 16));
@@ -284,7 +309,9 @@ __device__ __forceinline__ void check_finite(const f32x4 (&acc)[N], int* fault) 
 }
 
 // KMIX (with F8): the K cache is HSA_FP8_BF16_ROPE, the V cache fp8
-template <int NW, bool F8, bool SH, bool KMIX>
+// NR: decode with the upkeep after the attention (the query's own token read
+// from knew / vnew)
+template <int NW, bool F8, bool SH, bool KMIX, bool NR = false>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PPT = 1024 / NT;          // K (and V) pieces per thread per chunk
@@ -392,9 +419,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int64_t w0k = s0 % a.wk.capacity, w0v = s0 % a.wv.capacity;
   for (int j = tid; j < n_ent; j += NT) {
     if constexpr (F8)
-      resolve(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve<NR>(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
     else
-      resolve_ptr(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
+      resolve_ptr<NR>(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
   }
 
   __syncthreads();
@@ -423,8 +450,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int ek = p >> 4, cgk = p & 15;
       if constexpr (F8) {
         krow[b][i] = rowk[lo + ek];
-        kraw[b][i] = KMIX ? load_piece_kmix(a.kc, a.wk, krow[b][i], cgk)
-                          : load_piece<F8>(a.kc, a.wk, krow[b][i], cgk);
+        kraw[b][i] = KMIX ? load_piece_kmix<NR>(a.kc, a.wk, krow[b][i], cgk, a.knew, a.ring_rows)
+                          : load_piece<F8, NR>(a.kc, a.wk, krow[b][i], cgk, a.knew, a.ring_rows);
         kscl[b][i] = row_scale<F8>(a.kc, krow[b][i]);
       } else {
         krow[b][i] = 0;
@@ -441,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       const int ev = 2 * vpair + (i & 1), cgv = (tid >> 5) + (NT / 32) * (i >> 1);
       if constexpr (F8) {
         vrow[b][i] = rowv[lo + ev];
-        vraw[b][i] = load_piece<F8>(a.vc, a.wv, vrow[b][i], cgv);
+        vraw[b][i] = load_piece<F8, NR>(a.vc, a.wv, vrow[b][i], cgv, a.vnew, a.ring_rows);
         vscl[b][i] = row_scale<F8>(a.vc, vrow[b][i]);
       } else {
         vrow[b][i] = 0;
@@ -689,18 +716,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 // split) and split s's (m, l) sits in lane s mod 64, so every reduction stays
 // inside the wave and a split's place in it does not depend on how many
 // splits the launch has.  The first kMergePF partial rows are requested before
-// the (m, l) pairs are reduced.
+// the (m, l) pairs are reduced.  Every thread of the workgroup calls it (one
+// workgroup barrier); `on` false: a wave with no (query, head).
 constexpr int kMergeMaxSplits = 1024;
 constexpr int kMergePF = 64;          // partial rows a lane requests up front (HCA: 44 splits at 1M)
-__global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
-                                                        const u16* __restrict__ part_o,
-                                                        const float* __restrict__ part_ml,
-                                                        void* __restrict__ O, int o_f32,
-                                                        float* __restrict__ lse, int* fault) {
-  const int qh = blockIdx.x;   // query * H + head
-  const int q = qh / H, h = qh % H, lane = threadIdx.x;
-  __shared__ float wgt[kMergeMaxSplits];
-  const int ns = n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits;
+__device__ __forceinline__ void merge_one(int qh, bool on, int H, int n_splits,
+                                          const u16* __restrict__ part_o,
+                                          const float* __restrict__ part_ml, void* __restrict__ O,
+                                          int o_f32, float* __restrict__ lse, int* fault,
+                                          float* wgt) {
+  const int lane = threadIdx.x & 63;
+  const int q = on ? qh / H : 0, h = on ? qh % H : 0;
+  const int ns = !on ? 0 : (n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits);
   const uint32_t* po = (const uint32_t*)(part_o + ((int64_t)q * n_splits * H + h) * kD) + lane;
   const int64_t stride = (int64_t)H * kD / 2;    // 32-bit words between splits
   uint32_t v[kMergePF];
@@ -726,6 +753,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
   for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
   const float L = lloc;
   __syncthreads();   // wgt[] written by other lanes
+  if (!on) return;
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -749,6 +777,37 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
         (uint32_t)__builtin_bit_cast(u16, (__bf16)o0) |
         ((uint32_t)__builtin_bit_cast(u16, (__bf16)o1) << 16);
   if (lane == 0 && lse) lse[qh] = (M + log2f(L)) * kLn2;
+}
+
+// One (query, head) per one-wave workgroup.
+__global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
+                                                        const u16* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        void* __restrict__ O, int o_f32,
+                                                        float* __restrict__ lse, int* fault) {
+  __shared__ float wgt[kMergeMaxSplits];
+  merge_one(blockIdx.x, true, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt);
+}
+
+// The merge with the decode cache upkeep of an HCA layer: two (query, head)
+// waves per 128-thread workgroup, then one workgroup per request running the
+// upkeep (the attention read each new token from its input and has finished
+// with every page an fp8 re-encoding may rewrite).
+__global__ __launch_bounds__(128) void attn_merge_upd_kernel(int n_qh, int H, int n_splits,
+                                                             const u16* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             void* __restrict__ O, int o_f32,
+                                                             float* __restrict__ lse, int* fault,
+                                                             UpdateArgs upd) {
+  const int n_merge = (n_qh + 1) / 2;
+  if ((int)blockIdx.x >= n_merge) {
+    decode_update_body<true>(upd, blockIdx.x - n_merge, fault);
+    return;
+  }
+  __shared__ float wgt[2][kMergeMaxSplits];
+  const int wave = threadIdx.x >> 6;
+  const int qh = blockIdx.x * 2 + wave;
+  merge_one(qh, qh < n_qh, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt[wave]);
 }
 
 // ---------------------------------------------------------------- prefill HCA: query pairs
@@ -1075,7 +1134,7 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                        const hsa_tokens& wv, int n_win, const hsa_paged& kc,
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
-                       hipStream_t s) {
+                       hipStream_t s, const UpdateArgs* upd) {
   const bool span = q.req == nullptr && q.pos == nullptr;
   int64_t s_max = q.max_pos - n_win + 1 < 0 ? 0 : q.max_pos - n_win + 1;
   int64_t nv_max = (s_max + m - 1) / m;
@@ -1110,6 +1169,25 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.n_hg = p.n_hg;
   a.n_q = q.n;
   a.fault = fault_word();
+  a.knew = a.vnew = nullptr;
+  a.ring_rows = INT64_MAX;
+  // the decode upkeep (upd): after the attention, in the merge launch, when
+  // the queries are split (the attention then reads each query's own token
+  // from k_new / v_new); otherwise before it, on its own
+  bool upd_in_merge = false;
+  if (upd) {
+    const int64_t rows_k = (int64_t)wk.n_req * wk.capacity, rows_v = (int64_t)wv.n_req * wv.capacity;
+    const int64_t rows = rows_k > rows_v ? rows_k : rows_v;
+    upd_in_merge = !span && p.n_splits > 1 && p.nw >= 4 && rows + q.n < INT32_MAX - 2;
+    if (upd_in_merge) {
+      a.knew = upd->k_new;
+      a.vnew = upd->v_new;
+      a.ring_rows = rows;
+    } else {
+      hipError_t e = launch_update(*upd, q.n, s);
+      if (e != hipSuccess) return e;
+    }
+  }
   int64_t n_blocks = (int64_t)q.n * p.n_hg * p.n_splits;
   a.xcd = span ? 1 : 0;
   if (a.xcd) n_blocks = (n_blocks + 7) / 8 * 8;
@@ -1138,11 +1216,23 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   // tiles; decode (few workgroups, latency first): two
   if (p.nw == 4 && span && !f8)
     timed_launch(HSA_K_ATTN, attn_kernel<4, false, true, false>, grid, dim3(256), pre, s, a);
+  else if (p.nw == 8 && upd_in_merge)
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<8, true, false, true, true>
+                      : f8 ? attn_kernel<8, true, false, false, true>
+                           : attn_kernel<8, false, false, false, true>,
+                 grid, dim3(512), pre, s, a);
   else if (p.nw == 8)
     timed_launch(HSA_K_ATTN,
                  kmix ? attn_kernel<8, true, false, true>
                       : f8 ? attn_kernel<8, true, false, false> : attn_kernel<8, false, false, false>,
                  grid, dim3(512), pre, s, a);
+  else if (p.nw == 4 && upd_in_merge)
+    timed_launch(HSA_K_ATTN,
+                 kmix ? attn_kernel<4, true, false, true, true>
+                      : f8 ? attn_kernel<4, true, false, false, true>
+                           : attn_kernel<4, false, false, false, true>,
+                 grid, dim3(256), pre, s, a);
   else if (p.nw == 4)
     timed_launch(HSA_K_ATTN,
                  kmix ? attn_kernel<4, true, false, true>
@@ -1158,9 +1248,15 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
                  kmix ? attn_kernel<1, true, false, true>
                       : f8 ? attn_kernel<1, true, false, false> : attn_kernel<1, false, false, false>,
                  grid, dim3(64), pre, s, a);
-  if (p.n_splits > 1)
-    attn_merge_kernel<<<(unsigned)(q.n * H), 64, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml,
-                                                           O, a.o_f32, lse, a.fault);
+  if (p.n_splits > 1) {
+    const int n_qh = q.n * H;
+    if (upd_in_merge)
+      attn_merge_upd_kernel<<<(unsigned)((n_qh + 1) / 2 + q.n), 128, 0, s>>>(
+          n_qh, H, p.n_splits, a.part_o, a.part_ml, O, a.o_f32, lse, a.fault, *upd);
+    else
+      attn_merge_kernel<<<(unsigned)n_qh, 64, 0, s>>>(H, p.n_splits, a.part_o, a.part_ml, O,
+                                                       a.o_f32, lse, a.fault);
+  }
   return hipGetLastError();
 }
 

@@ -316,11 +316,15 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
 // request's result does not depend on the batch it is in)
 int attn_decode_cps(int k, int n_win);
 size_t attn_ws_bytes(int n_q, int H, int64_t max_entries, bool span, int decode_cps);
+// upd (decode, one token per request, listed queries = requests 0..n-1): the
+// cache upkeep, run after the attention in the merge launch when the queries
+// are split (the attention reads each query's own token from upd->k_new /
+// v_new), else before it
 hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tokens& wk,
                        const hsa_tokens& wv, int n_win, const hsa_paged& kc,
                        const hsa_paged& vc, int m, const int32_t* idx, int k, float scale,
                        void* O, int o_dtype, float* lse, void* ws, size_t ws_bytes,
-                       hipStream_t s);
+                       hipStream_t s, const UpdateArgs* upd = nullptr);
 
 // the decode upkeep kernel over prepared arguments (B requests, one token each)
 hipError_t launch_update(const UpdateArgs& u, int B, hipStream_t s);

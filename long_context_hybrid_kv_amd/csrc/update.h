@@ -2,12 +2,14 @@
 // 深度研究剖析" §11.4: the raw window and the incomplete tail live in a state
 // cache; every m tokens the tail becomes one compressed entry).
 //
-// Shared by the standalone upkeep kernel (HCA layers, drafts), the indexer
-// scan kernel (plain bf16 CSA layers: one extra workgroup per request beside
-// its scan) and the candidate selection kernel (CSA layers with fp8 caches or
-// RoPE, long rows: extra workgroups beside the selection).  The block that
-// completes at position t is not visible to the query at t (it starts inside
-// the window), so nothing in the same launch reads what the upkeep writes.
+// Shared by the standalone upkeep kernel (drafts, RoPE layers, short HCA
+// rows), the indexer scan kernel (plain bf16 CSA layers: one extra workgroup
+// per request beside its scan), the candidate selection kernel (CSA layers
+// with fp8 caches or RoPE, long rows: extra workgroups beside the selection)
+// and the attention's merge kernel (HCA layers: after the attention, which
+// read the new token from its input).  The block that completes at position t
+// is not visible to the query at t (it starts inside the window), so nothing
+// in the same launch reads what the upkeep writes.
 #pragma once
 #include "common.h"
 
