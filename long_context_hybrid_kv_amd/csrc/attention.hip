@@ -339,11 +339,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   }
   // the position, the request's entry counts and -- decode -- what the rows
   // depend on (top-k ids, or page ids) are requested together, before any of
-  // them is used: one memory round trip instead of three
+  // them is used: one memory round trip.  The ids are loaded first, into
+  // registers, and the position and counts last: those are uniform values the
+  // compiler waits for as soon as they are loaded, and loads complete in
+  // order, so that one wait covers every load.
   const bool listed = a.Q.pos != nullptr;
   const int r = a.Q.req_of(qi, a.fault);
-  const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
-  const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
   // dynamic LDS: the row ids of the split's entries (K, then V), then -- decode
   // launches -- the prefetched top-k or page ids
   // (fp8: 32-bit row ids, pool rows holding fp8 codes and window rows bf16;
@@ -353,28 +354,51 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   RowT* rowk = (RowT*)dyn_lds;
   RowT* rowv = rowk + a.cps * 64;
   int* spre = (int*)(rowv + a.cps * 64);
-  Prefetch pf{nullptr, 0, 0};
-  if (!a.xcd) {
-    const int e_nom = split * a.cps * 64, n_nom = a.cps * 64;
-    if (a.k > 0) {
-      const int lo = e_nom - a.n_win > 0 ? e_nom - a.n_win : 0;
-      const int hi = e_nom + n_nom < a.k ? e_nom + n_nom : a.k;
-      for (int i = tid; i < hi - lo; i += NT) spre[i] = a.idx[(int64_t)qi * a.k + lo + i];
-      pf = Prefetch{spre, lo, hi > lo ? hi - lo : 0};
-    } else if (!a.Q.req) {
-      const int p_lo = e_nom - a.n_win > 0 ? (e_nom - a.n_win) >> 6 : 0;
-      int n = ((e_nom + n_nom - 1) >> 6) + 1 - p_lo;
-      n = n < kPrePages ? n : kPrePages;
-      for (int i = tid; i < n; i += NT) {
-        const int lp = p_lo + i;
-        spre[i] = lp < a.kc.pages_per_req ? a.kc.page_table[(int64_t)r * a.kc.pages_per_req + lp] : -1;
-        spre[kPrePages + i] =
-            lp < a.vc.pages_per_req ? a.vc.page_table[(int64_t)r * a.vc.pages_per_req + lp] : -1;
-      }
-      pf = Prefetch{spre, p_lo, n};
-    }
-    __syncthreads();
+  const int e_nom = split * a.cps * 64, n_nom = a.cps * 64;
+  // CSA: top-k positions [pre_lo, pre_lo + n_pre); HCA (one query per request,
+  // in request order): pages [pre_lo, pre_lo + n_pre) of both caches
+  const int pre_mode = a.xcd ? 0 : (a.k > 0 ? 1 : (!a.Q.req ? 2 : 0));
+  int pre_lo = 0, n_pre = 0;
+  if (pre_mode == 1) {
+    pre_lo = e_nom - a.n_win > 0 ? e_nom - a.n_win : 0;
+    const int hi = e_nom + n_nom < a.k ? e_nom + n_nom : a.k;
+    n_pre = hi > pre_lo ? hi - pre_lo : 0;
+  } else if (pre_mode == 2) {
+    pre_lo = e_nom - a.n_win > 0 ? (e_nom - a.n_win) >> 6 : 0;
+    const int n = ((e_nom + n_nom - 1) >> 6) + 1 - pre_lo;
+    n_pre = n < kPrePages ? n : kPrePages;
   }
+  int id_a = -1, id_b = -1;   // this thread's first ids (K and V pages, or one top-k id)
+  if (tid < n_pre) {
+    if (pre_mode == 1) {
+      id_a = a.idx[(int64_t)qi * a.k + pre_lo + tid];
+    } else {
+      // clamped in-bounds reads (pages_per_req >= 1), masked below
+      const int lp = pre_lo + tid;
+      const int lk = lp < a.kc.pages_per_req ? lp : a.kc.pages_per_req - 1;
+      const int lv = lp < a.vc.pages_per_req ? lp : a.vc.pages_per_req - 1;
+      id_a = a.kc.page_table[(int64_t)r * a.kc.pages_per_req + lk];
+      id_b = a.vc.page_table[(int64_t)r * a.vc.pages_per_req + lv];
+    }
+  }
+  const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
+  const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
+  Prefetch pf{nullptr, 0, 0};
+  if (pre_mode != 0) {
+    if (tid < n_pre) {
+      if (pre_mode == 1) {
+        spre[tid] = id_a;
+      } else {
+        const int lp = pre_lo + tid;
+        spre[tid] = lp < a.kc.pages_per_req ? id_a : -1;
+        spre[kPrePages + tid] = lp < a.vc.pages_per_req ? id_b : -1;
+      }
+    }
+    if (pre_mode == 1)   // top-k ranges longer than the workgroup
+      for (int i = tid + NT; i < n_pre; i += NT) spre[i] = a.idx[(int64_t)qi * a.k + pre_lo + i];
+    pf = Prefetch{spre, pre_lo, n_pre};
+  }
+  if (!a.xcd) __syncthreads();
   int64_t t = p_raw;
   if (listed && (t > a.Q.max_pos || t < 0)) {
     atomicOr(a.fault, HSA_FAULT_POS);
@@ -416,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int e_base = c_lo * 64;
   const int n_ent = (c_hi > c_lo) ? (c_hi - c_lo) * 64 : 0;
   // the window start's ring slots: one division per workgroup (s0 is uniform)
-  const int64_t w0k = s0 % a.wk.capacity, w0v = s0 % a.wv.capacity;
+  const int64_t w0k = mod_nn(s0, a.wk.capacity), w0v = mod_nn(s0, a.wv.capacity);
   for (int j = tid; j < n_ent; j += NT) {
     if constexpr (F8)
       resolve<NR>(a, pf, qi, r, w0k, w0v, n_w, E, nv, e_base + j, &rowk[j], &rowv[j]);
@@ -724,7 +748,7 @@ __device__ __forceinline__ void merge_one(int qh, bool on, int H, int n_splits,
                                           const u16* __restrict__ part_o,
                                           const float* __restrict__ part_ml, void* __restrict__ O,
                                           int o_f32, float* __restrict__ lse, int* fault,
-                                          float* wgt) {
+                                          float* wgt, float* wls) {
   const int lane = threadIdx.x & 63;
   const int q = on ? qh / H : 0, h = on ? qh % H : 0;
   const int ns = !on ? 0 : (n_splits < kMergeMaxSplits ? n_splits : kMergeMaxSplits);
@@ -733,10 +757,13 @@ __device__ __forceinline__ void merge_one(int qh, bool on, int H, int n_splits,
   uint32_t v[kMergePF];
 #pragma unroll
   for (int j = 0; j < kMergePF; ++j) v[j] = j < ns ? po[j * stride] : 0u;
+  // each split's (max, sum) pair is read once: the max to wgt[], the sum to
+  // wls[] (the lane that reads them is the lane that uses them)
   float mloc = -INFINITY;
   for (int s = lane; s < ns; s += 64) {
     const float2 ml = *(const float2*)&part_ml[(((int64_t)q * n_splits + s) * H + h) * 2];
     wgt[s] = ml.x;
+    wls[s] = ml.y;
     mloc = fmaxf(mloc, ml.x);
   }
 #pragma unroll
@@ -744,8 +771,7 @@ __device__ __forceinline__ void merge_one(int qh, bool on, int H, int n_splits,
   const float M = mloc;
   float lloc = 0.f;
   for (int s = lane; s < ns; s += 64) {
-    const float ls = part_ml[(((int64_t)q * n_splits + s) * H + h) * 2 + 1];
-    const float wl = exp2f(wgt[s] - M) * ls;
+    const float wl = exp2f(wgt[s] - M) * wls[s];
     wgt[s] = wl;
     lloc += wl;
   }
@@ -785,8 +811,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(int H, int n_splits,
                                                         const float* __restrict__ part_ml,
                                                         void* __restrict__ O, int o_f32,
                                                         float* __restrict__ lse, int* fault) {
-  __shared__ float wgt[kMergeMaxSplits];
-  merge_one(blockIdx.x, true, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt);
+  __shared__ float wgt[kMergeMaxSplits], wls[kMergeMaxSplits];
+  merge_one(blockIdx.x, true, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt, wls);
 }
 
 // The merge with the decode cache upkeep of an HCA layer: two (query, head)
@@ -804,10 +830,11 @@ __global__ __launch_bounds__(128) void attn_merge_upd_kernel(int n_qh, int H, in
     decode_update_body<true>(upd, blockIdx.x - n_merge, fault);
     return;
   }
-  __shared__ float wgt[2][kMergeMaxSplits];
+  __shared__ float wgt[2][kMergeMaxSplits], wls[2][kMergeMaxSplits];
   const int wave = threadIdx.x >> 6;
   const int qh = blockIdx.x * 2 + wave;
-  merge_one(qh, qh < n_qh, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt[wave]);
+  merge_one(qh, qh < n_qh, H, n_splits, part_o, part_ml, O, o_f32, lse, fault, wgt[wave],
+            wls[wave]);
 }
 
 // ---------------------------------------------------------------- prefill HCA: query pairs
@@ -876,7 +903,7 @@ __global__ __launch_bounds__(256) void attn_pair_kernel(AttnArgs a) {
     const uint8_t* zero = (const uint8_t*)g_zero_row;
     // n_wu <= n_win + 1 rows from s0: at most one wrap of a ring whose
     // capacity the host checked (>= n_win + 1, or every position fits)
-    const int64_t w0k = s0 % a.wk.capacity, w0v = s0 % a.wv.capacity;
+    const int64_t w0k = mod_nn(s0, a.wk.capacity), w0v = mod_nn(s0, a.wv.capacity);
     for (int j = tid; j < n_chunks * 64; j += NT) {
       const uint8_t *pk = zero, *pv = zero;
       if (j < n_wu) {

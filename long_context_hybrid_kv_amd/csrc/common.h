@@ -155,14 +155,40 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 
 // ---------------------------------------------------------------- method definitions
 
+// A zero the compiler cannot see through.  A uniform value loaded at an index
+// offset by it stays in a vector register until readfirstlane() moves it to a
+// scalar one: the compiler would otherwise make that move (and wait for the
+// load) right after each load, a round trip per value.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+__device__ __forceinline__ int64_t readfirstlane64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// x / d and x % d for x >= 0, d >= 1.  A 64-bit division is a long scalar
+// sequence that every wave of a workgroup repeats; a power-of-two divisor (the
+// compression rates) is a shift, and operands below 2^32 take the 32-bit
+// division.  The branches are uniform wherever the operands are.
+__device__ __forceinline__ int64_t div_nn(int64_t x, int64_t d) {
+  if ((d & (d - 1)) == 0) return x >> __builtin_ctzll((uint64_t)d);
+  if (((uint64_t)x | (uint64_t)d) >> 32 == 0) return (int64_t)((uint32_t)x / (uint32_t)d);
+  return x / d;
+}
+__device__ __forceinline__ int64_t mod_nn(int64_t x, int64_t d) { return x - div_nn(x, d) * d; }
+
 __device__ __forceinline__ int64_t window_start(int64_t t, int n_win) {
   int64_t s = t - n_win + 1;
   return s < 0 ? 0 : s;
 }
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int n_win) {
   int64_t s = window_start(t, n_win);
-  int64_t a = (s + m - 1) / m;
-  int64_t b = (t + 1) / m;
+  int64_t a = div_nn(s + m - 1, m);
+  int64_t b = div_nn(t + 1, m);
   return a < b ? a : b;
 }
 
@@ -208,7 +234,7 @@ struct Tokens {
   int64_t capacity;
   int32_t dim;
   __device__ __forceinline__ u16* row(int r, int64_t p) const {
-    return (u16*)data + ((int64_t)r * capacity + (p % capacity)) * dim;
+    return (u16*)data + ((int64_t)r * capacity + mod_nn(p, capacity)) * dim;
   }
 };
 
@@ -230,18 +256,20 @@ struct Queries {
     }
     return r;
   }
+  // position of query i; a listed position outside [0, max_pos] is clamped
+  // into it and raises HSA_FAULT_POS
+  __device__ __forceinline__ int64_t pos_of(int i, int* fault) const {
+    if (!pos) return span_pos0 + i;
+    int64_t p = pos[i];
+    if (p > max_pos || p < 0) {
+      atomicOr(fault, HSA_FAULT_POS);
+      p = p < 0 ? 0 : max_pos;
+    }
+    return p;
+  }
   __device__ __forceinline__ void get(int i, int* r, int64_t* t, int* fault) const {
     *r = req_of(i, fault);
-    if (pos) {
-      int64_t p = pos[i];
-      if (p > max_pos || p < 0) {
-        atomicOr(fault, HSA_FAULT_POS);
-        p = p < 0 ? 0 : max_pos;
-      }
-      *t = p;
-    } else {
-      *t = span_pos0 + i;
-    }
+    *t = pos_of(i, fault);
   }
 };
 

@@ -68,8 +68,8 @@ constexpr int kHistSpan = 8192;    // prefill: scores per histogram workgroup
 // scores in the histogram bins down to the one holding its c-th largest, at
 // most kCandCap of them; one workgroup per query selects from their union
 constexpr int kCandCap = 256;      // candidates a scan workgroup may write
-constexpr int kCandBmMaxWords = 16384;   // bitmap words of the emission in LDS
 constexpr int kTopBins = 16;       // nonzero bins >= its cut bin a scan workgroup may list
+constexpr int kCandBmMaxWords = 16384;   // bitmap words of the emission in LDS
 constexpr int kThrCandMax = 4096;  // candidates of the threshold bin the selection refines in LDS
 constexpr int kCandMaxLists = 256;  // scan workgroups (lists) of a query the selection merges
 
@@ -321,8 +321,10 @@ __device__ __forceinline__ void write_hist_list(const uint32_t* lhist, const Idx
 // (score key << 32 | ~block), at most kCandCap of them, and every score left
 // out lies in a bin below b_c.  wcnt records how many there were (more than
 // kCandCap: the selection falls back to the full row), wbin the cut bin (-1
-// when nothing was left out).  n_sc scores in lsc belong to blocks s0 ...
-template <int NTH>
+// when nothing was left out), wtop the nonzero bins >= b_c with their counts
+// (in no particular order; the selection merges them as a set) and wntop how
+// many there were.  n_sc scores in lsc (LCAP slots) belong to blocks s0 ...
+template <int NTH, int LCAP>
 __device__ __forceinline__ void write_candidates(const uint32_t* lhist, const float* lsc, int n_sc,
                                                  int64_t s0, const IdxWs& ws, int qrow, int wg,
                                                  int c_local) {
@@ -331,6 +333,7 @@ __device__ __forceinline__ void write_candidates(const uint32_t* lhist, const fl
   __shared__ uint32_t s_n;
   constexpr int BPT = kBins / NTH;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t li = (int64_t)qrow * ws.n_lists + wg;
   const int lo = kBins - BPT * (tid + 1);        // thread 0 owns the highest bins
   uint32_t v[BPT], sm = 0;
 #pragma unroll
@@ -351,43 +354,63 @@ __device__ __forceinline__ void write_candidates(const uint32_t* lhist, const fl
   }
   __syncthreads();
   const int bc = s_bc;                           // 0 when the workgroup holds fewer scores
-  {
-    // the nonzero bins >= bc, listed as bin << 16 | count
-    uint32_t nz = 0;
+  // Two lists, each compacted with one wave scan and one atomic per wave on a
+  // packed counter (bins << 16 | candidates, both below 2^16): the thread's
+  // nonzero bins >= bc (held in v[]), and its candidates -- PER of the LCAP
+  // slots of lsc, read whether or not they hold a score so that no read waits
+  // behind a branch
+  constexpr int PER = LCAP / NTH;
+  static_assert(PER >= 1 && PER * NTH == LCAP && LCAP < 65536 && kBins < 65536, "packed counts");
+  uint32_t key[PER], cnt = 0, nb = 0;
+  bool c[PER];
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) nz += (lo + j >= bc && v[j] != 0);
-    uint32_t ntot;
-    uint32_t o = block_scan_nt<NTH>(nz, &ntot, sh);
-    uint32_t* lst = ws.wtop + ((int64_t)qrow * ws.n_lists + wg) * kTopBins;
+  for (int j = 0; j < PER; ++j) key[j] = order_key(lsc[tid + NTH * j]);
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) nb += (lo + j >= bc && v[j] != 0);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = tid + NTH * j < n_sc && (int)(key[j] >> 20) >= bc;
+    cnt += c[j];
+  }
+  const uint32_t mine = (nb << 16) | cnt;
+  uint32_t inc = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  const uint32_t wtot = __shfl(inc, 63);
+  uint32_t wb = 0;
+  if (wtot != 0) {   // uniform in the wave
+    if (lane == 0) wb = atomicAdd(&s_n, wtot);
+    wb = __shfl(wb, 0);
+  }
+  const uint32_t base = wb + inc - mine;
+  uint32_t pos = base & 0xFFFFu, ob = base >> 16;
+  uint64_t* dst = ws.wcand + li * kCandCap;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (c[j]) {
+      if (pos < (uint32_t)kCandCap)
+        dst[pos] = ((uint64_t)key[j] << 32) | (uint64_t)(~(uint32_t)(s0 + tid + NTH * j));
+      ++pos;
+    }
+  if (nb != 0 && ob < (uint32_t)kTopBins) {
+    uint32_t* lst = ws.wtop + li * kTopBins;
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j)
       if (lo + j >= bc && v[j] != 0) {
-        if (o < (uint32_t)kTopBins) lst[o] = ((uint32_t)(lo + j) << 16) | v[j];
-        ++o;
+        if (ob < (uint32_t)kTopBins) lst[ob] = ((uint32_t)(lo + j) << 16) | v[j];
+        ++ob;
       }
-    if (tid == 0) ws.wntop[(int64_t)qrow * ws.n_lists + wg] = (int32_t)ntot;
-  }
-  uint64_t* dst = ws.wcand + ((int64_t)qrow * ws.n_lists + wg) * kCandCap;
-  for (int base = 0; base < n_sc; base += NTH) {
-    const int i = base + tid;
-    const uint32_t key = i < n_sc ? order_key(lsc[i]) : 0u;
-    const bool c = i < n_sc && (int)(key >> 20) >= bc;
-    const uint64_t cm = __ballot(c);
-    if (cm) {
-      const int leader = __ffsll((unsigned long long)cm) - 1;
-      uint32_t cb = 0;
-      if (lane == leader) cb = atomicAdd(&s_n, (uint32_t)__popcll(cm));
-      cb = __shfl(cb, leader);
-      const uint32_t pos = cb + __popcll(cm & ((1ull << lane) - 1));
-      if (c && pos < (uint32_t)kCandCap)
-        dst[pos] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(s0 + i));
-    }
   }
   __syncthreads();
   if (tid == 0) {
-    ws.wcnt[(int64_t)qrow * ws.n_lists + wg] = (int32_t)s_n;
-    // anything below the cut bin left out?  (bins below bc hold tot - s_n scores)
-    ws.wbin[(int64_t)qrow * ws.n_lists + wg] = s_n < (uint32_t)n_sc ? bc : -1;
+    const uint32_t n_c = s_n & 0xFFFFu;
+    ws.wcnt[li] = (int32_t)n_c;
+    ws.wntop[li] = (int32_t)(s_n >> 16);
+    // anything below the cut bin left out?  (bins below bc hold tot - n_c scores)
+    ws.wbin[li] = n_c < (uint32_t)n_sc ? bc : -1;
   }
 }
 
@@ -426,11 +449,25 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
                       ? kic.page_table[(int64_t)r * kic.pages_per_req + lp + j]
                       : -1;
   }
-  int rq;
-  int64_t t;
-  Q.get(qrow, &rq, &t, fault);
-  const int64_t nv = clamp_nvis(n_visible(t, m, n_win), kic.n_entries, r, fault,
-                                c_first == 0 && threadIdx.x == 0);
+  // the entry count and the position, issued behind the page ids and moved to
+  // scalar registers only once both are in flight: one wait for all of them
+  const int z = opaque_zero();
+  const int32_t ne_v = kic.n_entries[r + z];
+  const int64_t p_v = Q.pos ? Q.pos[qrow + z] : 0;
+  const int64_t ne = (int32_t)__builtin_amdgcn_readfirstlane(ne_v);
+  int64_t t = Q.span_pos0 + qrow;
+  if (Q.pos) {
+    t = readfirstlane64(p_v);
+    if (t > Q.max_pos || t < 0) {
+      atomicOr(fault, HSA_FAULT_POS);
+      t = t < 0 ? 0 : Q.max_pos;
+    }
+  }
+  int64_t nv = n_visible(t, m, n_win);
+  if (nv > ne) {
+    if (c_first == 0 && threadIdx.x == 0) atomicOr(fault, HSA_FAULT_ENTRIES);
+    nv = ne < 0 ? 0 : ne;
+  }
   const int n_active = nv > 0 ? (int)((nv + kCH - 1) / kCH) : 1;
   if (c_first >= n_active) return;
   if (c_first == 0 && threadIdx.x == 0) ws.state[(int64_t)qrow * kStateInts + 5] = (int32_t)nv;
@@ -489,12 +526,10 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
           atomicOr(fault, HSA_FAULT_PAGE);
     }
   };
-  KeyT xa0[NT], xa1[NT], xb0[NT], xb1[NT];
-  load(0, xa0, xa1);
-  if (CPW > 1) load(1, xb0, xb1);
-
   // query head `row` in the channel order of the keys: bf16, channels 8g..8g+7
-  // then 32+8g..; fp8 and fp4, 16g..16g+7 then 16g+8..16g+15
+  // then 32+8g..; fp8 and fp4, 16g..16g+7 then 16g+8..16g+15.  Requested
+  // before the keys: loads complete in order, and the first chunk's scoring
+  // waits for these, not for the keys of the chunks behind it.
   bf16x8 a0 = {}, a1 = {};
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
@@ -503,6 +538,9 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
+  KeyT xa0[NT], xa1[NT], xb0[NT], xb1[NT];
+  load(0, xa0, xa1);
+  if (CPW > 1) load(1, xb0, xb1);
   // the LDS histogram is cleared while the keys are in flight
   __shared__ uint32_t lhist[kBins];
   __shared__ float lsc[CPW * kCH];
@@ -575,7 +613,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
     const int n_act = (n_active + CPW - 1) / CPW;
     int c_local = (3 * cand_k + n_act - 1) / n_act;
     c_local = c_local < 16 ? 16 : (c_local > kCandCap / 2 ? kCandCap / 2 : c_local);
-    write_candidates<NWV * 64>(lhist, lsc, (int)(s_end - s0), s0, ws, qrow, blockIdx.x, c_local);
+    write_candidates<NWV * 64, CPW * kCH>(lhist, lsc, (int)(s_end - s0), s0, ws, qrow, blockIdx.x, c_local);
   } else
     write_hist_list<NWV * 64>(lhist, ws, qrow, blockIdx.x);
 }
@@ -1453,32 +1491,35 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   // once its length is known.
   const int nl = ws.n_lists;
   const int64_t wrow = (int64_t)qrow * nl;
-  const int64_t nv = st[5];
-  int cnt = 0, bcw = -1, ntop = 0;
-  if (tid < nl) {
-    cnt = ws.wcnt[wrow + tid];
-    bcw = ws.wbin[wrow + tid];
-    ntop = ws.wntop[wrow + tid];
-  }
+  // (every load below is unconditional, from a clamped in-bounds address;
+  // what lies outside a list or past its count is masked where it is used --
+  // a conditional load's zero would overwrite a register still being loaded
+  // and make the compiler wait for the earlier loads)
+  const int tl = tid < nl ? tid : nl - 1;
+  const int cnt = ws.wcnt[wrow + tl];
+  const int bcw = ws.wbin[wrow + tl];
+  const int ntop = ws.wntop[wrow + tl];
   uint32_t e[TB];
 #pragma unroll
   for (int r = 0; r < TB; ++r) {
-    const int slot = r * NT + tid;
-    e[r] = slot / kTopBins < nl ? ws.wtop[wrow * kTopBins + slot] : 0u;
+    const int slot = r * NT + tid, last = nl * kTopBins - 1;
+    e[r] = ws.wtop[wrow * kTopBins + (slot < last ? slot : last)];
   }
   const int tpl = NT / nl;                                // threads per list (>= 4)
   const int lg = tid / tpl, sub = tid - lg * tpl;
   const int cov = tpl * SPEC < kCandCap ? tpl * SPEC : kCandCap;
+  const int lgc = lg < nl ? lg : nl - 1;
   uint64_t xs[SPEC];
 #pragma unroll
   for (int u = 0; u < SPEC; u += 2) {
-    const int j = sub * SPEC + u;
-    const uint4 v = (lg < nl && j < cov)
-                        ? *(const uint4*)(ws.wcand + (wrow + lg) * kCandCap + j)
-                        : make_uint4(0, 0, 0, 0);
+    const int j = sub * SPEC + u < kCandCap - 2 ? sub * SPEC + u : kCandCap - 2;
+    const uint4 v = *(const uint4*)(ws.wcand + (wrow + lgc) * kCandCap + j);
     xs[u] = ((uint64_t)v.y << 32) | v.x;
     xs[u + 1] = ((uint64_t)v.w << 32) | v.z;
   }
+  // the row length last: the compiler waits for it at once (a uniform value),
+  // and loads complete in order, so that one wait covers all of them
+  const int64_t nv = st[5];
   const int64_t W = (nv + 31) / 32;
   for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
 #pragma unroll
@@ -1486,6 +1527,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   if (tid == 0) {
     s_bad = 0; s_maxbc = -1; s_thr = -1; s_ovf = 0; s_above = 0; s_ntc = 0; s_tot = 0;
   }
+  // the loads above stay where they are: the compiler would otherwise sink
+  // them to their first use, a round trip per phase
+#pragma unroll
+  for (int r = 0; r < TB; ++r) asm volatile("" ::"v"(e[r]));
+#pragma unroll
+  for (int u = 0; u < SPEC; ++u) asm volatile("" ::"v"(xs[u]));
   const int n_wg = (int)((nv + ws.list_span - 1) / ws.list_span);   // this row's lists
   int path = 0;
   if (tid < nl) {
