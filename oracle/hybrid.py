@@ -273,6 +273,23 @@ def indexer_scores(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -
     return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float32).astype(np.float64)
 
 
+def indexer_scores_fp4(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -> np.ndarray:
+    """The index scores computed in FP4 (the wiki's §8: the lightning
+    indexer's attention computation runs in FP4), over fp4 keys.  Reading:
+    both operands in the format the keys are stored in (store_fp4_mx) -- each
+    query head's d_I channels quantized in 32-channel blocks, each block with
+    its own power-of-two scale by the same rule -- so that every product of a
+    query value and a key value is exact; then I[b] = sum_h w[h] *
+    max(0, q4[h] . KI_c[b]) in float64 as indexer_scores.
+    qi_bits: bf16 [H_I, d_I]; w: float32 [H_I]; kic_values: the fp4 keys'
+    float64 values [n, d_I]."""
+    qi = nx.bf16_value(qi_bits)
+    packed, sb = store_fp4_mx(qi.reshape(-1, qi.shape[-1]))
+    q4 = fp4_values(packed, sb).reshape(qi.shape)
+    dots = kic_values @ q4.T                        # [n, H_I]
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float32).astype(np.float64)
+
+
 def indexer_scores_bf16(qi_bits: np.ndarray, w: np.ndarray, kic_values: np.ndarray) -> np.ndarray:
     """The index scores as a bf16 selector ranks them (wiki §8: the scores are
     cast from fp32 to bf16 before the top-k): every score rounded once, after
