@@ -204,8 +204,11 @@ hsa_status hsa_kv_compress(const hsa_tokens* x, int32_t x_req, hsa_paged* out, i
  *   idx int32 [n][k]  out: selected blocks ascending, -1 padded
  *   score fp32 [n][k] or NULL: the indexer score of each idx entry (0 at pads)
  * Scores are computed in fp32 from bf16 operands (fp8 codes widen to bf16
- * exactly and the page scale multiplies the head sum; fp4 codes times their
- * power-of-two block scales are bf16 values, widened exactly).  Listed (decode) queries
+ * exactly and the page scale multiplies the head sum).  Over fp4 keys the
+ * indexer computes in FP4 (wiki §8): each query head is quantized to MX FP4
+ * by the keys' rule (32-channel blocks, scale 2^(floor(log2 amax) - 2),
+ * elements to the nearest e2m1 value, ties to even, clamped to +-6) and the
+ * products of the two fp4 operands, all exact, are summed in fp32.  Listed (decode) queries
  * support up to 2^21 visible blocks per query (HSA_ERR_UNSUPPORTED beyond). */
 size_t hsa_indexer_topk_workspace_bytes(const hsa_queries* q, int32_t m, int32_t n_win,
                                         int32_t k);

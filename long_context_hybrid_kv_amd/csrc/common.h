@@ -125,6 +125,54 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t c, float scale) {
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3);
   return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+// 32 consecutive bf16 values (v[0] holds channels 0..7) -> OCP MX FP4, by the
+// rule the key compressor applies: scale 2^x, x = floor(log2 amax) - 2 clamped
+// to [-127, 127] (0 for a block of zeros), each value / 2^x to the nearest
+// e2m1 code (ties to even, saturating at +-6).  Returns the 32 codes, channel
+// i in bits 4i .. 4i+3 of the 128-bit value (the nibble order of a stored
+// key), and the e8m0 scale byte x + 127 in *sbyte.
+__device__ __forceinline__ u32x4 mx_fp4_quantize(const bf16x8 (&v)[4], uint32_t* sbyte) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf((float)v[i >> 3][i & 7]));
+  int E;
+  (void)frexpf(amax, &E);                      // amax = f * 2^E, f in [0.5, 1)
+  int xs = amax > 0.f ? E - 3 : 0;
+  xs = xs < -127 ? -127 : (xs > 127 ? 127 : xs);
+  // exact in float: a bf16 value times 2^-x lands in [2^-6, 8) or is 0, and
+  // the grid's quanta are powers of two
+  const float inv = ldexpf(1.f, -xs);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const float x = (float)v[i >> 3][i & 7] * inv;
+    const uint32_t sign = __builtin_signbit(x) ? 8u : 0u;
+    float a = fminf(fabsf(x), 6.f);
+    const float q = a < 2.f ? 0.5f : (a < 4.f ? 1.f : 2.f);
+    a = __builtin_rintf(a / q) * q;            // ties to even on the grid
+    const uint32_t mag = a < 2.f ? (uint32_t)(2.f * a)
+                       : a < 4.f ? (uint32_t)(a + 2.f) : (uint32_t)(4.f + 0.5f * a);
+    w[i >> 3] |= (sign | mag) << (4 * (i & 7));
+  }
+  *sbyte = (uint32_t)(xs + 127);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// sum over 128 channels of a x b for MX FP4 operands on the 16x16x128 scaled
+// MFMA (A: lane l holds row l % 16, channels 32 (l / 16) .. +31, with its
+// block's scale byte; B likewise for column l % 16); acc += that product
+__device__ __forceinline__ f32x4 mfma_mx_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb,
+                                            f32x4 acc) {
+  const i32x8 a8 = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8 b8 = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  f32x4 r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc, 4, 4, 0, (int)sa, 0,
+                                                             (int)sb);
+  // an MFMA needs every lane of the wave: the empty statement keeps the
+  // compiler from sinking it into a branch that only some lanes take (where
+  // its result is used)
+  asm volatile("" : "+v"(r));
+  return r;
+}
 // an e8m0 scale byte (2^(byte - 127)) as a float
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __uint_as_float(b ? b << 23 : 0x00400000u);

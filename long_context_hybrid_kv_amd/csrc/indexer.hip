@@ -7,7 +7,12 @@
 // the B operand holds 16 compressed indexer keys, so each lane of the result
 // owns the 4 heads of one (query, block) pair and the head sum stays in-lane.
 // A B operand row is 16 contiguous bytes of a key, read straight from the
-// paged cache; prefill stages the A operand (queries) in LDS.
+// paged cache; prefill stages the A operand (queries) in LDS.  Over fp4 keys
+// (OCP MX FP4) the indexer computes in FP4: each query head is quantized to
+// MX FP4 by the keys' own rule, and the 16x16x128 MX-scaled MFMA takes both
+// operands as e2m1 codes with their e8m0 block scales (every product exact,
+// fp32 accumulation); the upper half of its 128-deep operands meets zero
+// query codes.
 //
 // Selection is exact, with no synchronisation between workgroups inside a
 // kernel (on this multi-XCD chip a device-scope fence per workgroup costs more
@@ -500,13 +505,13 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
         x0[u] = __builtin_nontemporal_load(
             (const KeyT*)(kic.data + ((int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row) * kDI) + g);
       } else if constexpr (F4K) {
-        // 32-byte keys: one load instruction reads 16 whole keys, lane (row, g)
-        // the 16 channels 16g .. 16g+15 (all in block g / 2) and that block's
-        // scale byte (.z)
+        // 32-byte keys, the MFMA's B operand: lane (row, g) reads MX block g & 1
+        // of key `row` (16 bytes, 32 channels) and its scale byte (x1[u].x);
+        // lanes g >= 2 fill the 128-deep operand's upper half, which meets
+        // zero query codes
         const int64_t er = (int64_t)(okp ? pg : 0) * kPage + 16 * (u & 3) + row;
-        const u32x2 cw = __builtin_nontemporal_load((const u32x2*)(kic.data + er * (kDI / 2)) + g);
-        const uint32_t sb = ((const uint8_t*)kic.scale)[er * (kDI / 32) + (g >> 1)];
-        x0[u] = u32x4{cw.x, cw.y, sb, 0u};
+        x0[u] = __builtin_nontemporal_load((const u32x4*)(kic.data + er * (kDI / 2)) + (g & 1));
+        x1[u].x = ((const uint8_t*)kic.scale)[er * (kDI / 32) + (g & 1)];
       } else {
         // whole rows: each load instruction reads 8 consecutive 128-byte keys,
         // lane (r8, p8) piece p8 of key r8 (score() moves them to the MFMA
@@ -531,10 +536,18 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   // before the keys: loads complete in order, and the first chunk's scoring
   // waits for these, not for the keys of the chunks behind it.
   bf16x8 a0 = {}, a1 = {};
+  bf16x8 aq[F4K ? 4 : 1] = {};   // fp4: this lane's 32 query channels (block g)
   if (row < kHI) {
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
-    a0 = qa[F8K || F4K ? 2 * g : g];
-    a1 = qa[F8K || F4K ? 2 * g + 1 : 4 + g];
+    if constexpr (F4K) {
+      if (g < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aq[i] = qa[4 * g + i];
+      }
+    } else {
+      a0 = qa[F8K ? 2 * g : g];
+      a1 = qa[F8K ? 2 * g + 1 : 4 + g];
+    }
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
@@ -546,6 +559,13 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   __shared__ float lsc[CPW * kCH];
   __shared__ bf16x8 ltile[F8K ? 1 : NWV][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
   for (int i = threadIdx.x; i < kBins; i += NWV * 64) lhist[i] = 0;
+  // fp4: the query heads in MX FP4 (the indexer computes in FP4), the MFMA's
+  // A operand: lane (row, g < 2) holds block g of head `row`; the other lanes
+  // zero codes with scale 1
+  u32x4 qf = {0u, 0u, 0u, 0u};
+  uint32_t qs = 127u;
+  if constexpr (F4K)
+    if (row < kHI && g < 2) qf = mx_fp4_quantize(aq, &qs);
   __syncthreads();
 
   auto score = [&](int c, const KeyT* x0, const KeyT* x1) {
@@ -559,9 +579,7 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
         k0 = e4m3x8_to_bf16x8(x0[u].xy);   // channels 16g .. 16g+7
         k1 = e4m3x8_to_bf16x8(x0[u].zw);   // channels 16g+8 .. 16g+15
       } else if constexpr (F4K) {
-        const float bs = e8m0_to_f32(x0[u].z);
-        k0 = e2m1x8_to_bf16x8(x0[u].x, bs);
-        k1 = e2m1x8_to_bf16x8(x0[u].y, bs);
+        // (scored by the MX FP4 MFMA below)
       } else {
         // the wave's 16 keys through its LDS tile: piece p of key r is stored
         // at slot p ^ (r & 7), so the row-wise writes and the MFMA-layout
@@ -576,8 +594,12 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
         k1 = ltile[wv][row * 8 + ((4 + g) ^ (row & 7))];
       }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1, acc, 0, 0, 0);
+      if constexpr (F4K) {
+        acc = mfma_mx_fp4(qf, qs, x0[u], x1[u].x, acc);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1, acc, 0, 0, 0);
+      }
       const int64_t b = w0b + 16 * u + row;
       if (g == 0 && b < b_end) {
         float sc = w0 * fmaxf(acc[0], 0.f) + w1 * fmaxf(acc[1], 0.f) +
@@ -804,6 +826,11 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   const int r = Q.span_req;
   const int64_t ne = kic.n_entries[r];
   bf16x8 a[4][2];
+  // fp4 keys: the A operand in MX FP4 (the indexer computes in FP4): lane
+  // (row, g < 2) holds block g of its (query, head) row, the other lanes zero
+  // codes with scale 1
+  u32x4 af[F4K ? 4 : 1];
+  uint32_t as[F4K ? 4 : 1];
   float wq[4][4];
   int64_t nvq[4];
   int64_t nv_max = 0;
@@ -812,11 +839,24 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     int ql = 16 * qt + 4 * at + (row >> 2);      // local row of the A operand's query
     a[at][0] = bf16x8{};
     a[at][1] = bf16x8{};
+    if constexpr (F4K) {
+      af[at] = u32x4{0u, 0u, 0u, 0u};
+      as[at] = 127u;
+    }
     if (ql < nq) {
       const bf16x8* qa =
           (const bf16x8*)(qI + ((int64_t)(q_base + ql) * kHI + (row & 3)) * kDI);
-      a[at][0] = qa[F4K ? 2 * g : g];   // fp4 keys: channels 16g .. 16g+15 per lane
-      a[at][1] = qa[F4K ? 2 * g + 1 : 4 + g];
+      if constexpr (F4K) {
+        if (g < 2) {
+          bf16x8 blk[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) blk[i] = qa[4 * g + i];
+          af[at] = mx_fp4_quantize(blk, &as[at]);
+        }
+      } else {
+        a[at][0] = qa[g];
+        a[at][1] = qa[4 + g];
+      }
     }
     int qg = 16 * qt + 4 * at + g;               // local query of this lane's result rows
     nvq[at] = 0;
@@ -863,9 +903,11 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   // branch-free key loads (rows past the end, or on a bad page, read row 0 of
   // page 0 and are never stored); the next tile's keys load while this one's
   // scores are computed
-  // key pieces: bf16 (16 bytes) or fp8 codes (8 bytes, widened to bf16 when
-  // scored, with the page scale applied to the head sum)
-  typedef typename std::conditional<F8K || F4K, u32x2, bf16x8>::type KeyT;
+  // key pieces: bf16 (16 bytes), fp8 codes (8 bytes, widened to bf16 when
+  // scored, with the page scale applied to the head sum) or an fp4 MX block
+  // (16 bytes; its scale byte in x1.x)
+  typedef typename std::conditional<F4K, u32x4,
+                                    typename std::conditional<F8K, u32x2, bf16x8>::type>::type KeyT;
   auto load = [&](int64_t tile, KeyT& x0, KeyT& x1, float& sc) {
     const int64_t b = 16 * tile + row;
     int page = -1;
@@ -873,9 +915,11 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     const bool ok = page >= 0;
     const KeyT* kr = (const KeyT*)kic.row(ok ? page : 0, ok ? b : 0);
     if constexpr (F4K) {
-      x0 = kr[g];   // 8 bytes: channels 16g .. 16g+15, all in block g / 2
+      // the B operand: lane (row, g) block g & 1 of the key (lanes g >= 2 meet
+      // zero query codes)
+      x0 = kr[g & 1];
       const int64_t er = (int64_t)(ok ? page : 0) * kPage + (ok ? (b & 63) : 0);
-      sc = e8m0_to_f32(((const uint8_t*)kic.scale)[er * (kDI / 32) + (g >> 1)]);
+      x1.x = ((const uint8_t*)kic.scale)[er * (kDI / 32) + (g & 1)];
     } else if constexpr (F8K) {
       x0 = kr[g];
       x1 = kr[4 + g];
@@ -906,8 +950,7 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
       k0 = e4m3x8_to_bf16x8(c0);
       k1 = e4m3x8_to_bf16x8(c1);
     } else if constexpr (F4K) {
-      k0 = e2m1x8_to_bf16x8(c0.x, cs);
-      k1 = e2m1x8_to_bf16x8(c0.y, cs);
+      // (scored by the MX FP4 MFMA below)
     } else {
       // through the wave's swizzled LDS tile into the MFMA layout (as the scan)
       asm volatile("" ::: "memory");
@@ -920,8 +963,12 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
 #pragma unroll
     for (int at = 0; at < 4; ++at) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], k0, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], k1, acc, 0, 0, 0);
+      if constexpr (F4K) {
+        acc = mfma_mx_fp4(af[at], as[at], c0, c1.x, acc);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][0], k0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[at][1], k1, acc, 0, 0, 0);
+      }
       if (b < nvq[at]) {
         float s = wq[at][0] * fmaxf(acc[0], 0.f) + wq[at][1] * fmaxf(acc[1], 0.f) +
                   wq[at][2] * fmaxf(acc[2], 0.f) + wq[at][3] * fmaxf(acc[3], 0.f);

@@ -2,11 +2,12 @@
 FP4 indexer, read as OCP MX FP4: e2m1 codes in 32-channel blocks with a
 power-of-two e8m0 scale) against the oracle fed the same fp4 cache.
 
-The compressor's codes and scale bytes equal the oracle's bit for bit.  The
-kernels widen each code times its block scale to bf16 exactly (a power-of-two
-scale keeps an e2m1 value a bf16 value), so the scores are the fp32 sums of
-exact products and the selection is compared with the same tie band as the
-bf16 path."""
+The compressor's codes and scale bytes equal the oracle's bit for bit.  Over
+fp4 keys the indexer computes in FP4: the kernels quantize each query head to
+MX FP4 by the keys' rule and score on the MX-scaled MFMA, so every product is
+exact and the scores are fp32 sums of them; the oracle's indexer_scores_fp4
+quantizes the same way and sums in float64.  The selection is compared with
+the same tie band as the bf16 path."""
 import numpy as np
 import pytest
 import torch
@@ -59,16 +60,17 @@ def test_prefill_indexer_fp4_keys(k):
     ok = orc.compress(inp["ki"], inp["zi"], m, "fp4")
     for t in range(T_):
         nv = orc.n_visible(t, m, n_win)
-        s = orc.indexer_scores(inp["qi"][t], inp["w"][t], ok.values[:nv])
+        s = orc.indexer_scores_fp4(inp["qi"][t], inp["w"][t], ok.values[:nv])
         T.check_topk(idx[t], s, k, where=f"row {t}")
         sel = idx[t][idx[t] >= 0]
         assert np.allclose(score[t][: len(sel)], s[sel], rtol=1e-4, atol=1e-3), t
 
 
-@pytest.mark.parametrize("Ls", [[1, 131, 700, 4099, 9001], [40000, 70001]])
+@pytest.mark.parametrize("Ls", [[1, 131, 700, 4099, 9001], [40000, 70001], [600001]])
 def test_decode_indexer_fp4_keys(Ls):
     """One query per request (the scan path): rows under and over the fused
-    selection's 16384 blocks, on a shuffled page pool."""
+    selection's 16384 blocks, and one of 150,000 blocks (the scan's four-chunk
+    workgroups), on a shuffled page pool."""
     w = configs.shrink(configs.CSA_DECODE_128K, B=len(Ls))
     m, n_win, k = w.m_csa, w.n_win, w.k_csa
     reqs = [gen.decode_request(w, "csa", r, L=int(Ls[r])) for r in range(len(Ls))]
@@ -90,7 +92,7 @@ def test_decode_indexer_fp4_keys(Ls):
         t = int(Ls[r])
         ok = orc.compress(d["ki"][:t], z, m, "fp4")
         nv = orc.n_visible(t, m, n_win)
-        s = orc.indexer_scores(d["qi"][0], d["w"][0], ok.values[:nv])
+        s = orc.indexer_scores_fp4(d["qi"][0], d["w"][0], ok.values[:nv])
         T.check_topk(idx[r], s, k, where=f"req {r} t {t}")
         sel = idx[r][idx[r] >= 0]
         assert np.allclose(score[r][: len(sel)], s[sel], rtol=1e-4, atol=1e-3), r
