@@ -18,7 +18,9 @@ from typing import Optional
 import torch  # load torch's HIP runtime first: the library binds to the same one
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhsa_attn.so")
+# HSA_ATTN_LIB names another build of the same library (the host-sanitizer
+# build); by default the in-tree libhsa_attn.so
+LIB_PATH = os.environ.get("HSA_ATTN_LIB") or os.path.join(_HERE, "libhsa_attn.so")
 
 BF16, FP8, FP32, FP8_BF16_ROPE, FP4 = 0, 1, 2, 3, 4
 LAYER_CSA, LAYER_HCA = 0, 1
