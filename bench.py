@@ -73,13 +73,13 @@ def bf(a):
 
 # ----------------------------------------------------------------------------- decode state
 
-def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, index_fp8=False,
-                       draft=1, kmix=False, index_fp4=False):
+def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, draft=1,
+                       kmix=False, index_fp4=False):
     """Caches of w.B requests holding tokens 0..L-1, rings up to L-1, and the
     new token's inputs (position L), in `copies` independent copies.  fp8 K / V
     caches carry the stash appending to them needs.
-    index_fp8 / index_fp4: the indexer keys are stored fp8 / fp4, and
-    step["kic_bf16"] holds the same keys in bf16 (for the selection recall).
+    index_fp4: the indexer keys are stored fp4 (the indexer computes in FP4),
+    and step["kic_bf16"] holds the same keys in bf16 (for the selection recall).
     draft > 1: the step's inputs are [B][draft][...] (tokens L .. L+draft-1);
     rings hold n_win + draft - 1 tokens and the indexer tail m + draft - 1.
     kmix: the K caches hold mixed entries (RoPE channels bf16, the rest fp8)."""
@@ -94,10 +94,10 @@ def build_decode_state(w, layer, L, T, gen, copies, fp8=False, shuffle=False, in
     stash = fp8 or kmix
     kc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8, page_order=perm, mixed=kmix, stash=stash)
     vc = T.PagedCache.allocate(B, n_ent, 128, fp8=fp8 or kmix, page_order=perm, stash=stash)
-    kic = (T.PagedCache.allocate(B, n_ent, 64, fp8=index_fp8, fp4=index_fp4, page_order=perm)
+    kic = (T.PagedCache.allocate(B, n_ent, 64, fp4=index_fp4, page_order=perm)
            if layer == "csa" else None)
     kic16 = (T.PagedCache.allocate(B, n_ent, 64, page_order=perm)
-             if layer == "csa" and (index_fp8 or index_fp4) else None)
+             if layer == "csa" and index_fp4 else None)
     cap = n_win + draft - 1
     ring_k = torch.zeros((B, cap, 128), dtype=torch.bfloat16, device="cuda")
     ring_v = torch.zeros_like(ring_k)
@@ -628,12 +628,11 @@ def bench_pro_decode(args, w, K, W):
     from long_context_hybrid_kv_amd import _lib as T
     from synth import gen
     L = w.L
-    f8i = getattr(args, "index_fp8", False)
     kmix = getattr(args, "kv_mixed", False)
     f4i = getattr(args, "index_fp4", False)
     t0 = time.time()
     lays = {layer: build_decode_state(w, layer, L, T, gen, args.copies, fp8=True,
-                                      index_fp8=f8i and layer == "csa", kmix=kmix,
+                                      kmix=kmix,
                                       index_fp4=f4i and layer == "csa")
             for layer in ("csa", "hca")}
     log(f"[bench] {w.name}: state built in {time.time() - t0:.1f}s")
@@ -651,15 +650,15 @@ def bench_pro_decode(args, w, K, W):
     T.check_device_error()
     nv, nvh = nvis(L, w.m_csa, w.n_win), nvis(L, w.m_hca, w.n_win)
     B = w.B
-    # indexer key bytes per visible block: 128 (bf16), 64 fp8 codes + the page
-    # scale, or 32 bytes of fp4 codes + 2 scale bytes
-    key_b = 64 + 4 / 64 if f8i else (34 if f4i else 128)
+    # indexer key bytes per visible block: 128 (bf16), or 32 bytes of fp4
+    # codes + 2 scale bytes
+    key_b = 34 if f4i else 128
     scan_bytes = int(B * nv * key_b)
     kv_b = 320 if kmix else 256          # K + V bytes per compressed entry (fp8; mixed K 192)
     step_bytes = B * (nv * key_b + w.k_csa * kv_b + nvh * kv_b + 2 * w.n_win * 512 +
                       4 * w.H * 256)
     extra = {}
-    if f8i or f4i:
+    if f4i:
         st = lays["csa"][1]
         q = T.Queries.list(st["pos"], L)
         i8, _ = T.indexer_topk(q, st["qI"], st["w"], lays["csa"][0][0].kic, w.m_csa, w.n_win,
@@ -669,7 +668,7 @@ def bench_pro_decode(args, w, K, W):
         rec = [len(set(i8[b].tolist()) & set(i16[b].tolist())) / w.k_csa for b in range(B)]
         extra["index_recall_vs_bf16_keys"] = round(float(np.mean(rec)), 4)
     roof = roofline_hbm("idx_scan_kernel", w.name, scan_bytes, scan_ms, cnt)
-    if f8i or f4i:
+    if f4i:
         roof["traffic"] = None
     del lays, steps
     return {"value": B / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms, "steps": K,
@@ -677,8 +676,7 @@ def bench_pro_decode(args, w, K, W):
             "step_algorithmic_bytes": int(step_bytes), **extra,
             "config": {"workload": w.name, "batch": B, "context": L, "heads": w.H, "kv_heads": 1,
                        "d": 128, "topk": w.k_csa, "window": w.n_win, "indexer": "4x64",
-                       "indexer_keys": ("fp8_e4m3+page_scale" if f8i else
-                                        "fp4_e2m1+e8m0_per_32" if f4i else "bf16"),
+                       "indexer_keys": "fp4_e2m1+e8m0_per_32" if f4i else "bf16",
                        "layers": "csa+hca (one hsa_decode_step each)",
                        "kv_dtype": ("k: fp8_e4m3 x64 + bf16 rope x64, v: fp8_e4m3+page_scale"
                                     if kmix else "fp8_e4m3+page_scale"),
@@ -1058,12 +1056,10 @@ def main():
                     help="csa_decode_128k: verify a draft of N tokens per request (1-3 at the "
                          "128K position: no block completes inside it, so replays append "
                          "nothing); tok/s counts draft tokens")
-    ap.add_argument("--index-fp8", action="store_true",
-                    help="pro_decode_1m with fp8 indexer keys; reports the selection recall "
-                         "against bf16 keys")
     ap.add_argument("--index-fp4", action="store_true",
-                    help="pro_decode_1m: fp4 indexer keys (e2m1, an e8m0 scale per 32 channels); "
-                         "also reports the selection recall against bf16 keys")
+                    help="pro_decode_1m: fp4 indexer keys (e2m1, an e8m0 scale per 32 channels; "
+                         "the indexer computes in FP4); also reports the selection recall "
+                         "against bf16 keys")
     ap.add_argument("--kv-mixed", action="store_true",
                     help="pro_decode_1m: K caches hold mixed entries (the 64 RoPE channels bf16, "
                          "the other 64 fp8 with a page scale); V stays fp8")
@@ -1105,10 +1101,8 @@ def main():
         sys.exit(2)
     if args.draft != 1 and (args.workload != "csa_decode_128k" or not 1 <= args.draft <= 3):
         ap.error("--draft takes 1..3 with --workload csa_decode_128k")
-    if (args.index_fp8 or args.index_fp4 or args.kv_mixed) and args.workload != "pro_decode_1m":
-        ap.error("--index-fp8 / --index-fp4 / --kv-mixed apply to --workload pro_decode_1m")
-    if args.index_fp8 and args.index_fp4:
-        ap.error("--index-fp8 and --index-fp4 exclude each other")
+    if (args.index_fp4 or args.kv_mixed) and args.workload != "pro_decode_1m":
+        ap.error("--index-fp4 / --kv-mixed apply to --workload pro_decode_1m")
     if args.index_bf16_scores and args.workload != "hybrid_prefill_128k":
         ap.error("--index-bf16-scores applies to --workload hybrid_prefill_128k")
     if args.steps < 1 or args.warmup < 0:

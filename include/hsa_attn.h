@@ -284,7 +284,10 @@ typedef struct {
   hsa_tokens ring_k, ring_v;    /* raw window K/V, capacity >= n_win (state cache) */
   hsa_tokens tail_i;            /* CSA: raw indexer keys of the open block, capacity >= m */
   hsa_paged  kc, vc;            /* compressed K/V (classical cache) */
-  hsa_paged  kic;               /* CSA: compressed indexer keys (bf16) */
+  hsa_paged  kic;               /* CSA: compressed indexer keys: bf16, or
+                                   HSA_FP4_E2M1_MX (scored in FP4; the step
+                                   appends MX entries; single-token steps
+                                   only, no drafts) */
   double     rope_theta;        /* > 0: partial RoPE with this base (the ring
                                    and the caches then hold turned keys); 0: Q
                                    and K are used as given */

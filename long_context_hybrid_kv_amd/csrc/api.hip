@@ -122,7 +122,8 @@ static hsa_status check_paged(const hsa_paged* p, const char* name, int dim, boo
   REQ(p->dtype == HSA_BF16 || p->dtype == HSA_FP8_E4M3 || p->dtype == HSA_FP8_BF16_ROPE ||
           p->dtype == HSA_FP4_E2M1_MX,
       n + ": unknown dtype");
-  SUP(allow_fp8 || p->dtype == HSA_BF16, n + ": must be bf16");
+  SUP(allow_fp8 || p->dtype == HSA_BF16 || (allow_fp4 && p->dtype == HSA_FP4_E2M1_MX),
+      n + (allow_fp4 ? ": must be bf16 or fp4" : ": must be bf16"));
   SUP(p->dtype != HSA_FP8_BF16_ROPE || (allow_mixed && p->dim == kD),
       n + ": the mixed bf16-RoPE / fp8 format is for compressed K caches of dim 128");
   SUP(p->dtype != HSA_FP4_E2M1_MX || (allow_fp4 && p->dim == kDI),
@@ -483,7 +484,9 @@ static hsa_status check_decode(const hsa_layer* L, int32_t B, int32_t n_tok, con
       "decode: page table too short for the appended entries");
   if (L->kind == HSA_LAYER_CSA) {
     REQ(qI && kI_new && w && L->alpha_i, "decode: CSA needs qI, kI_new, w and alpha_i");
-    if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
+    if ((s = check_paged(&L->kic, "kic", kDI, false, false, true)) != HSA_OK) return s;
+    SUP(L->kic.dtype != HSA_FP4_E2M1_MX || n_tok == 1,
+        "decode: fp4 indexer keys take one token per request (no drafts)");
     // a draft's rejected tokens must not overwrite a kept token of the open
     // block (hsa_decode_rewind): the tail holds m + n_tok - 1 rows
     if ((s = check_tokens(&L->tail_i, "tail_i", kDI, L->m + n_tok - 1)) != HSA_OK) return s;
@@ -645,7 +648,7 @@ hsa_status hsa_decode_rewind(const hsa_layer* L, int32_t B, const int64_t* keep,
   if ((s = check_append_caches(L, "decode_rewind")) != HSA_OK) return s;
   REQ(L->kc.n_req >= B && L->vc.n_req >= B, "decode_rewind: caches hold fewer than B requests");
   if (L->kind == HSA_LAYER_CSA) {
-    if ((s = check_paged(&L->kic, "kic", kDI, false)) != HSA_OK) return s;
+    if ((s = check_paged(&L->kic, "kic", kDI, false, false, true)) != HSA_OK) return s;
     REQ(L->kic.n_req >= B, "decode_rewind: kic holds fewer than B requests");
   }
   return hip_status(launch_decode_rewind(*L, B, keep, stream), "decode_rewind");

@@ -125,37 +125,42 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16x8(uint32_t c, float scale) {
   const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3);
   return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
-// 32 consecutive bf16 values (v[0] holds channels 0..7) -> OCP MX FP4, by the
-// rule the key compressor applies: scale 2^x, x = floor(log2 amax) - 2 clamped
-// to [-127, 127] (0 for a block of zeros), each value / 2^x to the nearest
-// e2m1 code (ties to even, saturating at +-6).  Returns the 32 codes, channel
-// i in bits 4i .. 4i+3 of the 128-bit value (the nibble order of a stored
-// key), and the e8m0 scale byte x + 127 in *sbyte.
-__device__ __forceinline__ u32x4 mx_fp4_quantize(const bf16x8 (&v)[4], uint32_t* sbyte) {
-  float amax = 0.f;
+// OCP MX FP4 of n_rows rows of 64 bf16 channels (row r at src + 64 r; rows
+// >= n_valid read as zeros) by the rule the key compressor applies: per
+// 32-channel block the scale 2^x, x = floor(log2 amax) - 2 clamped to
+// [-127, 127] (0 for a block of zeros), each value / 2^x to the nearest e2m1
+// code (ties to even, saturating at +-6; the sign bit follows the value).
+// One channel a thread: each wave takes whole rows (lanes 0..31 block 0,
+// 32..63 block 1).  Codes go to codes[r][w], channel c in bits 4 (c % 8) of
+// word c / 8 (the nibble order of a stored key); scale bytes x + 127 to
+// sb[r][c / 32].  Every thread of the workgroup calls it; the caller
+// synchronises before reading the arrays.  (The scaling is exact in fp32: a
+// bf16 value times 2^-x lands in [2^-6, 8) or is 0.)
+__device__ __forceinline__ void mx_fp4_rows(const u16* __restrict__ src, int n_rows, int n_valid,
+                                            uint32_t (*codes)[8], uint8_t (*sb)[2]) {
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int r = threadIdx.x >> 6; r < n_rows; r += nw) {
+    const float x = r < n_valid ? __uint_as_float((uint32_t)src[(int64_t)r * 64 + lane] << 16) : 0.f;
+    float a = fabsf(x);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf((float)v[i >> 3][i & 7]));
-  int E;
-  (void)frexpf(amax, &E);                      // amax = f * 2^E, f in [0.5, 1)
-  int xs = amax > 0.f ? E - 3 : 0;
-  xs = xs < -127 ? -127 : (xs > 127 ? 127 : xs);
-  // exact in float: a bf16 value times 2^-x lands in [2^-6, 8) or is 0, and
-  // the grid's quanta are powers of two
-  const float inv = ldexpf(1.f, -xs);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const float x = (float)v[i >> 3][i & 7] * inv;
-    const uint32_t sign = __builtin_signbit(x) ? 8u : 0u;
-    float a = fminf(fabsf(x), 6.f);
-    const float q = a < 2.f ? 0.5f : (a < 4.f ? 1.f : 2.f);
-    a = __builtin_rintf(a / q) * q;            // ties to even on the grid
-    const uint32_t mag = a < 2.f ? (uint32_t)(2.f * a)
-                       : a < 4.f ? (uint32_t)(a + 2.f) : (uint32_t)(4.f + 0.5f * a);
-    w[i >> 3] |= (sign | mag) << (4 * (i & 7));
+    for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+    int E;
+    (void)frexpf(a, &E);                       // a = f * 2^E, f in [0.5, 1)
+    int xs = a > 0.f ? E - 3 : 0;
+    xs = xs < -127 ? -127 : (xs > 127 ? 127 : xs);
+    const float y = x * ldexpf(1.f, -xs);
+    const float m = fminf(fabsf(y), 6.f);
+    // the grid's quantum is 0.5 below 2, 1 in [2, 4), 2 in [4, 6]: its
+    // multiples, rounded to even, give the magnitude code directly
+    const float n = __builtin_rintf(m * (m < 2.f ? 2.f : (m < 4.f ? 1.f : 0.5f)));
+    const uint32_t mag = (uint32_t)n + (m < 2.f ? 0u : (m < 4.f ? 2u : 4u));
+    uint32_t wd = ((__builtin_signbit(y) ? 8u : 0u) | mag) << (4 * (lane & 7));
+    wd |= __shfl_xor(wd, 1);
+    wd |= __shfl_xor(wd, 2);
+    wd |= __shfl_xor(wd, 4);
+    if ((lane & 7) == 0) codes[r][lane >> 3] = wd;
+    if ((lane & 31) == 0) sb[r][lane >> 5] = (uint8_t)(xs + 127);
   }
-  *sbyte = (uint32_t)(xs + 127);
-  return u32x4{w[0], w[1], w[2], w[3]};
 }
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 // sum over 128 channels of a x b for MX FP4 operands on the 16x16x128 scaled

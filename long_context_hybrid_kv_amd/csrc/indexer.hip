@@ -536,18 +536,10 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   // before the keys: loads complete in order, and the first chunk's scoring
   // waits for these, not for the keys of the chunks behind it.
   bf16x8 a0 = {}, a1 = {};
-  bf16x8 aq[F4K ? 4 : 1] = {};   // fp4: this lane's 32 query channels (block g)
-  if (row < kHI) {
+  if (!F4K && row < kHI) {   // (fp4: the query is quantized into LDS below)
     const bf16x8* qa = (const bf16x8*)(qI + ((int64_t)qrow * kHI + row) * kDI);
-    if constexpr (F4K) {
-      if (g < 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) aq[i] = qa[4 * g + i];
-      }
-    } else {
-      a0 = qa[F8K ? 2 * g : g];
-      a1 = qa[F8K ? 2 * g + 1 : 4 + g];
-    }
+    a0 = qa[F8K ? 2 * g : g];
+    a1 = qa[F8K ? 2 * g + 1 : 4 + g];
   }
   const float w0 = w[qrow * kHI + 0], w1 = w[qrow * kHI + 1], w2 = w[qrow * kHI + 2],
               w3 = w[qrow * kHI + 3];
@@ -559,14 +551,20 @@ __global__ __launch_bounds__(NWV * 64) void idx_scan_kernel(Queries Q, const u16
   __shared__ float lsc[CPW * kCH];
   __shared__ bf16x8 ltile[F8K ? 1 : NWV][F8K ? 1 : 128];   // bf16: one 16-key tile per wave
   for (int i = threadIdx.x; i < kBins; i += NWV * 64) lhist[i] = 0;
-  // fp4: the query heads in MX FP4 (the indexer computes in FP4), the MFMA's
-  // A operand: lane (row, g < 2) holds block g of head `row`; the other lanes
-  // zero codes with scale 1
+  // fp4: the query heads in MX FP4 (the indexer computes in FP4), quantized
+  // once per workgroup into LDS, then the MFMA's A operand: lane (row, g < 2)
+  // holds block g of head `row`; the other lanes zero codes with scale 1
+  __shared__ __align__(16) uint32_t qcodes[F4K ? kHI : 1][8];
+  __shared__ uint8_t qsb[F4K ? kHI : 1][2];
+  if constexpr (F4K) mx_fp4_rows(qI + (int64_t)qrow * kHI * kDI, kHI, kHI, qcodes, qsb);
+  __syncthreads();
   u32x4 qf = {0u, 0u, 0u, 0u};
   uint32_t qs = 127u;
   if constexpr (F4K)
-    if (row < kHI && g < 2) qf = mx_fp4_quantize(aq, &qs);
-  __syncthreads();
+    if (row < kHI && g < 2) {
+      qf = *(const u32x4*)&qcodes[row][4 * g];
+      qs = qsb[row][g];
+    }
 
   auto score = [&](int c, const KeyT* x0, const KeyT* x1) {
     const int64_t cb = (int64_t)(c_first + c) * kCH;
@@ -826,11 +824,6 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   const int r = Q.span_req;
   const int64_t ne = kic.n_entries[r];
   bf16x8 a[4][2];
-  // fp4 keys: the A operand in MX FP4 (the indexer computes in FP4): lane
-  // (row, g < 2) holds block g of its (query, head) row, the other lanes zero
-  // codes with scale 1
-  u32x4 af[F4K ? 4 : 1];
-  uint32_t as[F4K ? 4 : 1];
   float wq[4][4];
   int64_t nvq[4];
   int64_t nv_max = 0;
@@ -839,24 +832,11 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
     int ql = 16 * qt + 4 * at + (row >> 2);      // local row of the A operand's query
     a[at][0] = bf16x8{};
     a[at][1] = bf16x8{};
-    if constexpr (F4K) {
-      af[at] = u32x4{0u, 0u, 0u, 0u};
-      as[at] = 127u;
-    }
-    if (ql < nq) {
+    if (!F4K && ql < nq) {   // (fp4: the queries are quantized into LDS below)
       const bf16x8* qa =
           (const bf16x8*)(qI + ((int64_t)(q_base + ql) * kHI + (row & 3)) * kDI);
-      if constexpr (F4K) {
-        if (g < 2) {
-          bf16x8 blk[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) blk[i] = qa[4 * g + i];
-          af[at] = mx_fp4_quantize(blk, &as[at]);
-        }
-      } else {
-        a[at][0] = qa[g];
-        a[at][1] = qa[4 + g];
-      }
+      a[at][0] = qa[g];
+      a[at][1] = qa[4 + g];
     }
     int qg = 16 * qt + 4 * at + g;               // local query of this lane's result rows
     nvq[at] = 0;
@@ -899,7 +879,30 @@ __global__ __launch_bounds__(256) void idx_gemm_kernel(Queries Q, int q_base, in
   if (pg_lds)
     for (int i = threadIdx.x; i < n_pg; i += 256)
       pg[i] = (p_lo + i) * 64 < nv_max ? kic.page_of(r, (p_lo + i) * 64, fault) : -1;
+  // fp4 keys: the workgroup's 16 queries x 4 heads in MX FP4 (the indexer
+  // computes in FP4), quantized once into LDS; the A operand of tile at: lane
+  // (row, g < 2) holds block g of row 16 at + row (query 4 at + row / 4, head
+  // row % 4), the other lanes zero codes with scale 1
+  __shared__ __align__(16) uint32_t qcodes[F4K ? 64 : 1][8];
+  __shared__ uint8_t qsb[F4K ? 64 : 1][2];
+  if constexpr (F4K) {
+    const int nql = nq - 16 * qt < 16 ? nq - 16 * qt : 16;
+    mx_fp4_rows(qI + (int64_t)(q_base + 16 * qt) * kHI * kDI, 64, nql * kHI, qcodes, qsb);
+  }
   __syncthreads();
+  u32x4 af[F4K ? 4 : 1];
+  uint32_t as[F4K ? 4 : 1];
+  if constexpr (F4K) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      af[at] = u32x4{0u, 0u, 0u, 0u};
+      as[at] = 127u;
+      if (g < 2) {
+        af[at] = *(const u32x4*)&qcodes[16 * at + row][4 * g];
+        as[at] = qsb[16 * at + row][g];
+      }
+    }
+  }
   // branch-free key loads (rows past the end, or on a bad page, read row 0 of
   // page 0 and are never stored); the next tile's keys load while this one's
   // scores are computed
@@ -1853,11 +1856,12 @@ hipError_t launch_indexer(const hsa_queries& q, const void* qI, const float* w,
     // threshold / select / refine chain)
     const bool cand = R > kFusedMaxBlocksDecode && R / 32 <= kCandBmMaxWords &&
                       ws.n_lists <= kCandMaxLists;
-    // the decode cache upkeep: plain bf16 K / V caches in the scan launch; the
-    // full upkeep (fp8 page re-encoding, RoPE: registers the scan should not
-    // carry) in the candidate selection launch, or on its own before the scan
+    // the decode cache upkeep: plain bf16 caches in the scan launch; the full
+    // upkeep (fp8 page re-encoding, RoPE, fp4 indexer keys: registers the scan
+    // should not carry) in the candidate selection launch, or on its own
+    // before the scan
     const bool full_upd = upd && (upd->kc.dtype != HSA_BF16 || upd->vc.dtype != HSA_BF16 ||
-                               upd->rope_on);
+                               upd->rope_on || (upd->csa && upd->kic.dtype != HSA_BF16));
     if (full_upd && !cand) {
       hipError_t e = launch_update(*upd, q.n, s);
       if (e != hipSuccess) return e;

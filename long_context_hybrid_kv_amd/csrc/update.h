@@ -123,9 +123,10 @@ __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, 
 // writes and pools its own channel, so tokens of one request are handled in
 // order without cross-thread hand-off); every thread of the workgroup must call
 // this (it synchronises the workgroup).  F8: the full upkeep -- the K / V
-// caches may be fp8, keys and queries may be turned (RoPE); the indexer scan
-// launch, which carries the upkeep of plain bf16 CSA layers, is compiled
-// without it (its float64 page loops would raise the scan's registers).
+// caches may be fp8, keys and queries may be turned (RoPE), the indexer keys
+// may be fp4; the indexer scan launch, which carries the upkeep of plain bf16
+// CSA layers, is compiled without it (its float64 page loops would raise the
+// scan's registers).
 // With RoPE (F8 path) the token's pair angles are computed here, once, and
 // left in rcs[i] = (cos, sin) for the query at the same position; a position
 // outside [0, max_pos] is clamped for that (the attention clamps it too).
@@ -193,10 +194,29 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
     append_kv<F8>(u.kc, b, blk, vk, fault, red);
     append_kv<F8>(u.vc, b, blk, vv, fault, red);
   }
-  if (u.csa && c < kDI) {
+  if (u.csa && c < kDI) {   // wave 0, every lane: channel c of the indexer key
     const int pi = u.kic.page_of(b, blk, fault);
-    if (pi >= 0)
-      ((u16*)u.kic.row(pi, blk))[c] = f64_to_bf16(pool_last(u.ti, b, blk, u.m, c, u.ai, kDI, in));
+    const double v = pool_last(u.ti, b, blk, u.m, c, u.ai, kDI, in);
+    if (F8 && u.kic.dtype == HSA_FP4_E2M1_MX) {   // (fp4 keys take the full upkeep)
+      // MX FP4 as the compressor stores it: the 32-channel block's amax over
+      // its 32 lanes, the scale 2^x, x = floor(log2 amax) - 2, one e2m1 code a
+      // lane, channel 2j in the low nibble of byte j
+      double a = fabs(v);
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) a = fmax(a, __shfl_xor(a, o));
+      int E;
+      (void)frexp(a, &E);                      // a = f * 2^E, f in [0.5, 1)
+      int xs = a > 0.0 ? E - 3 : 0;
+      xs = xs < -127 ? -127 : (xs > 127 ? 127 : xs);
+      const uint32_t code = f64_to_e2m1(v * ldexp(1.0, -xs));
+      const uint32_t odd = __shfl_xor(code, 1);
+      if (pi >= 0 && (c & 1) == 0) u.kic.row(pi, blk)[c / 2] = (uint8_t)(code | (odd << 4));
+      if (pi >= 0 && (c & 31) == 0)
+        ((uint8_t*)u.kic.scale)[((int64_t)pi * kPage + (blk & 63)) * (kDI / 32) + c / 32] =
+            (uint8_t)(xs + 127);
+    } else if (pi >= 0) {
+      ((u16*)u.kic.row(pi, blk))[c] = f64_to_bf16(v);
+    }
   }
   __syncthreads();
   if (c == 0) {

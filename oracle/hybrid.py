@@ -337,11 +337,13 @@ def csa_query(t, q_bits, qi_bits, w, k_bits, v_bits, kc: Cache, vc: Cache, kic: 
     kc/vc/kic: compressed caches (at least the visible blocks).
     Returns dict(o, lse, idx, scores) where idx are the selected blocks
     (ascending, -1 padded) and scores the indexer scores of all visible blocks
-    (float64)."""
+    (float64).  Over fp4 indexer keys the scores are computed in FP4
+    (indexer_scores_fp4)."""
     d = q_bits.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     nv = n_visible(t, m, n_win)
-    sc = indexer_scores(qi_bits, w, kic.values[:nv])
+    score = indexer_scores_fp4 if kic.dtype == "fp4" else indexer_scores
+    sc = score(qi_bits, w, kic.values[:nv])
     idx = topk_blocks(sc, topk)
     sel = idx[idx >= 0]
     Kw, Vw = _window_rows(t, n_win, k_bits, v_bits)

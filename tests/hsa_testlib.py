@@ -104,7 +104,7 @@ def scale_of(d=128):
 # ----------------------------------------------------------------------------- decode state
 
 def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, index_fp8=False,
-                kmix=False, tail_cap=None, stash=False, rope=0.0):
+                kmix=False, tail_cap=None, stash=False, rope=0.0, index_fp4=False):
     """Caches holding tokens 0..L_r-1 of every request, rings/tails up to L_r-1,
     and the per-request token/query streams for `steps` decode steps.  Rings
     hold ring_cap tokens (default n_win; a draft of n tokens needs n_win + n - 1)
@@ -112,6 +112,7 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     m + n - 1).  stash: fp8 K / V caches carry the stash that appending to them
     needs (hsa_kv_compress fills it for the last page).
     index_fp8: the CSA indexer keys are stored fp8 (e4m3fn, one scale per page).
+    index_fp4: the CSA indexer keys are stored MX FP4 (e2m1, a scale per 32 channels).
     kmix: the K cache holds mixed entries (bf16 RoPE channels), V is fp8.
     rope > 0: the history's keys are turned at their positions (hsa_rope)
     before they are compressed and put in the ring, as a RoPE layer holds them."""
@@ -124,9 +125,9 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     max_entries = int(max(Ls)) // m + steps // m + 2
     ppr = -(-max_entries // 64)
     perm = (torch.from_numpy(gen.page_permutation(w, layer, B * ppr)) if shuffle else None)
-    def cache(dim, f8, mixed=False, st_=False):
+    def cache(dim, f8, mixed=False, st_=False, f4=False):
         return L.PagedCache.allocate(B, max_entries, dim, fp8=f8, page_order=perm, mixed=mixed,
-                                     stash=st_)
+                                     stash=st_, fp4=f4)
     st = {"reqs": reqs, "z": z, "m": m}
     st["alpha_k"] = L.pooling_weights(torch.from_numpy(z["zk"]).cuda())
     st["alpha_v"] = L.pooling_weights(torch.from_numpy(z["zv"]).cuda())
@@ -137,7 +138,7 @@ def build_state(w, layer, Ls, steps=1, fp8=False, shuffle=True, ring_cap=None, i
     ring_v = torch.zeros_like(ring_k)
     if layer == "csa":
         st["alpha_i"] = L.pooling_weights(torch.from_numpy(z["zi"]).cuda())
-        st["kic"] = cache(64, index_fp8)
+        st["kic"] = cache(64, index_fp8, f4=index_fp4)
         tcap = m if tail_cap is None else tail_cap
         tail = torch.zeros((B, tcap, 64), dtype=torch.bfloat16, device="cuda")
     for r, d in enumerate(reqs):

@@ -206,6 +206,14 @@ def test_draft_needs_a_tail_for_rewinds():
     assert call(_csa_layer(tail_cap=4), 4) == -1
     assert b"tail_i" in lib.hsa_last_error()
     assert call(_csa_layer(tail_cap=4 + 3), 4) == -3
+    # fp4 indexer keys: single-token steps only (the grouped draft scan has no fp4 path)
+    Lr = _csa_layer(tail_cap=4 + 3)
+    Lr.kic = _paged(dim=64, dtype=L.FP4, ppr=1 << 14)
+    assert call(Lr, 4) == -2
+    assert b"fp4" in lib.hsa_last_error()
+    # fp8 indexer keys stay outside the decode step
+    Lr.kic = _paged(dim=64, dtype=L.FP8, ppr=1 << 14)
+    assert call(Lr, 4) == -2
 
 
 def _rnd(b):

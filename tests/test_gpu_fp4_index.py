@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import hybrid as orc
+from oracle import numerics as nx
 from synth import configs, gen
 
 import hsa_testlib as T
@@ -96,3 +97,55 @@ def test_decode_indexer_fp4_keys(Ls):
         T.check_topk(idx[r], s, k, where=f"req {r} t {t}")
         sel = idx[r][idx[r] >= 0]
         assert np.allclose(score[r][: len(sel)], s[sel], rtol=1e-4, atol=1e-3), r
+
+
+def test_decode_steps_into_fp4_indexer_keys():
+    """hsa_decode_step over an fp4 indexer-key cache: every step's selection
+    (scored in FP4) and output against the oracle recomputed from the full
+    history, and the MX entries the steps append (codes and scale bytes) bit
+    for bit after the steps.  Rows under and over 16,384 blocks (the two
+    selection paths); blocks complete during the steps."""
+    w = configs.shrink(configs.RAGGED_SERVING, H=64, k_csa=64)
+    Ls = [5, 126, 1000, 1021, 3000, 70001]
+    S = 9
+    m = w.m_csa
+    st = T.build_state(w, "csa", Ls, steps=S, index_fp4=True)
+    lay = T.layer_of(w, "csa", st)
+    max_pos = max(Ls) + S
+    z = st["z"]
+    for s in range(S):
+        pos = torch.tensor([x + s for x in Ls], dtype=torch.int64, device="cuda")
+        reqs = st["reqs"]
+        Q = T.dev_bf16(np.stack([d["q"][s] for d in reqs]))
+        kn = T.dev_bf16(np.stack([d["k"][Ls[r] + s] for r, d in enumerate(reqs)]))
+        vn = T.dev_bf16(np.stack([d["v"][Ls[r] + s] for r, d in enumerate(reqs)]))
+        O, lse, idx = L.decode_step(
+            lay, pos, max_pos, Q, kn, vn, with_lse=True, with_idx=True,
+            qI=T.dev_bf16(np.stack([d["qi"][s] for d in reqs])),
+            kI_new=T.dev_bf16(np.stack([d["ki"][Ls[r] + s] for r, d in enumerate(reqs)])),
+            w=torch.from_numpy(np.stack([d["w"][s] for d in reqs])).cuda())
+        L.check_device_error()
+        O, lse, idx = T.to_f64(O), lse.cpu().numpy(), idx.cpu().numpy()
+        for r, d in enumerate(reqs):
+            t = Ls[r] + s
+            kc = orc.compress(d["k"][:t], z["zk"], m)
+            vc = orc.compress(d["v"][:t], z["zv"], m)
+            kic = orc.compress(d["ki"][:t], z["zi"], m, "fp4")
+            ref = orc.csa_query(t, d["q"][s], d["qi"][s], d["w"][s], d["k"][: t + 1],
+                                d["v"][: t + 1], kc, vc, kic, m, w.n_win, w.k_csa)
+            T.check_topk(idx[r], ref["scores"], w.k_csa, where=f"req {r} t {t}")
+            sel = idx[r][idx[r] >= 0]
+            if not np.array_equal(sel, ref["idx"][ref["idx"] >= 0]):
+                s0 = orc.window_start(t, w.n_win)
+                K = np.concatenate([nx.bf16_value(d["k"][s0:t + 1]), kc.values[sel]])
+                V = np.concatenate([nx.bf16_value(d["v"][s0:t + 1]), vc.values[sel]])
+                o, l = orc.attend(nx.bf16_value(d["q"][s]), K, V, T.scale_of())
+                ref = {"o": o, "lse": l}
+            assert np.max(np.abs(O[r] - ref["o"])) <= T.OUT_TOL, (r, t)
+            assert np.max(np.abs(lse[r] - ref["lse"])) <= T.LSE_TOL, (r, t)
+    for r, d in enumerate(st["reqs"]):
+        n = (Ls[r] + S) // m
+        assert int(st["kic"].n_entries[r]) == n
+        ref = orc.compress(d["ki"][: Ls[r] + S], z["zi"], m, "fp4")
+        assert np.array_equal(T.cache_bits(st["kic"], r, n), ref.bits), r
+        assert np.array_equal(st["kic"].logical_scales(r, n).cpu().numpy(), ref.scales), r
