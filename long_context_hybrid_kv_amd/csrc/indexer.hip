@@ -1359,18 +1359,20 @@ __global__ __launch_bounds__(NT) void idx_topk_kernel(int k, IdxWs ws, int32_t* 
   __threadfence_block();
   __syncthreads();
 
-  // ---- emit ascending block ids: each thread owns 8 consecutive bitmap words
-  // per round (loaded together); a block scan of their popcounts gives its
-  // output offset
+  // ---- emit ascending block ids: each thread owns wpt consecutive bitmap
+  // words per round (loaded together; wpt = 8 on long rows, fewer on short
+  // ones so that a dense bitmap's bits spread over more threads); a block scan
+  // of their popcounts gives its output offset
   int32_t* irow = idx + (int64_t)(out_row0 + qrow) * k;
   float* srow_out = score ? score + (int64_t)(out_row0 + qrow) * k : nullptr;
   uint32_t total = 0;
-  for (int64_t r0 = 0; r0 < W; r0 += (int64_t)NT * 8) {
-    const int64_t w0 = r0 + (int64_t)tid * 8;
+  const int wpt = W >= (int64_t)NT * 8 ? 8 : (int)((W + NT - 1) / NT);
+  for (int64_t r0 = 0; r0 < W; r0 += (int64_t)NT * wpt) {
+    const int64_t w0 = r0 + (int64_t)tid * wpt;
     uint32_t wd[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      wd[i] = w0 + i < W ? (bm_in_lds ? bm_l[w0 + i] : ld_agent(bm + w0 + i)) : 0u;
+      wd[i] = i < wpt && w0 + i < W ? (bm_in_lds ? bm_l[w0 + i] : ld_agent(bm + w0 + i)) : 0u;
     uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) cnt += __popc(wd[i]);
