@@ -9,6 +9,9 @@
   bit, and the outputs match the oracle attending with turned queries.  Both
   routes of the CSA upkeep are taken: its own launch (short rows) and the
   candidate selection launch (a row over 16,384 blocks).
+* The same at full size: the 1M-token Pro decode (4 requests, fp8 caches,
+  128 heads, top-1024) over a turned history, one step that completes a
+  block in both layers, every request checked.
 * hsa_decode_draft turns every draft token at its own position.
 * A 4K prefill that turns its K rows and queries with hsa_rope, then
   compresses, selects and attends, matches the oracle's prefill over turned
@@ -87,6 +90,22 @@ def _oracle(w, layer, d, t, s, kdt, vdt):
 
 def _check_query(w, layer, d, t, s, O, lse, idx, kdt, vdt, where):
     ref, (kc, vc) = _oracle(w, layer, d, t, s, kdt, vdt)
+    _compare(w, layer, d, t, s, ref, kc, vc, O, lse, idx, where)
+
+
+def _check_output(w, layer, d, t, s, c, O, lse, idx, where):
+    """As _check_query, over caches c the caller has compressed."""
+    if layer == "csa":
+        ref = orc.csa_query(t, d["q"][s], d["qi"][s], d["w"][s], d["k"][: t + 1],
+                            d["v"][: t + 1], c["kc"], c["vc"], c["kic"], w.m(layer), w.n_win,
+                            w.k_csa)
+    else:
+        ref = orc.hca_query(t, d["q"][s], d["k"][: t + 1], d["v"][: t + 1], c["kc"], c["vc"],
+                            w.m(layer), w.n_win)
+    _compare(w, layer, d, t, s, ref, c["kc"], c["vc"], O, lse, idx, where)
+
+
+def _compare(w, layer, d, t, s, ref, kc, vc, O, lse, idx, where):
     if layer == "csa":
         T.check_topk(idx, ref["scores"], w.k_csa, where=where)
         sel = idx[idx >= 0]
@@ -167,6 +186,54 @@ def test_decode_steps_with_rope(layer, fmt, Ls):
             _check_query(w, layer, d, p[r], s, Ob[r], lb[r], None if ib is None else ib[r],
                          kdt, vdt, f"step {s} req {r}")
         _check_state(w, layer, st, rot, p, kdt, vdt, f"step {s}")
+
+
+@pytest.fixture(scope="module", params=["csa", "hca"])
+def pro_1m_rope(request):
+    """The benchmark's Pro decode at full size (4 requests x 1M tokens, fp8
+    caches with their stashes, 128 heads, CSA top-1024) with partial RoPE: one
+    step at position 2^20 - 1, which completes a block in both layers (the
+    upkeep pools turned keys and re-encodes the open fp8 page)."""
+    layer = request.param
+    w = configs.PRO_DECODE_1M
+    p = [w.L - 1] * w.B
+    st = T.build_state(w, layer, p, steps=1, fp8=True, stash=True, shuffle=False, rope=THETA)
+    lay = T.layer_of(w, layer, st, rope=THETA)
+    print(f"rope pro decode {layer}: {w.B} x {w.L - 1}", flush=True)
+    O, lse, idx = L.decode_step(lay, torch.tensor(p, dtype=torch.int64, device="cuda"), max(p),
+                                with_lse=True, with_idx=(layer == "csa"),
+                                **_inputs(layer, st["reqs"], p, 0))
+    L.check_device_error()
+    yield dict(w=w, layer=layer, st=st, p=p, O=T.to_f64(O), lse=lse.cpu().numpy(),
+               idx=None if idx is None else idx.cpu().numpy())
+
+
+@pytest.mark.parametrize("r", range(4))
+def test_pro_decode_1m_with_rope_full(pro_1m_rope, r):
+    """One request of the full-size step: its output against the oracle over
+    its turned history, and its ring rows and caches bit for bit (the oracle
+    compresses each cache once, for both checks)."""
+    f = pro_1m_rope
+    w, layer, st, t = f["w"], f["layer"], f["st"], f["p"][r]
+    d = _turned([st["reqs"][r]], [t])[0]
+    m = w.m(layer)
+    c = {"kc": orc.compress(d["k"][:t + 1], st["z"]["zk"], m, "fp8"),
+         "vc": orc.compress(d["v"][:t + 1], st["z"]["zv"], m, "fp8")}
+    if layer == "csa":
+        c["kic"] = orc.compress(d["ki"][:t + 1], st["z"]["zi"], m)
+    _check_output(w, layer, d, t, 0, c, f["O"][r], f["lse"][r],
+                  None if f["idx"] is None else f["idx"][r], f"req {r}")
+    cap = st["ring_k"].data.shape[1]
+    ring = _bits(st["ring_k"].data)
+    for q in range(t - cap + 1, t + 1):
+        assert np.array_equal(ring[r, q % cap], d["k"][q]), (r, q, "ring")
+    for name, ref in c.items():
+        assert int(st[name].n_entries[r]) == (t + 1) // m, (r, name)
+        assert np.array_equal(T.cache_bits(st[name], r, len(ref)), ref.bits), (r, name)
+        if ref.scales is not None:
+            got = st[name].logical_scales(r, len(ref)).cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.scales.view(np.uint32)), \
+                (r, name, "scale")
 
 
 @pytest.mark.parametrize("layer,n_tok", [("csa", 4), ("hca", 3)])
