@@ -15,7 +15,7 @@
 * hsa_decode_draft turns every draft token at its own position.
 * A 4K prefill that turns its K rows and queries with hsa_rope, then
   compresses, selects and attends, matches the oracle's prefill over turned
-  inputs."""
+  inputs; so does the 128K prefill, on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -318,3 +318,48 @@ def test_prefill_with_rope(layer):
                                 oc["vc"], m, w.n_win)
         assert np.max(np.abs(Ob[t] - ref["o"])) <= T.OUT_TOL, f"row {t}"
         assert np.max(np.abs(lb[t] - ref["lse"])) <= T.LSE_TOL, f"row {t} lse"
+
+
+PREFILL_ROWS = [0, 1, 127, 128, 129, 4095, 4096, 65535, 65536, 100000, 131070, 131071]
+
+
+@pytest.mark.parametrize("layer", ["csa", "hca"])
+def test_prefill_128k_with_rope_sampled(layer):
+    """The 128K prefill with RoPE at full size: hsa_rope over all K rows (bit
+    for bit against the oracle) and all queries (bit for bit on the sampled
+    rows), the caches compressed from the turned keys (bit for bit), then the
+    selection and attention; sampled rows against the oracle one by one."""
+    w = configs.HYBRID_PREFILL_128K
+    inp = gen.prefill_layer(w, layer)
+    Tn, m = w.T, w.m(layer)
+    print(f"rope prefill 128k {layer}", flush=True)
+    kr = L.rope(T.dev_bf16(inp["k"]), THETA)
+    Qr = L.rope(T.dev_bf16(inp["q"]), THETA)
+    kt = orc.rope(inp["k"], np.arange(Tn), THETA)
+    assert np.array_equal(_bits(kr), kt)
+    rows = sorted(set(PREFILL_ROWS) | set(np.random.default_rng(5).integers(0, Tn, 21).tolist()))
+    qt = orc.rope(inp["q"][rows], np.array(rows)[:, None], THETA)
+    assert np.array_equal(_bits(Qr[rows]), qt)
+    gc = T.compress_layer(dict(inp, k=_bits(kr)), layer, m)
+    oc = orc.layer_caches(dict(inp, k=kt), layer, m)
+    for name in oc:
+        assert np.array_equal(T.cache_bits(gc[name], 0, len(oc[name])), oc[name].bits), name
+    q = L.Queries.span(Tn)
+    tk, tv = T.tokens(_bits(kr)), T.tokens(inp["v"])
+    if layer == "csa":
+        idx, _ = L.indexer_topk(q, T.dev_bf16(inp["qi"]), torch.from_numpy(inp["w"]).cuda(),
+                                gc["kic"], m, w.n_win, w.k_csa)
+        O, lse = L.csa_attn(q, Qr, tk, tv, w.n_win, gc["kc"], gc["vc"], m, idx, w.k_csa,
+                            with_lse=True, out_fp32=True)
+        idx = idx.cpu().numpy()
+    else:
+        O, lse = L.hca_attn(q, Qr, tk, tv, w.n_win, gc["kc"], gc["vc"], m, with_lse=True,
+                            out_fp32=True)
+    L.check_device_error()
+    Ob, lb = T.to_f64(O[rows]), lse[rows].cpu().numpy()
+    d = {"q": qt, "k": kt, "v": inp["v"]}
+    if layer == "csa":
+        d.update(qi=inp["qi"][rows], w=inp["w"][rows])
+    for j, t in enumerate(rows):
+        _check_output(w, layer, d, t, j, oc, Ob[j], lb[j], idx[t] if layer == "csa" else None,
+                      f"{layer} row {t}")
