@@ -207,15 +207,32 @@ __device__ __forceinline__ float score_get(const void* row, int64_t i, int64_t l
   else return i < lim ? ((const float*)row)[i] : 0.f;
 }
 
+// DPP lane move of x within the wave: ctrl selects the source lane (row
+// shift or row broadcast), row_mask the 16-lane rows written; lanes with no
+// source or in rows not written read 0
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (every lane active): sums
+// within each 16-lane row by row shifts of 1, 2, 4 and 8 lanes, then the
+// rows' totals carried on by the row broadcasts of lane 15 (into rows 1 and
+// 3) and lane 31 (into rows 2 and 3); no LDS round trip
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
+  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
+  return x;
+}
+
 // exclusive prefix sum over a 256-thread block; returns the block total in *total
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wv] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
@@ -274,12 +291,7 @@ __device__ __forceinline__ void block_and_or(uint64_t* a, uint64_t* o, uint64_t*
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh[wv] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
@@ -378,12 +390,7 @@ __device__ __forceinline__ void write_candidates(const uint32_t* lhist, const fl
     cnt += c[j];
   }
   const uint32_t mine = (nb << 16) | cnt;
-  uint32_t inc = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
+  const uint32_t inc = wave_incl_scan(mine);
   const uint32_t wtot = __shfl(inc, 63);
   uint32_t wb = 0;
   if (wtot != 0) {   // uniform in the wave
@@ -1666,10 +1673,37 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
         }
       };
       const int my_cnt = lg < nl ? s_cnt[lg] : 0;
+      {
+        // the candidates read up front: bitmap marks, then one LDS atomic per
+        // wave reserves the threshold-bin slots of all of them (one
+        // reservation per candidate is a dependent LDS round trip each)
+        bool cin[SPEC];
+        uint64_t cmk[SPEC];
+        uint32_t nin = 0;
 #pragma unroll
-      for (int u = 0; u < SPEC; ++u) {
-        const int j = sub * SPEC + u;
-        classify(xs[u], j < my_cnt && j < cov);
+        for (int u = 0; u < SPEC; ++u) {
+          const int j = sub * SPEC + u;
+          const int bin = j < my_cnt && j < cov ? (int)(xs[u] >> 52) : -1;
+          if (bin > thr) {
+            const uint32_t blk = ~(uint32_t)xs[u];
+            atomicOr(&bm[blk >> 5], 1u << (blk & 31));
+          }
+          cin[u] = bin == thr;
+          cmk[u] = __ballot(cin[u]);
+          nin += (uint32_t)__popcll(cmk[u]);
+        }
+        if (nin) {   // uniform in the wave
+          uint32_t cb = 0;
+          if (lane == 0) cb = atomicAdd(&s_ntc, nin);
+          cb = __shfl(cb, 0);
+          const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+          for (int u = 0; u < SPEC; ++u) {
+            const uint32_t p = cb + (uint32_t)__popcll(cmk[u] & below);
+            if (cin[u] && p < (uint32_t)kThrCandMax) tc[p] = xs[u];
+            cb += (uint32_t)__popcll(cmk[u]);
+          }
+        }
       }
       if (s_ovf) {   // uniform: some list holds more than was read up front
         for (int base = cov; base < kCandCap; base += tpl * SPEC) {
