@@ -766,18 +766,14 @@ __device__ __forceinline__ void merge_one(int qh, bool on, int H, int n_splits,
     wls[s] = ml.y;
     mloc = fmaxf(mloc, ml.x);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-  const float M = mloc;
+  const float M = wave_max_f32(mloc);
   float lloc = 0.f;
   for (int s = lane; s < ns; s += 64) {
     const float wl = exp2f(wgt[s] - M) * wls[s];
     wgt[s] = wl;
     lloc += wl;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
-  const float L = lloc;
+  const float L = wave_sum_f32(lloc);
   __syncthreads();   // wgt[] written by other lanes
   if (!on) return;
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));

@@ -223,6 +223,61 @@ __device__ __forceinline__ int64_t readfirstlane64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// ---- wave-wide scans and reductions by DPP lane moves (no LDS round trip;
+// every lane of the wave active).  A step moves x from the lane CTRL names
+// (row shift or row broadcast) into the 16-lane rows ROW_MASK selects; lanes
+// with no source lane, and rows not selected, receive the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// inclusive scan of an associative op over the 64 lanes, on 32-bit words:
+// within each row by shifts of 1, 2, 4 and 8 lanes, then the rows' results
+// carried on by the broadcasts of lane 15 (into rows 1 and 3) and lane 31
+// (into rows 2 and 3)
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_bits(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_move<0x111, 0xf>(x, id));   // row_shr:1
+  x = op(x, dpp_move<0x112, 0xf>(x, id));   // row_shr:2
+  x = op(x, dpp_move<0x114, 0xf>(x, id));   // row_shr:4
+  x = op(x, dpp_move<0x118, 0xf>(x, id));   // row_shr:8
+  x = op(x, dpp_move<0x142, 0xa>(x, id));   // row_bcast:15
+  x = op(x, dpp_move<0x143, 0xc>(x, id));   // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  return wave_incl_bits(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// the value of lane `l` (l uniform) in every lane
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+
+// reductions over the wave, the result in every lane
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) { return lane_value(wave_incl_sum(x), 63); }
+__device__ __forceinline__ int wave_max_i32(int x) {
+  const uint32_t r = wave_incl_bits((uint32_t)x, 0x80000000u,
+                                    [](uint32_t a, uint32_t b) { return (uint32_t)max((int)a, (int)b); });
+  return (int)lane_value(r, 63);
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  const uint32_t r = wave_incl_bits(__float_as_uint(x), __float_as_uint(-INFINITY), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float(lane_value(r, 63));
+}
+// (a float sum in the scan's order: lane 0 first within each row, then the
+// rows in order -- fixed, independent of what the lanes hold)
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  const uint32_t r = wave_incl_bits(__float_as_uint(x), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float(lane_value(r, 63));
+}
+
 // x / d and x % d for x >= 0, d >= 1.  A 64-bit division is a long scalar
 // sequence that every wave of a workgroup repeats; a power-of-two divisor (the
 // compression rates) is a shift, and operands below 2^32 take the 32-bit

@@ -207,32 +207,10 @@ __device__ __forceinline__ float score_get(const void* row, int64_t i, int64_t l
   else return i < lim ? ((const float*)row)[i] : 0.f;
 }
 
-// DPP lane move of x within the wave: ctrl selects the source lane (row
-// shift or row broadcast), row_mask the 16-lane rows written; lanes with no
-// source or in rows not written read 0
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
-}
-
-// inclusive prefix sum over the 64 lanes of a wave (every lane active): sums
-// within each 16-lane row by row shifts of 1, 2, 4 and 8 lanes, then the
-// rows' totals carried on by the row broadcasts of lane 15 (into rows 1 and
-// 3) and lane 31 (into rows 2 and 3); no LDS round trip
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += dpp_or_zero<0x111, 0xf>(x);   // row_shr:1
-  x += dpp_or_zero<0x112, 0xf>(x);   // row_shr:2
-  x += dpp_or_zero<0x114, 0xf>(x);   // row_shr:4
-  x += dpp_or_zero<0x118, 0xf>(x);   // row_shr:8
-  x += dpp_or_zero<0x142, 0xa>(x);   // row_bcast:15
-  x += dpp_or_zero<0x143, 0xc>(x);   // row_bcast:31
-  return x;
-}
-
 // exclusive prefix sum over a 256-thread block; returns the block total in *total
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) sh[wv] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
@@ -291,7 +269,7 @@ __device__ __forceinline__ void block_and_or(uint64_t* a, uint64_t* o, uint64_t*
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t* total, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
+  const uint32_t x = wave_incl_sum(v);
   if (lane == 63) sh[wv] = x;
   __syncthreads();
   uint32_t off = 0, tot = 0;
@@ -390,12 +368,12 @@ __device__ __forceinline__ void write_candidates(const uint32_t* lhist, const fl
     cnt += c[j];
   }
   const uint32_t mine = (nb << 16) | cnt;
-  const uint32_t inc = wave_incl_scan(mine);
-  const uint32_t wtot = __shfl(inc, 63);
+  const uint32_t inc = wave_incl_sum(mine);
+  const uint32_t wtot = lane_value(inc, 63);
   uint32_t wb = 0;
   if (wtot != 0) {   // uniform in the wave
     if (lane == 0) wb = atomicAdd(&s_n, wtot);
-    wb = __shfl(wb, 0);
+    wb = lane_value(wb, 0);
   }
   const uint32_t base = wb + inc - mine;
   uint32_t pos = base & 0xFFFFu, ob = base >> 16;
@@ -1605,13 +1583,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     {   // the live lists' flags, largest cut and sum: one atomic per wave
       const bool live = tid < nl && tid < n_wg;
       const bool bad = live && (cnt > kCandCap || ntop > kTopBins), ovf = live && cnt > cov;
-      int mbc = live ? bcw : -1;
-      uint32_t sum = live ? (uint32_t)cnt : 0u;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        mbc = max(mbc, __shfl_xor(mbc, o));
-        sum += __shfl_xor(sum, o);
-      }
+      const int mbc = wave_max_i32(live ? bcw : -1);
+      const uint32_t sum = wave_sum_u32(live ? (uint32_t)cnt : 0u);
       const uint64_t bb = __ballot(bad), bo = __ballot(ovf);
       if (lane == 0 && tid < nl) {
         if (bb) atomicOr(&s_bad, 1);
@@ -1667,7 +1640,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
           const int leader = __ffsll((unsigned long long)cm) - 1;
           uint32_t cb = 0;
           if (lane == leader) cb = atomicAdd(&s_ntc, (uint32_t)__popcll(cm));
-          cb = __shfl(cb, leader);
+          cb = lane_value(cb, leader);
           const uint32_t p = cb + __popcll(cm & ((1ull << lane) - 1));
           if (c && p < (uint32_t)kThrCandMax) tc[p] = x;
         }
@@ -1695,7 +1668,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
         if (nin) {   // uniform in the wave
           uint32_t cb = 0;
           if (lane == 0) cb = atomicAdd(&s_ntc, nin);
-          cb = __shfl(cb, 0);
+          cb = lane_value(cb, 0);
           const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
           for (int u = 0; u < SPEC; ++u) {
