@@ -246,6 +246,32 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                         const int32_t* idx, int32_t k, float scale, void* O, int32_t o_dtype,
                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* A CSA layer's prefill in one call (wiki §5.3: indexer, top-k, then the
+ * main attention over the selection and the window, as hsa_indexer_topk
+ * followed by hsa_csa_attn).  The span is cut into stages of stage_q
+ * consecutive queries (0: 8192); the attention of stage p runs on a stream of
+ * the library's own (one per device, default priority, created on first use)
+ * while the indexer and top-k of stage p + 1 run on `stream`, with events
+ * ordering each stage's attention after its selection and `stream` after the
+ * last attention.  Results are bit-identical to the two calls on the same
+ * span.  q must be a span.  Arguments as hsa_indexer_topk (qI, w, H_I, d_I,
+ * kIc, idx: required here, [n][k]) and hsa_csa_attn (Q .. lse); the indexer
+ * keys are bf16, fp8 or fp4 as there, the scores fp32.  Workspace:
+ * hsa_csa_prefill_workspace_bytes.  Host calls are serialised by a lock
+ * (the side stream is shared); work already enqueued on `stream` before the
+ * call is ordered before all of it, work enqueued after the call after all
+ * of it.  Inside a stream capture the side stream joins the capture through
+ * the same events. */
+size_t hsa_csa_prefill_workspace_bytes(const hsa_queries* q, int32_t H, int32_t m,
+                                       int32_t n_win, int32_t k);
+hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w,
+                           int32_t H_I, int32_t d_I, const hsa_paged* kIc, const void* Q,
+                           int32_t H, int32_t d, const hsa_tokens* win_k,
+                           const hsa_tokens* win_v, int32_t n_win, const hsa_paged* kc,
+                           const hsa_paged* vc, int32_t m, int32_t k, float scale,
+                           int32_t* idx, void* O, int32_t o_dtype, float* lse,
+                           int32_t stage_q, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* HCA attention (wiki §5.2 + §5.4): as hsa_csa_attn with every visible
  * compressed entry (b < n_vis(t)) instead of a selection. */
 size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win,

@@ -85,6 +85,14 @@ _SIGS = {
                                C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_void_p,
                                C.c_int32, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]),
+    "hsa_csa_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
+                                                     C.c_int32, C.c_int32]),
+    "hsa_csa_prefill": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_void_p, C.c_int32,
+                                  C.c_int32, C.POINTER(_Paged), C.c_void_p, C.c_int32, C.c_int32,
+                                  C.POINTER(_Tokens), C.POINTER(_Tokens), C.c_int32,
+                                  C.POINTER(_Paged), C.POINTER(_Paged), C.c_int32, C.c_int32,
+                                  C.c_float, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                  C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "hsa_hca_attn_workspace_bytes": (C.c_size_t, [C.POINTER(_Queries), C.c_int32, C.c_int32,
                                                   C.c_int32]),
     "hsa_hca_attn": (C.c_int, [C.POINTER(_Queries), C.c_void_p, C.c_int32, C.c_int32,
@@ -381,6 +389,28 @@ def csa_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: i
                               C.byref(kcc), C.byref(vcc), m, _ptr(idx), k, scale, _ptr(O),
                               FP32 if out_fp32 else BF16, _ptr(lse), ws, wsb, _stream()), "csa_attn")
     return O, lse
+
+
+def csa_prefill(q: Queries, qI: torch.Tensor, w: torch.Tensor, kIc: PagedCache, Q: torch.Tensor,
+                win_k: Tokens, win_v: Tokens, n_win: int, kc: PagedCache, vc: PagedCache, m: int,
+                k: int, scale: Optional[float] = None, with_lse: bool = False,
+                out_fp32: bool = False, stage_q: int = 0, ws_key="csa_prefill"):
+    """hsa_csa_prefill: a CSA layer's indexer, top-k and attention over a span.
+    Returns (idx, O, lse)."""
+    H, d = Q.shape[-2], Q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    qc, kic, wk, wv, kcc, vcc = q.c(), kIc.c(), win_k.c(), win_v.c(), kc.c(), vc.c()
+    idx = torch.empty((q.n, k), dtype=torch.int32, device=Q.device)
+    O = torch.empty(Q.shape, dtype=torch.float32 if out_fp32 else torch.bfloat16, device=Q.device)
+    lse = torch.empty((q.n, H), dtype=torch.float32, device=Q.device) if with_lse else None
+    nb = lib().hsa_csa_prefill_workspace_bytes(C.byref(qc), H, m, n_win, k)
+    ws, wsb = _ws_args(_WS.get(ws_key, nb, Q.device))
+    _check(lib().hsa_csa_prefill(C.byref(qc), _ptr(qI), _ptr(w), qI.shape[-2], qI.shape[-1],
+                                 C.byref(kic), _ptr(Q), H, d, C.byref(wk), C.byref(wv), n_win,
+                                 C.byref(kcc), C.byref(vcc), m, k, scale, _ptr(idx), _ptr(O),
+                                 FP32 if out_fp32 else BF16, _ptr(lse), stage_q, ws, wsb,
+                                 _stream()), "csa_prefill")
+    return idx, O, lse
 
 
 def hca_attn(q: Queries, Q: torch.Tensor, win_k: Tokens, win_v: Tokens, n_win: int,

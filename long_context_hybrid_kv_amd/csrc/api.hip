@@ -379,6 +379,95 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
                     "csa_attn");
 }
 
+// ---------------------------------------------------------------- CSA prefill, pipelined
+
+// The side stream the attention stages run on and the events that order them,
+// one set per device, created on first use and kept until the process ends.
+struct PipeState {
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev;
+};
+static std::mutex g_pipe_mu;
+static PipeState g_pipe[64];
+constexpr int kStageQueries = 8192;
+
+size_t hsa_csa_prefill_workspace_bytes(const hsa_queries* q, int32_t H, int32_t m, int32_t n_win,
+                                       int32_t k) {
+  if (!q || q->pos || H < 16) return 0;
+  // every stage's selection fits the full span's layout (the score rows are
+  // as long as the longest row of the span, the passes as wide); span
+  // attention needs none
+  return hsa_indexer_topk_workspace_bytes(q, m, n_win, k) +
+         hsa_csa_attn_workspace_bytes(q, H, n_win, k);
+}
+
+hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
+                           int32_t d_I, const hsa_paged* kIc, const void* Q, int32_t H, int32_t d,
+                           const hsa_tokens* win_k, const hsa_tokens* win_v, int32_t n_win,
+                           const hsa_paged* kc, const hsa_paged* vc, int32_t m, int32_t k,
+                           float scale, int32_t* idx, void* O, int32_t o_dtype, float* lse,
+                           int32_t stage_q, void* ws, size_t ws_bytes, hipStream_t stream) {
+  hsa_status s;
+  REQ(q, "csa_prefill: null queries");
+  REQ(!q->pos && !q->req, "csa_prefill: queries must be a span");
+  REQ(stage_q >= 0, "csa_prefill: negative stage size");
+  REQ(o_dtype == HSA_BF16 || o_dtype == HSA_FP32, "csa_prefill: o_dtype must be bf16 or fp32");
+  if ((s = check_paged(kIc, "kIc", kDI, true, false, true)) != HSA_OK) return s;
+  if ((s = check_attn_common(q, Q, H, d, win_k, win_v, n_win, kc, vc, m, scale, O)) != HSA_OK)
+    return s;
+  REQ(kIc->n_req == kc->n_req, "csa_prefill: kIc and kc differ in n_req");
+  REQ(qI && w && idx, "csa_prefill: null qI, w or idx");
+  SUP(H_I == kHI && d_I == kDI, "csa_prefill: H_I must be 4 and d_I 64");
+  REQ(k >= 1 && k <= (1 << 20), "csa_prefill: k out of range");
+  REQ((int64_t)kIc->pages_per_req * kPage >= nvis_host(q->max_pos, m, n_win),
+      "csa_prefill: indexer page table too short");
+  if ((s = check_ws(ws, ws_bytes, hsa_csa_prefill_workspace_bytes(q, H, m, n_win, k))) != HSA_OK)
+    return s;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(HSA_ERR_HIP, "csa_prefill: no current device");
+  const int S = stage_q > 0 ? stage_q : kStageQueries;
+  const int n_st = (int)((q->n + (int64_t)S - 1) / S);
+  std::lock_guard<std::mutex> lk(g_pipe_mu);
+  PipeState& P = g_pipe[dev];
+  if (!P.side) {
+    hipStream_t st = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_status(e, "csa_prefill: side stream");
+    P.side = st;
+  }
+  while ((int)P.ev.size() < n_st + 1) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_status(e, "csa_prefill: event");
+    P.ev.push_back(ev);
+  }
+  const size_t o_row = (size_t)H * kD * (o_dtype == HSA_FP32 ? 4 : 2);
+  hipError_t e = hipSuccess;
+  for (int p = 0; p < n_st && e == hipSuccess; ++p) {
+    const int64_t c0 = (int64_t)p * S;
+    const int nq = (int)(q->n - c0 < S ? q->n - c0 : S);
+    hsa_queries sub = *q;
+    sub.n = nq;
+    sub.span_pos0 = q->span_pos0 + c0;
+    sub.max_pos = sub.span_pos0 + nq - 1;
+    int32_t* idx_p = idx + c0 * k;
+    e = launch_indexer(sub, (const u16*)qI + c0 * kHI * kDI, w + c0 * kHI, *kIc, m, n_win, k,
+                       idx_p, nullptr, ws, ws_bytes, stream, nullptr, 1, false);
+    if (e == hipSuccess) e = hipEventRecord(P.ev[p], stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(P.side, P.ev[p], 0);
+    if (e == hipSuccess)
+      e = launch_attn(sub, (const u16*)Q + c0 * H * kD, H, *win_k, *win_v, n_win, *kc, *vc, m,
+                      idx_p, k, scale, (uint8_t*)O + c0 * o_row, o_dtype,
+                      lse ? lse + c0 * H : nullptr, nullptr, 0, P.side);
+  }
+  // `stream` waits for the side stream's last stage, also after a failed launch
+  hipError_t j = hipEventRecord(P.ev[n_st], P.side);
+  if (j == hipSuccess) j = hipStreamWaitEvent(stream, P.ev[n_st], 0);
+  if (e != hipSuccess) return hip_status(e, "csa_prefill");
+  return hip_status(j, "csa_prefill: join");
+}
+
 size_t hsa_hca_attn_workspace_bytes(const hsa_queries* q, int32_t H, int32_t n_win, int32_t m) {
   if (!q || q->n < 1 || H < 16 || n_win < 1 || m < 1 || q->max_pos < 0) return 0;
   return attn_ws_bytes(q->n, H, n_win + nvis_host(q->max_pos, m, n_win), is_span(q),

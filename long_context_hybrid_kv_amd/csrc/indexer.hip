@@ -6,8 +6,10 @@
 // tokens x 4 heads in prefill; one query's 4 heads and 12 zero rows in decode),
 // the B operand holds 16 compressed indexer keys, so each lane of the result
 // owns the 4 heads of one (query, block) pair and the head sum stays in-lane.
-// A B operand row is 16 contiguous bytes of a key, read straight from the
-// paged cache; prefill stages the A operand (queries) in LDS.  Over fp4 keys
+// bf16 keys load as whole 128-byte rows (8 keys per load instruction) into a
+// per-wave swizzled LDS tile and are read back in the MFMA B layout (fp8 keys
+// load as pieces and widen in registers); prefill also stages the A operand
+// (queries) in LDS.  Over fp4 keys
 // (OCP MX FP4) the indexer computes in FP4: each query head is quantized to
 // MX FP4 by the keys' own rule, and the 16x16x128 MX-scaled MFMA takes both
 // operands as e2m1 codes with their e8m0 block scales (every product exact,

@@ -303,3 +303,31 @@ def test_decode_rope_theta_rules_and_workspace():
         assert lib.hsa_decode_step(C.byref(Lr), 1, f, 1000, f, f, f, f, f, f, f, None, None, f,
                                    1 << 30, None) == -1
         assert b"rope_theta" in lib.hsa_last_error()
+
+
+def test_csa_prefill_validation():
+    """hsa_csa_prefill takes spans only and checks the indexer's and the
+    attention's arguments, its stage size and its workspace, on the host."""
+    lib = L.lib()
+    f = C.c_void_p(0x1000)
+    q = L._Queries(4, None, None, 0, 0, 3)
+    pc, ki, tk = _paged(), _paged(dim=64), _tokens()
+    nb = lib.hsa_csa_prefill_workspace_bytes(C.byref(q), 16, 4, 128, 16)
+    assert nb >= lib.hsa_indexer_topk_workspace_bytes(C.byref(q), 4, 128, 16) > 0
+    big = 1 << 30
+
+    def call(qq=q, hi=4, kic=ki, idx=f, ws_bytes=big, stage=0, H=16, o_dtype=0):
+        return lib.hsa_csa_prefill(C.byref(qq), f, f, hi, 64, C.byref(kic), f, H, 128,
+                                   C.byref(tk), C.byref(tk), 128, C.byref(pc), C.byref(pc), 4,
+                                   16, 0.1, idx, f, o_dtype, None, stage, f, ws_bytes, None)
+
+    pos = C.c_void_p(0x2000)
+    listed = L._Queries(4, None, pos, 0, 0, 3)
+    assert call(qq=listed) == -1 and b"span" in lib.hsa_last_error()
+    assert call(idx=None) == -1
+    assert call(hi=8) == -2
+    assert call(stage=-1) == -1
+    assert call(H=24) == -2
+    assert call(o_dtype=7) == -1
+    assert call(ws_bytes=16) == -3
+    assert call(kic=_paged(dim=128)) == -2
