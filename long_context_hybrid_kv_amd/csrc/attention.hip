@@ -51,6 +51,7 @@ struct AttnArgs {
   float* part_ml;        // [n][splits][H][2]: (max, sum)
   int n_splits, cps, n_hg, n_q;
   int xcd;               // 1: keep consecutive queries on one XCD (prefill)
+  int pt_lds;            // 1: CSA decode reads the request's page tables into LDS
   int* fault;
   // decode with the cache upkeep after the attention: the query's own token
   // (the newest window row) is read from row qi of knew / vnew instead of the
@@ -110,8 +111,11 @@ struct Prefetch {
   const int* p;       // LDS, or nullptr (prefill: look up directly)
   int lo;             // CSA: first idx position held; HCA: first page held
   int n;              // entries held (CSA: idx positions; HCA: pages, K at p[i], V at p[64 + i])
+  const int* pt;      // CSA decode: the request's page table rows in LDS (K, then V), or nullptr
+  int pt_k;           // K page-table entries held (V's follow them)
 };
 constexpr int kPrePages = 64;   // HCA: page ids held per cache
+constexpr int kPtLdsMax = 4096; // CSA decode: page-table entries per cache read into LDS
 
 // block id of compressed entry j of query qi (CSA: its top-k id), or -1
 __device__ __forceinline__ int64_t entry_block(const AttnArgs& a, const Prefetch& pf, int qi,
@@ -132,6 +136,12 @@ __device__ __forceinline__ int entry_page(const AttnArgs& a, const Paged& c, con
       atomicOr(a.fault, HSA_FAULT_PAGE);
       return -1;
     }
+  }
+  if (pf.pt) {   // (b < n_vis <= pages_per_req * 64: the entry is held)
+    const int p = pf.pt[(which ? pf.pt_k : 0) + (int)(b >> 6)];
+    if ((unsigned)p < (unsigned)c.n_pages) return p;
+    atomicOr(a.fault, HSA_FAULT_PAGE);
+    return -1;
   }
   return c.page_of(r, b, a.fault);
 }
@@ -381,9 +391,29 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       id_b = a.vc.page_table[(int64_t)r * a.vc.pages_per_req + lv];
     }
   }
+  // CSA decode (a.pt_lds: the request is the query's index, no load): the
+  // request's page-table rows of both caches are read with the ids, so the
+  // rows of the selected blocks resolve from LDS instead of through a page
+  // table read that waits for the ids (one round trip fewer).  Whole rounds
+  // past both rows are skipped (uniform); the rest read clamped addresses.
+  constexpr int PTT = NW >= 4 ? kPtLdsMax / NT : 1;
+  const bool pt_lds = NW >= 4 && pre_mode == 1 && a.pt_lds;
+  const int ppk = a.kc.pages_per_req, ppv = a.vc.pages_per_req;
+  const int pp_max = ppk > ppv ? ppk : ppv;
+  int ptk_r[PTT], ptv_r[PTT];
+  if (pt_lds) {
+#pragma unroll
+    for (int i = 0; i < PTT; ++i) {
+      if (i * NT < pp_max) {
+        const int j = tid + NT * i;
+        ptk_r[i] = a.kc.page_table[(int64_t)r * ppk + (j < ppk ? j : ppk - 1)];
+        ptv_r[i] = a.vc.page_table[(int64_t)r * ppv + (j < ppv ? j : ppv - 1)];
+      }
+    }
+  }
   const int64_t ne_k = a.kc.n_entries[r], ne_v = a.vc.n_entries[r];
   const int64_t p_raw = listed ? a.Q.pos[qi] : a.Q.span_pos0 + qi;
-  Prefetch pf{nullptr, 0, 0};
+  Prefetch pf{nullptr, 0, 0, nullptr, 0};
   if (pre_mode != 0) {
     if (tid < n_pre) {
       if (pre_mode == 1) {
@@ -396,7 +426,20 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
     if (pre_mode == 1)   // top-k ranges longer than the workgroup
       for (int i = tid + NT; i < n_pre; i += NT) spre[i] = a.idx[(int64_t)qi * a.k + pre_lo + i];
-    pf = Prefetch{spre, pre_lo, n_pre};
+    pf = Prefetch{spre, pre_lo, n_pre, nullptr, 0};
+    if (pt_lds) {
+      int* spt = spre + a.cps * 64 + a.n_win + 2 * kPrePages;
+#pragma unroll
+      for (int i = 0; i < PTT; ++i) {
+        if (i * NT < pp_max) {
+          const int j = tid + NT * i;
+          if (j < ppk) spt[j] = ptk_r[i];
+          if (j < ppv) spt[ppk + j] = ptv_r[i];
+        }
+      }
+      pf.pt = spt;
+      pf.pt_k = ppk;
+    }
   }
   if (!a.xcd) __syncthreads();
   int64_t t = p_raw;
@@ -1192,6 +1235,10 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   a.n_hg = p.n_hg;
   a.n_q = q.n;
   a.fault = fault_word();
+  // CSA decode of single-token queries (request = query index): the page
+  // tables go to LDS when both rows are short enough
+  a.pt_lds = (!span && k > 0 && q.req == nullptr && p.nw >= 4 &&
+              kc.pages_per_req <= kPtLdsMax && vc.pages_per_req <= kPtLdsMax) ? 1 : 0;
   a.knew = a.vnew = nullptr;
   a.ring_rows = INT64_MAX;
   // the decode upkeep (upd): after the attention, in the merge launch, when
@@ -1234,7 +1281,8 @@ hipError_t launch_attn(const hsa_queries& q, const void* Q, int H, const hsa_tok
   // prefetched top-k ids (a split's entries plus one window) or page ids
   const size_t row_bytes = f8 ? sizeof(int) : sizeof(const uint8_t*);
   const unsigned pre = (unsigned)(2 * p.cps * 64 * row_bytes) +
-                       (span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int)));
+                       (span ? 0u : (unsigned)((p.cps * 64 + n_win + 2 * kPrePages) * sizeof(int))) +
+                       (a.pt_lds ? (unsigned)((kc.pages_per_req + vc.pages_per_req) * sizeof(int)) : 0u);
   // prefill (many workgroups per CU help): one LDS buffer for the K and V^T
   // tiles; decode (few workgroups, latency first): two
   if (p.nw == 4 && span && !f8)

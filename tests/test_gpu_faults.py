@@ -122,3 +122,41 @@ def test_v_beyond_fp16_range_raises_range_fault_in_decode_splits():
     assert fault_bits() & FAULT_RANGE
     assert not torch.isfinite(O[0]).all()
     assert torch.isfinite(O[1]).all()
+
+
+@pytest.mark.parametrize("H", [64, 16])
+def test_page_table_entry_out_of_range_raises_page_fault(H):
+    """A K page-table entry outside the pool, on a page that holds selected
+    blocks: the CSA decode attention reads zeros for those rows and raises
+    HSA_FAULT_PAGE (H = 64 reads the request's page table into LDS, H = 16
+    looks each page up in memory); the restored table raises nothing and gives
+    the first output back."""
+    FAULT_PAGE = 1
+    w = configs.shrink(configs.CSA_DECODE_128K, B=2, H=H, k_csa=64)
+    Ls = [9000, 6000]
+    st = T.build_state(w, "csa", Ls)
+    assert fault_bits() == 0
+    pos = torch.tensor(Ls, dtype=torch.int64, device="cuda")
+    q = L.Queries.list(pos, max(Ls))
+    Q = T.dev_bf16(np.stack([d["q"][0] for d in st["reqs"]]))
+    qi = T.dev_bf16(np.stack([d["qi"][0] for d in st["reqs"]]))
+    wt = torch.from_numpy(np.stack([d["w"][0] for d in st["reqs"]])).cuda()
+    idx, _ = L.indexer_topk(q, qi, wt, st["kic"], w.m_csa, w.n_win, w.k_csa)
+    O0, _ = L.csa_attn(q, Q, st["ring_k"], st["ring_v"], w.n_win, st["kc"], st["vc"], w.m_csa,
+                       idx, w.k_csa, out_fp32=True)
+    assert fault_bits() == 0
+    r, lp = 1, int(idx[1, 0].item()) // 64          # a page request 1 attends to
+    table = st["kc"].page_table
+    good = int(table[r, lp].item())
+    print(f"H={H}: page table entry ({r}, {lp}) set past the pool", flush=True)
+    table[r, lp] = st["kc"].data.shape[0] + 5
+    O1, _ = L.csa_attn(q, Q, st["ring_k"], st["ring_v"], w.n_win, st["kc"], st["vc"], w.m_csa,
+                       idx, w.k_csa, out_fp32=True)
+    assert fault_bits() & FAULT_PAGE
+    assert torch.equal(O1[0], O0[0])                 # request 0 does not use the entry
+    assert torch.isfinite(O1).all()
+    table[r, lp] = good
+    O2, _ = L.csa_attn(q, Q, st["ring_k"], st["ring_v"], w.n_win, st["kc"], st["vc"], w.m_csa,
+                       idx, w.k_csa, out_fp32=True)
+    assert fault_bits() == 0
+    assert torch.equal(O2, O0)
