@@ -249,12 +249,13 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
 /* A CSA layer's prefill in one call (wiki §5.3: indexer, top-k, then the
  * main attention over the selection and the window, as hsa_indexer_topk
  * followed by hsa_csa_attn).  The span is cut into stages of stage_q
- * consecutive queries (0: 8192); the attention of stage p runs on a stream of
- * the library's own (one per device, default priority, created on first use)
- * while the indexer and top-k of stage p + 1 run on `stream`, with events
- * ordering each stage's attention after its selection and `stream` after the
- * last attention.  Results are bit-identical to the two calls on the same
- * span.  q must be a span.  Arguments as hsa_indexer_topk (qI, w, H_I, d_I,
+ * consecutive queries (0: 4096).  The selections (indexer + top-k) of even
+ * stages run on `stream`, those of odd stages on a second stream, each with
+ * its own half of the selection workspace; every stage's attention runs on a
+ * third stream, after its stage's selection.  The two extra streams are the
+ * library's own (one pair per device, default priority, created on first
+ * use); events order them after the work already on `stream` and `stream`
+ * after both.  Results are bit-identical to the two calls on the same span.  q must be a span.  Arguments as hsa_indexer_topk (qI, w, H_I, d_I,
  * kIc, idx: required here, [n][k]) and hsa_csa_attn (Q .. lse); the indexer
  * keys are bf16, fp8 or fp4 as there, the scores fp32.  Workspace:
  * hsa_csa_prefill_workspace_bytes.  Host calls are serialised by a lock

@@ -381,15 +381,22 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
 
 // ---------------------------------------------------------------- CSA prefill, pipelined
 
-// The side stream the attention stages run on and the events that order them,
-// one set per device, created on first use and kept until the process ends.
+// The streams of the pipeline -- `sel`: odd stages' selections (even ones run
+// on the caller's stream), `att`: every stage's attention -- and the events
+// that order them, one set per device, created on first use and kept until
+// the process ends.
 struct PipeState {
-  hipStream_t side = nullptr;
+  hipStream_t sel = nullptr, att = nullptr;
   std::vector<hipEvent_t> ev;
 };
 static std::mutex g_pipe_mu;
 static PipeState g_pipe[64];
-constexpr int kStageQueries = 8192;
+constexpr int kStageQueries = 4096;
+
+// one selection workspace per selection stream
+static size_t csa_prefill_sel_bytes(const hsa_queries* q, int m, int n_win, int k) {
+  return (hsa_indexer_topk_workspace_bytes(q, m, n_win, k) + 255) & ~size_t(255);
+}
 
 size_t hsa_csa_prefill_workspace_bytes(const hsa_queries* q, int32_t H, int32_t m, int32_t n_win,
                                        int32_t k) {
@@ -397,8 +404,7 @@ size_t hsa_csa_prefill_workspace_bytes(const hsa_queries* q, int32_t H, int32_t 
   // every stage's selection fits the full span's layout (the score rows are
   // as long as the longest row of the span, the passes as wide); span
   // attention needs none
-  return hsa_indexer_topk_workspace_bytes(q, m, n_win, k) +
-         hsa_csa_attn_workspace_bytes(q, H, n_win, k);
+  return 2 * csa_prefill_sel_bytes(q, m, n_win, k) + hsa_csa_attn_workspace_bytes(q, H, n_win, k);
 }
 
 hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w, int32_t H_I,
@@ -430,20 +436,24 @@ hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w,
   const int n_st = (int)((q->n + (int64_t)S - 1) / S);
   std::lock_guard<std::mutex> lk(g_pipe_mu);
   PipeState& P = g_pipe[dev];
-  if (!P.side) {
-    hipStream_t st = nullptr;
-    hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_status(e, "csa_prefill: side stream");
-    P.side = st;
+  for (hipStream_t* st : {&P.sel, &P.att}) {
+    if (*st) continue;
+    hipError_t e = hipStreamCreateWithFlags(st, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_status(e, "csa_prefill: stream");
   }
-  while ((int)P.ev.size() < n_st + 1) {
+  // events: [0] fork, [1 + p] stage p's selection done, [1 + n_st], [2 + n_st] joins
+  while ((int)P.ev.size() < n_st + 3) {
     hipEvent_t ev;
     hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (e != hipSuccess) return hip_status(e, "csa_prefill: event");
     P.ev.push_back(ev);
   }
   const size_t o_row = (size_t)H * kD * (o_dtype == HSA_FP32 ? 4 : 2);
-  hipError_t e = hipSuccess;
+  const size_t half = csa_prefill_sel_bytes(q, m, n_win, k);
+  // the side streams start after everything already enqueued on `stream`
+  hipError_t e = hipEventRecord(P.ev[0], stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(P.sel, P.ev[0], 0);
+  if (e == hipSuccess) e = hipStreamWaitEvent(P.att, P.ev[0], 0);
   for (int p = 0; p < n_st && e == hipSuccess; ++p) {
     const int64_t c0 = (int64_t)p * S;
     const int nq = (int)(q->n - c0 < S ? q->n - c0 : S);
@@ -452,18 +462,24 @@ hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w,
     sub.span_pos0 = q->span_pos0 + c0;
     sub.max_pos = sub.span_pos0 + nq - 1;
     int32_t* idx_p = idx + c0 * k;
+    // consecutive stages' selections on two streams, each with its own half of
+    // the workspace (a stream's stages reuse its half in order)
+    hipStream_t ss = (p & 1) ? P.sel : stream;
     e = launch_indexer(sub, (const u16*)qI + c0 * kHI * kDI, w + c0 * kHI, *kIc, m, n_win, k,
-                       idx_p, nullptr, ws, ws_bytes, stream, nullptr, 1, false);
-    if (e == hipSuccess) e = hipEventRecord(P.ev[p], stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(P.side, P.ev[p], 0);
+                       idx_p, nullptr, (uint8_t*)ws + (p & 1) * half, half, ss, nullptr, 1,
+                       false);
+    if (e == hipSuccess) e = hipEventRecord(P.ev[1 + p], ss);
+    if (e == hipSuccess) e = hipStreamWaitEvent(P.att, P.ev[1 + p], 0);
     if (e == hipSuccess)
       e = launch_attn(sub, (const u16*)Q + c0 * H * kD, H, *win_k, *win_v, n_win, *kc, *vc, m,
                       idx_p, k, scale, (uint8_t*)O + c0 * o_row, o_dtype,
-                      lse ? lse + c0 * H : nullptr, nullptr, 0, P.side);
+                      lse ? lse + c0 * H : nullptr, nullptr, 0, P.att);
   }
-  // `stream` waits for the side stream's last stage, also after a failed launch
-  hipError_t j = hipEventRecord(P.ev[n_st], P.side);
-  if (j == hipSuccess) j = hipStreamWaitEvent(stream, P.ev[n_st], 0);
+  // `stream` waits for both side streams, also after a failed launch
+  hipError_t j = hipEventRecord(P.ev[1 + n_st], P.sel);
+  if (j == hipSuccess) j = hipStreamWaitEvent(stream, P.ev[1 + n_st], 0);
+  if (j == hipSuccess) j = hipEventRecord(P.ev[2 + n_st], P.att);
+  if (j == hipSuccess) j = hipStreamWaitEvent(stream, P.ev[2 + n_st], 0);
   if (e != hipSuccess) return hip_status(e, "csa_prefill");
   return hip_status(j, "csa_prefill: join");
 }
