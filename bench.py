@@ -244,15 +244,16 @@ def time_steps(steps_cycle, K, W):
     return ms
 
 
-def kernel_avg_ms(T, kid, fn, n):
+def kernel_avg_ms(T, kid, fn, n, warm=4):
     """Average duration of one kernel over n eager calls of fn(i): HIP events
     on the kernel's own stream, handed by the library to the kernel's dispatch
     (HSA_K_INDEXER_SCAN, _GEMM, _ATTN) or recorded around its launches (_SEL,
     _COMPRESS).  Returns (ms per launch, launches)."""
     import torch
-    # a few untimed calls first: the first eager calls after a graph replay or
-    # a different workload run slower than the steady state
-    for i in range(min(n, 4)):
+    # a few untimed calls first (warm > 0: calls that may repeat): the first
+    # eager calls after a graph replay or a different workload run slower than
+    # the steady state
+    for i in range(min(n, warm)):
         fn(i)
     torch.cuda.synchronize()
     T.kernel_timing_read(kid)
@@ -378,15 +379,16 @@ def mfma_summary(args):
     command line.  Writes profiles/mfma_<kernel>_<workload>.json."""
     kernel, workload, csv_path, alg_flops = args.mfma_summary
     alg = float(alg_flops)
-    busy, n = _pmc_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", kernel)
-    bf16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel)
-    f16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_F16", kernel)
-    grbm, _ = _pmc_per_dispatch(csv_path, "GRBM_GUI_ACTIVE", kernel)
+    g = args.grid   # one launch shape (the CSA prefill attention has two)
+    busy, n = _pmc_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", kernel, grid=g)
+    bf16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel, grid=g)
+    f16, _ = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_F16", kernel, grid=g)
+    grbm, _ = _pmc_per_dispatch(csv_path, "GRBM_GUI_ACTIVE", kernel, grid=g)
     active = grbm / 8
     simds = 256 * 4
     executed = (bf16 + f16) * 512
     name = kernel.split("<")[0]
-    out = {"kernel": kernel, "workload": workload,
+    out = {"kernel": kernel, "workload": workload, "grid_threads": g,
            "source_hash": source_hash(*kernel_sources(name)), "dispatches": n,
            "mfma_busy_cycles_per_simd": round(busy / simds, 1),
            "active_cycles": round(active, 1),
@@ -1010,7 +1012,9 @@ def bench_ragged(args, w):
     ms = total_ms / len(calls)
     # the dominant kernel's live duration: the scan over all 256 steps of copy 0
     restore()
-    scan_ms, cnt = kernel_avg_ms(T, T.K_INDEXER_SCAN, lambda i: calls[i * RAGGED_COPIES](), S)
+    # (no warm-up calls: the steps advance every request's position in order)
+    scan_ms, cnt = kernel_avg_ms(T, T.K_INDEXER_SCAN, lambda i: calls[i * RAGGED_COPIES](), S,
+                                 warm=0)
     restore()
     T.check_device_error()
     # algorithmic bytes per step (averaged over the 256 steps), from the seeded lengths
