@@ -250,12 +250,13 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
  * main attention over the selection and the window, as hsa_indexer_topk
  * followed by hsa_csa_attn).  The span is cut into stages of stage_q
  * consecutive queries (0: 4096).  The selections (indexer + top-k) of even
- * stages run on `stream`, those of odd stages on a second stream, each with
- * its own half of the selection workspace; every stage's attention runs on a
- * third stream, after its stage's selection.  The two extra streams are the
- * library's own (one pair per device, default priority, created on first
- * use); events order them after the work already on `stream` and `stream`
- * after both.  Results are bit-identical to the two calls on the same span.  q must be a span.  Arguments as hsa_indexer_topk (qI, w, H_I, d_I,
+ * and odd stages run on two streams, each with its own half of the selection
+ * workspace; every stage's attention runs on a third stream, after its
+ * stage's selection.  The three streams are the library's own (one set per
+ * device, created on first use and kept; default priority; each with a mask
+ * of every compute unit, which gives it a hardware queue of its own); events
+ * order them after the work already on `stream`, and `stream` after them.
+ * Results are bit-identical to the two calls on the same span.  q must be a span.  Arguments as hsa_indexer_topk (qI, w, H_I, d_I,
  * kIc, idx: required here, [n][k]) and hsa_csa_attn (Q .. lse); the indexer
  * keys are bf16, fp8 or fp4 as there, the scores fp32.  Workspace:
  * hsa_csa_prefill_workspace_bytes.  Host calls are serialised by a lock

@@ -78,3 +78,42 @@ def test_csa_prefill_offset_span():
     L.check_device_error()
     assert torch.equal(idx0, idx1) and torch.equal(O0, O1) and torch.equal(lse0, lse1)
     assert T_ >= p0 + n
+
+
+def test_csa_prefill_graph_replays():
+    """hsa_csa_prefill captured in a HIP graph (its own streams join the capture
+    through its fork and join events): every replay, with eager calls and host
+    synchronisation between them, equals the eager result bit for bit."""
+    w = configs.PREFILL_4K
+    inp = gen.prefill_layer(w, "csa")
+    T_ = inp["k"].shape[0]
+    gc = T.compress_layer(inp, "csa", w.m_csa)
+    q = L.Queries.span(T_)
+    qi, wt = T.dev_bf16(inp["qi"]), torch.from_numpy(inp["w"]).cuda()
+    Q, tk, tv = T.dev_bf16(inp["q"]), T.tokens(inp["k"]), T.tokens(inp["v"])
+    args = (q, qi, wt, gc["kic"], Q, tk, tv, w.n_win, gc["kc"], gc["vc"], w.m_csa, w.k_csa)
+    idx0, O0, _ = L.csa_prefill(*args, stage_q=1000, ws_key="graph_eager")
+    idx0, O0 = idx0.clone(), O0.clone()
+    torch.cuda.synchronize()
+    print("csa_prefill graph capture", flush=True)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            idx_g, O_g, _ = L.csa_prefill(*args, stage_q=1000, ws_key="graph")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx_g.fill_(-7)
+        O_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx_g, idx0), f"replay {rep}: idx"
+        assert torch.equal(O_g, O0), f"replay {rep}: O"
+        # eager work between the replays
+        idx_e, O_e, _ = L.csa_prefill(*args, stage_q=1000, ws_key="graph_eager")
+        torch.cuda.synchronize()
+        assert torch.equal(O_e, O0)
+    L.check_device_error()
+    del g
