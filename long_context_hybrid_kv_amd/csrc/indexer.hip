@@ -1602,8 +1602,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
       if (g < nl && j < s_ntop[g] && e[r] != 0u) atomicAdd(&hist[e[r] >> 16], e[r] & 0xFFFFu);
     }
     __syncthreads();
-    // threshold bin: thread t owns bins kBins - BPT(t+1) .. kBins - BPT t - 1
-    {
+    // threshold bin of the histogram in `hist` (the bin holding the k-th
+    // largest key, and the count above it): thread t owns bins
+    // kBins - BPT(t+1) .. kBins - BPT t - 1
+    auto find_threshold = [&]() {
       const int lo = kBins - BPT * (tid + 1);
       uint32_t v[BPT], sm = 0;
 #pragma unroll
@@ -1621,8 +1623,28 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
           cum += v[j];
         }
       }
-    }
-    __syncthreads();
+      __syncthreads();
+    };
+    // a key (score key << 32 | ~block) above the threshold bin -> bitmap; in
+    // it -> the threshold-bin candidates (one slot reservation per wave)
+    auto classify_thr = [&](uint64_t x, bool valid, int thr) {
+      const int bin = valid ? (int)(x >> 52) : -1;
+      if (bin > thr) {
+        const uint32_t blk = ~(uint32_t)x;
+        atomicOr(&bm[blk >> 5], 1u << (blk & 31));
+      }
+      const bool c = bin == thr;
+      const uint64_t cm = __ballot(c);
+      if (cm) {
+        const int leader = __ffsll((unsigned long long)cm) - 1;
+        uint32_t cb = 0;
+        if (lane == leader) cb = atomicAdd(&s_ntc, (uint32_t)__popcll(cm));
+        cb = lane_value(cb, leader);
+        const uint32_t p = cb + __popcll(cm & ((1ull << lane) - 1));
+        if (c && p < (uint32_t)kThrCandMax) tc[p] = x;
+      }
+    };
+    find_threshold();
     // the union holds the row's top-k iff every score left out lies in a bin
     // below the threshold bin
     tot = s_tot;
@@ -1712,13 +1734,50 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     if (tid == 0)   // which path served the query (stored at the end, off the critical path)
       path = full ? (s_bad ? 1 : (s_thr < 0 ? 2 : (s_thr < s_maxbc ? 3 : 4))) : 0;
     if (full) {
-      // exact selection over the whole row (rare)
+      // exact selection over the whole row: when the union cannot prove the
+      // answer -- a row scanned by few workgroups (each hands over at most
+      // kCandCap / 2 candidates, so under about 3k / 128 workgroups the union
+      // rarely holds the top-k), a list overflow, a tie storm.  One pass builds
+      // the row's histogram of the top 12 key bits and finds the threshold bin,
+      // a second marks the blocks above it and collects those inside it, which
+      // are refined like the union's; a threshold bin too full for LDS takes
+      // the 64-bit radix selection over the row.
       auto fkey = [&](int64_t i) {
         return ((uint64_t)order_key(score_load<S16>(srow, i)) << 32) | (uint64_t)(~(uint32_t)i);
       };
-      const uint64_t T = radix_kth<NT>(nv, k, fkey, 64, 0ull, h256, sh);
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) hist[tid + NT * j] = 0;
+      for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
+      if (tid == 0) { s_thr = -1; s_above = 0; s_ntc = 0; }
+      __syncthreads();
       for (int64_t i = tid; i < nv; i += NT)
-        if (fkey(i) >= T) atomicOr(&bm[i >> 5], 1u << (i & 31));
+        atomicAdd(&hist[order_key(score_load<S16>(srow, i)) >> 20], 1u);
+      __syncthreads();
+      find_threshold();
+      const int thr = s_thr;   // (nv > k: a bin holds the k-th largest key)
+      for (int64_t b0 = 0; b0 < nv; b0 += NT) {
+        const int64_t i = b0 + tid;
+        const bool valid = i < nv;
+        classify_thr(valid ? fkey(i) : 0ull, valid, thr);
+      }
+      __syncthreads();
+      const uint32_t ntc = s_ntc;
+      if (ntc <= (uint32_t)kThrCandMax) {
+        const uint64_t T = radix_kth<NT>((int64_t)ntc, k - (int)s_above,
+                                         [&](int64_t i) { return tc[i]; }, 52,
+                                         (uint64_t)thr << 52, h256, sh);
+        for (uint32_t i = tid; i < ntc; i += NT)
+          if (tc[i] >= T) {
+            const uint32_t blk = ~(uint32_t)tc[i];
+            atomicOr(&bm[blk >> 5], 1u << (blk & 31));
+          }
+      } else {
+        for (int64_t i = tid; i < W; i += NT) bm[i] = 0;
+        __syncthreads();
+        const uint64_t T = radix_kth<NT>(nv, k, fkey, 64, 0ull, h256, sh);
+        for (int64_t i = tid; i < nv; i += NT)
+          if (fkey(i) >= T) atomicOr(&bm[i >> 5], 1u << (i & 31));
+      }
     }
   } else {
     __syncthreads();
