@@ -866,7 +866,7 @@ __global__ __launch_bounds__(128) void attn_merge_upd_kernel(int n_qh, int H, in
                                                              UpdateArgs upd) {
   const int n_merge = (n_qh + 1) / 2;
   if ((int)blockIdx.x >= n_merge) {
-    decode_update_body<true>(upd, blockIdx.x - n_merge, fault);
+    decode_update_body<true, 16>(upd, blockIdx.x - n_merge, fault);
     return;
   }
   __shared__ float wgt[2][kMergeMaxSplits], wls[2][kMergeMaxSplits];

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(1024) void compress_page_kernel(Tokens x, int x_req
 // Decode-time cache upkeep for B requests (one workgroup each); the CSA decode
 // step runs the same upkeep inside the indexer scan launch instead.
 __global__ __launch_bounds__(128) void decode_update_kernel(UpdateArgs u, int* fault) {
-  decode_update_body<true>(u, blockIdx.x, fault);
+  decode_update_body<true, 16>(u, blockIdx.x, fault);
 }
 
 // Rewind after a draft: request b keeps tokens 0 .. keep[b] - 1, so each of its

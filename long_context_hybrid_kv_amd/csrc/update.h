@@ -51,6 +51,40 @@ __device__ __forceinline__ double pool_last(const Tokens& src, int r, int64_t bl
   return acc;
 }
 
+// pool_last of the K and V rings together, with PB ring rows of each (and
+// their weights) requested at once: the block's m - 1 older rows cost
+// ceil((m - 1) / PB) memory round trips instead of one per row, while the
+// float64 sums still run in slot order, so the values are pool_last's.
+template <int PB>
+__device__ __forceinline__ void pool_last_kv(const Tokens& rk, const Tokens& rv, int r,
+                                             int64_t blk, int m, int c,
+                                             const float* __restrict__ ak,
+                                             const float* __restrict__ av, u16 kn, u16 vn,
+                                             double* vk, double* vv) {
+  double sk = 0.0, sv = 0.0;
+  const int n = m - 1;
+  for (int j0 = 0; j0 < n; j0 += PB) {
+    u16 xk[PB], xv[PB];
+    float wk[PB], wv[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int j = j0 + u < n ? j0 + u : n - 1;   // (clamped reads past the block are unused)
+      xk[u] = rk.row(r, blk * m + j)[c];
+      xv[u] = rv.row(r, blk * m + j)[c];
+      wk[u] = ak[(int64_t)j * kD + c];
+      wv[u] = av[(int64_t)j * kD + c];
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (j0 + u < n) {
+        sk += (double)wk[u] * (double)bf16_to_f32(xk[u]);
+        sv += (double)wv[u] * (double)bf16_to_f32(xv[u]);
+      }
+  }
+  *vk = sk + (double)ak[(int64_t)n * kD + c] * (double)bf16_to_f32(kn);
+  *vv = sv + (double)av[(int64_t)n * kD + c] * (double)bf16_to_f32(vn);
+}
+
 // Largest v over the workgroup (every thread calls it; red holds >= 16 doubles).
 __device__ __forceinline__ double block_max(double v, double* red) {
 #pragma unroll
@@ -130,7 +164,10 @@ __device__ inline void append_kv(const Paged& pc, int b, int64_t blk, double v, 
 // With RoPE (F8 path) the token's pair angles are computed here, once, and
 // left in rcs[i] = (cos, sin) for the query at the same position; a position
 // outside [0, max_pos] is clamped for that (the attention clamps it too).
-template <bool F8>
+// PB > 1: a completed block's older ring rows are read PB at a time
+// (pool_last_kv); the launches that carry HCA layers' upkeep (m = 128) use it,
+// the others keep the registers of the plain loop.
+template <bool F8, int PB = 1>
 __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, int* fault,
                                            double (*rcs)[2]) {
   const int c = threadIdx.x;
@@ -189,8 +226,15 @@ __device__ inline void decode_update_token(const UpdateArgs& u, int b, int i, in
   if (!ok) return;
   {
     __shared__ double red[16];
-    const double vk = on ? pool_last(u.rk, b, blk, u.m, c, u.ak, kD, kn) : 0.0;
-    const double vv = on ? pool_last(u.rv, b, blk, u.m, c, u.av, kD, vn) : 0.0;
+    double vk = 0.0, vv = 0.0;
+    if (on) {
+      if constexpr (PB > 1) {
+        pool_last_kv<PB>(u.rk, u.rv, b, blk, u.m, c, u.ak, u.av, kn, vn, &vk, &vv);
+      } else {
+        vk = pool_last(u.rk, b, blk, u.m, c, u.ak, kD, kn);
+        vv = pool_last(u.rv, b, blk, u.m, c, u.av, kD, vn);
+      }
+    }
     append_kv<F8>(u.kc, b, blk, vk, fault, red);
     append_kv<F8>(u.vc, b, blk, vv, fault, red);
   }
@@ -243,11 +287,11 @@ __device__ inline void rope_query(const UpdateArgs& u, int b, int i, const doubl
 
 // Request b's n_tok tokens in order, and (a draft) its queries' request and
 // position for the selection and attention that follow.
-template <bool F8>
+template <bool F8, int PB = 1>
 __device__ inline void decode_update_body(const UpdateArgs& u, int b, int* fault) {
   __shared__ double rcs[kRopeDim / 2][2];   // RoPE: the current token's pair angles
   for (int i = 0; i < u.n_tok; ++i) {
-    decode_update_token<F8>(u, b, i, fault, rcs);
+    decode_update_token<F8, PB>(u, b, i, fault, rcs);
     __syncthreads();   // the next token's block check reuses the shared flag; rcs is complete
     if constexpr (F8) {
       if (u.q_out) {
