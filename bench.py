@@ -781,7 +781,7 @@ def bench_prefill(args, w):
     def csa():
         # the layer's selection and attention in one call, pipelined over
         # stages of queries (the bf16-score option keeps the separate calls)
-        if s16:
+        if s16 or getattr(args, "csa_separate_calls", False):
             return csa_serial()
         compress("csa")
         d = st["csa"]
@@ -874,9 +874,10 @@ def bench_prefill(args, w):
             "config": {"workload": w.name, "T": Tn, "heads": w.H, "kv_heads": 1, "d": 128,
                        "topk": w.k_csa, "window": w.n_win, "layers": "csa+hca", "planted": True,
                        "timed_pass": "compress + indexer + top-k + attention, both layers",
-                       "csa_layer": ("separate indexer_topk + csa_attn calls" if s16 else
-                                     "hsa_csa_prefill: selection of stage p+1 beside the "
-                                     "attention of stage p (8192-query stages)"),
+                       "csa_layer": ("separate indexer_topk + csa_attn calls"
+                                     if s16 or getattr(args, "csa_separate_calls", False) else
+                                     "hsa_csa_prefill: the selections of the next stages beside "
+                                     "the attention of each stage (4096-query stages)"),
                        **({"index_scores": "bf16"} if s16 else {})},
             "roofline": roof, "kernels": kernels}
 
@@ -1093,6 +1094,10 @@ def main():
                          "(hsa_indexer_topk_bf16_scores); also times the selector alone both ways "
                          "and reports the recall of the fp32-score selection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--csa-separate-calls", action="store_true",
+                    help="prefill: time the CSA layer as hsa_indexer_topk + hsa_csa_attn "
+                         "instead of hsa_csa_prefill (the library's pipeline streams are then "
+                         "never created; used for counter runs)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work per workload")
     ap.add_argument("--calibrate-copy", action="store_true",
