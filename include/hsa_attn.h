@@ -56,7 +56,9 @@
  *   - Ownership: the caller owns every buffer, including the workspace.  The
  *     library never allocates device memory and never synchronises, except in
  *     hsa_check_device_error().
- *   - Asynchrony: every compute call only enqueues work on `stream`.
+ *   - Asynchrony: every compute call only enqueues work on `stream`
+ *     (hsa_csa_prefill also on streams of its own, ordered with `stream` by
+ *     events, so that it behaves as one call on `stream`).
  *   - Validation: arguments are checked on the host before anything is
  *     enqueued; a failed check returns a negative status, enqueues nothing,
  *     and sets a thread-local message (hsa_last_error()).
