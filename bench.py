@@ -877,7 +877,7 @@ def bench_prefill(args, w):
                        "csa_layer": ("separate indexer_topk + csa_attn calls"
                                      if s16 or getattr(args, "csa_separate_calls", False) else
                                      "hsa_csa_prefill: the selections of the next stages beside "
-                                     "the attention of each stage (4096-query stages)"),
+                                     "the attention of each stage (16384-query stages)"),
                        **({"index_scores": "bf16"} if s16 else {})},
             "roofline": roof, "kernels": kernels}
 

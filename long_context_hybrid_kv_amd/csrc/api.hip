@@ -391,7 +391,7 @@ struct PipeState {
 };
 static std::mutex g_pipe_mu;
 static PipeState g_pipe[64];
-constexpr int kStageQueries = 4096;
+constexpr int kStageQueries = 16384;
 
 // one selection workspace per selection stream
 static size_t csa_prefill_sel_bytes(const hsa_queries* q, int m, int n_win, int k) {
