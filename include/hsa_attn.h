@@ -251,7 +251,8 @@ hsa_status hsa_csa_attn(const hsa_queries* q, const void* Q, int32_t H, int32_t 
 /* A CSA layer's prefill in one call (wiki §5.3: indexer, top-k, then the
  * main attention over the selection and the window, as hsa_indexer_topk
  * followed by hsa_csa_attn).  The span is cut into stages of stage_q
- * consecutive queries (0: 16384).  The selections (indexer + top-k) of even
+ * consecutive queries (0: 16384; widened when the span would need more than
+ * 1024 stages).  The selections (indexer + top-k) of even
  * and odd stages run on two streams, each with its own half of the selection
  * workspace; every stage's attention runs on a third stream, after its
  * stage's selection.  The three streams are the library's own (one set per

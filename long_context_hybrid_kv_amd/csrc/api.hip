@@ -392,6 +392,7 @@ struct PipeState {
 static std::mutex g_pipe_mu;
 static PipeState g_pipe[64];
 constexpr int kStageQueries = 16384;
+constexpr int kMaxStages = 1024;
 
 // one selection workspace per selection stream
 static size_t csa_prefill_sel_bytes(const hsa_queries* q, int m, int n_win, int k) {
@@ -432,7 +433,9 @@ hsa_status hsa_csa_prefill(const hsa_queries* q, const void* qI, const float* w,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
     return fail(HSA_ERR_HIP, "csa_prefill: no current device");
-  const int S = stage_q > 0 ? stage_q : kStageQueries;
+  // at most kMaxStages stages (one event each): a smaller stage_q is widened
+  int S = stage_q > 0 ? stage_q : kStageQueries;
+  if ((q->n + (int64_t)S - 1) / S > kMaxStages) S = (int)((q->n + kMaxStages - 1) / kMaxStages);
   const int n_st = (int)((q->n + (int64_t)S - 1) / S);
   std::lock_guard<std::mutex> lk(g_pipe_mu);
   PipeState& P = g_pipe[dev];
